@@ -1,0 +1,352 @@
+"""Pins of the CPU oracle to facts other than itself: closed forms, hand-worked values, brute force on tiny
+inputs, invariants, and special cases that reduce to a library routine (torch / numpy).  Runs on the CPU."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+# --------------------------------------------------------------- decoding
+def test_fp8_hand_values():
+    g = json.load(open(os.path.join(GOLD, "fp8_e4m3fn_hand.json")))
+    for code, val in g["codes"].items():
+        got = oracle.fp8_decode([int(code, 16)])[0]
+        assert got == val, code
+        assert math.copysign(1.0, got) == math.copysign(1.0, val), code
+
+
+def test_fp8_all_codes_vs_library_and_order():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.fp8_decode(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.all(np.isnan(ours[nan]))
+    assert np.array_equal(ours[~nan], lib[~nan])
+    pos = ours[:0x7F]
+    assert np.all(np.diff(pos) > 0)              # codes 0..0x7E increase strictly
+    assert np.array_equal(ours[0x80:0xFF], -pos)  # sign bit mirrors
+
+
+def test_bf16_rne_equals_veltkamp_split():
+    # Introducing Kiln, "The hyper-connection arithmetic was what spilled": in fp32, c = 65537 x and
+    # hi = c - (c - x) is exactly the round-to-nearest-even bf16 value (checked there on 100,000 values).
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(100_000) * np.exp2(rng.integers(-60, 60, 100_000))).astype(np.float32)
+    base = torch.from_numpy(x).to(torch.bfloat16).float().numpy().view(np.uint32)
+    ties = (base | np.uint32(0x8000)).view(np.float32)[:2000]     # exact half-way cases
+    x = np.concatenate([x, ties])
+    c = (x * np.float32(65537)).astype(np.float32)
+    hi = (c - (c - x)).astype(np.float32)
+    ours = oracle.bf16_round(x.astype(np.float64))
+    ours_f = (ours.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(ours_f, hi)
+    lib = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, lib)
+
+
+def test_bf16_round_ties_to_even_hand():
+    assert list(oracle.bf16_round([1.0, 1 + 2**-8, 1 + 3 * 2**-8, -(1 + 2**-8), 0.0, -0.0])) == \
+        [0x3F80, 0x3F80, 0x3F82, 0xBF80, 0x0000, 0x8000]
+
+
+# ---------------------------------------------------------------- indexer
+def _pool(P, ps, DI, rng, lo=-127, hi=127):
+    return rng.integers(lo, hi + 1, (P, ps, DI)).astype(np.int8)
+
+
+def test_indexer_unit_query_picks_coordinate():
+    rng = np.random.default_rng(2)
+    kp = _pool(5, 8, 16, rng)
+    pt = np.array([3, 0, 4, 1, 2], dtype=np.int32)
+    for d in (0, 7, 15):
+        q = np.zeros((1, 16), np.int8)
+        q[0, d] = 1
+        s = oracle.indexer_scores(q, kp, pt, 37)
+        for p in range(37):
+            assert s[p] == max(0, int(kp[pt[p // 8], p % 8, d]))
+
+
+def test_indexer_closed_forms_and_int32_bound():
+    kp = np.ones((2, 64, 128), np.int8)
+    q = np.ones((16, 128), np.int8)
+    assert np.all(oracle.indexer_scores(q, kp, np.array([0, 1], np.int32), 100) == 16 * 128)
+    s = oracle.indexer_scores(np.full((16, 128), 127, np.int8), np.full((1, 64, 128), 127, np.int8),
+                              np.array([0], np.int32), 64)
+    assert np.all(s == 16 * 128 * 127 * 127) and 16 * 128 * 127 * 127 == 33_032_192
+    # an all-negative head contributes nothing
+    q2 = np.ones((2, 128), np.int8)
+    q2[1] = -1
+    assert np.all(oracle.indexer_scores(q2, kp, np.array([0, 1], np.int32), 128) == 128)
+
+
+def test_indexer_relu_pair_gives_abs_dot():
+    rng = np.random.default_rng(3)
+    kp = _pool(4, 16, 32, rng)
+    v = rng.integers(-127, 128, 32).astype(np.int8)
+    q = np.stack([v, -v.astype(np.int16)]).astype(np.int8)    # relu(x) + relu(-x) = |x|
+    pt = np.array([2, 0, 3, 1], np.int32)
+    s = oracle.indexer_scores(q, kp, pt, 60)
+    keys = kp[pt].reshape(-1, 32)[:60].astype(np.int64)
+    assert np.array_equal(s, np.abs(keys @ v.astype(np.int64)))
+
+
+def test_indexer_page_table_indirection():
+    ps = 8
+    P = 6
+    kp = np.zeros((P, ps, 4), np.int8)
+    for pg in range(P):
+        for sl in range(ps):
+            kp[pg, sl, 0], kp[pg, sl, 1] = pg, sl
+    q = np.zeros((2, 4), np.int8)
+    q[0, 0] = 1
+    q[1, 1] = 1
+    pt = np.array([5, 2, 0, 4], np.int32)
+    s = oracle.indexer_scores(q, kp, pt, 29)
+    assert [int(v) for v in s] == [int(pt[p // ps]) + p % ps for p in range(29)]
+
+
+# ------------------------------------------------------------------ top-k
+def _brute_topk(s, k):
+    """Position p is kept iff fewer than k positions beat it under (score desc, position asc)."""
+    L = len(s)
+    keep = [p for p in range(L) if sum(1 for r in range(L) if s[r] > s[p] or (s[r] == s[p] and r < p)) < k]
+    return keep + [-1] * (k - len(keep))
+
+
+def test_topk_hand_cases():
+    g = json.load(open(os.path.join(GOLD, "topk_hand.json")))
+    for c in g["cases"]:
+        assert list(oracle.topk(np.array(c["scores"], np.int32), c["k"])) == c["sel"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    L = int(rng.integers(1, 200))
+    k = int(rng.integers(1, 260))
+    s = rng.integers(0, 6 if seed % 2 else 10**6, L).astype(np.int32)   # odd seeds: tie-heavy
+    assert list(oracle.topk(s, k)) == _brute_topk(list(s), k)
+
+
+def test_topk_threshold_characterisation():
+    rng = np.random.default_rng(9)
+    s = rng.integers(0, 50, 4000).astype(np.int32)
+    k = 256
+    sel = oracle.topk(s, k)
+    assert np.all(np.diff(sel) > 0) and len(sel) == k
+    T = np.sort(s)[::-1][k - 1]
+    gt = np.nonzero(s > T)[0]
+    eq = np.nonzero(s == T)[0][: k - len(gt)]
+    assert np.array_equal(sel, np.sort(np.concatenate([gt, eq])))
+
+
+def test_topk_k_at_least_L_and_all_equal():
+    s = np.arange(10, dtype=np.int32)[::-1].copy()
+    assert list(oracle.topk(s, 12)) == list(range(10)) + [-1, -1]
+    assert list(oracle.topk(np.full(100, 7, np.int32), 5)) == [0, 1, 2, 3, 4]
+
+
+# -------------------------------------------------------------- attention
+def _fp8_lib(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _latents_lib(kv, ks, pt, ps, positions):
+    """Decoded latents of positions through torch's FP8 decode (independent of the oracle's)."""
+    out = []
+    for p in positions:
+        pg, sl = pt[p // ps], p % ps
+        if kv.dtype == np.uint8:
+            c = _fp8_lib(kv[pg, sl]) * np.repeat(ks[pg, sl].astype(np.float64), 128)[: kv.shape[2]]
+        else:
+            c = kv[pg, sl].astype(np.float64)
+        out.append(c)
+    return np.array(out)
+
+
+def _small_attn_inputs(seed, fp8=True, P=6, ps=16, H=4, Dc=192, L=80):
+    rng = np.random.default_rng(seed)
+    lat = torch.from_numpy(rng.standard_normal((P * ps, 1, Dc)).astype(np.float32))
+    if fp8:
+        codes, sc = synth.quant_fp8_blocks(lat, 1, 128)
+        kv = codes.reshape(P, ps, Dc).numpy()
+        ks = sc.reshape(P, ps, -1).numpy()
+    else:
+        kv, ks = lat.reshape(P, ps, Dc).numpy(), None
+    q = rng.standard_normal((H, Dc)).astype(np.float32)
+    pt = rng.permutation(P).astype(np.int32)
+    return q, kv, ks, pt, ps, L
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_attention_all_positions_is_full_attention(fp8):
+    q, kv, ks, pt, ps, L = _small_attn_inputs(4, fp8)
+    sel = np.arange(L, dtype=np.int32)
+    Dv = 128
+    o, p = oracle.attention(q, kv, ks, pt, sel, 0.125, Dv, want_p=True)
+    C = torch.from_numpy(_latents_lib(kv, ks, pt, ps, range(L)))
+    Q = torch.from_numpy(q.astype(np.float64))
+    ref = torch.softmax(0.125 * Q @ C.T, dim=-1) @ C[:, :Dv]
+    assert np.allclose(o, ref.numpy(), rtol=1e-12, atol=1e-13)
+    assert np.all(np.abs(p.sum(1) - 1.0) < 1e-12)
+
+
+def test_attention_special_cases():
+    q, kv, ks, pt, ps, L = _small_attn_inputs(5)
+    Dv = 160
+    # a single selected position returns its value part exactly
+    sel = np.array([-1, 17, -1, -1], np.int32)
+    o = oracle.attention(q, kv, ks, pt, sel, 0.1, Dv)
+    c17 = _latents_lib(kv, ks, pt, ps, [17])[0][:Dv]
+    assert np.array_equal(o, np.tile(c17, (q.shape[0], 1)))
+    # q = 0 gives the mean of the selected values
+    sel = np.array([3, 9, 40, 77, -1], np.int32)
+    o0 = oracle.attention(np.zeros_like(q), kv, ks, pt, sel, 0.1, Dv)
+    mean = _latents_lib(kv, ks, pt, ps, [3, 9, 40, 77])[:, :Dv].mean(0)
+    assert np.allclose(o0, np.tile(mean, (q.shape[0], 1)), rtol=0, atol=1e-14)
+    # order of the selected list does not matter
+    o1 = oracle.attention(q, kv, ks, pt, sel, 0.1, Dv)
+    o2 = oracle.attention(q, kv, ks, pt, sel[[4, 2, 0, 3, 1]], 0.1, Dv)
+    assert np.allclose(o1, o2, rtol=1e-13, atol=1e-15)
+    # no selected entry (empty sequence) -> zeros
+    assert np.all(oracle.attention(q, kv, ks, pt, np.full(4, -1, np.int32), 0.1, Dv) == 0)
+
+
+def test_attention_identical_latents():
+    q, kv, ks, pt, ps, L = _small_attn_inputs(6)
+    kv[:] = kv[0, 0]
+    ks[:] = ks[0, 0]
+    o = oracle.attention(q, kv, ks, pt, np.arange(0, 60, 3, dtype=np.int32), 0.3, 192)
+    c = _latents_lib(kv, ks, pt, ps, [0])[0]
+    assert np.allclose(o, np.tile(c, (q.shape[0], 1)), rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------- projection
+def _dec_mat(w, s):
+    """Decode block-scaled FP8 [..., R, C] through torch (library) for a dense reference."""
+    v = _fp8_lib(w)
+    R, Cc = w.shape[-2:]
+    sc = np.repeat(np.repeat(s.astype(np.float64), 128, axis=-2), 128, axis=-1)[..., :R, :Cc]
+    return v * sc
+
+
+def test_out_proj_identity_and_library():
+    rng = np.random.default_rng(7)
+    H, Dv = 4, 16
+    o = rng.standard_normal((H, Dv))
+    x = rng.standard_normal(H * Dv).astype(np.float32)
+    h = oracle.out_proj(o, None, None, np.eye(H * Dv, dtype=np.float32), None, x)
+    assert np.array_equal(h, x.astype(np.float64) + o.ravel())
+    # FP8 block-scaled W_UV and W_O against a dense numpy product of torch-decoded weights
+    H, Dv, hd, D = 3, 256, 128, 384
+    o = rng.standard_normal((H, Dv))
+    wuv, suv = synth.quant_fp8_blocks(torch.from_numpy(rng.standard_normal((H, hd, Dv)).astype(np.float32) * .02),
+                                      128, 128)
+    wo, so = synth.quant_fp8_blocks(torch.from_numpy(rng.standard_normal((D, H * hd)).astype(np.float32) * .02),
+                                    128, 128)
+    xb = torch.from_numpy(rng.standard_normal(D).astype(np.float32)).to(torch.bfloat16)
+    xbits = xb.view(torch.int16).numpy().view(np.uint16)
+    h = oracle.out_proj(o, wuv.numpy(), suv.numpy(), wo.numpy(), so.numpy(), xbits)
+    Wuv = _dec_mat(wuv.numpy(), suv.numpy())
+    Wo = _dec_mat(wo.numpy(), so.numpy())
+    u = np.einsum("hrv,hv->hr", Wuv, o).ravel()
+    ref = xb.double().numpy() + Wo @ u
+    assert np.allclose(h, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- router
+def test_router_brute_force_and_gates():
+    rng = np.random.default_rng(8)
+    E, D, ke = 12, 40, 3
+    h = rng.standard_normal(D)
+    wr = (rng.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)
+    wr[5] = wr[2]                                        # exact tie: expert 2 must win over 5
+    bias = np.zeros(E, np.float32)
+    lg, ex, g = oracle.router(h, wr, bias, ke)
+    assert np.allclose(lg, wr.astype(np.float64) @ h, rtol=1e-13, atol=1e-13)
+    order = sorted(range(E), key=lambda e: (-lg[e], e))
+    assert list(ex) == order[:ke]
+    assert abs(g.sum() - 1) < 1e-15 and np.all(np.diff(g) <= 0)
+    ref = torch.softmax(torch.tensor(lg[ex]), 0).numpy()
+    assert np.allclose(g, ref, rtol=1e-14)
+    # one-hot router rows read h directly; ke = 1 gives gate 1
+    wr1 = np.eye(D, dtype=np.float32)[:E]
+    lg1, ex1, g1 = oracle.router(h, wr1, None, 1)
+    assert np.array_equal(lg1, h[:E]) and ex1[0] == int(np.argmax(h[:E])) and g1[0] == 1.0
+    # tie between duplicated rows resolves to the lower id on both sides of the boundary
+    wr2 = np.zeros((4, D), np.float32)
+    lg2, ex2, _ = oracle.router(h, wr2, np.array([0, 1, 1, 0], np.float32), 2)
+    assert list(ex2) == [1, 2]
+
+
+# ------------------------------------------------------------------- FFN
+def _expert_bank(rng, n, D, I, fp8):
+    bank = {}
+    for e in range(n):
+        ws = [rng.standard_normal(s).astype(np.float32) * 0.05 for s in ((I, D), (I, D), (D, I))]
+        if fp8:
+            parts = []
+            for w in ws:
+                c, s = synth.quant_fp8_blocks(torch.from_numpy(w), 128, 128)
+                parts += [c.numpy(), s.numpy()]
+            bank[e] = tuple(parts)
+        else:
+            bank[e] = (ws[0], None, ws[1], None, ws[2], None)
+    return bank
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_ffn_single_expert_is_dense_swiglu(fp8):
+    rng = np.random.default_rng(10)
+    D, I = 256, 384
+    bank = _expert_bank(rng, 3, D, I, fp8)
+    h = rng.standard_normal(D)
+    y = oracle.ffn(h, [1], [1.0], bank.__getitem__, 3, 0)
+    wg, sg, wu, su, wd, sd = bank[1]
+    dec = (lambda w, s: _dec_mat(w, s)) if fp8 else (lambda w, s: w.astype(np.float64))
+    Wg, Wu, Wd = (torch.from_numpy(dec(w, s)) for w, s in ((wg, sg), (wu, su), (wd, sd)))
+    ht = torch.from_numpy(h)
+    ref = ht + Wd @ (torch.nn.functional.silu(Wg @ ht) * (Wu @ ht))
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_ffn_structure():
+    rng = np.random.default_rng(11)
+    D, I = 128, 128
+    bank = _expert_bank(rng, 5, D, I, False)          # experts 0..3 routed, 4 shared
+    h = rng.standard_normal(D)
+    y_sh = oracle.ffn(h, [2, 0], [0.75, 0.25], bank.__getitem__, 4, 1)
+    y_no = oracle.ffn(h, [2, 0], [0.75, 0.25], lambda e: bank[e], 4, 0)
+    f_sh = oracle.ffn(h, [4], [1.0], bank.__getitem__, 5, 0) - h       # shared expert alone, gate 1
+    assert np.allclose(y_sh - y_no, f_sh, rtol=1e-12, atol=1e-13)
+    y2 = oracle.ffn(h, [2, 0], [1.5, 0.5], bank.__getitem__, 4, 0)      # linear in the gates
+    assert np.allclose(y2 - h, 2 * (y_no - h), rtol=1e-13, atol=1e-14)
+    zero = {e: (w[0], None, w[2], None, np.zeros_like(w[4]), None) for e, w in bank.items()}
+    assert np.array_equal(oracle.ffn(h, [1, 3], [0.5, 0.5], zero.__getitem__, 4, 1), h)   # W_down = 0
+
+
+# ------------------------------------------------------------ whole rows
+def test_layer_rows_tiny_fp8():
+    spec = synth.small_fp8_spec(B=2, seq_lens=(700, 0), D=256, H=4, head_dim=128, topk=256, E=6, ke=2, I=256)
+    t = synth.make_layer(spec, seed=3)
+    orc = oracle.LayerOracle(spec, t)
+    r0 = orc.row(0)
+    assert np.all(np.diff(r0["sel"]) > 0) and r0["sel"].min() >= 0
+    assert len(set(r0["experts"])) == spec.ke and abs(r0["gates"].sum() - 1) < 1e-14
+    r1 = orc.row(1)                                   # padding row: nothing selected, o = 0, h = x
+    assert np.all(r1["sel"] == -1) and np.all(r1["o"] == 0)
+    assert np.array_equal(r1["h"], oracle.bf16_to_f64(t["x"][1].view(torch.int16).numpy().view(np.uint16)))
