@@ -1,0 +1,217 @@
+/*
+ * dl.h — C ABI of the sparse-attention MoE decode layer step for AMD MI355X (gfx950).
+ *
+ * One decode step of a long-context sparse-attention mixture-of-experts layer:
+ *   S1  an int8 indexer scores every cached position of each sequence,
+ *   S2  the best `top_k` positions are kept,
+ *   S3-S5 attention runs over only those FP8 latent entries, then W_UV, W_O and the residual,
+ *   S6  a router picks each token's experts,
+ *   S7-S9 the chosen FP8 SwiGLU experts (plus shared experts) stream through the FFN.
+ * Sources (the pages this follows):
+ *   "RunanywhereAI/trnrt" summary, "The interesting bit": sparse attention over the top 2,048
+ *     positions; decode layers as fused kernels.
+ *   "Introducing Kiln: LLM Inference on AWS Trainium":
+ *     "How was Kiln measured against vLLM on H200?" — sparse attention over a compressed latent
+ *       cache that is not split across heads; routed experts (8 per token) and a shared expert;
+ *       FP8 weights with 128 x 128 block scales;
+ *     "What moved the number from 19.4 to 122.9 tokens a second?" — separate scoring and top-k
+ *       kernels over a separate pool-key cache; MoE tile skip;
+ *     "A collective costs per graph, so the graphs got big" — each expert applied once to all of
+ *       its tokens;
+ *     "The decode kernels, and why they are opt-in" — gather the selected entries, do not mask;
+ *     "What could only a device show?" — padded rows must not write what others read; a host copy
+ *       is not ordered behind work already queued.
+ *
+ * Conventions for every entry point
+ *   Memory      Every tensor pointer is a DEVICE pointer owned by the caller, row-major and
+ *               densely packed in the stated shape.  The library never allocates, frees or keeps
+ *               device memory; scratch comes from the caller's workspace `ws` of `ws_bytes` bytes
+ *               (query the size first; 256-byte alignment).  Inputs are never modified; outputs are
+ *               overwritten completely (including -1 padding).  Descriptor structs (dl_pages,
+ *               dl_mat, dl_layer_desc, dl_layer_io) live in HOST memory and are read during the
+ *               call only.
+ *   Streams     Work is only enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *               stream).  Nothing synchronises; the caller orders its own writes of the inputs on
+ *               that stream.  Concurrent calls need distinct workspaces.
+ *   Errors      Arguments are checked on the host before anything is enqueued.  On error the call
+ *               returns a negative dl_status, enqueues nothing and sets dl_last_error().  A request
+ *               the kernels do not support is rejected (DL_ERR_UNSUPPORTED), never degraded.  A
+ *               failed launch returns DL_ERR_HIP.
+ *   Padding     seq_lens[b] == 0 marks a padding row: its sel is all -1, its attention output is 0
+ *               (so its hidden state is the residual), and it writes only its own output rows.
+ *   Determinism Identical inputs give bitwise identical outputs (no floating-point atomics).
+ */
+#ifndef DL_H
+#define DL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DL_ABI_VERSION 1
+
+typedef enum {
+    DL_OK = 0,
+    DL_ERR_NULL = -1,        /* a required pointer is NULL */
+    DL_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+    DL_ERR_DTYPE = -3,       /* unsupported dtype or dtype combination */
+    DL_ERR_UNSUPPORTED = -4, /* valid request the kernels do not implement */
+    DL_ERR_WORKSPACE = -5,   /* workspace NULL, misaligned or too small */
+    DL_ERR_HIP = -6          /* a HIP launch failed */
+} dl_status;
+
+typedef enum { DL_F32 = 0, DL_BF16 = 1, DL_FP8_E4M3 = 2, DL_I8 = 3, DL_I32 = 4 } dl_dtype;
+
+/* Paged cache geometry of a batch.  Position p of row b lives in page
+ * page_table[b * max_pages_per_seq + p / page_size], slot p % page_size.
+ * page_size is a power of two; entries past ceil(seq_lens[b] / page_size) are never read. */
+typedef struct {
+    int32_t batch;             /* B >= 1 */
+    int32_t page_size;         /* tokens per page, power of two, 1..1024 */
+    int32_t max_pages_per_seq; /* columns of page_table; max seq_len <= this * page_size */
+    const int32_t *seq_lens;   /* device int32 [B], 0 <= seq_lens[b] <= max_pages_per_seq * page_size */
+    const int32_t *page_table; /* device int32 [B, max_pages_per_seq], page ids of the pools */
+} dl_pages;
+
+/* A stack of weight matrices, row-major [count][rows = out][cols = in].
+ * DL_FP8_E4M3: w holds OCP e4m3fn codes and scale holds one fp32 per 128 x 128 block,
+ * [count][ceil(rows/128)][ceil(cols/128)]; the weight is code * scale ("FP8 weights with
+ * 128 x 128 block scales", Kiln, "How was Kiln measured against vLLM on H200?").
+ * DL_F32: w holds fp32 values, scale is NULL. */
+typedef struct {
+    const void *w;
+    const float *scale;
+    int32_t dtype;
+    int32_t count, rows, cols;
+} dl_mat;
+
+int dl_abi_version(void);
+/* Message of the last failed call on this host thread (library-owned, valid until the next call). */
+const char *dl_last_error(void);
+
+/* ---------------------------------------------------------------- S1 + S2
+ * Indexer scoring and exact top-k selection (Kiln, "What moved the number ...": a scoring kernel
+ * and a top-k kernel over a separate key cache; trnrt summary: the top 2,048 positions are kept).
+ * For every row b and position p < seq_lens[b]:
+ *   score[p] = sum_{h < n_heads} max(0, sum_{d < dim} q_idx[b,h,d] * k_pool[page, slot, d])
+ * accumulated exactly in int32.  The kept set is the first min(top_k, seq_lens[b]) positions under
+ * the order (score descending, position ascending) — ties go to the lower position.
+ *   q_idx   int8 [B, n_heads, dim]
+ *   k_pool  int8 [n_pages, page_size, dim]
+ *   sel     int32 [B, top_k]  out: kept positions in ascending order, then -1
+ *   sel_score int32 [B, top_k] out, nullable: score of each kept position (0 for padding)
+ * Limits: 1 <= n_heads <= 64, dim % 16 == 0, dim <= 256, n_heads * dim <= 131071 (int32 bound),
+ * 1 <= top_k <= 65536.  Workspace: dl_indexer_topk_workspace(pages). */
+size_t dl_indexer_topk_workspace(const dl_pages *pages);
+int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_pool, int32_t n_heads,
+                    int32_t dim, int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* ---------------------------------------------------------------- S3 - S5
+ * Sparse MLA decode attention over the kept positions only (Kiln, "The decode kernels ...":
+ * gather the selected entries instead of masking all keys), every head reading the same latent
+ * vector (Kiln, "How was Kiln measured ...": compressed latent cache not split across heads):
+ *   c_j     = latent of position sel[b,j] (FP8 code * scale of its 128-feature block, or fp32)
+ *   logit   = sm_scale * q[b,h,:] . c_j          (all d_c features act as the key)
+ *   p       = softmax over the kept j            (fp32, max subtracted)
+ *   o[b,h]  = sum_j p_j * c_j[:d_v]              (the first d_v features act as the value)
+ * then, when w_o is given:  out[b] = residual[b] + W_O concat_h(W_UV[h] o[b,h])  (W_UV optional),
+ * else out = o.
+ *   q        bf16 or fp32 [B, n_heads, d_c]
+ *   kv_pool  FP8 codes [n_pages, page_size, d_c] with kv_scale fp32 [n_pages, page_size, ceil(d_c/128)],
+ *            or fp32 [n_pages, page_size, d_c] with kv_scale NULL
+ *   sel      int32 [B, top_k] as written by dl_indexer_topk (-1 entries skipped)
+ *   w_uv     nullable; count = n_heads, cols = d_v, rows = head_dim
+ *   w_o      nullable; rows = D, cols = n_heads * (w_uv ? head_dim : d_v)
+ *   residual bf16 or fp32 [B, D] (required with w_o)
+ *   out      fp32 [B, n_heads, d_v] (no w_o) or fp32 [B, D]
+ * Limits: d_v <= d_c <= 1024; FP8 weights need rows % 16 == 0 and cols % 128 == 0.
+ * Workspace: dl_sparse_attn_workspace(...). */
+size_t dl_sparse_attn_workspace(int32_t batch, int32_t n_heads, int32_t d_v, int32_t top_k, const dl_mat *w_uv,
+                                const dl_mat *w_o);
+int dl_sparse_attn_decode(const dl_pages *pages, const void *q, int32_t q_dt, const void *kv_pool,
+                          const float *kv_scale, int32_t kv_dt, int32_t n_heads, int32_t d_c, int32_t d_v,
+                          float sm_scale, const int32_t *sel, int32_t top_k, const dl_mat *w_uv, const dl_mat *w_o,
+                          const void *residual, int32_t res_dt, float *out, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* ---------------------------------------------------------------- S6
+ * Router (Kiln, "How was Kiln measured ...": routed experts, 8 per token):
+ *   logits[b,e] = W_r[e] . h[b] + bias[e]     (fp64 accumulation of fp32 products)
+ *   experts[b]  = the top_k experts by (logit descending, expert id ascending), in that order
+ *   gates[b]    = softmax over those top_k logits
+ *   h fp32 [B, D]; w_r fp32 [n_experts, D]; bias fp32 [n_experts] nullable;
+ *   experts int32 [B, top_k]; gates fp32 [B, top_k]; logits fp32 [B, n_experts] nullable.
+ * Limits: 1 <= top_k <= 32, top_k <= n_experts <= 4096.  Workspace: dl_moe_route_workspace(B, n_experts). */
+size_t dl_moe_route_workspace(int32_t B, int32_t n_experts);
+int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const float *bias, int32_t n_experts,
+                 int32_t top_k, int32_t *experts, float *gates, float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- S7 - S9
+ * Expert FFN (Kiln, "A collective costs per graph ...": each expert applied once to all of its
+ * tokens; "What moved the number ...": experts with no token are skipped):
+ *   f_e(h) = W_down[e] (silu(W_gate[e] h) * (W_up[e] h)),  silu(g) = g / (1 + e^-g)
+ *   out[b] = residual[b] + sum_{j<top_k} gates[b,j] f_{experts[b,j]}(h[b]) + sum_s f_{n_routed+s}(h[b])
+ * summed in that order (residual NULL: 0).
+ *   h fp32 [B, D]; experts int32 [B, top_k] (each < n_routed); gates fp32 [B, top_k];
+ *   w_gate, w_up: count = n_routed + n_shared, rows = inter, cols = D;
+ *   w_down: count = n_routed + n_shared, rows = D, cols = inter;
+ *   residual fp32 [B, D] nullable; out [B, D] in out_dt (DL_F32 or DL_BF16, rounded once, RNE).
+ * Limits: B * (top_k + n_shared) <= 16384; n_routed + n_shared <= 4096.  With FP8 weights the
+ * activations enter the matrix cores as two FP8 parts (value and remainder) with per-128-block
+ * scales.  Workspace: dl_moe_ffn_workspace(...). */
+size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared);
+int dl_moe_ffn(const float *h, int32_t B, int32_t D, int32_t inter, const int32_t *experts, const float *gates,
+               int32_t top_k, const dl_mat *w_gate, const dl_mat *w_up, const dl_mat *w_down, int32_t n_routed,
+               int32_t n_shared, const float *residual, void *out, int32_t out_dt, void *ws, size_t ws_bytes,
+               void *stream);
+
+/* ---------------------------------------------------------------- the whole step
+ * dl_layer_step == dl_indexer_topk -> dl_sparse_attn_decode(w_uv, w_o, residual = x) -> dl_moe_route
+ * -> dl_moe_ffn(residual = h), with every intermediate kept in the workspace. */
+typedef struct dl_layer_desc {
+    int32_t D;           /* hidden size */
+    int32_t n_heads;     /* query heads */
+    int32_t d_c, d_v;    /* latent (key) width and value width */
+    int32_t idx_heads;   /* indexer heads */
+    int32_t idx_dim;     /* indexer dim */
+    int32_t top_k;       /* positions kept */
+    int32_t n_routed, n_shared, expert_top_k, inter;
+    float sm_scale;
+    int32_t q_dt;        /* DL_BF16 | DL_F32 (q and x) */
+    int32_t kv_dt;       /* DL_FP8_E4M3 | DL_F32 */
+    int32_t out_dt;      /* DL_BF16 | DL_F32 */
+    dl_mat w_uv;         /* w == NULL: no W_UV */
+    dl_mat w_o;
+    const float *w_r;    /* fp32 [n_routed, D] */
+    const float *r_bias; /* fp32 [n_routed], nullable */
+    dl_mat w_gate, w_up, w_down;
+} dl_layer_desc;
+
+typedef struct dl_layer_io {
+    dl_pages pages;
+    const void *x;        /* [B, D] q_dt */
+    const void *q;        /* [B, n_heads, d_c] q_dt */
+    const int8_t *q_idx;  /* [B, idx_heads, idx_dim] */
+    const void *kv_pool;  /* [n_pages, page_size, d_c] kv_dt */
+    const float *kv_scale;/* [n_pages, page_size, ceil(d_c/128)] or NULL */
+    const int8_t *k_pool; /* [n_pages, page_size, idx_dim] */
+    void *y;              /* out [B, D] out_dt */
+    /* optional debug outputs (nullable), for stage-wise checks of the fused step */
+    int32_t *sel;         /* [B, top_k] */
+    float *h;             /* [B, D] fp32 hidden state after attention + residual */
+    int32_t *experts;     /* [B, expert_top_k] */
+    float *gates;         /* [B, expert_top_k] */
+    float *o;             /* [B, n_heads, d_v] attention output before projection */
+} dl_layer_io;
+
+size_t dl_layer_workspace(const dl_layer_desc *desc, const dl_pages *pages);
+int dl_layer_step(const dl_layer_desc *desc, const dl_layer_io *io, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DL_H */

@@ -1,0 +1,240 @@
+"""Python binding of libdl.so, the gfx950 sparse-attention MoE decode layer step.
+
+Argument marshalling only: torch tensors supply device pointers and the current HIP stream; every step
+runs in the library's kernels.  Importing works without a GPU (so the C ABI can be inspected), but every
+compute call requires the built library and a visible GPU and raises otherwise — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdl.so")
+ABI_VERSION = 1
+
+DL_F32, DL_BF16, DL_FP8_E4M3, DL_I8, DL_I32 = 0, 1, 2, 3, 4
+STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE", -4: "DL_ERR_UNSUPPORTED",
+          -5: "DL_ERR_WORKSPACE", -6: "DL_ERR_HIP"}
+
+EXPORTS = ["dl_abi_version", "dl_last_error", "dl_indexer_topk_workspace", "dl_indexer_topk",
+           "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
+           "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step"]
+
+
+class DLError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Pages(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32),
+                ("seq_lens", C.c_void_p), ("page_table", C.c_void_p)]
+
+
+class Mat(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("scale", C.c_void_p), ("dtype", C.c_int32), ("count", C.c_int32),
+                ("rows", C.c_int32), ("cols", C.c_int32)]
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("D", C.c_int32), ("n_heads", C.c_int32), ("d_c", C.c_int32), ("d_v", C.c_int32),
+                ("idx_heads", C.c_int32), ("idx_dim", C.c_int32), ("top_k", C.c_int32), ("n_routed", C.c_int32),
+                ("n_shared", C.c_int32), ("expert_top_k", C.c_int32), ("inter", C.c_int32), ("sm_scale", C.c_float),
+                ("q_dt", C.c_int32), ("kv_dt", C.c_int32), ("out_dt", C.c_int32), ("w_uv", Mat), ("w_o", Mat),
+                ("w_r", C.c_void_p), ("r_bias", C.c_void_p), ("w_gate", Mat), ("w_up", Mat), ("w_down", Mat)]
+
+
+class LayerIO(C.Structure):
+    _fields_ = [("pages", Pages), ("x", C.c_void_p), ("q", C.c_void_p), ("q_idx", C.c_void_p),
+                ("kv_pool", C.c_void_p), ("kv_scale", C.c_void_p), ("k_pool", C.c_void_p), ("y", C.c_void_p),
+                ("sel", C.c_void_p), ("h", C.c_void_p), ("experts", C.c_void_p), ("gates", C.c_void_p),
+                ("o", C.c_void_p)]
+
+
+_lib = None
+
+
+def load(require_gpu: bool = True):
+    """Load libdl.so (raises if it is missing or its ABI differs)."""
+    global _lib
+    if require_gpu and not torch.cuda.is_available():
+        raise RuntimeError("sparse_attention_moe_amd needs a ROCm GPU (gfx950); none is visible")
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = C.CDLL(LIB_PATH)
+        P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+        L.dl_abi_version.restype = C.c_int
+        L.dl_last_error.restype = C.c_char_p
+        L.dl_indexer_topk_workspace.restype = sz
+        L.dl_indexer_topk_workspace.argtypes = [C.POINTER(Pages)]
+        L.dl_indexer_topk.argtypes = [C.POINTER(Pages), P, P, i32, i32, i32, P, P, P, sz, P]
+        L.dl_sparse_attn_workspace.restype = sz
+        L.dl_sparse_attn_workspace.argtypes = [i32, i32, i32, i32, C.POINTER(Mat), C.POINTER(Mat)]
+        L.dl_sparse_attn_decode.argtypes = [C.POINTER(Pages), P, i32, P, P, i32, i32, i32, i32, C.c_float, P, i32,
+                                            C.POINTER(Mat), C.POINTER(Mat), P, i32, P, P, sz, P]
+        L.dl_moe_route_workspace.restype = sz
+        L.dl_moe_route_workspace.argtypes = [i32, i32]
+        L.dl_moe_route.argtypes = [P, i32, i32, P, P, i32, i32, P, P, P, P, sz, P]
+        L.dl_moe_ffn_workspace.restype = sz
+        L.dl_moe_ffn_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.dl_moe_ffn.argtypes = [P, i32, i32, i32, P, P, i32, C.POINTER(Mat), C.POINTER(Mat), C.POINTER(Mat), i32,
+                                 i32, P, P, i32, P, sz, P]
+        L.dl_layer_workspace.restype = sz
+        L.dl_layer_workspace.argtypes = [C.POINTER(LayerDesc), C.POINTER(Pages)]
+        L.dl_layer_step.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), P, sz, P]
+        if L.dl_abi_version() != ABI_VERSION:
+            raise ImportError(f"libdl ABI {L.dl_abi_version()} != {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DLError(rc, _lib.dl_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "tensors must be contiguous"
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    return {torch.float32: DL_F32, torch.bfloat16: DL_BF16, torch.uint8: DL_FP8_E4M3,
+            torch.float8_e4m3fn: DL_FP8_E4M3, torch.int8: DL_I8, torch.int32: DL_I32}[t.dtype]
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte-aligned device buffer (torch's allocator aligns to at least 512 bytes)."""
+    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+def pages(seq_lens: torch.Tensor, page_table: torch.Tensor, page_size: int) -> Pages:
+    return Pages(seq_lens.numel(), page_size, page_table.shape[1], _ptr(seq_lens), _ptr(page_table))
+
+
+def mat(w: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None) -> Mat:
+    if w is None:
+        return Mat(None, None, 0, 0, 0, 0)
+    w3 = w if w.dim() == 3 else w.unsqueeze(0)
+    dt = DL_FP8_E4M3 if w.dtype in (torch.uint8, torch.float8_e4m3fn) else DL_F32
+    return Mat(_ptr(w), _ptr(scale), dt, w3.shape[0], w3.shape[1], w3.shape[2])
+
+
+# ---------------------------------------------------------------- stage calls
+def indexer_topk(pg: Pages, q_idx, k_pool, top_k: int, sel, sel_score=None, ws=None, stream=None):
+    L = load()
+    need = L.dl_indexer_topk_workspace(C.byref(pg))
+    if ws is None:
+        ws = workspace(need, q_idx.device)
+    _check(L.dl_indexer_topk(C.byref(pg), _ptr(q_idx), _ptr(k_pool), q_idx.shape[1], q_idx.shape[2], top_k,
+                             _ptr(sel), _ptr(sel_score), _ptr(ws), ws.numel(), _stream(stream)))
+    return sel
+
+
+def sparse_attn_decode(pg: Pages, q, kv_pool, kv_scale, n_heads, d_c, d_v, sm_scale, sel, top_k, out,
+                       w_uv: Optional[Mat] = None, w_o: Optional[Mat] = None, residual=None, ws=None, stream=None):
+    L = load()
+    puv = C.byref(w_uv) if w_uv is not None else None
+    po = C.byref(w_o) if w_o is not None else None
+    need = L.dl_sparse_attn_workspace(pg.batch, n_heads, d_v, top_k, puv, po)
+    if ws is None:
+        ws = workspace(need, q.device)
+    kv_dt = DL_F32 if kv_pool.dtype == torch.float32 else DL_FP8_E4M3
+    res_dt = _dt(residual) if residual is not None else 0
+    _check(L.dl_sparse_attn_decode(C.byref(pg), _ptr(q), _dt(q), _ptr(kv_pool), _ptr(kv_scale), kv_dt, n_heads, d_c,
+                                   d_v, float(sm_scale), _ptr(sel), top_k, puv, po, _ptr(residual), res_dt, _ptr(out),
+                                   _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_route(h, w_r, bias, top_k, experts, gates, logits=None, ws=None, stream=None):
+    L = load()
+    B, D = h.shape
+    E = w_r.shape[0]
+    if ws is None:
+        ws = workspace(L.dl_moe_route_workspace(B, E), h.device)
+    _check(L.dl_moe_route(_ptr(h), B, D, _ptr(w_r), _ptr(bias), E, top_k, _ptr(experts), _ptr(gates), _ptr(logits),
+                          _ptr(ws), ws.numel(), _stream(stream)))
+    return experts, gates
+
+
+def moe_ffn(h, experts, gates, w_gate: Mat, w_up: Mat, w_down: Mat, n_routed, n_shared, out, residual=None,
+            ws=None, stream=None):
+    L = load()
+    B, D = h.shape
+    ke = experts.shape[1]
+    inter = w_gate.rows
+    if ws is None:
+        ws = workspace(L.dl_moe_ffn_workspace(B, D, inter, ke, n_routed, n_shared), h.device)
+    _check(L.dl_moe_ffn(_ptr(h), B, D, inter, _ptr(experts), _ptr(gates), ke, C.byref(w_gate), C.byref(w_up),
+                        C.byref(w_down), n_routed, n_shared, _ptr(residual), _ptr(out), _dt(out), _ptr(ws), ws.numel(),
+                        _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- whole step
+class LayerStep:
+    """dl_layer_step over one layer instance given as a dict of device tensors (names as synth.make_layer).
+
+    Holds the descriptor, the io struct and the workspace, so repeated calls only enqueue."""
+
+    def __init__(self, spec, t: Dict[str, torch.Tensor], debug: bool = False):
+        L = load()
+        self.spec, self.t = spec, t
+        dev = t["x"].device
+        B = spec.B
+        self.keep = []
+        self.pg = pages(t["seq_lens"], t["page_table"], spec.page_size)
+        d = LayerDesc()
+        d.D, d.n_heads, d.d_c, d.d_v = spec.D, spec.H, spec.Dc, spec.Dv
+        d.idx_heads, d.idx_dim, d.top_k = spec.HI, spec.DI, spec.topk
+        d.n_routed, d.n_shared, d.expert_top_k, d.inter = spec.E, spec.n_shared, spec.ke, spec.I
+        d.sm_scale = spec.scale
+        d.q_dt = _dt(t["x"])
+        d.kv_dt = DL_F32 if t["kv"].dtype == torch.float32 else DL_FP8_E4M3
+        d.out_dt = DL_BF16 if spec.fp8 else DL_F32
+        d.w_uv = mat(t.get("w_uv"), t.get("w_uv_scale"))
+        d.w_o = mat(t["w_o"], t.get("w_o_scale"))
+        d.w_r = _ptr(t["w_r"])
+        d.r_bias = _ptr(t["r_bias"])
+        d.w_gate = mat(t["w_gate"], t.get("w_gate_scale"))
+        d.w_up = mat(t["w_up"], t.get("w_up_scale"))
+        d.w_down = mat(t["w_down"], t.get("w_down_scale"))
+        self.desc = d
+        self.y = torch.empty(B, spec.D, dtype=torch.bfloat16 if spec.fp8 else torch.float32, device=dev)
+        io = LayerIO()
+        io.pages = self.pg
+        io.x, io.q, io.q_idx = _ptr(t["x"]), _ptr(t["q"]), _ptr(t["q_idx"])
+        io.kv_pool, io.kv_scale, io.k_pool = _ptr(t["kv"]), _ptr(t.get("kv_scale")), _ptr(t["k_pool"])
+        io.y = _ptr(self.y)
+        self.dbg = {}
+        if debug:
+            self.dbg = dict(sel=torch.empty(B, spec.topk, dtype=torch.int32, device=dev),
+                            h=torch.empty(B, spec.D, dtype=torch.float32, device=dev),
+                            experts=torch.empty(B, spec.ke, dtype=torch.int32, device=dev),
+                            gates=torch.empty(B, spec.ke, dtype=torch.float32, device=dev),
+                            o=torch.empty(B, spec.H, spec.Dv, dtype=torch.float32, device=dev))
+            for k, v in self.dbg.items():
+                setattr(io, k, _ptr(v))
+        self.io = io
+        self.ws = workspace(L.dl_layer_workspace(C.byref(d), C.byref(self.pg)), dev)
+
+    def __call__(self, stream=None):
+        _check(load().dl_layer_step(C.byref(self.desc), C.byref(self.io), _ptr(self.ws), self.ws.numel(),
+                                    _stream(stream)))
+        return self.y

@@ -1,0 +1,526 @@
+// Host side of the C ABI: argument checks, workspace layout and the launch sequence of each entry
+// point.  Nothing here computes; every step of the path runs in the gfx950 kernels.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dl_common.h"
+#include "dl_internal.h"
+
+namespace dl {
+
+static thread_local char g_err[512] = "";
+
+int fail(int st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+int hip_check(const char *what)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(DL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return DL_OK;
+}
+
+#define DL_TRY(x)              \
+    do {                       \
+        int _r = (x);          \
+        if (_r != DL_OK) return _r; \
+    } while (0)
+
+static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+static int check_pages(const dl_pages *pg)
+{
+    if (!pg) return fail(DL_ERR_NULL, "pages is NULL");
+    if (!pg->seq_lens || !pg->page_table) return fail(DL_ERR_NULL, "seq_lens/page_table NULL");
+    if (pg->batch < 1 || pg->batch > 4096) return fail(DL_ERR_SHAPE, "batch %d", pg->batch);
+    if (!pow2(pg->page_size) || pg->page_size > 1024) return fail(DL_ERR_SHAPE, "page_size %d", pg->page_size);
+    if (pg->max_pages_per_seq < 1) return fail(DL_ERR_SHAPE, "max_pages_per_seq %d", pg->max_pages_per_seq);
+    if ((long)pg->max_pages_per_seq * pg->page_size > (1L << 30)) return fail(DL_ERR_SHAPE, "context too long");
+    return DL_OK;
+}
+
+// FP8 weights need 16-row tiles and 128-column blocks; fp32 weights any shape.
+static int check_mat(const dl_mat *m, const char *name, int count, int rows, int cols)
+{
+    if (!m || !m->w) return fail(DL_ERR_NULL, "%s: weights NULL", name);
+    if (m->count != count || m->rows != rows || m->cols != cols)
+        return fail(DL_ERR_SHAPE, "%s: [%d,%d,%d] expected [%d,%d,%d]", name, m->count, m->rows, m->cols, count, rows,
+                    cols);
+    if (m->dtype == DL_FP8_E4M3) {
+        if (!m->scale) return fail(DL_ERR_NULL, "%s: FP8 needs block scales", name);
+        if (rows % 16 || cols % 128) return fail(DL_ERR_UNSUPPORTED, "%s: FP8 needs rows%%16==0, cols%%128==0", name);
+    } else if (m->dtype == DL_F32) {
+        if (m->scale) return fail(DL_ERR_DTYPE, "%s: fp32 weights take no scale", name);
+    } else {
+        return fail(DL_ERR_DTYPE, "%s: dtype %d", name, m->dtype);
+    }
+    return DL_OK;
+}
+
+static int check_ws(void *ws, size_t have, size_t need)
+{
+    if (need == 0) return DL_OK;
+    if (!ws) return fail(DL_ERR_WORKSPACE, "workspace NULL (%zu bytes needed)", need);
+    if (((uintptr_t)ws) & 255) return fail(DL_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (have < need) return fail(DL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+    return DL_OK;
+}
+
+static int check_indexer(int HI, int DI, int top_k)
+{
+    if (HI < 1 || HI > 64) return fail(DL_ERR_UNSUPPORTED, "indexer heads %d (1..64)", HI);
+    if (DI < 16 || DI > 256 || DI % 16) return fail(DL_ERR_UNSUPPORTED, "indexer dim %d (16..256, %%16)", DI);
+    if ((long)HI * DI > 131071) return fail(DL_ERR_SHAPE, "indexer heads*dim may overflow int32");
+    if (top_k < 1 || top_k > 65536) return fail(DL_ERR_SHAPE, "top_k %d", top_k);
+    return DL_OK;
+}
+
+// ------------------------------------------------------------------ attention + projection
+struct AttnWs {
+    float *o;                  // [B, H, Dv] (when the caller's out is not o)
+    uint8_t *oq; float *oqs;   // 4 parts of o for W_UV
+    float *u;                  // [B, H*hd]
+    uint8_t *uq; float *uqs;   // 4 parts of u for W_O
+};
+static constexpr int PROJ_PARTS = 4;  // projections ahead of the router keep ~16 significant bits
+static constexpr int FFN_PARTS = 2;
+
+static void attn_ws_layout(Ws &w, int B, int H, int Dv, const dl_mat *w_uv, const dl_mat *w_o, AttnWs &a)
+{
+    a = AttnWs{};
+    if (!w_o) return;
+    const long BH = (long)B * H;
+    a.o = w.take<float>(BH * Dv);
+    const int hd = w_uv ? w_uv->rows : Dv;
+    if (w_uv) {
+        if (w_uv->dtype == DL_FP8_E4M3) {
+            a.oq = w.take<uint8_t>(PROJ_PARTS * BH * Dv);
+            a.oqs = w.take<float>(PROJ_PARTS * BH * (Dv / 128));
+        }
+        a.u = w.take<float>(BH * hd);
+    }
+    if (w_o->dtype == DL_FP8_E4M3) {
+        a.uq = w.take<uint8_t>(PROJ_PARTS * BH * hd);
+        a.uqs = w.take<float>(PROJ_PARTS * BH * (hd / 128));
+    }
+}
+
+static GemvArgs mat_args(const dl_mat *m)
+{
+    GemvArgs g;
+    memset(&g, 0, sizeof g);
+    if (m->dtype == DL_FP8_E4M3) {
+        g.w = (const uint8_t *)m->w;
+        g.wsc = m->scale;
+    } else {
+        g.wf = (const float *)m->w;
+    }
+    g.mat_elems = (long)m->rows * m->cols;
+    g.rows = m->rows;
+    g.cols = m->cols;
+    g.nrb = (m->rows + 127) / 128;
+    g.nkb = (m->cols + 127) / 128;
+    return g;
+}
+
+// out = residual + W_O concat_h(W_UV[h] o[b,h]), o fp32 [B, H, Dv].
+static int run_projection(int B, int H, int Dv, const float *o, const dl_mat *w_uv, const dl_mat *w_o,
+                          const void *resid, int resid_dt, float *out, const AttnWs &a, hipStream_t s)
+{
+    const long BH = (long)B * H;
+    const float *act = o;
+    int K = Dv;
+    if (w_uv) {
+        const int hd = w_uv->rows;
+        GemvArgs g = mat_args(w_uv);
+        g.n_active_host = H;
+        g.ntok_host = B;
+        g.max_groups = (B + 15) / 16;
+        g.a_ts = H;
+        g.a_ms = 1;
+        g.o_ts = (long)H * hd;
+        g.o_ms = hd;
+        g.out = a.u;
+        const bool f8 = w_uv->dtype == DL_FP8_E4M3;
+        if (f8) {
+            DL_TRY(launch_quant(o, BH, nullptr, Dv, a.oq, a.oqs, BH * Dv, BH * (Dv / 128), PROJ_PARTS, s));
+            g.aq = a.oq; g.asc = a.oqs; g.aq_part = BH * Dv; g.asc_part = BH * (Dv / 128);
+        } else {
+            g.af = o;
+        }
+        DL_TRY(launch_gemv(g, PROJ_PARTS, EPI_STORE, f8, s));
+        act = a.u;
+        K = H * hd;
+    } else {
+        K = H * Dv;
+    }
+    GemvArgs g = mat_args(w_o);
+    g.n_active_host = 1;
+    g.ntok_host = B;
+    g.max_groups = (B + 15) / 16;
+    g.a_ts = 1;
+    g.a_ms = 0;
+    g.o_ts = w_o->rows;
+    g.o_ms = 0;
+    g.out = out;
+    g.resid = resid;
+    g.resid_dt = resid_dt;
+    g.r_ts = w_o->rows;
+    const bool f8 = w_o->dtype == DL_FP8_E4M3;
+    if (f8) {
+        DL_TRY(launch_quant(act, B, nullptr, K, a.uq, a.uqs, (long)B * K, (long)B * (K / 128), PROJ_PARTS, s));
+        g.aq = a.uq; g.asc = a.uqs; g.aq_part = (long)B * K; g.asc_part = (long)B * (K / 128);
+    } else {
+        g.af = act;
+    }
+    return launch_gemv(g, PROJ_PARTS, resid ? EPI_RESID : EPI_STORE, f8, s);
+}
+
+// ------------------------------------------------------------------ FFN
+struct FfnWs {
+    MoePlan plan;
+    uint8_t *hq; float *hqs;   // 2 parts of h  [2][B][D]
+    float *Z;                  // [P, I]
+    uint8_t *zq; float *zqs;   // 2 parts of Z
+    float *F;                  // [P, D]
+};
+
+static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool fp8, FfnWs &f)
+{
+    const int NE = E + S;
+    const long P = (long)B * (ke + S);
+    f.plan.n_active = w.take<int>(1);
+    f.plan.n_pairs = w.take<int>(1);
+    f.plan.active = w.take<int>(NE);
+    f.plan.tok_off = w.take<int>(NE);
+    f.plan.tok_cnt = w.take<int>(NE);
+    f.plan.pair_tok = w.take<int>(P);
+    f.plan.pair_idx = w.take<int>(P);
+    f.hq = nullptr; f.hqs = nullptr; f.zq = nullptr; f.zqs = nullptr;
+    if (fp8) {
+        f.hq = w.take<uint8_t>((long)FFN_PARTS * B * D);
+        f.hqs = w.take<float>((long)FFN_PARTS * B * (D / 128));
+    }
+    f.Z = w.take<float>(P * I);
+    if (fp8) {
+        f.zq = w.take<uint8_t>((long)FFN_PARTS * P * I);
+        f.zqs = w.take<float>((long)FFN_PARTS * P * (I / 128));
+    }
+    f.F = w.take<float>(P * D);
+}
+
+static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, const float *gates, int ke,
+                   const dl_mat *wg, const dl_mat *wu, const dl_mat *wd, int E, int S, const void *resid,
+                   int resid_dt, void *out, int out_dt, const FfnWs &f, hipStream_t s)
+{
+    const bool f8 = wg->dtype == DL_FP8_E4M3;
+    const int NE = E + S;
+    const long P = (long)B * (ke + S);
+    DL_TRY(launch_plan(experts, B, ke, E, S, f.plan, s));
+    // gate/up + SwiGLU -> Z
+    GemvArgs g = mat_args(wg);
+    g.w2 = (const uint8_t *)(f8 ? wu->w : nullptr);
+    g.wsc2 = f8 ? wu->scale : nullptr;
+    g.wf2 = f8 ? nullptr : (const float *)wu->w;
+    g.active = f.plan.active;
+    g.n_active_dev = f.plan.n_active;
+    g.n_active_host = NE;
+    g.tok_off = f.plan.tok_off;
+    g.tok_cnt = f.plan.tok_cnt;
+    g.max_groups = (B + 15) / 16;
+    g.pair_act = f.plan.pair_tok;
+    g.o_ts = I;
+    g.out = f.Z;
+    if (f8) {
+        DL_TRY(launch_quant(h, B, nullptr, D, f.hq, f.hqs, (long)B * D, (long)B * (D / 128), FFN_PARTS, s));
+        g.aq = f.hq; g.asc = f.hqs; g.aq_part = (long)B * D; g.asc_part = (long)B * (D / 128);
+    } else {
+        g.af = h;
+    }
+    DL_TRY(launch_gemv(g, FFN_PARTS, EPI_SWIGLU, f8, s));
+    // down -> F
+    GemvArgs d = mat_args(wd);
+    d.active = f.plan.active;
+    d.n_active_dev = f.plan.n_active;
+    d.n_active_host = NE;
+    d.tok_off = f.plan.tok_off;
+    d.tok_cnt = f.plan.tok_cnt;
+    d.max_groups = (B + 15) / 16;
+    d.pair_act = nullptr;  // Z rows are per pair
+    d.o_ts = D;
+    d.out = f.F;
+    if (f8) {
+        DL_TRY(launch_quant(f.Z, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I, P * (I / 128), FFN_PARTS, s));
+        d.aq = f.zq; d.asc = f.zqs; d.aq_part = P * I; d.asc_part = P * (I / 128);
+    } else {
+        d.af = f.Z;
+    }
+    DL_TRY(launch_gemv(d, FFN_PARTS, EPI_STORE, f8, s));
+    return launch_combine(f.F, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt, s);
+}
+
+struct LayerWs {
+    TopkWs topk;
+    int32_t *sel;
+    AttnWs attn;
+    float *o, *h;
+    double *logits64;
+    int32_t *experts;
+    float *gates;
+    FfnWs ffn;
+};
+
+static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, const dl_layer_io *io, LayerWs &L)
+{
+    const int B = pg->batch;
+    topk_ws_layout(w, *pg, L.topk);
+    L.sel = (io && io->sel) ? io->sel : w.take<int32_t>((long)B * d->top_k);
+    L.o = (io && io->o) ? io->o : w.take<float>((long)B * d->n_heads * d->d_v);
+    attn_ws_layout(w, B, d->n_heads, d->d_v, d->w_uv.w ? &d->w_uv : nullptr, nullptr, L.attn);  // o handled above
+    const int hd = d->w_uv.w ? d->w_uv.rows : d->d_v;
+    const long BH = (long)B * d->n_heads;
+    L.attn.o = L.o;
+    if (d->w_uv.w) {
+        if (d->w_uv.dtype == DL_FP8_E4M3) {
+            L.attn.oq = w.take<uint8_t>(PROJ_PARTS * BH * d->d_v);
+            L.attn.oqs = w.take<float>(PROJ_PARTS * BH * (d->d_v / 128));
+        }
+        L.attn.u = w.take<float>(BH * hd);
+    }
+    if (d->w_o.dtype == DL_FP8_E4M3) {
+        L.attn.uq = w.take<uint8_t>(PROJ_PARTS * BH * hd);
+        L.attn.uqs = w.take<float>(PROJ_PARTS * BH * (hd / 128));
+    }
+    L.h = (io && io->h) ? io->h : w.take<float>((long)B * d->D);
+    L.logits64 = w.take<double>((long)B * d->n_routed);
+    L.experts = (io && io->experts) ? io->experts : w.take<int32_t>((long)B * d->expert_top_k);
+    L.gates = (io && io->gates) ? io->gates : w.take<float>((long)B * d->expert_top_k);
+    ffn_ws_layout(w, B, d->D, d->inter, d->expert_top_k, d->n_routed, d->n_shared, d->w_gate.dtype == DL_FP8_E4M3,
+                  L.ffn);
+}
+
+static int check_ffn_shapes(int B, int D, int I, int ke, int E, int S, const dl_mat *wg, const dl_mat *wu,
+                            const dl_mat *wd)
+{
+    if (B < 1 || D < 1 || I < 1) return fail(DL_ERR_SHAPE, "ffn B=%d D=%d I=%d", B, D, I);
+    if (ke < 1 || ke > 32 || ke > E) return fail(DL_ERR_SHAPE, "expert top_k %d of %d", ke, E);
+    if (S < 0 || E + S > 4096) return fail(DL_ERR_SHAPE, "experts %d + %d", E, S);
+    if ((long)B * (ke + S) > 16384) return fail(DL_ERR_SHAPE, "B*(top_k+shared) > 16384");
+    if ((long)B * ke > 16384) return fail(DL_ERR_SHAPE, "B*top_k > 16384");
+    DL_TRY(check_mat(wg, "w_gate", E + S, I, D));
+    DL_TRY(check_mat(wu, "w_up", E + S, I, D));
+    DL_TRY(check_mat(wd, "w_down", E + S, D, I));
+    if (wg->dtype != wu->dtype || wg->dtype != wd->dtype) return fail(DL_ERR_DTYPE, "expert weights mix dtypes");
+    return DL_OK;
+}
+
+static int check_attn_shapes(int B, int H, int Dc, int Dv, int top_k, int q_dt, int kv_dt, const float *kv_scale,
+                             bool check_scale = true)
+{
+    if (H < 1 || Dc < 4 || Dv < 4 || Dv > Dc || Dc > 1024) return fail(DL_ERR_SHAPE, "H=%d d_c=%d d_v=%d", H, Dc, Dv);
+    if (top_k < 1 || top_k > 4096) return fail(DL_ERR_UNSUPPORTED, "attention top_k %d (1..4096)", top_k);
+    if (q_dt != DL_BF16 && q_dt != DL_F32) return fail(DL_ERR_DTYPE, "q dtype %d", q_dt);
+    if (kv_dt == DL_FP8_E4M3) {
+        if (check_scale && !kv_scale) return fail(DL_ERR_NULL, "FP8 KV needs scales");
+    } else if (kv_dt == DL_F32) {
+        if (check_scale && kv_scale) return fail(DL_ERR_DTYPE, "fp32 KV takes no scales");
+    } else {
+        return fail(DL_ERR_DTYPE, "kv dtype %d", kv_dt);
+    }
+    (void)B;
+    return DL_OK;
+}
+
+static int check_proj(int H, int Dv, const dl_mat *w_uv, const dl_mat *w_o, int *D_out)
+{
+    int hd = Dv;
+    if (w_uv) {
+        if (!w_uv->w) return fail(DL_ERR_NULL, "w_uv");
+        DL_TRY(check_mat(w_uv, "w_uv", H, w_uv->rows, Dv));
+        hd = w_uv->rows;
+    }
+    if (!w_o || !w_o->w) return fail(DL_ERR_NULL, "w_o");
+    DL_TRY(check_mat(w_o, "w_o", 1, w_o->rows, H * hd));
+    *D_out = w_o->rows;
+    return DL_OK;
+}
+
+}  // namespace dl
+
+using namespace dl;
+
+extern "C" {
+
+int dl_abi_version(void) { return DL_ABI_VERSION; }
+const char *dl_last_error(void) { return g_err; }
+
+size_t dl_indexer_topk_workspace(const dl_pages *pages)
+{
+    if (!pages) return 0;
+    Ws w(nullptr);
+    TopkWs t;
+    topk_ws_layout(w, *pages, t);
+    return w.used();
+}
+
+int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_pool, int32_t n_heads, int32_t dim,
+                    int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    DL_TRY(check_pages(pages));
+    if (!q_idx || !k_pool || !sel) return fail(DL_ERR_NULL, "q_idx/k_pool/sel NULL");
+    DL_TRY(check_indexer(n_heads, dim, top_k));
+    DL_TRY(check_ws(ws, ws_bytes, dl_indexer_topk_workspace(pages)));
+    (void)hipGetLastError();
+    Ws w(ws);
+    TopkWs t;
+    topk_ws_layout(w, *pages, t);
+    return launch_indexer_topk(*pages, q_idx, k_pool, n_heads, dim, top_k, sel, sel_score, t, (hipStream_t)stream);
+}
+
+size_t dl_sparse_attn_workspace(int32_t batch, int32_t n_heads, int32_t d_v, int32_t top_k, const dl_mat *w_uv,
+                                const dl_mat *w_o)
+{
+    (void)top_k;
+    Ws w(nullptr);
+    AttnWs a;
+    attn_ws_layout(w, batch, n_heads, d_v, w_uv, w_o, a);
+    return w.used();
+}
+
+int dl_sparse_attn_decode(const dl_pages *pages, const void *q, int32_t q_dt, const void *kv_pool,
+                          const float *kv_scale, int32_t kv_dt, int32_t n_heads, int32_t d_c, int32_t d_v,
+                          float sm_scale, const int32_t *sel, int32_t top_k, const dl_mat *w_uv, const dl_mat *w_o,
+                          const void *residual, int32_t res_dt, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    DL_TRY(check_pages(pages));
+    if (!q || !kv_pool || !sel || !out) return fail(DL_ERR_NULL, "q/kv_pool/sel/out NULL");
+    DL_TRY(check_attn_shapes(pages->batch, n_heads, d_c, d_v, top_k, q_dt, kv_dt, kv_scale));
+    if (w_uv && !w_o) return fail(DL_ERR_SHAPE, "w_uv given without w_o");
+    int D = 0;
+    if (w_o) {
+        DL_TRY(check_proj(n_heads, d_v, w_uv, w_o, &D));
+        if (!residual) return fail(DL_ERR_NULL, "residual required with w_o");
+        if (res_dt != DL_BF16 && res_dt != DL_F32) return fail(DL_ERR_DTYPE, "residual dtype %d", res_dt);
+    }
+    DL_TRY(check_ws(ws, ws_bytes, dl_sparse_attn_workspace(pages->batch, n_heads, d_v, top_k, w_uv, w_o)));
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    Ws w(ws);
+    AttnWs a;
+    attn_ws_layout(w, pages->batch, n_heads, d_v, w_uv, w_o, a);
+    float *o = w_o ? a.o : out;
+    DL_TRY(launch_attention(*pages, q, q_dt, kv_pool, kv_scale, kv_dt, n_heads, d_c, d_v, sm_scale, sel, top_k, o, s));
+    if (!w_o) return DL_OK;
+    return run_projection(pages->batch, n_heads, d_v, o, w_uv, w_o, residual, res_dt, out, a, s);
+}
+
+size_t dl_moe_route_workspace(int32_t B, int32_t n_experts)
+{
+    Ws w(nullptr);
+    w.take<double>((long)B * n_experts);
+    return w.used();
+}
+
+int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const float *bias, int32_t n_experts,
+                 int32_t top_k, int32_t *experts, float *gates, float *logits, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (!h || !w_r || !experts || !gates) return fail(DL_ERR_NULL, "h/w_r/experts/gates NULL");
+    if (B < 1 || B > 65536 || D < 1) return fail(DL_ERR_SHAPE, "B=%d D=%d", B, D);
+    if (top_k < 1 || top_k > 32 || n_experts < top_k || n_experts > 4096)
+        return fail(DL_ERR_SHAPE, "top_k %d of %d experts", top_k, n_experts);
+    DL_TRY(check_ws(ws, ws_bytes, dl_moe_route_workspace(B, n_experts)));
+    (void)hipGetLastError();
+    Ws w(ws);
+    double *l64 = w.take<double>((long)B * n_experts);
+    return launch_route(h, B, D, w_r, bias, n_experts, top_k, experts, gates, logits, l64, (hipStream_t)stream);
+}
+
+size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared)
+{
+    Ws w(nullptr);
+    FfnWs f;
+    ffn_ws_layout(w, B, D, inter, top_k, n_routed, n_shared, true, f);
+    return w.used();
+}
+
+int dl_moe_ffn(const float *h, int32_t B, int32_t D, int32_t inter, const int32_t *experts, const float *gates,
+               int32_t top_k, const dl_mat *w_gate, const dl_mat *w_up, const dl_mat *w_down, int32_t n_routed,
+               int32_t n_shared, const float *residual, void *out, int32_t out_dt, void *ws, size_t ws_bytes,
+               void *stream)
+{
+    g_err[0] = 0;
+    if (!h || !experts || !gates || !out) return fail(DL_ERR_NULL, "h/experts/gates/out NULL");
+    DL_TRY(check_ffn_shapes(B, D, inter, top_k, n_routed, n_shared, w_gate, w_up, w_down));
+    if (out_dt != DL_F32 && out_dt != DL_BF16) return fail(DL_ERR_DTYPE, "out dtype %d", out_dt);
+    DL_TRY(check_ws(ws, ws_bytes, dl_moe_ffn_workspace(B, D, inter, top_k, n_routed, n_shared)));
+    (void)hipGetLastError();
+    Ws w(ws);
+    FfnWs f;
+    ffn_ws_layout(w, B, D, inter, top_k, n_routed, n_shared, w_gate->dtype == DL_FP8_E4M3, f);
+    return run_ffn(h, B, D, inter, experts, gates, top_k, w_gate, w_up, w_down, n_routed, n_shared, residual, DL_F32,
+                   out, out_dt, f, (hipStream_t)stream);
+}
+
+static int check_layer(const dl_layer_desc *d, const dl_pages *pg)
+{
+    if (!d) return fail(DL_ERR_NULL, "desc NULL");
+    DL_TRY(check_pages(pg));
+    DL_TRY(check_indexer(d->idx_heads, d->idx_dim, d->top_k));
+    DL_TRY(check_attn_shapes(pg->batch, d->n_heads, d->d_c, d->d_v, d->top_k, d->q_dt, d->kv_dt, nullptr, false));
+    int D = 0;
+    DL_TRY(check_proj(d->n_heads, d->d_v, d->w_uv.w ? &d->w_uv : nullptr, &d->w_o, &D));
+    if (D != d->D) return fail(DL_ERR_SHAPE, "w_o rows %d != D %d", D, d->D);
+    if (!d->w_r) return fail(DL_ERR_NULL, "w_r");
+    DL_TRY(check_ffn_shapes(pg->batch, d->D, d->inter, d->expert_top_k, d->n_routed, d->n_shared, &d->w_gate,
+                            &d->w_up, &d->w_down));
+    if (d->out_dt != DL_F32 && d->out_dt != DL_BF16) return fail(DL_ERR_DTYPE, "out dtype %d", d->out_dt);
+    return DL_OK;
+}
+
+size_t dl_layer_workspace(const dl_layer_desc *desc, const dl_pages *pages)
+{
+    if (!desc || !pages) return 0;
+    Ws w(nullptr);
+    LayerWs L;
+    layer_ws_layout(w, desc, pages, nullptr, L);
+    return w.used();
+}
+
+int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (!io) return fail(DL_ERR_NULL, "io NULL");
+    DL_TRY(check_layer(d, &io->pages));
+    if (d->kv_dt == DL_FP8_E4M3 && !io->kv_scale) return fail(DL_ERR_NULL, "FP8 KV needs kv_scale");
+    if (d->kv_dt == DL_F32 && io->kv_scale) return fail(DL_ERR_DTYPE, "fp32 KV takes no kv_scale");
+    if (!io->x || !io->q || !io->q_idx || !io->kv_pool || !io->k_pool || !io->y) return fail(DL_ERR_NULL, "io tensor NULL");
+    DL_TRY(check_ws(ws, ws_bytes, dl_layer_workspace(d, &io->pages)));
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    const dl_pages &pg = io->pages;
+    const int B = pg.batch;
+    Ws w(ws);
+    LayerWs L;
+    layer_ws_layout(w, d, &pg, io, L);
+    DL_TRY(launch_indexer_topk(pg, io->q_idx, io->k_pool, d->idx_heads, d->idx_dim, d->top_k, L.sel, nullptr, L.topk, s));
+    DL_TRY(launch_attention(pg, io->q, d->q_dt, io->kv_pool, io->kv_scale, d->kv_dt, d->n_heads, d->d_c, d->d_v,
+                            d->sm_scale, L.sel, d->top_k, L.o, s));
+    DL_TRY(run_projection(B, d->n_heads, d->d_v, L.o, d->w_uv.w ? &d->w_uv : nullptr, &d->w_o, io->x, d->q_dt, L.h,
+                          L.attn, s));
+    DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates, nullptr,
+                        L.logits64, s));
+    return run_ffn(L.h, B, d->D, d->inter, L.experts, L.gates, d->expert_top_k, &d->w_gate, &d->w_up, &d->w_down,
+                   d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s);
+}
+
+}  // extern "C"

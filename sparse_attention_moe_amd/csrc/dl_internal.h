@@ -1,0 +1,106 @@
+// Host-side internals shared by the launch code of the decode layer step.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/dl.h"
+
+namespace dl {
+
+// Sets the thread's last-error message and returns `st`.
+int fail(int st, const char *fmt, ...);
+int hip_check(const char *what);  // DL_OK or DL_ERR_HIP after a launch
+
+// Carves 256-byte-aligned regions out of a workspace.  With base == nullptr it only measures.
+struct Ws {
+    char *base;
+    size_t off = 0;
+    explicit Ws(void *b) : base((char *)b) {}
+    template <class T>
+    T *take(size_t n)
+    {
+        off = (off + 255) & ~(size_t)255;
+        T *p = base ? (T *)(base + off) : nullptr;
+        off += n * sizeof(T);
+        return p;
+    }
+    size_t used() const { return (off + 255) & ~(size_t)255; }
+};
+
+// ------------------------------------------------------------- indexer + top-k
+struct SelState {      // per row, in the workspace
+    int lo, hi;        // the threshold score T lies in [lo, hi]
+    int above;         // number of scores > hi
+    int done;          // 1: T == lo == hi is final
+    int need;          // how many scores == T are kept (lowest positions first)
+    int n_sel;         // min(top_k, L)
+    int pad0, pad1;
+};
+
+struct TopkWs {
+    int32_t *scores;   // [B, Lmax]
+    unsigned *hist1;   // [B, NB1]
+    unsigned *hist2;   // [B, NB2]
+    int *ticket;       // [B]
+    SelState *state;   // [B]
+    int *cnt;          // [B, nchunk, 2]
+};
+void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t);
+int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k_pool, int HI, int DI, int top_k,
+                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s);
+
+// ------------------------------------------------------------- GEMV engine
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+struct GemvArgs {
+    // weights: FP8 codes + block scales, or fp32 (wf)
+    const uint8_t *w;  const float *wsc;  const float *wf;
+    const uint8_t *w2; const float *wsc2; const float *wf2;   // second matrix of SwiGLU (up)
+    long mat_elems;
+    int rows, cols, nrb, nkb;
+    // which matrices and which tokens
+    const int *active;       // matrix id of active slot u (nullptr: u itself)
+    const int *n_active_dev; // device count of active slots (nullptr: n_active_host)
+    int n_active_host;
+    const int *tok_off, *tok_cnt;  // plan mode: pairs of slot u are [tok_off[u], +tok_cnt[u])
+    int ntok_host;                 // uniform mode: tokens 0..ntok-1 for every matrix
+    int max_groups;                // upper bound of ceil(tokens per matrix / 16)
+    const int *pair_act;           // plan mode: activation row of global pair p
+    int a_ts, a_ms;                // uniform mode: activation row = t*a_ts + m*a_ms
+    long o_ts, o_ms;               // output offset = t*o_ts + m*o_ms (uniform) or p*o_ts (plan)
+    // activations: NS FP8 parts [part][row][cols] + scales [part][row][nkb], or fp32 [row][cols]
+    const uint8_t *aq; const float *asc;
+    long aq_part, asc_part;
+    const float *af;
+    // output
+    float *out;
+    const void *resid; int resid_dt; long r_ts;    // EPI_RESID: resid[t*r_ts + row]
+};
+int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
+
+// x fp32 rows -> NS FP8 parts with one dynamic scale per (part, row, 128 block).
+int launch_quant(const float *x, long rows_host, const int *rows_dev, int cols, uint8_t *q, float *sc,
+                 long q_part, long sc_part, int ns, hipStream_t s);
+
+// ------------------------------------------------------------- attention
+int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
+                     int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, hipStream_t s);
+
+// ------------------------------------------------------------- MoE
+struct MoePlan {
+    int *n_active;   // [1]
+    int *n_pairs;    // [1]
+    int *active;     // [NE]
+    int *tok_off;    // [NE]
+    int *tok_cnt;    // [NE]
+    int *pair_tok;   // [B*(ke+S)]
+    int *pair_idx;   // [B, ke+S]
+};
+int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
+                 float *gates, float *logits, double *logits64, hipStream_t s);
+int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s);
+int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
+                   const void *resid, int resid_dt, void *out, int out_dt, hipStream_t s);
+
+}  // namespace dl

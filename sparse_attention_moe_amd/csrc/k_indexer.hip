@@ -1,0 +1,450 @@
+// S1 + S2: int8 indexer scoring on the matrix cores and an exact radix top-k.
+//
+// Scoring ("What moved the number from 19.4 to 122.9 tokens a second?", Introducing Kiln: dedicated
+// scoring and top-k kernels over a separate key cache).  score[p] = sum_h relu(q_h . k_p), exact
+// int32.  The indexer heads form the M side (16 rows) of v_mfma_i32_16x16x64_i8 and 16 cached
+// positions the N side, so one instruction scores 16 positions for 16 heads over 64 key bytes.
+// Every key byte is read once with 16-byte loads; a wave covers 64 positions (one 8 KB page at
+// the 64-token, 128-byte layout) per step.
+//
+// Selection (trnrt summary, "The interesting bit": the top 2,048 positions are kept; ties go to
+// the lower position).  Radix select on the exact integer scores:
+//   pass 1 (fused into scoring): a log-linear histogram (exact below 256, then 128 bins per
+//            binade) locates the bin holding the k-th largest score;
+//   refine:  4,096-bin histograms of the scores inside [lo, hi] narrow the range until lo == hi;
+//   count:   per 4,096-position chunk, how many scores are > T and == T;
+//   write:   an ordered compaction: a position is kept if its score is > T, or == T and fewer than
+//            `need` equal scores precede it; its output slot is the number of kept positions
+//            before it, so the list comes out in ascending position order.
+// The last workgroup of a row (atomic ticket after a device-scope fence) turns each histogram into
+// the next range; no workgroup ever waits on another.
+#include "dl_common.h"
+#include "dl_internal.h"
+
+namespace dl {
+
+static constexpr int NB1 = 256 + 23 * 128;  // log-linear bins covering 0 .. 2^31-1
+static constexpr int NB2 = 4096;
+static constexpr int SCORE_POS_PER_BLOCK = 1024;  // 4 waves x 4 steps x 64 positions
+static constexpr int SEL_CHUNK = 4096;            // 256 threads x 16 positions
+
+__device__ __forceinline__ int bin1_of(int s)
+{
+    if (s < 256) return s;
+    int n = 31 - __clz(s);  // 8 .. 30
+    return 256 + (n - 8) * 128 + ((s >> (n - 7)) & 127);
+}
+__device__ __forceinline__ void bin1_range(int b, int &lo, int &hi)
+{
+    if (b < 256) { lo = hi = b; return; }
+    int n = 8 + (b - 256) / 128, m = (b - 256) % 128;
+    lo = (128 + m) << (n - 7);
+    hi = lo + (1 << (n - 7)) - 1;
+}
+
+// Largest bin b with (count of bins >= b) >= k, and the count strictly above it.
+// Called by all 256 threads of the deciding workgroup; reads the histogram coherently.
+__device__ void block_pick(const unsigned *hist, int nbins, int k, int *s_tmp, int &bin_out, int &above_out)
+{
+    const int tid = threadIdx.x;
+    const int per = (nbins + 255) / 256;
+    // thread t owns bins [t*per, (t+1)*per); suffix sums from the top
+    int seg = 0;
+    for (int i = 0; i < per; i++) {
+        int b = tid * per + i;
+        if (b < nbins) seg += (int)ld_agent_u(hist + b);
+    }
+    s_tmp[tid] = seg;
+    __syncthreads();
+    if (tid == 0) {
+        int cum = 0, t = 255;
+        for (; t >= 0; t--) {
+            if (cum + s_tmp[t] >= k) break;
+            cum += s_tmp[t];
+        }
+        int bin = 0, above = cum;
+        if (t >= 0) {
+            for (int b = min(nbins, (t + 1) * per) - 1; b >= t * per; b--) {
+                int h = (int)ld_agent_u(hist + b);
+                if (cum + h >= k) { bin = b; above = cum; break; }
+                cum += h;
+            }
+        }
+        s_tmp[256] = bin;
+        s_tmp[257] = above;
+    }
+    __syncthreads();
+    bin_out = s_tmp[256];
+    above_out = s_tmp[257];
+    __syncthreads();
+}
+
+// Last-workgroup election for row b: every thread fences its global atomics first.
+__device__ __forceinline__ bool last_block(int *ticket, int nblk, int *s_flag)
+{
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = atomicAdd(ticket, 1);
+        *s_flag = (t == nblk - 1);
+    }
+    __syncthreads();
+    bool last = *s_flag != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+// Per-row initial selection state; clears the pass-1 histogram and tickets.
+__global__ void k_sel_init(const int32_t *seq_lens, int B, int top_k, unsigned *hist1, unsigned *hist2, int *ticket,
+                           SelState *st)
+{
+    const int b = blockIdx.x;
+    for (int i = threadIdx.x; i < NB1; i += blockDim.x) hist1[(long)b * NB1 + i] = 0;
+    for (int i = threadIdx.x; i < NB2; i += blockDim.x) hist2[(long)b * NB2 + i] = 0;
+    if (threadIdx.x == 0) {
+        int L = seq_lens[b];
+        SelState s;
+        s.n_sel = min(L, top_k);
+        if (L <= top_k) {  // keep everything: every score (>= 0) is above T = -1
+            s.lo = s.hi = -1; s.above = L; s.done = 1; s.need = 0;
+        } else {
+            s.lo = 0; s.hi = 0x7FFFFFFF; s.above = 0; s.done = 0; s.need = 0;
+        }
+        s.pad0 = s.pad1 = 0;
+        st[b] = s;
+        ticket[b] = 0;
+    }
+}
+
+// Scores of 1,024 positions per workgroup.  NHG groups of 16 indexer heads, KCH chunks of 64 key bytes.
+template <int NHG, int KCH>
+__global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ q_idx, const int8_t *__restrict__ k_pool,
+                                                     const int32_t *__restrict__ page_table,
+                                                     const int32_t *__restrict__ seq_lens, int max_pages, int ps_shift,
+                                                     int HI, int DI, int top_k, int32_t *__restrict__ scores,
+                                                     long Lmax, unsigned *__restrict__ hist1, int *__restrict__ ticket,
+                                                     SelState *__restrict__ st)
+{
+    __shared__ unsigned s_hist[NB1];
+    __shared__ int s_tmp[260];
+    const int b = blockIdx.y;
+    const int L = seq_lens[b];
+    const long blk0 = (long)blockIdx.x * SCORE_POS_PER_BLOCK;
+    if (blk0 >= L) return;
+    const int nblk = (L + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, lg = lane >> 4;
+    for (int i = tid; i < NB1; i += 256) s_hist[i] = 0;
+
+    // A operand: q rows (indexer heads) for this lane: head hg*16+ln, bytes kc*64 + lg*16 .. +16
+    v4i A[NHG][KCH];
+#pragma unroll
+    for (int hg = 0; hg < NHG; hg++)
+#pragma unroll
+        for (int kc = 0; kc < KCH; kc++) {
+            int h = hg * 16 + ln, d = kc * 64 + lg * 16;
+            A[hg][kc] = (h < HI && d < DI) ? ldg16(q_idx + ((long)b * HI + h) * DI + d) : v4i{0, 0, 0, 0};
+        }
+    const int32_t *pt = page_table + (long)b * max_pages;
+    const int ps_mask = (1 << ps_shift) - 1;
+    __syncthreads();
+
+    for (int step = 0; step < 4; step++) {
+        const long g0 = blk0 + (long)(step * 4 + wave) * 64;  // this wave's 64 positions
+        if (g0 >= L) break;
+        v4i Bk[4][KCH];
+#pragma unroll
+        for (int sg = 0; sg < 4; sg++) {
+            long pos = g0 + sg * 16 + ln;
+            bool ok = pos < L;
+            long row = ok ? ((long)pt[pos >> ps_shift] << ps_shift) + (pos & ps_mask) : 0;
+#pragma unroll
+            for (int kc = 0; kc < KCH; kc++) {
+                int d = kc * 64 + lg * 16;
+                Bk[sg][kc] = (ok && d < DI) ? ldg16(k_pool + row * DI + d) : v4i{0, 0, 0, 0};
+            }
+        }
+        int mine = 0;
+#pragma unroll
+        for (int sg = 0; sg < 4; sg++) {
+            int part = 0;
+#pragma unroll
+            for (int hg = 0; hg < NHG; hg++) {
+                v4i acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int kc = 0; kc < KCH; kc++)
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[hg][kc], Bk[sg][kc], acc, 0, 0, 0);
+                // lane holds heads hg*16 + 4*lg + i of position sg*16 + ln
+                part += max(acc[0], 0) + max(acc[1], 0) + max(acc[2], 0) + max(acc[3], 0);
+            }
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (lg == sg) mine = part;
+        }
+        long pos = g0 + lane;
+        if (pos < L) {
+            scores[(long)b * Lmax + pos] = mine;
+            atomicAdd(&s_hist[bin1_of(mine)], 1u);
+        }
+    }
+    __syncthreads();
+    unsigned *gh = hist1 + (long)b * NB1;
+    for (int i = tid; i < NB1; i += 256) {
+        unsigned v = s_hist[i];
+        if (v) atomicAdd(gh + i, v);
+    }
+    if (!last_block(ticket + b, nblk, &s_tmp[258])) return;
+    if (st[b].done) {  // keep-all row: nothing to pick
+        if (tid == 0) ticket[b] = 0;
+        return;
+    }
+    int bin, above;
+    block_pick(gh, NB1, top_k, s_tmp, bin, above);
+    if (tid == 0) {
+        int lo, hi;
+        bin1_range(bin, lo, hi);
+        SelState s = st[b];
+        s.lo = lo; s.hi = hi; s.above = above;
+        if (lo == hi) { s.done = 1; s.need = top_k - above; }
+        st[b] = s;
+        ticket[b] = 0;
+    }
+}
+
+// One refinement pass: 4,096-bin histogram of the scores inside [lo, hi].
+__global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ scores, long Lmax,
+                                                    const int32_t *__restrict__ seq_lens, int top_k,
+                                                    unsigned *__restrict__ hist2, int *__restrict__ ticket,
+                                                    SelState *__restrict__ st)
+{
+    __shared__ unsigned s_hist[NB2];
+    __shared__ int s_tmp[260];
+    const int b = blockIdx.y;
+    const int L = seq_lens[b];
+    const long c0 = (long)blockIdx.x * SEL_CHUNK;
+    if (c0 >= L) return;
+    SelState s0 = st[b];
+    if (s0.done) return;
+    const int nblk = (L + SEL_CHUNK - 1) / SEL_CHUNK;
+    const int tid = threadIdx.x;
+    const unsigned lo = (unsigned)s0.lo, hi = (unsigned)s0.hi;
+    const unsigned width = hi - lo;  // >= 1
+    const int shift = max(0, (32 - __clz(width)) - 12);
+    for (int i = tid; i < NB2; i += 256) s_hist[i] = 0;
+    __syncthreads();
+    const int32_t *sc = scores + (long)b * Lmax;
+    for (int i = 0; i < SEL_CHUNK / 256; i++) {
+        long p = c0 + (long)i * 256 + tid;
+        if (p < L) {
+            unsigned v = (unsigned)sc[p];
+            if (v >= lo && v <= hi) atomicAdd(&s_hist[(v - lo) >> shift], 1u);
+        }
+    }
+    __syncthreads();
+    unsigned *gh = hist2 + (long)b * NB2;
+    for (int i = tid; i < NB2; i += 256) {
+        unsigned v = s_hist[i];
+        if (v) atomicAdd(gh + i, v);
+    }
+    if (!last_block(ticket + b, nblk, &s_tmp[258])) return;
+    int bin, above;
+    block_pick(gh, NB2, top_k - s0.above, s_tmp, bin, above);
+    for (int i = tid; i < NB2; i += 256) gh[i] = 0;  // ready for the next pass
+    if (tid == 0) {
+        SelState s = s0;
+        unsigned nlo = lo + ((unsigned)bin << shift);
+        unsigned nhi = min(hi, nlo + ((1u << shift) - 1u));
+        s.lo = (int)nlo; s.hi = (int)nhi; s.above = s0.above + above;
+        if (nlo == nhi) { s.done = 1; s.need = top_k - s.above; }
+        st[b] = s;
+        ticket[b] = 0;
+    }
+}
+
+__device__ __forceinline__ void load16(const int32_t *sc, long p0, int L, int v[16])
+{
+    if (p0 + 16 <= L) {
+        const v4i *q = (const v4i *)(sc + p0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v4i t = q[i];
+            v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = (p0 + i < L) ? sc[p0 + i] : INT32_MIN;
+    }
+}
+
+// Per chunk: how many scores are > T and == T.
+__global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ scores, long Lmax,
+                                                   const int32_t *__restrict__ seq_lens, const SelState *__restrict__ st,
+                                                   int nchunk, int *__restrict__ cnt)
+{
+    __shared__ int s_red[2][4];
+    const int b = blockIdx.y;
+    const int L = seq_lens[b];
+    const long c0 = (long)blockIdx.x * SEL_CHUNK;
+    if (c0 >= L) return;
+    const int T = st[b].lo;
+    const int tid = threadIdx.x;
+    int v[16];
+    load16(scores + (long)b * Lmax, c0 + (long)tid * 16, L, v);
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        gt += v[i] > T;
+        eq += v[i] == T;
+    }
+    gt = wave_sum_i(gt);
+    eq = wave_sum_i(eq);
+    if ((tid & 63) == 0) { s_red[0][tid >> 6] = gt; s_red[1][tid >> 6] = eq; }
+    __syncthreads();
+    if (tid == 0) {
+        long o = ((long)b * nchunk + blockIdx.x) * 2;
+        cnt[o] = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+        cnt[o + 1] = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+    }
+}
+
+// Inclusive scan of one int across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Ordered compaction of the kept positions of one chunk.
+__global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ scores, long Lmax,
+                                                   const int32_t *__restrict__ seq_lens, const SelState *__restrict__ st,
+                                                   int nchunk, const int *__restrict__ cnt, int top_k,
+                                                   int32_t *__restrict__ sel, int32_t *__restrict__ sel_score)
+{
+    __shared__ int s_w[2][4];
+    __shared__ int s_base[2];
+    const int b = blockIdx.y;
+    const int L = seq_lens[b];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const SelState s = st[b];
+    int32_t *so = sel + (long)b * top_k;
+    int32_t *ss = sel_score ? sel_score + (long)b * top_k : nullptr;
+    if (blockIdx.x == 0)  // padding of the unused slots
+        for (int i = s.n_sel + tid; i < top_k; i += 256) {
+            so[i] = -1;
+            if (ss) ss[i] = 0;
+        }
+    const long c0 = (long)blockIdx.x * SEL_CHUNK;
+    if (c0 >= L) return;
+    const int T = s.lo, need = s.need;
+    // counts of all earlier chunks of this row
+    int pg = 0, pe = 0;
+    for (int c = tid; c < (int)blockIdx.x; c += 256) {
+        pg += cnt[((long)b * nchunk + c) * 2];
+        pe += cnt[((long)b * nchunk + c) * 2 + 1];
+    }
+    pg = wave_sum_i(pg);
+    pe = wave_sum_i(pe);
+    if (lane == 0) { s_w[0][wave] = pg; s_w[1][wave] = pe; }
+    __syncthreads();
+    if (tid == 0) {
+        s_base[0] = s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
+        s_base[1] = s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
+    }
+    __syncthreads();
+    const int base_g = s_base[0], base_e = s_base[1];
+    const long p0 = c0 + (long)tid * 16;
+    int v[16];
+    load16(scores + (long)b * Lmax, p0, L, v);
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        gt += v[i] > T;
+        eq += v[i] == T;
+    }
+    // exclusive scan of (gt, eq) over the 256 threads
+    int ig = wave_incl_scan(gt), ie = wave_incl_scan(eq);
+    __syncthreads();
+    if (lane == 63) { s_w[0][wave] = ig; s_w[1][wave] = ie; }
+    __syncthreads();
+    int wg = 0, we = 0;
+    for (int w = 0; w < wave; w++) { wg += s_w[0][w]; we += s_w[1][w]; }
+    int g = base_g + wg + ig - gt;  // kept-above scores before my first position
+    int e = base_e + we + ie - eq;  // equal scores before my first position
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        int sv = v[i];
+        if (sv > T) {
+            int slot = g + min(e, need);
+            so[slot] = (int32_t)(p0 + i);
+            if (ss) ss[slot] = sv;
+            g++;
+        } else if (sv == T) {
+            if (e < need) {
+                int slot = g + e;
+                so[slot] = (int32_t)(p0 + i);
+                if (ss) ss[slot] = sv;
+            }
+            e++;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host side
+static int max_len(const dl_pages &pg) { return pg.max_pages_per_seq * pg.page_size; }
+
+void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t)
+{
+    const long B = pg.batch, Lmax = max_len(pg);
+    const long nchunk = (Lmax + SEL_CHUNK - 1) / SEL_CHUNK;
+    t.scores = w.take<int32_t>(B * Lmax);
+    t.hist1 = w.take<unsigned>(B * NB1);
+    t.hist2 = w.take<unsigned>(B * NB2);
+    t.ticket = w.take<int>(B);
+    t.state = w.take<SelState>(B);
+    t.cnt = w.take<int>(B * nchunk * 2);
+}
+
+template <int NHG, int KCH>
+static void launch_score(dim3 g, hipStream_t s, const int8_t *q, const int8_t *kp, const dl_pages &pg, int ps_shift,
+                         int HI, int DI, int k, const TopkWs &t, long Lmax)
+{
+    hipLaunchKernelGGL((k_index_score<NHG, KCH>), g, dim3(256), 0, s, q, kp, pg.page_table, pg.seq_lens,
+                       pg.max_pages_per_seq, ps_shift, HI, DI, k, t.scores, Lmax, t.hist1, t.ticket, t.state);
+}
+
+int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k_pool, int HI, int DI, int top_k,
+                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s)
+{
+    const int B = pg.batch;
+    const long Lmax = max_len(pg);
+    const int ps_shift = __builtin_ctz((unsigned)pg.page_size);
+    const int nchunk = (int)((Lmax + SEL_CHUNK - 1) / SEL_CHUNK);
+    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, pg.seq_lens, B, top_k, t.hist1, t.hist2, t.ticket,
+                       t.state);
+    dim3 gs((unsigned)((Lmax + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK), B);
+    const int nhg = (HI + 15) / 16, kch = (DI + 63) / 64;
+#define DL_SCORE_CASE(H_, K_) \
+    if (nhg == H_ && kch == K_) launch_score<H_, K_>(gs, s, q_idx, k_pool, pg, ps_shift, HI, DI, top_k, t, Lmax); else
+    DL_SCORE_CASE(1, 1) DL_SCORE_CASE(1, 2) DL_SCORE_CASE(1, 3) DL_SCORE_CASE(1, 4)
+    DL_SCORE_CASE(2, 1) DL_SCORE_CASE(2, 2) DL_SCORE_CASE(2, 3) DL_SCORE_CASE(2, 4)
+    DL_SCORE_CASE(3, 1) DL_SCORE_CASE(3, 2) DL_SCORE_CASE(3, 3) DL_SCORE_CASE(3, 4)
+    DL_SCORE_CASE(4, 1) DL_SCORE_CASE(4, 2) DL_SCORE_CASE(4, 3) DL_SCORE_CASE(4, 4)
+    return fail(DL_ERR_UNSUPPORTED, "indexer shape heads=%d dim=%d", HI, DI);
+#undef DL_SCORE_CASE
+    dim3 gc(nchunk, B);
+    // 31-bit scores: pass 1 leaves a range of at most 2^23 values; each refinement takes 12 bits.
+    for (int r = 0; r < 2; r++)
+        hipLaunchKernelGGL(k_sel_refine, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, top_k, t.hist2, t.ticket,
+                           t.state);
+    hipLaunchKernelGGL(k_sel_count, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, t.state, nchunk, t.cnt);
+    hipLaunchKernelGGL(k_sel_write, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, t.state, nchunk, t.cnt, top_k,
+                       sel, sel_score);
+    return hip_check("indexer_topk");
+}
+
+}  // namespace dl

@@ -1,0 +1,219 @@
+// S6 + S7 + combine: router, dispatch plan and the fixed-order sum of expert outputs.
+//
+// The model routes every token to 8 experts plus a shared one (Introducing Kiln, "How was Kiln
+// measured against vLLM on H200?"); its expert kernel applies each expert once to all of its tokens
+// ("A collective costs per graph, so the graphs got big") from a routing plan, and experts without
+// tokens are skipped ("What moved the number ...").  Router logits accumulate fp32 products in fp64
+// so the expert choice matches an exact evaluation except for genuinely near-equal logits.
+#include "dl_common.h"
+#include "dl_internal.h"
+
+namespace dl {
+
+static constexpr int ROUTE_TOK = 16;
+
+// logits64[b, e] = w_r[e] . h[b] + bias[e]: one wave per expert, 16 tokens per workgroup column.
+__global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ h, int B, int D,
+                                                      const float *__restrict__ wr, const float *__restrict__ bias,
+                                                      int E, double *__restrict__ logits64, float *__restrict__ logits)
+{
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int b0 = blockIdx.y * ROUTE_TOK;
+    if (e >= E) return;
+    const int nt = min(ROUTE_TOK, B - b0);
+    double acc[ROUTE_TOK];
+#pragma unroll
+    for (int t = 0; t < ROUTE_TOK; t++) acc[t] = 0.0;
+    const float *w = wr + (long)e * D;
+    for (int d = lane; d < D; d += 64) {
+        const double wv = (double)w[d];
+#pragma unroll
+        for (int t = 0; t < ROUTE_TOK; t++)
+            if (t < nt) acc[t] = fma(wv, (double)h[(long)(b0 + t) * D + d], acc[t]);
+    }
+    const double bv = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int t = 0; t < ROUTE_TOK; t++) {
+        if (t >= nt) break;
+        const double v = wave_sum_d(acc[t]) + bv;
+        if (lane == 0) {
+            logits64[(long)(b0 + t) * E + e] = v;
+            if (logits) logits[(long)(b0 + t) * E + e] = (float)v;
+        }
+    }
+}
+
+// Top-k experts per token by (logit desc, id asc) and their softmax gates; one wave per token.
+__global__ __launch_bounds__(256) void k_route_topk(const double *__restrict__ logits64, int B, int E, int ke,
+                                                    int32_t *__restrict__ experts, float *__restrict__ gates)
+{
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (b >= B) return;
+    const double *l = logits64 + (long)b * E;
+    // taken[] as a bitmask over this lane's experts e = lane + 64*i
+    unsigned long long taken = 0;
+    double sel_l[32];
+    int sel_e[32];
+    for (int j = 0; j < ke; j++) {
+        double best = -INFINITY;
+        int be = 0x7FFFFFFF;
+        for (int i = 0, e = lane; e < E; i++, e += 64) {
+            if ((taken >> i) & 1ull) continue;
+            const double v = l[e];
+            if (v > best || (v == best && e < be)) { best = v; be = e; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const double ov = __shfl_xor(best, o, 64);
+            const int oe = __shfl_xor(be, o, 64);
+            if (ov > best || (ov == best && oe < be)) { best = ov; be = oe; }
+        }
+        if ((be & 63) == lane) taken |= 1ull << (be >> 6);
+        sel_l[j] = best;
+        sel_e[j] = be;
+    }
+    if (lane == 0) {
+        double z = 0.0;
+        for (int j = 0; j < ke; j++) z += exp(sel_l[j] - sel_l[0]);
+        for (int j = 0; j < ke; j++) {
+            experts[(long)b * ke + j] = sel_e[j];
+            gates[(long)b * ke + j] = (float)(exp(sel_l[j] - sel_l[0]) / z);
+        }
+    }
+}
+
+// Dispatch plan in one workgroup: active experts in ascending id (shared experts last), each
+// expert's tokens in ascending order, and the pair index of every (token, slot).
+__global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ experts, int B, int ke, int E, int S,
+                                               int *__restrict__ n_active, int *__restrict__ n_pairs,
+                                               int *__restrict__ active, int *__restrict__ tok_off,
+                                               int *__restrict__ tok_cnt, int *__restrict__ pair_tok,
+                                               int *__restrict__ pair_idx)
+{
+    __shared__ int s_cnt[4096];
+    __shared__ int s_scan[1024];
+    __shared__ int s_exp[16384];
+    const int tid = threadIdx.x;
+    const int nT = 1024;
+    const int per = (E + nT - 1) / nT;
+    const int kk = ke + S;
+    // tokens per routed expert
+    for (int e = tid; e < E; e += nT) s_cnt[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < B * ke; i += nT) {
+        const int e = experts[i];
+        s_exp[i] = e;
+        atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    // thread t owns experts [t*per, (t+1)*per): count its active experts and pairs
+    int na = 0, np = 0;
+    for (int i = 0; i < per; i++) {
+        const int e = tid * per + i;
+        if (e < E && s_cnt[e] > 0) { na++; np += s_cnt[e]; }
+    }
+    // exclusive scans of the active-expert and pair counts
+    s_scan[tid] = na;
+    __syncthreads();
+    for (int o = 1; o < nT; o <<= 1) {
+        const int v = tid >= o ? s_scan[tid - o] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    const int a0 = s_scan[tid] - na;
+    const int na_tot = s_scan[nT - 1];
+    __syncthreads();
+    s_scan[tid] = np;
+    __syncthreads();
+    for (int o = 1; o < nT; o <<= 1) {
+        const int v = tid >= o ? s_scan[tid - o] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    int p0 = s_scan[tid] - np;
+    int a = a0;
+    for (int i = 0; i < per; i++) {
+        const int e = tid * per + i;
+        if (e >= E || s_cnt[e] == 0) continue;
+        active[a] = e;
+        tok_off[a] = p0;
+        tok_cnt[a] = s_cnt[e];
+        int p = p0;
+        for (int b = 0; b < B; b++)
+            for (int j = 0; j < ke; j++)
+                if (s_exp[b * ke + j] == e) {
+                    pair_tok[p] = b;
+                    pair_idx[(long)b * kk + j] = p;
+                    p++;
+                }
+        p0 = p;
+        a++;
+    }
+    // shared experts: every token, after all routed pairs
+    const int routed_pairs = B * ke;
+    for (int i = tid; i < S * B; i += nT) {
+        const int s = i / B, b = i % B;
+        const int p = routed_pairs + s * B + b;
+        pair_tok[p] = b;
+        pair_idx[(long)b * kk + ke + s] = p;
+    }
+    if (tid < S) {
+        active[na_tot + tid] = E + tid;
+        tok_off[na_tot + tid] = routed_pairs + tid * B;
+        tok_cnt[na_tot + tid] = B;
+    }
+    if (tid == 0) {
+        *n_active = na_tot + S;
+        *n_pairs = routed_pairs + S * B;
+    }
+}
+
+// out[b, d] = resid[b, d] + sum_j gate[b, j] f_j[d] + sum_s f_s[d], in that order.
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, const int *__restrict__ pair_idx,
+                                                 const float *__restrict__ gates, int B, int D, int ke, int S,
+                                                 const void *__restrict__ resid, int resid_dt, void *__restrict__ out,
+                                                 int out_dt)
+{
+    const int b = blockIdx.y;
+    const int d = blockIdx.x * 256 + threadIdx.x;
+    if (d >= D) return;
+    const int kk = ke + S;
+    float acc = resid ? act_load(resid, resid_dt, (long)b * D + d) : 0.f;
+    for (int j = 0; j < ke; j++) {
+        const int p = pair_idx[(long)b * kk + j];
+        acc = fmaf(gates[(long)b * ke + j], F[(long)p * D + d], acc);
+    }
+    for (int s = 0; s < S; s++) acc += F[(long)pair_idx[(long)b * kk + ke + s] * D + d];
+    if (out_dt == DL_BF16) ((uint16_t *)out)[(long)b * D + d] = f32_to_bf16(acc);
+    else ((float *)out)[(long)b * D + d] = acc;
+}
+
+int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
+                 float *gates, float *logits, double *logits64, hipStream_t s)
+{
+    dim3 g((E + 3) / 4, (B + ROUTE_TOK - 1) / ROUTE_TOK);
+    hipLaunchKernelGGL(k_route_logits, g, dim3(256), 0, s, h, B, D, w_r, bias, E, logits64, logits);
+    hipLaunchKernelGGL(k_route_topk, dim3((B + 3) / 4), dim3(256), 0, s, logits64, B, E, ke, experts, gates);
+    return hip_check("route");
+}
+
+int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, experts, B, ke, E, S, p.n_active, p.n_pairs, p.active,
+                       p.tok_off, p.tok_cnt, p.pair_tok, p.pair_idx);
+    return hip_check("plan");
+}
+
+int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
+                   const void *resid, int resid_dt, void *out, int out_dt, hipStream_t s)
+{
+    dim3 g((D + 255) / 256, B);
+    hipLaunchKernelGGL(k_combine, g, dim3(256), 0, s, F, p.pair_idx, gates, B, D, ke, S, resid, resid_dt, out, out_dt);
+    return hip_check("combine");
+}
+
+}  // namespace dl

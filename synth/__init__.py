@@ -238,10 +238,13 @@ def make_layer(spec: LayerSpec, seed: int = 0, device="cpu", instance: int = 0,
     return out
 
 
-def small_fp8_spec(name="small-fp8", B=3, seq_lens=(3000, 700, 0), D=1024, H=16, Dc=576, Dv=512,
+def small_fp8_spec(name="small-fp8", B=None, seq_lens=(3000, 700, 0), D=1024, H=16, Dc=576, Dv=512,
                    head_dim=128, HI=16, DI=128, topk=512, E=16, ke=4, n_shared=1, I=512, **kw) -> LayerSpec:
     """A reduced FP8 layer with the big configurations' structure (several tiles, ragged tail,
     a padding row) that the oracle finishes in seconds."""
+    if B is None:
+        B = len(seq_lens)
+    assert B == len(seq_lens), "one length per row"
     return LayerSpec(name, B=B, D=D, H=H, Dc=Dc, Dv=Dv, head_dim=head_dim, HI=HI, DI=DI, topk=topk,
                      E=E, ke=ke, n_shared=n_shared, I=I, seq_lens=tuple(seq_lens), fp8=True, **kw)
 

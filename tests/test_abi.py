@@ -1,0 +1,89 @@
+"""The C-ABI library loads, exports every entry point include/dl.h declares, and rejects bad arguments on the
+host (before any GPU work).  Runs on the CPU: no call here reaches a kernel."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import sparse_attention_moe_amd as dl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dl.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dl_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dl.LIB_PATH):
+        pytest.fail("libdl.so is not built: run __graft_entry__.build()")
+    return dl.load(require_gpu=False)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(dl.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dl_abi_version() == dl.ABI_VERSION
+
+
+def test_indexer_rejects_bad_arguments(lib):
+    P = dl.Pages(2, 64, 4, 0x1000, 0x2000)  # fake device pointers: validation fails before any use
+    ws = C.c_void_p(0x10000)
+    rc = lib.dl_indexer_topk(None, 1, 1, 16, 128, 2048, 1, None, ws, 1 << 30, None)
+    assert rc == -1 and b"pages" in lib.dl_last_error()
+    rc = lib.dl_indexer_topk(C.byref(P), None, 1, 16, 128, 2048, 1, None, ws, 1 << 30, None)
+    assert rc == -1
+    assert lib.dl_indexer_topk(C.byref(P), 1, 1, 65, 128, 2048, 1, None, ws, 1 << 30, None) == -4
+    assert lib.dl_indexer_topk(C.byref(P), 1, 1, 16, 100, 2048, 1, None, ws, 1 << 30, None) == -4
+    assert lib.dl_indexer_topk(C.byref(P), 1, 1, 16, 128, 0, 1, None, ws, 1 << 30, None) == -2
+    bad = dl.Pages(2, 48, 4, 0x1000, 0x2000)  # page size not a power of two
+    assert lib.dl_indexer_topk(C.byref(bad), 1, 1, 16, 128, 2048, 1, None, ws, 1 << 30, None) == -2
+    assert lib.dl_indexer_topk(C.byref(P), 1, 1, 16, 128, 2048, 1, None, ws, 16, None) == -5
+    assert lib.dl_indexer_topk(C.byref(P), 1, 1, 16, 128, 2048, 1, None, C.c_void_p(0x10001), 1 << 30, None) == -5
+    need = lib.dl_indexer_topk_workspace(C.byref(P))
+    assert need >= 2 * 256 * 4  # at least the score rows
+
+
+def test_ffn_and_route_reject_bad_arguments(lib):
+    wg = dl.Mat(1, 1, dl.DL_FP8_E4M3, 9, 2048, 6144)
+    wd = dl.Mat(1, 1, dl.DL_FP8_E4M3, 9, 6144, 2048)
+    ws = C.c_void_p(0x10000)
+    ok = lib.dl_moe_ffn_workspace(8, 6144, 2048, 2, 8, 1)
+    # expert top_k above the routed count
+    assert lib.dl_moe_ffn(1, 8, 6144, 2048, 1, 1, 9, C.byref(wg), C.byref(wg), C.byref(wd), 8, 1, None, 1,
+                          dl.DL_BF16, ws, ok, None) == -2
+    # FP8 weights without scales
+    ns = dl.Mat(1, None, dl.DL_FP8_E4M3, 9, 2048, 6144)
+    assert lib.dl_moe_ffn(1, 8, 6144, 2048, 1, 1, 2, C.byref(ns), C.byref(wg), C.byref(wd), 8, 1, None, 1,
+                          dl.DL_BF16, ws, ok, None) == -1
+    # FP8 weights with columns that are not whole 128-blocks
+    odd = dl.Mat(1, 1, dl.DL_FP8_E4M3, 9, 2048, 6100)
+    assert lib.dl_moe_ffn(1, 8, 6100, 2048, 1, 1, 2, C.byref(odd), C.byref(odd), C.byref(wd), 8, 1, None, 1,
+                          dl.DL_BF16, ws, ok, None) in (-2, -4)
+    # unsupported output dtype
+    assert lib.dl_moe_ffn(1, 8, 6144, 2048, 1, 1, 2, C.byref(wg), C.byref(wg), C.byref(wd), 8, 1, None, 1,
+                          dl.DL_I8, ws, ok, None) == -3
+    assert lib.dl_moe_route(1, 4, 64, 1, None, 8, 9, 1, 1, None, ws, 1 << 20, None) == -2
+    assert lib.dl_moe_route(None, 4, 64, 1, None, 8, 2, 1, 1, None, ws, 1 << 20, None) == -1
+    assert lib.dl_moe_route(1, 4, 64, 1, None, 8, 2, 1, 1, None, None, 0, None) == -5
+
+
+def test_attention_rejects_bad_arguments(lib):
+    P = dl.Pages(2, 64, 4, 0x1000, 0x2000)
+    ws = C.c_void_p(0x10000)
+    # FP8 KV without scales
+    assert lib.dl_sparse_attn_decode(C.byref(P), 1, dl.DL_BF16, 1, None, dl.DL_FP8_E4M3, 64, 576, 512, 0.04, 1, 2048,
+                                     None, None, None, 0, 1, ws, 1 << 30, None) == -1
+    # value wider than the latent
+    assert lib.dl_sparse_attn_decode(C.byref(P), 1, dl.DL_BF16, 1, 1, dl.DL_FP8_E4M3, 64, 576, 640, 0.04, 1, 2048,
+                                     None, None, None, 0, 1, ws, 1 << 30, None) == -2
+    # W_O without a residual
+    wo = dl.Mat(1, 1, dl.DL_FP8_E4M3, 1, 6144, 64 * 512)
+    assert lib.dl_sparse_attn_decode(C.byref(P), 1, dl.DL_BF16, 1, 1, dl.DL_FP8_E4M3, 64, 576, 512, 0.04, 1, 2048,
+                                     None, C.byref(wo), None, 0, 1, ws, 1 << 30, None) == -1

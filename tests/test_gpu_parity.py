@@ -1,0 +1,187 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on seeded synthetic layers.
+
+Bit-exact: kept positions (and their scores), expert choices (up to oracle logits within 1e-6).
+Floating point: max |err| <= 2e-2 * max |oracle| for o, h - x, y - h and y, each against its own maximum."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_moe_amd as dl
+import synth
+from parity import FP_TOL, assert_close, check_rows, host, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _layer(spec, seed=0, weights=True):
+    say(f"[gen] {spec.name} B={spec.B} lens={spec.seq_lens[:4]} seed={seed}")
+    return synth.make_layer(spec, seed=seed, device=DEV, weights=weights)
+
+
+def _topk(spec, t):
+    sel = torch.empty(spec.B, spec.topk, dtype=torch.int32, device=DEV)
+    ss = torch.empty_like(sel)
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+    say(f"[gpu] indexer_topk {spec.name} HI={spec.HI} DI={spec.DI} k={spec.topk}")
+    dl.indexer_topk(pg, t["q_idx"], t["k_pool"], spec.topk, sel, ss)
+    torch.cuda.synchronize()
+    return host(sel), host(ss)
+
+
+def _check_topk(spec, t, rows=None):
+    sel, ss = _topk(spec, t)
+    orc = oracle.LayerOracle(spec, t)
+    for b in (rows if rows is not None else range(spec.B)):
+        r = orc.row(b, stages=("sel",))
+        assert np.array_equal(sel[b], r["sel"]), f"{spec.name} row {b}: first diff at " \
+            f"{np.nonzero(sel[b] != r['sel'])[0][:5]}"
+        n = int((r["sel"] >= 0).sum())
+        assert np.array_equal(ss[b][:n], r["scores"][r["sel"][:n]])
+        assert np.all(ss[b][n:] == 0)
+
+
+SMALL = {
+    "tiny-fp32": synth.config(1),
+    "fp8-ragged": synth.small_fp8_spec(),
+    "fp8-ternary-ties": synth.small_fp8_spec(name="ternary", key_values="ternary", seq_lens=(5000, 2049, 2048, 17)),
+    "fp8-permuted": synth.small_fp8_spec(name="perm", permute_pages=True, extra_pages=5, seq_lens=(4100, 64, 1)),
+    "page16": synth.small_fp8_spec(name="page16", page_size=16, seq_lens=(3001, 512)),
+    "heads4-dim64": synth.small_fp8_spec(name="hi4di64", HI=4, DI=64, seq_lens=(2500, 1300)),
+    "heads20-dim48": synth.small_fp8_spec(name="hi20di48", HI=20, DI=48, seq_lens=(2600,), B=1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_indexer_topk_small(name):
+    spec = SMALL[name]
+    t = _layer(spec, seed=1, weights=False)
+    _check_topk(spec, t)
+
+
+def test_indexer_topk_k_above_length_and_empty_rows():
+    spec = synth.small_fp8_spec(name="short", seq_lens=(100, 0, 511, 512, 513), B=5, topk=512)
+    t = _layer(spec, seed=2, weights=False)
+    _check_topk(spec, t)
+
+
+def test_indexer_topk_all_equal_scores():
+    spec = synth.small_fp8_spec(name="flat", seq_lens=(6000, 3000), B=2)
+    t = _layer(spec, seed=3, weights=False)
+    t["q_idx"].zero_()  # every score is 0: the lowest positions win
+    sel, _ = _topk(spec, t)
+    assert np.array_equal(sel[0], np.arange(spec.topk))
+    assert np.array_equal(sel[1], np.arange(spec.topk))
+
+
+LAYERS = {
+    "tiny-fp32": synth.config(1),
+    "fp8-ragged-pad": synth.small_fp8_spec(),
+    "fp8-zipf-perm": synth.small_fp8_spec(name="zipf", zipf_s=1.1, permute_pages=True, B=4,
+                                          seq_lens=(2500, 4096, 1000, 3333)),
+    "fp8-dup-router": synth.small_fp8_spec(name="dup", dup_router_rows=True, seq_lens=(1500, 2600), B=2),
+    "fp8-ke1-noshared": synth.small_fp8_spec(name="ke1", ke=1, n_shared=0, seq_lens=(900, 3000), B=2),
+    "fp8-b20": synth.small_fp8_spec(name="b20", B=20, seq_lens=tuple(600 + 97 * i for i in range(20)), topk=256),
+}
+
+
+@pytest.mark.parametrize("name", list(LAYERS))
+def test_layer_step_small(name):
+    spec = LAYERS[name]
+    t = _layer(spec, seed=4)
+    step = dl.LayerStep(spec, t, debug=True)
+    say(f"[gpu] layer_step {spec.name}")
+    y = step()
+    torch.cuda.synchronize()
+    w = check_rows(spec, t, step.dbg, y, list(range(spec.B)))
+    say(f"{name}: {w}")
+
+
+def test_fused_equals_unfused_and_replays():
+    spec = synth.small_fp8_spec(name="fused", B=3, seq_lens=(3000, 700, 0))
+    t = _layer(spec, seed=5)
+    step = dl.LayerStep(spec, t, debug=True)
+    say("[gpu] fused step + 4 separate calls")
+    y = step().clone()
+    ref = {k: v.clone() for k, v in step.dbg.items()}
+    B = spec.B
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+    sel = torch.empty(B, spec.topk, dtype=torch.int32, device=DEV)
+    dl.indexer_topk(pg, t["q_idx"], t["k_pool"], spec.topk, sel)
+    h = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
+    dl.sparse_attn_decode(pg, t["q"], t["kv"], t.get("kv_scale"), spec.H, spec.Dc, spec.Dv, spec.scale, sel,
+                          spec.topk, h, w_uv=dl.mat(t["w_uv"], t["w_uv_scale"]), w_o=dl.mat(t["w_o"], t["w_o_scale"]),
+                          residual=t["x"])
+    ex = torch.empty(B, spec.ke, dtype=torch.int32, device=DEV)
+    g = torch.empty(B, spec.ke, dtype=torch.float32, device=DEV)
+    dl.moe_route(h, t["w_r"], t["r_bias"], spec.ke, ex, g)
+    y2 = torch.empty_like(y)
+    dl.moe_ffn(h, ex, g, dl.mat(t["w_gate"], t["w_gate_scale"]), dl.mat(t["w_up"], t["w_up_scale"]),
+               dl.mat(t["w_down"], t["w_down_scale"]), spec.E, spec.n_shared, y2, residual=h)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, ref["sel"]) and torch.equal(h, ref["h"])
+    assert torch.equal(ex, ref["experts"]) and torch.equal(g, ref["gates"])
+    assert torch.equal(y2, y)
+    say("[gpu] 50 replays")
+    for i in range(50):
+        yi = step()
+        if i % 10 == 9:
+            torch.cuda.synchronize()
+            assert torch.equal(yi, y)
+            for k, v in step.dbg.items():
+                assert torch.equal(v, ref[k]), k
+
+
+def test_attention_only_matches_oracle():
+    spec = synth.small_fp8_spec(name="attn", B=2, seq_lens=(2600, 333))
+    t = _layer(spec, seed=6, weights=False)
+    sel, _ = _topk(spec, t)
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+    o = torch.empty(spec.B, spec.H, spec.Dv, dtype=torch.float32, device=DEV)
+    dl.sparse_attn_decode(pg, t["q"], t["kv"], t["kv_scale"], spec.H, spec.Dc, spec.Dv, spec.scale,
+                          torch.from_numpy(sel).to(DEV), spec.topk, o)
+    torch.cuda.synchronize()
+    orc = oracle.LayerOracle(spec, t)
+    for b in range(spec.B):
+        ref = oracle.attention(orc.a("q")[b], orc.a("kv"), orc.a("kv_scale"), orc.a("page_table")[b], sel[b],
+                               spec.scale, spec.Dv)
+        assert_close(f"o row {b}", host(o)[b], ref)
+
+
+# ------------------------------------------------------------------ the five named workloads
+FULL_ROWS = {2: [0, 7], 3: [0], 4: [0, 5, 11], 5: [0, 63]}
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_config(cfg):
+    spec = synth.config(cfg)
+    t = _layer(spec, seed=0)
+    step = dl.LayerStep(spec, t, debug=True)
+    say(f"[gpu] layer_step {spec.name}")
+    y = step()
+    torch.cuda.synchronize()
+    say(f"[cpu] oracle rows {FULL_ROWS[cfg]}")
+    w = check_rows(spec, t, step.dbg, y, FULL_ROWS[cfg])
+    # every row: kept positions are ascending, unique, in range
+    sel = host(step.dbg["sel"])
+    lens = host(t["seq_lens"])
+    for b in range(spec.B):
+        n = min(spec.topk, int(lens[b]))
+        assert np.all(np.diff(sel[b][:n]) > 0) and np.all(sel[b][n:] == -1)
+        if n:
+            assert sel[b][0] >= 0 and sel[b][n - 1] < lens[b]
+    say(f"cfg{cfg}: {w}")
+    del step, t
+    torch.cuda.empty_cache()
+
+
+def test_tiny_config_full_oracle():
+    spec = synth.config(1)
+    t = _layer(spec, seed=0)
+    step = dl.LayerStep(spec, t, debug=True)
+    y = step()
+    torch.cuda.synchronize()
+    w = check_rows(spec, t, step.dbg, y, [0])
+    assert w["y"] <= FP_TOL
