@@ -1,0 +1,151 @@
+"""Benchmark of the fused decode layer step (dl_layer_step) on one MI355X.
+
+One step = one pass of the whole hot path (indexer + top-k, sparse attention, W_UV/W_O, router, expert FFN)
+over one batch of seeded synthetic inputs resident in HBM.  The default workload is batch 8 at 128K context
+(hidden 6144, 64 heads over a 576-wide FP8 latent, top-2,048, 256 experts top-8 + 1 shared, FP8 weights).
+
+To keep the 256 MB last-level cache from serving repeats, the timed steps rotate over --instances distinct
+layer instances (separate weights, caches and inputs; ~10.5 GB each).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_attention_moe_amd as dl  # noqa: E402
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode layer-steps/s + achieved HBM GB/s (% of peak), batch 8 @ 128K ctx"
+EXPERT_BYTES_GATE_UP = lambda s: 2 * s.I * s.D + 2 * (s.I // 128) * (s.D // 128) * 4  # per touched expert
+EXPERT_BYTES_DOWN = lambda s: s.D * s.I + (s.D // 128) * (s.I // 128) * 4
+
+
+def algorithmic_bytes(spec, lens, n_touched: int) -> dict:
+    """Bytes the method must read per step (weights and caches once; activations are negligible)."""
+    keys = sum(int(l) for l in lens) * spec.DI
+    nb = (spec.Dc + 127) // 128
+    kv = sum(min(int(l), spec.topk) for l in lens) * (spec.Dc + 4 * nb)
+    hd = spec.head_dim or spec.Dv
+    wuv = spec.H * hd * spec.Dv + spec.H * (hd // 128) * (spec.Dv // 128) * 4 if spec.head_dim else 0
+    wo = spec.D * spec.wo_in + (spec.D // 128) * (spec.wo_in // 128) * 4
+    wr = spec.E * spec.D * 4
+    gu = n_touched * EXPERT_BYTES_GATE_UP(spec)
+    dn = n_touched * EXPERT_BYTES_DOWN(spec)
+    return dict(indexer_keys=keys, selected_kv=kv, w_uv=wuv, w_o=wo, w_r=wr, expert_gate_up=gu, expert_down=dn,
+                total=keys + kv + wuv + wo + wr + gu + dn)
+
+
+def touched(spec, experts: np.ndarray) -> int:
+    return len(set(int(e) for e in experts.ravel())) + spec.n_shared
+
+
+def cpu_baseline(spec, t, rows):
+    """The oracle, as it stands, on a bounded sample: `rows` rows of one step (each row is independent)."""
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    orc = oracle.LayerOracle(spec, t)
+    for b in rows:  # host copies of the caches and the touched experts are made before timing
+        _ = orc.a("k_pool"), orc.a("kv"), orc.a("kv_scale")
+    t0 = time.perf_counter()
+    for b in rows:
+        orc.row(b)
+    dt = time.perf_counter() - t0
+    per_step = dt / len(rows) * spec.B
+    return {"value": 1.0 / per_step, "unit": "layer-steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {spec.B} rows of one {spec.name} step (indexer over the full context, "
+                      f"attention, projections, router, FFN), {dt:.1f} s, scaled to a whole step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    spec = synth.config(args.config)
+    dev = "cuda"
+    insts, steps_obj = [], []
+    t0 = time.perf_counter()
+    for i in range(args.instances):
+        t = synth.make_layer(spec, seed=args.seed, device=dev, instance=i)
+        insts.append(t)
+        steps_obj.append(dl.LayerStep(spec, t, debug=True))
+    torch.cuda.synchronize()
+    print(f"[bench] generated {args.instances} x {spec.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    n = len(steps_obj)
+    for i in range(args.warmup):
+        steps_obj[i % n]()
+    torch.cuda.synchronize()
+    # timed region 1: the whole step, nothing else recorded
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        steps_obj[i % n]()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # timed region 2: same steps with phase events on the library's stream (per-kernel durations)
+    dl.profile_enable(True)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        steps_obj[i % n]()
+    torch.cuda.synchronize()
+    ph, nst = dl.profile_read()
+    dl.profile_enable(False)
+    ph = {k: v / nst for k, v in ph.items()}
+    # algorithmic bytes of the steps actually run (touched experts per instance)
+    per_inst = []
+    for s in steps_obj:
+        ex = s.dbg["experts"].cpu().numpy()
+        per_inst.append((touched(spec, ex), algorithmic_bytes(spec, spec.seq_lens, touched(spec, ex))))
+    avg_touch = sum(p[0] for p in per_inst) / n
+    avg_bytes = {k: sum(p[1][k] for p in per_inst) / n for k in per_inst[0][1]}
+    steps_per_s = 1000.0 / ms
+    step_gbs = avg_bytes["total"] / (ms * 1e-3) / 1e9
+    gu_gbs = avg_bytes["expert_gate_up"] / (ph["expert_gate_up"] * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": round(steps_per_s, 2), "unit": "layer-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-weights/int8-indexer/fp32-accum",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.B, "context": int(max(spec.seq_lens)), "hidden": spec.D,
+                   "heads": spec.H, "latent": spec.Dc, "top_k": spec.topk, "experts": f"{spec.E}+{spec.n_shared}",
+                   "expert_top_k": spec.ke, "inter": spec.I, "instances_rotated": n},
+        "tokens_per_s_per_layer": round(steps_per_s * spec.B, 1),
+        "step_hbm": {"algorithmic_bytes": int(avg_bytes["total"]), "achieved_gbs": round(step_gbs, 1),
+                     "peak_gbs": HBM_PEAK_GBS, "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                     "touched_experts": round(avg_touch, 2)},
+        "phase_ms": {k: round(v, 4) for k, v in ph.items()},
+        "roofline": {"kernel": "k_gemv_fp8<2,SWIGLU> (expert gate/up)", "bound": "hbm",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(avg_bytes["expert_gate_up"]),
+                     "ms_per_launch": round(ph["expert_gate_up"], 4)},
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(spec, insts[0], list(range(args.cpu_rows)))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -206,10 +206,23 @@ typedef struct dl_layer_io {
     int32_t *experts;     /* [B, expert_top_k] */
     float *gates;         /* [B, expert_top_k] */
     float *o;             /* [B, n_heads, d_v] attention output before projection */
+    float *y32;           /* [B, D] the output in fp32 before its one rounding */
 } dl_layer_io;
 
 size_t dl_layer_workspace(const dl_layer_desc *desc, const dl_pages *pages);
 int dl_layer_step(const dl_layer_desc *desc, const dl_layer_io *io, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- measurement
+ * When enabled, every dl_layer_step records a HIP event on its stream at each phase boundary:
+ *   0 indexer + top-k   1 attention   2 W_UV + W_O (+ activation split)   3 router
+ *   4 dispatch plan + split of h   5 expert gate/up (one kernel)   6 split of Z
+ *   7 expert down (one kernel)   8 combine
+ * dl_profile_read waits for the recorded steps, adds each phase's elapsed milliseconds into
+ * ms_sum[DL_N_PHASES], stores the number of steps in *steps and forgets them.  Measurement only:
+ * single host thread, events are created on first use and kept until dl_profile_enable(0). */
+#define DL_N_PHASES 9
+int dl_profile_enable(int on);
+int dl_profile_read(double *ms_sum, int64_t *steps);
 
 #ifdef __cplusplus
 }

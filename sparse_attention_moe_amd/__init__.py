@@ -22,7 +22,11 @@ STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE",
 
 EXPORTS = ["dl_abi_version", "dl_last_error", "dl_indexer_topk_workspace", "dl_indexer_topk",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
-           "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step"]
+           "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
+           "dl_profile_read"]
+N_PHASES = 9
+PHASES = ["indexer_topk", "attention", "projection", "router", "plan_split_h", "expert_gate_up", "split_z",
+          "expert_down", "combine"]
 
 
 class DLError(RuntimeError):
@@ -53,7 +57,7 @@ class LayerIO(C.Structure):
     _fields_ = [("pages", Pages), ("x", C.c_void_p), ("q", C.c_void_p), ("q_idx", C.c_void_p),
                 ("kv_pool", C.c_void_p), ("kv_scale", C.c_void_p), ("k_pool", C.c_void_p), ("y", C.c_void_p),
                 ("sel", C.c_void_p), ("h", C.c_void_p), ("experts", C.c_void_p), ("gates", C.c_void_p),
-                ("o", C.c_void_p)]
+                ("o", C.c_void_p), ("y32", C.c_void_p)]
 
 
 _lib = None
@@ -88,6 +92,8 @@ def load(require_gpu: bool = True):
         L.dl_layer_workspace.restype = sz
         L.dl_layer_workspace.argtypes = [C.POINTER(LayerDesc), C.POINTER(Pages)]
         L.dl_layer_step.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), P, sz, P]
+        L.dl_profile_enable.argtypes = [C.c_int]
+        L.dl_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
         if L.dl_abi_version() != ABI_VERSION:
             raise ImportError(f"libdl ABI {L.dl_abi_version()} != {ABI_VERSION}")
         _lib = L
@@ -187,6 +193,18 @@ def moe_ffn(h, experts, gates, w_gate: Mat, w_up: Mat, w_down: Mat, n_routed, n_
     return out
 
 
+def profile_enable(on: bool):
+    _check(load().dl_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """-> (dict phase -> summed ms, number of steps) for the steps recorded since the last read."""
+    arr = (C.c_double * N_PHASES)()
+    n = C.c_int64()
+    _check(load().dl_profile_read(arr, C.byref(n)))
+    return {PHASES[i]: arr[i] for i in range(N_PHASES)}, n.value
+
+
 # ---------------------------------------------------------------- whole step
 class LayerStep:
     """dl_layer_step over one layer instance given as a dict of device tensors (names as synth.make_layer).
@@ -228,7 +246,8 @@ class LayerStep:
                             h=torch.empty(B, spec.D, dtype=torch.float32, device=dev),
                             experts=torch.empty(B, spec.ke, dtype=torch.int32, device=dev),
                             gates=torch.empty(B, spec.ke, dtype=torch.float32, device=dev),
-                            o=torch.empty(B, spec.H, spec.Dv, dtype=torch.float32, device=dev))
+                            o=torch.empty(B, spec.H, spec.Dv, dtype=torch.float32, device=dev),
+                            y32=torch.empty(B, spec.D, dtype=torch.float32, device=dev))
             for k, v in self.dbg.items():
                 setattr(io, k, _ptr(v))
         self.io = io

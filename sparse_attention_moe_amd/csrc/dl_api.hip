@@ -1,6 +1,7 @@
 // Host side of the C ABI: argument checks, workspace layout and the launch sequence of each entry
 // point.  Nothing here computes; every step of the path runs in the gfx950 kernels.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -34,6 +35,47 @@ int hip_check(const char *what)
     } while (0)
 
 static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// ------------------------------------------------------------------ phase events (measurement only)
+struct StepMarks {
+    hipEvent_t ev[DL_N_PHASES + 1];
+};
+static bool g_prof = false;
+static StepMarks *g_pend = nullptr;  // recorded, not yet read
+static int g_npend = 0, g_cap = 0;
+static StepMarks *g_free = nullptr;
+static int g_nfree = 0, g_fcap = 0;
+
+struct Marks {
+    StepMarks *m = nullptr;
+    hipStream_t s = nullptr;
+    void at(int i) const
+    {
+        if (m) hipEventRecord(m->ev[i], s);
+    }
+};
+
+static int marks_begin(Marks &mk, hipStream_t s)
+{
+    mk.s = s;
+    mk.m = nullptr;
+    if (!g_prof) return DL_OK;
+    if (g_npend == g_cap) {
+        g_cap = g_cap ? 2 * g_cap : 64;
+        g_pend = (StepMarks *)realloc(g_pend, sizeof(StepMarks) * g_cap);
+        if (!g_pend) return fail(DL_ERR_HIP, "profile: out of host memory");
+    }
+    StepMarks sm;
+    if (g_nfree) {
+        sm = g_free[--g_nfree];
+    } else {
+        for (int i = 0; i <= DL_N_PHASES; i++)
+            if (hipEventCreate(&sm.ev[i]) != hipSuccess) return fail(DL_ERR_HIP, "profile: hipEventCreate");
+    }
+    g_pend[g_npend] = sm;
+    mk.m = &g_pend[g_npend++];
+    return DL_OK;
+}
 
 static int check_pages(const dl_pages *pg)
 {
@@ -134,6 +176,7 @@ static GemvArgs mat_args(const dl_mat *m)
 static int run_projection(int B, int H, int Dv, const float *o, const dl_mat *w_uv, const dl_mat *w_o,
                           const void *resid, int resid_dt, float *out, const AttnWs &a, hipStream_t s)
 {
+
     const long BH = (long)B * H;
     const float *act = o;
     int K = Dv;
@@ -218,7 +261,8 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
 
 static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, const float *gates, int ke,
                    const dl_mat *wg, const dl_mat *wu, const dl_mat *wd, int E, int S, const void *resid,
-                   int resid_dt, void *out, int out_dt, const FfnWs &f, hipStream_t s)
+                   int resid_dt, void *out, int out_dt, const FfnWs &f, hipStream_t s, const Marks &mk = Marks(),
+                   float *out32 = nullptr)
 {
     const bool f8 = wg->dtype == DL_FP8_E4M3;
     const int NE = E + S;
@@ -244,7 +288,9 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     } else {
         g.af = h;
     }
+    mk.at(5);
     DL_TRY(launch_gemv(g, FFN_PARTS, EPI_SWIGLU, f8, s));
+    mk.at(6);
     // down -> F
     GemvArgs d = mat_args(wd);
     d.active = f.plan.active;
@@ -262,8 +308,12 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     } else {
         d.af = f.Z;
     }
+    mk.at(7);
     DL_TRY(launch_gemv(d, FFN_PARTS, EPI_STORE, f8, s));
-    return launch_combine(f.F, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt, s);
+    mk.at(8);
+    DL_TRY(launch_combine(f.F, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt, out32, s));
+    mk.at(9);
+    return DL_OK;
 }
 
 struct LayerWs {
@@ -512,15 +562,61 @@ int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_
     Ws w(ws);
     LayerWs L;
     layer_ws_layout(w, d, &pg, io, L);
+    Marks mk;
+    DL_TRY(marks_begin(mk, s));
+    mk.at(0);
     DL_TRY(launch_indexer_topk(pg, io->q_idx, io->k_pool, d->idx_heads, d->idx_dim, d->top_k, L.sel, nullptr, L.topk, s));
+    mk.at(1);
     DL_TRY(launch_attention(pg, io->q, d->q_dt, io->kv_pool, io->kv_scale, d->kv_dt, d->n_heads, d->d_c, d->d_v,
                             d->sm_scale, L.sel, d->top_k, L.o, s));
+    mk.at(2);
     DL_TRY(run_projection(B, d->n_heads, d->d_v, L.o, d->w_uv.w ? &d->w_uv : nullptr, &d->w_o, io->x, d->q_dt, L.h,
                           L.attn, s));
+    mk.at(3);
     DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates, nullptr,
                         L.logits64, s));
+    mk.at(4);
     return run_ffn(L.h, B, d->D, d->inter, L.experts, L.gates, d->expert_top_k, &d->w_gate, &d->w_up, &d->w_down,
-                   d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s);
+                   d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s, mk, io->y32);
+}
+
+int dl_profile_enable(int on)
+{
+    g_err[0] = 0;
+    g_prof = on != 0;
+    if (!g_prof) {
+        for (int i = 0; i < g_npend; i++)
+            for (int j = 0; j <= DL_N_PHASES; j++) hipEventDestroy(g_pend[i].ev[j]);
+        for (int i = 0; i < g_nfree; i++)
+            for (int j = 0; j <= DL_N_PHASES; j++) hipEventDestroy(g_free[i].ev[j]);
+        g_npend = g_nfree = 0;
+    }
+    return DL_OK;
+}
+
+int dl_profile_read(double *ms_sum, int64_t *steps)
+{
+    g_err[0] = 0;
+    if (!ms_sum || !steps) return fail(DL_ERR_NULL, "ms_sum/steps NULL");
+    for (int j = 0; j < DL_N_PHASES; j++) ms_sum[j] = 0.0;
+    *steps = g_npend;
+    for (int i = 0; i < g_npend; i++) {
+        StepMarks &m = g_pend[i];
+        if (hipEventSynchronize(m.ev[DL_N_PHASES]) != hipSuccess) return fail(DL_ERR_HIP, "profile: sync");
+        for (int j = 0; j < DL_N_PHASES; j++) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, m.ev[j], m.ev[j + 1]) != hipSuccess) return fail(DL_ERR_HIP, "profile: elapsed");
+            ms_sum[j] += ms;
+        }
+        if (g_nfree == g_fcap) {
+            g_fcap = g_fcap ? 2 * g_fcap : 64;
+            g_free = (StepMarks *)realloc(g_free, sizeof(StepMarks) * g_fcap);
+            if (!g_free) return fail(DL_ERR_HIP, "profile: out of host memory");
+        }
+        g_free[g_nfree++] = m;
+    }
+    g_npend = 0;
+    return DL_OK;
 }
 
 }  // extern "C"

@@ -101,6 +101,6 @@ int launch_route(const float *h, int B, int D, const float *w_r, const float *bi
                  float *gates, float *logits, double *logits64, hipStream_t s);
 int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s);
 int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
-                   const void *resid, int resid_dt, void *out, int out_dt, hipStream_t s);
+                   const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s);
 
 }  // namespace dl

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ exper
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, const int *__restrict__ pair_idx,
                                                  const float *__restrict__ gates, int B, int D, int ke, int S,
                                                  const void *__restrict__ resid, int resid_dt, void *__restrict__ out,
-                                                 int out_dt)
+                                                 int out_dt, float *__restrict__ out32)
 {
     const int b = blockIdx.y;
     const int d = blockIdx.x * 256 + threadIdx.x;
@@ -188,6 +188,7 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, co
         acc = fmaf(gates[(long)b * ke + j], F[(long)p * D + d], acc);
     }
     for (int s = 0; s < S; s++) acc += F[(long)pair_idx[(long)b * kk + ke + s] * D + d];
+    if (out32) out32[(long)b * D + d] = acc;
     if (out_dt == DL_BF16) ((uint16_t *)out)[(long)b * D + d] = f32_to_bf16(acc);
     else ((float *)out)[(long)b * D + d] = acc;
 }
@@ -209,10 +210,11 @@ int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePl
 }
 
 int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
-                   const void *resid, int resid_dt, void *out, int out_dt, hipStream_t s)
+                   const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s)
 {
     dim3 g((D + 255) / 256, B);
-    hipLaunchKernelGGL(k_combine, g, dim3(256), 0, s, F, p.pair_idx, gates, B, D, ke, S, resid, resid_dt, out, out_dt);
+    hipLaunchKernelGGL(k_combine, g, dim3(256), 0, s, F, p.pair_idx, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
+                       out32);
     return hip_check("combine");
 }
 

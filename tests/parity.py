@@ -27,6 +27,13 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
+def host_out(y: np.ndarray) -> np.ndarray:
+    """Oracle output (bf16 bit patterns or fp32) as fp64."""
+    if y.dtype == np.uint16:
+        return (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return y.astype(np.float64)
+
+
 def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -61,37 +68,52 @@ def expert_mismatch(gpu_ex: np.ndarray, orc_ex: np.ndarray, logits: np.ndarray) 
 
 def check_rows(spec, t: Dict[str, torch.Tensor], dbg: Dict[str, torch.Tensor], y: torch.Tensor, rows: List[int],
                stages=("sel", "o", "h", "route", "y")) -> Dict[str, float]:
-    """Stage-wise parity of the fused step's outputs on `rows` against the oracle. Returns the worst errors."""
+    """Stage-wise parity of the fused step's outputs on `rows` against the oracle. Returns the worst errors.
+    Every stage in `stages` is compared for every row (a near-tie expert swap skips only that row's FFN)."""
     orc = oracle.LayerOracle(spec, t)
     x = host(t["x"]).astype(np.float64)
     worst = {"o": 0.0, "h-x": 0.0, "y-h": 0.0, "y": 0.0, "gates": 0.0, "near_ties": 0}
+    n_cmp = {"sel": 0, "o": 0, "h": 0, "route": 0, "y": 0}
     sel_g = host(dbg["sel"]) if "sel" in dbg else None
     for b in rows:
         r = orc.row(b, stages)
         if sel_g is not None:
             assert np.array_equal(sel_g[b], r["sel"]), f"row {b}: sel differs at " \
                 f"{np.nonzero(sel_g[b] != r['sel'])[0][:8]}"
+            n_cmp["sel"] += 1
         if "o" not in r:
             continue
         if "o" in dbg:
             worst["o"] = max(worst["o"], assert_close(f"row {b} o", host(dbg["o"])[b], r["o"]))
+            n_cmp["o"] += 1
         if "h" not in r:
             continue
         hg = host(dbg["h"])[b]
         worst["h-x"] = max(worst["h-x"], assert_close(f"row {b} h-x", hg - x[b], r["h"] - x[b]))
-        if "route" not in r:
+        n_cmp["h"] += 1
+        if "experts" not in r:
             continue
         mm = expert_mismatch(host(dbg["experts"])[b], r["experts"], r["logits"])
         if mm is not None and mm != "near-tie":
             raise AssertionError(f"row {b}: {mm}")
+        n_cmp["route"] += 1
         if mm == "near-tie":
             worst["near_ties"] += 1
             say(f"row {b}: expert choice differs at a near-tie (<= {ROUTER_TIE}); FFN output not compared")
             continue
         worst["gates"] = max(worst["gates"], assert_close(f"row {b} gates", host(dbg["gates"])[b], r["gates"]))
-        if "y" not in r:
+        if "y64" not in r:
             continue
         yg = host(y)[b]
-        worst["y-h"] = max(worst["y-h"], assert_close(f"row {b} y-h", yg - hg, r["y64"] - r["h"]))
-        worst["y"] = max(worst["y"], assert_close(f"row {b} y", yg, r["y64"]))
+        y32 = host(dbg["y32"])[b]
+        worst["y-h"] = max(worst["y-h"], assert_close(f"row {b} y-h", y32 - hg, r["y64"] - r["h"]))
+        worst["y"] = max(worst["y"], assert_close(f"row {b} y", yg, host_out(r["y"])))
+        n_cmp["y"] += 1
+    want = {"sel": "sel" in stages, "o": "o" in stages, "h": "h" in stages, "route": "route" in stages,
+            "y": "y" in stages}
+    for k, on in want.items():
+        if on:
+            need = len(rows) - (worst["near_ties"] if k == "y" else 0)
+            assert n_cmp[k] == need, f"stage {k} compared on {n_cmp[k]} of {need} rows"
+    worst["rows"] = len(rows)
     return worst
