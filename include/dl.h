@@ -145,8 +145,9 @@ int dl_sparse_attn_decode(const dl_pages *pages, const void *q, int32_t q_dt, co
  *   gates[b]    = softmax over those top_k logits
  *   h fp32 [B, D]; w_r fp32 [n_experts, D]; bias fp32 [n_experts] nullable;
  *   experts int32 [B, top_k]; gates fp32 [B, top_k]; logits fp32 [B, n_experts] nullable.
- * Limits: 1 <= top_k <= 32, top_k <= n_experts <= 4096.  Workspace: dl_moe_route_workspace(B, n_experts). */
-size_t dl_moe_route_workspace(int32_t B, int32_t n_experts);
+ * Limits: 1 <= top_k <= 32, top_k <= n_experts <= 4096, D % 4 == 0.
+ * Workspace: dl_moe_route_workspace(B, D, n_experts). */
+size_t dl_moe_route_workspace(int32_t B, int32_t D, int32_t n_experts);
 int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const float *bias, int32_t n_experts,
                  int32_t top_k, int32_t *experts, float *gates, float *logits, void *ws, size_t ws_bytes, void *stream);
 

@@ -83,7 +83,7 @@ def load(require_gpu: bool = True):
         L.dl_sparse_attn_decode.argtypes = [C.POINTER(Pages), P, i32, P, P, i32, i32, i32, i32, C.c_float, P, i32,
                                             C.POINTER(Mat), C.POINTER(Mat), P, i32, P, P, sz, P]
         L.dl_moe_route_workspace.restype = sz
-        L.dl_moe_route_workspace.argtypes = [i32, i32]
+        L.dl_moe_route_workspace.argtypes = [i32, i32, i32]
         L.dl_moe_route.argtypes = [P, i32, i32, P, P, i32, i32, P, P, P, P, sz, P]
         L.dl_moe_ffn_workspace.restype = sz
         L.dl_moe_ffn_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -173,7 +173,7 @@ def moe_route(h, w_r, bias, top_k, experts, gates, logits=None, ws=None, stream=
     B, D = h.shape
     E = w_r.shape[0]
     if ws is None:
-        ws = workspace(L.dl_moe_route_workspace(B, E), h.device)
+        ws = workspace(L.dl_moe_route_workspace(B, D, E), h.device)
     _check(L.dl_moe_route(_ptr(h), B, D, _ptr(w_r), _ptr(bias), E, top_k, _ptr(experts), _ptr(gates), _ptr(logits),
                           _ptr(ws), ws.numel(), _stream(stream)))
     return experts, gates

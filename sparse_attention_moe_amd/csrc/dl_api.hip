@@ -125,7 +125,11 @@ static int check_indexer(int HI, int DI, int top_k)
 }
 
 // ------------------------------------------------------------------ attention + projection
+static constexpr int MAX_KSPLIT = 16;
+
 struct AttnWs {
+    float *opart, *ml;         // split partials of the matrix-core attention
+    float *kpart;              // [MAX_KSPLIT, B, D] K-chunk partials of W_O
     float *o;                  // [B, H, Dv] (when the caller's out is not o)
     uint8_t *oq; float *oqs;   // 4 parts of o for W_UV
     float *u;                  // [B, H*hd]
@@ -134,9 +138,17 @@ struct AttnWs {
 static constexpr int PROJ_PARTS = 4;  // projections ahead of the router keep ~16 significant bits
 static constexpr int FFN_PARTS = 2;
 
-static void attn_ws_layout(Ws &w, int B, int H, int Dv, const dl_mat *w_uv, const dl_mat *w_o, AttnWs &a)
+static void attn_split_ws(Ws &w, int B, int H, int Dv, int top_k, AttnWs &a)
+{
+    const long ns = attention_splits(top_k);
+    a.opart = w.take<float>((long)B * ns * H * Dv);
+    a.ml = w.take<float>((long)B * ns * H * 2);
+}
+
+static void attn_ws_layout(Ws &w, int B, int H, int Dv, int top_k, const dl_mat *w_uv, const dl_mat *w_o, AttnWs &a)
 {
     a = AttnWs{};
+    attn_split_ws(w, B, H, Dv, top_k, a);
     if (!w_o) return;
     const long BH = (long)B * H;
     a.o = w.take<float>(BH * Dv);
@@ -151,7 +163,17 @@ static void attn_ws_layout(Ws &w, int B, int H, int Dv, const dl_mat *w_uv, cons
     if (w_o->dtype == DL_FP8_E4M3) {
         a.uq = w.take<uint8_t>(PROJ_PARTS * BH * hd);
         a.uqs = w.take<float>(PROJ_PARTS * BH * (hd / 128));
+        a.kpart = w.take<float>((long)MAX_KSPLIT * B * w_o->rows);
     }
+}
+
+// K split of a one-matrix projection so that enough waves stream it: about 2,048 work items, chunks of
+// at least 4 blocks, a power of two that divides the block count.
+static int pick_ksplit(long items, int nkb)
+{
+    int ks = 1;
+    while (ks < MAX_KSPLIT && items * ks < 2048 && nkb % (2 * ks) == 0 && nkb / (2 * ks) >= 4) ks *= 2;
+    return ks;
 }
 
 static GemvArgs mat_args(const dl_mat *m)
@@ -164,6 +186,8 @@ static GemvArgs mat_args(const dl_mat *m)
     } else {
         g.wf = (const float *)m->w;
     }
+    g.ksplit = 1;
+    g.kchunk = (m->cols + 127) / 128;
     g.mat_elems = (long)m->rows * m->cols;
     g.rows = m->rows;
     g.cols = m->cols;
@@ -220,6 +244,10 @@ static int run_projection(int B, int H, int Dv, const float *o, const dl_mat *w_
     if (f8) {
         DL_TRY(launch_quant(act, B, nullptr, K, a.uq, a.uqs, (long)B * K, (long)B * (K / 128), PROJ_PARTS, s));
         g.aq = a.uq; g.asc = a.uqs; g.aq_part = (long)B * K; g.asc_part = (long)B * (K / 128);
+        g.ksplit = pick_ksplit((long)(w_o->rows / 16) * g.max_groups, g.nkb);
+        g.kchunk = g.nkb / g.ksplit;
+        g.part = a.kpart;
+        g.n_out = (long)B * w_o->rows;
     } else {
         g.af = act;
     }
@@ -321,7 +349,7 @@ struct LayerWs {
     int32_t *sel;
     AttnWs attn;
     float *o, *h;
-    double *logits64;
+    double *logits64, *rpart;
     int32_t *experts;
     float *gates;
     FfnWs ffn;
@@ -333,7 +361,7 @@ static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, c
     topk_ws_layout(w, *pg, L.topk);
     L.sel = (io && io->sel) ? io->sel : w.take<int32_t>((long)B * d->top_k);
     L.o = (io && io->o) ? io->o : w.take<float>((long)B * d->n_heads * d->d_v);
-    attn_ws_layout(w, B, d->n_heads, d->d_v, d->w_uv.w ? &d->w_uv : nullptr, nullptr, L.attn);  // o handled above
+    attn_ws_layout(w, B, d->n_heads, d->d_v, d->top_k, d->w_uv.w ? &d->w_uv : nullptr, nullptr, L.attn);
     const int hd = d->w_uv.w ? d->w_uv.rows : d->d_v;
     const long BH = (long)B * d->n_heads;
     L.attn.o = L.o;
@@ -347,9 +375,11 @@ static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, c
     if (d->w_o.dtype == DL_FP8_E4M3) {
         L.attn.uq = w.take<uint8_t>(PROJ_PARTS * BH * hd);
         L.attn.uqs = w.take<float>(PROJ_PARTS * BH * (hd / 128));
+        L.attn.kpart = w.take<float>((long)MAX_KSPLIT * B * d->w_o.rows);
     }
     L.h = (io && io->h) ? io->h : w.take<float>((long)B * d->D);
     L.logits64 = w.take<double>((long)B * d->n_routed);
+    L.rpart = w.take<double>((long)route_chunks(d->D) * B * d->n_routed);
     L.experts = (io && io->experts) ? io->experts : w.take<int32_t>((long)B * d->expert_top_k);
     L.gates = (io && io->gates) ? io->gates : w.take<float>((long)B * d->expert_top_k);
     ffn_ws_layout(w, B, d->D, d->inter, d->expert_top_k, d->n_routed, d->n_shared, d->w_gate.dtype == DL_FP8_E4M3,
@@ -438,10 +468,9 @@ int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_
 size_t dl_sparse_attn_workspace(int32_t batch, int32_t n_heads, int32_t d_v, int32_t top_k, const dl_mat *w_uv,
                                 const dl_mat *w_o)
 {
-    (void)top_k;
     Ws w(nullptr);
     AttnWs a;
-    attn_ws_layout(w, batch, n_heads, d_v, w_uv, w_o, a);
+    attn_ws_layout(w, batch, n_heads, d_v, top_k, w_uv, w_o, a);
     return w.used();
 }
 
@@ -466,17 +495,19 @@ int dl_sparse_attn_decode(const dl_pages *pages, const void *q, int32_t q_dt, co
     hipStream_t s = (hipStream_t)stream;
     Ws w(ws);
     AttnWs a;
-    attn_ws_layout(w, pages->batch, n_heads, d_v, w_uv, w_o, a);
+    attn_ws_layout(w, pages->batch, n_heads, d_v, top_k, w_uv, w_o, a);
     float *o = w_o ? a.o : out;
-    DL_TRY(launch_attention(*pages, q, q_dt, kv_pool, kv_scale, kv_dt, n_heads, d_c, d_v, sm_scale, sel, top_k, o, s));
+    DL_TRY(launch_attention(*pages, q, q_dt, kv_pool, kv_scale, kv_dt, n_heads, d_c, d_v, sm_scale, sel, top_k, o,
+                            a.opart, a.ml, s));
     if (!w_o) return DL_OK;
     return run_projection(pages->batch, n_heads, d_v, o, w_uv, w_o, residual, res_dt, out, a, s);
 }
 
-size_t dl_moe_route_workspace(int32_t B, int32_t n_experts)
+size_t dl_moe_route_workspace(int32_t B, int32_t D, int32_t n_experts)
 {
     Ws w(nullptr);
     w.take<double>((long)B * n_experts);
+    w.take<double>((long)route_chunks(D) * B * n_experts);
     return w.used();
 }
 
@@ -488,11 +519,13 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
     if (B < 1 || B > 65536 || D < 1) return fail(DL_ERR_SHAPE, "B=%d D=%d", B, D);
     if (top_k < 1 || top_k > 32 || n_experts < top_k || n_experts > 4096)
         return fail(DL_ERR_SHAPE, "top_k %d of %d experts", top_k, n_experts);
-    DL_TRY(check_ws(ws, ws_bytes, dl_moe_route_workspace(B, n_experts)));
+    if (D % 4) return fail(DL_ERR_UNSUPPORTED, "router hidden size %d (multiple of 4)", D);
+    DL_TRY(check_ws(ws, ws_bytes, dl_moe_route_workspace(B, D, n_experts)));
     (void)hipGetLastError();
     Ws w(ws);
     double *l64 = w.take<double>((long)B * n_experts);
-    return launch_route(h, B, D, w_r, bias, n_experts, top_k, experts, gates, logits, l64, (hipStream_t)stream);
+    double *part = w.take<double>((long)route_chunks(D) * B * n_experts);
+    return launch_route(h, B, D, w_r, bias, n_experts, top_k, experts, gates, logits, l64, part, (hipStream_t)stream);
 }
 
 size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared)
@@ -534,6 +567,7 @@ static int check_layer(const dl_layer_desc *d, const dl_pages *pg)
     DL_TRY(check_ffn_shapes(pg->batch, d->D, d->inter, d->expert_top_k, d->n_routed, d->n_shared, &d->w_gate,
                             &d->w_up, &d->w_down));
     if (d->out_dt != DL_F32 && d->out_dt != DL_BF16) return fail(DL_ERR_DTYPE, "out dtype %d", d->out_dt);
+    if (d->D % 4) return fail(DL_ERR_UNSUPPORTED, "hidden size %d (multiple of 4)", d->D);
     return DL_OK;
 }
 
@@ -568,13 +602,13 @@ int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_
     DL_TRY(launch_indexer_topk(pg, io->q_idx, io->k_pool, d->idx_heads, d->idx_dim, d->top_k, L.sel, nullptr, L.topk, s));
     mk.at(1);
     DL_TRY(launch_attention(pg, io->q, d->q_dt, io->kv_pool, io->kv_scale, d->kv_dt, d->n_heads, d->d_c, d->d_v,
-                            d->sm_scale, L.sel, d->top_k, L.o, s));
+                            d->sm_scale, L.sel, d->top_k, L.o, L.attn.opart, L.attn.ml, s));
     mk.at(2);
     DL_TRY(run_projection(B, d->n_heads, d->d_v, L.o, d->w_uv.w ? &d->w_uv : nullptr, &d->w_o, io->x, d->q_dt, L.h,
                           L.attn, s));
     mk.at(3);
     DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates, nullptr,
-                        L.logits64, s));
+                        L.logits64, L.rpart, s));
     mk.at(4);
     return run_ffn(L.h, B, d->D, d->inter, L.experts, L.gates, d->expert_top_k, &d->w_gate, &d->w_up, &d->w_down,
                    d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s, mk, io->y32);

@@ -76,6 +76,11 @@ struct GemvArgs {
     // output
     float *out;
     const void *resid; int resid_dt; long r_ts;    // EPI_RESID: resid[t*r_ts + row]
+    // split of K into ksplit chunks of kchunk blocks: raw partial sums go to part[chunk][out offset]
+    // (and part2 for the second SwiGLU matrix), then a reduction applies the epilogue
+    int ksplit, kchunk;
+    float *part, *part2;
+    long n_out;        // elements of the output array (partial buffer stride)
 };
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
 
@@ -84,8 +89,12 @@ int launch_quant(const float *x, long rows_host, const int *rows_dev, int cols, 
                  long q_part, long sc_part, int ns, hipStream_t s);
 
 // ------------------------------------------------------------- attention
+// opart [B, splits, H, Dv] and ml [B, splits, H, 2] are scratch for the matrix-core path.
+bool attention_mfma_ok(int H, int Dc, int Dv, int q_dt, int kv_dt);
+int attention_splits(int top_k);
 int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
-                     int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, hipStream_t s);
+                     int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, float *opart,
+                     float *ml, hipStream_t s);
 
 // ------------------------------------------------------------- MoE
 struct MoePlan {
@@ -97,8 +106,10 @@ struct MoePlan {
     int *pair_tok;   // [B*(ke+S)]
     int *pair_idx;   // [B, ke+S]
 };
+int route_chunks(int D);  // hidden-size chunks of the router's partial dot products
+// logits64 [B, E] and part [route_chunks(D), B, E] are scratch (fp64).
 int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
-                 float *gates, float *logits, double *logits64, hipStream_t s);
+                 float *gates, float *logits, double *logits64, double *part, hipStream_t s);
 int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s);
 int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
                    const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s);

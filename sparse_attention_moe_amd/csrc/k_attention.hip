@@ -5,9 +5,18 @@
 // position shared by all heads ("How was Kiln measured against vLLM on H200?").  The key is the
 // whole latent (d_c features), the value its first d_v features.
 //
-// A workgroup owns HG heads of one row: it resolves the page of every kept position once, scores
-// all of them for its heads (each latent row is decoded once for HG heads), takes an exact fp32
-// softmax, and accumulates the values with 4 consecutive features per thread.
+// Two kernels:
+//  * k_attn_mfma (FP8 latents, bf16 queries, 16 | heads): split over the kept positions like flash
+//    decoding.  A workgroup owns 16 heads of one row and a run of kept positions, staged 64 at a time
+//    into LDS through the page table.  Scores are a [16 heads x 64] x [64 x d_c] product on the matrix
+//    cores (v_mfma_f32_16x16x32_bf16): the queries are bf16 already and every e4m3 code is exactly a
+//    bf16, so the products are exact and each 128-feature block's sum takes its scale once.  The
+//    softmax runs online across chunks in fp32.  For the values, wave w owns a quarter of the d_v
+//    features and computes O^T = C^T P' with P' = p * (block scale) split into bf16 high and low
+//    halves (about 16 significant bits), so the output keeps fp32-level accuracy.  A small kernel
+//    merges the splits (max-rescaled sums).
+//  * k_attn (any shape, fp32 or FP8 latents): a workgroup owns 4 heads of one row and scores every
+//    kept position on the vector units in fp32.
 #include "dl_common.h"
 #include "dl_internal.h"
 
@@ -169,9 +178,250 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q, int q_
     }
 }
 
-int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
-                     int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, hipStream_t s)
+
+// ----------------------------------------------------------------------------- matrix-core path
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+static constexpr int AM_NJ = 64;     // kept positions per chunk (one 16-position tile per wave)
+static constexpr int AM_MAXDC = 1024;
+static constexpr int AM_MAXNB = 8;   // 128-feature blocks of the latent
+
+// 8 e4m3 codes (two dwords) -> 8 bf16, exactly.
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1)
 {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return v8bf{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max16(float v)
+{
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float sum16(float v)
+{
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// grid (nsplit, H/16, B), 256 threads.  opart [B, nsplit, H, Dv] unnormalised sums, ml [B, nsplit, H, 2].
+template <int KQ>  // d_c / 32
+__global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
+                                                   const float *__restrict__ ks, const int32_t *__restrict__ pt,
+                                                   int max_pages, int ps_shift, const int32_t *__restrict__ sel,
+                                                   int top_k, int H, int Dv, float sm_scale, int chunks_per_split,
+                                                   float *__restrict__ opart, float *__restrict__ ml)
+{
+    constexpr int Dc = KQ * 32;
+    constexpr int DCP = Dc + 16;  // padded LDS row: conflict-free 8-byte reads across 16 positions
+    constexpr int NB = (Dc + 127) / 128;
+    __shared__ __attribute__((aligned(16))) uint8_t s_c[AM_NJ * DCP];
+    __shared__ float s_sc[AM_NJ][AM_MAXNB];
+    __shared__ float s_p[16][AM_NJ + 4];
+    __shared__ long s_row[AM_NJ];
+    __shared__ float s_red[4][16];
+    __shared__ float s_m[16], s_l[16], s_alpha[16];
+    const int split = blockIdx.x, h0 = blockIdx.y * 16, b = blockIdx.z;
+    const int nsplit = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    const int ps_mask = (1 << ps_shift) - 1;
+    // queries of this workgroup's 16 heads as A operands (head ln, features kk*32 + lg*8 .. +8)
+    v8bf Aq[KQ];
+    const uint16_t *qr = q + ((long)b * H + h0 + ln) * Dc + lg * 8;
+#pragma unroll
+    for (int kk = 0; kk < KQ; kk++) Aq[kk] = *(const v8bf *)(qr + kk * 32);
+    // value tiles of this wave: features [w*Dv/4, (w+1)*Dv/4)
+    const int vw = Dv >> 2, vt0 = w * (vw >> 4), nvt = vw >> 4;
+    v4f acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (tid < 16) { s_m[tid] = -INFINITY; s_l[tid] = 0.f; }
+    const int jbase = split * chunks_per_split * AM_NJ;
+    for (int ch = 0; ch < chunks_per_split; ch++) {
+        const int j0 = jbase + ch * AM_NJ;
+        if (j0 >= top_k) break;
+        __syncthreads();  // LDS of the previous chunk is no longer read
+        if (tid < AM_NJ) {
+            const int j = j0 + tid;
+            const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
+            const long row = p < 0 ? -1 : ((long)pt[(long)b * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
+            s_row[tid] = row;
+#pragma unroll
+            for (int k = 0; k < NB; k++) s_sc[tid][k] = row < 0 ? 0.f : ks[row * NB + k];
+        }
+        __syncthreads();
+        // gather the chunk's latent codes (16 bytes per load); empty slots become zeros
+        for (int id = tid; id < AM_NJ * (Dc / 16); id += 256) {
+            const int pos = id / (Dc / 16), c16 = id % (Dc / 16);
+            const long row = s_row[pos];
+            v4i v = {0, 0, 0, 0};
+            if (row >= 0) v = *(const v4i *)(kv + row * Dc + c16 * 16);
+            *(v4i *)(s_c + pos * DCP + c16 * 16) = v;
+        }
+        __syncthreads();
+        // scores of the 16 heads for positions w*16 .. w*16+15
+        const int jp = w * 16 + ln;
+        v4f S = {0.f, 0.f, 0.f, 0.f};
+        const uint8_t *cr = s_c + jp * DCP + lg * 8;
+#pragma unroll
+        for (int blk = 0; blk < NB; blk++) {
+            v4f a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = blk * 4; kk < (blk * 4 + 4 < KQ ? blk * 4 + 4 : KQ); kk++) {
+                const uint2 cw = *(const uint2 *)(cr + kk * 32);
+                a = mfma_bf16(Aq[kk], fp8x8_to_bf16(cw.x, cw.y), a);
+            }
+            S += a * s_sc[jp][blk];
+        }
+        const bool valid = s_row[jp] >= 0;
+        float sv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) sv[i] = valid ? S[i] * sm_scale : -INFINITY;
+        // chunk maximum per head (lane holds heads 4*lg+i of position ln)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float m = max16(sv[i]);
+            if (ln == 0) s_red[w][4 * lg + i] = m;
+        }
+        __syncthreads();
+        if (tid < 16) {
+            const float mc = fmaxf(fmaxf(s_red[0][tid], s_red[1][tid]), fmaxf(s_red[2][tid], s_red[3][tid]));
+            const float mo = s_m[tid], mn = fmaxf(mo, mc);
+            s_alpha[tid] = (mn == -INFINITY) ? 1.f : expf(mo - mn);
+            s_m[tid] = mn;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int hh = 4 * lg + i;
+            const float mn = s_m[hh];
+            const float pv = (sv[i] == -INFINITY) ? 0.f : expf(sv[i] - mn);
+            s_p[hh][jp] = pv;
+            const float ssum = sum16(pv);
+            if (ln == 0) s_red[w][hh] = ssum;
+        }
+        __syncthreads();
+        if (tid < 16) s_l[tid] = s_l[tid] * s_alpha[tid] + (s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid]);
+        // values: O^T[v][h] += sum_j C[j][v] * p[h][j] * scale[j][blk(v)], this wave's feature tiles
+        const float al = s_alpha[ln];
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[i] *= al;
+#pragma unroll
+        for (int kk = 0; kk < AM_NJ / 32; kk++) {
+            const int jj = kk * 32 + lg * 8;
+            float pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) pr[e] = s_p[ln][jj + e];
+            int cur_blk = -1;
+            v8bf Bh, Bl;
+#pragma unroll
+            for (int t = 0; t < 8; t++) {
+                if (t >= nvt) break;
+                const int v0 = (vt0 + t) * 16;
+                const int blk = v0 >> 7;
+                if (blk != cur_blk) {
+                    cur_blk = blk;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const float x = pr[e] * s_sc[jj + e][blk];
+                        const __bf16 hi = (__bf16)x;
+                        Bh[e] = hi;
+                        Bl[e] = (__bf16)(x - (float)hi);
+                    }
+                }
+                // A: codes of positions jj..jj+7 at feature v0 + ln
+                const uint8_t *cc = s_c + jj * DCP + v0 + ln;
+                uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    w0 |= (uint32_t)cc[e * DCP] << (8 * e);
+                    w1 |= (uint32_t)cc[(e + 4) * DCP] << (8 * e);
+                }
+                const v8bf Av = fp8x8_to_bf16(w0, w1);
+                acc[t] = mfma_bf16(Av, Bh, acc[t]);
+                acc[t] = mfma_bf16(Av, Bl, acc[t]);
+            }
+        }
+    }
+    __syncthreads();
+    // partial sums: lane holds O^T[v = tile*16 + 4*lg + i][head ln]
+    float *op = opart + (((long)b * nsplit + split) * H + h0 + ln) * Dv;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        if (t >= nvt) break;
+        *(v4f *)(op + (vt0 + t) * 16 + 4 * lg) = acc[t];
+    }
+    if (tid < 16) {
+        float *m2 = ml + (((long)b * nsplit + split) * H + h0 + tid) * 2;
+        m2[0] = s_m[tid];
+        m2[1] = s_l[tid];
+    }
+}
+
+// o[b, h, v] = sum_s e^(m_s - M) O_s[v] / sum_s e^(m_s - M) l_s, splits merged in order.
+__global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ opart, const float *__restrict__ ml,
+                                                    int nsplit, int H, int Dv, float *__restrict__ o)
+{
+    const int bh = blockIdx.x;  // b*H + h
+    const int b = bh / H, h = bh % H;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < nsplit; s2++) M = fmaxf(M, ml[(((long)b * nsplit + s2) * H + h) * 2]);
+    float den = 0.f;
+    for (int s2 = 0; s2 < nsplit; s2++) {
+        const float m = ml[(((long)b * nsplit + s2) * H + h) * 2];
+        if (m != -INFINITY) den += expf(m - M) * ml[(((long)b * nsplit + s2) * H + h) * 2 + 1];
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    for (int v = threadIdx.x; v < Dv; v += 256) {
+        float num = 0.f;
+        for (int s2 = 0; s2 < nsplit; s2++) {
+            const float m = ml[(((long)b * nsplit + s2) * H + h) * 2];
+            if (m == -INFINITY) continue;
+            num += expf(m - M) * opart[(((long)b * nsplit + s2) * H + h) * Dv + v];
+        }
+        o[(long)bh * Dv + v] = num * inv;
+    }
+}
+
+bool attention_mfma_ok(int H, int Dc, int Dv, int q_dt, int kv_dt)
+{
+    return kv_dt == DL_FP8_E4M3 && q_dt == DL_BF16 && H % 16 == 0 && (Dc == 576 || Dc == 512 || Dc == 256 ||
+           Dc == 128) && Dv % 64 == 0 && Dv / 4 <= 128 && Dv <= Dc;
+}
+
+static constexpr int AM_CHUNKS = 4;  // chunks per split: 256 kept positions per workgroup
+
+int attention_splits(int top_k) { return (top_k + AM_NJ * AM_CHUNKS - 1) / (AM_NJ * AM_CHUNKS); }
+
+int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
+                     int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, float *opart,
+                     float *ml, hipStream_t s)
+{
+    if (attention_mfma_ok(H, Dc, Dv, q_dt, kv_dt) && opart && ml) {
+        const int ps_shift = __builtin_ctz((unsigned)pg.page_size);
+        const int nsplit = attention_splits(top_k);
+        dim3 g(nsplit, H / 16, pg.batch);
+#define DL_AM(KQ_)                                                                                                  \
+    if (Dc == KQ_ * 32)                                                                                             \
+        hipLaunchKernelGGL((k_attn_mfma<KQ_>), g, dim3(256), 0, s, (const uint16_t *)q, (const uint8_t *)kv, kv_scale, \
+                           pg.page_table, pg.max_pages_per_seq, ps_shift, sel, top_k, H, Dv, sm_scale, AM_CHUNKS,    \
+                           opart, ml);
+        DL_AM(18) DL_AM(16) DL_AM(8) DL_AM(4)
+#undef DL_AM
+        hipLaunchKernelGGL(k_attn_merge, dim3(pg.batch * H), dim3(256), 0, s, opart, ml, nsplit, H, Dv, o);
+        return hip_check("attention_mfma");
+    }
     if (top_k > ATT_MAX_K || Dc > ATT_MAX_DC) return fail(DL_ERR_UNSUPPORTED, "attention top_k %d / d_c %d", top_k, Dc);
     if (Dv % 4 || (256 % (Dv / 4))) return fail(DL_ERR_UNSUPPORTED, "attention d_v %d (power of two 4..1024)", Dv);
     if (Dc % 4) return fail(DL_ERR_UNSUPPORTED, "attention d_c %d", Dc);

@@ -68,10 +68,13 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
     const int nwaves = gridDim.x * 4;
     const int n_act = a.n_active_dev ? *a.n_active_dev : a.n_active_host;
     const int tiles = a.rows >> 4;
-    const long total = (long)n_act * tiles * a.max_groups;
-    for (long item = wave; item < total; item += nwaves) {
+    const long total = (long)n_act * tiles * a.max_groups * a.ksplit;
+    for (long item0 = wave; item0 < total; item0 += nwaves) {
+        const int kc = (int)(item0 % a.ksplit);
+        const long item = item0 / a.ksplit;
         ItemInfo it;
         if (!decode_item(a, item, tiles, it)) continue;
+        const int kb0 = kc * a.kchunk, kb1 = min(a.nkb, kb0 + a.kchunk);
         const int tt = it.t0 + ln;
         const bool tv = tt < it.cnt;
         long arow = 0;
@@ -85,8 +88,7 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
         const uint8_t *ap = a.aq + arow * a.cols + lg * 32;
         const float *asp = a.asc + arow * a.nkb;
         v4f tot = {0.f, 0.f, 0.f, 0.f}, tot2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int kb = 0; kb < a.nkb; kb++) {
+        for (int kb = kb0; kb < kb1; kb++) {
             const v8i A = ld32(wp + kb * 128);
             v8i A2;
             if (SW) A2 = ld32(wp2 + kb * 128);
@@ -112,6 +114,12 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
         }
         if (!tv) continue;
         const long ooff = a.tok_cnt ? (long)(it.off + tt) * a.o_ts : (long)tt * a.o_ts + (long)it.m * a.o_ms;
+        if (a.ksplit > 1) {
+            float *p = a.part + (long)kc * a.n_out + ooff + it.r0 + 4 * lg;
+            *(v4f *)p = tot;
+            if (SW) *(v4f *)(a.part2 + (long)kc * a.n_out + ooff + it.r0 + 4 * lg) = tot2;
+            continue;
+        }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int r = it.r0 + 4 * lg + i;
@@ -121,6 +129,24 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
             a.out[ooff + r] = v;
         }
     }
+}
+
+// Sum of the K-chunk partials in chunk order, then the epilogue.  EPI_RESID here needs the residual laid
+// out like the output (r_ts == o_ts, uniform mode with one matrix).
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemv_reduce(GemvArgs a)
+{
+    constexpr bool SW = EPI == EPI_SWIGLU;
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= a.n_out) return;
+    float v = 0.f, v2 = 0.f;
+    for (int kc = 0; kc < a.ksplit; kc++) {
+        v += a.part[(long)kc * a.n_out + e];
+        if (SW) v2 += a.part2[(long)kc * a.n_out + e];
+    }
+    if (EPI == EPI_RESID) v += act_load(a.resid, a.resid_dt, e);
+    if (SW) v = silu(v) * v2;
+    a.out[e] = v;
 }
 
 // fp32 weights: one wave per (matrix, row, token group); lanes split the columns.
@@ -228,14 +254,22 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
     // upper bound of the item count (device-side counts can only be smaller)
     const long n_act = a.n_active_host;
     if (fp8) {
-        const long items = n_act * (a.rows / 16) * a.max_groups;
+        const long items = n_act * (a.rows / 16) * a.max_groups * a.ksplit;
         const dim3 g(grid_for(items, 4, 2048));
+        bool done = false;
 #define DL_G(NS_, E_) \
-    if (ns == NS_ && epi == E_) { hipLaunchKernelGGL((k_gemv_fp8<NS_, E_>), g, dim3(256), 0, s, a); return hip_check("gemv_fp8"); }
+    if (!done && ns == NS_ && epi == E_) { hipLaunchKernelGGL((k_gemv_fp8<NS_, E_>), g, dim3(256), 0, s, a); done = true; }
         DL_G(2, EPI_STORE) DL_G(2, EPI_RESID) DL_G(2, EPI_SWIGLU)
         DL_G(4, EPI_STORE) DL_G(4, EPI_RESID) DL_G(4, EPI_SWIGLU)
 #undef DL_G
-        return fail(DL_ERR_UNSUPPORTED, "gemv parts=%d", ns);
+        if (!done) return fail(DL_ERR_UNSUPPORTED, "gemv parts=%d", ns);
+        if (a.ksplit > 1) {
+            const dim3 gr((unsigned)((a.n_out + 255) / 256));
+            if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemv_reduce<EPI_STORE>), gr, dim3(256), 0, s, a);
+            else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv_reduce<EPI_RESID>), gr, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_gemv_reduce<EPI_SWIGLU>), gr, dim3(256), 0, s, a);
+        }
+        return hip_check("gemv_fp8");
     }
     const long items = n_act * a.rows * a.max_groups;
     const dim3 g(grid_for(items, 4, 4096));

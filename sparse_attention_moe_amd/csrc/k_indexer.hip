@@ -42,36 +42,67 @@ __device__ __forceinline__ void bin1_range(int b, int &lo, int &hi)
     hi = lo + (1 << (n - 7)) - 1;
 }
 
-// Largest bin b with (count of bins >= b) >= k, and the count strictly above it.
-// Called by all 256 threads of the deciding workgroup; reads the histogram coherently.
-__device__ void block_pick(const unsigned *hist, int nbins, int k, int *s_tmp, int &bin_out, int &above_out)
+// Inclusive scan of one int across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v)
 {
-    const int tid = threadIdx.x;
-    const int per = (nbins + 255) / 256;
-    // thread t owns bins [t*per, (t+1)*per); suffix sums from the top
-    int seg = 0;
-    for (int i = 0; i < per; i++) {
-        int b = tid * per + i;
-        if (b < nbins) seg += (int)ld_agent_u(hist + b);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
     }
-    s_tmp[tid] = seg;
+    return v;
+}
+
+// Largest bin b with (count of bins >= b) >= k, and the count strictly above it.  Called by all 256
+// threads of the deciding workgroup: the histogram is copied into LDS with coherent loads (all in flight
+// at once), the 256 segment sums are suffix-scanned, and the one thread whose segment holds the k-th
+// largest score walks it.
+template <int NBINS>
+__device__ void block_pick(const unsigned *gh, unsigned *sh, int k, int *s_tmp, int &bin_out, int &above_out)
+{
+    constexpr int PER = (NBINS + 255) / 256;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int b = i * 256 + tid;
+        v[i] = b < NBINS ? ld_agent_u(gh + b) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int b = i * 256 + tid;
+        if (b < NBINS) sh[b] = v[i];
+    }
     __syncthreads();
-    if (tid == 0) {
-        int cum = 0, t = 255;
-        for (; t >= 0; t--) {
-            if (cum + s_tmp[t] >= k) break;
-            cum += s_tmp[t];
-        }
-        int bin = 0, above = cum;
-        if (t >= 0) {
-            for (int b = min(nbins, (t + 1) * per) - 1; b >= t * per; b--) {
-                int h = (int)ld_agent_u(hist + b);
-                if (cum + h >= k) { bin = b; above = cum; break; }
-                cum += h;
-            }
+    // thread tid owns segment t = 255 - tid (bins [t*PER, (t+1)*PER)), so a prefix scan over tid is a
+    // suffix scan over the bins
+    const int t = 255 - tid;
+    int seg = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int b = t * PER + i;
+        if (b < NBINS) seg += (int)sh[b];
+    }
+    int inc = wave_incl_scan(seg);
+    if (lane == 63) s_tmp[wave] = inc;
+    if (tid == 0) { s_tmp[256] = 0; s_tmp[257] = 0; }
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; w++) before += s_tmp[w];
+    inc += before;
+    const int exc = inc - seg;  // bins above my segment
+    if (inc >= k && exc < k) {
+        int cum = exc, bin = t * PER;
+        for (int i = PER - 1; i >= 0; i--) {
+            const int b = t * PER + i;
+            if (b >= NBINS) continue;
+            const int hcount = (int)sh[b];
+            if (cum + hcount >= k) { bin = b; break; }
+            cum += hcount;
         }
         s_tmp[256] = bin;
-        s_tmp[257] = above;
+        s_tmp[257] = cum;
     }
     __syncthreads();
     bin_out = s_tmp[256];
@@ -199,7 +230,7 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
         return;
     }
     int bin, above;
-    block_pick(gh, NB1, top_k, s_tmp, bin, above);
+    block_pick<NB1>(gh, s_hist, top_k, s_tmp, bin, above);
     if (tid == 0) {
         int lo, hi;
         bin1_range(bin, lo, hi);
@@ -248,7 +279,7 @@ __global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ 
     }
     if (!last_block(ticket + b, nblk, &s_tmp[258])) return;
     int bin, above;
-    block_pick(gh, NB2, top_k - s0.above, s_tmp, bin, above);
+    block_pick<NB2>(gh, s_hist, top_k - s0.above, s_tmp, bin, above);
     for (int i = tid; i < NB2; i += 256) gh[i] = 0;  // ready for the next pass
     if (tid == 0) {
         SelState s = s0;
@@ -305,18 +336,6 @@ __global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ s
         cnt[o] = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
         cnt[o + 1] = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
     }
-}
-
-// Inclusive scan of one int across the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v)
-{
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-    }
-    return v;
 }
 
 // Ordered compaction of the kept positions of one chunk.

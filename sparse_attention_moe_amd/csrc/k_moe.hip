@@ -10,48 +10,86 @@
 
 namespace dl {
 
-static constexpr int ROUTE_TOK = 16;
+static constexpr int ROUTE_EXP = 4;    // experts per wave
+static constexpr int ROUTE_TOK = 8;    // tokens per wave pass
+static constexpr int ROUTE_KC = 1024;  // hidden features per wave (16 per lane)
 
-// logits64[b, e] = w_r[e] . h[b] + bias[e]: one wave per expert, 16 tokens per workgroup column.
-__global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ h, int B, int D,
-                                                      const float *__restrict__ wr, const float *__restrict__ bias,
-                                                      int E, double *__restrict__ logits64, float *__restrict__ logits)
+// Partial router logits: part[c, b, e] = sum over hidden chunk c of w_r[e, d] * h[b, d], with the fp32
+// products formed exactly in fp64 and summed in fp64.  One wave per (4 experts, chunk, 8 tokens); each lane
+// owns 16 consecutive features, so the w_r rows stream once with 16-byte loads.
+__global__ __launch_bounds__(64) void k_route_partial(const float *__restrict__ h, int B, int D,
+                                                      const float *__restrict__ wr, int E,
+                                                      double *__restrict__ part)
 {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int b0 = blockIdx.y * ROUTE_TOK;
-    if (e >= E) return;
+    const int lane = threadIdx.x;
+    const int e0 = blockIdx.x * ROUTE_EXP;
+    const int c = blockIdx.y;
+    const int b0 = blockIdx.z * ROUTE_TOK;
+    const int d0 = c * ROUTE_KC + lane * 16;
     const int nt = min(ROUTE_TOK, B - b0);
-    double acc[ROUTE_TOK];
+    double w[ROUTE_EXP][16];
 #pragma unroll
-    for (int t = 0; t < ROUTE_TOK; t++) acc[t] = 0.0;
-    const float *w = wr + (long)e * D;
-    for (int d = lane; d < D; d += 64) {
-        const double wv = (double)w[d];
+    for (int x = 0; x < ROUTE_EXP; x++) {
+        const int e = e0 + x;
 #pragma unroll
-        for (int t = 0; t < ROUTE_TOK; t++)
-            if (t < nt) acc[t] = fma(wv, (double)h[(long)(b0 + t) * D + d], acc[t]);
+        for (int q = 0; q < 4; q++) {
+            const int d = d0 + q * 4;
+            v4f v = {0.f, 0.f, 0.f, 0.f};
+            if (e < E && d < D) v = *(const v4f *)(wr + (long)e * D + d);
+#pragma unroll
+            for (int i = 0; i < 4; i++) w[x][q * 4 + i] = (double)v[i];
+        }
     }
-    const double bv = bias ? (double)bias[e] : 0.0;
+    double acc[ROUTE_EXP][ROUTE_TOK];
+#pragma unroll
+    for (int x = 0; x < ROUTE_EXP; x++)
+#pragma unroll
+        for (int t = 0; t < ROUTE_TOK; t++) acc[x][t] = 0.0;
 #pragma unroll
     for (int t = 0; t < ROUTE_TOK; t++) {
         if (t >= nt) break;
-        const double v = wave_sum_d(acc[t]) + bv;
-        if (lane == 0) {
-            logits64[(long)(b0 + t) * E + e] = v;
-            if (logits) logits[(long)(b0 + t) * E + e] = (float)v;
+        const float *hr = h + (long)(b0 + t) * D;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int d = d0 + q * 4;
+            v4f v = {0.f, 0.f, 0.f, 0.f};
+            if (d < D) v = *(const v4f *)(hr + d);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const double hv = (double)v[i];
+#pragma unroll
+                for (int x = 0; x < ROUTE_EXP; x++) acc[x][t] = fma(w[x][q * 4 + i], hv, acc[x][t]);
+            }
         }
     }
+#pragma unroll
+    for (int x = 0; x < ROUTE_EXP; x++)
+#pragma unroll
+        for (int t = 0; t < ROUTE_TOK; t++) {
+            if (t >= nt) break;
+            const double v = wave_sum_d(acc[x][t]);
+            if (lane == 0 && e0 + x < E) part[((long)c * B + b0 + t) * E + e0 + x] = v;
+        }
 }
 
 // Top-k experts per token by (logit desc, id asc) and their softmax gates; one wave per token.
-__global__ __launch_bounds__(256) void k_route_topk(const double *__restrict__ logits64, int B, int E, int ke,
-                                                    int32_t *__restrict__ experts, float *__restrict__ gates)
+__global__ __launch_bounds__(256) void k_route_topk(const double *__restrict__ part, int nchunk, int B, int E, int ke,
+                                                    const float *__restrict__ bias, int32_t *__restrict__ experts,
+                                                    float *__restrict__ gates, float *__restrict__ logits,
+                                                    double *__restrict__ logits64)
 {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (b >= B) return;
-    const double *l = logits64 + (long)b * E;
+    double *l = logits64 + (long)b * E;
+    // logits = chunk partials summed in chunk order, plus the bias
+    for (int e = lane; e < E; e += 64) {
+        double v = 0.0;
+        for (int c = 0; c < nchunk; c++) v += part[((long)c * B + b) * E + e];
+        if (bias) v += (double)bias[e];
+        l[e] = v;
+        if (logits) logits[(long)b * E + e] = (float)v;
+    }
     // taken[] as a bitmask over this lane's experts e = lane + 64*i
     unsigned long long taken = 0;
     double sel_l[32];
@@ -193,12 +231,16 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, co
     else ((float *)out)[(long)b * D + d] = acc;
 }
 
+int route_chunks(int D) { return (D + ROUTE_KC - 1) / ROUTE_KC; }
+
 int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
-                 float *gates, float *logits, double *logits64, hipStream_t s)
+                 float *gates, float *logits, double *logits64, double *part, hipStream_t s)
 {
-    dim3 g((E + 3) / 4, (B + ROUTE_TOK - 1) / ROUTE_TOK);
-    hipLaunchKernelGGL(k_route_logits, g, dim3(256), 0, s, h, B, D, w_r, bias, E, logits64, logits);
-    hipLaunchKernelGGL(k_route_topk, dim3((B + 3) / 4), dim3(256), 0, s, logits64, B, E, ke, experts, gates);
+    const int nc = route_chunks(D);
+    dim3 g((E + ROUTE_EXP - 1) / ROUTE_EXP, nc, (B + ROUTE_TOK - 1) / ROUTE_TOK);
+    hipLaunchKernelGGL(k_route_partial, g, dim3(64), 0, s, h, B, D, w_r, E, part);
+    hipLaunchKernelGGL(k_route_topk, dim3((B + 3) / 4), dim3(256), 0, s, part, nc, B, E, ke, bias, experts, gates,
+                       logits, logits64);
     return hip_check("route");
 }
 
