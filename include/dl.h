@@ -128,7 +128,7 @@ int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_
  *   w_o      nullable; rows = D, cols = n_heads * (w_uv ? head_dim : d_v)
  *   residual bf16 or fp32 [B, D] (required with w_o)
  *   out      fp32 [B, n_heads, d_v] (no w_o) or fp32 [B, D]
- * Limits: d_v <= d_c <= 1024; FP8 weights need rows % 16 == 0 and cols % 128 == 0.
+ * Limits: d_v <= d_c <= 1024; FP8 weights need rows % 32 == 0 and cols % 128 == 0.
  * Workspace: dl_sparse_attn_workspace(...). */
 size_t dl_sparse_attn_workspace(int32_t batch, int32_t n_heads, int32_t d_v, int32_t top_k, const dl_mat *w_uv,
                                 const dl_mat *w_o);

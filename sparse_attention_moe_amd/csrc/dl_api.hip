@@ -28,6 +28,24 @@ int hip_check(const char *what)
     return DL_OK;
 }
 
+int resident_blocks(const void *kernel, int threads)
+{
+    // per device and kernel; the few kernels of the library make a tiny linear cache enough
+    struct Entry { int dev; const void *k; int blocks; };
+    static thread_local Entry cache[64];
+    static thread_local int n = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    for (int i = 0; i < n; i++)
+        if (cache[i].dev == dev && cache[i].k == kernel) return cache[i].blocks;
+    int per_cu = 1, cus = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    const int blocks = per_cu * cus;
+    if (n < 64) cache[n++] = Entry{dev, kernel, blocks};
+    return blocks;
+}
+
 #define DL_TRY(x)              \
     do {                       \
         int _r = (x);          \
@@ -97,7 +115,7 @@ static int check_mat(const dl_mat *m, const char *name, int count, int rows, int
                     cols);
     if (m->dtype == DL_FP8_E4M3) {
         if (!m->scale) return fail(DL_ERR_NULL, "%s: FP8 needs block scales", name);
-        if (rows % 16 || cols % 128) return fail(DL_ERR_UNSUPPORTED, "%s: FP8 needs rows%%16==0, cols%%128==0", name);
+        if (rows % 32 || cols % 128) return fail(DL_ERR_UNSUPPORTED, "%s: FP8 needs rows%%32==0, cols%%128==0", name);
     } else if (m->dtype == DL_F32) {
         if (m->scale) return fail(DL_ERR_DTYPE, "%s: fp32 weights take no scale", name);
     } else {
@@ -255,9 +273,12 @@ static int run_projection(int B, int H, int Dv, const float *o, const dl_mat *w_
 }
 
 // ------------------------------------------------------------------ FFN
+static constexpr int GU_KSPLIT = 2;  // K chunks of the FP8 gate/up pass (balances the waves' work)
+
 struct FfnWs {
     MoePlan plan;
     uint8_t *hq; float *hqs;   // 2 parts of h  [2][B][D]
+    float *gpart, *upart;      // [GU_KSPLIT, P, I] gate/up partial sums (FP8 path)
     float *Z;                  // [P, I]
     uint8_t *zq; float *zqs;   // 2 parts of Z
     float *F;                  // [P, D]
@@ -269,6 +290,7 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
     const long P = (long)B * (ke + S);
     f.plan.n_active = w.take<int>(1);
     f.plan.n_pairs = w.take<int>(1);
+    f.plan.n_groups = w.take<int>(1);
     f.plan.active = w.take<int>(NE);
     f.plan.tok_off = w.take<int>(NE);
     f.plan.tok_cnt = w.take<int>(NE);
@@ -280,7 +302,10 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
         f.hqs = w.take<float>((long)FFN_PARTS * B * (D / 128));
     }
     f.Z = w.take<float>(P * I);
+    f.gpart = f.upart = nullptr;
     if (fp8) {
+        f.gpart = w.take<float>((long)GU_KSPLIT * P * I);
+        f.upart = w.take<float>((long)GU_KSPLIT * P * I);
         f.zq = w.take<uint8_t>((long)FFN_PARTS * P * I);
         f.zqs = w.take<float>((long)FFN_PARTS * P * (I / 128));
     }
@@ -307,12 +332,21 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     g.tok_off = f.plan.tok_off;
     g.tok_cnt = f.plan.tok_cnt;
     g.max_groups = (B + 15) / 16;
+    g.groups_dev = f.plan.n_groups;
     g.pair_act = f.plan.pair_tok;
     g.o_ts = I;
     g.out = f.Z;
     if (f8) {
         DL_TRY(launch_quant(h, B, nullptr, D, f.hq, f.hqs, (long)B * D, (long)B * (D / 128), FFN_PARTS, s));
         g.aq = f.hq; g.asc = f.hqs; g.aq_part = (long)B * D; g.asc_part = (long)B * (D / 128);
+        if (g.nkb % GU_KSPLIT == 0) {
+            g.ksplit = GU_KSPLIT;
+            g.kchunk = g.nkb / GU_KSPLIT;
+            g.part = f.gpart;
+            g.part2 = f.upart;
+            g.n_out = P * I;
+            g.reduce_in_consumer = true;
+        }
     } else {
         g.af = h;
     }
@@ -327,11 +361,16 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     d.tok_off = f.plan.tok_off;
     d.tok_cnt = f.plan.tok_cnt;
     d.max_groups = (B + 15) / 16;
+    d.groups_dev = f.plan.n_groups;
     d.pair_act = nullptr;  // Z rows are per pair
     d.o_ts = D;
     d.out = f.F;
     if (f8) {
-        DL_TRY(launch_quant(f.Z, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I, P * (I / 128), FFN_PARTS, s));
+        if (g.ksplit > 1)
+            DL_TRY(launch_swiglu_quant(f.gpart, f.upart, g.ksplit, P * I, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I,
+                                       P * (I / 128), FFN_PARTS, s));
+        else
+            DL_TRY(launch_quant(f.Z, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I, P * (I / 128), FFN_PARTS, s));
         d.aq = f.zq; d.asc = f.zqs; d.aq_part = P * I; d.asc_part = P * (I / 128);
     } else {
         d.af = f.Z;

@@ -11,6 +11,8 @@ namespace dl {
 // Sets the thread's last-error message and returns `st`.
 int fail(int st, const char *fmt, ...);
 int hip_check(const char *what);  // DL_OK or DL_ERR_HIP after a launch
+// Workgroups of `threads` threads of `kernel` resident on the current device at once (cached).
+int resident_blocks(const void *kernel, int threads);
 
 // Carves 256-byte-aligned regions out of a workspace.  With base == nullptr it only measures.
 struct Ws {
@@ -29,7 +31,7 @@ struct Ws {
 };
 
 // ------------------------------------------------------------- indexer + top-k
-struct SelState {      // per row, in the workspace
+struct SelState {      // per row and pass, in the workspace
     int lo, hi;        // the threshold score T lies in [lo, hi]
     int above;         // number of scores > hi
     int done;          // 1: T == lo == hi is final
@@ -41,9 +43,8 @@ struct SelState {      // per row, in the workspace
 struct TopkWs {
     int32_t *scores;   // [B, Lmax]
     unsigned *hist1;   // [B, NB1]
-    unsigned *hist2;   // [B, NB2]
-    int *ticket;       // [B]
-    SelState *state;   // [B]
+    unsigned *hist2;   // [2, B, NB2]
+    SelState *state;   // [4, B]
     int *cnt;          // [B, nchunk, 2]
 };
 void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t);
@@ -66,6 +67,7 @@ struct GemvArgs {
     const int *tok_off, *tok_cnt;  // plan mode: pairs of slot u are [tok_off[u], +tok_cnt[u])
     int ntok_host;                 // uniform mode: tokens 0..ntok-1 for every matrix
     int max_groups;                // upper bound of ceil(tokens per matrix / 16)
+    const int *groups_dev;         // plan mode: device value of that bound (nullptr: max_groups)
     const int *pair_act;           // plan mode: activation row of global pair p
     int a_ts, a_ms;                // uniform mode: activation row = t*a_ts + m*a_ms
     long o_ts, o_ms;               // output offset = t*o_ts + m*o_ms (uniform) or p*o_ts (plan)
@@ -81,9 +83,14 @@ struct GemvArgs {
     int ksplit, kchunk;
     float *part, *part2;
     long n_out;        // elements of the output array (partial buffer stride)
+    bool reduce_in_consumer;  // the next kernel sums the partials itself (no reduction launch)
 };
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
 
+// SwiGLU of summed gate/up K-chunk partials, split into NS FP8 parts (rows may come from the device).
+int launch_swiglu_quant(const float *pg, const float *pu, int ksplit, long stride, long rows_host,
+                        const int *rows_dev, int cols, uint8_t *q, float *sc, long q_part, long sc_part, int ns,
+                        hipStream_t s);
 // x fp32 rows -> NS FP8 parts with one dynamic scale per (part, row, 128 block).
 int launch_quant(const float *x, long rows_host, const int *rows_dev, int cols, uint8_t *q, float *sc,
                  long q_part, long sc_part, int ns, hipStream_t s);
@@ -100,6 +107,7 @@ int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv
 struct MoePlan {
     int *n_active;   // [1]
     int *n_pairs;    // [1]
+    int *n_groups;   // [1] max over active experts of ceil(tokens / 16)
     int *active;     // [NE]
     int *tok_off;    // [NE]
     int *tok_cnt;    // [NE]

@@ -36,98 +36,150 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-struct ItemInfo {
-    int m, off, cnt, t0, r0;
+// Work item: (active matrix u, RT*16-row tile, group of 16 tokens, K chunk), numbered with the K chunk
+// fastest, then the token group, then the tile, then u.  Each wave owns one contiguous, equal share of the
+// items, so consecutive items almost always belong to the same matrix and token set (no new metadata),
+// and the load pipeline runs on across item boundaries.
+template <int NS, bool SW, int RT>
+struct Stage {
+    v8i A[RT], A2[RT];
+    v8i Bv[NS];
+    float as[NS];
 };
 
-__device__ __forceinline__ bool decode_item(const GemvArgs &a, long item, int tiles, ItemInfo &it)
+template <int RT>
+struct Ctx {
+    int u, m, cnt, off, t0, r0, kc, kb0, kb1;
+    bool valid, tv;
+    int tt;
+    const uint8_t *wp, *wp2, *ap;
+    const float *wsp, *wsp2, *asp;
+};
+
+template <int NS, bool SW, int RT>
+__device__ __forceinline__ void load_stage(Stage<NS, SW, RT> &st, const Ctx<RT> &c, long cols, long aq_part,
+                                           long asc_part, int kb)
 {
-    const int g = (int)(item % a.max_groups);
-    const long t2 = item / a.max_groups;
-    const int tile = (int)(t2 % tiles);
-    const int u = (int)(t2 / tiles);
-    it.m = a.active ? a.active[u] : u;
-    if (a.tok_cnt) {
-        it.cnt = a.tok_cnt[u];
-        it.off = a.tok_off[u];
-    } else {
-        it.cnt = a.ntok_host;
-        it.off = 0;
+#pragma unroll
+    for (int r = 0; r < RT; r++) {
+        st.A[r] = ld32(c.wp + r * 16 * cols + kb * 128);
+        if (SW) st.A2[r] = ld32(c.wp2 + r * 16 * cols + kb * 128);
     }
-    it.t0 = g * 16;
-    it.r0 = tile * 16;
-    return it.t0 < it.cnt;
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        st.Bv[s] = ld32(c.ap + s * aq_part + kb * 128);
+        st.as[s] = c.asp[s * asc_part + kb];
+    }
 }
 
-template <int NS, int EPI>
+// Item -> context.  Reuses `prev` (same matrix and token group) when possible: then no memory is read.
+template <int RT, bool SW>
+__device__ __forceinline__ void make_ctx(const GemvArgs &a, int item, int groups, int tiles, const Ctx<RT> *prev,
+                                         Ctx<RT> &c)
+{
+    const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+    const int kc = item % a.ksplit;
+    int r = item / a.ksplit;
+    const int g = r % groups;
+    r /= groups;
+    const int tile = r % tiles;
+    const int u = r / tiles;
+    if (prev && prev->u == u && prev->t0 == g * 16) {
+        c = *prev;
+    } else {
+        c.u = u;
+        c.m = __builtin_amdgcn_readfirstlane(a.active ? a.active[u] : u);
+        c.cnt = a.tok_cnt ? a.tok_cnt[u] : a.ntok_host;
+        c.off = a.tok_cnt ? a.tok_off[u] : 0;
+        c.t0 = g * 16;
+        c.valid = c.t0 < c.cnt;
+        c.tt = c.t0 + ln;
+        c.tv = c.tt < c.cnt;
+        // lanes past the last token read the first token's row and get a zero scale (no branches)
+        const int ts = c.tv ? c.tt : c.t0;
+        const long arow = !c.valid ? 0
+                          : a.pair_act ? a.pair_act[c.off + ts]
+                          : a.tok_cnt  ? (long)(c.off + ts)
+                                       : (long)ts * a.a_ts + (long)c.m * a.a_ms;
+        c.ap = a.aq + arow * a.cols + lg * 32;
+        c.asp = a.asc + arow * a.nkb;
+    }
+    c.kc = kc;
+    c.r0 = tile * 16 * RT;
+    c.kb0 = kc * a.kchunk;
+    c.kb1 = min(a.nkb, c.kb0 + a.kchunk);
+    const long wrow = (long)c.m * a.mat_elems + (long)(c.r0 + ln) * a.cols + lg * 32;
+    c.wp = a.w + wrow;
+    c.wp2 = SW ? a.w2 + wrow : nullptr;
+    const long sbase = ((long)c.m * a.nrb + (c.r0 >> 7)) * a.nkb;
+    c.wsp = a.wsc + sbase;
+    c.wsp2 = SW ? a.wsc2 + sbase : nullptr;
+}
+
+template <int NS, int EPI, int RT>
 __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
 {
     constexpr bool SW = EPI == EPI_SWIGLU;
-    const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+    const int lane = threadIdx.x & 63, lg = lane >> 4;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * 4;
     const int n_act = a.n_active_dev ? *a.n_active_dev : a.n_active_host;
-    const int tiles = a.rows >> 4;
-    const long total = (long)n_act * tiles * a.max_groups * a.ksplit;
-    for (long item0 = wave; item0 < total; item0 += nwaves) {
-        const int kc = (int)(item0 % a.ksplit);
-        const long item = item0 / a.ksplit;
-        ItemInfo it;
-        if (!decode_item(a, item, tiles, it)) continue;
-        const int kb0 = kc * a.kchunk, kb1 = min(a.nkb, kb0 + a.kchunk);
-        const int tt = it.t0 + ln;
-        const bool tv = tt < it.cnt;
-        long arow = 0;
-        if (tv) arow = a.pair_act ? a.pair_act[it.off + tt] : a.tok_cnt ? (long)(it.off + tt) : (long)tt * a.a_ts + (long)it.m * a.a_ms;
-        const long wrow = (long)it.m * a.mat_elems + (long)(it.r0 + ln) * a.cols + lg * 32;
-        const uint8_t *wp = a.w + wrow;
-        const uint8_t *wp2 = SW ? a.w2 + wrow : nullptr;
-        const long sbase = ((long)it.m * a.nrb + (it.r0 >> 7)) * a.nkb;
-        const float *wsp = a.wsc + sbase;
-        const float *wsp2 = SW ? a.wsc2 + sbase : nullptr;
-        const uint8_t *ap = a.aq + arow * a.cols + lg * 32;
-        const float *asp = a.asc + arow * a.nkb;
-        v4f tot = {0.f, 0.f, 0.f, 0.f}, tot2 = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = kb0; kb < kb1; kb++) {
-            const v8i A = ld32(wp + kb * 128);
-            v8i A2;
-            if (SW) A2 = ld32(wp2 + kb * 128);
-            v8i Bv[NS];
-            float as[NS];
+    const int groups = a.groups_dev ? *a.groups_dev : a.max_groups;
+    const int tiles = a.rows / (16 * RT);
+    const int total = n_act * tiles * groups * a.ksplit;
+    const int i0 = (int)((long)wave * total / nwaves), i1 = (int)((long)(wave + 1) * total / nwaves);
+    if (i0 >= i1) return;
+    Ctx<RT> c, n;
+    make_ctx<RT, SW>(a, i0, groups, tiles, nullptr, c);
+    Stage<NS, SW, RT> cur, nxt;
+    if (c.valid) load_stage<NS, SW, RT>(cur, c, a.cols, a.aq_part, a.asc_part, c.kb0);
+    for (int it = i0; it < i1; it++) {
+        const bool more = it + 1 < i1;
+        if (more) make_ctx<RT, SW>(a, it + 1, groups, tiles, &c, n);
+        if (c.valid) {
+            v4f tot[RT], tot2[RT];
 #pragma unroll
-            for (int s = 0; s < NS; s++) {
-                Bv[s] = tv ? ld32(ap + s * a.aq_part + kb * 128) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-                as[s] = tv ? asp[s * a.asc_part + kb] : 0.f;
+            for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
+            const float tmask = c.tv ? 1.f : 0.f;
+            for (int kb = c.kb0; kb < c.kb1; kb++) {
+                if (kb + 1 < c.kb1) load_stage<NS, SW, RT>(nxt, c, a.cols, a.aq_part, a.asc_part, kb + 1);
+                else if (more && n.valid) load_stage<NS, SW, RT>(nxt, n, a.cols, a.aq_part, a.asc_part, n.kb0);
+                const float ws = c.wsp[kb] * tmask;
+                const float ws2 = SW ? c.wsp2[kb] * tmask : 0.f;
+#pragma unroll
+                for (int s = 0; s < NS; s++) {
+                    const float f = ws * cur.as[s], f2 = ws2 * cur.as[s];
+#pragma unroll
+                    for (int r = 0; r < RT; r++) {
+                        tot[r] += mfma_fp8(cur.A[r], cur.Bv[s]) * f;
+                        if (SW) tot2[r] += mfma_fp8(cur.A2[r], cur.Bv[s]) * f2;
+                    }
+                }
+                cur = nxt;
             }
-            const float ws = wsp[kb];
-            const float ws2 = SW ? wsp2[kb] : 0.f;
+            if (c.tv) {
+                const long ooff = a.tok_cnt ? (long)(c.off + c.tt) * a.o_ts : (long)c.tt * a.o_ts + (long)c.m * a.o_ms;
 #pragma unroll
-            for (int s = 0; s < NS; s++) {
-                const v4f acc = mfma_fp8(A, Bv[s]);
-                const float f = ws * as[s];
-                tot += acc * f;
-                if (SW) {
-                    const v4f acc2 = mfma_fp8(A2, Bv[s]);
-                    tot2 += acc2 * (ws2 * as[s]);
+                for (int r = 0; r < RT; r++) {
+                    const int rr = c.r0 + r * 16 + 4 * lg;
+                    if (a.ksplit > 1) {
+                        *(v4f *)(a.part + (long)c.kc * a.n_out + ooff + rr) = tot[r];
+                        if (SW) *(v4f *)(a.part2 + (long)c.kc * a.n_out + ooff + rr) = tot2[r];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            float v = tot[r][i];
+                            if (EPI == EPI_RESID) v += act_load(a.resid, a.resid_dt, (long)c.tt * a.r_ts + rr + i);
+                            if (SW) v = silu(v) * tot2[r][i];
+                            a.out[ooff + rr + i] = v;
+                        }
+                    }
                 }
             }
+        } else if (more && n.valid) {
+            load_stage<NS, SW, RT>(cur, n, a.cols, a.aq_part, a.asc_part, n.kb0);
         }
-        if (!tv) continue;
-        const long ooff = a.tok_cnt ? (long)(it.off + tt) * a.o_ts : (long)tt * a.o_ts + (long)it.m * a.o_ms;
-        if (a.ksplit > 1) {
-            float *p = a.part + (long)kc * a.n_out + ooff + it.r0 + 4 * lg;
-            *(v4f *)p = tot;
-            if (SW) *(v4f *)(a.part2 + (long)kc * a.n_out + ooff + it.r0 + 4 * lg) = tot2;
-            continue;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int r = it.r0 + 4 * lg + i;
-            float v = tot[i];
-            if (EPI == EPI_RESID) v += act_load(a.resid, a.resid_dt, (long)tt * a.r_ts + r);
-            if (SW) v = silu(v) * tot2[i];
-            a.out[ooff + r] = v;
-        }
+        if (more) c = n;
     }
 }
 
@@ -241,6 +293,46 @@ __global__ __launch_bounds__(256) void k_quant(const float *__restrict__ x, long
     }
 }
 
+// Z = silu(sum_c G_c) * (sum_c U_c) from the K-chunk partials of the gate/up pass, split into NS FP8 parts
+// like k_quant.  rows come from the device (pairs of the plan).
+template <int NS>
+__global__ __launch_bounds__(256) void k_swiglu_quant(const float *__restrict__ pg, const float *__restrict__ pu,
+                                                      int ksplit, long stride, long rows_host, const int *rows_dev,
+                                                      int cols, uint8_t *__restrict__ q, float *__restrict__ sc,
+                                                      long q_part, long sc_part)
+{
+    const int lane = threadIdx.x & 63;
+    const long wave = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long nwaves = (long)gridDim.x * 4;
+    const long rows = rows_dev ? *rows_dev : rows_host;
+    const int nkb = cols >> 7;
+    for (long it = wave; it < rows * nkb; it += nwaves) {
+        const long row = it / nkb;
+        const int kb = (int)(it % nkb);
+        const long e = row * cols + kb * 128 + lane * 2;
+        v2f g = {0.f, 0.f}, u = {0.f, 0.f};
+        for (int c = 0; c < ksplit; c++) {
+            g += *(const v2f *)(pg + c * stride + e);
+            u += *(const v2f *)(pu + c * stride + e);
+        }
+        float r0 = silu(g.x) * u.x, r1 = silu(g.y) * u.y;
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
+            const float scale = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+            const float inv = 1.0f / scale;
+            const float c0 = fminf(fmaxf(r0 * inv, -448.f), 448.f);
+            const float c1 = fminf(fmaxf(r1 * inv, -448.f), 448.f);
+            const uint32_t code = f32x2_to_fp8(c0, c1);
+            *(uint16_t *)(q + s * q_part + e) = (uint16_t)code;
+            if (lane == 0) sc[s * sc_part + row * nkb + kb] = scale;
+            const v2f d = fp8x2_lo(code);
+            r0 -= d.x * scale;
+            r1 -= d.y * scale;
+        }
+    }
+}
+
 static int grid_for(long items, int per_block_waves = 4, int max_blocks = 8192)
 {
     long b = (items + per_block_waves - 1) / per_block_waves;
@@ -254,16 +346,20 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
     // upper bound of the item count (device-side counts can only be smaller)
     const long n_act = a.n_active_host;
     if (fp8) {
-        const long items = n_act * (a.rows / 16) * a.max_groups * a.ksplit;
-        const dim3 g(grid_for(items, 4, 2048));
+        // persistent grid: exactly the workgroups that fit on the device at once, so every wave's equal
+        // share of the items runs concurrently
         bool done = false;
-#define DL_G(NS_, E_) \
-    if (!done && ns == NS_ && epi == E_) { hipLaunchKernelGGL((k_gemv_fp8<NS_, E_>), g, dim3(256), 0, s, a); done = true; }
-        DL_G(2, EPI_STORE) DL_G(2, EPI_RESID) DL_G(2, EPI_SWIGLU)
-        DL_G(4, EPI_STORE) DL_G(4, EPI_RESID) DL_G(4, EPI_SWIGLU)
+#define DL_G(NS_, E_, RT_)                                                                    \
+    if (!done && ns == NS_ && epi == E_) {                                                    \
+        const dim3 g(resident_blocks((const void *)k_gemv_fp8<NS_, E_, RT_>, 256));           \
+        hipLaunchKernelGGL((k_gemv_fp8<NS_, E_, RT_>), g, dim3(256), 0, s, a);               \
+        done = true;                                                                          \
+    }
+        DL_G(2, EPI_STORE, 2) DL_G(2, EPI_RESID, 2) DL_G(2, EPI_SWIGLU, 2)
+        DL_G(4, EPI_STORE, 2) DL_G(4, EPI_RESID, 2) DL_G(4, EPI_SWIGLU, 2)
 #undef DL_G
         if (!done) return fail(DL_ERR_UNSUPPORTED, "gemv parts=%d", ns);
-        if (a.ksplit > 1) {
+        if (a.ksplit > 1 && !a.reduce_in_consumer) {
             const dim3 gr((unsigned)((a.n_out + 255) / 256));
             if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemv_reduce<EPI_STORE>), gr, dim3(256), 0, s, a);
             else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv_reduce<EPI_RESID>), gr, dim3(256), 0, s, a);
@@ -277,6 +373,19 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
     else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv_f32<EPI_RESID>), g, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_gemv_f32<EPI_SWIGLU>), g, dim3(256), 0, s, a);
     return hip_check("gemv_f32");
+}
+
+int launch_swiglu_quant(const float *pg, const float *pu, int ksplit, long stride, long rows_host,
+                        const int *rows_dev, int cols, uint8_t *q, float *sc, long q_part, long sc_part, int ns,
+                        hipStream_t s)
+{
+    const long items = rows_host * (cols / 128);
+    const dim3 g(grid_for(items, 4, 4096));
+    if (ns == 2)
+        hipLaunchKernelGGL((k_swiglu_quant<2>), g, dim3(256), 0, s, pg, pu, ksplit, stride, rows_host, rows_dev, cols, q,
+                           sc, q_part, sc_part);
+    else return fail(DL_ERR_UNSUPPORTED, "swiglu quant parts=%d", ns);
+    return hip_check("swiglu_quant");
 }
 
 int launch_quant(const float *x, long rows_host, const int *rows_dev, int cols, uint8_t *q, float *sc, long q_part,

@@ -16,8 +16,11 @@
 //   write:   an ordered compaction: a position is kept if its score is > T, or == T and fewer than
 //            `need` equal scores precede it; its output slot is the number of kept positions
 //            before it, so the list comes out in ascending position order.
-// The last workgroup of a row (atomic ticket after a device-scope fence) turns each histogram into
-// the next range; no workgroup ever waits on another.
+// Each histogram is turned into the next range at the start of the following kernel, by every one of
+// its workgroups (the same deterministic pick, from 16 KB that the kernel boundary made visible);
+// workgroup 0 records the result for later kernels.  No workgroup waits on, or fences for, another:
+// on this part an in-kernel device-scope fence writes back the whole L2 of the XCD, which costs far
+// more than recomputing a 4,096-bin pick.
 #include "dl_common.h"
 #include "dl_internal.h"
 
@@ -55,9 +58,9 @@ __device__ __forceinline__ int wave_incl_scan(int v)
 }
 
 // Largest bin b with (count of bins >= b) >= k, and the count strictly above it.  Called by all 256
-// threads of the deciding workgroup: the histogram is copied into LDS with coherent loads (all in flight
-// at once), the 256 segment sums are suffix-scanned, and the one thread whose segment holds the k-th
-// largest score walks it.
+// threads of a workgroup: the histogram (finished by an earlier kernel) is copied into LDS with all loads
+// in flight at once, the 256 segment sums are suffix-scanned, and the one thread whose segment holds the
+// k-th largest score walks it.
 template <int NBINS>
 __device__ void block_pick(const unsigned *gh, unsigned *sh, int k, int *s_tmp, int &bin_out, int &above_out)
 {
@@ -67,7 +70,7 @@ __device__ void block_pick(const unsigned *gh, unsigned *sh, int k, int *s_tmp, 
 #pragma unroll
     for (int i = 0; i < PER; i++) {
         const int b = i * 256 + tid;
-        v[i] = b < NBINS ? ld_agent_u(gh + b) : 0u;
+        v[i] = b < NBINS ? gh[b] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < PER; i++) {
@@ -110,28 +113,37 @@ __device__ void block_pick(const unsigned *gh, unsigned *sh, int k, int *s_tmp, 
     __syncthreads();
 }
 
-// Last-workgroup election for row b: every thread fences its global atomics first.
-__device__ __forceinline__ bool last_block(int *ticket, int nblk, int *s_flag)
+// The selection state after one more histogram: pass 1 uses the log-linear bins, later passes 4,096
+// equal bins spanning the current [lo, hi].  A finished state passes through unchanged.
+template <bool FIRST>
+__device__ SelState advance(const SelState prev, const unsigned *gh, int top_k, unsigned *sh, int *s_tmp)
 {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int t = atomicAdd(ticket, 1);
-        *s_flag = (t == nblk - 1);
+    if (prev.done) return prev;
+    SelState s = prev;
+    int bin, above;
+    if (FIRST) {
+        block_pick<NB1>(gh, sh, top_k, s_tmp, bin, above);
+        int lo, hi;
+        bin1_range(bin, lo, hi);
+        s.lo = lo; s.hi = hi; s.above = above;
+    } else {
+        const unsigned lo = (unsigned)prev.lo, hi = (unsigned)prev.hi;
+        const int shift = max(0, (32 - __clz(hi - lo)) - 12);
+        block_pick<NB2>(gh, sh, top_k - prev.above, s_tmp, bin, above);
+        const unsigned nlo = lo + ((unsigned)bin << shift);
+        const unsigned nhi = min(hi, nlo + ((1u << shift) - 1u));
+        s.lo = (int)nlo; s.hi = (int)nhi; s.above = prev.above + above;
     }
-    __syncthreads();
-    bool last = *s_flag != 0;
-    if (last) __threadfence();
-    return last;
+    if (s.lo == s.hi) { s.done = 1; s.need = top_k - s.above; }
+    return s;
 }
 
-// Per-row initial selection state; clears the pass-1 histogram and tickets.
-__global__ void k_sel_init(const int32_t *seq_lens, int B, int top_k, unsigned *hist1, unsigned *hist2, int *ticket,
-                           SelState *st)
+// Per-row initial selection state; clears the histograms of all passes.
+__global__ void k_sel_init(const int32_t *seq_lens, int B, int top_k, unsigned *hist1, unsigned *hist2, SelState *st)
 {
     const int b = blockIdx.x;
     for (int i = threadIdx.x; i < NB1; i += blockDim.x) hist1[(long)b * NB1 + i] = 0;
-    for (int i = threadIdx.x; i < NB2; i += blockDim.x) hist2[(long)b * NB2 + i] = 0;
+    for (int i = threadIdx.x; i < 2 * NB2; i += blockDim.x) hist2[(long)b * 2 * NB2 + i] = 0;
     if (threadIdx.x == 0) {
         int L = seq_lens[b];
         SelState s;
@@ -142,8 +154,7 @@ __global__ void k_sel_init(const int32_t *seq_lens, int B, int top_k, unsigned *
             s.lo = 0; s.hi = 0x7FFFFFFF; s.above = 0; s.done = 0; s.need = 0;
         }
         s.pad0 = s.pad1 = 0;
-        st[b] = s;
-        ticket[b] = 0;
+        st[b] = s;  // state 0 of row b
     }
 }
 
@@ -152,17 +163,14 @@ template <int NHG, int KCH>
 __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ q_idx, const int8_t *__restrict__ k_pool,
                                                      const int32_t *__restrict__ page_table,
                                                      const int32_t *__restrict__ seq_lens, int max_pages, int ps_shift,
-                                                     int HI, int DI, int top_k, int32_t *__restrict__ scores,
-                                                     long Lmax, unsigned *__restrict__ hist1, int *__restrict__ ticket,
-                                                     SelState *__restrict__ st)
+                                                     int HI, int DI, int32_t *__restrict__ scores, long Lmax,
+                                                     unsigned *__restrict__ hist1)
 {
     __shared__ unsigned s_hist[NB1];
-    __shared__ int s_tmp[260];
     const int b = blockIdx.y;
     const int L = seq_lens[b];
     const long blk0 = (long)blockIdx.x * SCORE_POS_PER_BLOCK;
     if (blk0 >= L) return;
-    const int nblk = (L + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
     for (int i = tid; i < NB1; i += 256) s_hist[i] = 0;
@@ -221,74 +229,49 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
     __syncthreads();
     unsigned *gh = hist1 + (long)b * NB1;
     for (int i = tid; i < NB1; i += 256) {
-        unsigned v = s_hist[i];
+        const unsigned v = s_hist[i];
         if (v) atomicAdd(gh + i, v);
-    }
-    if (!last_block(ticket + b, nblk, &s_tmp[258])) return;
-    if (st[b].done) {  // keep-all row: nothing to pick
-        if (tid == 0) ticket[b] = 0;
-        return;
-    }
-    int bin, above;
-    block_pick<NB1>(gh, s_hist, top_k, s_tmp, bin, above);
-    if (tid == 0) {
-        int lo, hi;
-        bin1_range(bin, lo, hi);
-        SelState s = st[b];
-        s.lo = lo; s.hi = hi; s.above = above;
-        if (lo == hi) { s.done = 1; s.need = top_k - above; }
-        st[b] = s;
-        ticket[b] = 0;
     }
 }
 
-// One refinement pass: 4,096-bin histogram of the scores inside [lo, hi].
+// One refinement pass (PASS = 1, 2): advance the state with histogram PASS, then histogram the scores
+// inside the new [lo, hi] with 4,096 bins into histogram PASS + 1.
+template <int PASS>
 __global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ scores, long Lmax,
                                                     const int32_t *__restrict__ seq_lens, int top_k,
-                                                    unsigned *__restrict__ hist2, int *__restrict__ ticket,
-                                                    SelState *__restrict__ st)
+                                                    const unsigned *__restrict__ hist_in, unsigned *__restrict__ hist_out,
+                                                    SelState *__restrict__ st, int B)
 {
-    __shared__ unsigned s_hist[NB2];
+    __shared__ unsigned s_hist[NB2 > NB1 ? NB2 : NB1];
     __shared__ int s_tmp[260];
     const int b = blockIdx.y;
     const int L = seq_lens[b];
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
-    if (c0 >= L) return;
-    SelState s0 = st[b];
-    if (s0.done) return;
-    const int nblk = (L + SEL_CHUNK - 1) / SEL_CHUNK;
+    if (c0 >= L && blockIdx.x != 0) return;
     const int tid = threadIdx.x;
-    const unsigned lo = (unsigned)s0.lo, hi = (unsigned)s0.hi;
-    const unsigned width = hi - lo;  // >= 1
-    const int shift = max(0, (32 - __clz(width)) - 12);
+    const SelState prev = st[(long)(PASS - 1) * B + b];
+    const SelState cur = PASS == 1 ? advance<true>(prev, hist_in + (long)b * NB1, top_k, s_hist, s_tmp)
+                                   : advance<false>(prev, hist_in + (long)b * NB2, top_k, s_hist, s_tmp);
+    if (blockIdx.x == 0 && tid == 0) st[(long)PASS * B + b] = cur;
+    if (c0 >= L || cur.done) return;
+    const unsigned lo = (unsigned)cur.lo, hi = (unsigned)cur.hi;
+    const int shift = max(0, (32 - __clz(hi - lo)) - 12);
+    __syncthreads();
     for (int i = tid; i < NB2; i += 256) s_hist[i] = 0;
     __syncthreads();
     const int32_t *sc = scores + (long)b * Lmax;
     for (int i = 0; i < SEL_CHUNK / 256; i++) {
-        long p = c0 + (long)i * 256 + tid;
+        const long p = c0 + (long)i * 256 + tid;
         if (p < L) {
-            unsigned v = (unsigned)sc[p];
+            const unsigned v = (unsigned)sc[p];
             if (v >= lo && v <= hi) atomicAdd(&s_hist[(v - lo) >> shift], 1u);
         }
     }
     __syncthreads();
-    unsigned *gh = hist2 + (long)b * NB2;
+    unsigned *gh = hist_out + (long)b * NB2;
     for (int i = tid; i < NB2; i += 256) {
-        unsigned v = s_hist[i];
+        const unsigned v = s_hist[i];
         if (v) atomicAdd(gh + i, v);
-    }
-    if (!last_block(ticket + b, nblk, &s_tmp[258])) return;
-    int bin, above;
-    block_pick<NB2>(gh, s_hist, top_k - s0.above, s_tmp, bin, above);
-    for (int i = tid; i < NB2; i += 256) gh[i] = 0;  // ready for the next pass
-    if (tid == 0) {
-        SelState s = s0;
-        unsigned nlo = lo + ((unsigned)bin << shift);
-        unsigned nhi = min(hi, nlo + ((1u << shift) - 1u));
-        s.lo = (int)nlo; s.hi = (int)nhi; s.above = s0.above + above;
-        if (nlo == nhi) { s.done = 1; s.need = top_k - s.above; }
-        st[b] = s;
-        ticket[b] = 0;
     }
 }
 
@@ -309,16 +292,22 @@ __device__ __forceinline__ void load16(const int32_t *sc, long p0, int L, int v[
 
 // Per chunk: how many scores are > T and == T.
 __global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ scores, long Lmax,
-                                                   const int32_t *__restrict__ seq_lens, const SelState *__restrict__ st,
+                                                   const int32_t *__restrict__ seq_lens, int top_k,
+                                                   const unsigned *__restrict__ hist3, SelState *__restrict__ st, int B,
                                                    int nchunk, int *__restrict__ cnt)
 {
+    __shared__ unsigned s_hist[NB2];
+    __shared__ int s_tmp[260];
     __shared__ int s_red[2][4];
     const int b = blockIdx.y;
     const int L = seq_lens[b];
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
-    if (c0 >= L) return;
-    const int T = st[b].lo;
+    if (c0 >= L && blockIdx.x != 0) return;
     const int tid = threadIdx.x;
+    const SelState cur = advance<false>(st[2L * B + b], hist3 + (long)b * NB2, top_k, s_hist, s_tmp);
+    if (blockIdx.x == 0 && tid == 0) st[3L * B + b] = cur;
+    if (c0 >= L) return;
+    const int T = cur.lo;
     int v[16];
     load16(scores + (long)b * Lmax, c0 + (long)tid * 16, L, v);
     int gt = 0, eq = 0;
@@ -349,7 +338,7 @@ __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ s
     const int b = blockIdx.y;
     const int L = seq_lens[b];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const SelState s = st[b];
+    const SelState s = st[3L * gridDim.y + b];
     int32_t *so = sel + (long)b * top_k;
     int32_t *ss = sel_score ? sel_score + (long)b * top_k : nullptr;
     if (blockIdx.x == 0)  // padding of the unused slots
@@ -422,18 +411,17 @@ void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t)
     const long nchunk = (Lmax + SEL_CHUNK - 1) / SEL_CHUNK;
     t.scores = w.take<int32_t>(B * Lmax);
     t.hist1 = w.take<unsigned>(B * NB1);
-    t.hist2 = w.take<unsigned>(B * NB2);
-    t.ticket = w.take<int>(B);
-    t.state = w.take<SelState>(B);
+    t.hist2 = w.take<unsigned>(B * 2 * NB2);  // histograms of passes 2 and 3
+    t.state = w.take<SelState>(4 * B);        // state after 0 .. 3 histograms
     t.cnt = w.take<int>(B * nchunk * 2);
 }
 
 template <int NHG, int KCH>
 static void launch_score(dim3 g, hipStream_t s, const int8_t *q, const int8_t *kp, const dl_pages &pg, int ps_shift,
-                         int HI, int DI, int k, const TopkWs &t, long Lmax)
+                         int HI, int DI, const TopkWs &t, long Lmax)
 {
     hipLaunchKernelGGL((k_index_score<NHG, KCH>), g, dim3(256), 0, s, q, kp, pg.page_table, pg.seq_lens,
-                       pg.max_pages_per_seq, ps_shift, HI, DI, k, t.scores, Lmax, t.hist1, t.ticket, t.state);
+                       pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax, t.hist1);
 }
 
 int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k_pool, int HI, int DI, int top_k,
@@ -443,12 +431,11 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     const long Lmax = max_len(pg);
     const int ps_shift = __builtin_ctz((unsigned)pg.page_size);
     const int nchunk = (int)((Lmax + SEL_CHUNK - 1) / SEL_CHUNK);
-    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, pg.seq_lens, B, top_k, t.hist1, t.hist2, t.ticket,
-                       t.state);
+    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, pg.seq_lens, B, top_k, t.hist1, t.hist2, t.state);
     dim3 gs((unsigned)((Lmax + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK), B);
     const int nhg = (HI + 15) / 16, kch = (DI + 63) / 64;
 #define DL_SCORE_CASE(H_, K_) \
-    if (nhg == H_ && kch == K_) launch_score<H_, K_>(gs, s, q_idx, k_pool, pg, ps_shift, HI, DI, top_k, t, Lmax); else
+    if (nhg == H_ && kch == K_) launch_score<H_, K_>(gs, s, q_idx, k_pool, pg, ps_shift, HI, DI, t, Lmax); else
     DL_SCORE_CASE(1, 1) DL_SCORE_CASE(1, 2) DL_SCORE_CASE(1, 3) DL_SCORE_CASE(1, 4)
     DL_SCORE_CASE(2, 1) DL_SCORE_CASE(2, 2) DL_SCORE_CASE(2, 3) DL_SCORE_CASE(2, 4)
     DL_SCORE_CASE(3, 1) DL_SCORE_CASE(3, 2) DL_SCORE_CASE(3, 3) DL_SCORE_CASE(3, 4)
@@ -456,11 +443,15 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     return fail(DL_ERR_UNSUPPORTED, "indexer shape heads=%d dim=%d", HI, DI);
 #undef DL_SCORE_CASE
     dim3 gc(nchunk, B);
-    // 31-bit scores: pass 1 leaves a range of at most 2^23 values; each refinement takes 12 bits.
-    for (int r = 0; r < 2; r++)
-        hipLaunchKernelGGL(k_sel_refine, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, top_k, t.hist2, t.ticket,
-                           t.state);
-    hipLaunchKernelGGL(k_sel_count, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, t.state, nchunk, t.cnt);
+    // 31-bit scores: pass 1 leaves a range of at most 2^23 values; each refinement takes 12 bits, so the
+    // state after histogram 3 is always final.
+    unsigned *h2 = t.hist2, *h3 = t.hist2 + (long)B * NB2;
+    hipLaunchKernelGGL((k_sel_refine<1>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, top_k, t.hist1, h2,
+                       t.state, B);
+    hipLaunchKernelGGL((k_sel_refine<2>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, top_k, h2, h3, t.state,
+                       B);
+    hipLaunchKernelGGL(k_sel_count, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, top_k, h3, t.state, B, nchunk,
+                       t.cnt);
     hipLaunchKernelGGL(k_sel_write, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, t.state, nchunk, t.cnt, top_k,
                        sel, sel_score);
     return hip_check("indexer_topk");

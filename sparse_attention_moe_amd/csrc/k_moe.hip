@@ -126,6 +126,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const double *__restrict__ p
 // expert's tokens in ascending order, and the pair index of every (token, slot).
 __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ experts, int B, int ke, int E, int S,
                                                int *__restrict__ n_active, int *__restrict__ n_pairs,
+                                               int *__restrict__ n_groups,
                                                int *__restrict__ active, int *__restrict__ tok_off,
                                                int *__restrict__ tok_cnt, int *__restrict__ pair_tok,
                                                int *__restrict__ pair_idx)
@@ -204,9 +205,19 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ exper
         tok_off[na_tot + tid] = routed_pairs + tid * B;
         tok_cnt[na_tot + tid] = B;
     }
+    // largest token group count over the active experts (shared experts have B tokens)
+    int mx = S > 0 ? B : 0;
+    for (int e = tid; e < E; e += nT) mx = max(mx, s_cnt[e]);
+    mx = wave_max_i(mx);
+    __syncthreads();
+    if ((tid & 63) == 0) s_scan[tid >> 6] = mx;
+    __syncthreads();
     if (tid == 0) {
+        int m2 = 0;
+        for (int w = 0; w < nT / 64; w++) m2 = max(m2, s_scan[w]);
         *n_active = na_tot + S;
         *n_pairs = routed_pairs + S * B;
+        *n_groups = (m2 + 15) / 16;
     }
 }
 
@@ -246,7 +257,8 @@ int launch_route(const float *h, int B, int D, const float *w_r, const float *bi
 
 int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, experts, B, ke, E, S, p.n_active, p.n_pairs, p.active,
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, experts, B, ke, E, S, p.n_active, p.n_pairs, p.n_groups,
+                       p.active,
                        p.tok_off, p.tok_cnt, p.pair_tok, p.pair_idx);
     return hip_check("plan");
 }
