@@ -76,19 +76,33 @@ typedef struct {
     const int32_t *page_table; /* device int32 [B, max_pages_per_seq], page ids of the pools */
 } dl_pages;
 
-/* A stack of weight matrices, row-major [count][rows = out][cols = in].
+/* A stack of weight matrices [count][rows = out][cols = in].
  * DL_FP8_E4M3: w holds OCP e4m3fn codes and scale holds one fp32 per 128 x 128 block,
  * [count][ceil(rows/128)][ceil(cols/128)]; the weight is code * scale ("FP8 weights with
  * 128 x 128 block scales", Kiln, "How was Kiln measured against vLLM on H200?").
- * DL_F32: w holds fp32 values, scale is NULL. */
+ * DL_F32: w holds fp32 values, scale is NULL.
+ * layout DL_LAYOUT_ROWS: row-major.  DL_LAYOUT_TILES (FP8 only): the loader's re-tiling done by
+ * dl_pack_weights — every 16-row x 128-column tile is 2,048 contiguous bytes, tiles ordered by
+ * (matrix, 16-row tile, 128-column block), and inside a tile byte h*1024 + l*16 + i holds
+ * row l % 16, column h*64 + (l / 16)*16 + i (h < 2, l < 64, i < 16): the operand of one matrix-core
+ * instruction, so every weight load is a contiguous 1 KB. */
+#define DL_LAYOUT_ROWS 0
+#define DL_LAYOUT_TILES 1
 typedef struct {
     const void *w;
     const float *scale;
     int32_t dtype;
     int32_t count, rows, cols;
+    int32_t layout;
 } dl_mat;
 
 int dl_abi_version(void);
+
+/* Re-tile a row-major FP8 weight stack (src->layout == DL_LAYOUT_ROWS, rows % 16 == 0,
+ * cols % 128 == 0) into DL_LAYOUT_TILES at dst (device, count*rows*cols bytes, not overlapping src).
+ * Scales are unchanged.  Done once when weights are loaded, the way Kiln's loader fits each
+ * 128 x 128 block to a kernel tile ("Expert parallelism without an all-to-all"). */
+int dl_pack_weights(const dl_mat *src, void *dst, void *stream);
 /* Message of the last failed call on this host thread (library-owned, valid until the next call). */
 const char *dl_last_error(void);
 

@@ -20,7 +20,7 @@ DL_F32, DL_BF16, DL_FP8_E4M3, DL_I8, DL_I32 = 0, 1, 2, 3, 4
 STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE", -4: "DL_ERR_UNSUPPORTED",
           -5: "DL_ERR_WORKSPACE", -6: "DL_ERR_HIP"}
 
-EXPORTS = ["dl_abi_version", "dl_last_error", "dl_indexer_topk_workspace", "dl_indexer_topk",
+EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_indexer_topk_workspace", "dl_indexer_topk",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
            "dl_profile_read"]
@@ -40,9 +40,12 @@ class Pages(C.Structure):
                 ("seq_lens", C.c_void_p), ("page_table", C.c_void_p)]
 
 
+DL_LAYOUT_ROWS, DL_LAYOUT_TILES = 0, 1
+
+
 class Mat(C.Structure):
     _fields_ = [("w", C.c_void_p), ("scale", C.c_void_p), ("dtype", C.c_int32), ("count", C.c_int32),
-                ("rows", C.c_int32), ("cols", C.c_int32)]
+                ("rows", C.c_int32), ("cols", C.c_int32), ("layout", C.c_int32)]
 
 
 class LayerDesc(C.Structure):
@@ -74,6 +77,7 @@ def load(require_gpu: bool = True):
         L = C.CDLL(LIB_PATH)
         P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
         L.dl_abi_version.restype = C.c_int
+        L.dl_pack_weights.argtypes = [C.POINTER(Mat), P, P]
         L.dl_last_error.restype = C.c_char_p
         L.dl_indexer_topk_workspace.restype = sz
         L.dl_indexer_topk_workspace.argtypes = [C.POINTER(Pages)]
@@ -133,12 +137,21 @@ def pages(seq_lens: torch.Tensor, page_table: torch.Tensor, page_size: int) -> P
     return Pages(seq_lens.numel(), page_size, page_table.shape[1], _ptr(seq_lens), _ptr(page_table))
 
 
-def mat(w: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None) -> Mat:
+def mat(w: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None, layout: int = DL_LAYOUT_ROWS) -> Mat:
+    """dl_mat over a [count, rows, cols] (or [rows, cols]) weight tensor; tiled tensors keep that shape."""
     if w is None:
-        return Mat(None, None, 0, 0, 0, 0)
+        return Mat(None, None, 0, 0, 0, 0, 0)
     w3 = w if w.dim() == 3 else w.unsqueeze(0)
     dt = DL_FP8_E4M3 if w.dtype in (torch.uint8, torch.float8_e4m3fn) else DL_F32
-    return Mat(_ptr(w), _ptr(scale), dt, w3.shape[0], w3.shape[1], w3.shape[2])
+    return Mat(_ptr(w), _ptr(scale), dt, w3.shape[0], w3.shape[1], w3.shape[2], layout)
+
+
+def pack_weights(w: torch.Tensor, scale: torch.Tensor, stream=None) -> torch.Tensor:
+    """Tiled copy (DL_LAYOUT_TILES) of a row-major FP8 weight tensor; same shape and bytes."""
+    L = load()
+    dst = torch.empty_like(w)
+    _check(L.dl_pack_weights(C.byref(mat(w, scale)), _ptr(dst), _stream(stream)))
+    return dst
 
 
 # ---------------------------------------------------------------- stage calls
@@ -211,7 +224,10 @@ class LayerStep:
 
     Holds the descriptor, the io struct and the workspace, so repeated calls only enqueue."""
 
-    def __init__(self, spec, t: Dict[str, torch.Tensor], debug: bool = False):
+    def __init__(self, spec, t: Dict[str, torch.Tensor], debug: bool = False, tiles: bool = True,
+                 drop_rows: bool = False):
+        """tiles: FP8 weights are re-tiled once (dl_pack_weights) and the step streams the tiles.
+        drop_rows: afterwards drop the row-major weights from `t` (saves memory when nothing else needs them)."""
         L = load()
         self.spec, self.t = spec, t
         dev = t["x"].device
@@ -223,16 +239,26 @@ class LayerStep:
         d.idx_heads, d.idx_dim, d.top_k = spec.HI, spec.DI, spec.topk
         d.n_routed, d.n_shared, d.expert_top_k, d.inter = spec.E, spec.n_shared, spec.ke, spec.I
         d.sm_scale = spec.scale
+        self.w = {}
+        for name in ("w_uv", "w_o", "w_gate", "w_up", "w_down"):
+            w = t.get(name)
+            lay = DL_LAYOUT_ROWS
+            if w is not None and tiles and w.dtype == torch.uint8:
+                w = pack_weights(w, t[name + "_scale"])
+                lay = DL_LAYOUT_TILES
+                if drop_rows:
+                    t[name] = None
+            self.w[name] = (w, t.get(name + "_scale"), lay)
         d.q_dt = _dt(t["x"])
         d.kv_dt = DL_F32 if t["kv"].dtype == torch.float32 else DL_FP8_E4M3
         d.out_dt = DL_BF16 if spec.fp8 else DL_F32
-        d.w_uv = mat(t.get("w_uv"), t.get("w_uv_scale"))
-        d.w_o = mat(t["w_o"], t.get("w_o_scale"))
+        d.w_uv = self.mat("w_uv")
+        d.w_o = self.mat("w_o")
         d.w_r = _ptr(t["w_r"])
         d.r_bias = _ptr(t["r_bias"])
-        d.w_gate = mat(t["w_gate"], t.get("w_gate_scale"))
-        d.w_up = mat(t["w_up"], t.get("w_up_scale"))
-        d.w_down = mat(t["w_down"], t.get("w_down_scale"))
+        d.w_gate = self.mat("w_gate")
+        d.w_up = self.mat("w_up")
+        d.w_down = self.mat("w_down")
         self.desc = d
         self.y = torch.empty(B, spec.D, dtype=torch.bfloat16 if spec.fp8 else torch.float32, device=dev)
         io = LayerIO()
@@ -252,6 +278,10 @@ class LayerStep:
                 setattr(io, k, _ptr(v))
         self.io = io
         self.ws = workspace(L.dl_layer_workspace(C.byref(d), C.byref(self.pg)), dev)
+
+    def mat(self, name: str) -> Mat:
+        w, sc, lay = self.w[name]
+        return mat(w, sc, lay)
 
     def __call__(self, stream=None):
         _check(load().dl_layer_step(C.byref(self.desc), C.byref(self.io), _ptr(self.ws), self.ws.numel(),

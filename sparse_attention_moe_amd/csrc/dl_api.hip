@@ -113,6 +113,8 @@ static int check_mat(const dl_mat *m, const char *name, int count, int rows, int
     if (m->count != count || m->rows != rows || m->cols != cols)
         return fail(DL_ERR_SHAPE, "%s: [%d,%d,%d] expected [%d,%d,%d]", name, m->count, m->rows, m->cols, count, rows,
                     cols);
+    if (m->layout != DL_LAYOUT_ROWS && m->layout != DL_LAYOUT_TILES) return fail(DL_ERR_SHAPE, "%s: layout %d", name, m->layout);
+    if (m->layout == DL_LAYOUT_TILES && m->dtype != DL_FP8_E4M3) return fail(DL_ERR_DTYPE, "%s: tiles need FP8", name);
     if (m->dtype == DL_FP8_E4M3) {
         if (!m->scale) return fail(DL_ERR_NULL, "%s: FP8 needs block scales", name);
         if (rows % 32 || cols % 128) return fail(DL_ERR_UNSUPPORTED, "%s: FP8 needs rows%%32==0, cols%%128==0", name);
@@ -201,6 +203,7 @@ static GemvArgs mat_args(const dl_mat *m)
     if (m->dtype == DL_FP8_E4M3) {
         g.w = (const uint8_t *)m->w;
         g.wsc = m->scale;
+        g.tiled = m->layout == DL_LAYOUT_TILES;
     } else {
         g.wf = (const float *)m->w;
     }
@@ -437,6 +440,7 @@ static int check_ffn_shapes(int B, int D, int I, int ke, int E, int S, const dl_
     DL_TRY(check_mat(wu, "w_up", E + S, I, D));
     DL_TRY(check_mat(wd, "w_down", E + S, D, I));
     if (wg->dtype != wu->dtype || wg->dtype != wd->dtype) return fail(DL_ERR_DTYPE, "expert weights mix dtypes");
+    if (wg->layout != wu->layout) return fail(DL_ERR_SHAPE, "gate and up weights need the same layout");
     return DL_OK;
 }
 
@@ -478,6 +482,21 @@ using namespace dl;
 extern "C" {
 
 int dl_abi_version(void) { return DL_ABI_VERSION; }
+
+int dl_pack_weights(const dl_mat *src, void *dst, void *stream)
+{
+    g_err[0] = 0;
+    if (!src || !src->w || !dst) return fail(DL_ERR_NULL, "src/dst NULL");
+    if (src->dtype != DL_FP8_E4M3) return fail(DL_ERR_DTYPE, "only FP8 weights are tiled");
+    if (src->layout != DL_LAYOUT_ROWS) return fail(DL_ERR_SHAPE, "source must be row-major");
+    if (src->count < 1 || src->rows < 16 || src->rows % 16 || src->cols < 128 || src->cols % 128)
+        return fail(DL_ERR_SHAPE, "pack needs rows %% 16 == 0 and cols %% 128 == 0");
+    const long bytes = (long)src->count * src->rows * src->cols;
+    const char *a = (const char *)src->w, *b = (const char *)dst;
+    if (a < b + bytes && b < a + bytes) return fail(DL_ERR_SHAPE, "src and dst overlap");
+    (void)hipGetLastError();
+    return launch_pack((const uint8_t *)src->w, (uint8_t *)dst, src->count, src->rows, src->cols, (hipStream_t)stream);
+}
 const char *dl_last_error(void) { return g_err; }
 
 size_t dl_indexer_topk_workspace(const dl_pages *pages)

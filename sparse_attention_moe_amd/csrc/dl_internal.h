@@ -60,6 +60,7 @@ struct GemvArgs {
     const uint8_t *w2; const float *wsc2; const float *wf2;   // second matrix of SwiGLU (up)
     long mat_elems;
     int rows, cols, nrb, nkb;
+    int tiled;               // FP8 weights in DL_LAYOUT_TILES
     // which matrices and which tokens
     const int *active;       // matrix id of active slot u (nullptr: u itself)
     const int *n_active_dev; // device count of active slots (nullptr: n_active_host)
@@ -86,6 +87,7 @@ struct GemvArgs {
     bool reduce_in_consumer;  // the next kernel sums the partials itself (no reduction launch)
 };
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
+int launch_pack(const uint8_t *src, uint8_t *dst, long count, int rows, int cols, hipStream_t s);
 
 // SwiGLU of summed gate/up K-chunk partials, split into NS FP8 parts (rows may come from the device).
 int launch_swiglu_quant(const float *pg, const float *pu, int ksplit, long stride, long rows_host,

@@ -56,24 +56,41 @@ struct Ctx {
     const float *wsp, *wsp2, *asp;
 };
 
-template <int NS, bool SW, int RT>
+// Two 16-byte halves of an operand: at p and p + gap.
+__device__ __forceinline__ v8i ld16x2(const uint8_t *p, int gap)
+{
+    v4i a = *(const v4i *)p, b = *(const v4i *)(p + gap);
+    return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Operand bytes of lane l = (ln, lg): row ln of the tile, K bytes {lg*16 .. +16} and {64 + lg*16 .. +16}
+// of the 128-wide block.  Row-major weights: two loads 64 B apart in the row; tiled weights: 16 B at
+// l*16 and 1024 + l*16 of the tile's 2 KB.  The activations use the same K assignment.
+template <int NS, bool SW, int RT, bool TL>
 __device__ __forceinline__ void load_stage(Stage<NS, SW, RT> &st, const Ctx<RT> &c, long cols, long aq_part,
                                            long asc_part, int kb)
 {
 #pragma unroll
     for (int r = 0; r < RT; r++) {
-        st.A[r] = ld32(c.wp + r * 16 * cols + kb * 128);
-        if (SW) st.A2[r] = ld32(c.wp2 + r * 16 * cols + kb * 128);
+        if (TL) {
+            // consecutive 16-row tiles are cols/128 blocks of 2 KB apart
+            const uint8_t *t = c.wp + (long)r * (cols / 128) * 2048 + (long)kb * 2048;
+            st.A[r] = ld16x2(t, 1024);
+            if (SW) st.A2[r] = ld16x2(c.wp2 + (long)r * (cols / 128) * 2048 + (long)kb * 2048, 1024);
+        } else {
+            st.A[r] = ld16x2(c.wp + r * 16 * cols + kb * 128, 64);
+            if (SW) st.A2[r] = ld16x2(c.wp2 + r * 16 * cols + kb * 128, 64);
+        }
     }
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-        st.Bv[s] = ld32(c.ap + s * aq_part + kb * 128);
+        st.Bv[s] = ld16x2(c.ap + s * aq_part + kb * 128, 64);
         st.as[s] = c.asp[s * asc_part + kb];
     }
 }
 
 // Item -> context.  Reuses `prev` (same matrix and token group) when possible: then no memory is read.
-template <int RT, bool SW>
+template <int RT, bool SW, bool TL>
 __device__ __forceinline__ void make_ctx(const GemvArgs &a, int item, int groups, int tiles, const Ctx<RT> *prev,
                                          Ctx<RT> &c)
 {
@@ -101,14 +118,15 @@ __device__ __forceinline__ void make_ctx(const GemvArgs &a, int item, int groups
                           : a.pair_act ? a.pair_act[c.off + ts]
                           : a.tok_cnt  ? (long)(c.off + ts)
                                        : (long)ts * a.a_ts + (long)c.m * a.a_ms;
-        c.ap = a.aq + arow * a.cols + lg * 32;
+        c.ap = a.aq + arow * a.cols + lg * 16;
         c.asp = a.asc + arow * a.nkb;
     }
     c.kc = kc;
     c.r0 = tile * 16 * RT;
     c.kb0 = kc * a.kchunk;
     c.kb1 = min(a.nkb, c.kb0 + a.kchunk);
-    const long wrow = (long)c.m * a.mat_elems + (long)(c.r0 + ln) * a.cols + lg * 32;
+    const long wrow = TL ? (long)c.m * a.mat_elems + (long)(c.r0 / 16) * a.nkb * 2048 + lane * 16
+                         : (long)c.m * a.mat_elems + (long)(c.r0 + ln) * a.cols + lg * 16;
     c.wp = a.w + wrow;
     c.wp2 = SW ? a.w2 + wrow : nullptr;
     const long sbase = ((long)c.m * a.nrb + (c.r0 >> 7)) * a.nkb;
@@ -116,7 +134,7 @@ __device__ __forceinline__ void make_ctx(const GemvArgs &a, int item, int groups
     c.wsp2 = SW ? a.wsc2 + sbase : nullptr;
 }
 
-template <int NS, int EPI, int RT>
+template <int NS, int EPI, int RT, bool TL>
 __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
 {
     constexpr bool SW = EPI == EPI_SWIGLU;
@@ -130,20 +148,20 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
     const int i0 = (int)((long)wave * total / nwaves), i1 = (int)((long)(wave + 1) * total / nwaves);
     if (i0 >= i1) return;
     Ctx<RT> c, n;
-    make_ctx<RT, SW>(a, i0, groups, tiles, nullptr, c);
+    make_ctx<RT, SW, TL>(a, i0, groups, tiles, nullptr, c);
     Stage<NS, SW, RT> cur, nxt;
-    if (c.valid) load_stage<NS, SW, RT>(cur, c, a.cols, a.aq_part, a.asc_part, c.kb0);
+    if (c.valid) load_stage<NS, SW, RT, TL>(cur, c, a.cols, a.aq_part, a.asc_part, c.kb0);
     for (int it = i0; it < i1; it++) {
         const bool more = it + 1 < i1;
-        if (more) make_ctx<RT, SW>(a, it + 1, groups, tiles, &c, n);
+        if (more) make_ctx<RT, SW, TL>(a, it + 1, groups, tiles, &c, n);
         if (c.valid) {
             v4f tot[RT], tot2[RT];
 #pragma unroll
             for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
             const float tmask = c.tv ? 1.f : 0.f;
             for (int kb = c.kb0; kb < c.kb1; kb++) {
-                if (kb + 1 < c.kb1) load_stage<NS, SW, RT>(nxt, c, a.cols, a.aq_part, a.asc_part, kb + 1);
-                else if (more && n.valid) load_stage<NS, SW, RT>(nxt, n, a.cols, a.aq_part, a.asc_part, n.kb0);
+                if (kb + 1 < c.kb1) load_stage<NS, SW, RT, TL>(nxt, c, a.cols, a.aq_part, a.asc_part, kb + 1);
+                else if (more && n.valid) load_stage<NS, SW, RT, TL>(nxt, n, a.cols, a.aq_part, a.asc_part, n.kb0);
                 const float ws = c.wsp[kb] * tmask;
                 const float ws2 = SW ? c.wsp2[kb] * tmask : 0.f;
 #pragma unroll
@@ -177,7 +195,7 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
                 }
             }
         } else if (more && n.valid) {
-            load_stage<NS, SW, RT>(cur, n, a.cols, a.aq_part, a.asc_part, n.kb0);
+            load_stage<NS, SW, RT, TL>(cur, n, a.cols, a.aq_part, a.asc_part, n.kb0);
         }
         if (more) c = n;
     }
@@ -349,14 +367,16 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
         // persistent grid: exactly the workgroups that fit on the device at once, so every wave's equal
         // share of the items runs concurrently
         bool done = false;
-#define DL_G(NS_, E_, RT_)                                                                    \
-    if (!done && ns == NS_ && epi == E_) {                                                    \
-        const dim3 g(resident_blocks((const void *)k_gemv_fp8<NS_, E_, RT_>, 256));           \
-        hipLaunchKernelGGL((k_gemv_fp8<NS_, E_, RT_>), g, dim3(256), 0, s, a);               \
+#define DL_G(NS_, E_, TL_)                                                                    \
+    if (!done && ns == NS_ && epi == E_ && (a.tiled != 0) == TL_) {                           \
+        const dim3 g(resident_blocks((const void *)k_gemv_fp8<NS_, E_, 2, TL_>, 256));        \
+        hipLaunchKernelGGL((k_gemv_fp8<NS_, E_, 2, TL_>), g, dim3(256), 0, s, a);            \
         done = true;                                                                          \
     }
-        DL_G(2, EPI_STORE, 2) DL_G(2, EPI_RESID, 2) DL_G(2, EPI_SWIGLU, 2)
-        DL_G(4, EPI_STORE, 2) DL_G(4, EPI_RESID, 2) DL_G(4, EPI_SWIGLU, 2)
+        DL_G(2, EPI_STORE, false) DL_G(2, EPI_RESID, false) DL_G(2, EPI_SWIGLU, false)
+        DL_G(4, EPI_STORE, false) DL_G(4, EPI_RESID, false) DL_G(4, EPI_SWIGLU, false)
+        DL_G(2, EPI_STORE, true) DL_G(2, EPI_RESID, true) DL_G(2, EPI_SWIGLU, true)
+        DL_G(4, EPI_STORE, true) DL_G(4, EPI_RESID, true) DL_G(4, EPI_SWIGLU, true)
 #undef DL_G
         if (!done) return fail(DL_ERR_UNSUPPORTED, "gemv parts=%d", ns);
         if (a.ksplit > 1 && !a.reduce_in_consumer) {
@@ -373,6 +393,35 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
     else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv_f32<EPI_RESID>), g, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_gemv_f32<EPI_SWIGLU>), g, dim3(256), 0, s, a);
     return hip_check("gemv_f32");
+}
+
+// Row-major FP8 [count][rows][cols] -> tiles (see dl.h): one thread per 16-byte output chunk.
+__global__ __launch_bounds__(256) void k_pack(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, long count,
+                                              int rows, int cols)
+{
+    const long nkb = cols / 128, tiles = rows / 16;
+    const long n16 = count * tiles * nkb * 128;  // 16-byte chunks
+    for (long o = (long)blockIdx.x * 256 + threadIdx.x; o < n16; o += (long)gridDim.x * 256) {
+        const int l = (int)(o % 64);
+        const int h = (int)((o / 64) % 2);
+        long t = o / 128;  // (matrix, tile, block)
+        const long kb = t % nkb;
+        t /= nkb;
+        const long tile = t % tiles;
+        const long m = t / tiles;
+        const long row = tile * 16 + (l % 16);
+        const long col = kb * 128 + h * 64 + (l / 16) * 16;
+        *(v4i *)(dst + o * 16) = *(const v4i *)(src + (m * rows + row) * cols + col);
+    }
+}
+
+int launch_pack(const uint8_t *src, uint8_t *dst, long count, int rows, int cols, hipStream_t s)
+{
+    const long n16 = count * (long)rows * cols / 16;
+    long blocks = (n16 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, count, rows, cols);
+    return hip_check("pack");
 }
 
 int launch_swiglu_quant(const float *pg, const float *pu, int ksplit, long stride, long rows_host,

@@ -185,3 +185,35 @@ def test_tiny_config_full_oracle():
     torch.cuda.synchronize()
     w = check_rows(spec, t, step.dbg, y, [0])
     assert w["y"] <= FP_TOL
+
+
+def test_pack_weights_layout():
+    """dl_pack_weights follows the tile layout stated in dl.h (checked against a numpy re-tiling)."""
+    g = torch.Generator(device=DEV).manual_seed(7)
+    w = torch.randint(0, 126, (3, 64, 384), generator=g, device=DEV, dtype=torch.uint8)
+    sc = torch.ones(3, 1, 3, device=DEV)
+    tiled = dl.pack_weights(w, sc)
+    torch.cuda.synchronize()
+    src = w.cpu().numpy()
+    got = tiled.cpu().numpy().reshape(-1)
+    count, rows, cols = src.shape
+    ref = np.empty_like(got)
+    o = 0
+    for m in range(count):
+        for t in range(rows // 16):
+            for kb in range(cols // 128):
+                for h in range(2):
+                    for l in range(64):
+                        r, c = t * 16 + l % 16, kb * 128 + h * 64 + (l // 16) * 16
+                        ref[o:o + 16] = src[m, r, c:c + 16]
+                        o += 16
+    assert np.array_equal(got, ref)
+
+
+def test_rows_and_tiles_layouts_agree():
+    spec = synth.small_fp8_spec(name="layouts", B=2, seq_lens=(1700, 900))
+    t = _layer(spec, seed=8)
+    y_rows = dl.LayerStep(spec, t, debug=True, tiles=False)().clone()
+    y_tiles = dl.LayerStep(spec, t, debug=True, tiles=True)()
+    torch.cuda.synchronize()
+    assert torch.equal(y_rows, y_tiles)
