@@ -265,7 +265,7 @@ static int run_projection(int B, int H, int Dv, const float *o, const dl_mat *w_
     if (f8) {
         DL_TRY(launch_quant(act, B, nullptr, K, a.uq, a.uqs, (long)B * K, (long)B * (K / 128), PROJ_PARTS, s));
         g.aq = a.uq; g.asc = a.uqs; g.aq_part = (long)B * K; g.asc_part = (long)B * (K / 128);
-        g.ksplit = pick_ksplit((long)(w_o->rows / 16) * g.max_groups, g.nkb);
+        g.ksplit = pick_ksplit((long)(w_o->rows / 32) * g.max_groups, g.nkb);
         g.kchunk = g.nkb / g.ksplit;
         g.part = a.kpart;
         g.n_out = (long)B * w_o->rows;
@@ -273,6 +273,56 @@ static int run_projection(int B, int H, int Dv, const float *o, const dl_mat *w_
         g.af = act;
     }
     return launch_gemv(g, PROJ_PARTS, resid ? EPI_RESID : EPI_STORE, f8, s);
+}
+
+// Attention over the kept positions, then (with w_o) out = residual + W_O concat_h(W_UV[h] o[h]).
+// With the matrix-core attention, FP8 W_UV/W_O and hd = 128 or 256, the split merge, W_UV and the split
+// of u run as one kernel, and W_O's K-chunk reduction adds the residual (and, with hq, splits h for the
+// FFN).  Both entry points use this routine, so the fused step and the separate calls agree bit for bit.
+static int run_attn_proj(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale,
+                         int kv_dt, int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k,
+                         const dl_mat *w_uv, const dl_mat *w_o, const void *resid, int resid_dt, float *o,
+                         float *out, const AttnWs &a, uint8_t *hq, float *hqs, bool *h_split, hipStream_t s,
+                         const Marks &mk)
+{
+    const int B = pg.batch;
+    if (h_split) *h_split = false;
+    const int hd = w_uv ? w_uv->rows : Dv;
+    const bool fuse = w_o && w_uv && attention_mfma_ok(H, Dc, Dv, q_dt, kv_dt) && w_uv->dtype == DL_FP8_E4M3 &&
+                      w_o->dtype == DL_FP8_E4M3 && attention_merge_uv_ok(Dv, hd);
+    if (!fuse) {
+        DL_TRY(launch_attention(pg, q, q_dt, kv, kv_scale, kv_dt, H, Dc, Dv, sm_scale, sel, top_k, o, a.opart, a.ml, s));
+        mk.at(2);
+        if (!w_o) return DL_OK;
+        return run_projection(B, H, Dv, o, w_uv, w_o, resid, resid_dt, out, a, s);
+    }
+    DL_TRY(launch_attention(pg, q, q_dt, kv, kv_scale, kv_dt, H, Dc, Dv, sm_scale, sel, top_k, nullptr, a.opart, a.ml,
+                            s));
+    mk.at(2);
+    const long K = (long)H * hd;
+    DL_TRY(launch_attn_merge_uv(B, H, Dv, top_k, a.opart, a.ml, o, (const uint8_t *)w_uv->w, w_uv->scale, hd,
+                                w_uv->layout == DL_LAYOUT_TILES, a.uq, a.uqs, (long)B * K, (long)B * (K / 128), s));
+    GemvArgs g = mat_args(w_o);
+    g.n_active_host = 1;
+    g.ntok_host = B;
+    g.max_groups = (B + 15) / 16;
+    g.a_ts = 1;
+    g.o_ts = w_o->rows;
+    g.out = out;
+    g.resid = resid;
+    g.resid_dt = resid_dt;
+    g.r_ts = w_o->rows;
+    g.aq = a.uq; g.asc = a.uqs; g.aq_part = (long)B * K; g.asc_part = (long)B * (K / 128);
+    g.ksplit = pick_ksplit((long)(w_o->rows / 32) * g.max_groups, g.nkb);
+    g.kchunk = g.nkb / g.ksplit;
+    g.part = a.kpart;
+    g.n_out = (long)B * w_o->rows;
+    g.reduce_in_consumer = g.ksplit > 1;
+    DL_TRY(launch_gemv(g, PROJ_PARTS, EPI_RESID, true, s));
+    if (g.ksplit == 1) return DL_OK;
+    DL_TRY(launch_resid_reduce_split(g, out, hq, hqs, (long)B * w_o->rows, (long)B * (w_o->rows / 128), s));
+    if (h_split) *h_split = hq != nullptr;
+    return DL_OK;
 }
 
 // ------------------------------------------------------------------ FFN
@@ -318,12 +368,12 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
 static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, const float *gates, int ke,
                    const dl_mat *wg, const dl_mat *wu, const dl_mat *wd, int E, int S, const void *resid,
                    int resid_dt, void *out, int out_dt, const FfnWs &f, hipStream_t s, const Marks &mk = Marks(),
-                   float *out32 = nullptr)
+                   float *out32 = nullptr, bool plan_ready = false, bool h_split_ready = false)
 {
     const bool f8 = wg->dtype == DL_FP8_E4M3;
     const int NE = E + S;
     const long P = (long)B * (ke + S);
-    DL_TRY(launch_plan(experts, B, ke, E, S, f.plan, s));
+    if (!plan_ready) DL_TRY(launch_plan(experts, B, ke, E, S, f.plan, s));
     // gate/up + SwiGLU -> Z
     GemvArgs g = mat_args(wg);
     g.w2 = (const uint8_t *)(f8 ? wu->w : nullptr);
@@ -340,7 +390,8 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     g.o_ts = I;
     g.out = f.Z;
     if (f8) {
-        DL_TRY(launch_quant(h, B, nullptr, D, f.hq, f.hqs, (long)B * D, (long)B * (D / 128), FFN_PARTS, s));
+        if (!h_split_ready)
+            DL_TRY(launch_quant(h, B, nullptr, D, f.hq, f.hqs, (long)B * D, (long)B * (D / 128), FFN_PARTS, s));
         g.aq = f.hq; g.asc = f.hqs; g.aq_part = (long)B * D; g.asc_part = (long)B * (D / 128);
         if (g.nkb % GU_KSPLIT == 0) {
             g.ksplit = GU_KSPLIT;
@@ -555,10 +606,8 @@ int dl_sparse_attn_decode(const dl_pages *pages, const void *q, int32_t q_dt, co
     AttnWs a;
     attn_ws_layout(w, pages->batch, n_heads, d_v, top_k, w_uv, w_o, a);
     float *o = w_o ? a.o : out;
-    DL_TRY(launch_attention(*pages, q, q_dt, kv_pool, kv_scale, kv_dt, n_heads, d_c, d_v, sm_scale, sel, top_k, o,
-                            a.opart, a.ml, s));
-    if (!w_o) return DL_OK;
-    return run_projection(pages->batch, n_heads, d_v, o, w_uv, w_o, residual, res_dt, out, a, s);
+    return run_attn_proj(*pages, q, q_dt, kv_pool, kv_scale, kv_dt, n_heads, d_c, d_v, sm_scale, sel, top_k, w_uv, w_o,
+                         residual, res_dt, o, out, a, nullptr, nullptr, nullptr, s, Marks());
 }
 
 size_t dl_moe_route_workspace(int32_t B, int32_t D, int32_t n_experts)
@@ -656,20 +705,28 @@ int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_
     layer_ws_layout(w, d, &pg, io, L);
     Marks mk;
     DL_TRY(marks_begin(mk, s));
+    const dl_mat *wuv = d->w_uv.w ? &d->w_uv : nullptr;
+    const bool f8_ffn = d->w_gate.dtype == DL_FP8_E4M3;
+    const bool fuse_route = route_plan_ok(d->n_routed, d->expert_top_k, B);
     mk.at(0);
     DL_TRY(launch_indexer_topk(pg, io->q_idx, io->k_pool, d->idx_heads, d->idx_dim, d->top_k, L.sel, nullptr, L.topk, s));
     mk.at(1);
-    DL_TRY(launch_attention(pg, io->q, d->q_dt, io->kv_pool, io->kv_scale, d->kv_dt, d->n_heads, d->d_c, d->d_v,
-                            d->sm_scale, L.sel, d->top_k, L.o, L.attn.opart, L.attn.ml, s));
-    mk.at(2);
-    DL_TRY(run_projection(B, d->n_heads, d->d_v, L.o, d->w_uv.w ? &d->w_uv : nullptr, &d->w_o, io->x, d->q_dt, L.h,
-                          L.attn, s));
+    bool h_split = false;
+    DL_TRY(run_attn_proj(pg, io->q, d->q_dt, io->kv_pool, io->kv_scale, d->kv_dt, d->n_heads, d->d_c, d->d_v,
+                         d->sm_scale, L.sel, d->top_k, wuv, &d->w_o, io->x, d->q_dt, L.o, L.h, L.attn,
+                         f8_ffn ? L.ffn.hq : nullptr, L.ffn.hqs, &h_split, s, mk));
     mk.at(3);
-    DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates, nullptr,
-                        L.logits64, L.rpart, s));
+    if (fuse_route) {
+        DL_TRY(launch_route_partial(L.h, B, d->D, d->w_r, d->n_routed, L.rpart, s));
+        DL_TRY(launch_route_plan(L.rpart, B, d->D, d->r_bias, d->n_routed, d->expert_top_k, d->n_shared, L.experts,
+                                 L.gates, nullptr, L.ffn.plan, s));
+    } else {
+        DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates, nullptr,
+                            L.logits64, L.rpart, s));
+    }
     mk.at(4);
     return run_ffn(L.h, B, d->D, d->inter, L.experts, L.gates, d->expert_top_k, &d->w_gate, &d->w_up, &d->w_down,
-                   d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s, mk, io->y32);
+                   d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s, mk, io->y32, fuse_route, h_split);
 }
 
 int dl_profile_enable(int on)

@@ -101,9 +101,18 @@ int launch_quant(const float *x, long rows_host, const int *rows_dev, int cols, 
 // opart [B, splits, H, Dv] and ml [B, splits, H, 2] are scratch for the matrix-core path.
 bool attention_mfma_ok(int H, int Dc, int Dv, int q_dt, int kv_dt);
 int attention_splits(int top_k);
+// With the matrix-core path and o == nullptr only the split partials are written (the caller merges).
 int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
                      int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, float *opart,
                      float *ml, hipStream_t s);
+bool attention_merge_uv_ok(int Dv, int hd);
+// Merge of the split partials + W_UV (fp32, exact decode) + 4-part FP8 split of u for W_O.
+int launch_attn_merge_uv(int B, int H, int Dv, int top_k, const float *opart, const float *ml, float *o,
+                         const uint8_t *wuv, const float *wsc, int hd, int tiled, uint8_t *uq, float *uqs,
+                         long uq_part, long uqs_part, hipStream_t s);
+// h = resid + sum of W_O's K-chunk partials; with hq != nullptr also h split into 2 FP8 parts.
+int launch_resid_reduce_split(const GemvArgs &a, float *h, uint8_t *hq, float *hqs, long hq_part, long hqs_part,
+                              hipStream_t s);
 
 // ------------------------------------------------------------- MoE
 struct MoePlan {
@@ -121,6 +130,11 @@ int route_chunks(int D);  // hidden-size chunks of the router's partial dot prod
 int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
                  float *gates, float *logits, double *logits64, double *part, hipStream_t s);
 int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s);
+// Router top-k (from launch_route's chunk partials) fused with the dispatch plan: E <= 1024, ke <= 16.
+bool route_plan_ok(int E, int ke, int B);
+int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s);
+int launch_route_plan(const double *part, int B, int D, const float *bias, int E, int ke, int S, int32_t *experts,
+                      float *gates, float *logits, const MoePlan &p, hipStream_t s);
 int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
                    const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s);
 

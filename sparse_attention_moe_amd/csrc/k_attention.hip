@@ -394,6 +394,116 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ op
     }
 }
 
+// Split merge fused with the per-head value up-projection and its FP8 split: one workgroup per (row, head).
+//   o      = merged attention output (also stored: [B, H, Dv])
+//   u[r]   = sum_v W_UV[h][r][v] o[v]   on the vector units in fp32 (each code decoded exactly, one scale
+//            per 128-column block), hd = 128 or 256 rows
+//   uq, uqs: u split into NSU FP8 parts with one scale per (part, row b, 128-block) — the activation layout
+//            the W_O pass reads ([part][B][H*hd] and [part][B][H*hd/128]).
+template <int NSU>
+__global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__ opart, const float *__restrict__ ml,
+                                                       int nsplit, int H, int Dv, float *__restrict__ o,
+                                                       const uint8_t *__restrict__ wuv, const float *__restrict__ wsc,
+                                                       int hd, int tiled, uint8_t *__restrict__ uq,
+                                                       float *__restrict__ uqs, long uq_part, long uqs_part)
+{
+    __shared__ float s_o[1024];
+    __shared__ float s_u[256][2];
+    __shared__ float s_w[4];
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // 1. merge the splits
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < nsplit; s2++) M = fmaxf(M, ml[(((long)b * nsplit + s2) * H + h) * 2]);
+    float den = 0.f;
+    for (int s2 = 0; s2 < nsplit; s2++) {
+        const float m = ml[(((long)b * nsplit + s2) * H + h) * 2];
+        if (m != -INFINITY) den += expf(m - M) * ml[(((long)b * nsplit + s2) * H + h) * 2 + 1];
+    }
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    for (int v = tid; v < Dv; v += 256) {
+        float num = 0.f;
+        for (int s2 = 0; s2 < nsplit; s2++) {
+            const float m = ml[(((long)b * nsplit + s2) * H + h) * 2];
+            if (m == -INFINITY) continue;
+            num += expf(m - M) * opart[(((long)b * nsplit + s2) * H + h) * Dv + v];
+        }
+        const float ov = num * inv;
+        s_o[v] = ov;
+        o[(long)bh * Dv + v] = ov;
+    }
+    __syncthreads();
+    // 2. u = W_UV[h] o: thread -> (row r, half of the columns); 16 codes per load
+    const int nkb = Dv / 128, nrb = (hd + 127) / 128;
+    const int per_row = 256 / hd;  // 2 (hd = 128) or 1 (hd = 256)
+    const int r = tid / per_row, part = tid % per_row;
+    const int c_lo = part * (Dv / per_row), c_hi = c_lo + Dv / per_row;
+    const uint8_t *wm = wuv + (long)h * hd * Dv;
+    float acc = 0.f;
+    for (int c0 = c_lo; c0 < c_hi; c0 += 128) {
+        const int kb = c0 / 128;
+        float blk = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const int c = c0 + q * 16;
+            long off;
+            if (tiled) {
+                const int hh = (c % 128) / 64, lg = (c % 64) / 16, l = lg * 16 + r % 16;
+                off = ((long)(r / 16) * nkb + kb) * 2048 + hh * 1024 + l * 16;
+            } else {
+                off = (long)r * Dv + c;
+            }
+            const v4i w = *(const v4i *)(wm + off);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const v2f lo = fp8x2_lo((uint32_t)w[i]), hi = fp8x2_hi((uint32_t)w[i]);
+                blk = fmaf(lo.x, s_o[c + 4 * i], blk);
+                blk = fmaf(lo.y, s_o[c + 4 * i + 1], blk);
+                blk = fmaf(hi.x, s_o[c + 4 * i + 2], blk);
+                blk = fmaf(hi.y, s_o[c + 4 * i + 3], blk);
+            }
+        }
+        acc = fmaf(blk, wsc[((long)h * nrb + r / 128) * nkb + kb], acc);
+    }
+    s_u[r][part] = acc;
+    __syncthreads();
+    // 3. split u into NSU parts, one wave per 128-row block of u
+    const int nub = hd / 128;
+    const long K = (long)H * hd;
+    if (wv < nub) {
+        const int r0 = wv * 128 + lane * 2;
+        float x0 = s_u[r0][0] + (per_row > 1 ? s_u[r0][1] : 0.f);
+        float x1 = s_u[r0 + 1][0] + (per_row > 1 ? s_u[r0 + 1][1] : 0.f);
+        const long e = (long)b * K + (long)h * hd + r0;
+        const long sc_i = (long)b * (K / 128) + (long)h * nub + wv;
+#pragma unroll
+        for (int s = 0; s < NSU; s++) {
+            const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+            const float scale = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+            const float iv = 1.0f / scale;
+            const uint32_t code = f32x2_to_fp8(fminf(fmaxf(x0 * iv, -448.f), 448.f), fminf(fmaxf(x1 * iv, -448.f), 448.f));
+            *(uint16_t *)(uq + s * uq_part + e) = (uint16_t)code;
+            if (lane == 0) uqs[s * uqs_part + sc_i] = scale;
+            const v2f d = fp8x2_lo(code);
+            x0 -= d.x * scale;
+            x1 -= d.y * scale;
+        }
+    }
+    (void)s_w;
+}
+
+bool attention_merge_uv_ok(int Dv, int hd) { return Dv % 128 == 0 && Dv <= 1024 && (hd == 128 || hd == 256); }
+
+int launch_attn_merge_uv(int B, int H, int Dv, int top_k, const float *opart, const float *ml, float *o,
+                         const uint8_t *wuv, const float *wsc, int hd, int tiled, uint8_t *uq, float *uqs,
+                         long uq_part, long uqs_part, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_attn_merge_uv<4>), dim3(B * H), dim3(256), 0, s, opart, ml, attention_splits(top_k), H, Dv,
+                       o, wuv, wsc, hd, tiled, uq, uqs, uq_part, uqs_part);
+    return hip_check("attn_merge_uv");
+}
+
 bool attention_mfma_ok(int H, int Dc, int Dv, int q_dt, int kv_dt)
 {
     return kv_dt == DL_FP8_E4M3 && q_dt == DL_BF16 && H % 16 == 0 && (Dc == 576 || Dc == 512 || Dc == 256 ||
@@ -419,7 +529,7 @@ int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv
                            opart, ml);
         DL_AM(18) DL_AM(16) DL_AM(8) DL_AM(4)
 #undef DL_AM
-        hipLaunchKernelGGL(k_attn_merge, dim3(pg.batch * H), dim3(256), 0, s, opart, ml, nsplit, H, Dv, o);
+        if (o) hipLaunchKernelGGL(k_attn_merge, dim3(pg.batch * H), dim3(256), 0, s, opart, ml, nsplit, H, Dv, o);
         return hip_check("attention_mfma");
     }
     if (top_k > ATT_MAX_K || Dc > ATT_MAX_DC) return fail(DL_ERR_UNSUPPORTED, "attention top_k %d / d_c %d", top_k, Dc);

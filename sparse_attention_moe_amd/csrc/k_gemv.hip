@@ -424,6 +424,46 @@ int launch_pack(const uint8_t *src, uint8_t *dst, long count, int rows, int cols
     return hip_check("pack");
 }
 
+// h = resid + sum_c part[c]: one wave per (row, 128-block); optionally h split into 2 FP8 parts.
+__global__ __launch_bounds__(256) void k_resid_reduce_split(GemvArgs a, float *__restrict__ h, uint8_t *__restrict__ hq,
+                                                            float *__restrict__ hqs, long hq_part, long hqs_part)
+{
+    const int lane = threadIdx.x & 63;
+    const long wave = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int D = a.rows, nkb = D / 128;
+    const long rows = a.n_out / D;
+    if (wave >= rows * nkb) return;
+    const long row = wave / nkb;
+    const int kb = (int)(wave % nkb);
+    const long e = row * D + kb * 128 + lane * 2;
+    v2f v = {0.f, 0.f};
+    for (int c = 0; c < a.ksplit; c++) v += *(const v2f *)(a.part + (long)c * a.n_out + e);
+    float r0 = v.x + act_load(a.resid, a.resid_dt, e), r1 = v.y + act_load(a.resid, a.resid_dt, e + 1);
+    *(v2f *)(h + e) = v2f{r0, r1};
+    if (!hq) return;
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+        const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
+        const float scale = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+        const float inv = 1.0f / scale;
+        const uint32_t code = f32x2_to_fp8(fminf(fmaxf(r0 * inv, -448.f), 448.f), fminf(fmaxf(r1 * inv, -448.f), 448.f));
+        *(uint16_t *)(hq + s * hq_part + e) = (uint16_t)code;
+        if (lane == 0) hqs[s * hqs_part + row * nkb + kb] = scale;
+        const v2f d = fp8x2_lo(code);
+        r0 -= d.x * scale;
+        r1 -= d.y * scale;
+    }
+}
+
+int launch_resid_reduce_split(const GemvArgs &a, float *h, uint8_t *hq, float *hqs, long hq_part, long hqs_part,
+                              hipStream_t s)
+{
+    const long waves = a.n_out / 128;
+    hipLaunchKernelGGL(k_resid_reduce_split, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a, h, hq, hqs, hq_part,
+                       hqs_part);
+    return hip_check("resid_reduce_split");
+}
+
 int launch_swiglu_quant(const float *pg, const float *pu, int ksplit, long stride, long rows_host,
                         const int *rows_dev, int cols, uint8_t *q, float *sc, long q_part, long sc_part, int ns,
                         hipStream_t s)

@@ -40,28 +40,27 @@ __global__ __launch_bounds__(64) void k_route_partial(const float *__restrict__ 
             for (int i = 0; i < 4; i++) w[x][q * 4 + i] = (double)v[i];
         }
     }
+    // every token's 16 features first (all loads in flight together), then the fp64 products
+    v4f hv[ROUTE_TOK][4];
+#pragma unroll
+    for (int t = 0; t < ROUTE_TOK; t++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int d = d0 + q * 4;
+            hv[t][q] = (t < nt && d < D) ? *(const v4f *)(h + (long)(b0 + t) * D + d) : v4f{0.f, 0.f, 0.f, 0.f};
+        }
     double acc[ROUTE_EXP][ROUTE_TOK];
 #pragma unroll
     for (int x = 0; x < ROUTE_EXP; x++)
 #pragma unroll
-        for (int t = 0; t < ROUTE_TOK; t++) acc[x][t] = 0.0;
+        for (int t = 0; t < ROUTE_TOK; t++) {
+            double a2 = 0.0;
 #pragma unroll
-    for (int t = 0; t < ROUTE_TOK; t++) {
-        if (t >= nt) break;
-        const float *hr = h + (long)(b0 + t) * D;
+            for (int q = 0; q < 4; q++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int d = d0 + q * 4;
-            v4f v = {0.f, 0.f, 0.f, 0.f};
-            if (d < D) v = *(const v4f *)(hr + d);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const double hv = (double)v[i];
-#pragma unroll
-                for (int x = 0; x < ROUTE_EXP; x++) acc[x][t] = fma(w[x][q * 4 + i], hv, acc[x][t]);
-            }
+                for (int i = 0; i < 4; i++) a2 = fma(w[x][q * 4 + i], (double)hv[t][q][i], a2);
+            acc[x][t] = a2;
         }
-    }
 #pragma unroll
     for (int x = 0; x < ROUTE_EXP; x++)
 #pragma unroll
@@ -221,6 +220,149 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ exper
     }
 }
 
+// Router top-k fused with the dispatch plan, one workgroup of 1024 threads:
+//   1. wave w takes tokens b = w, w + 16, ...: each lane owns experts e = lane + 64 i (i < 16), whose logit is
+//      the sum of the chunk partials (in chunk order) plus the bias; ke rounds of a wave argmax by
+//      (logit desc, id asc) pick the experts; gates are the softmax over the picked logits.
+//   2. the plan, exactly as k_plan, from the picked experts kept in LDS.
+static constexpr int RP_MAXE = 1024;
+__global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ part, int nchunk, int B, int E, int ke,
+                                                     int S, const float *__restrict__ bias,
+                                                     int32_t *__restrict__ experts, float *__restrict__ gates,
+                                                     float *__restrict__ logits, int *__restrict__ n_active,
+                                                     int *__restrict__ n_pairs, int *__restrict__ n_groups,
+                                                     int *__restrict__ active, int *__restrict__ tok_off,
+                                                     int *__restrict__ tok_cnt, int *__restrict__ pair_tok,
+                                                     int *__restrict__ pair_idx)
+{
+    __shared__ int s_cnt[RP_MAXE];
+    __shared__ int s_scan[1024];
+    __shared__ int s_exp[16384];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nT = 1024;
+    const int kk = ke + S;
+    for (int e = tid; e < E; e += nT) s_cnt[e] = 0;
+    for (int b = wv; b < B; b += 16) {
+        double l[RP_MAXE / 64];
+#pragma unroll
+        for (int i = 0; i < RP_MAXE / 64; i++) {
+            const int e = lane + 64 * i;
+            double v = -INFINITY;
+            if (e < E) {
+                v = 0.0;
+                for (int c = 0; c < nchunk; c++) v += part[((long)c * B + b) * E + e];
+                if (bias) v += (double)bias[e];
+                if (logits) logits[(long)b * E + e] = (float)v;
+            }
+            l[i] = v;
+        }
+        double top0 = 0.0, z = 0.0, my_g = 0.0;
+        int my_e = 0;
+        for (int j = 0; j < ke; j++) {
+            double best = -INFINITY;
+            int bi = 0, be = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 0; i < RP_MAXE / 64; i++) {
+                const int e = lane + 64 * i;
+                if (e < E && (l[i] > best || (l[i] == best && e < be))) { best = l[i]; be = e; bi = i; }
+            }
+            int me = be;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const double ov = __shfl_xor(best, o, 64);
+                const int oe = __shfl_xor(be, o, 64);
+                if (ov > best || (ov == best && oe < be)) { best = ov; be = oe; }
+            }
+            if (me == be) {  // the owning lane retires its expert
+#pragma unroll
+                for (int i = 0; i < RP_MAXE / 64; i++)
+                    if (i == bi) l[i] = -INFINITY;
+            }
+            if (j == 0) top0 = best;
+            const double g = exp(best - top0);
+            z += g;
+            if (lane == j) { my_g = g; my_e = be; }  // lane j keeps slot j
+            if (lane == 0) s_exp[b * ke + j] = be;
+        }
+        if (lane < ke) {
+            experts[(long)b * ke + lane] = my_e;
+            gates[(long)b * ke + lane] = (float)(my_g / z);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < B * ke; i += nT) atomicAdd(&s_cnt[s_exp[i]], 1);
+    __syncthreads();
+    const int per = (E + nT - 1) / nT;
+    int na = 0, np = 0;
+    for (int i = 0; i < per; i++) {
+        const int e = tid * per + i;
+        if (e < E && s_cnt[e] > 0) { na++; np += s_cnt[e]; }
+    }
+    s_scan[tid] = na;
+    __syncthreads();
+    for (int o = 1; o < nT; o <<= 1) {
+        const int v = tid >= o ? s_scan[tid - o] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    const int a0 = s_scan[tid] - na;
+    const int na_tot = s_scan[nT - 1];
+    __syncthreads();
+    s_scan[tid] = np;
+    __syncthreads();
+    for (int o = 1; o < nT; o <<= 1) {
+        const int v = tid >= o ? s_scan[tid - o] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    int p0 = s_scan[tid] - np;
+    int a = a0;
+    for (int i = 0; i < per; i++) {
+        const int e = tid * per + i;
+        if (e >= E || s_cnt[e] == 0) continue;
+        active[a] = e;
+        tok_off[a] = p0;
+        tok_cnt[a] = s_cnt[e];
+        int p = p0;
+        for (int b = 0; b < B; b++)
+            for (int j = 0; j < ke; j++)
+                if (s_exp[b * ke + j] == e) {
+                    pair_tok[p] = b;
+                    pair_idx[(long)b * kk + j] = p;
+                    p++;
+                }
+        p0 = p;
+        a++;
+    }
+    const int routed_pairs = B * ke;
+    for (int i = tid; i < S * B; i += nT) {
+        const int s2 = i / B, b = i % B;
+        const int p = routed_pairs + s2 * B + b;
+        pair_tok[p] = b;
+        pair_idx[(long)b * kk + ke + s2] = p;
+    }
+    if (tid < S) {
+        active[na_tot + tid] = E + tid;
+        tok_off[na_tot + tid] = routed_pairs + tid * B;
+        tok_cnt[na_tot + tid] = B;
+    }
+    int mx = S > 0 ? B : 0;
+    for (int e = tid; e < E; e += nT) mx = max(mx, s_cnt[e]);
+    mx = wave_max_i(mx);
+    __syncthreads();
+    if (lane == 0) s_scan[wv] = mx;
+    __syncthreads();
+    if (tid == 0) {
+        int m2 = 0;
+        for (int w = 0; w < nT / 64; w++) m2 = max(m2, s_scan[w]);
+        *n_active = na_tot + S;
+        *n_pairs = routed_pairs + S * B;
+        *n_groups = (m2 + 15) / 16;
+    }
+}
+
 // out[b, d] = resid[b, d] + sum_j gate[b, j] f_j[d] + sum_s f_s[d], in that order.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, const int *__restrict__ pair_idx,
                                                  const float *__restrict__ gates, int B, int D, int ke, int S,
@@ -253,6 +395,24 @@ int launch_route(const float *h, int B, int D, const float *w_r, const float *bi
     hipLaunchKernelGGL(k_route_topk, dim3((B + 3) / 4), dim3(256), 0, s, part, nc, B, E, ke, bias, experts, gates,
                        logits, logits64);
     return hip_check("route");
+}
+
+bool route_plan_ok(int E, int ke, int B) { return E <= RP_MAXE && ke <= 16 && (long)B * ke <= 16384; }
+
+int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s)
+{
+    dim3 g((E + ROUTE_EXP - 1) / ROUTE_EXP, route_chunks(D), (B + ROUTE_TOK - 1) / ROUTE_TOK);
+    hipLaunchKernelGGL(k_route_partial, g, dim3(64), 0, s, h, B, D, w_r, E, part);
+    return hip_check("route_partial");
+}
+
+int launch_route_plan(const double *part, int B, int D, const float *bias, int E, int ke, int S, int32_t *experts,
+                      float *gates, float *logits, const MoePlan &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_route_plan, dim3(1), dim3(1024), 0, s, part, route_chunks(D), B, E, ke, S, bias, experts,
+                       gates, logits, p.n_active, p.n_pairs, p.n_groups, p.active, p.tok_off, p.tok_cnt, p.pair_tok,
+                       p.pair_idx);
+    return hip_check("route_plan");
 }
 
 int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s)
