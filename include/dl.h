@@ -159,7 +159,7 @@ int dl_sparse_attn_decode(const dl_pages *pages, const void *q, int32_t q_dt, co
  *   gates[b]    = softmax over those top_k logits
  *   h fp32 [B, D]; w_r fp32 [n_experts, D]; bias fp32 [n_experts] nullable;
  *   experts int32 [B, top_k]; gates fp32 [B, top_k]; logits fp32 [B, n_experts] nullable.
- * Limits: 1 <= top_k <= 32, top_k <= n_experts <= 4096, D % 4 == 0.
+ * Limits: 1 <= top_k <= 32, top_k <= n_experts <= 1024, D % 4 == 0, D <= 16384.
  * Workspace: dl_moe_route_workspace(B, D, n_experts). */
 size_t dl_moe_route_workspace(int32_t B, int32_t D, int32_t n_experts);
 int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const float *bias, int32_t n_experts,
@@ -175,7 +175,7 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
  *   w_gate, w_up: count = n_routed + n_shared, rows = inter, cols = D;
  *   w_down: count = n_routed + n_shared, rows = D, cols = inter;
  *   residual fp32 [B, D] nullable; out [B, D] in out_dt (DL_F32 or DL_BF16, rounded once, RNE).
- * Limits: B * (top_k + n_shared) <= 16384; n_routed + n_shared <= 4096.  With FP8 weights the
+ * Limits: B * (top_k + n_shared) <= 16384; top_k + n_shared <= 40; n_routed <= 1024; n_routed + n_shared <= 4096.  With FP8 weights the
  * activations enter the matrix cores as two FP8 parts (value and remainder) with per-128-block
  * scales.  Workspace: dl_moe_ffn_workspace(...). */
 size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared);

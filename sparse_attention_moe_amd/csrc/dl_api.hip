@@ -484,7 +484,8 @@ static int check_ffn_shapes(int B, int D, int I, int ke, int E, int S, const dl_
 {
     if (B < 1 || D < 1 || I < 1) return fail(DL_ERR_SHAPE, "ffn B=%d D=%d I=%d", B, D, I);
     if (ke < 1 || ke > 32 || ke > E) return fail(DL_ERR_SHAPE, "expert top_k %d of %d", ke, E);
-    if (S < 0 || E + S > 4096) return fail(DL_ERR_SHAPE, "experts %d + %d", E, S);
+    if (ke + S > 40) return fail(DL_ERR_UNSUPPORTED, "top_k + shared experts %d (<= 40)", ke + S);
+    if (S < 0 || E > 1024 || E + S > 4096) return fail(DL_ERR_SHAPE, "experts %d + %d", E, S);
     if ((long)B * (ke + S) > 16384) return fail(DL_ERR_SHAPE, "B*(top_k+shared) > 16384");
     if ((long)B * ke > 16384) return fail(DL_ERR_SHAPE, "B*top_k > 16384");
     DL_TRY(check_mat(wg, "w_gate", E + S, I, D));
@@ -624,9 +625,9 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
     g_err[0] = 0;
     if (!h || !w_r || !experts || !gates) return fail(DL_ERR_NULL, "h/w_r/experts/gates NULL");
     if (B < 1 || B > 65536 || D < 1) return fail(DL_ERR_SHAPE, "B=%d D=%d", B, D);
-    if (top_k < 1 || top_k > 32 || n_experts < top_k || n_experts > 4096)
+    if (top_k < 1 || top_k > 32 || n_experts < top_k || n_experts > 1024)
         return fail(DL_ERR_SHAPE, "top_k %d of %d experts", top_k, n_experts);
-    if (D % 4) return fail(DL_ERR_UNSUPPORTED, "router hidden size %d (multiple of 4)", D);
+    if (D % 4 || D > 16384) return fail(DL_ERR_UNSUPPORTED, "router hidden size %d (multiple of 4, <= 16384)", D);
     DL_TRY(check_ws(ws, ws_bytes, dl_moe_route_workspace(B, D, n_experts)));
     (void)hipGetLastError();
     Ws w(ws);
@@ -674,7 +675,7 @@ static int check_layer(const dl_layer_desc *d, const dl_pages *pg)
     DL_TRY(check_ffn_shapes(pg->batch, d->D, d->inter, d->expert_top_k, d->n_routed, d->n_shared, &d->w_gate,
                             &d->w_up, &d->w_down));
     if (d->out_dt != DL_F32 && d->out_dt != DL_BF16) return fail(DL_ERR_DTYPE, "out dtype %d", d->out_dt);
-    if (d->D % 4) return fail(DL_ERR_UNSUPPORTED, "hidden size %d (multiple of 4)", d->D);
+    if (d->D % 4 || d->D > 16384) return fail(DL_ERR_UNSUPPORTED, "hidden size %d (multiple of 4, <= 16384)", d->D);
     return DL_OK;
 }
 
@@ -719,7 +720,7 @@ int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_
     if (fuse_route) {
         DL_TRY(launch_route_partial(L.h, B, d->D, d->w_r, d->n_routed, L.rpart, s));
         DL_TRY(launch_route_plan(L.rpart, B, d->D, d->r_bias, d->n_routed, d->expert_top_k, d->n_shared, L.experts,
-                                 L.gates, nullptr, L.ffn.plan, s));
+                                 L.gates, nullptr, L.logits64, L.ffn.plan, s));
     } else {
         DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates, nullptr,
                             L.logits64, L.rpart, s));

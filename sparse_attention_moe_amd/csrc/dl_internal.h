@@ -134,7 +134,7 @@ int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePl
 bool route_plan_ok(int E, int ke, int B);
 int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s);
 int launch_route_plan(const double *part, int B, int D, const float *bias, int E, int ke, int S, int32_t *experts,
-                      float *gates, float *logits, const MoePlan &p, hipStream_t s);
+                      float *gates, float *logits, double *logits64, const MoePlan &p, hipStream_t s);
 int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
                    const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s);
 

@@ -186,6 +186,8 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 static constexpr int AM_NJ = 64;     // kept positions per chunk (one 16-position tile per wave)
 static constexpr int AM_MAXDC = 1024;
 static constexpr int AM_MAXNB = 8;   // 128-feature blocks of the latent
+static constexpr int AM_MAXSPLIT = 32;  // splits of the kept positions (top_k <= 4,096)
+static constexpr int AM_CHUNKS = 2;     // chunks per split: 128 kept positions per workgroup
 
 // 8 e4m3 codes (two dwords) -> 8 bf16, exactly.
 __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1)
@@ -216,71 +218,88 @@ __device__ __forceinline__ float sum16(float v)
 }
 
 // grid (nsplit, H/16, B), 256 threads.  opart [B, nsplit, H, Dv] unnormalised sums, ml [B, nsplit, H, 2].
-template <int KQ>  // d_c / 32
+// The split's page-table lookups happen once up front; chunk c+1's latent codes are loaded into registers
+// while chunk c is computed (double buffering through LDS); the queries sit in LDS.
+template <int KQ, int CH>  // d_c / 32, chunks of 64 positions per split
 __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                    const float *__restrict__ ks, const int32_t *__restrict__ pt,
                                                    int max_pages, int ps_shift, const int32_t *__restrict__ sel,
-                                                   int top_k, int H, int Dv, float sm_scale, int chunks_per_split,
+                                                   int top_k, int H, int Dv, float sm_scale,
                                                    float *__restrict__ opart, float *__restrict__ ml)
 {
     constexpr int Dc = KQ * 32;
     constexpr int DCP = Dc + 16;  // padded LDS row: conflict-free 8-byte reads across 16 positions
     constexpr int NB = (Dc + 127) / 128;
+    constexpr int NP = CH * AM_NJ;                       // positions of the split
+    constexpr int NLD = (AM_NJ * (Dc / 16) + 255) / 256;  // 16-byte code loads per thread per chunk
     __shared__ __attribute__((aligned(16))) uint8_t s_c[AM_NJ * DCP];
-    __shared__ float s_sc[AM_NJ][AM_MAXNB];
+    __shared__ __attribute__((aligned(16))) uint16_t s_q[16 * Dc];
+    __shared__ float s_sc[NP][NB];
     __shared__ float s_p[16][AM_NJ + 4];
-    __shared__ long s_row[AM_NJ];
+    __shared__ long s_row[NP];
     __shared__ float s_red[4][16];
     __shared__ float s_m[16], s_l[16], s_alpha[16];
     const int split = blockIdx.x, h0 = blockIdx.y * 16, b = blockIdx.z;
     const int nsplit = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
     const int ps_mask = (1 << ps_shift) - 1;
-    // queries of this workgroup's 16 heads as A operands (head ln, features kk*32 + lg*8 .. +8)
-    v8bf Aq[KQ];
-    const uint16_t *qr = q + ((long)b * H + h0 + ln) * Dc + lg * 8;
+    const int jbase = split * NP;
+    // queries of the 16 heads -> LDS; rows and scales of every position of the split
+    for (int i = tid; i < 16 * Dc / 8; i += 256)
+        *(v4i *)(s_q + i * 8) = *(const v4i *)(q + ((long)b * H + h0) * Dc + i * 8);
+    for (int i = tid; i < NP; i += 256) {
+        const int j = jbase + i;
+        const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
+        s_row[i] = p < 0 ? -1 : ((long)pt[(long)b * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
+    }
+    if (tid < 16) { s_m[tid] = -INFINITY; s_l[tid] = 0.f; }
+    __syncthreads();
+    for (int i = tid; i < NP * NB; i += 256) {
+        const long row = s_row[i / NB];
+        s_sc[i / NB][i % NB] = row < 0 ? 0.f : ks[row * NB + i % NB];
+    }
+    const int nch = min(CH, (top_k - jbase + AM_NJ - 1) / AM_NJ);
+    // chunk 0's codes into registers
+    v4i R[NLD];
+    auto load_chunk = [&](int ch) {
 #pragma unroll
-    for (int kk = 0; kk < KQ; kk++) Aq[kk] = *(const v8bf *)(qr + kk * 32);
-    // value tiles of this wave: features [w*Dv/4, (w+1)*Dv/4)
+        for (int k = 0; k < NLD; k++) {
+            const int id = k * 256 + tid;
+            R[k] = v4i{0, 0, 0, 0};
+            if (id < AM_NJ * (Dc / 16)) {
+                const int pos = id / (Dc / 16), c16 = id % (Dc / 16);
+                const long row = s_row[ch * AM_NJ + pos];
+                if (row >= 0) R[k] = *(const v4i *)(kv + row * Dc + c16 * 16);
+            }
+        }
+    };
+    if (nch > 0) load_chunk(0);
     const int vw = Dv >> 2, vt0 = w * (vw >> 4), nvt = vw >> 4;
     v4f acc[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (tid < 16) { s_m[tid] = -INFINITY; s_l[tid] = 0.f; }
-    const int jbase = split * chunks_per_split * AM_NJ;
-    for (int ch = 0; ch < chunks_per_split; ch++) {
-        const int j0 = jbase + ch * AM_NJ;
-        if (j0 >= top_k) break;
-        __syncthreads();  // LDS of the previous chunk is no longer read
-        if (tid < AM_NJ) {
-            const int j = j0 + tid;
-            const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
-            const long row = p < 0 ? -1 : ((long)pt[(long)b * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
-            s_row[tid] = row;
+    for (int ch = 0; ch < nch; ch++) {
+        __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
-            for (int k = 0; k < NB; k++) s_sc[tid][k] = row < 0 ? 0.f : ks[row * NB + k];
+        for (int k = 0; k < NLD; k++) {
+            const int id = k * 256 + tid;
+            if (id < AM_NJ * (Dc / 16)) *(v4i *)(s_c + (id / (Dc / 16)) * DCP + (id % (Dc / 16)) * 16) = R[k];
         }
         __syncthreads();
-        // gather the chunk's latent codes (16 bytes per load); empty slots become zeros
-        for (int id = tid; id < AM_NJ * (Dc / 16); id += 256) {
-            const int pos = id / (Dc / 16), c16 = id % (Dc / 16);
-            const long row = s_row[pos];
-            v4i v = {0, 0, 0, 0};
-            if (row >= 0) v = *(const v4i *)(kv + row * Dc + c16 * 16);
-            *(v4i *)(s_c + pos * DCP + c16 * 16) = v;
-        }
-        __syncthreads();
-        // scores of the 16 heads for positions w*16 .. w*16+15
-        const int jp = w * 16 + ln;
+        if (ch + 1 < nch) load_chunk(ch + 1);  // in flight while this chunk is computed
+        const int jl = w * 16 + ln;             // this lane's position within the chunk
+        const int jp = ch * AM_NJ + jl;         // ... within the split
         v4f S = {0.f, 0.f, 0.f, 0.f};
-        const uint8_t *cr = s_c + jp * DCP + lg * 8;
+        const uint8_t *cr = s_c + jl * DCP + lg * 8;
+        const uint16_t *qr = s_q + ln * Dc + lg * 8;
 #pragma unroll
         for (int blk = 0; blk < NB; blk++) {
             v4f a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = blk * 4; kk < (blk * 4 + 4 < KQ ? blk * 4 + 4 : KQ); kk++) {
                 const uint2 cw = *(const uint2 *)(cr + kk * 32);
-                a = mfma_bf16(Aq[kk], fp8x8_to_bf16(cw.x, cw.y), a);
+                const v8bf Aq = *(const v8bf *)(qr + kk * 32);
+                a = mfma_bf16(Aq, fp8x8_to_bf16(cw.x, cw.y), a);
             }
             S += a * s_sc[jp][blk];
         }
@@ -288,7 +307,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t *__restrict__ 
         float sv[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) sv[i] = valid ? S[i] * sm_scale : -INFINITY;
-        // chunk maximum per head (lane holds heads 4*lg+i of position ln)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const float m = max16(sv[i]);
@@ -307,13 +325,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t *__restrict__ 
             const int hh = 4 * lg + i;
             const float mn = s_m[hh];
             const float pv = (sv[i] == -INFINITY) ? 0.f : expf(sv[i] - mn);
-            s_p[hh][jp] = pv;
+            s_p[hh][jl] = pv;
             const float ssum = sum16(pv);
             if (ln == 0) s_red[w][hh] = ssum;
         }
         __syncthreads();
         if (tid < 16) s_l[tid] = s_l[tid] * s_alpha[tid] + (s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid]);
-        // values: O^T[v][h] += sum_j C[j][v] * p[h][j] * scale[j][blk(v)], this wave's feature tiles
         const float al = s_alpha[ln];
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[i] *= al;
@@ -334,13 +351,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t *__restrict__ 
                     cur_blk = blk;
 #pragma unroll
                     for (int e = 0; e < 8; e++) {
-                        const float x = pr[e] * s_sc[jj + e][blk];
+                        const float x = pr[e] * s_sc[ch * AM_NJ + jj + e][blk];
                         const __bf16 hi = (__bf16)x;
                         Bh[e] = hi;
                         Bl[e] = (__bf16)(x - (float)hi);
                     }
                 }
-                // A: codes of positions jj..jj+7 at feature v0 + ln
                 const uint8_t *cc = s_c + jj * DCP + v0 + ln;
                 uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -355,7 +371,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t *__restrict__ 
         }
     }
     __syncthreads();
-    // partial sums: lane holds O^T[v = tile*16 + 4*lg + i][head ln]
     float *op = opart + (((long)b * nsplit + split) * H + h0 + ln) * Dv;
 #pragma unroll
     for (int t = 0; t < 8; t++) {
@@ -375,21 +390,33 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ op
 {
     const int bh = blockIdx.x;  // b*H + h
     const int b = bh / H, h = bh % H;
+    // every split's (m, l) in flight at once; weights w_s = e^(m_s - M)
+    float sm[AM_MAXSPLIT], sl[AM_MAXSPLIT];
+#pragma unroll
+    for (int s2 = 0; s2 < AM_MAXSPLIT; s2++) {
+        const bool ok = s2 < nsplit;
+        sm[s2] = ok ? ml[(((long)b * nsplit + s2) * H + h) * 2] : -INFINITY;
+        sl[s2] = ok ? ml[(((long)b * nsplit + s2) * H + h) * 2 + 1] : 0.f;
+    }
     float M = -INFINITY;
-    for (int s2 = 0; s2 < nsplit; s2++) M = fmaxf(M, ml[(((long)b * nsplit + s2) * H + h) * 2]);
+#pragma unroll
+    for (int s2 = 0; s2 < AM_MAXSPLIT; s2++) M = fmaxf(M, sm[s2]);
     float den = 0.f;
-    for (int s2 = 0; s2 < nsplit; s2++) {
-        const float m = ml[(((long)b * nsplit + s2) * H + h) * 2];
-        if (m != -INFINITY) den += expf(m - M) * ml[(((long)b * nsplit + s2) * H + h) * 2 + 1];
+#pragma unroll
+    for (int s2 = 0; s2 < AM_MAXSPLIT; s2++) {
+        sm[s2] = sm[s2] == -INFINITY ? 0.f : expf(sm[s2] - M);  // weight of split s2 (0 if empty)
+        den += sm[s2] * sl[s2];
     }
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     for (int v = threadIdx.x; v < Dv; v += 256) {
+        float op[AM_MAXSPLIT];
+#pragma unroll
+        for (int s2 = 0; s2 < AM_MAXSPLIT; s2++)
+            op[s2] = s2 < nsplit ? opart[(((long)b * nsplit + s2) * H + h) * Dv + v] : 0.f;
         float num = 0.f;
-        for (int s2 = 0; s2 < nsplit; s2++) {
-            const float m = ml[(((long)b * nsplit + s2) * H + h) * 2];
-            if (m == -INFINITY) continue;
-            num += expf(m - M) * opart[(((long)b * nsplit + s2) * H + h) * Dv + v];
-        }
+#pragma unroll
+        for (int s2 = 0; s2 < AM_MAXSPLIT; s2++)
+            if (s2 < nsplit && sm[s2] != 0.f) num += sm[s2] * op[s2];
         o[(long)bh * Dv + v] = num * inv;
     }
 }
@@ -414,21 +441,33 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__
     const int b = bh / H, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // 1. merge the splits
+    // every split's (m, l) in flight at once; weights w_s = e^(m_s - M)
+    float sm[AM_MAXSPLIT], sl[AM_MAXSPLIT];
+#pragma unroll
+    for (int s2 = 0; s2 < AM_MAXSPLIT; s2++) {
+        const bool ok = s2 < nsplit;
+        sm[s2] = ok ? ml[(((long)b * nsplit + s2) * H + h) * 2] : -INFINITY;
+        sl[s2] = ok ? ml[(((long)b * nsplit + s2) * H + h) * 2 + 1] : 0.f;
+    }
     float M = -INFINITY;
-    for (int s2 = 0; s2 < nsplit; s2++) M = fmaxf(M, ml[(((long)b * nsplit + s2) * H + h) * 2]);
+#pragma unroll
+    for (int s2 = 0; s2 < AM_MAXSPLIT; s2++) M = fmaxf(M, sm[s2]);
     float den = 0.f;
-    for (int s2 = 0; s2 < nsplit; s2++) {
-        const float m = ml[(((long)b * nsplit + s2) * H + h) * 2];
-        if (m != -INFINITY) den += expf(m - M) * ml[(((long)b * nsplit + s2) * H + h) * 2 + 1];
+#pragma unroll
+    for (int s2 = 0; s2 < AM_MAXSPLIT; s2++) {
+        sm[s2] = sm[s2] == -INFINITY ? 0.f : expf(sm[s2] - M);  // weight of split s2 (0 if empty)
+        den += sm[s2] * sl[s2];
     }
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     for (int v = tid; v < Dv; v += 256) {
+        float op[AM_MAXSPLIT];
+#pragma unroll
+        for (int s2 = 0; s2 < AM_MAXSPLIT; s2++)
+            op[s2] = s2 < nsplit ? opart[(((long)b * nsplit + s2) * H + h) * Dv + v] : 0.f;
         float num = 0.f;
-        for (int s2 = 0; s2 < nsplit; s2++) {
-            const float m = ml[(((long)b * nsplit + s2) * H + h) * 2];
-            if (m == -INFINITY) continue;
-            num += expf(m - M) * opart[(((long)b * nsplit + s2) * H + h) * Dv + v];
-        }
+#pragma unroll
+        for (int s2 = 0; s2 < AM_MAXSPLIT; s2++)
+            if (s2 < nsplit && sm[s2] != 0.f) num += sm[s2] * op[s2];
         const float ov = num * inv;
         s_o[v] = ov;
         o[(long)bh * Dv + v] = ov;
@@ -510,8 +549,6 @@ bool attention_mfma_ok(int H, int Dc, int Dv, int q_dt, int kv_dt)
            Dc == 128) && Dv % 64 == 0 && Dv / 4 <= 128 && Dv <= Dc;
 }
 
-static constexpr int AM_CHUNKS = 4;  // chunks per split: 256 kept positions per workgroup
-
 int attention_splits(int top_k) { return (top_k + AM_NJ * AM_CHUNKS - 1) / (AM_NJ * AM_CHUNKS); }
 
 int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
@@ -524,8 +561,8 @@ int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv
         dim3 g(nsplit, H / 16, pg.batch);
 #define DL_AM(KQ_)                                                                                                  \
     if (Dc == KQ_ * 32)                                                                                             \
-        hipLaunchKernelGGL((k_attn_mfma<KQ_>), g, dim3(256), 0, s, (const uint16_t *)q, (const uint8_t *)kv, kv_scale, \
-                           pg.page_table, pg.max_pages_per_seq, ps_shift, sel, top_k, H, Dv, sm_scale, AM_CHUNKS,    \
+        hipLaunchKernelGGL((k_attn_mfma<KQ_, AM_CHUNKS>), g, dim3(256), 0, s, (const uint16_t *)q, (const uint8_t *)kv, \
+                           kv_scale, pg.page_table, pg.max_pages_per_seq, ps_shift, sel, top_k, H, Dv, sm_scale,     \
                            opart, ml);
         DL_AM(18) DL_AM(16) DL_AM(8) DL_AM(4)
 #undef DL_AM

@@ -209,11 +209,16 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(GemvArgs a)
     constexpr bool SW = EPI == EPI_SWIGLU;
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
     if (e >= a.n_out) return;
-    float v = 0.f, v2 = 0.f;
-    for (int kc = 0; kc < a.ksplit; kc++) {
-        v += a.part[(long)kc * a.n_out + e];
-        if (SW) v2 += a.part2[(long)kc * a.n_out + e];
+    float p1[16], p2[16];
+#pragma unroll
+    for (int kc = 0; kc < 16; kc++) {
+        p1[kc] = kc < a.ksplit ? a.part[(long)kc * a.n_out + e] : 0.f;
+        p2[kc] = (SW && kc < a.ksplit) ? a.part2[(long)kc * a.n_out + e] : 0.f;
     }
+    float v = 0.f, v2 = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 16; kc++)
+        if (kc < a.ksplit) { v += p1[kc]; if (SW) v2 += p2[kc]; }
     if (EPI == EPI_RESID) v += act_load(a.resid, a.resid_dt, e);
     if (SW) v = silu(v) * v2;
     a.out[e] = v;
@@ -328,11 +333,16 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const float *__restrict__ 
         const long row = it / nkb;
         const int kb = (int)(it % nkb);
         const long e = row * cols + kb * 128 + lane * 2;
-        v2f g = {0.f, 0.f}, u = {0.f, 0.f};
-        for (int c = 0; c < ksplit; c++) {
-            g += *(const v2f *)(pg + c * stride + e);
-            u += *(const v2f *)(pu + c * stride + e);
+        v2f gc[4], uc[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            gc[c] = c < ksplit ? *(const v2f *)(pg + c * stride + e) : v2f{0.f, 0.f};
+            uc[c] = c < ksplit ? *(const v2f *)(pu + c * stride + e) : v2f{0.f, 0.f};
         }
+        v2f g = {0.f, 0.f}, u = {0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+            if (c < ksplit) { g += gc[c]; u += uc[c]; }
         float r0 = silu(g.x) * u.x, r1 = silu(g.y) * u.y;
 #pragma unroll
         for (int s = 0; s < NS; s++) {
@@ -436,8 +446,13 @@ __global__ __launch_bounds__(256) void k_resid_reduce_split(GemvArgs a, float *_
     const long row = wave / nkb;
     const int kb = (int)(wave % nkb);
     const long e = row * D + kb * 128 + lane * 2;
+    v2f pc[16];
+#pragma unroll
+    for (int c = 0; c < 16; c++) pc[c] = c < a.ksplit ? *(const v2f *)(a.part + (long)c * a.n_out + e) : v2f{0.f, 0.f};
     v2f v = {0.f, 0.f};
-    for (int c = 0; c < a.ksplit; c++) v += *(const v2f *)(a.part + (long)c * a.n_out + e);
+#pragma unroll
+    for (int c = 0; c < 16; c++)
+        if (c < a.ksplit) v += pc[c];
     float r0 = v.x + act_load(a.resid, a.resid_dt, e), r1 = v.y + act_load(a.resid, a.resid_dt, e + 1);
     *(v2f *)(h + e) = v2f{r0, r1};
     if (!hq) return;

@@ -10,13 +10,14 @@
 
 namespace dl {
 
-static constexpr int ROUTE_EXP = 4;    // experts per wave
-static constexpr int ROUTE_TOK = 8;    // tokens per wave pass
-static constexpr int ROUTE_KC = 1024;  // hidden features per wave (16 per lane)
+static constexpr int ROUTE_EXP = 4;   // experts per wave
+static constexpr int ROUTE_TB = 4;    // tokens per pass of a wave
+static constexpr int ROUTE_KC = 512;  // hidden features per wave (8 per lane)
+static constexpr int ROUTE_MAXC = 32; // chunks: hidden size <= 16,384
 
 // Partial router logits: part[c, b, e] = sum over hidden chunk c of w_r[e, d] * h[b, d], with the fp32
-// products formed exactly in fp64 and summed in fp64.  One wave per (4 experts, chunk, 8 tokens); each lane
-// owns 16 consecutive features, so the w_r rows stream once with 16-byte loads.
+// products formed exactly in fp64 and summed in fp64.  One wave per (4 experts, chunk); each lane owns 8
+// consecutive features, holds the 4 experts' weights in fp32 and walks the tokens 4 at a time.
 __global__ __launch_bounds__(64) void k_route_partial(const float *__restrict__ h, int B, int D,
                                                       const float *__restrict__ wr, int E,
                                                       double *__restrict__ part)
@@ -24,54 +25,84 @@ __global__ __launch_bounds__(64) void k_route_partial(const float *__restrict__ 
     const int lane = threadIdx.x;
     const int e0 = blockIdx.x * ROUTE_EXP;
     const int c = blockIdx.y;
-    const int b0 = blockIdx.z * ROUTE_TOK;
-    const int d0 = c * ROUTE_KC + lane * 16;
-    const int nt = min(ROUTE_TOK, B - b0);
-    double w[ROUTE_EXP][16];
+    const int d0 = c * ROUTE_KC + lane * 8;
+    v4f w[ROUTE_EXP][2];
 #pragma unroll
-    for (int x = 0; x < ROUTE_EXP; x++) {
-        const int e = e0 + x;
+    for (int x = 0; x < ROUTE_EXP; x++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int d = d0 + q * 4;
-            v4f v = {0.f, 0.f, 0.f, 0.f};
-            if (e < E && d < D) v = *(const v4f *)(wr + (long)e * D + d);
-#pragma unroll
-            for (int i = 0; i < 4; i++) w[x][q * 4 + i] = (double)v[i];
+        for (int q = 0; q < 2; q++) {
+            const int e = e0 + x, d = d0 + q * 4;
+            w[x][q] = (e < E && d < D) ? *(const v4f *)(wr + (long)e * D + d) : v4f{0.f, 0.f, 0.f, 0.f};
         }
+    for (int b0 = 0; b0 < B; b0 += ROUTE_TB) {
+        v4f hv[ROUTE_TB][2];
+#pragma unroll
+        for (int t = 0; t < ROUTE_TB; t++)
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                const int d = d0 + q * 4;
+                hv[t][q] = (b0 + t < B && d < D) ? *(const v4f *)(h + (long)(b0 + t) * D + d) : v4f{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int x = 0; x < ROUTE_EXP; x++)
+#pragma unroll
+            for (int t = 0; t < ROUTE_TB; t++) {
+                double acc = 0.0;
+#pragma unroll
+                for (int q = 0; q < 2; q++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) acc = fma((double)w[x][q][i], (double)hv[t][q][i], acc);
+                acc = wave_sum_d(acc);
+                if (lane == 0 && e0 + x < E && b0 + t < B) part[((long)c * B + b0 + t) * E + e0 + x] = acc;
+            }
     }
-    // every token's 16 features first (all loads in flight together), then the fp64 products
-    v4f hv[ROUTE_TOK][4];
-#pragma unroll
-    for (int t = 0; t < ROUTE_TOK; t++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int d = d0 + q * 4;
-            hv[t][q] = (t < nt && d < D) ? *(const v4f *)(h + (long)(b0 + t) * D + d) : v4f{0.f, 0.f, 0.f, 0.f};
-        }
-    double acc[ROUTE_EXP][ROUTE_TOK];
-#pragma unroll
-    for (int x = 0; x < ROUTE_EXP; x++)
-#pragma unroll
-        for (int t = 0; t < ROUTE_TOK; t++) {
-            double a2 = 0.0;
-#pragma unroll
-            for (int q = 0; q < 4; q++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) a2 = fma(w[x][q * 4 + i], (double)hv[t][q][i], a2);
-            acc[x][t] = a2;
-        }
-#pragma unroll
-    for (int x = 0; x < ROUTE_EXP; x++)
-#pragma unroll
-        for (int t = 0; t < ROUTE_TOK; t++) {
-            if (t >= nt) break;
-            const double v = wave_sum_d(acc[x][t]);
-            if (lane == 0 && e0 + x < E) part[((long)c * B + b0 + t) * E + e0 + x] = v;
-        }
 }
 
-// Top-k experts per token by (logit desc, id asc) and their softmax gates; one wave per token.
+// Top-k of one token's logits by (logit desc, id asc) in one wave: each lane owns experts lane + 64 i;
+// ke rounds of a wave argmax, the owner retiring its pick.  Lane j < ke returns pick j and its softmax
+// gate over the picked logits.  (Shared by the routing entry point and the fused router + plan kernel.)
+template <int NSLOT>
+__device__ __forceinline__ void token_topk(const double *__restrict__ lrow, int E, int ke, int &my_e, float &my_gate)
+{
+    const int lane = threadIdx.x & 63;
+    double l[NSLOT];
+#pragma unroll
+    for (int i = 0; i < NSLOT; i++) {
+        const int e = lane + 64 * i;
+        l[i] = e < E ? lrow[e] : -INFINITY;
+    }
+    double top0 = 0.0, z = 0.0, my_g = 0.0;
+    my_e = 0;
+    for (int j = 0; j < ke; j++) {
+        double best = -INFINITY;
+        int bi = 0, be = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < NSLOT; i++) {
+            const int e = lane + 64 * i;
+            if (e < E && (l[i] > best || (l[i] == best && e < be))) { best = l[i]; be = e; bi = i; }
+        }
+        const int me = be;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const double ov = __shfl_xor(best, o, 64);
+            const int oe = __shfl_xor(be, o, 64);
+            if (ov > best || (ov == best && oe < be)) { best = ov; be = oe; }
+        }
+        if (me == be) {
+#pragma unroll
+            for (int i = 0; i < NSLOT; i++)
+                if (i == bi) l[i] = -INFINITY;
+        }
+        if (j == 0) top0 = best;
+        const double g = exp(best - top0);
+        z += g;
+        if (lane == j) { my_g = g; my_e = be; }
+    }
+    my_gate = (float)(my_g / z);
+}
+
+// logits64[b, e] = chunk partials summed in chunk order + bias (all threads), then one wave per token.
+template <int NSLOT>
 __global__ __launch_bounds__(256) void k_route_topk(const double *__restrict__ part, int nchunk, int B, int E, int ke,
                                                     const float *__restrict__ bias, int32_t *__restrict__ experts,
                                                     float *__restrict__ gates, float *__restrict__ logits,
@@ -81,43 +112,25 @@ __global__ __launch_bounds__(256) void k_route_topk(const double *__restrict__ p
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (b >= B) return;
     double *l = logits64 + (long)b * E;
-    // logits = chunk partials summed in chunk order, plus the bias
     for (int e = lane; e < E; e += 64) {
+        double pc[ROUTE_MAXC];
+#pragma unroll
+        for (int c = 0; c < ROUTE_MAXC; c++) pc[c] = c < nchunk ? part[((long)c * B + b) * E + e] : 0.0;
         double v = 0.0;
-        for (int c = 0; c < nchunk; c++) v += part[((long)c * B + b) * E + e];
+#pragma unroll
+        for (int c = 0; c < ROUTE_MAXC; c++)
+            if (c < nchunk) v += pc[c];
         if (bias) v += (double)bias[e];
         l[e] = v;
         if (logits) logits[(long)b * E + e] = (float)v;
     }
-    // taken[] as a bitmask over this lane's experts e = lane + 64*i
-    unsigned long long taken = 0;
-    double sel_l[32];
-    int sel_e[32];
-    for (int j = 0; j < ke; j++) {
-        double best = -INFINITY;
-        int be = 0x7FFFFFFF;
-        for (int i = 0, e = lane; e < E; i++, e += 64) {
-            if ((taken >> i) & 1ull) continue;
-            const double v = l[e];
-            if (v > best || (v == best && e < be)) { best = v; be = e; }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const double ov = __shfl_xor(best, o, 64);
-            const int oe = __shfl_xor(be, o, 64);
-            if (ov > best || (ov == best && oe < be)) { best = ov; be = oe; }
-        }
-        if ((be & 63) == lane) taken |= 1ull << (be >> 6);
-        sel_l[j] = best;
-        sel_e[j] = be;
-    }
-    if (lane == 0) {
-        double z = 0.0;
-        for (int j = 0; j < ke; j++) z += exp(sel_l[j] - sel_l[0]);
-        for (int j = 0; j < ke; j++) {
-            experts[(long)b * ke + j] = sel_e[j];
-            gates[(long)b * ke + j] = (float)(exp(sel_l[j] - sel_l[0]) / z);
-        }
+    // each lane reads back only the logits it wrote itself (same thread, same addresses)
+    int me;
+    float mg;
+    token_topk<NSLOT>(l, E, ke, me, mg);
+    if (lane < ke) {
+        experts[(long)b * ke + lane] = me;
+        gates[(long)b * ke + lane] = mg;
     }
 }
 
@@ -226,70 +239,75 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ exper
 //      (logit desc, id asc) pick the experts; gates are the softmax over the picked logits.
 //   2. the plan, exactly as k_plan, from the picked experts kept in LDS.
 static constexpr int RP_MAXE = 1024;
+
+// Exclusive scan of one int over the 1024 threads (16 waves); also returns the total.
+__device__ __forceinline__ int block_excl_scan_1024(int v, int *s_w, int &total)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    __syncthreads();
+    if (lane == 63) s_w[wv] = inc;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int w = 0; w < 16; w++) {
+        const int x = s_w[w];
+        if (w < wv) before += x;
+        total += x;
+    }
+    return before + inc - v;
+}
+
+template <int NSLOT>  // experts per lane: E <= 64 * NSLOT
 __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ part, int nchunk, int B, int E, int ke,
                                                      int S, const float *__restrict__ bias,
-                                                     int32_t *__restrict__ experts, float *__restrict__ gates,
-                                                     float *__restrict__ logits, int *__restrict__ n_active,
-                                                     int *__restrict__ n_pairs, int *__restrict__ n_groups,
-                                                     int *__restrict__ active, int *__restrict__ tok_off,
-                                                     int *__restrict__ tok_cnt, int *__restrict__ pair_tok,
-                                                     int *__restrict__ pair_idx)
+                                                     double *__restrict__ logits64, int32_t *__restrict__ experts,
+                                                     float *__restrict__ gates, float *__restrict__ logits,
+                                                     int *__restrict__ n_active, int *__restrict__ n_pairs,
+                                                     int *__restrict__ n_groups, int *__restrict__ active,
+                                                     int *__restrict__ tok_off, int *__restrict__ tok_cnt,
+                                                     int *__restrict__ pair_tok, int *__restrict__ pair_idx)
 {
     __shared__ int s_cnt[RP_MAXE];
-    __shared__ int s_scan[1024];
+    __shared__ int s_w[16];
     __shared__ int s_exp[16384];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nT = 1024;
     const int kk = ke + S;
     for (int e = tid; e < E; e += nT) s_cnt[e] = 0;
+    // 1. logits = chunk partials summed in chunk order, plus the bias
+    for (int i = tid; i < B * E; i += nT) {
+        const int b = i / E, e = i % E;
+        double pc[ROUTE_MAXC];  // every chunk's partial in flight at once, then summed in chunk order
+#pragma unroll
+        for (int c = 0; c < ROUTE_MAXC; c++) pc[c] = c < nchunk ? part[((long)c * B + b) * E + e] : 0.0;
+        double v = 0.0;
+#pragma unroll
+        for (int c = 0; c < ROUTE_MAXC; c++)
+            if (c < nchunk) v += pc[c];
+        if (bias) v += (double)bias[e];
+        logits64[i] = v;
+        if (logits) logits[i] = (float)v;
+    }
+    __syncthreads();
+    // 2. per token: the picked experts and gates
     for (int b = wv; b < B; b += 16) {
-        double l[RP_MAXE / 64];
-#pragma unroll
-        for (int i = 0; i < RP_MAXE / 64; i++) {
-            const int e = lane + 64 * i;
-            double v = -INFINITY;
-            if (e < E) {
-                v = 0.0;
-                for (int c = 0; c < nchunk; c++) v += part[((long)c * B + b) * E + e];
-                if (bias) v += (double)bias[e];
-                if (logits) logits[(long)b * E + e] = (float)v;
-            }
-            l[i] = v;
-        }
-        double top0 = 0.0, z = 0.0, my_g = 0.0;
-        int my_e = 0;
-        for (int j = 0; j < ke; j++) {
-            double best = -INFINITY;
-            int bi = 0, be = 0x7FFFFFFF;
-#pragma unroll
-            for (int i = 0; i < RP_MAXE / 64; i++) {
-                const int e = lane + 64 * i;
-                if (e < E && (l[i] > best || (l[i] == best && e < be))) { best = l[i]; be = e; bi = i; }
-            }
-            int me = be;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const double ov = __shfl_xor(best, o, 64);
-                const int oe = __shfl_xor(be, o, 64);
-                if (ov > best || (ov == best && oe < be)) { best = ov; be = oe; }
-            }
-            if (me == be) {  // the owning lane retires its expert
-#pragma unroll
-                for (int i = 0; i < RP_MAXE / 64; i++)
-                    if (i == bi) l[i] = -INFINITY;
-            }
-            if (j == 0) top0 = best;
-            const double g = exp(best - top0);
-            z += g;
-            if (lane == j) { my_g = g; my_e = be; }  // lane j keeps slot j
-            if (lane == 0) s_exp[b * ke + j] = be;
-        }
+        int me;
+        float mg;
+        token_topk<NSLOT>(logits64 + (long)b * E, E, ke, me, mg);
         if (lane < ke) {
-            experts[(long)b * ke + lane] = my_e;
-            gates[(long)b * ke + lane] = (float)(my_g / z);
+            experts[(long)b * ke + lane] = me;
+            gates[(long)b * ke + lane] = mg;
+            s_exp[b * ke + lane] = me;
         }
     }
     __syncthreads();
+    // 3. dispatch plan (same rules as k_plan)
     for (int i = tid; i < B * ke; i += nT) atomicAdd(&s_cnt[s_exp[i]], 1);
     __syncthreads();
     const int per = (E + nT - 1) / nT;
@@ -298,26 +316,9 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
         const int e = tid * per + i;
         if (e < E && s_cnt[e] > 0) { na++; np += s_cnt[e]; }
     }
-    s_scan[tid] = na;
-    __syncthreads();
-    for (int o = 1; o < nT; o <<= 1) {
-        const int v = tid >= o ? s_scan[tid - o] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    const int a0 = s_scan[tid] - na;
-    const int na_tot = s_scan[nT - 1];
-    __syncthreads();
-    s_scan[tid] = np;
-    __syncthreads();
-    for (int o = 1; o < nT; o <<= 1) {
-        const int v = tid >= o ? s_scan[tid - o] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    int p0 = s_scan[tid] - np;
+    int na_tot, np_tot;
+    const int a0 = block_excl_scan_1024(na, s_w, na_tot);
+    int p0 = block_excl_scan_1024(np, s_w, np_tot);
     int a = a0;
     for (int i = 0; i < per; i++) {
         const int e = tid * per + i;
@@ -352,11 +353,11 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
     for (int e = tid; e < E; e += nT) mx = max(mx, s_cnt[e]);
     mx = wave_max_i(mx);
     __syncthreads();
-    if (lane == 0) s_scan[wv] = mx;
+    if (lane == 0) s_w[wv] = mx;
     __syncthreads();
     if (tid == 0) {
         int m2 = 0;
-        for (int w = 0; w < nT / 64; w++) m2 = max(m2, s_scan[w]);
+        for (int w = 0; w < 16; w++) m2 = max(m2, s_w[w]);
         *n_active = na_tot + S;
         *n_pairs = routed_pairs + S * B;
         *n_groups = (m2 + 15) / 16;
@@ -374,11 +375,21 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, co
     if (d >= D) return;
     const int kk = ke + S;
     float acc = resid ? act_load(resid, resid_dt, (long)b * D + d) : 0.f;
-    for (int j = 0; j < ke; j++) {
-        const int p = pair_idx[(long)b * kk + j];
-        acc = fmaf(gates[(long)b * ke + j], F[(long)p * D + d], acc);
+    // all pair indices, then all expert outputs in flight at once; summed in slot order
+    constexpr int MAXK = 40;
+    float f[MAXK], g[MAXK];
+#pragma unroll
+    for (int j = 0; j < MAXK; j++) {
+        const int p = j < kk ? pair_idx[(long)b * kk + j] : 0;
+        f[j] = j < kk ? F[(long)p * D + d] : 0.f;
+        g[j] = j < ke ? gates[(long)b * ke + j] : 1.f;
     }
-    for (int s = 0; s < S; s++) acc += F[(long)pair_idx[(long)b * kk + ke + s] * D + d];
+#pragma unroll
+    for (int j = 0; j < MAXK; j++) {
+        if (j >= kk) break;
+        if (j < ke) acc = fmaf(g[j], f[j], acc);
+        else acc += f[j];
+    }
     if (out32) out32[(long)b * D + d] = acc;
     if (out_dt == DL_BF16) ((uint16_t *)out)[(long)b * D + d] = f32_to_bf16(acc);
     else ((float *)out)[(long)b * D + d] = acc;
@@ -390,28 +401,35 @@ int launch_route(const float *h, int B, int D, const float *w_r, const float *bi
                  float *gates, float *logits, double *logits64, double *part, hipStream_t s)
 {
     const int nc = route_chunks(D);
-    dim3 g((E + ROUTE_EXP - 1) / ROUTE_EXP, nc, (B + ROUTE_TOK - 1) / ROUTE_TOK);
+    dim3 g((E + ROUTE_EXP - 1) / ROUTE_EXP, nc);
     hipLaunchKernelGGL(k_route_partial, g, dim3(64), 0, s, h, B, D, w_r, E, part);
-    hipLaunchKernelGGL(k_route_topk, dim3((B + 3) / 4), dim3(256), 0, s, part, nc, B, E, ke, bias, experts, gates,
-                       logits, logits64);
+    if (E <= 256)
+        hipLaunchKernelGGL((k_route_topk<4>), dim3((B + 3) / 4), dim3(256), 0, s, part, nc, B, E, ke, bias, experts,
+                           gates, logits, logits64);
+    else
+        hipLaunchKernelGGL((k_route_topk<16>), dim3((B + 3) / 4), dim3(256), 0, s, part, nc, B, E, ke, bias, experts,
+                           gates, logits, logits64);
     return hip_check("route");
 }
 
-bool route_plan_ok(int E, int ke, int B) { return E <= RP_MAXE && ke <= 16 && (long)B * ke <= 16384; }
+bool route_plan_ok(int E, int ke, int B) { return E <= RP_MAXE && ke <= 32 && (long)B * ke <= 16384; }
 
 int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s)
 {
-    dim3 g((E + ROUTE_EXP - 1) / ROUTE_EXP, route_chunks(D), (B + ROUTE_TOK - 1) / ROUTE_TOK);
+    dim3 g((E + ROUTE_EXP - 1) / ROUTE_EXP, route_chunks(D));
     hipLaunchKernelGGL(k_route_partial, g, dim3(64), 0, s, h, B, D, w_r, E, part);
     return hip_check("route_partial");
 }
 
 int launch_route_plan(const double *part, int B, int D, const float *bias, int E, int ke, int S, int32_t *experts,
-                      float *gates, float *logits, const MoePlan &p, hipStream_t s)
+                      float *gates, float *logits, double *logits64, const MoePlan &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_route_plan, dim3(1), dim3(1024), 0, s, part, route_chunks(D), B, E, ke, S, bias, experts,
-                       gates, logits, p.n_active, p.n_pairs, p.n_groups, p.active, p.tok_off, p.tok_cnt, p.pair_tok,
-                       p.pair_idx);
+#define DL_RP(NS_)                                                                                                  \
+    hipLaunchKernelGGL((k_route_plan<NS_>), dim3(1), dim3(1024), 0, s, part, route_chunks(D), B, E, ke, S, bias,     \
+                       logits64, experts, gates, logits, p.n_active, p.n_pairs, p.n_groups, p.active, p.tok_off,     \
+                       p.tok_cnt, p.pair_tok, p.pair_idx)
+    if (E <= 256) DL_RP(4); else DL_RP(16);
+#undef DL_RP
     return hip_check("route_plan");
 }
 
