@@ -10,8 +10,10 @@ layer instances (separate weights, caches and inputs; ~10.5 GB each).  Prints on
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,6 +47,43 @@ def algorithmic_bytes(spec, lens, n_touched: int) -> dict:
                 total=keys + kv + wuv + wo + wr + gu + dn)
 
 
+# HBM traffic of the gate/up kernel as read by rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE per dispatch,
+# scaled by what the same counters read for a plain copy of known size).  Reported only while the kernel's
+# source is the one the counters were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_b8-128k.md")
+KERNEL_SOURCES = ("sparse_attention_moe_amd/csrc/k_gemv.hip", "sparse_attention_moe_amd/csrc/dl_common.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^- (\w+): (\S+)\s*$", text, re.M))
+    if vals.get("kernel_source_sha256") != kernel_source_hash() or vals.get("workload") != workload:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+def copy_calibration(mib: int, reps: int = 3):
+    """A plain device copy of known size, for scaling the PMC byte counters (not timed, not reported)."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: {reps} x {mib << 20} bytes", file=sys.stderr, flush=True)
+
+
 def touched(spec, experts: np.ndarray) -> int:
     return len(set(int(e) for e in experts.ravel())) + spec.n_shared
 
@@ -76,6 +115,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the run, copy this many MiB device-to-device (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -138,13 +179,15 @@ def main():
         "phase_ms": {k: round(v, 4) for k, v in ph.items()},
         "roofline": {"kernel": "k_gemv_fp8<2,SWIGLU> (expert gate/up)", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(spec.name),
                      "bytes_per_launch": int(avg_bytes["expert_gate_up"]),
                      "ms_per_launch": round(ph["expert_gate_up"], 4)},
     }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(spec, insts[0], list(range(args.cpu_rows)))
     print(json.dumps(rec), flush=True)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
 
 
 if __name__ == "__main__":
