@@ -23,11 +23,11 @@
  *       is not ordered behind work already queued.
  *
  * Conventions for every entry point
- *   Memory      Every tensor pointer is a DEVICE pointer owned by the caller, row-major and
- *               densely packed in the stated shape.  The library never allocates, frees or keeps
- *               device memory; scratch comes from the caller's workspace `ws` of `ws_bytes` bytes
- *               (query the size first; 256-byte alignment).  Inputs are never modified; outputs are
- *               overwritten completely (including -1 padding).  Descriptor structs (dl_pages,
+ *   Memory      Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte aligned,
+ *               row-major and densely packed in the stated shape.  The library never allocates,
+ *               frees or keeps device memory; scratch comes from the caller's workspace `ws` of
+ *               `ws_bytes` bytes (query the size first; 256-byte alignment).  Inputs are never
+ *               modified; outputs are overwritten completely (including -1 padding).  Descriptor structs (dl_pages,
  *               dl_mat, dl_layer_desc, dl_layer_io) live in HOST memory and are read during the
  *               call only.
  *   Streams     Work is only enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
@@ -175,7 +175,8 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
  *   w_gate, w_up: count = n_routed + n_shared, rows = inter, cols = D;
  *   w_down: count = n_routed + n_shared, rows = D, cols = inter;
  *   residual fp32 [B, D] nullable; out [B, D] in out_dt (DL_F32 or DL_BF16, rounded once, RNE).
- * Limits: B * (top_k + n_shared) <= 16384; top_k + n_shared <= 40; n_routed <= 1024; n_routed + n_shared <= 4096.  With FP8 weights the
+ * Limits: D % 4 == 0; B * (top_k + n_shared) <= 16384; top_k + n_shared <= 40; n_routed <= 1024;
+ * n_routed + n_shared <= 4096.  With FP8 weights the
  * activations enter the matrix cores as two FP8 parts (value and remainder) with per-128-block
  * scales.  Workspace: dl_moe_ffn_workspace(...). */
 size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared);

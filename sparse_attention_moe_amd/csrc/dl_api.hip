@@ -483,6 +483,7 @@ static int check_ffn_shapes(int B, int D, int I, int ke, int E, int S, const dl_
                             const dl_mat *wd)
 {
     if (B < 1 || D < 1 || I < 1) return fail(DL_ERR_SHAPE, "ffn B=%d D=%d I=%d", B, D, I);
+    if (D % 4) return fail(DL_ERR_UNSUPPORTED, "ffn hidden size %d (multiple of 4)", D);
     if (ke < 1 || ke > 32 || ke > E) return fail(DL_ERR_SHAPE, "expert top_k %d of %d", ke, E);
     if (ke + S > 40) return fail(DL_ERR_UNSUPPORTED, "top_k + shared experts %d (<= 40)", ke + S);
     if (S < 0 || E > 1024 || E + S > 4096) return fail(DL_ERR_SHAPE, "experts %d + %d", E, S);

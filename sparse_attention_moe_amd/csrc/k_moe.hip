@@ -364,35 +364,52 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
     }
 }
 
-// out[b, d] = resid[b, d] + sum_j gate[b, j] f_j[d] + sum_s f_s[d], in that order.
+// out[b, d] = resid[b, d] + sum_j gate[b, j] f_j[d] + sum_s f_s[d], in that order.  A thread owns 4
+// consecutive features of one token; the token's pair indices and gates are wave-uniform (scalar loads), and
+// the expert outputs are fetched 8 slots at a time so their loads are in flight together.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, const int *__restrict__ pair_idx,
                                                  const float *__restrict__ gates, int B, int D, int ke, int S,
                                                  const void *__restrict__ resid, int resid_dt, void *__restrict__ out,
                                                  int out_dt, float *__restrict__ out32)
 {
     const int b = blockIdx.y;
-    const int d = blockIdx.x * 256 + threadIdx.x;
+    const int d = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (d >= D) return;
     const int kk = ke + S;
-    float acc = resid ? act_load(resid, resid_dt, (long)b * D + d) : 0.f;
-    // all pair indices, then all expert outputs in flight at once; summed in slot order
-    constexpr int MAXK = 40;
-    float f[MAXK], g[MAXK];
+    const long row = (long)b * D + d;
+    v4f acc;
+    if (!resid) acc = v4f{0.f, 0.f, 0.f, 0.f};
+    else if (resid_dt == DL_BF16) {
+        const uint2 r = *(const uint2 *)((const uint16_t *)resid + row);
+        acc = v4f{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
+                  __uint_as_float(r.y & 0xFFFF0000u)};
+    } else acc = *(const v4f *)((const float *)resid + row);
+    const int *pi = pair_idx + (long)b * kk;
+    const float *gt = gates + (long)b * ke;
+    for (int j0 = 0; j0 < kk; j0 += 8) {
+        v4f f[8];
 #pragma unroll
-    for (int j = 0; j < MAXK; j++) {
-        const int p = j < kk ? pair_idx[(long)b * kk + j] : 0;
-        f[j] = j < kk ? F[(long)p * D + d] : 0.f;
-        g[j] = j < ke ? gates[(long)b * ke + j] : 1.f;
-    }
+        for (int u = 0; u < 8; u++)
+            if (j0 + u < kk) f[u] = *(const v4f *)(F + (long)pi[j0 + u] * D + d);
 #pragma unroll
-    for (int j = 0; j < MAXK; j++) {
-        if (j >= kk) break;
-        if (j < ke) acc = fmaf(g[j], f[j], acc);
-        else acc += f[j];
+        for (int u = 0; u < 8; u++) {
+            const int j = j0 + u;
+            if (j < kk) {
+                if (j < ke) {
+                    const float g = gt[j];
+                    acc.x = fmaf(g, f[u].x, acc.x); acc.y = fmaf(g, f[u].y, acc.y);
+                    acc.z = fmaf(g, f[u].z, acc.z); acc.w = fmaf(g, f[u].w, acc.w);
+                } else acc += f[u];
+            }
+        }
     }
-    if (out32) out32[(long)b * D + d] = acc;
-    if (out_dt == DL_BF16) ((uint16_t *)out)[(long)b * D + d] = f32_to_bf16(acc);
-    else ((float *)out)[(long)b * D + d] = acc;
+    if (out32) *(v4f *)(out32 + row) = acc;
+    if (out_dt == DL_BF16) {
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+        o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+        *(uint2 *)((uint16_t *)out + row) = o;
+    } else *(v4f *)((float *)out + row) = acc;
 }
 
 int route_chunks(int D) { return (D + ROUTE_KC - 1) / ROUTE_KC; }
@@ -444,7 +461,7 @@ int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePl
 int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
                    const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s)
 {
-    dim3 g((D + 255) / 256, B);
+    dim3 g((D / 4 + 255) / 256, B);
     hipLaunchKernelGGL(k_combine, g, dim3(256), 0, s, F, p.pair_idx, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
                        out32);
     return hip_check("combine");
