@@ -442,7 +442,7 @@ struct LayerWs {
     int32_t *sel;
     AttnWs attn;
     float *o, *h;
-    double *logits64, *rpart;
+    double *rpart;
     int32_t *experts;
     float *gates;
     FfnWs ffn;
@@ -471,7 +471,6 @@ static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, c
         L.attn.kpart = w.take<float>((long)MAX_KSPLIT * B * d->w_o.rows);
     }
     L.h = (io && io->h) ? io->h : w.take<float>((long)B * d->D);
-    L.logits64 = w.take<double>((long)B * d->n_routed);
     L.rpart = w.take<double>((long)route_chunks(d->D) * B * d->n_routed);
     L.experts = (io && io->experts) ? io->experts : w.take<int32_t>((long)B * d->expert_top_k);
     L.gates = (io && io->gates) ? io->gates : w.take<float>((long)B * d->expert_top_k);
@@ -615,7 +614,6 @@ int dl_sparse_attn_decode(const dl_pages *pages, const void *q, int32_t q_dt, co
 size_t dl_moe_route_workspace(int32_t B, int32_t D, int32_t n_experts)
 {
     Ws w(nullptr);
-    w.take<double>((long)B * n_experts);
     w.take<double>((long)route_chunks(D) * B * n_experts);
     return w.used();
 }
@@ -632,9 +630,8 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
     DL_TRY(check_ws(ws, ws_bytes, dl_moe_route_workspace(B, D, n_experts)));
     (void)hipGetLastError();
     Ws w(ws);
-    double *l64 = w.take<double>((long)B * n_experts);
     double *part = w.take<double>((long)route_chunks(D) * B * n_experts);
-    return launch_route(h, B, D, w_r, bias, n_experts, top_k, experts, gates, logits, l64, part, (hipStream_t)stream);
+    return launch_route(h, B, D, w_r, bias, n_experts, top_k, experts, gates, logits, part, (hipStream_t)stream);
 }
 
 size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared)
@@ -721,10 +718,10 @@ int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_
     if (fuse_route) {
         DL_TRY(launch_route_partial(L.h, B, d->D, d->w_r, d->n_routed, L.rpart, s));
         DL_TRY(launch_route_plan(L.rpart, B, d->D, d->r_bias, d->n_routed, d->expert_top_k, d->n_shared, L.experts,
-                                 L.gates, nullptr, L.logits64, L.ffn.plan, s));
+                                 L.gates, nullptr, &L.ffn.plan, s));
     } else {
         DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates, nullptr,
-                            L.logits64, L.rpart, s));
+                            L.rpart, s));
     }
     mk.at(4);
     return run_ffn(L.h, B, d->D, d->inter, L.experts, L.gates, d->expert_top_k, &d->w_gate, &d->w_up, &d->w_down,

@@ -126,15 +126,15 @@ struct MoePlan {
     int *pair_idx;   // [B, ke+S]
 };
 int route_chunks(int D);  // hidden-size chunks of the router's partial dot products
-// logits64 [B, E] and part [route_chunks(D), B, E] are scratch (fp64).
+// part [route_chunks(D), B, E] is scratch (fp64).
 int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
-                 float *gates, float *logits, double *logits64, double *part, hipStream_t s);
+                 float *gates, float *logits, double *part, hipStream_t s);
 int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s);
-// Router top-k (from launch_route's chunk partials) fused with the dispatch plan: E <= 1024, ke <= 16.
+// Router top-k (from launch_route_partial's chunk partials), with p != nullptr fused with the dispatch plan.
 bool route_plan_ok(int E, int ke, int B);
 int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s);
 int launch_route_plan(const double *part, int B, int D, const float *bias, int E, int ke, int S, int32_t *experts,
-                      float *gates, float *logits, double *logits64, const MoePlan &p, hipStream_t s);
+                      float *gates, float *logits, const MoePlan *p, hipStream_t s);
 int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
                    const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s);
 

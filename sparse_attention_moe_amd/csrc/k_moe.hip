@@ -8,61 +8,93 @@
 #include "dl_common.h"
 #include "dl_internal.h"
 
+#include <string.h>
+
 namespace dl {
 
-static constexpr int ROUTE_EXP = 4;   // experts per wave
-static constexpr int ROUTE_TB = 4;    // tokens per pass of a wave
-static constexpr int ROUTE_KC = 512;  // hidden features per wave (8 per lane)
+static constexpr int ROUTE_KC = 512;  // hidden features per workgroup (4 waves x 128)
 static constexpr int ROUTE_MAXC = 32; // chunks: hidden size <= 16,384
+static constexpr int RP_MAXE = 1024;  // experts the router + plan kernel handles
+static constexpr int RP_LCAP = 8192;  // logits held in LDS at once (tokens per block = RP_LCAP / E)
 
-// Partial router logits: part[c, b, e] = sum over hidden chunk c of w_r[e, d] * h[b, d], with the fp32
-// products formed exactly in fp64 and summed in fp64.  One wave per (4 experts, chunk); each lane owns 8
-// consecutive features, holds the 4 experts' weights in fp32 and walks the tokens 4 at a time.
-__global__ __launch_bounds__(64) void k_route_partial(const float *__restrict__ h, int B, int D,
-                                                      const float *__restrict__ wr, int E,
-                                                      double *__restrict__ part)
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+// Partial router logits on the fp64 matrix cores: part[c, b, e] = sum over hidden chunk c of w_r[e, d] * h[b, d].
+// A workgroup owns 16 experts (the M side of v_mfma_f64_16x16x4f64) and a 512-feature chunk, one 128-feature
+// quarter per wave; 16 tokens form the N side.  Every fp32 product is exact in fp64 and the sums are fp64.
+// Lane (r, g) = (lane % 16, lane / 16) holds expert r's and token r's features 16 j + 4 g .. + 4 (j < 8);
+// instruction i of a group takes the i-th of those four, so A and B agree on the K index.  The four
+// quarters are added in order through LDS.
+__global__ __launch_bounds__(256) void k_route_partial(const float *__restrict__ h, int B, int D,
+                                                       const float *__restrict__ wr, int E, double *__restrict__ part)
 {
-    const int lane = threadIdx.x;
-    const int e0 = blockIdx.x * ROUTE_EXP;
-    const int c = blockIdx.y;
-    const int d0 = c * ROUTE_KC + lane * 8;
-    v4f w[ROUTE_EXP][2];
+    __shared__ double s_d[4][16][17];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int e0 = blockIdx.x * 16, c = blockIdx.y;
+    const int kq = c * ROUTE_KC + w * 128 + 4 * g;
+    const int e = e0 + r;
+    v4f wv[8];
 #pragma unroll
-    for (int x = 0; x < ROUTE_EXP; x++)
+    for (int j = 0; j < 8; j++) {
+        const int k = kq + 16 * j;
+        wv[j] = (e < E && k < D) ? *(const v4f *)(wr + (long)e * D + k) : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int t0 = 0; t0 < B; t0 += 16) {
+        const int t = t0 + r;
+        v4f hv[8];
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
-            const int e = e0 + x, d = d0 + q * 4;
-            w[x][q] = (e < E && d < D) ? *(const v4f *)(wr + (long)e * D + d) : v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 8; j++) {
+            const int k = kq + 16 * j;
+            hv[j] = (t < B && k < D) ? *(const v4f *)(h + (long)t * D + k) : v4f{0.f, 0.f, 0.f, 0.f};
         }
-    for (int b0 = 0; b0 < B; b0 += ROUTE_TB) {
-        v4f hv[ROUTE_TB][2];
+        v4d acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int t = 0; t < ROUTE_TB; t++)
+        for (int j = 0; j < 8; j++)
 #pragma unroll
-            for (int q = 0; q < 2; q++) {
-                const int d = d0 + q * 4;
-                hv[t][q] = (b0 + t < B && d < D) ? *(const v4f *)(h + (long)(b0 + t) * D + d) : v4f{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int i = 0; i < 4; i++)
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wv[j][i], (double)hv[j][i], acc, 0, 0, 0);
+        // the fp64 instruction's result layout: acc[i] of lane (r, g) = row 4 i + g (expert), column r (token)
 #pragma unroll
-        for (int x = 0; x < ROUTE_EXP; x++)
-#pragma unroll
-            for (int t = 0; t < ROUTE_TB; t++) {
-                double acc = 0.0;
-#pragma unroll
-                for (int q = 0; q < 2; q++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) acc = fma((double)w[x][q][i], (double)hv[t][q][i], acc);
-                acc = wave_sum_d(acc);
-                if (lane == 0 && e0 + x < E && b0 + t < B) part[((long)c * B + b0 + t) * E + e0 + x] = acc;
-            }
+        for (int i = 0; i < 4; i++) s_d[w][4 * i + g][r] = acc[i];
+        __syncthreads();
+        {
+            const int ee = threadIdx.x >> 4, tt = threadIdx.x & 15;
+            if (e0 + ee < E && t0 + tt < B)
+                part[((long)c * B + t0 + tt) * E + e0 + ee] =
+                    ((s_d[0][ee][tt] + s_d[1][ee][tt]) + s_d[2][ee][tt]) + s_d[3][ee][tt];
+        }
+        __syncthreads();
     }
 }
 
-// Top-k of one token's logits by (logit desc, id asc) in one wave: each lane owns experts lane + 64 i;
-// ke rounds of a wave argmax, the owner retiring its pick.  Lane j < ke returns pick j and its softmax
-// gate over the picked logits.  (Shared by the routing entry point and the fused router + plan kernel.)
+// ------------------------------------------------------------------ wave reductions on the DPP network
+// Maximum of an unsigned over the wave, broadcast.  Row prefix maxima (shifts 1, 2, 4, 8), then rows are
+// combined with the row-broadcast forms; lane 63 ends up with the maximum.  Zero is the identity.
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v)
+{
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ unsigned wave_min_u32(unsigned v) { return ~wave_max_u32(~v); }
+
+// Order-preserving map of a float to an unsigned (x < y  =>  key(x) < key(y)); every finite value and the
+// infinities map above 0.
+__device__ __forceinline__ unsigned ordered_key(float f)
+{
+    const unsigned u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exact top-k of one token's fp64 logits by (logit desc, id asc) in one wave: each lane owns experts
+// lane + 64 i; ke rounds of a wave argmax, the owner retiring its pick.  Lane j < ke returns pick j.
 template <int NSLOT>
-__device__ __forceinline__ void token_topk(const double *__restrict__ lrow, int E, int ke, int &my_e, float &my_gate)
+__device__ __forceinline__ int token_topk_exact(const double *lrow, int E, int ke)
 {
     const int lane = threadIdx.x & 63;
     double l[NSLOT];
@@ -71,8 +103,7 @@ __device__ __forceinline__ void token_topk(const double *__restrict__ lrow, int 
         const int e = lane + 64 * i;
         l[i] = e < E ? lrow[e] : -INFINITY;
     }
-    double top0 = 0.0, z = 0.0, my_g = 0.0;
-    my_e = 0;
+    int my_e = 0;
     for (int j = 0; j < ke; j++) {
         double best = -INFINITY;
         int bi = 0, be = 0x7FFFFFFF;
@@ -93,275 +124,242 @@ __device__ __forceinline__ void token_topk(const double *__restrict__ lrow, int 
             for (int i = 0; i < NSLOT; i++)
                 if (i == bi) l[i] = -INFINITY;
         }
-        if (j == 0) top0 = best;
-        const double g = exp(best - top0);
-        z += g;
-        if (lane == j) { my_g = g; my_e = be; }
+        if (lane == j) my_e = be;
     }
-    my_gate = (float)(my_g / z);
+    return my_e;
 }
 
-// logits64[b, e] = chunk partials summed in chunk order + bias (all threads), then one wave per token.
+// Top-k of one token in one wave.  Selection runs on fp32 keys of the fp64 logits (an order-preserving
+// map: a strictly larger key means a strictly larger logit) with two DPP reductions per round: the
+// largest key, then the lowest expert id holding it.  ke + 1 rounds are taken; when no two of those
+// ke + 1 keys are equal, the keys order the picks and the boundary exactly as the fp64 logits do.
+// Otherwise (a rounding tie) the exact fp64 selection decides.  Lane j < ke returns pick j.
 template <int NSLOT>
-__global__ __launch_bounds__(256) void k_route_topk(const double *__restrict__ part, int nchunk, int B, int E, int ke,
-                                                    const float *__restrict__ bias, int32_t *__restrict__ experts,
-                                                    float *__restrict__ gates, float *__restrict__ logits,
-                                                    double *__restrict__ logits64)
+__device__ __forceinline__ int token_topk(const double *lrow, int E, int ke)
 {
     const int lane = threadIdx.x & 63;
-    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (b >= B) return;
-    double *l = logits64 + (long)b * E;
-    for (int e = lane; e < E; e += 64) {
-        double pc[ROUTE_MAXC];
+    unsigned key[NSLOT];
 #pragma unroll
-        for (int c = 0; c < ROUTE_MAXC; c++) pc[c] = c < nchunk ? part[((long)c * B + b) * E + e] : 0.0;
-        double v = 0.0;
+    for (int i = 0; i < NSLOT; i++) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? ordered_key((float)lrow[e]) : 0u;
+    }
+    int my_e = 0;
+    unsigned prev = 0;
+    bool tie = false;
+    const int rounds = ke < E ? ke + 1 : ke;
+    for (int j = 0; j < rounds; j++) {
+        unsigned bk = 0;
+        int bi = 0;
 #pragma unroll
-        for (int c = 0; c < ROUTE_MAXC; c++)
-            if (c < nchunk) v += pc[c];
-        if (bias) v += (double)bias[e];
-        l[e] = v;
-        if (logits) logits[(long)b * E + e] = (float)v;
+        for (int i = 0; i < NSLOT; i++)
+            if (key[i] > bk) { bk = key[i]; bi = i; }
+        const unsigned K = wave_max_u32(bk);
+        const unsigned id = wave_min_u32(bk == K ? (unsigned)(lane + 64 * bi) : 0xFFFFFFFFu);
+        if (j > 0 && K == prev) tie = true;
+        prev = K;
+        if (j < ke) {
+            if (lane == (int)(id & 63)) {
+#pragma unroll
+                for (int i = 0; i < NSLOT; i++)
+                    if (i == (int)(id >> 6)) key[i] = 0u;
+            }
+            if (lane == j) my_e = (int)id;
+        }
     }
-    // each lane reads back only the logits it wrote itself (same thread, same addresses)
-    int me;
-    float mg;
-    token_topk<NSLOT>(l, E, ke, me, mg);
-    if (lane < ke) {
-        experts[(long)b * ke + lane] = me;
-        gates[(long)b * ke + lane] = mg;
-    }
+    if (tie) my_e = token_topk_exact<NSLOT>(lrow, E, ke);
+    return my_e;
 }
 
-// Dispatch plan in one workgroup: active experts in ascending id (shared experts last), each
-// expert's tokens in ascending order, and the pair index of every (token, slot).
-__global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ experts, int B, int ke, int E, int S,
-                                               int *__restrict__ n_active, int *__restrict__ n_pairs,
-                                               int *__restrict__ n_groups,
-                                               int *__restrict__ active, int *__restrict__ tok_off,
-                                               int *__restrict__ tok_cnt, int *__restrict__ pair_tok,
-                                               int *__restrict__ pair_idx)
+// ------------------------------------------------------------------ dispatch plan
+// From the picks s_exp[b * ke + j] (in LDS) of a whole workgroup of 1024 threads: active experts in
+// ascending id (shared experts last), each expert's pairs in (token, slot) order, and the pair index of
+// every (token, slot).  `distinct`: no token picks an expert twice (router output), so an expert's pair
+// rank is the number of earlier tokens in its token mask (B <= 64); otherwise the earlier picks are counted.
+__device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool distinct, int *s_cnt, int *s_off,
+                           unsigned long long *s_mask, const MoePlan &p)
 {
-    __shared__ int s_cnt[4096];
-    __shared__ int s_scan[1024];
-    __shared__ int s_exp[16384];
-    const int tid = threadIdx.x;
-    const int nT = 1024;
-    const int per = (E + nT - 1) / nT;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nT = blockDim.x;
     const int kk = ke + S;
-    // tokens per routed expert
-    for (int e = tid; e < E; e += nT) s_cnt[e] = 0;
+    const int np = B * ke;
+    const bool use_mask = distinct && B <= 64;
+    for (int e = tid; e < E; e += nT) { s_cnt[e] = 0; s_mask[e] = 0ull; }
     __syncthreads();
-    for (int i = tid; i < B * ke; i += nT) {
-        const int e = experts[i];
-        s_exp[i] = e;
+    for (int i = tid; i < np; i += nT) {
+        const int e = s_exp[i];
         atomicAdd(&s_cnt[e], 1);
+        if (use_mask) atomicOr(&s_mask[e], 1ull << (i / ke));
     }
     __syncthreads();
-    // thread t owns experts [t*per, (t+1)*per): count its active experts and pairs
-    int na = 0, np = 0;
-    for (int i = 0; i < per; i++) {
-        const int e = tid * per + i;
-        if (e < E && s_cnt[e] > 0) { na++; np += s_cnt[e]; }
-    }
-    // exclusive scans of the active-expert and pair counts
-    s_scan[tid] = na;
-    __syncthreads();
-    for (int o = 1; o < nT; o <<= 1) {
-        const int v = tid >= o ? s_scan[tid - o] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    const int a0 = s_scan[tid] - na;
-    const int na_tot = s_scan[nT - 1];
-    __syncthreads();
-    s_scan[tid] = np;
-    __syncthreads();
-    for (int o = 1; o < nT; o <<= 1) {
-        const int v = tid >= o ? s_scan[tid - o] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    int p0 = s_scan[tid] - np;
-    int a = a0;
-    for (int i = 0; i < per; i++) {
-        const int e = tid * per + i;
-        if (e >= E || s_cnt[e] == 0) continue;
-        active[a] = e;
-        tok_off[a] = p0;
-        tok_cnt[a] = s_cnt[e];
-        int p = p0;
-        for (int b = 0; b < B; b++)
-            for (int j = 0; j < ke; j++)
-                if (s_exp[b * ke + j] == e) {
-                    pair_tok[p] = b;
-                    pair_idx[(long)b * kk + j] = p;
-                    p++;
-                }
-        p0 = p;
-        a++;
-    }
-    // shared experts: every token, after all routed pairs
-    const int routed_pairs = B * ke;
-    for (int i = tid; i < S * B; i += nT) {
-        const int s = i / B, b = i % B;
-        const int p = routed_pairs + s * B + b;
-        pair_tok[p] = b;
-        pair_idx[(long)b * kk + ke + s] = p;
-    }
-    if (tid < S) {
-        active[na_tot + tid] = E + tid;
-        tok_off[na_tot + tid] = routed_pairs + tid * B;
-        tok_cnt[na_tot + tid] = B;
-    }
-    // largest token group count over the active experts (shared experts have B tokens)
-    int mx = S > 0 ? B : 0;
-    for (int e = tid; e < E; e += nT) mx = max(mx, s_cnt[e]);
-    mx = wave_max_i(mx);
-    __syncthreads();
-    if ((tid & 63) == 0) s_scan[tid >> 6] = mx;
-    __syncthreads();
-    if (tid == 0) {
-        int m2 = 0;
-        for (int w = 0; w < nT / 64; w++) m2 = max(m2, s_scan[w]);
-        *n_active = na_tot + S;
-        *n_pairs = routed_pairs + S * B;
-        *n_groups = (m2 + 15) / 16;
-    }
-}
-
-// Router top-k fused with the dispatch plan, one workgroup of 1024 threads:
-//   1. wave w takes tokens b = w, w + 16, ...: each lane owns experts e = lane + 64 i (i < 16), whose logit is
-//      the sum of the chunk partials (in chunk order) plus the bias; ke rounds of a wave argmax by
-//      (logit desc, id asc) pick the experts; gates are the softmax over the picked logits.
-//   2. the plan, exactly as k_plan, from the picked experts kept in LDS.
-static constexpr int RP_MAXE = 1024;
-
-// Exclusive scan of one int over the 1024 threads (16 waves); also returns the total.
-__device__ __forceinline__ int block_excl_scan_1024(int v, int *s_w, int &total)
-{
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int inc = v;
+    if (tid < 64) {
+        // lane owns experts [lane * per, (lane + 1) * per)
+        const int per = (E + 63) / 64;
+        int na = 0, npl = 0, mx = 0;
+        for (int i = 0; i < per; i++) {
+            const int e = lane * per + i;
+            if (e < E) {
+                const int c = s_cnt[e];
+                na += c > 0;
+                npl += c;
+                mx = max(mx, c);
+            }
+        }
+        int ia = na, ip = npl;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += t;
-    }
-    __syncthreads();
-    if (lane == 63) s_w[wv] = inc;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-    for (int w = 0; w < 16; w++) {
-        const int x = s_w[w];
-        if (w < wv) before += x;
-        total += x;
-    }
-    return before + inc - v;
-}
-
-template <int NSLOT>  // experts per lane: E <= 64 * NSLOT
-__global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ part, int nchunk, int B, int E, int ke,
-                                                     int S, const float *__restrict__ bias,
-                                                     double *__restrict__ logits64, int32_t *__restrict__ experts,
-                                                     float *__restrict__ gates, float *__restrict__ logits,
-                                                     int *__restrict__ n_active, int *__restrict__ n_pairs,
-                                                     int *__restrict__ n_groups, int *__restrict__ active,
-                                                     int *__restrict__ tok_off, int *__restrict__ tok_cnt,
-                                                     int *__restrict__ pair_tok, int *__restrict__ pair_idx)
-{
-    __shared__ int s_cnt[RP_MAXE];
-    __shared__ int s_w[16];
-    __shared__ int s_exp[16384];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int nT = 1024;
-    const int kk = ke + S;
-    for (int e = tid; e < E; e += nT) s_cnt[e] = 0;
-    // 1. logits = chunk partials summed in chunk order, plus the bias
-    for (int i = tid; i < B * E; i += nT) {
-        const int b = i / E, e = i % E;
-        double pc[ROUTE_MAXC];  // every chunk's partial in flight at once, then summed in chunk order
-#pragma unroll
-        for (int c = 0; c < ROUTE_MAXC; c++) pc[c] = c < nchunk ? part[((long)c * B + b) * E + e] : 0.0;
-        double v = 0.0;
-#pragma unroll
-        for (int c = 0; c < ROUTE_MAXC; c++)
-            if (c < nchunk) v += pc[c];
-        if (bias) v += (double)bias[e];
-        logits64[i] = v;
-        if (logits) logits[i] = (float)v;
-    }
-    __syncthreads();
-    // 2. per token: the picked experts and gates
-    for (int b = wv; b < B; b += 16) {
-        int me;
-        float mg;
-        token_topk<NSLOT>(logits64 + (long)b * E, E, ke, me, mg);
-        if (lane < ke) {
-            experts[(long)b * ke + lane] = me;
-            gates[(long)b * ke + lane] = mg;
-            s_exp[b * ke + lane] = me;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int ta = __shfl_up(ia, o, 64), tp = __shfl_up(ip, o, 64);
+            if (lane >= o) { ia += ta; ip += tp; }
+        }
+        const int na_tot = __shfl(ia, 63, 64);
+        int a = ia - na, q = ip - npl;
+        for (int i = 0; i < per; i++) {
+            const int e = lane * per + i;
+            if (e < E && s_cnt[e] > 0) {
+                p.active[a] = e;
+                p.tok_off[a] = q;
+                p.tok_cnt[a] = s_cnt[e];
+                s_off[e] = q;
+                a++;
+                q += s_cnt[e];
+            }
+        }
+        for (int sx = lane; sx < S; sx += 64) {
+            p.active[na_tot + sx] = E + sx;
+            p.tok_off[na_tot + sx] = np + sx * B;
+            p.tok_cnt[na_tot + sx] = B;
+        }
+        mx = wave_max_i(mx);
+        if (S > 0) mx = max(mx, B);
+        if (lane == 0) {
+            *p.n_active = na_tot + S;
+            *p.n_pairs = np + S * B;
+            *p.n_groups = (mx + 15) / 16;
         }
     }
     __syncthreads();
-    // 3. dispatch plan (same rules as k_plan)
-    for (int i = tid; i < B * ke; i += nT) atomicAdd(&s_cnt[s_exp[i]], 1);
-    __syncthreads();
-    const int per = (E + nT - 1) / nT;
-    int na = 0, np = 0;
-    for (int i = 0; i < per; i++) {
-        const int e = tid * per + i;
-        if (e < E && s_cnt[e] > 0) { na++; np += s_cnt[e]; }
+    for (int i = tid; i < np; i += nT) {
+        const int b = i / ke, j = i - b * ke, e = s_exp[i];
+        int rank = 0;
+        if (use_mask) rank = __popcll(s_mask[e] & ((1ull << b) - 1ull));
+        else
+            for (int i2 = 0; i2 < i; i2++) rank += s_exp[i2] == e;
+        const int q = s_off[e] + rank;
+        p.pair_tok[q] = b;
+        p.pair_idx[(long)b * kk + j] = q;
     }
-    int na_tot, np_tot;
-    const int a0 = block_excl_scan_1024(na, s_w, na_tot);
-    int p0 = block_excl_scan_1024(np, s_w, np_tot);
-    int a = a0;
-    for (int i = 0; i < per; i++) {
-        const int e = tid * per + i;
-        if (e >= E || s_cnt[e] == 0) continue;
-        active[a] = e;
-        tok_off[a] = p0;
-        tok_cnt[a] = s_cnt[e];
-        int p = p0;
-        for (int b = 0; b < B; b++)
-            for (int j = 0; j < ke; j++)
-                if (s_exp[b * ke + j] == e) {
-                    pair_tok[p] = b;
-                    pair_idx[(long)b * kk + j] = p;
-                    p++;
-                }
-        p0 = p;
-        a++;
-    }
-    const int routed_pairs = B * ke;
     for (int i = tid; i < S * B; i += nT) {
-        const int s2 = i / B, b = i % B;
-        const int p = routed_pairs + s2 * B + b;
-        pair_tok[p] = b;
-        pair_idx[(long)b * kk + ke + s2] = p;
+        const int sx = i / B, b = i - sx * B;
+        const int q = np + sx * B + b;
+        p.pair_tok[q] = b;
+        p.pair_idx[(long)b * kk + ke + sx] = q;
     }
-    if (tid < S) {
-        active[na_tot + tid] = E + tid;
-        tok_off[na_tot + tid] = routed_pairs + tid * B;
-        tok_cnt[na_tot + tid] = B;
-    }
-    int mx = S > 0 ? B : 0;
-    for (int e = tid; e < E; e += nT) mx = max(mx, s_cnt[e]);
-    mx = wave_max_i(mx);
+}
+
+// Dispatch plan of caller-given picks (experts [B, ke], each < E; ids out of range are clamped so that
+// no access leaves the arrays).
+__global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ experts, int B, int ke, int E, int S,
+                                               MoePlan p)
+{
+    __shared__ int s_exp[16384];
+    __shared__ int s_cnt[RP_MAXE], s_off[RP_MAXE];
+    __shared__ unsigned long long s_mask[RP_MAXE];
+    for (int i = threadIdx.x; i < B * ke; i += blockDim.x) s_exp[i] = min(max(experts[i], 0), E - 1);
     __syncthreads();
-    if (lane == 0) s_w[wv] = mx;
-    __syncthreads();
-    if (tid == 0) {
-        int m2 = 0;
-        for (int w = 0; w < 16; w++) m2 = max(m2, s_w[w]);
-        *n_active = na_tot + S;
-        *n_pairs = routed_pairs + S * B;
-        *n_groups = (m2 + 15) / 16;
+    build_plan(s_exp, B, ke, E, S, false, s_cnt, s_off, s_mask, p);
+}
+
+// Router top-k fused with the dispatch plan, one workgroup of 1024 threads.  Tokens are taken in blocks
+// of RP_LCAP / E: the block's logits (chunk partials summed in chunk order, plus the bias) go to LDS,
+// then wave w picks the experts of tokens w, w + 16, ... and their gates (softmax over the picked
+// logits, summed in pick order).  With p.active != nullptr the plan follows (B * ke <= 16384).
+template <int NSLOT>  // experts per lane: E <= 64 * NSLOT
+__global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ part, int nchunk, int B, int E, int ke,
+                                                     int S, const float *__restrict__ bias,
+                                                     int32_t *__restrict__ experts, float *__restrict__ gates,
+                                                     float *__restrict__ logits, MoePlan p)
+{
+    __shared__ double s_l[RP_LCAP];
+    __shared__ int s_exp[16384];
+    __shared__ int s_cnt[RP_MAXE], s_off[RP_MAXE];
+    __shared__ unsigned long long s_mask[RP_MAXE];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nT = 1024;
+    const bool plan = p.active != nullptr;
+    const int tb = RP_LCAP / E;
+    for (int b0 = 0; b0 < B; b0 += tb) {
+        const int nb = min(tb, B - b0);
+        for (int i = tid; i < nb * E; i += nT) {
+            const int b = b0 + i / E, e = i % E;
+            double pc[ROUTE_MAXC];  // every chunk's partial in flight at once, then summed in chunk order
+#pragma unroll
+            for (int c = 0; c < ROUTE_MAXC; c++) pc[c] = c < nchunk ? part[((long)c * B + b) * E + e] : 0.0;
+            double v = 0.0;
+#pragma unroll
+            for (int c = 0; c < ROUTE_MAXC; c++)
+                if (c < nchunk) v += pc[c];
+            if (bias) v += (double)bias[e];
+            s_l[i] = v;
+            if (logits) logits[(long)b * E + e] = (float)v;
+        }
+        __syncthreads();
+        for (int bl = wv; bl < nb; bl += 16) {
+            const double *lrow = s_l + (long)bl * E;
+            const int me = token_topk<NSLOT>(lrow, E, ke);
+            const double lm = lane < ke ? lrow[me] : 0.0;
+            const double l0 = __shfl(lm, 0, 64);
+            const double gx = exp(lm - l0);
+            double z = 0.0;
+            for (int j = 0; j < ke; j++) z += __shfl(gx, j, 64);
+            if (lane < ke) {
+                const int b = b0 + bl;
+                experts[(long)b * ke + lane] = me;
+                gates[(long)b * ke + lane] = (float)(gx / z);
+                if (plan) s_exp[b * ke + lane] = me;
+            }
+        }
+        __syncthreads();
     }
+    if (plan) build_plan(s_exp, B, ke, E, S, true, s_cnt, s_off, s_mask, p);
+}
+
+int route_chunks(int D) { return (D + ROUTE_KC - 1) / ROUTE_KC; }
+
+bool route_plan_ok(int E, int ke, int B) { return E <= RP_MAXE && ke <= 32 && (long)B * ke <= 16384; }
+
+int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s)
+{
+    dim3 g((E + 15) / 16, route_chunks(D));
+    hipLaunchKernelGGL(k_route_partial, g, dim3(256), 0, s, h, B, D, w_r, E, part);
+    return hip_check("route_partial");
+}
+
+int launch_route_plan(const double *part, int B, int D, const float *bias, int E, int ke, int S, int32_t *experts,
+                      float *gates, float *logits, const MoePlan *p, hipStream_t s)
+{
+    MoePlan none;
+    memset(&none, 0, sizeof none);
+    const MoePlan &pp = p ? *p : none;
+#define DL_RP(NS_)                                                                                                  \
+    hipLaunchKernelGGL((k_route_plan<NS_>), dim3(1), dim3(1024), 0, s, part, route_chunks(D), B, E, ke, S, bias,     \
+                       experts, gates, logits, pp)
+    if (E <= 256) DL_RP(4); else DL_RP(16);
+#undef DL_RP
+    return hip_check("route_plan");
+}
+
+int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
+                 float *gates, float *logits, double *part, hipStream_t s)
+{
+    int st = launch_route_partial(h, B, D, w_r, E, part, s);
+    if (st != DL_OK) return st;
+    return launch_route_plan(part, B, D, bias, E, ke, 0, experts, gates, logits, nullptr, s);
+}
+
+int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, experts, B, ke, E, S, p);
+    return hip_check("plan");
 }
 
 // out[b, d] = resid[b, d] + sum_j gate[b, j] f_j[d] + sum_s f_s[d], in that order.  A thread owns 4
@@ -410,52 +408,6 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, co
         o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
         *(uint2 *)((uint16_t *)out + row) = o;
     } else *(v4f *)((float *)out + row) = acc;
-}
-
-int route_chunks(int D) { return (D + ROUTE_KC - 1) / ROUTE_KC; }
-
-int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
-                 float *gates, float *logits, double *logits64, double *part, hipStream_t s)
-{
-    const int nc = route_chunks(D);
-    dim3 g((E + ROUTE_EXP - 1) / ROUTE_EXP, nc);
-    hipLaunchKernelGGL(k_route_partial, g, dim3(64), 0, s, h, B, D, w_r, E, part);
-    if (E <= 256)
-        hipLaunchKernelGGL((k_route_topk<4>), dim3((B + 3) / 4), dim3(256), 0, s, part, nc, B, E, ke, bias, experts,
-                           gates, logits, logits64);
-    else
-        hipLaunchKernelGGL((k_route_topk<16>), dim3((B + 3) / 4), dim3(256), 0, s, part, nc, B, E, ke, bias, experts,
-                           gates, logits, logits64);
-    return hip_check("route");
-}
-
-bool route_plan_ok(int E, int ke, int B) { return E <= RP_MAXE && ke <= 32 && (long)B * ke <= 16384; }
-
-int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s)
-{
-    dim3 g((E + ROUTE_EXP - 1) / ROUTE_EXP, route_chunks(D));
-    hipLaunchKernelGGL(k_route_partial, g, dim3(64), 0, s, h, B, D, w_r, E, part);
-    return hip_check("route_partial");
-}
-
-int launch_route_plan(const double *part, int B, int D, const float *bias, int E, int ke, int S, int32_t *experts,
-                      float *gates, float *logits, double *logits64, const MoePlan &p, hipStream_t s)
-{
-#define DL_RP(NS_)                                                                                                  \
-    hipLaunchKernelGGL((k_route_plan<NS_>), dim3(1), dim3(1024), 0, s, part, route_chunks(D), B, E, ke, S, bias,     \
-                       logits64, experts, gates, logits, p.n_active, p.n_pairs, p.n_groups, p.active, p.tok_off,     \
-                       p.tok_cnt, p.pair_tok, p.pair_idx)
-    if (E <= 256) DL_RP(4); else DL_RP(16);
-#undef DL_RP
-    return hip_check("route_plan");
-}
-
-int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s)
-{
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, experts, B, ke, E, S, p.n_active, p.n_pairs, p.n_groups,
-                       p.active,
-                       p.tok_off, p.tok_cnt, p.pair_tok, p.pair_idx);
-    return hip_check("plan");
 }
 
 int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,

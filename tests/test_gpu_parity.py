@@ -2,6 +2,8 @@
 
 Bit-exact: kept positions (and their scores), expert choices (up to oracle logits within 1e-6).
 Floating point: max |err| <= 2e-2 * max |oracle| for o, h - x, y - h and y, each against its own maximum."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,7 @@ import torch
 import oracle
 import sparse_attention_moe_amd as dl
 import synth
-from parity import FP_TOL, assert_close, check_rows, host, say
+from parity import FP_TOL, assert_close, check_rows, expert_mismatch, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -148,6 +150,43 @@ def test_attention_only_matches_oracle():
         ref = oracle.attention(orc.a("q")[b], orc.a("kv"), orc.a("kv_scale"), orc.a("page_table")[b], sel[b],
                                spec.scale, spec.Dv)
         assert_close(f"o row {b}", host(o)[b], ref)
+
+
+@pytest.mark.parametrize("B,E,ke,D,dup", [(40, 256, 8, 6144, False), (70, 300, 6, 1000, False),
+                                          (9, 1024, 32, 2048, True), (3, 64, 1, 512, True)])
+def test_route_standalone(B, E, ke, D, dup):
+    """dl_moe_route against the oracle: several token blocks, more than 256 experts, a ragged last hidden
+    chunk, and (dup) two pairs of identical router rows forced to the top, an exact tie the lower id wins."""
+    g = torch.Generator().manual_seed(11 + B)
+    h = torch.randn(B, D, generator=g)
+    w_r = torch.randn(E, D, generator=g) / math.sqrt(D)
+    bias = torch.randn(E, generator=g) * 0.1
+    if dup:
+        w_r[1], w_r[5] = w_r[0], w_r[4]
+        bias[0] = bias[1] = 10.0
+        bias[4] = bias[5] = 9.0
+    ex = torch.empty(B, ke, dtype=torch.int32, device=DEV)
+    gt = torch.empty(B, ke, dtype=torch.float32, device=DEV)
+    lg = torch.empty(B, E, dtype=torch.float32, device=DEV)
+    say(f"[gpu] moe_route B={B} E={E} ke={ke} D={D} dup={dup}")
+    dl.moe_route(h.to(DEV), w_r.to(DEV), bias.to(DEV), ke, ex, gt, logits=lg)
+    torch.cuda.synchronize()
+    ex, gt, lg = host(ex), host(gt), host(lg)
+    near = 0
+    for b in range(B):
+        ol, oe, og = oracle.router(h[b].double().numpy(), w_r.numpy(), bias.numpy(), ke)
+        m = expert_mismatch(ex[b], oe, ol)
+        assert m in (None, "near-tie"), f"row {b}: {m}"
+        near += m is not None
+        if m is None:
+            assert np.allclose(gt[b], og, rtol=0, atol=1e-6), f"row {b} gates"
+        assert np.allclose(lg[b], ol, rtol=0, atol=1e-6 * max(1.0, float(np.abs(ol).max()))), f"row {b} logits"
+        if dup:  # of two exactly tied experts the lower id is picked first, and right before the other
+            lst = [int(v) for v in ex[b]]
+            for lo, hi in ((0, 1), (4, 5)):
+                if hi in lst:
+                    assert lo in lst and lst.index(hi) == lst.index(lo) + 1, f"row {b}: {lst}"
+    say(f"near ties: {near}")
 
 
 # ------------------------------------------------------------------ the five named workloads
