@@ -47,6 +47,8 @@ struct Stage {
     float as[NS];
 };
 
+// Weight scales of the item's K range: lane j holds the scale of K-block kb0 + j (j < 64); the compute
+// loop reads them with readlane instead of one vector load per K-block.
 template <int RT>
 struct Ctx {
     int u, m, cnt, off, t0, r0, kc, kb0, kb1;
@@ -54,6 +56,7 @@ struct Ctx {
     int tt;
     const uint8_t *wp, *wp2, *ap;
     const float *wsp, *wsp2, *asp;
+    float wsv, wsv2;
 };
 
 // Two 16-byte halves of an operand: at p and p + gap.
@@ -84,8 +87,14 @@ __device__ __forceinline__ void load_stage(Stage<NS, SW, RT> &st, const Ctx<RT> 
     }
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-        st.Bv[s] = ld16x2(c.ap + s * aq_part + kb * 128, 64);
-        st.as[s] = c.asp[s * asc_part + kb];
+        // lanes of empty token slots load nothing (their result is scaled by 0)
+        if (c.tv) {
+            st.Bv[s] = ld16x2(c.ap + s * aq_part + kb * 128, 64);
+            st.as[s] = c.asp[s * asc_part + kb];
+        } else {
+            st.Bv[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            st.as[s] = 0.f;
+        }
     }
 }
 
@@ -132,7 +141,12 @@ __device__ __forceinline__ void make_ctx(const GemvArgs &a, int item, int groups
     const long sbase = ((long)c.m * a.nrb + (c.r0 >> 7)) * a.nkb;
     c.wsp = a.wsc + sbase;
     c.wsp2 = SW ? a.wsc2 + sbase : nullptr;
+    const bool in = c.valid && lane < c.kb1 - c.kb0;
+    c.wsv = in ? c.wsp[c.kb0 + lane] : 0.f;
+    c.wsv2 = (SW && in) ? c.wsp2[c.kb0 + lane] : 0.f;
 }
+
+__device__ __forceinline__ float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
 template <int NS, int EPI, int RT, bool TL>
 __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
@@ -162,8 +176,9 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
             for (int kb = c.kb0; kb < c.kb1; kb++) {
                 if (kb + 1 < c.kb1) load_stage<NS, SW, RT, TL>(nxt, c, a.cols, a.aq_part, a.asc_part, kb + 1);
                 else if (more && n.valid) load_stage<NS, SW, RT, TL>(nxt, n, a.cols, a.aq_part, a.asc_part, n.kb0);
-                const float ws = c.wsp[kb] * tmask;
-                const float ws2 = SW ? c.wsp2[kb] * tmask : 0.f;
+                const int kr = kb - c.kb0;
+                const float ws = (kr < 64 ? lane_f(c.wsv, kr) : c.wsp[kb]) * tmask;
+                const float ws2 = SW ? (kr < 64 ? lane_f(c.wsv2, kr) : c.wsp2[kb]) * tmask : 0.f;
 #pragma unroll
                 for (int s = 0; s < NS; s++) {
                     const float f = ws * cur.as[s], f2 = ws2 * cur.as[s];
