@@ -8,6 +8,8 @@
 #include "dl_common.h"
 #include "dl_internal.h"
 
+#include <algorithm>
+
 namespace dl {
 
 static thread_local char g_err[512] = "";
@@ -145,11 +147,10 @@ static int check_indexer(int HI, int DI, int top_k)
 }
 
 // ------------------------------------------------------------------ attention + projection
-static constexpr int MAX_KSPLIT = 16;
 
 struct AttnWs {
     float *opart, *ml;         // split partials of the matrix-core attention
-    float *kpart;              // [MAX_KSPLIT, B, D] K-chunk partials of W_O
+    float *kpart;              // [2 MAX_KSPLIT, B, D] partial slots of W_O
     float *o;                  // [B, H, Dv] (when the caller's out is not o)
     uint8_t *oq; float *oqs;   // 4 parts of o for W_UV
     float *u;                  // [B, H*hd]
@@ -183,17 +184,8 @@ static void attn_ws_layout(Ws &w, int B, int H, int Dv, int top_k, const dl_mat 
     if (w_o->dtype == DL_FP8_E4M3) {
         a.uq = w.take<uint8_t>(PROJ_PARTS * BH * hd);
         a.uqs = w.take<float>(PROJ_PARTS * BH * (hd / 128));
-        a.kpart = w.take<float>((long)MAX_KSPLIT * B * w_o->rows);
+        a.kpart = w.take<float>(2L * MAX_KSPLIT * B * w_o->rows);
     }
-}
-
-// K split of a one-matrix projection so that enough waves stream it: about 2,048 work items, chunks of
-// at least 4 blocks, a power of two that divides the block count.
-static int pick_ksplit(long items, int nkb)
-{
-    int ks = 1;
-    while (ks < MAX_KSPLIT && items * ks < 2048 && nkb % (2 * ks) == 0 && nkb / (2 * ks) >= 4) ks *= 2;
-    return ks;
 }
 
 static GemvArgs mat_args(const dl_mat *m)
@@ -265,8 +257,8 @@ static int run_projection(int B, int H, int Dv, const float *o, const dl_mat *w_
     if (f8) {
         DL_TRY(launch_quant(act, B, nullptr, K, a.uq, a.uqs, (long)B * K, (long)B * (K / 128), PROJ_PARTS, s));
         g.aq = a.uq; g.asc = a.uqs; g.aq_part = (long)B * K; g.asc_part = (long)B * (K / 128);
-        g.ksplit = pick_ksplit((long)(w_o->rows / 32) * g.max_groups, g.nkb);
-        g.kchunk = g.nkb / g.ksplit;
+        if (!gemv_oneshot(g, true))
+            gemv_flat(g, PROJ_PARTS, resid ? EPI_RESID : EPI_STORE, (long)(w_o->rows / 32) * g.max_groups, MAX_KSPLIT);
         g.part = a.kpart;
         g.n_out = (long)B * w_o->rows;
     } else {
@@ -313,28 +305,26 @@ static int run_attn_proj(const dl_pages &pg, const void *q, int q_dt, const void
     g.resid_dt = resid_dt;
     g.r_ts = w_o->rows;
     g.aq = a.uq; g.asc = a.uqs; g.aq_part = (long)B * K; g.asc_part = (long)B * (K / 128);
-    g.ksplit = pick_ksplit((long)(w_o->rows / 32) * g.max_groups, g.nkb);
-    g.kchunk = g.nkb / g.ksplit;
+    if (!gemv_oneshot(g, true)) gemv_flat(g, PROJ_PARTS, EPI_RESID, (long)(w_o->rows / 32) * g.max_groups, MAX_KSPLIT);
     g.part = a.kpart;
     g.n_out = (long)B * w_o->rows;
-    g.reduce_in_consumer = g.ksplit > 1;
+    g.reduce_in_consumer = true;
     DL_TRY(launch_gemv(g, PROJ_PARTS, EPI_RESID, true, s));
-    if (g.ksplit == 1) return DL_OK;
     DL_TRY(launch_resid_reduce_split(g, out, hq, hqs, (long)B * w_o->rows, (long)B * (w_o->rows / 128), s));
     if (h_split) *h_split = hq != nullptr;
     return DL_OK;
 }
 
 // ------------------------------------------------------------------ FFN
-static constexpr int GU_KSPLIT = 2;  // K chunks of the FP8 gate/up pass (balances the waves' work)
+static constexpr int GU_MAXK = 4;  // most K chunks of the FP8 gate/up pass (partial slots: twice that)
 
 struct FfnWs {
     MoePlan plan;
     uint8_t *hq; float *hqs;   // 2 parts of h  [2][B][D]
-    float *gpart, *upart;      // [GU_KSPLIT, P, I] gate/up partial sums (FP8 path)
+    float *gpart, *upart;      // [2 GU_MAXK, P, I] gate/up partial slots (FP8 path)
     float *Z;                  // [P, I]
     uint8_t *zq; float *zqs;   // 2 parts of Z
-    float *F;                  // [P, D]
+    float *F;                  // [P, D] expert outputs
 };
 
 static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool fp8, FfnWs &f)
@@ -357,8 +347,8 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
     f.Z = w.take<float>(P * I);
     f.gpart = f.upart = nullptr;
     if (fp8) {
-        f.gpart = w.take<float>((long)GU_KSPLIT * P * I);
-        f.upart = w.take<float>((long)GU_KSPLIT * P * I);
+        f.gpart = w.take<float>(2L * GU_MAXK * P * I);
+        f.upart = w.take<float>(2L * GU_MAXK * P * I);
         f.zq = w.take<uint8_t>((long)FFN_PARTS * P * I);
         f.zqs = w.take<float>((long)FFN_PARTS * P * (I / 128));
     }
@@ -379,9 +369,11 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     g.w2 = (const uint8_t *)(f8 ? wu->w : nullptr);
     g.wsc2 = f8 ? wu->scale : nullptr;
     g.wf2 = f8 ? nullptr : (const float *)wu->w;
+    // active experts: at most every routed pick plus the shared experts
+    const int na_est = (int)std::min<long>(NE, (long)B * ke + S);
     g.active = f.plan.active;
     g.n_active_dev = f.plan.n_active;
-    g.n_active_host = NE;
+    g.n_active_host = na_est;
     g.tok_off = f.plan.tok_off;
     g.tok_cnt = f.plan.tok_cnt;
     g.max_groups = (B + 15) / 16;
@@ -393,14 +385,11 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
         if (!h_split_ready)
             DL_TRY(launch_quant(h, B, nullptr, D, f.hq, f.hqs, (long)B * D, (long)B * (D / 128), FFN_PARTS, s));
         g.aq = f.hq; g.asc = f.hqs; g.aq_part = (long)B * D; g.asc_part = (long)B * (D / 128);
-        if (g.nkb % GU_KSPLIT == 0) {
-            g.ksplit = GU_KSPLIT;
-            g.kchunk = g.nkb / GU_KSPLIT;
-            g.part = f.gpart;
-            g.part2 = f.upart;
-            g.n_out = P * I;
-            g.reduce_in_consumer = true;
-        }
+        gemv_flat(g, FFN_PARTS, EPI_SWIGLU, (long)na_est * (I / 32) * g.max_groups, GU_MAXK);
+        g.part = f.gpart;
+        g.part2 = f.upart;
+        g.n_out = P * I;
+        g.reduce_in_consumer = true;
     } else {
         g.af = h;
     }
@@ -411,7 +400,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     GemvArgs d = mat_args(wd);
     d.active = f.plan.active;
     d.n_active_dev = f.plan.n_active;
-    d.n_active_host = NE;
+    d.n_active_host = na_est;
     d.tok_off = f.plan.tok_off;
     d.tok_cnt = f.plan.tok_cnt;
     d.max_groups = (B + 15) / 16;
@@ -420,11 +409,8 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     d.o_ts = D;
     d.out = f.F;
     if (f8) {
-        if (g.ksplit > 1)
-            DL_TRY(launch_swiglu_quant(f.gpart, f.upart, g.ksplit, P * I, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I,
-                                       P * (I / 128), FFN_PARTS, s));
-        else
-            DL_TRY(launch_quant(f.Z, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I, P * (I / 128), FFN_PARTS, s));
+        DL_TRY(launch_swiglu_quant(f.gpart, f.upart, gemv_slots(g), P * I, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I,
+                                   P * (I / 128), FFN_PARTS, s));
         d.aq = f.zq; d.asc = f.zqs; d.aq_part = P * I; d.asc_part = P * (I / 128);
     } else {
         d.af = f.Z;
@@ -432,7 +418,8 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     mk.at(7);
     DL_TRY(launch_gemv(d, FFN_PARTS, EPI_STORE, f8, s));
     mk.at(8);
-    DL_TRY(launch_combine(f.F, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt, out32, s));
+    DL_TRY(launch_combine(f.F, 1, P * D, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
+                          out32, s));
     mk.at(9);
     return DL_OK;
 }
@@ -468,7 +455,7 @@ static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, c
     if (d->w_o.dtype == DL_FP8_E4M3) {
         L.attn.uq = w.take<uint8_t>(PROJ_PARTS * BH * hd);
         L.attn.uqs = w.take<float>(PROJ_PARTS * BH * (hd / 128));
-        L.attn.kpart = w.take<float>((long)MAX_KSPLIT * B * d->w_o.rows);
+        L.attn.kpart = w.take<float>(2L * MAX_KSPLIT * B * d->w_o.rows);
     }
     L.h = (io && io->h) ? io->h : w.take<float>((long)B * d->D);
     L.rpart = w.take<double>((long)route_chunks(d->D) * B * d->n_routed);

@@ -82,15 +82,26 @@ struct GemvArgs {
     // split of K into ksplit chunks of kchunk blocks: raw partial sums go to part[chunk][out offset]
     // (and part2 for the second SwiGLU matrix), then a reduction applies the epilogue
     int ksplit, kchunk;
+    int flat;          // balanced step ranges; a chunk may be split in two partial slots (see k_gemv.hip)
+    int oneshot;       // one-shot projection kernel: partial slot per group of 8 K-blocks
     float *part, *part2;
     long n_out;        // elements of the output array (partial buffer stride)
     bool reduce_in_consumer;  // the next kernel sums the partials itself (no reduction launch)
 };
+// Partial slots the GEMV writes: 2 per K chunk in flat mode, else 1 per chunk (0 without a split).
+__host__ __device__ inline int gemv_slots(const GemvArgs &a) { return a.flat ? 2 * a.ksplit : a.ksplit; }
+static constexpr int MAX_KSPLIT = 16;
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
+// Flat mode for an FP8 GEMV of about `units_est` units: the K split (<= max_ksplit chunks) with chunks no
+// longer than a wave's share of steps.
+void gemv_flat(GemvArgs &a, int ns, int epi, long units_est, int max_ksplit);
+// One-shot mode for a single FP8 matrix in uniform mode (rows % 128 == 0, K % 1024 == 0); false if
+// the shape does not fit (then nothing is changed).
+bool gemv_oneshot(GemvArgs &a, bool fp8);
 int launch_pack(const uint8_t *src, uint8_t *dst, long count, int rows, int cols, hipStream_t s);
 
-// SwiGLU of summed gate/up K-chunk partials, split into NS FP8 parts (rows may come from the device).
-int launch_swiglu_quant(const float *pg, const float *pu, int ksplit, long stride, long rows_host,
+// SwiGLU of summed gate/up partial slots, split into NS FP8 parts (rows may come from the device).
+int launch_swiglu_quant(const float *pg, const float *pu, int nslot, long stride, long rows_host,
                         const int *rows_dev, int cols, uint8_t *q, float *sc, long q_part, long sc_part, int ns,
                         hipStream_t s);
 // x fp32 rows -> NS FP8 parts with one dynamic scale per (part, row, 128 block).
@@ -135,7 +146,9 @@ bool route_plan_ok(int E, int ke, int B);
 int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s);
 int launch_route_plan(const double *part, int B, int D, const float *bias, int E, int ke, int S, int32_t *experts,
                       float *gates, float *logits, const MoePlan *p, hipStream_t s);
-int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
+// F: nslot partial slots of the expert outputs, fstride floats apart, summed in slot order.
+int launch_combine(const float *F, int nslot, long fstride, const MoePlan &p, const float *gates, int B, int D, int ke,
+                   int S,
                    const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s);
 
 }  // namespace dl

@@ -36,10 +36,13 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// Work item: (active matrix u, RT*16-row tile, group of 16 tokens, K chunk), numbered with the K chunk
-// fastest, then the token group, then the tile, then u.  Each wave owns one contiguous, equal share of the
-// items, so consecutive items almost always belong to the same matrix and token set (no new metadata),
-// and the load pipeline runs on across item boundaries.
+// Work: units (active matrix u, RT*16-row tile, group of 16 tokens), numbered with the token group fastest,
+// then the tile, then u; a unit's K range is nkb steps of one 128-wide block, cut into chunks of kchunk
+// blocks.  The steps of all units form one sequence.  Without `flat` each wave owns a contiguous share of whole
+// (unit, chunk) items; with `flat` each wave owns an equal share of steps (at least kchunk), so a chunk may be
+// split between two neighbouring waves: the first writes partial slot 2 kc, the second 2 kc + 1, and a chunk
+// done by one wave zero-fills 2 kc + 1.  Either way consecutive segments of a wave mostly share the matrix
+// and token group (no new metadata) and the load pipeline runs on across segment boundaries.
 template <int NS, bool SW, int RT>
 struct Stage {
     v8i A[RT], A2[RT];
@@ -51,7 +54,7 @@ struct Stage {
 // loop reads them with readlane instead of one vector load per K-block.
 template <int RT>
 struct Ctx {
-    int u, m, cnt, off, t0, r0, kc, kb0, kb1;
+    int u, m, cnt, off, t0, r0, kc, kb0, kb1, piece, whole;
     bool valid, tv;
     int tt;
     const uint8_t *wp, *wp2, *ap;
@@ -98,18 +101,19 @@ __device__ __forceinline__ void load_stage(Stage<NS, SW, RT> &st, const Ctx<RT> 
     }
 }
 
-// Item -> context.  Reuses `prev` (same matrix and token group) when possible: then no memory is read.
+// Segment (steps [s, e) of one unit's chunk) -> context.  Reuses `prev` (same matrix and token group) when
+// possible: then no memory is read.
 template <int RT, bool SW, bool TL>
-__device__ __forceinline__ void make_ctx(const GemvArgs &a, int item, int groups, int tiles, const Ctx<RT> *prev,
-                                         Ctx<RT> &c)
+__device__ __forceinline__ void make_ctx(const GemvArgs &a, long s, long e, int groups, int tiles,
+                                         const Ctx<RT> *prev, Ctx<RT> &c)
 {
     const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
-    const int kc = item % a.ksplit;
-    int r = item / a.ksplit;
-    const int g = r % groups;
-    r /= groups;
-    const int tile = r % tiles;
-    const int u = r / tiles;
+    const int unit = (int)(s / a.nkb);
+    const int kb = (int)(s - (long)unit * a.nkb);
+    const int kc = kb / a.kchunk;
+    const int g = unit % groups;
+    const int tile = (unit / groups) % tiles;
+    const int u = unit / groups / tiles;
     if (prev && prev->u == u && prev->t0 == g * 16) {
         c = *prev;
     } else {
@@ -130,10 +134,13 @@ __device__ __forceinline__ void make_ctx(const GemvArgs &a, int item, int groups
         c.ap = a.aq + arow * a.cols + lg * 16;
         c.asp = a.asc + arow * a.nkb;
     }
+    const int kb_end = min(a.nkb, (kc + 1) * a.kchunk);
     c.kc = kc;
+    c.kb0 = kb;
+    c.kb1 = kb + (int)(e - s);
+    c.piece = kb != kc * a.kchunk;
+    c.whole = !c.piece && c.kb1 == kb_end;
     c.r0 = tile * 16 * RT;
-    c.kb0 = kc * a.kchunk;
-    c.kb1 = min(a.nkb, c.kb0 + a.kchunk);
     const long wrow = TL ? (long)c.m * a.mat_elems + (long)(c.r0 / 16) * a.nkb * 2048 + lane * 16
                          : (long)c.m * a.mat_elems + (long)(c.r0 + ln) * a.cols + lg * 16;
     c.wp = a.w + wrow;
@@ -149,7 +156,7 @@ __device__ __forceinline__ void make_ctx(const GemvArgs &a, int item, int groups
 __device__ __forceinline__ float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
 template <int NS, int EPI, int RT, bool TL>
-__global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
+__global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k_gemv_fp8(GemvArgs a)
 {
     constexpr bool SW = EPI == EPI_SWIGLU;
     const int lane = threadIdx.x & 63, lg = lane >> 4;
@@ -158,16 +165,41 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
     const int n_act = a.n_active_dev ? *a.n_active_dev : a.n_active_host;
     const int groups = a.groups_dev ? *a.groups_dev : a.max_groups;
     const int tiles = a.rows / (16 * RT);
-    const int total = n_act * tiles * groups * a.ksplit;
-    const int i0 = (int)((long)wave * total / nwaves), i1 = (int)((long)(wave + 1) * total / nwaves);
-    if (i0 >= i1) return;
+    const long units = (long)n_act * tiles * groups;
+    const long S = units * a.nkb;  // steps of all units
+    long s0, s1;
+    if (a.flat) {
+        // at least kchunk steps per wave, so a chunk is split at most once
+        long W = nwaves;
+        if (S / a.kchunk < W) W = S / a.kchunk > 0 ? S / a.kchunk : 1;
+        if (wave >= W) return;
+        s0 = wave * S / W;
+        s1 = (wave + 1) * S / W;
+    } else {
+        // whole (unit, chunk) items
+        const long items = units * a.ksplit;
+        const long i0 = wave * items / nwaves, i1 = (wave + 1) * items / nwaves;
+        s0 = (i0 / a.ksplit) * a.nkb + min((long)a.nkb, (i0 % a.ksplit) * a.kchunk);
+        s1 = (i1 / a.ksplit) * a.nkb + min((long)a.nkb, (i1 % a.ksplit) * a.kchunk);
+    }
+    if (s0 >= s1) return;
+    // end of the segment starting at step x: the end of its chunk, or s1
+    auto seg_end = [&](long x) {
+        const long unit = x / a.nkb;
+        const int kb = (int)(x - unit * a.nkb);
+        const long ce = unit * a.nkb + min(a.nkb, (kb / a.kchunk + 1) * a.kchunk);
+        return ce < s1 ? ce : s1;
+    };
+    const bool parts = a.flat || a.ksplit > 1;
     Ctx<RT> c, n;
-    make_ctx<RT, SW, TL>(a, i0, groups, tiles, nullptr, c);
+    long e = seg_end(s0);
+    make_ctx<RT, SW, TL>(a, s0, e, groups, tiles, nullptr, c);
     Stage<NS, SW, RT> cur, nxt;
     if (c.valid) load_stage<NS, SW, RT, TL>(cur, c, a.cols, a.aq_part, a.asc_part, c.kb0);
-    for (int it = i0; it < i1; it++) {
-        const bool more = it + 1 < i1;
-        if (more) make_ctx<RT, SW, TL>(a, it + 1, groups, tiles, &c, n);
+    for (long s = s0; s < s1;) {
+        const bool more = e < s1;
+        const long e2 = more ? seg_end(e) : e;
+        if (more) make_ctx<RT, SW, TL>(a, e, e2, groups, tiles, &c, n);
         if (c.valid) {
             v4f tot[RT], tot2[RT];
 #pragma unroll
@@ -192,12 +224,18 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
             }
             if (c.tv) {
                 const long ooff = a.tok_cnt ? (long)(c.off + c.tt) * a.o_ts : (long)c.tt * a.o_ts + (long)c.m * a.o_ms;
+                const long slot = a.flat ? 2 * c.kc + c.piece : c.kc;
 #pragma unroll
                 for (int r = 0; r < RT; r++) {
                     const int rr = c.r0 + r * 16 + 4 * lg;
-                    if (a.ksplit > 1) {
-                        *(v4f *)(a.part + (long)c.kc * a.n_out + ooff + rr) = tot[r];
-                        if (SW) *(v4f *)(a.part2 + (long)c.kc * a.n_out + ooff + rr) = tot2[r];
+                    if (parts) {
+                        *(v4f *)(a.part + slot * a.n_out + ooff + rr) = tot[r];
+                        if (SW) *(v4f *)(a.part2 + slot * a.n_out + ooff + rr) = tot2[r];
+                        if (a.flat && c.whole) {
+                            const v4f z = {0.f, 0.f, 0.f, 0.f};
+                            *(v4f *)(a.part + (slot + 1) * a.n_out + ooff + rr) = z;
+                            if (SW) *(v4f *)(a.part2 + (slot + 1) * a.n_out + ooff + rr) = z;
+                        }
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
@@ -212,8 +250,89 @@ __global__ __launch_bounds__(256) void k_gemv_fp8(GemvArgs a)
         } else if (more && n.valid) {
             load_stage<NS, SW, RT, TL>(cur, n, a.cols, a.aq_part, a.asc_part, n.kb0);
         }
+        s = e;
+        e = e2;
         if (more) c = n;
     }
+}
+
+// One-shot projection GEMV (one FP8 matrix, either layout, tokens 0..ntok-1): a workgroup owns 128 rows
+// (8 tiles) and a group of 8 K-blocks, wave w the blocks 2w and 2w + 1 of it.  Every wave issues all of its
+// weight loads (32 KB) before any arithmetic, so the whole matrix is in flight at once instead of a few
+// blocks per wave, then adds its token groups' activations; the four waves' sums go through LDS and are added
+// in wave order into partial slot (K group) of [slot][token][row].
+template <int NS, bool TL>
+__global__ __launch_bounds__(256) void k_proj_shot(GemvArgs a)
+{
+    constexpr int RT = 8, KB = 2;
+    __shared__ v4f s_acc[4][RT][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ln = lane & 15, lg = lane >> 4;
+    const int rb = blockIdx.x, kq = blockIdx.y;
+    const int kb0 = kq * 8 + w * KB;
+    v8i A[KB][RT];
+#pragma unroll
+    for (int k = 0; k < KB; k++)
+#pragma unroll
+        for (int r = 0; r < RT; r++)
+            A[k][r] = TL ? ld16x2(a.w + ((long)(rb * RT + r) * a.nkb + kb0 + k) * 2048 + lane * 16, 1024)
+                         : ld16x2(a.w + (long)((rb * RT + r) * 16 + ln) * a.cols + (kb0 + k) * 128 + lg * 16, 64);
+    float ws[KB];
+#pragma unroll
+    for (int k = 0; k < KB; k++) ws[k] = a.wsc[(long)rb * a.nkb + kb0 + k];
+    for (int t0 = 0; t0 < a.ntok_host; t0 += 16) {
+        const int t = t0 + ln;
+        const bool tv = t < a.ntok_host;
+        v8i Bv[KB][NS];
+        float as[KB][NS];
+#pragma unroll
+        for (int k = 0; k < KB; k++)
+#pragma unroll
+            for (int s = 0; s < NS; s++) {
+                if (tv) {
+                    Bv[k][s] = ld16x2(a.aq + s * a.aq_part + (long)t * a.cols + (kb0 + k) * 128 + lg * 16, 64);
+                    as[k][s] = a.asc[s * a.asc_part + (long)t * a.nkb + kb0 + k];
+                } else {
+                    Bv[k][s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                    as[k][s] = 0.f;
+                }
+            }
+        v4f tot[RT];
+#pragma unroll
+        for (int r = 0; r < RT; r++) tot[r] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KB; k++)
+#pragma unroll
+            for (int s = 0; s < NS; s++) {
+                const float f = ws[k] * as[k][s];
+#pragma unroll
+                for (int r = 0; r < RT; r++) tot[r] += mfma_fp8(A[k][r], Bv[k][s]) * f;
+            }
+#pragma unroll
+        for (int r = 0; r < RT; r++) s_acc[w][r][lane] = tot[r];
+        __syncthreads();
+        // wave w adds the four waves' sums of tiles 2w, 2w + 1
+        if (tv) {
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                const int r = 2 * w + q;
+                const v4f v = ((s_acc[0][r][lane] + s_acc[1][r][lane]) + s_acc[2][r][lane]) + s_acc[3][r][lane];
+                *(v4f *)(a.part + (long)kq * a.n_out + (long)t * a.o_ts + (rb * RT + r) * 16 + 4 * lg) = v;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+bool gemv_oneshot(GemvArgs &a, bool fp8)
+{
+    if (!fp8 || a.n_active_host != 1 || a.tok_cnt || a.a_ts != 1 || a.rows % 128 || a.nkb % 8 ||
+        a.nkb / 8 > MAX_KSPLIT)
+        return false;
+    a.oneshot = 1;
+    a.flat = 0;
+    a.ksplit = a.nkb / 8;
+    a.kchunk = 8;
+    return true;
 }
 
 // Sum of the K-chunk partials in chunk order, then the epilogue.  EPI_RESID here needs the residual laid
@@ -224,16 +343,12 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(GemvArgs a)
     constexpr bool SW = EPI == EPI_SWIGLU;
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
     if (e >= a.n_out) return;
-    float p1[16], p2[16];
-#pragma unroll
-    for (int kc = 0; kc < 16; kc++) {
-        p1[kc] = kc < a.ksplit ? a.part[(long)kc * a.n_out + e] : 0.f;
-        p2[kc] = (SW && kc < a.ksplit) ? a.part2[(long)kc * a.n_out + e] : 0.f;
-    }
+    const int nslot = gemv_slots(a);
     float v = 0.f, v2 = 0.f;
-#pragma unroll
-    for (int kc = 0; kc < 16; kc++)
-        if (kc < a.ksplit) { v += p1[kc]; if (SW) v2 += p2[kc]; }
+    for (int k = 0; k < nslot; k++) {
+        v += a.part[(long)k * a.n_out + e];
+        if (SW) v2 += a.part2[(long)k * a.n_out + e];
+    }
     if (EPI == EPI_RESID) v += act_load(a.resid, a.resid_dt, e);
     if (SW) v = silu(v) * v2;
     a.out[e] = v;
@@ -331,11 +446,11 @@ __global__ __launch_bounds__(256) void k_quant(const float *__restrict__ x, long
     }
 }
 
-// Z = silu(sum_c G_c) * (sum_c U_c) from the K-chunk partials of the gate/up pass, split into NS FP8 parts
-// like k_quant.  rows come from the device (pairs of the plan).
+// Z = silu(sum_c G_c) * (sum_c U_c) from the nslot (<= 8) partial slots of the gate/up pass, summed in slot
+// order, split into NS FP8 parts like k_quant.  rows come from the device (pairs of the plan).
 template <int NS>
 __global__ __launch_bounds__(256) void k_swiglu_quant(const float *__restrict__ pg, const float *__restrict__ pu,
-                                                      int ksplit, long stride, long rows_host, const int *rows_dev,
+                                                      int nslot, long stride, long rows_host, const int *rows_dev,
                                                       int cols, uint8_t *__restrict__ q, float *__restrict__ sc,
                                                       long q_part, long sc_part)
 {
@@ -348,16 +463,16 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const float *__restrict__ 
         const long row = it / nkb;
         const int kb = (int)(it % nkb);
         const long e = row * cols + kb * 128 + lane * 2;
-        v2f gc[4], uc[4];
+        v2f gc[8], uc[8];
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            gc[c] = c < ksplit ? *(const v2f *)(pg + c * stride + e) : v2f{0.f, 0.f};
-            uc[c] = c < ksplit ? *(const v2f *)(pu + c * stride + e) : v2f{0.f, 0.f};
+        for (int c = 0; c < 8; c++) {
+            gc[c] = c < nslot ? *(const v2f *)(pg + c * stride + e) : v2f{0.f, 0.f};
+            uc[c] = c < nslot ? *(const v2f *)(pu + c * stride + e) : v2f{0.f, 0.f};
         }
         v2f g = {0.f, 0.f}, u = {0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; c++)
-            if (c < ksplit) { g += gc[c]; u += uc[c]; }
+        for (int c = 0; c < 8; c++)
+            if (c < nslot) { g += gc[c]; u += uc[c]; }
         float r0 = silu(g.x) * u.x, r1 = silu(g.y) * u.y;
 #pragma unroll
         for (int s = 0; s < NS; s++) {
@@ -384,6 +499,31 @@ static int grid_for(long items, int per_block_waves = 4, int max_blocks = 8192)
     return (int)b;
 }
 
+static const void *gemv_kernel(int ns, int epi, bool tiled)
+{
+#define DL_K(NS_, E_, TL_) \
+    if (ns == NS_ && epi == E_ && tiled == TL_) return (const void *)k_gemv_fp8<NS_, E_, 2, TL_>;
+    DL_K(2, EPI_STORE, false) DL_K(2, EPI_RESID, false) DL_K(2, EPI_SWIGLU, false)
+    DL_K(4, EPI_STORE, false) DL_K(4, EPI_RESID, false) DL_K(4, EPI_SWIGLU, false)
+    DL_K(2, EPI_STORE, true) DL_K(2, EPI_RESID, true) DL_K(2, EPI_SWIGLU, true)
+    DL_K(4, EPI_STORE, true) DL_K(4, EPI_RESID, true) DL_K(4, EPI_SWIGLU, true)
+#undef DL_K
+    return nullptr;
+}
+
+void gemv_flat(GemvArgs &a, int ns, int epi, long units_est, int max_ksplit)
+{
+    const void *k = gemv_kernel(ns, epi, a.tiled != 0);
+    const long waves = k ? 4L * resident_blocks(k, 256) : 1024;
+    const long spw = units_est * a.nkb / waves;  // steps per wave
+    int ks = 1;
+    while (ks < max_ksplit && !(a.nkb % ks == 0 && a.nkb / ks <= spw)) ks++;
+    while (a.nkb % ks) ks--;
+    a.flat = 1;
+    a.ksplit = ks;
+    a.kchunk = a.nkb / ks;
+}
+
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
 {
     // upper bound of the item count (device-side counts can only be smaller)
@@ -391,20 +531,25 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
     if (fp8) {
         // persistent grid: exactly the workgroups that fit on the device at once, so every wave's equal
         // share of the items runs concurrently
-        bool done = false;
-#define DL_G(NS_, E_, TL_)                                                                    \
-    if (!done && ns == NS_ && epi == E_ && (a.tiled != 0) == TL_) {                           \
-        const dim3 g(resident_blocks((const void *)k_gemv_fp8<NS_, E_, 2, TL_>, 256));        \
-        hipLaunchKernelGGL((k_gemv_fp8<NS_, E_, 2, TL_>), g, dim3(256), 0, s, a);            \
-        done = true;                                                                          \
-    }
-        DL_G(2, EPI_STORE, false) DL_G(2, EPI_RESID, false) DL_G(2, EPI_SWIGLU, false)
-        DL_G(4, EPI_STORE, false) DL_G(4, EPI_RESID, false) DL_G(4, EPI_SWIGLU, false)
-        DL_G(2, EPI_STORE, true) DL_G(2, EPI_RESID, true) DL_G(2, EPI_SWIGLU, true)
-        DL_G(4, EPI_STORE, true) DL_G(4, EPI_RESID, true) DL_G(4, EPI_SWIGLU, true)
-#undef DL_G
-        if (!done) return fail(DL_ERR_UNSUPPORTED, "gemv parts=%d", ns);
-        if (a.ksplit > 1 && !a.reduce_in_consumer) {
+        if (a.oneshot) {
+            if (ns != 4 || !a.part) return fail(DL_ERR_UNSUPPORTED, "one-shot gemv parts=%d", ns);
+            if (a.tiled) hipLaunchKernelGGL((k_proj_shot<4, true>), dim3(a.rows / 128, a.nkb / 8), dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_proj_shot<4, false>), dim3(a.rows / 128, a.nkb / 8), dim3(256), 0, s, a);
+            if (!a.reduce_in_consumer) {
+                const dim3 gr((unsigned)((a.n_out + 255) / 256));
+                if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv_reduce<EPI_RESID>), gr, dim3(256), 0, s, a);
+                else hipLaunchKernelGGL((k_gemv_reduce<EPI_STORE>), gr, dim3(256), 0, s, a);
+            }
+            return hip_check("proj_shot");
+        }
+        const void *k = gemv_kernel(ns, epi, a.tiled != 0);
+        if (!k) return fail(DL_ERR_UNSUPPORTED, "gemv parts=%d", ns);
+        if ((a.flat || a.ksplit > 1) && !a.part) return fail(DL_ERR_UNSUPPORTED, "gemv split without partials");
+        GemvArgs arg = a;
+        void *args[] = {(void *)&arg};
+        if (hipLaunchKernel(k, dim3(resident_blocks(k, 256)), dim3(256), args, 0, s) != hipSuccess)
+            return hip_check("gemv_fp8");
+        if ((a.ksplit > 1 || a.flat) && !a.reduce_in_consumer) {
             const dim3 gr((unsigned)((a.n_out + 255) / 256));
             if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemv_reduce<EPI_STORE>), gr, dim3(256), 0, s, a);
             else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv_reduce<EPI_RESID>), gr, dim3(256), 0, s, a);
@@ -461,13 +606,15 @@ __global__ __launch_bounds__(256) void k_resid_reduce_split(GemvArgs a, float *_
     const long row = wave / nkb;
     const int kb = (int)(wave % nkb);
     const long e = row * D + kb * 128 + lane * 2;
-    v2f pc[16];
+    const int nslot = gemv_slots(a);
+    v2f pc[2 * MAX_KSPLIT];
 #pragma unroll
-    for (int c = 0; c < 16; c++) pc[c] = c < a.ksplit ? *(const v2f *)(a.part + (long)c * a.n_out + e) : v2f{0.f, 0.f};
+    for (int c = 0; c < 2 * MAX_KSPLIT; c++)
+        pc[c] = c < nslot ? *(const v2f *)(a.part + (long)c * a.n_out + e) : v2f{0.f, 0.f};
     v2f v = {0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 16; c++)
-        if (c < a.ksplit) v += pc[c];
+    for (int c = 0; c < 2 * MAX_KSPLIT; c++)
+        if (c < nslot) v += pc[c];
     float r0 = v.x + act_load(a.resid, a.resid_dt, e), r1 = v.y + act_load(a.resid, a.resid_dt, e + 1);
     *(v2f *)(h + e) = v2f{r0, r1};
     if (!hq) return;
@@ -494,14 +641,14 @@ int launch_resid_reduce_split(const GemvArgs &a, float *h, uint8_t *hq, float *h
     return hip_check("resid_reduce_split");
 }
 
-int launch_swiglu_quant(const float *pg, const float *pu, int ksplit, long stride, long rows_host,
+int launch_swiglu_quant(const float *pg, const float *pu, int nslot, long stride, long rows_host,
                         const int *rows_dev, int cols, uint8_t *q, float *sc, long q_part, long sc_part, int ns,
                         hipStream_t s)
 {
     const long items = rows_host * (cols / 128);
     const dim3 g(grid_for(items, 4, 4096));
     if (ns == 2)
-        hipLaunchKernelGGL((k_swiglu_quant<2>), g, dim3(256), 0, s, pg, pu, ksplit, stride, rows_host, rows_dev, cols, q,
+        hipLaunchKernelGGL((k_swiglu_quant<2>), g, dim3(256), 0, s, pg, pu, nslot, stride, rows_host, rows_dev, cols, q,
                            sc, q_part, sc_part);
     else return fail(DL_ERR_UNSUPPORTED, "swiglu quant parts=%d", ns);
     return hip_check("swiglu_quant");

@@ -362,10 +362,12 @@ int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePl
     return hip_check("plan");
 }
 
-// out[b, d] = resid[b, d] + sum_j gate[b, j] f_j[d] + sum_s f_s[d], in that order.  A thread owns 4
+// out[b, d] = resid[b, d] + sum_j gate[b, j] f_j[d] + sum_s f_s[d], in that order, where f is the sum of the
+// expert output's nslot partial slots (in slot order).  A thread owns 4
 // consecutive features of one token; the token's pair indices and gates are wave-uniform (scalar loads), and
 // the expert outputs are fetched 8 slots at a time so their loads are in flight together.
-__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, const int *__restrict__ pair_idx,
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, int nslot, long fstride,
+                                                 const int *__restrict__ pair_idx,
                                                  const float *__restrict__ gates, int B, int D, int ke, int S,
                                                  const void *__restrict__ resid, int resid_dt, void *__restrict__ out,
                                                  int out_dt, float *__restrict__ out32)
@@ -389,6 +391,11 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, co
 #pragma unroll
         for (int u = 0; u < 8; u++)
             if (j0 + u < kk) f[u] = *(const v4f *)(F + (long)pi[j0 + u] * D + d);
+        for (int k = 1; k < nslot; k++) {
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                if (j0 + u < kk) f[u] += *(const v4f *)(F + k * fstride + (long)pi[j0 + u] * D + d);
+        }
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             const int j = j0 + u;
@@ -410,11 +417,12 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, co
     } else *(v4f *)((float *)out + row) = acc;
 }
 
-int launch_combine(const float *F, const MoePlan &p, const float *gates, int B, int D, int ke, int S,
+int launch_combine(const float *F, int nslot, long fstride, const MoePlan &p, const float *gates, int B, int D, int ke,
+                   int S,
                    const void *resid, int resid_dt, void *out, int out_dt, float *out32, hipStream_t s)
 {
     dim3 g((D / 4 + 255) / 256, B);
-    hipLaunchKernelGGL(k_combine, g, dim3(256), 0, s, F, p.pair_idx, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
+    hipLaunchKernelGGL(k_combine, g, dim3(256), 0, s, F, nslot, fstride, p.pair_idx, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
                        out32);
     return hip_check("combine");
 }
