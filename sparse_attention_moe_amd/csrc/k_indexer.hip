@@ -186,23 +186,34 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
         }
     const int32_t *pt = page_table + (long)b * max_pages;
     const int ps_mask = (1 << ps_shift) - 1;
-    __syncthreads();
-
-    for (int step = 0; step < 4; step++) {
-        const long g0 = blk0 + (long)(step * 4 + wave) * 64;  // this wave's 64 positions
-        if (g0 >= L) break;
-        v4i Bk[4][KCH];
+    // cache rows of every position this lane loads (step st, group sg: position g0(st) + sg*16 + ln), all
+    // page-table reads in flight at once
+    long row[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; st++)
 #pragma unroll
         for (int sg = 0; sg < 4; sg++) {
-            long pos = g0 + sg * 16 + ln;
-            bool ok = pos < L;
-            long row = ok ? ((long)pt[pos >> ps_shift] << ps_shift) + (pos & ps_mask) : 0;
+            const long pos = blk0 + (long)(st * 4 + wave) * 64 + sg * 16 + ln;
+            row[st][sg] = pos < L ? ((long)pt[pos >> ps_shift] << ps_shift) + (pos & ps_mask) : -1;
+        }
+    __syncthreads();
+    // keys of step st: 4 groups of 16 positions x KCH chunks of 64 bytes; two steps in flight
+    auto load_keys = [&](int st, v4i (&Bk)[4][KCH]) {
+#pragma unroll
+        for (int sg = 0; sg < 4; sg++)
 #pragma unroll
             for (int kc = 0; kc < KCH; kc++) {
-                int d = kc * 64 + lg * 16;
-                Bk[sg][kc] = (ok && d < DI) ? ldg16(k_pool + row * DI + d) : v4i{0, 0, 0, 0};
+                const int d = kc * 64 + lg * 16;
+                Bk[sg][kc] = (row[st][sg] >= 0 && d < DI) ? ldg16(k_pool + row[st][sg] * DI + d) : v4i{0, 0, 0, 0};
             }
-        }
+    };
+    v4i K0[4][KCH], K1[4][KCH];
+    load_keys(0, K0);
+    load_keys(1, K1);
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+        const long g0 = blk0 + (long)(st * 4 + wave) * 64;  // this wave's 64 positions
+        v4i (&Bk)[4][KCH] = (st & 1) ? K1 : K0;
         int mine = 0;
 #pragma unroll
         for (int sg = 0; sg < 4; sg++) {
@@ -220,7 +231,8 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
             part += __shfl_xor(part, 32, 64);
             if (lg == sg) mine = part;
         }
-        long pos = g0 + lane;
+        if (st + 2 < 4) load_keys(st + 2, Bk);  // this buffer is free again
+        const long pos = g0 + lane;
         if (pos < L) {
             scores[(long)b * Lmax + pos] = mine;
             atomicAdd(&s_hist[bin1_of(mine)], 1u);
@@ -231,6 +243,21 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
     for (int i = tid; i < NB1; i += 256) {
         const unsigned v = s_hist[i];
         if (v) atomicAdd(gh + i, v);
+    }
+}
+
+__device__ __forceinline__ void load16(const int32_t *sc, long p0, int L, int v[16])
+{
+    if (p0 + 16 <= L) {
+        const v4i *q = (const v4i *)(sc + p0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v4i t = q[i];
+            v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = (p0 + i < L) ? sc[p0 + i] : INT32_MIN;
     }
 }
 
@@ -259,34 +286,20 @@ __global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ 
     __syncthreads();
     for (int i = tid; i < NB2; i += 256) s_hist[i] = 0;
     __syncthreads();
-    const int32_t *sc = scores + (long)b * Lmax;
-    for (int i = 0; i < SEL_CHUNK / 256; i++) {
-        const long p = c0 + (long)i * 256 + tid;
-        if (p < L) {
-            const unsigned v = (unsigned)sc[p];
-            if (v >= lo && v <= hi) atomicAdd(&s_hist[(v - lo) >> shift], 1u);
-        }
+    // the thread's 16 consecutive scores, all loads in flight at once (positions past L read INT32_MIN,
+    // which is outside every range)
+    int v[16];
+    load16(scores + (long)b * Lmax, c0 + (long)tid * 16, L, v);
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const unsigned x = (unsigned)v[i];
+        if (v[i] >= 0 && x >= lo && x <= hi) atomicAdd(&s_hist[(x - lo) >> shift], 1u);
     }
     __syncthreads();
     unsigned *gh = hist_out + (long)b * NB2;
     for (int i = tid; i < NB2; i += 256) {
         const unsigned v = s_hist[i];
         if (v) atomicAdd(gh + i, v);
-    }
-}
-
-__device__ __forceinline__ void load16(const int32_t *sc, long p0, int L, int v[16])
-{
-    if (p0 + 16 <= L) {
-        const v4i *q = (const v4i *)(sc + p0);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            v4i t = q[i];
-            v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = (p0 + i < L) ? sc[p0 + i] : INT32_MIN;
     }
 }
 
