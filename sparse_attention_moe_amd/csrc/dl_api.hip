@@ -161,7 +161,7 @@ static constexpr int FFN_PARTS = 2;
 
 static void attn_split_ws(Ws &w, int B, int H, int Dv, int top_k, AttnWs &a)
 {
-    const long ns = attention_splits(top_k);
+    const long ns = attention_splits(top_k, B, H);
     a.opart = w.take<float>((long)B * ns * H * Dv);
     a.ml = w.take<float>((long)B * ns * H * 2);
 }

@@ -111,7 +111,7 @@ int launch_quant(const float *x, long rows_host, const int *rows_dev, int cols, 
 // ------------------------------------------------------------- attention
 // opart [B, splits, H, Dv] and ml [B, splits, H, 2] are scratch for the matrix-core path.
 bool attention_mfma_ok(int H, int Dc, int Dv, int q_dt, int kv_dt);
-int attention_splits(int top_k);
+int attention_splits(int top_k, int B, int H);
 // With the matrix-core path and o == nullptr only the split partials are written (the caller merges).
 int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
                      int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, float *opart,
