@@ -333,7 +333,7 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
     const long P = (long)B * (ke + S);
     f.plan.n_active = w.take<int>(1);
     f.plan.n_pairs = w.take<int>(1);
-    f.plan.n_groups = w.take<int>(1);
+    f.plan.grp_off = w.take<int>(NE + 1);
     f.plan.active = w.take<int>(NE);
     f.plan.tok_off = w.take<int>(NE);
     f.plan.tok_cnt = w.take<int>(NE);
@@ -377,7 +377,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     g.tok_off = f.plan.tok_off;
     g.tok_cnt = f.plan.tok_cnt;
     g.max_groups = (B + 15) / 16;
-    g.groups_dev = f.plan.n_groups;
+    g.grp_off = f8 ? f.plan.grp_off : nullptr;
     g.pair_act = f.plan.pair_tok;
     g.o_ts = I;
     g.out = f.Z;
@@ -404,7 +404,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     d.tok_off = f.plan.tok_off;
     d.tok_cnt = f.plan.tok_cnt;
     d.max_groups = (B + 15) / 16;
-    d.groups_dev = f.plan.n_groups;
+    d.grp_off = f8 ? f.plan.grp_off : nullptr;
     d.pair_act = nullptr;  // Z rows are per pair
     d.o_ts = D;
     d.out = f.F;

@@ -67,8 +67,8 @@ struct GemvArgs {
     int n_active_host;
     const int *tok_off, *tok_cnt;  // plan mode: pairs of slot u are [tok_off[u], +tok_cnt[u])
     int ntok_host;                 // uniform mode: tokens 0..ntok-1 for every matrix
-    int max_groups;                // upper bound of ceil(tokens per matrix / 16)
-    const int *groups_dev;         // plan mode: device value of that bound (nullptr: max_groups)
+    int max_groups;                // fp32 path: upper bound of ceil(tokens per matrix / 16)
+    const int *grp_off;            // plan mode: prefix over active slots of their token groups (16 / NS tokens)
     const int *pair_act;           // plan mode: activation row of global pair p
     int a_ts, a_ms;                // uniform mode: activation row = t*a_ts + m*a_ms
     long o_ts, o_ms;               // output offset = t*o_ts + m*o_ms (uniform) or p*o_ts (plan)
@@ -91,6 +91,7 @@ struct GemvArgs {
 // Partial slots the GEMV writes: 2 per K chunk in flat mode, else 1 per chunk (0 without a split).
 __host__ __device__ inline int gemv_slots(const GemvArgs &a) { return a.flat ? 2 * a.ksplit : a.ksplit; }
 static constexpr int MAX_KSPLIT = 16;
+static constexpr int GEMV_MAXMAT = 4096;  // active matrices of one FP8 GEMV (plan mode)
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
 // Flat mode for an FP8 GEMV of about `units_est` units: the K split (<= max_ksplit chunks) with chunks no
 // longer than a wave's share of steps.
@@ -126,10 +127,11 @@ int launch_resid_reduce_split(const GemvArgs &a, float *h, uint8_t *hq, float *h
                               hipStream_t s);
 
 // ------------------------------------------------------------- MoE
+static constexpr int PLAN_TPG = 8;  // tokens per group of the expert GEMV (16 MFMA columns / 2 FP8 parts)
 struct MoePlan {
     int *n_active;   // [1]
     int *n_pairs;    // [1]
-    int *n_groups;   // [1] max over active experts of ceil(tokens / 16)
+    int *grp_off;    // [NE + 1] prefix over active slots of ceil(tokens / PLAN_TPG)
     int *active;     // [NE]
     int *tok_off;    // [NE]
     int *tok_cnt;    // [NE]

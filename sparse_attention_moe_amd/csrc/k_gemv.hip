@@ -7,15 +7,17 @@
 // blocks: each block is exactly one v_mfma_f32_16x16x128_f8f6f4 on the raw codes, and the block's
 // partial sums are scaled once — the codes are never decoded on the vector units.
 //
-// The activations (up to 16 tokens per pass, the N side of the instruction) enter as NS FP8 parts:
-// part 0 is the value rounded to e4m3 with a per-(row, 128-block) scale, part s the remainder of
-// parts < s with its own scale.  Two parts carry about 10 significant bits, four about 16, so the
-// projections ahead of the router keep near-fp32 accuracy while the expert FFN uses two.
+// The activations enter as NS FP8 parts: part 0 is the value rounded to e4m3 with a per-(row, 128-block)
+// scale, part s the remainder of parts < s with its own scale.  Two parts carry about 10 significant bits,
+// four about 16, so the projections ahead of the router keep near-fp32 accuracy while the expert FFN uses
+// two.  The parts share the 16 columns (the N side) of one instruction: a token group is 16 / NS tokens x NS
+// parts, each lane scales its column by its own part's scale, and the parts of a token are added once at
+// the end of an item (DPP within the 16-lane row).  An expert with one or two tokens thus costs one
+// instruction, one activation load and one scale load per weight tile and K block.
 //
-// Work items are (active matrix, 16-row tile, group of 16 tokens); matrices and tokens can come
-// from a device-side plan (experts with no token are simply absent: the MoE tile skip of Kiln's
-// "What moved the number ..." section).  Waves take items round-robin; every weight byte is read
-// once with 16-byte loads.
+// Work items are (active matrix, 16-row tile, token group); matrices and token groups come from a
+// device-side plan in the MoE (experts with no token are simply absent: the MoE tile skip of Kiln's
+// "What moved the number ..." section).  Every weight byte is read once with 16-byte loads.
 #include "dl_common.h"
 #include "dl_internal.h"
 
@@ -43,11 +45,11 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // split between two neighbouring waves: the first writes partial slot 2 kc, the second 2 kc + 1, and a chunk
 // done by one wave zero-fills 2 kc + 1.  Either way consecutive segments of a wave mostly share the matrix
 // and token group (no new metadata) and the load pipeline runs on across segment boundaries.
-template <int NS, bool SW, int RT>
+template <bool SW, int RT>
 struct Stage {
     v8i A[RT], A2[RT];
-    v8i Bv[NS];
-    float as[NS];
+    v8i Bv;
+    float as;
 };
 
 // Weight scales of the item's K range: lane j holds the scale of K-block kb0 + j (j < 64); the compute
@@ -72,9 +74,8 @@ __device__ __forceinline__ v8i ld16x2(const uint8_t *p, int gap)
 // Operand bytes of lane l = (ln, lg): row ln of the tile, K bytes {lg*16 .. +16} and {64 + lg*16 .. +16}
 // of the 128-wide block.  Row-major weights: two loads 64 B apart in the row; tiled weights: 16 B at
 // l*16 and 1024 + l*16 of the tile's 2 KB.  The activations use the same K assignment.
-template <int NS, bool SW, int RT, bool TL>
-__device__ __forceinline__ void load_stage(Stage<NS, SW, RT> &st, const Ctx<RT> &c, long cols, long aq_part,
-                                           long asc_part, int kb)
+template <bool SW, int RT, bool TL>
+__device__ __forceinline__ void load_stage(Stage<SW, RT> &st, const Ctx<RT> &c, long cols, int kb)
 {
 #pragma unroll
     for (int r = 0; r < RT; r++) {
@@ -88,51 +89,64 @@ __device__ __forceinline__ void load_stage(Stage<NS, SW, RT> &st, const Ctx<RT> 
             if (SW) st.A2[r] = ld16x2(c.wp2 + r * 16 * cols + kb * 128, 64);
         }
     }
-#pragma unroll
-    for (int s = 0; s < NS; s++) {
-        // lanes of empty token slots load nothing (their result is scaled by 0)
-        if (c.tv) {
-            st.Bv[s] = ld16x2(c.ap + s * aq_part + kb * 128, 64);
-            st.as[s] = c.asp[s * asc_part + kb];
-        } else {
-            st.Bv[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            st.as[s] = 0.f;
-        }
+    // lanes of empty token slots load nothing (their result is scaled by 0)
+    if (c.tv) {
+        st.Bv = ld16x2(c.ap + kb * 128, 64);
+        st.as = c.asp[kb];
+    } else {
+        st.Bv = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        st.as = 0.f;
     }
 }
 
-// Segment (steps [s, e) of one unit's chunk) -> context.  Reuses `prev` (same matrix and token group) when
-// possible: then no memory is read.
-template <int RT, bool SW, bool TL>
-__device__ __forceinline__ void make_ctx(const GemvArgs &a, long s, long e, int groups, int tiles,
-                                         const Ctx<RT> *prev, Ctx<RT> &c)
+// Segment (steps [s, e) of one unit's chunk) -> context.  Units are (u, tile, g) with g fastest; in plan mode
+// matrix slot u has goff[u+1] - goff[u] token groups (goff in LDS), else every matrix has `groups`.  Reuses
+// `prev` (same matrix and token group) when possible: then no memory is read.
+template <int NS, int RT, bool SW, bool TL>
+__device__ __forceinline__ void make_ctx(const GemvArgs &a, long s, long e, int groups, int tiles, int n_act,
+                                         const int *goff, const Ctx<RT> *prev, Ctx<RT> &c)
 {
+    constexpr int TPG = 16 / NS;
     const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
     const int unit = (int)(s / a.nkb);
     const int kb = (int)(s - (long)unit * a.nkb);
     const int kc = kb / a.kchunk;
-    const int g = unit % groups;
-    const int tile = (unit / groups) % tiles;
-    const int u = unit / groups / tiles;
-    if (prev && prev->u == u && prev->t0 == g * 16) {
+    int u, tile, g;
+    if (goff) {
+        int lo = 0, hi = n_act - 1;  // last slot with tiles * goff[slot] <= unit
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tiles * goff[mid] <= unit) lo = mid; else hi = mid - 1;
+        }
+        u = lo;
+        const int gc = goff[u + 1] - goff[u], r = unit - tiles * goff[u];
+        tile = r / gc;
+        g = r - tile * gc;
+    } else {
+        g = unit % groups;
+        tile = (unit / groups) % tiles;
+        u = unit / groups / tiles;
+    }
+    if (prev && prev->u == u && prev->t0 == g * TPG) {
         c = *prev;
     } else {
         c.u = u;
         c.m = __builtin_amdgcn_readfirstlane(a.active ? a.active[u] : u);
         c.cnt = a.tok_cnt ? a.tok_cnt[u] : a.ntok_host;
         c.off = a.tok_cnt ? a.tok_off[u] : 0;
-        c.t0 = g * 16;
+        c.t0 = g * TPG;
         c.valid = c.t0 < c.cnt;
-        c.tt = c.t0 + ln;
+        // column ln = token t0 + ln % TPG, part ln / TPG
+        c.tt = c.t0 + ln % TPG;
         c.tv = c.tt < c.cnt;
-        // lanes past the last token read the first token's row and get a zero scale (no branches)
         const int ts = c.tv ? c.tt : c.t0;
         const long arow = !c.valid ? 0
                           : a.pair_act ? a.pair_act[c.off + ts]
                           : a.tok_cnt  ? (long)(c.off + ts)
                                        : (long)ts * a.a_ts + (long)c.m * a.a_ms;
-        c.ap = a.aq + arow * a.cols + lg * 16;
-        c.asp = a.asc + arow * a.nkb;
+        const int sp = ln / TPG;
+        c.ap = a.aq + sp * a.aq_part + arow * a.cols + lg * 16;
+        c.asp = a.asc + sp * a.asc_part + arow * a.nkb;
     }
     const int kb_end = min(a.nkb, (kc + 1) * a.kchunk);
     c.kc = kc;
@@ -155,17 +169,44 @@ __device__ __forceinline__ void make_ctx(const GemvArgs &a, long s, long e, int 
 
 __device__ __forceinline__ float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
+// Sum over the NS part columns of a token (lanes ln, ln + 16/NS, ... of the 16-lane row), on the DPP network.
+__device__ __forceinline__ float row_ror(float v, int n8)
+{
+    return n8 ? __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false))
+              : __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));
+}
+template <int NS>
+__device__ __forceinline__ v4f sum_parts(v4f v)
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (NS == 4) v[i] += row_ror(v[i], 0);
+        if (NS >= 2) v[i] += row_ror(v[i], 1);
+    }
+    return v;
+}
+
 template <int NS, int EPI, int RT, bool TL>
 __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k_gemv_fp8(GemvArgs a)
 {
     constexpr bool SW = EPI == EPI_SWIGLU;
-    const int lane = threadIdx.x & 63, lg = lane >> 4;
+    constexpr int TPG = 16 / NS;  // tokens per group (the parts share the 16 columns)
+    __shared__ int s_goff[GEMV_MAXMAT + 1];
+    const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
     const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int nwaves = gridDim.x * 4;
     const int n_act = a.n_active_dev ? *a.n_active_dev : a.n_active_host;
-    const int groups = a.groups_dev ? *a.groups_dev : a.max_groups;
+    const int groups = (a.ntok_host + TPG - 1) / TPG;  // uniform mode
     const int tiles = a.rows / (16 * RT);
-    const long units = (long)n_act * tiles * groups;
+    long units;
+    if (a.grp_off) {
+        for (int i = threadIdx.x; i <= n_act; i += 256) s_goff[i] = a.grp_off[i];
+        __syncthreads();
+        units = (long)tiles * s_goff[n_act];
+    } else {
+        units = (long)n_act * tiles * groups;
+    }
+    const int *goff = a.grp_off ? s_goff : nullptr;
     const long S = units * a.nkb;  // steps of all units
     long s0, s1;
     if (a.flat) {
@@ -193,36 +234,39 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     const bool parts = a.flat || a.ksplit > 1;
     Ctx<RT> c, n;
     long e = seg_end(s0);
-    make_ctx<RT, SW, TL>(a, s0, e, groups, tiles, nullptr, c);
-    Stage<NS, SW, RT> cur, nxt;
-    if (c.valid) load_stage<NS, SW, RT, TL>(cur, c, a.cols, a.aq_part, a.asc_part, c.kb0);
+    make_ctx<NS, RT, SW, TL>(a, s0, e, groups, tiles, n_act, goff, nullptr, c);
+    Stage<SW, RT> cur, nxt;
+    if (c.valid) load_stage<SW, RT, TL>(cur, c, a.cols, c.kb0);
     for (long s = s0; s < s1;) {
         const bool more = e < s1;
         const long e2 = more ? seg_end(e) : e;
-        if (more) make_ctx<RT, SW, TL>(a, e, e2, groups, tiles, &c, n);
+        if (more) make_ctx<NS, RT, SW, TL>(a, e, e2, groups, tiles, n_act, goff, &c, n);
         if (c.valid) {
             v4f tot[RT], tot2[RT];
 #pragma unroll
             for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
             const float tmask = c.tv ? 1.f : 0.f;
             for (int kb = c.kb0; kb < c.kb1; kb++) {
-                if (kb + 1 < c.kb1) load_stage<NS, SW, RT, TL>(nxt, c, a.cols, a.aq_part, a.asc_part, kb + 1);
-                else if (more && n.valid) load_stage<NS, SW, RT, TL>(nxt, n, a.cols, a.aq_part, a.asc_part, n.kb0);
+                if (kb + 1 < c.kb1) load_stage<SW, RT, TL>(nxt, c, a.cols, kb + 1);
+                else if (more && n.valid) load_stage<SW, RT, TL>(nxt, n, a.cols, n.kb0);
                 const int kr = kb - c.kb0;
                 const float ws = (kr < 64 ? lane_f(c.wsv, kr) : c.wsp[kb]) * tmask;
                 const float ws2 = SW ? (kr < 64 ? lane_f(c.wsv2, kr) : c.wsp2[kb]) * tmask : 0.f;
+                const float f = ws * cur.as, f2 = ws2 * cur.as;
 #pragma unroll
-                for (int s = 0; s < NS; s++) {
-                    const float f = ws * cur.as[s], f2 = ws2 * cur.as[s];
-#pragma unroll
-                    for (int r = 0; r < RT; r++) {
-                        tot[r] += mfma_fp8(cur.A[r], cur.Bv[s]) * f;
-                        if (SW) tot2[r] += mfma_fp8(cur.A2[r], cur.Bv[s]) * f2;
-                    }
+                for (int r = 0; r < RT; r++) {
+                    tot[r] += mfma_fp8(cur.A[r], cur.Bv) * f;
+                    if (SW) tot2[r] += mfma_fp8(cur.A2[r], cur.Bv) * f2;
                 }
                 cur = nxt;
             }
-            if (c.tv) {
+            // add the parts of each token (columns ln, ln + TPG, ...): every lane of the part ends with the sum
+#pragma unroll
+            for (int r = 0; r < RT; r++) {
+                tot[r] = sum_parts<NS>(tot[r]);
+                if (SW) tot2[r] = sum_parts<NS>(tot2[r]);
+            }
+            if (c.tv && ln < TPG) {
                 const long ooff = a.tok_cnt ? (long)(c.off + c.tt) * a.o_ts : (long)c.tt * a.o_ts + (long)c.m * a.o_ms;
                 const long slot = a.flat ? 2 * c.kc + c.piece : c.kc;
 #pragma unroll
@@ -248,7 +292,7 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
                 }
             }
         } else if (more && n.valid) {
-            load_stage<NS, SW, RT, TL>(cur, n, a.cols, a.aq_part, a.asc_part, n.kb0);
+            load_stage<SW, RT, TL>(cur, n, a.cols, n.kb0);
         }
         s = e;
         e = e2;
@@ -279,39 +323,36 @@ __global__ __launch_bounds__(256) void k_proj_shot(GemvArgs a)
     float ws[KB];
 #pragma unroll
     for (int k = 0; k < KB; k++) ws[k] = a.wsc[(long)rb * a.nkb + kb0 + k];
-    for (int t0 = 0; t0 < a.ntok_host; t0 += 16) {
-        const int t = t0 + ln;
+    constexpr int TPG = 16 / NS;  // tokens per group: the NS parts share the 16 columns
+    for (int t0 = 0; t0 < a.ntok_host; t0 += TPG) {
+        const int t = t0 + ln % TPG, sp = ln / TPG;
         const bool tv = t < a.ntok_host;
-        v8i Bv[KB][NS];
-        float as[KB][NS];
+        v8i Bv[KB];
+        float as[KB];
 #pragma unroll
-        for (int k = 0; k < KB; k++)
-#pragma unroll
-            for (int s = 0; s < NS; s++) {
-                if (tv) {
-                    Bv[k][s] = ld16x2(a.aq + s * a.aq_part + (long)t * a.cols + (kb0 + k) * 128 + lg * 16, 64);
-                    as[k][s] = a.asc[s * a.asc_part + (long)t * a.nkb + kb0 + k];
-                } else {
-                    Bv[k][s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-                    as[k][s] = 0.f;
-                }
+        for (int k = 0; k < KB; k++) {
+            if (tv) {
+                Bv[k] = ld16x2(a.aq + sp * a.aq_part + (long)t * a.cols + (kb0 + k) * 128 + lg * 16, 64);
+                as[k] = a.asc[sp * a.asc_part + (long)t * a.nkb + kb0 + k];
+            } else {
+                Bv[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                as[k] = 0.f;
             }
+        }
         v4f tot[RT];
 #pragma unroll
         for (int r = 0; r < RT; r++) tot[r] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KB; k++)
+        for (int k = 0; k < KB; k++) {
+            const float f = ws[k] * as[k];
 #pragma unroll
-            for (int s = 0; s < NS; s++) {
-                const float f = ws[k] * as[k][s];
+            for (int r = 0; r < RT; r++) tot[r] += mfma_fp8(A[k][r], Bv[k]) * f;
+        }
 #pragma unroll
-                for (int r = 0; r < RT; r++) tot[r] += mfma_fp8(A[k][r], Bv[k][s]) * f;
-            }
-#pragma unroll
-        for (int r = 0; r < RT; r++) s_acc[w][r][lane] = tot[r];
+        for (int r = 0; r < RT; r++) s_acc[w][r][lane] = sum_parts<NS>(tot[r]);
         __syncthreads();
         // wave w adds the four waves' sums of tiles 2w, 2w + 1
-        if (tv) {
+        if (tv && sp == 0) {
 #pragma unroll
             for (int q = 0; q < 2; q++) {
                 const int r = 2 * w + q;

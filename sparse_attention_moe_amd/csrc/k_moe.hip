@@ -173,8 +173,9 @@ __device__ __forceinline__ int token_topk(const double *lrow, int E, int ke)
 
 // ------------------------------------------------------------------ dispatch plan
 // From the picks s_exp[b * ke + j] (in LDS) of a whole workgroup of 1024 threads: active experts in
-// ascending id (shared experts last), each expert's pairs in (token, slot) order, and the pair index of
-// every (token, slot).  `distinct`: no token picks an expert twice (router output), so an expert's pair
+// ascending id (shared experts last), each expert's pairs in (token, slot) order, the pair index of every
+// (token, slot), and the prefix over active experts of their token groups of PLAN_TPG (grp_off, n_active + 1
+// entries) that the expert GEMV enumerates its work by.  `distinct`: no token picks an expert twice (router output), so an expert's pair
 // rank is the number of earlier tokens in its token mask (B <= 64); otherwise the earlier picks are counted.
 __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool distinct, int *s_cnt, int *s_off,
                            unsigned long long *s_mask, const MoePlan &p)
@@ -195,46 +196,48 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
     if (tid < 64) {
         // lane owns experts [lane * per, (lane + 1) * per)
         const int per = (E + 63) / 64;
-        int na = 0, npl = 0, mx = 0;
+        int na = 0, npl = 0, ng = 0;
         for (int i = 0; i < per; i++) {
             const int e = lane * per + i;
             if (e < E) {
                 const int c = s_cnt[e];
                 na += c > 0;
                 npl += c;
-                mx = max(mx, c);
+                ng += (c + PLAN_TPG - 1) / PLAN_TPG;
             }
         }
-        int ia = na, ip = npl;
+        int ia = na, ip = npl, ig = ng;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
-            const int ta = __shfl_up(ia, o, 64), tp = __shfl_up(ip, o, 64);
-            if (lane >= o) { ia += ta; ip += tp; }
+            const int ta = __shfl_up(ia, o, 64), tp = __shfl_up(ip, o, 64), tg = __shfl_up(ig, o, 64);
+            if (lane >= o) { ia += ta; ip += tp; ig += tg; }
         }
-        const int na_tot = __shfl(ia, 63, 64);
-        int a = ia - na, q = ip - npl;
+        const int na_tot = __shfl(ia, 63, 64), ng_tot = __shfl(ig, 63, 64);
+        int a = ia - na, q = ip - npl, gq = ig - ng;
         for (int i = 0; i < per; i++) {
             const int e = lane * per + i;
             if (e < E && s_cnt[e] > 0) {
                 p.active[a] = e;
                 p.tok_off[a] = q;
                 p.tok_cnt[a] = s_cnt[e];
+                p.grp_off[a] = gq;
                 s_off[e] = q;
                 a++;
                 q += s_cnt[e];
+                gq += (s_cnt[e] + PLAN_TPG - 1) / PLAN_TPG;
             }
         }
+        const int gs = (B + PLAN_TPG - 1) / PLAN_TPG;  // token groups of a shared expert
         for (int sx = lane; sx < S; sx += 64) {
             p.active[na_tot + sx] = E + sx;
             p.tok_off[na_tot + sx] = np + sx * B;
             p.tok_cnt[na_tot + sx] = B;
+            p.grp_off[na_tot + sx] = ng_tot + sx * gs;
         }
-        mx = wave_max_i(mx);
-        if (S > 0) mx = max(mx, B);
         if (lane == 0) {
+            p.grp_off[na_tot + S] = ng_tot + S * gs;
             *p.n_active = na_tot + S;
             *p.n_pairs = np + S * B;
-            *p.n_groups = (mx + 15) / 16;
         }
     }
     __syncthreads();
