@@ -12,45 +12,47 @@
 
 namespace dl {
 
-static constexpr int ROUTE_KC = 512;  // hidden features per workgroup (4 waves x 128)
-static constexpr int ROUTE_MAXC = 32; // chunks: hidden size <= 16,384
+static constexpr int ROUTE_KW = 256;  // hidden features per wave
+static constexpr int ROUTE_KC = 4 * ROUTE_KW;  // hidden features per workgroup
+static constexpr int ROUTE_MAXC = 16; // chunks: hidden size <= 16,384
 static constexpr int RP_MAXE = 1024;  // experts the router + plan kernel handles
 static constexpr int RP_LCAP = 8192;  // logits held in LDS at once (tokens per block = RP_LCAP / E)
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 // Partial router logits on the fp64 matrix cores: part[c, b, e] = sum over hidden chunk c of w_r[e, d] * h[b, d].
-// A workgroup owns 16 experts (the M side of v_mfma_f64_16x16x4f64) and a 512-feature chunk, one 128-feature
-// quarter per wave; 16 tokens form the N side.  Every fp32 product is exact in fp64 and the sums are fp64.
-// Lane (r, g) = (lane % 16, lane / 16) holds expert r's and token r's features 16 j + 4 g .. + 4 (j < 8);
-// instruction i of a group takes the i-th of those four, so A and B agree on the K index.  The four
-// quarters are added in order through LDS.
+// A workgroup owns 16 experts (the M side of v_mfma_f64_16x16x4f64) and a chunk of ROUTE_KC features,
+// ROUTE_KW per wave; 16 tokens form the N side.  Every fp32 product is exact in fp64 and the sums are fp64.
+// Lane (r, g) = (lane % 16, lane / 16) holds expert r's and token r's features 16 j + 4 g .. + 4 of the wave's
+// range; instruction i of a group takes the i-th of those four, so A and B agree on the K index.  The four
+// waves' sums are added in order through LDS.
 __global__ __launch_bounds__(256) void k_route_partial(const float *__restrict__ h, int B, int D,
                                                        const float *__restrict__ wr, int E, double *__restrict__ part)
 {
+    constexpr int NJ = ROUTE_KW / 16;
     __shared__ double s_d[4][16][17];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int e0 = blockIdx.x * 16, c = blockIdx.y;
-    const int kq = c * ROUTE_KC + w * 128 + 4 * g;
+    const int kq = c * ROUTE_KC + w * ROUTE_KW + 4 * g;
     const int e = e0 + r;
-    v4f wv[8];
+    v4f wv[NJ];
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
+    for (int j = 0; j < NJ; j++) {
         const int k = kq + 16 * j;
         wv[j] = (e < E && k < D) ? *(const v4f *)(wr + (long)e * D + k) : v4f{0.f, 0.f, 0.f, 0.f};
     }
     for (int t0 = 0; t0 < B; t0 += 16) {
         const int t = t0 + r;
-        v4f hv[8];
+        v4f hv[NJ];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
+        for (int j = 0; j < NJ; j++) {
             const int k = kq + 16 * j;
             hv[j] = (t < B && k < D) ? *(const v4f *)(h + (long)t * D + k) : v4f{0.f, 0.f, 0.f, 0.f};
         }
         v4d acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int j = 0; j < 8; j++)
+        for (int j = 0; j < NJ; j++)
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wv[j][i], (double)hv[j][i], acc, 0, 0, 0);
@@ -292,18 +294,31 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
     const int tb = RP_LCAP / E;
     for (int b0 = 0; b0 < B; b0 += tb) {
         const int nb = min(tb, B - b0);
-        for (int i = tid; i < nb * E; i += nT) {
-            const int b = b0 + i / E, e = i % E;
-            double pc[ROUTE_MAXC];  // every chunk's partial in flight at once, then summed in chunk order
+        // two logits per thread per pass, every chunk's partial of both in flight at once, summed in chunk order
+        for (int i0 = tid; i0 < nb * E; i0 += 2 * nT) {
+            double pc[2][ROUTE_MAXC];
 #pragma unroll
-            for (int c = 0; c < ROUTE_MAXC; c++) pc[c] = c < nchunk ? part[((long)c * B + b) * E + e] : 0.0;
-            double v = 0.0;
+            for (int k = 0; k < 2; k++) {
+                const int i = i0 + k * nT;
+                const int b = b0 + i / E, e = i % E;
+                const bool ok = i < nb * E;
 #pragma unroll
-            for (int c = 0; c < ROUTE_MAXC; c++)
-                if (c < nchunk) v += pc[c];
-            if (bias) v += (double)bias[e];
-            s_l[i] = v;
-            if (logits) logits[(long)b * E + e] = (float)v;
+                for (int c = 0; c < ROUTE_MAXC; c++)
+                    pc[k][c] = (ok && c < nchunk) ? part[((long)c * B + b) * E + e] : 0.0;
+            }
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                const int i = i0 + k * nT;
+                if (i >= nb * E) break;
+                const int b = b0 + i / E, e = i % E;
+                double v = 0.0;
+#pragma unroll
+                for (int c = 0; c < ROUTE_MAXC; c++)
+                    if (c < nchunk) v += pc[k][c];
+                if (bias) v += (double)bias[e];
+                s_l[i] = v;
+                if (logits) logits[(long)b * E + e] = (float)v;
+            }
         }
         __syncthreads();
         for (int bl = wv; bl < nb; bl += 16) {
