@@ -454,7 +454,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_mla(const uint16_t *__restrict_
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int head = r * 4 + lg, col = ln * 4;
-                *(v4f *)(op + (long)head * Dv + vb * 128 + half * 64 + col) = *(const v4f *)&st[head][col];
+                // streaming store: read once by the merge, so it should not sit dirty in the last-level
+                // cache until the expert weight stream evicts it (its write-back would then compete with
+                // that stream for HBM)
+                __builtin_nontemporal_store(*(const v4f *)&st[head][col],
+                                            (v4f *)(op + (long)head * Dv + vb * 128 + half * 64 + col));
             }
         }
     }

@@ -70,6 +70,13 @@ __device__ __forceinline__ v8i ld16x2(const uint8_t *p, int gap)
     v4i a = *(const v4i *)p, b = *(const v4i *)(p + gap);
     return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+// Weight bytes are read once per step: streaming (non-temporal) loads keep them from displacing the
+// step's small intermediates in the caches.
+__device__ __forceinline__ v8i ldw16x2(const uint8_t *p, int gap)
+{
+    v4i a = __builtin_nontemporal_load((const v4i *)p), b = __builtin_nontemporal_load((const v4i *)(p + gap));
+    return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
 // Operand bytes of lane l = (ln, lg): row ln of the tile, K bytes {lg*16 .. +16} and {64 + lg*16 .. +16}
 // of the 128-wide block.  Row-major weights: two loads 64 B apart in the row; tiled weights: 16 B at
@@ -82,11 +89,11 @@ __device__ __forceinline__ void load_stage(Stage<SW, RT> &st, const Ctx<RT> &c, 
         if (TL) {
             // consecutive 16-row tiles are cols/128 blocks of 2 KB apart
             const uint8_t *t = c.wp + (long)r * (cols / 128) * 2048 + (long)kb * 2048;
-            st.A[r] = ld16x2(t, 1024);
-            if (SW) st.A2[r] = ld16x2(c.wp2 + (long)r * (cols / 128) * 2048 + (long)kb * 2048, 1024);
+            st.A[r] = ldw16x2(t, 1024);
+            if (SW) st.A2[r] = ldw16x2(c.wp2 + (long)r * (cols / 128) * 2048 + (long)kb * 2048, 1024);
         } else {
-            st.A[r] = ld16x2(c.wp + r * 16 * cols + kb * 128, 64);
-            if (SW) st.A2[r] = ld16x2(c.wp2 + r * 16 * cols + kb * 128, 64);
+            st.A[r] = ldw16x2(c.wp + r * 16 * cols + kb * 128, 64);
+            if (SW) st.A2[r] = ldw16x2(c.wp2 + r * 16 * cols + kb * 128, 64);
         }
     }
     // lanes of empty token slots load nothing (their result is scaled by 0)
@@ -318,8 +325,8 @@ __global__ __launch_bounds__(256) void k_proj_shot(GemvArgs a)
     for (int k = 0; k < KB; k++)
 #pragma unroll
         for (int r = 0; r < RT; r++)
-            A[k][r] = TL ? ld16x2(a.w + ((long)(rb * RT + r) * a.nkb + kb0 + k) * 2048 + lane * 16, 1024)
-                         : ld16x2(a.w + (long)((rb * RT + r) * 16 + ln) * a.cols + (kb0 + k) * 128 + lg * 16, 64);
+            A[k][r] = TL ? ldw16x2(a.w + ((long)(rb * RT + r) * a.nkb + kb0 + k) * 2048 + lane * 16, 1024)
+                         : ldw16x2(a.w + (long)((rb * RT + r) * 16 + ln) * a.cols + (kb0 + k) * 128 + lg * 16, 64);
     float ws[KB];
 #pragma unroll
     for (int k = 0; k < KB; k++) ws[k] = a.wsc[(long)rb * a.nkb + kb0 + k];

@@ -204,7 +204,10 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
 #pragma unroll
             for (int kc = 0; kc < KCH; kc++) {
                 const int d = kc * 64 + lg * 16;
-                Bk[sg][kc] = (row[st][sg] >= 0 && d < DI) ? ldg16(k_pool + row[st][sg] * DI + d) : v4i{0, 0, 0, 0};
+                // streaming loads: every key byte is read once per step
+                Bk[sg][kc] = (row[st][sg] >= 0 && d < DI)
+                                 ? __builtin_nontemporal_load((const v4i *)(k_pool + row[st][sg] * DI + d))
+                                 : v4i{0, 0, 0, 0};
             }
     };
     v4i K0[4][KCH], K1[4][KCH];
