@@ -142,7 +142,7 @@ int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_
  *   w_o      nullable; rows = D, cols = n_heads * (w_uv ? head_dim : d_v)
  *   residual bf16 or fp32 [B, D] (required with w_o)
  *   out      fp32 [B, n_heads, d_v] (no w_o) or fp32 [B, D]
- * Limits: d_v <= d_c <= 1024; FP8 weights need rows % 32 == 0 and cols % 128 == 0.
+ * Limits: d_v <= d_c <= 1024; FP8 weights need rows % 32 == 0 and cols % 128 == 0; W_O cols <= 262144.
  * Workspace: dl_sparse_attn_workspace(...). */
 size_t dl_sparse_attn_workspace(int32_t batch, int32_t n_heads, int32_t d_v, int32_t top_k, const dl_mat *w_uv,
                                 const dl_mat *w_o);
@@ -175,8 +175,8 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
  *   w_gate, w_up: count = n_routed + n_shared, rows = inter, cols = D;
  *   w_down: count = n_routed + n_shared, rows = D, cols = inter;
  *   residual fp32 [B, D] nullable; out [B, D] in out_dt (DL_F32 or DL_BF16, rounded once, RNE).
- * Limits: D % 4 == 0; B * (top_k + n_shared) <= 16384; top_k + n_shared <= 40; n_routed <= 1024;
- * n_routed + n_shared <= 4096.  With FP8 weights the
+ * Limits: D % 4 == 0; D <= 65536; inter <= 16384; B * (top_k + n_shared) <= 16384;
+ * top_k + n_shared <= 40; n_routed <= 1024; n_routed + n_shared <= 4096.  With FP8 weights the
  * activations enter the matrix cores as two FP8 parts (value and remainder) with per-128-block
  * scales.  Workspace: dl_moe_ffn_workspace(...). */
 size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared);

@@ -470,6 +470,7 @@ static int check_ffn_shapes(int B, int D, int I, int ke, int E, int S, const dl_
 {
     if (B < 1 || D < 1 || I < 1) return fail(DL_ERR_SHAPE, "ffn B=%d D=%d I=%d", B, D, I);
     if (D % 4) return fail(DL_ERR_UNSUPPORTED, "ffn hidden size %d (multiple of 4)", D);
+    if (D > 65536 || I > 16384) return fail(DL_ERR_UNSUPPORTED, "ffn D=%d (<= 65536) I=%d (<= 16384)", D, I);
     if (ke < 1 || ke > 32 || ke > E) return fail(DL_ERR_SHAPE, "expert top_k %d of %d", ke, E);
     if (ke + S > 40) return fail(DL_ERR_UNSUPPORTED, "top_k + shared experts %d (<= 40)", ke + S);
     if (S < 0 || E > 1024 || E + S > 4096) return fail(DL_ERR_SHAPE, "experts %d + %d", E, S);
@@ -510,6 +511,8 @@ static int check_proj(int H, int Dv, const dl_mat *w_uv, const dl_mat *w_o, int 
     }
     if (!w_o || !w_o->w) return fail(DL_ERR_NULL, "w_o");
     DL_TRY(check_mat(w_o, "w_o", 1, w_o->rows, H * hd));
+    if ((long)H * hd > (long)MAX_KSPLIT * GEMV_MAXCHUNK * 128)
+        return fail(DL_ERR_UNSUPPORTED, "W_O input width %ld (<= %d)", (long)H * hd, MAX_KSPLIT * GEMV_MAXCHUNK * 128);
     *D_out = w_o->rows;
     return DL_OK;
 }

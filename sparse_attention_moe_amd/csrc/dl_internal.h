@@ -91,6 +91,7 @@ struct GemvArgs {
 // Partial slots the GEMV writes: 2 per K chunk in flat mode, else 1 per chunk (0 without a split).
 __host__ __device__ inline int gemv_slots(const GemvArgs &a) { return a.flat ? 2 * a.ksplit : a.ksplit; }
 static constexpr int MAX_KSPLIT = 16;
+static constexpr int GEMV_MAXCHUNK = 128;  // most 128-wide K-blocks in one chunk of the FP8 GEMV
 static constexpr int GEMV_MAXMAT = 4096;  // active matrices of one FP8 GEMV (plan mode)
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
 // Flat mode for an FP8 GEMV of about `units_est` units: the K split (<= max_ksplit chunks) with chunks no

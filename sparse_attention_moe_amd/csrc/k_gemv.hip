@@ -52,8 +52,8 @@ struct Stage {
     float as;
 };
 
-// Weight scales of the item's K range: lane j holds the scale of K-block kb0 + j (j < 64); the compute
-// loop reads them with readlane instead of one vector load per K-block.
+// Weight scales of the segment's K range (at most 128 blocks): lane j holds the scale of K-block kb0 + j in wsv
+// and of kb0 + 64 + j in wsvB; the compute loop reads them with readlane, so no scale is loaded per K-block.
 template <int RT>
 struct Ctx {
     int u, m, cnt, off, t0, r0, kc, kb0, kb1, piece, whole;
@@ -61,7 +61,7 @@ struct Ctx {
     int tt;
     const uint8_t *wp, *wp2, *ap;
     const float *wsp, *wsp2, *asp;
-    float wsv, wsv2;
+    float wsv, wsv2, wsvB, wsvB2;
 };
 
 // Two 16-byte halves of an operand: at p and p + gap.
@@ -96,14 +96,10 @@ __device__ __forceinline__ void load_stage(Stage<SW, RT> &st, const Ctx<RT> &c, 
             if (SW) st.A2[r] = ldw16x2(c.wp2 + r * 16 * cols + kb * 128, 64);
         }
     }
-    // lanes of empty token slots load nothing (their result is scaled by 0)
-    if (c.tv) {
-        st.Bv = ld16x2(c.ap + kb * 128, 64);
-        st.as = c.asp[kb];
-    } else {
-        st.Bv = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        st.as = 0.f;
-    }
+    // lanes of empty token slots read a valid row of the group (their column is scaled by 0); every lane
+    // loads, so each step issues the same loads
+    st.Bv = ld16x2(c.ap + kb * 128, 64);
+    st.as = c.asp[kb];
 }
 
 // Segment (steps [s, e) of one unit's chunk) -> context.  Units are (u, tile, g) with g fastest; in plan mode
@@ -169,9 +165,13 @@ __device__ __forceinline__ void make_ctx(const GemvArgs &a, long s, long e, int 
     const long sbase = ((long)c.m * a.nrb + (c.r0 >> 7)) * a.nkb;
     c.wsp = a.wsc + sbase;
     c.wsp2 = SW ? a.wsc2 + sbase : nullptr;
-    const bool in = c.valid && lane < c.kb1 - c.kb0;
-    c.wsv = in ? c.wsp[c.kb0 + lane] : 0.f;
-    c.wsv2 = (SW && in) ? c.wsp2[c.kb0 + lane] : 0.f;
+    // every lane loads (indices clamped to the segment), so no load here depends on the lane
+    const int last = c.kb1 - c.kb0 - 1;
+    const int i0 = c.kb0 + min(lane, last), i1 = c.kb0 + min(lane + 64, last);
+    c.wsv = c.wsp[i0];
+    c.wsvB = c.wsp[i1];
+    c.wsv2 = SW ? c.wsp2[i0] : 0.f;
+    c.wsvB2 = SW ? c.wsp2[i1] : 0.f;
 }
 
 __device__ __forceinline__ float lane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
@@ -240,34 +240,39 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     };
     const bool parts = a.flat || a.ksplit > 1;
     Ctx<RT> c, n;
-    long e = seg_end(s0);
+    long e = seg_end(s0), e2 = e;
     make_ctx<NS, RT, SW, TL>(a, s0, e, groups, tiles, n_act, goff, nullptr, c);
-    Stage<SW, RT> cur, nxt;
-    if (c.valid) load_stage<SW, RT, TL>(cur, c, a.cols, c.kb0);
-    for (long s = s0; s < s1;) {
-        const bool more = e < s1;
-        const long e2 = more ? seg_end(e) : e;
-        if (more) make_ctx<NS, RT, SW, TL>(a, e, e2, groups, tiles, n_act, goff, &c, n);
-        if (c.valid) {
-            v4f tot[RT], tot2[RT];
+    v4f tot[RT], tot2[RT];
 #pragma unroll
-            for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
-            const float tmask = c.tv ? 1.f : 0.f;
-            for (int kb = c.kb0; kb < c.kb1; kb++) {
-                if (kb + 1 < c.kb1) load_stage<SW, RT, TL>(nxt, c, a.cols, kb + 1);
-                else if (more && n.valid) load_stage<SW, RT, TL>(nxt, n, a.cols, n.kb0);
-                const int kr = kb - c.kb0;
-                const float ws = (kr < 64 ? lane_f(c.wsv, kr) : c.wsp[kb]) * tmask;
-                const float ws2 = SW ? (kr < 64 ? lane_f(c.wsv2, kr) : c.wsp2[kb]) * tmask : 0.f;
-                const float f = ws * cur.as, f2 = ws2 * cur.as;
+    for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
+    Stage<SW, RT> X, Y;
+    int kb = c.kb0;  // K-block of step s, in segment c
+    long s = s0;
+    load_stage<SW, RT, TL>(X, c, a.cols, kb);
+    // Step s: first the loads of step s + 1 into the other stage (from the next segment's context when s + 1
+    // starts one; the last step re-reads its own tile, so every step issues the same loads), then the
+    // arithmetic of step s, which waits only for the older stage.  The stages alternate by unrolling two
+    // steps, never by copying registers that loads are still filling.
+    auto step = [&](Stage<SW, RT> &P, Stage<SW, RT> &Q) __attribute__((always_inline)) -> bool {
+        if (s + 1 == e && e < s1) {
+            e2 = seg_end(e);
+            make_ctx<NS, RT, SW, TL>(a, e, e2, groups, tiles, n_act, goff, &c, n);
+            load_stage<SW, RT, TL>(Q, n, a.cols, n.kb0);
+        } else {
+            load_stage<SW, RT, TL>(Q, c, a.cols, s + 1 < s1 ? kb + 1 : kb);
+        }
+        const int kr = kb - c.kb0;
+        const float tmask = c.tv ? 1.f : 0.f;
+        const float ws = lane_f(kr < 64 ? c.wsv : c.wsvB, kr & 63) * tmask;
+        const float ws2 = SW ? lane_f(kr < 64 ? c.wsv2 : c.wsvB2, kr & 63) * tmask : 0.f;
+        const float f = ws * P.as, f2 = ws2 * P.as;
 #pragma unroll
-                for (int r = 0; r < RT; r++) {
-                    tot[r] += mfma_fp8(cur.A[r], cur.Bv) * f;
-                    if (SW) tot2[r] += mfma_fp8(cur.A2[r], cur.Bv) * f2;
-                }
-                cur = nxt;
-            }
-            // add the parts of each token (columns ln, ln + TPG, ...): every lane of the part ends with the sum
+        for (int r = 0; r < RT; r++) {
+            tot[r] += mfma_fp8(P.A[r], P.Bv) * f;
+            if (SW) tot2[r] += mfma_fp8(P.A2[r], P.Bv) * f2;
+        }
+        if (s + 1 == e) {
+            // end of the segment: add the parts of each token (columns ln, ln + TPG, ...), then store
 #pragma unroll
             for (int r = 0; r < RT; r++) {
                 tot[r] = sum_parts<NS>(tot[r]);
@@ -298,12 +303,19 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
                     }
                 }
             }
-        } else if (more && n.valid) {
-            load_stage<SW, RT, TL>(cur, n, a.cols, n.kb0);
+#pragma unroll
+            for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
+            if (e < s1) {
+                c = n;
+                e = e2;
+            }
+            kb = c.kb0;
+        } else {
+            kb++;
         }
-        s = e;
-        e = e2;
-        if (more) c = n;
+        return ++s < s1;
+    };
+    while (step(X, Y) && step(Y, X)) {
     }
 }
 
@@ -564,12 +576,14 @@ void gemv_flat(GemvArgs &a, int ns, int epi, long units_est, int max_ksplit)
     const void *k = gemv_kernel(ns, epi, a.tiled != 0);
     const long waves = k ? 4L * resident_blocks(k, 256) : 1024;
     const long spw = units_est * a.nkb / waves;  // steps per wave
+    // fewest chunks that fit a wave's share, preferring equal chunks; never more than GEMV_MAXCHUNK blocks each
     int ks = 1;
     while (ks < max_ksplit && !(a.nkb % ks == 0 && a.nkb / ks <= spw)) ks++;
-    while (a.nkb % ks) ks--;
+    while (ks > 1 && a.nkb % ks) ks--;
+    while (ks < max_ksplit && (a.nkb + ks - 1) / ks > GEMV_MAXCHUNK) ks++;
     a.flat = 1;
-    a.ksplit = ks;
-    a.kchunk = a.nkb / ks;
+    a.kchunk = (a.nkb + ks - 1) / ks;
+    a.ksplit = (a.nkb + a.kchunk - 1) / a.kchunk;
 }
 
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
@@ -593,6 +607,8 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
         const void *k = gemv_kernel(ns, epi, a.tiled != 0);
         if (!k) return fail(DL_ERR_UNSUPPORTED, "gemv parts=%d", ns);
         if ((a.flat || a.ksplit > 1) && !a.part) return fail(DL_ERR_UNSUPPORTED, "gemv split without partials");
+        if (a.kchunk > GEMV_MAXCHUNK)
+            return fail(DL_ERR_UNSUPPORTED, "gemv K chunk of %d blocks (<= %d)", a.kchunk, GEMV_MAXCHUNK);
         GemvArgs arg = a;
         void *args[] = {(void *)&arg};
         if (hipLaunchKernel(k, dim3(resident_blocks(k, 256)), dim3(256), args, 0, s) != hipSuccess)
