@@ -7,8 +7,9 @@ moves numpy arrays in and out.  Every function follows the passage cited at the
 matching C function.
 
 Parity pins live in tests/test_oracle_pins.py.  Pinned: FP8/bf16 decode and
-rounding, indexer, top-k, attention, projection, router, FFN (closed forms,
-brute force, invariants, library special cases).  None is "parity unpinned".
+rounding, indexer, top-k, attention, projection, router, FFN, the current-token
+append (closed forms, brute force, invariants, library special cases).  None is
+"parity unpinned".
 """
 from __future__ import annotations
 
@@ -65,6 +66,9 @@ def lib():
         L.o_router.argtypes = [P, P, P, i32, i32, i32, P, P, P]
         L.o_ffn.argtypes = [P, P, P, i32, C.POINTER(_Mat), C.POINTER(_Mat), C.POINTER(_Mat), i32, i32, i32, i32, P]
         L.o_round_out.argtypes = [P, C.c_long, i32, P]
+        L.o_fp8_round.restype = C.c_uint8
+        L.o_fp8_round.argtypes = [C.c_double]
+        L.o_kv_append_row.argtypes = [P, i32, i32, P, i32, i32, C.c_float, P, P, P]
         L.o_init()
         _lib = L
     return _lib
@@ -92,6 +96,13 @@ def fp8_decode(codes) -> np.ndarray:
     return np.array([L.o_fp8_e4m3fn(int(v)) for v in c]).reshape(np.shape(codes))
 
 
+def fp8_round(x) -> np.ndarray:
+    """Real values -> e4m3fn codes (uint8): nearest, ties to even, saturating at 448."""
+    L = lib()
+    v = np.asarray(x, dtype=np.float64)
+    return np.array([L.o_fp8_round(float(t)) for t in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
 def bf16_round(x) -> np.ndarray:
     """fp64 values -> bf16 bit patterns (uint16), round to nearest even."""
     L = lib()
@@ -107,6 +118,22 @@ def bf16_to_f64(b) -> np.ndarray:
 
 
 # ------------------------------------------------------------------- stages
+def kv_append_row(latent: np.ndarray, key: np.ndarray, key_scale: float):
+    """One row of the current-token append: (latent codes uint8 [Dc], block scales fp32 [ceil(Dc/128)],
+    indexer key int8 [DI]) for a latent and key given as fp32 or bf16 bit patterns."""
+    L = lib()
+    lat, lat_dt = _act(np.ravel(latent))
+    k, k_dt = _act(np.ravel(key))
+    Dc, DI = lat.size, k.size
+    codes = np.empty(Dc, dtype=np.uint8)
+    scales = np.empty((Dc + 127) // 128, dtype=np.float32)
+    kout = np.empty(DI, dtype=np.int8)
+    if L.o_kv_append_row(_p(lat), lat_dt, Dc, _p(k), k_dt, DI, float(key_scale), _p(codes), _p(scales), _p(kout)):
+        raise ValueError("kv_append_row: bad arguments")
+    return codes, scales, kout
+
+
+
 def indexer_scores(q_idx: np.ndarray, k_pool: np.ndarray, page_table_row: np.ndarray, L: int) -> np.ndarray:
     """q_idx int8 [HI, DI]; k_pool int8 [P, page, DI]; -> int32 [L]."""
     q = _c(q_idx, np.int8)

@@ -24,6 +24,9 @@
  *            attention gathers only the selected entries instead of masking.
  *   [Kiln-H] same page, "The hyper-connection arithmetic was what spilled":
  *            exact round-to-nearest-even bf16.
+ *   [Kiln-V] same page, "What could only a device show?": padded decode rows
+ *            that wrote one shared cache slot raced; padding must not write a
+ *            slot that another row reads.
  * Where the pages leave a step open, the reading used is stated at the
  * function.
  *
@@ -452,6 +455,86 @@ void o_round_out(const double *y, long n, int32_t out_dt, void *out)
         else
             ((float *)out)[i] = (float)y[i];
     }
+}
+
+/* ------------------------------------------------------- current-token append */
+
+/* Round a real number to the nearest e4m3fn value, ties to the even code, and
+ * return the code.  Straight from the format: 4 significant bits, so the
+ * spacing in the binade [2^e, 2^(e+1)) is 2^(e-3), fixed at 2^-9 below 2^-6
+ * (subnormals).  Magnitudes of 448 and above give 448 (saturation: the format
+ * has no infinity and the pages give no overflow rule).  The code is found by
+ * searching the decoding table, so encoding and decoding cannot disagree.
+ * The sign is kept, also for a value that rounds to zero. */
+uint8_t o_fp8_round(double x)
+{
+    fp8_table_init();
+    const int neg = signbit(x) ? 1 : 0;
+    double a = fabs(x), r;
+    if (isnan(x))
+        return 0x7F;
+    if (a >= 448.0) {
+        r = 448.0;
+    } else if (a == 0.0) {
+        r = 0.0;
+    } else {
+        int e = ilogb(a);
+        if (e < -6)
+            e = -6;
+        const double ulp = ldexp(1.0, e - 3);
+        r = nearbyint(a / ulp) * ulp; /* default mode: half to even */
+    }
+    for (int c = 0; c < 127; c++)
+        if (g_fp8[c] == r)
+            return (uint8_t)((neg << 7) | c);
+    return 0x7F; /* unreachable: every r above is a finite code */
+}
+
+/* Reading of the append step (the step before S1; the pages store every cached
+ * entry this way but do not print the quantiser).  The latent cache holds e4m3fn
+ * codes with one fp32 scale per (token, 128-feature block) [Kiln-M]:
+ *   scale = amax / 448 in fp32 (amax = largest |x| of the block, exact in fp32),
+ *   code  = o_fp8_round(x / scale), the quotient taken in fp32;
+ * a block whose scale is 0 (all zero) stores zero codes.  The indexer key is
+ * int8 [Kiln-T]: k / key_scale in fp32, rounded to the nearest integer (ties to
+ * even) and clamped to [-127, 127]; one key_scale serves every position so that
+ * the exact integer scores of S1 stay comparable.  Inputs fp32 or bf16.
+ * Outputs of one row: codes [Dc], scales [ceil(Dc/128)], key [DI]. */
+int o_kv_append_row(const void *latent, int32_t lat_dt, int32_t Dc, const void *key, int32_t key_dt, int32_t DI,
+                    float key_scale, uint8_t *codes, float *scales, int8_t *key_out)
+{
+    if (Dc < 1 || DI < 0 || (lat_dt != O_F32 && lat_dt != O_BF16) || (key_dt != O_F32 && key_dt != O_BF16))
+        return -1;
+    const int nb = (Dc + 127) / 128;
+    for (int j = 0; j < nb; j++) {
+        const int d0 = j * 128, d1 = d0 + 128 < Dc ? d0 + 128 : Dc;
+        float amax = 0.0f;
+        for (int d = d0; d < d1; d++) {
+            const float v = (float)fabs(act_at(latent, lat_dt, (size_t)d));
+            if (v > amax)
+                amax = v;
+        }
+        const float sc = amax / 448.0f;
+        scales[j] = sc;
+        for (int d = d0; d < d1; d++) {
+            if (sc == 0.0f) {
+                codes[d] = 0;
+            } else {
+                const float q = (float)act_at(latent, lat_dt, (size_t)d) / sc;
+                codes[d] = o_fp8_round((double)q);
+            }
+        }
+    }
+    for (int d = 0; d < DI; d++) {
+        const float t = (float)act_at(key, key_dt, (size_t)d) / key_scale;
+        double n = nearbyint((double)t);
+        if (n > 127.0)
+            n = 127.0;
+        if (n < -127.0)
+            n = -127.0;
+        key_out[d] = (int8_t)n;
+    }
+    return 0;
 }
 
 void o_init(void) { fp8_table_init(); }

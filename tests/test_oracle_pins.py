@@ -350,3 +350,76 @@ def test_layer_rows_tiny_fp8():
     r1 = orc.row(1)                                   # padding row: nothing selected, o = 0, h = x
     assert np.all(r1["sel"] == -1) and np.all(r1["o"] == 0)
     assert np.array_equal(r1["h"], oracle.bf16_to_f64(t["x"][1].view(torch.int16).numpy().view(np.uint16)))
+
+
+# ------------------------------------------------------------- current-token append
+def _torch_fp8_codes(x32: np.ndarray) -> np.ndarray:
+    """torch's own float32 -> e4m3fn conversion (nearest, ties to even), as codes."""
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_round_hand_values():
+    # ties go to the even code; the format saturates at 448; the sign of a zero result is kept
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -11: 0x01, 2.0 ** -9: 0x01,
+             448.0: 0x7E, 1000.0: 0x7E, -1000.0: 0xFE, -1e-4: 0x80, 0.0: 0x00, 240.0: 0x77, 248.0: 0x78}
+    for x, code in cases.items():
+        assert int(oracle.fp8_round([x])[0]) == code, x
+
+
+def test_fp8_round_vs_library():
+    # every code, every midpoint between neighbouring codes (exact in fp32), and random values from the
+    # subnormal range up to just below 448, both signs: the same codes as torch's conversion
+    dec = oracle.fp8_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (dec[:-1] + dec[1:]) / 2
+    rng = np.random.default_rng(5)
+    rand = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(447.0), 20000))
+    x = np.concatenate([dec, mids, rand]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    assert np.array_equal(oracle.fp8_round(x.astype(np.float64)), _torch_fp8_codes(x))
+    # round trip of every finite code
+    assert np.array_equal(oracle.fp8_round(dec), np.arange(0x7F, dtype=np.uint8))
+
+
+@pytest.mark.parametrize("Dc,bf16", [(576, False), (576, True), (64, False), (200, True)])
+def test_kv_append_row(Dc, bf16):
+    rng = np.random.default_rng(Dc + bf16)
+    lat = rng.standard_normal(Dc).astype(np.float32) * np.float32(3.0)
+    lat[: min(128, Dc)] *= np.float32(1e-3)           # a block of small values
+    if Dc > 256:
+        lat[128:256] = 0.0                             # an all-zero block
+    key = np.concatenate([rng.uniform(-200, 200, 100), [0.5, 1.5, 2.5, -0.5, -2.5, 127.5, -127.5, 1e6]])
+    key = key.astype(np.float32)
+    if bf16:
+        lat_in = torch.from_numpy(lat).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        key_in = torch.from_numpy(key).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        lat = torch.from_numpy(lat).to(torch.bfloat16).float().numpy()
+        key = torch.from_numpy(key).to(torch.bfloat16).float().numpy()
+    else:
+        lat_in, key_in = lat, key
+    ks = np.float32(0.75)
+    codes, scales, k8 = oracle.kv_append_row(lat_in, key_in, ks)
+    nb = (Dc + 127) // 128
+    assert scales.shape == (nb,) and codes.shape == (Dc,)
+    for j in range(nb):
+        blk = lat[j * 128:(j + 1) * 128]
+        amax = np.float32(np.max(np.abs(blk)))
+        if amax == 0:
+            assert scales[j] == 0 and not codes[j * 128:(j + 1) * 128].any()
+            continue
+        q = blk / scales[j]                            # fp32 quotient
+        # the codes are torch's rounding of the quotient, the largest element maps to +-448, and the decoded
+        # value is within half a code spacing of the quotient
+        assert np.array_equal(codes[j * 128:(j + 1) * 128], _torch_fp8_codes(q))
+        big = int(np.argmax(np.abs(blk)))
+        assert codes[j * 128 + big] in (0x7E, 0xFE)
+        dq = oracle.fp8_decode(codes[j * 128:(j + 1) * 128])
+        spacing = np.where(np.abs(q) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(q), 1e-30))) - 3))
+        assert np.all(np.abs(dq - q) <= spacing / 2 + 1e-12)
+        assert abs(scales[j] * 448.0 - amax) <= amax * 2.0 ** -23
+    # keys: numpy's round-half-even of the fp32 quotient, clamped to +-127
+    want = np.clip(np.rint(key / ks), -127, 127).astype(np.int8)
+    assert np.array_equal(k8, want)
+    assert list(k8[-8:]) == [1, 2, 3, -1, -3, 127, -127, 127] or bf16
+    # exact halves with a unit scale: ties to even
+    _, _, kt = oracle.kv_append_row(np.zeros(64, np.float32), np.array([0.5, 1.5, 2.5, -0.5, -2.5, 126.5], np.float32), 1.0)
+    assert list(kt) == [0, 2, 2, 0, -2, 126]
