@@ -154,6 +154,28 @@ def main():
     ph, nst = dl.profile_read()
     dl.profile_enable(False)
     ph = {k: v / nst for k, v in ph.items()}
+    # the current-token append (the step before S1; not part of the timed step): its own launches, bf16 inputs
+    app_rec = None
+    if spec.Dc >= 256:
+        B_app = max(8, spec.B)
+        app = synth.make_append(seed=args.seed, B=B_app, Dc=spec.Dc, DI=spec.DI, page_size=spec.page_size,
+                                bf16=True, device=dev)
+        apg = dl.pages(app["seq_lens"], app["page_table"], spec.page_size)
+        call = lambda: dl.kv_append(apg, app["latent"], app["key"], float(app["key_scale"]), app["kv_pool"],
+                                    app["kv_scale"], app["k_pool"])
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        app_us = e0.elapsed_time(e1) / args.steps * 1000.0
+        nb = (spec.Dc + 127) // 128
+        app_bytes = B_app * (2 * spec.Dc + 2 * spec.DI + spec.Dc + 4 * nb + spec.DI)
+        app_rec = {"us_per_call": round(app_us, 2), "rows": B_app, "bytes_per_call": app_bytes,
+                   "bound": "latency", "achieved_gbs": round(app_bytes / (app_us * 1e-6) / 1e9, 2)}
     # algorithmic bytes of the steps actually run (touched experts per instance)
     per_inst = []
     for s in steps_obj:
@@ -183,6 +205,8 @@ def main():
                      "bytes_per_launch": int(avg_bytes["expert_gate_up"]),
                      "ms_per_launch": round(ph["expert_gate_up"], 4)},
     }
+    if app_rec:
+        rec["kv_append"] = app_rec
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(spec, insts[0], list(range(args.cpu_rows)))
     print(json.dumps(rec), flush=True)

@@ -106,6 +106,33 @@ int dl_pack_weights(const dl_mat *src, void *dst, void *stream);
 /* Message of the last failed call on this host thread (library-owned, valid until the next call). */
 const char *dl_last_error(void);
 
+/* ---------------------------------------------------------------- current-token append
+ * The step before S1: write each row's new token into its cache slot, in the layout S1 and S3 read
+ * (Kiln, "How was Kiln measured ...": a compressed latent cache in FP8; "What moved the number ...":
+ * a separate key cache for the scoring kernel).  The pages do not print the quantiser; this is the
+ * plainest one that fits the stored layout.  The new token is position p = seq_lens[b] - 1 (the
+ * lengths already count it), page page_table[b, p / page_size], slot p % page_size:
+ *   kv_scale[page, slot, j] = s_j = amax_j / 448 in fp32, amax_j = max |latent[b, d]| over the
+ *                             128-feature block j (s_j = 0 for an all-zero block);
+ *   kv_pool[page, slot, d]  = e4m3fn code of latent[b, d] / s_j (fp32 quotient, nearest, ties to even,
+ *                             saturating at 448; 0 when s_j == 0);
+ *   k_pool[page, slot, i]   = round-half-even(key[b, i] / key_scale) clamped to [-127, 127], one
+ *                             key_scale for every position so that the integer scores stay comparable.
+ * Padding rows (seq_lens[b] == 0) write nothing ("What could only a device show?": padded rows that
+ * wrote one shared slot raced).  When several rows address the same physical slot, only the lowest
+ * row writes it, so the result never depends on the order the rows run in.
+ *   latent   [B, d_c] in lat_dt (DL_F32 or DL_BF16)
+ *   key      [B, idx_dim] in key_dt (DL_F32 or DL_BF16); unused (may be NULL) when idx_dim == 0
+ *   kv_pool  FP8 codes [n_pages, page_size, d_c], kv_scale fp32 [n_pages, page_size, ceil(d_c/128)],
+ *   k_pool   int8 [n_pages, page_size, idx_dim]: in/out — only the addressed slots are written, every
+ *            other byte of the pools is left unchanged (the exception to "outputs are overwritten").
+ * page_table entries of the written pages must be valid page ids of the pools (not checked).
+ * Limits: 1 <= d_c <= 1024; 0 <= idx_dim <= 1024; key_scale finite and > 0 when idx_dim > 0.
+ * No workspace. */
+int dl_kv_append(const dl_pages *pages, const void *latent, int32_t lat_dt, int32_t d_c, const void *key,
+                 int32_t key_dt, int32_t idx_dim, float key_scale, uint8_t *kv_pool, float *kv_scale, int8_t *k_pool,
+                 void *stream);
+
 /* ---------------------------------------------------------------- S1 + S2
  * Indexer scoring and exact top-k selection (Kiln, "What moved the number ...": a scoring kernel
  * and a top-k kernel over a separate key cache; trnrt summary: the top 2,048 positions are kept).

@@ -20,7 +20,7 @@ DL_F32, DL_BF16, DL_FP8_E4M3, DL_I8, DL_I32 = 0, 1, 2, 3, 4
 STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE", -4: "DL_ERR_UNSUPPORTED",
           -5: "DL_ERR_WORKSPACE", -6: "DL_ERR_HIP"}
 
-EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_indexer_topk_workspace", "dl_indexer_topk",
+EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append", "dl_indexer_topk_workspace", "dl_indexer_topk",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
            "dl_profile_read"]
@@ -79,6 +79,7 @@ def load(require_gpu: bool = True):
         L.dl_abi_version.restype = C.c_int
         L.dl_pack_weights.argtypes = [C.POINTER(Mat), P, P]
         L.dl_last_error.restype = C.c_char_p
+        L.dl_kv_append.argtypes = [C.POINTER(Pages), P, i32, i32, P, i32, i32, C.c_float, P, P, P, P]
         L.dl_indexer_topk_workspace.restype = sz
         L.dl_indexer_topk_workspace.argtypes = [C.POINTER(Pages)]
         L.dl_indexer_topk.argtypes = [C.POINTER(Pages), P, P, i32, i32, i32, P, P, P, sz, P]
@@ -155,6 +156,15 @@ def pack_weights(w: torch.Tensor, scale: torch.Tensor, stream=None) -> torch.Ten
 
 
 # ---------------------------------------------------------------- stage calls
+def kv_append(pg: Pages, latent, key, key_scale: float, kv_pool, kv_scale, k_pool, stream=None):
+    """Quantise each row's new token into its cache slot (position seq_lens[b] - 1); pools are updated in place."""
+    L = load()
+    DI = key.shape[-1] if key is not None else 0
+    _check(L.dl_kv_append(C.byref(pg), _ptr(latent), _dt(latent), latent.shape[-1], _ptr(key),
+                          _dt(key) if key is not None else DL_F32, DI, float(key_scale), _ptr(kv_pool),
+                          _ptr(kv_scale), _ptr(k_pool), _stream(stream)))
+
+
 def indexer_topk(pg: Pages, q_idx, k_pool, top_k: int, sel, sel_score=None, ws=None, stream=None):
     L = load()
     need = L.dl_indexer_topk_workspace(C.byref(pg))

@@ -550,6 +550,25 @@ size_t dl_indexer_topk_workspace(const dl_pages *pages)
     return w.used();
 }
 
+int dl_kv_append(const dl_pages *pages, const void *latent, int32_t lat_dt, int32_t d_c, const void *key,
+                 int32_t key_dt, int32_t idx_dim, float key_scale, uint8_t *kv_pool, float *kv_scale, int8_t *k_pool,
+                 void *stream)
+{
+    g_err[0] = 0;
+    DL_TRY(check_pages(pages));
+    if (!latent || !kv_pool || !kv_scale) return fail(DL_ERR_NULL, "latent/kv_pool/kv_scale NULL");
+    if (idx_dim > 0 && (!key || !k_pool)) return fail(DL_ERR_NULL, "key/k_pool NULL");
+    if (d_c < 1 || d_c > 1024 || idx_dim < 0 || idx_dim > 1024)
+        return fail(DL_ERR_SHAPE, "append d_c=%d idx_dim=%d", d_c, idx_dim);
+    if (lat_dt != DL_F32 && lat_dt != DL_BF16) return fail(DL_ERR_DTYPE, "latent dtype %d", lat_dt);
+    if (idx_dim > 0 && key_dt != DL_F32 && key_dt != DL_BF16) return fail(DL_ERR_DTYPE, "key dtype %d", key_dt);
+    if (idx_dim > 0 && !(key_scale > 0.f && key_scale <= 3.4028235e38f))
+        return fail(DL_ERR_SHAPE, "key_scale %g (finite, > 0)", (double)key_scale);
+    (void)hipGetLastError();
+    return launch_kv_append(*pages, latent, lat_dt, d_c, key, key_dt, idx_dim, key_scale, kv_pool, kv_scale, k_pool,
+                            (hipStream_t)stream);
+}
+
 int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_pool, int32_t n_heads, int32_t dim,
                     int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws, size_t ws_bytes, void *stream)
 {

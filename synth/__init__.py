@@ -259,3 +259,49 @@ def to_numpy(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
     return t.numpy()
+
+
+def make_append(seed: int = 0, B: int = 9, Dc: int = 576, DI: int = 128, page_size: int = 64,
+                max_pages: int = 4, bf16: bool = False, device="cpu") -> Dict[str, torch.Tensor]:
+    """Inputs of the current-token append, on ``device``: B rows' new-token latents [B, Dc] and indexer keys
+    [B, DI] (fp32, or bf16 when ``bf16``), a key scale, the cache geometry, and pools pre-filled with random
+    bytes so that bytes the append must leave alone can be checked.
+
+    Row 3 is padding (length 0).  Rows 5 and 7 address the same physical slot.  Row 4's first two latent
+    blocks contain the value 448 (so that their block scale is exactly 1) and otherwise midpoints between
+    neighbouring e4m3 values (normal and subnormal), i.e. exact rounding ties; row 2 has an all-zero block.
+    The keys include exact halves of the key scale (ties) and values far outside the int8 range."""
+    assert B >= 8 and Dc >= 256
+    n_pages = B * max_pages + 3
+    g = _gen("cpu", seed, 0, "append-geom")
+    perm = torch.randperm(n_pages, generator=g)[: B * max_pages].to(torch.int32)
+    page_table = perm.reshape(B, max_pages).clone()
+    cap = max_pages * page_size
+    lens = torch.randint(1, cap + 1, (B,), generator=g, dtype=torch.int32)
+    lens[0], lens[1], lens[2], lens[3] = 1, page_size, page_size + 1, 0
+    lens[5] = lens[7] = cap - page_size + 7
+    page_table[7, max_pages - 1] = page_table[5, max_pages - 1]      # same physical slot as row 5
+    lat = _randn((B, Dc), "cpu", seed, 0, "append-latent", std=3.0)
+    lat[2, 128:256] = 0.0
+    lat[6, :128] *= 1e-3
+    grid = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    mids = (grid[:-1] + grid[1:]) / 2                                   # 126 exact ties
+    signs = torch.where(torch.arange(126) % 2 == 0, 1.0, -1.0)
+    lat[4, :128] = torch.cat([torch.tensor([448.0]), mids * signs, torch.zeros(1)])
+    lat[4, 128:256] = torch.cat([torch.tensor([-448.0]), (mids[:16] * signs[:16]).repeat(8)[:127]])
+    gk = _gen("cpu", seed, 0, "append-key")
+    key = (torch.rand((B, DI), generator=gk) * 400.0 - 200.0)
+    key_scale = 0.5
+    n_tie = min(DI, 16)
+    key[:, :n_tie] = (torch.arange(n_tie, dtype=torch.float32) - 8.0 + 0.5) * key_scale
+    key[:, n_tie:n_tie + 2] = torch.tensor([1000.0, -1000.0])[: max(0, min(2, DI - n_tie))]
+    dt = torch.bfloat16 if bf16 else torch.float32
+    nb = (Dc + 127) // 128
+    gp = _gen("cpu", seed, 0, "append-pools")
+    return {
+        "seq_lens": lens.to(device), "page_table": page_table.to(device),
+        "latent": lat.to(dt).to(device), "key": key.to(dt).to(device), "key_scale": torch.tensor(key_scale),
+        "kv_pool": torch.randint(0, 256, (n_pages, page_size, Dc), generator=gp, dtype=torch.uint8).to(device),
+        "kv_scale": torch.rand((n_pages, page_size, nb), generator=gp).to(device),
+        "k_pool": torch.randint(-128, 128, (n_pages, page_size, DI), generator=gp, dtype=torch.int8).to(device),
+    }

@@ -87,3 +87,38 @@ def test_attention_rejects_bad_arguments(lib):
     wo = dl.Mat(1, 1, dl.DL_FP8_E4M3, 1, 6144, 64 * 512)
     assert lib.dl_sparse_attn_decode(C.byref(P), 1, dl.DL_BF16, 1, 1, dl.DL_FP8_E4M3, 64, 576, 512, 0.04, 1, 2048,
                                      None, C.byref(wo), None, 0, 1, ws, 1 << 30, None) == -1
+
+
+def test_ffn_rejects_sizes_beyond_the_chunk_limits(lib):
+    ws = C.c_void_p(0x10000)
+    # inter above 16384 (the down projection streams its K in one chunk of at most 128 blocks)
+    wg = dl.Mat(1, 1, dl.DL_FP8_E4M3, 9, 16512, 256)
+    wd = dl.Mat(1, 1, dl.DL_FP8_E4M3, 9, 256, 16512)
+    assert lib.dl_moe_ffn(1, 8, 256, 16512, 1, 1, 2, C.byref(wg), C.byref(wg), C.byref(wd), 8, 1, None, 1,
+                          dl.DL_BF16, ws, 1 << 40, None) == -4
+    # hidden size above 65536
+    wg = dl.Mat(1, 1, dl.DL_FP8_E4M3, 9, 256, 65664)
+    wd = dl.Mat(1, 1, dl.DL_FP8_E4M3, 9, 65664, 256)
+    assert lib.dl_moe_ffn(1, 8, 65664, 256, 1, 1, 2, C.byref(wg), C.byref(wg), C.byref(wd), 8, 1, None, 1,
+                          dl.DL_BF16, ws, 1 << 40, None) == -4
+    assert b"65536" in lib.dl_last_error()
+
+
+def test_kv_append_rejects_bad_arguments(lib):
+    P = dl.Pages(2, 64, 4, 0x1000, 0x2000)
+    F32, BF16 = dl.DL_F32, dl.DL_BF16
+    # NULL pages, NULL latent, NULL key with a key width
+    assert lib.dl_kv_append(None, 1, F32, 576, 1, F32, 128, 1.0, 1, 1, 1, None) == -1
+    assert lib.dl_kv_append(C.byref(P), None, F32, 576, 1, F32, 128, 1.0, 1, 1, 1, None) == -1
+    assert lib.dl_kv_append(C.byref(P), 1, F32, 576, None, F32, 128, 1.0, 1, 1, 1, None) == -1
+    # widths out of range
+    assert lib.dl_kv_append(C.byref(P), 1, F32, 0, 1, F32, 128, 1.0, 1, 1, 1, None) == -2
+    assert lib.dl_kv_append(C.byref(P), 1, F32, 2048, 1, F32, 128, 1.0, 1, 1, 1, None) == -2
+    assert lib.dl_kv_append(C.byref(P), 1, F32, 576, 1, F32, 1025, 1.0, 1, 1, 1, None) == -2
+    # dtypes other than fp32 / bf16
+    assert lib.dl_kv_append(C.byref(P), 1, dl.DL_I8, 576, 1, F32, 128, 1.0, 1, 1, 1, None) == -3
+    assert lib.dl_kv_append(C.byref(P), 1, BF16, 576, 1, dl.DL_FP8_E4M3, 128, 1.0, 1, 1, 1, None) == -3
+    # key scale not finite and positive
+    for ks in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.dl_kv_append(C.byref(P), 1, F32, 576, 1, F32, 128, ks, 1, 1, 1, None) == -2, ks
+    assert b"key_scale" in lib.dl_last_error()

@@ -256,3 +256,34 @@ def test_rows_and_tiles_layouts_agree():
     y_tiles = dl.LayerStep(spec, t, debug=True, tiles=True)()
     torch.cuda.synchronize()
     assert torch.equal(y_rows, y_tiles)
+
+
+# ------------------------------------------------------------- current-token append
+@pytest.mark.parametrize("bf16", [False, True])
+def test_kv_append_bit_exact(bf16):
+    t = synth.make_append(seed=3, bf16=bf16, device=DEV)
+    h = {k: synth.to_numpy(v) for k, v in t.items()}
+    lens, pt, ps = h["seq_lens"], h["page_table"], 64
+    kv, kvs, kp = h["kv_pool"].copy(), h["kv_scale"].copy(), h["k_pool"].copy()
+    Dc, DI = kv.shape[2], kp.shape[2]
+    written = set()
+    for b in range(lens.shape[0]):                    # expected: the oracle's row, at the lowest row's slot
+        if lens[b] <= 0:
+            continue
+        p = int(lens[b]) - 1
+        page, slot = int(pt[b, p // ps]), p % ps
+        if (page, slot) in written:
+            continue
+        written.add((page, slot))
+        codes, scales, k8 = oracle.kv_append_row(h["latent"][b], h["key"][b], float(h["key_scale"]))
+        kv[page, slot], kvs[page, slot], kp[page, slot] = codes, scales, k8
+    assert len(written) == lens.shape[0] - 2          # one padding row, one row sharing a slot
+    say(f"[gpu] kv_append bf16={bf16} B={lens.shape[0]} Dc={Dc} DI={DI}")
+    pg = dl.pages(t["seq_lens"], t["page_table"], ps)
+    dl.kv_append(pg, t["latent"], t["key"], float(h["key_scale"]), t["kv_pool"], t["kv_scale"], t["k_pool"])
+    torch.cuda.synchronize()
+    got_kv, got_s, got_k = host(t["kv_pool"]), host(t["kv_scale"]), host(t["k_pool"])
+    bad = np.argwhere(got_kv != kv)
+    assert bad.size == 0, f"{len(bad)} latent bytes differ, first {bad[:3].tolist()}: {got_kv[tuple(bad[0])]} vs {kv[tuple(bad[0])]}"
+    assert np.array_equal(got_s.view(np.uint32), kvs.view(np.uint32))
+    assert np.array_equal(got_k, kp)
