@@ -84,6 +84,33 @@ def copy_calibration(mib: int, reps: int = 3):
     print(f"[bench] copy calibration: {reps} x {mib << 20} bytes", file=sys.stderr, flush=True)
 
 
+def read_ceiling(reps: int, mib: int = 1536) -> dict:
+    """HBM read rate of a plain streaming read (dl_probe_read: the expert stream's access pattern without the
+    arithmetic) over random bytes, like FP8 weights, and over a constant fill: context for `roofline`, whose
+    peak stays the published 8 TB/s.  Each buffer is far larger than the 256 MB last-level cache."""
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    for kind in ("random", "constant"):
+        buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+        if kind == "random":
+            buf.random_(0, 256, generator=g)
+        else:
+            buf.fill_(0x3C)
+        n = dl.probe_read(buf)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            dl.probe_read(buf)
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"{kind}_gbs"] = round(n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del buf
+    out["bytes_per_read"] = n
+    return out
+
+
 def touched(spec, experts: np.ndarray) -> int:
     return len(set(int(e) for e in experts.ravel())) + spec.n_shared
 
@@ -115,6 +142,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1)
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device (counter calibration)")
     args = ap.parse_args()
@@ -207,6 +235,8 @@ def main():
     }
     if app_rec:
         rec["kv_append"] = app_rec
+    if not args.no_read_ceiling:
+        rec["read_ceiling"] = read_ceiling(args.steps)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(spec, insts[0], list(range(args.cpu_rows)))
     print(json.dumps(rec), flush=True)

@@ -267,6 +267,13 @@ int dl_layer_step(const dl_layer_desc *desc, const dl_layer_io *io, void *ws, si
 int dl_profile_enable(int on);
 int dl_profile_read(double *ms_sum, int64_t *steps);
 
+/* Measurement aid, not part of the step: enqueue one streaming read of the first *bytes_read bytes of
+ * the device buffer buf (16-byte non-temporal loads, each wave of a full-device grid reading its own
+ * contiguous range, as the expert GEMV streams its weights); *bytes_read (host) receives the count,
+ * which rounds `bytes` down to whole rounds of the grid.  Timing it with events on `stream` gives the
+ * HBM read rate reachable for the buffer's contents.  DL_ERR_SHAPE if bytes is below one round. */
+int dl_probe_read(const void *buf, size_t bytes, size_t *bytes_read, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE",
 EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append", "dl_indexer_topk_workspace", "dl_indexer_topk",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
-           "dl_profile_read"]
+           "dl_profile_read", "dl_probe_read"]
 N_PHASES = 9
 PHASES = ["indexer_topk", "attention", "projection", "router", "plan_split_h", "expert_gate_up", "split_z",
           "expert_down", "combine"]
@@ -99,6 +99,7 @@ def load(require_gpu: bool = True):
         L.dl_layer_step.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), P, sz, P]
         L.dl_profile_enable.argtypes = [C.c_int]
         L.dl_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+        L.dl_probe_read.argtypes = [P, sz, C.POINTER(sz), P]
         if L.dl_abi_version() != ABI_VERSION:
             raise ImportError(f"libdl ABI {L.dl_abi_version()} != {ABI_VERSION}")
         _lib = L
@@ -214,6 +215,14 @@ def moe_ffn(h, experts, gates, w_gate: Mat, w_up: Mat, w_down: Mat, n_routed, n_
                         C.byref(w_down), n_routed, n_shared, _ptr(residual), _ptr(out), _dt(out), _ptr(ws), ws.numel(),
                         _stream(stream)))
     return out
+
+
+def probe_read(buf: torch.Tensor, stream=None) -> int:
+    """Enqueue one streaming read of buf (measurement aid); returns the number of bytes it reads."""
+    L = load()
+    n = C.c_size_t(0)
+    _check(L.dl_probe_read(_ptr(buf), buf.numel() * buf.element_size(), C.byref(n), _stream(stream)))
+    return n.value
 
 
 def profile_enable(on: bool):

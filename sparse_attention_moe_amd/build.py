@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdl.so")
-SOURCES = ["dl_api.hip", "k_append.hip", "k_indexer.hip", "k_attention.hip", "k_gemv.hip", "k_moe.hip"]
+SOURCES = ["dl_api.hip", "k_append.hip", "k_indexer.hip", "k_attention.hip", "k_gemv.hip", "k_moe.hip", "k_probe.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # packed fp32 VALU ops stay off: every fp32 op is issued unpacked
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -737,6 +737,14 @@ int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_
                    d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s, mk, io->y32, fuse_route, h_split);
 }
 
+int dl_probe_read(const void *buf, size_t bytes, size_t *bytes_read, void *stream)
+{
+    g_err[0] = 0;
+    if (!buf) return fail(DL_ERR_NULL, "probe_read: buffer NULL");
+    (void)hipGetLastError();
+    return launch_probe_read(buf, bytes, bytes_read, (hipStream_t)stream);
+}
+
 int dl_profile_enable(int on)
 {
     g_err[0] = 0;

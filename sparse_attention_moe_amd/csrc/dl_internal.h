@@ -48,6 +48,7 @@ struct TopkWs {
     int *cnt;          // [B, nchunk, 2]
 };
 void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t);
+int launch_probe_read(const void *buf, size_t bytes, size_t *bytes_read, hipStream_t s);
 int launch_kv_append(const dl_pages &pg, const void *latent, int lat_dt, int Dc, const void *key, int key_dt, int DI,
                      float key_scale, uint8_t *kv, float *kv_scale, int8_t *kp, hipStream_t s);
 int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k_pool, int HI, int DI, int top_k,
