@@ -151,6 +151,21 @@ int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_
                     int32_t dim, int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* Multi-row decode (multi-token-prediction verification: TileRT, "Running the Generation Example with
+ * Multi-Token Prediction (MTP)", depth 1 or 3; Kiln, "What did we measure that did not pay?": MTP
+ * drafts verified in one step).  Each sequence b carries R = rows_per_seq query rows, the last R tokens
+ * of the sequence (seq_lens already counts them): row r (0-based) is the token at position
+ * seq_lens[b] - R + r and scores only the positions p <= its own, i.e. its visible length is
+ * seq_lens[b] - (R - 1 - r) (causal among the R rows; a row with no visible position is padding).
+ * The key pages of a sequence are read once for all of its rows.  Rows are numbered i = b * R + r:
+ *   q_idx int8 [B * R, n_heads, dim]; sel [B * R, top_k], sel_score [B * R, top_k] as in dl_indexer_topk.
+ * R = 1 is dl_indexer_topk.  Limits: 1 <= R <= 4, B * R <= 4096, as dl_indexer_topk otherwise.
+ * Workspace: dl_indexer_topk_rows_workspace(pages, rows_per_seq). */
+size_t dl_indexer_topk_rows_workspace(const dl_pages *pages, int32_t rows_per_seq);
+int dl_indexer_topk_rows(const dl_pages *pages, int32_t rows_per_seq, const int8_t *q_idx, const int8_t *k_pool,
+                         int32_t n_heads, int32_t dim, int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws,
+                         size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- S3 - S5
  * Sparse MLA decode attention over the kept positions only (Kiln, "The decode kernels ...":
  * gather the selected entries instead of masking all keys), every head reading the same latent
@@ -254,6 +269,14 @@ typedef struct dl_layer_io {
 
 size_t dl_layer_workspace(const dl_layer_desc *desc, const dl_pages *pages);
 int dl_layer_step(const dl_layer_desc *desc, const dl_layer_io *io, void *ws, size_t ws_bytes, void *stream);
+/* The step over R = rows_per_seq query rows per sequence (multi-row decode, as dl_indexer_topk_rows):
+ * io->pages describes the B sequences; x, q, q_idx, y and the debug outputs hold B * R rows (row
+ * i = b * R + r).  Row r selects among the positions up to its own, and every later stage treats each row
+ * as one token (B * R tokens into the router and the FFN).  R = 1 is dl_layer_step.
+ * Limits: 1 <= R <= 4, B * R <= 4096.  Workspace: dl_layer_workspace_rows(desc, pages, rows_per_seq). */
+size_t dl_layer_workspace_rows(const dl_layer_desc *desc, const dl_pages *pages, int32_t rows_per_seq);
+int dl_layer_step_rows(const dl_layer_desc *desc, const dl_layer_io *io, int32_t rows_per_seq, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------- measurement
  * When enabled, every dl_layer_step records a HIP event on its stream at each phase boundary:

@@ -304,9 +304,16 @@ class LayerOracle:
         return self._exp[e]
 
     def row(self, b: int, stages=("sel", "o", "h", "route", "y")) -> Dict[str, np.ndarray]:
+        """Row b of the step.  With R = spec.R query rows per sequence (multi-row decode: the verification of
+        multi-token-prediction drafts, TileRT "Running the Generation Example with Multi-Token Prediction
+        (MTP)" and Kiln "What did we measure that did not pay?"), row b is the token at position
+        seq_lens[b // R] - R + b % R of sequence b // R and sees the positions up to its own (reading: causal
+        among the R rows, like any decode token); everything after the visible length is per row."""
         sp = self.spec
-        L = int(self.a("seq_lens")[b])
-        pt = self.a("page_table")[b]
+        R = getattr(sp, "R", 1)
+        seq, rr = b // R, b % R
+        L = max(0, int(self.a("seq_lens")[seq]) - (R - 1 - rr))
+        pt = self.a("page_table")[seq]
         r: Dict[str, np.ndarray] = {}
         scores = indexer_scores(self.a("q_idx")[b], self.a("k_pool"), pt, L)
         r["scores"] = scores

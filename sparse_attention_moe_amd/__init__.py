@@ -21,6 +21,7 @@ STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE",
           -5: "DL_ERR_WORKSPACE", -6: "DL_ERR_HIP"}
 
 EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append", "dl_indexer_topk_workspace", "dl_indexer_topk",
+           "dl_indexer_topk_rows_workspace", "dl_indexer_topk_rows", "dl_layer_workspace_rows", "dl_layer_step_rows",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
            "dl_profile_read", "dl_probe_read"]
@@ -80,6 +81,12 @@ def load(require_gpu: bool = True):
         L.dl_pack_weights.argtypes = [C.POINTER(Mat), P, P]
         L.dl_last_error.restype = C.c_char_p
         L.dl_kv_append.argtypes = [C.POINTER(Pages), P, i32, i32, P, i32, i32, C.c_float, P, P, P, P]
+        L.dl_indexer_topk_rows_workspace.restype = sz
+        L.dl_indexer_topk_rows_workspace.argtypes = [C.POINTER(Pages), i32]
+        L.dl_indexer_topk_rows.argtypes = [C.POINTER(Pages), i32, P, P, i32, i32, i32, P, P, P, sz, P]
+        L.dl_layer_workspace_rows.restype = sz
+        L.dl_layer_workspace_rows.argtypes = [C.POINTER(LayerDesc), C.POINTER(Pages), i32]
+        L.dl_layer_step_rows.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), i32, P, sz, P]
         L.dl_indexer_topk_workspace.restype = sz
         L.dl_indexer_topk_workspace.argtypes = [C.POINTER(Pages)]
         L.dl_indexer_topk.argtypes = [C.POINTER(Pages), P, P, i32, i32, i32, P, P, P, sz, P]
@@ -166,13 +173,15 @@ def kv_append(pg: Pages, latent, key, key_scale: float, kv_pool, kv_scale, k_poo
                           _ptr(kv_scale), _ptr(k_pool), _stream(stream)))
 
 
-def indexer_topk(pg: Pages, q_idx, k_pool, top_k: int, sel, sel_score=None, ws=None, stream=None):
+def indexer_topk(pg: Pages, q_idx, k_pool, top_k: int, sel, sel_score=None, ws=None, stream=None,
+                 rows_per_seq: int = 1):
     L = load()
-    need = L.dl_indexer_topk_workspace(C.byref(pg))
+    need = L.dl_indexer_topk_rows_workspace(C.byref(pg), rows_per_seq)
     if ws is None:
         ws = workspace(need, q_idx.device)
-    _check(L.dl_indexer_topk(C.byref(pg), _ptr(q_idx), _ptr(k_pool), q_idx.shape[1], q_idx.shape[2], top_k,
-                             _ptr(sel), _ptr(sel_score), _ptr(ws), ws.numel(), _stream(stream)))
+    _check(L.dl_indexer_topk_rows(C.byref(pg), rows_per_seq, _ptr(q_idx), _ptr(k_pool), q_idx.shape[1],
+                                  q_idx.shape[2], top_k, _ptr(sel), _ptr(sel_score), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
     return sel
 
 
@@ -250,7 +259,8 @@ class LayerStep:
         L = load()
         self.spec, self.t = spec, t
         dev = t["x"].device
-        B = spec.B
+        self.R = getattr(spec, "R", 1)
+        B = spec.B * self.R  # rows
         self.keep = []
         self.pg = pages(t["seq_lens"], t["page_table"], spec.page_size)
         d = LayerDesc()
@@ -296,13 +306,13 @@ class LayerStep:
             for k, v in self.dbg.items():
                 setattr(io, k, _ptr(v))
         self.io = io
-        self.ws = workspace(L.dl_layer_workspace(C.byref(d), C.byref(self.pg)), dev)
+        self.ws = workspace(L.dl_layer_workspace_rows(C.byref(d), C.byref(self.pg), self.R), dev)
 
     def mat(self, name: str) -> Mat:
         w, sc, lay = self.w[name]
         return mat(w, sc, lay)
 
     def __call__(self, stream=None):
-        _check(load().dl_layer_step(C.byref(self.desc), C.byref(self.io), _ptr(self.ws), self.ws.numel(),
-                                    _stream(stream)))
+        _check(load().dl_layer_step_rows(C.byref(self.desc), C.byref(self.io), self.R, _ptr(self.ws), self.ws.numel(),
+                                         _stream(stream)))
         return self.y

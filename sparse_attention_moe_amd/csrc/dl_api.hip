@@ -275,21 +275,22 @@ static int run_attn_proj(const dl_pages &pg, const void *q, int q_dt, const void
                          int kv_dt, int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k,
                          const dl_mat *w_uv, const dl_mat *w_o, const void *resid, int resid_dt, float *o,
                          float *out, const AttnWs &a, uint8_t *hq, float *hqs, bool *h_split, hipStream_t s,
-                         const Marks &mk)
+                         const Marks &mk, int R = 1)
 {
-    const int B = pg.batch;
+    const int B = pg.batch * R;  // rows
     if (h_split) *h_split = false;
     const int hd = w_uv ? w_uv->rows : Dv;
     const bool fuse = w_o && w_uv && attention_mfma_ok(H, Dc, Dv, q_dt, kv_dt) && w_uv->dtype == DL_FP8_E4M3 &&
                       w_o->dtype == DL_FP8_E4M3 && attention_merge_uv_ok(Dv, hd);
     if (!fuse) {
-        DL_TRY(launch_attention(pg, q, q_dt, kv, kv_scale, kv_dt, H, Dc, Dv, sm_scale, sel, top_k, o, a.opart, a.ml, s));
+        DL_TRY(launch_attention(pg, q, q_dt, kv, kv_scale, kv_dt, H, Dc, Dv, sm_scale, sel, top_k, o, a.opart, a.ml, s,
+                                R));
         mk.at(2);
         if (!w_o) return DL_OK;
         return run_projection(B, H, Dv, o, w_uv, w_o, resid, resid_dt, out, a, s);
     }
     DL_TRY(launch_attention(pg, q, q_dt, kv, kv_scale, kv_dt, H, Dc, Dv, sm_scale, sel, top_k, nullptr, a.opart, a.ml,
-                            s));
+                            s, R));
     mk.at(2);
     const long K = (long)H * hd;
     DL_TRY(launch_attn_merge_uv(B, H, Dv, top_k, a.opart, a.ml, o, (const uint8_t *)w_uv->w, w_uv->scale, hd,
@@ -435,10 +436,11 @@ struct LayerWs {
     FfnWs ffn;
 };
 
-static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, const dl_layer_io *io, LayerWs &L)
+static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, const dl_layer_io *io, LayerWs &L,
+                            int R = 1)
 {
-    const int B = pg->batch;
-    topk_ws_layout(w, *pg, L.topk);
+    const int B = pg->batch * R;  // rows
+    topk_ws_layout(w, *pg, L.topk, R);
     L.sel = (io && io->sel) ? io->sel : w.take<int32_t>((long)B * d->top_k);
     L.o = (io && io->o) ? io->o : w.take<float>((long)B * d->n_heads * d->d_v);
     attn_ws_layout(w, B, d->n_heads, d->d_v, d->top_k, d->w_uv.w ? &d->w_uv : nullptr, nullptr, L.attn);
@@ -541,14 +543,16 @@ int dl_pack_weights(const dl_mat *src, void *dst, void *stream)
 }
 const char *dl_last_error(void) { return g_err; }
 
-size_t dl_indexer_topk_workspace(const dl_pages *pages)
+size_t dl_indexer_topk_rows_workspace(const dl_pages *pages, int32_t rows_per_seq)
 {
-    if (!pages) return 0;
+    if (!pages || rows_per_seq < 1 || rows_per_seq > DL_MAX_ROWS_PER_SEQ) return 0;
     Ws w(nullptr);
     TopkWs t;
-    topk_ws_layout(w, *pages, t);
+    topk_ws_layout(w, *pages, t, rows_per_seq);
     return w.used();
 }
+
+size_t dl_indexer_topk_workspace(const dl_pages *pages) { return dl_indexer_topk_rows_workspace(pages, 1); }
 
 int dl_kv_append(const dl_pages *pages, const void *latent, int32_t lat_dt, int32_t d_c, const void *key,
                  int32_t key_dt, int32_t idx_dim, float key_scale, uint8_t *kv_pool, float *kv_scale, int8_t *k_pool,
@@ -569,19 +573,29 @@ int dl_kv_append(const dl_pages *pages, const void *latent, int32_t lat_dt, int3
                             (hipStream_t)stream);
 }
 
-int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_pool, int32_t n_heads, int32_t dim,
-                    int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws, size_t ws_bytes, void *stream)
+int dl_indexer_topk_rows(const dl_pages *pages, int32_t rows_per_seq, const int8_t *q_idx, const int8_t *k_pool,
+                         int32_t n_heads, int32_t dim, int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws,
+                         size_t ws_bytes, void *stream)
 {
     g_err[0] = 0;
     DL_TRY(check_pages(pages));
+    const int R = rows_per_seq;
+    if (R < 1 || R > DL_MAX_ROWS_PER_SEQ) return fail(DL_ERR_UNSUPPORTED, "rows per sequence %d (1..%d)", R, DL_MAX_ROWS_PER_SEQ);
+    if ((long)pages->batch * R > 4096) return fail(DL_ERR_SHAPE, "rows %ld (<= 4096)", (long)pages->batch * R);
     if (!q_idx || !k_pool || !sel) return fail(DL_ERR_NULL, "q_idx/k_pool/sel NULL");
     DL_TRY(check_indexer(n_heads, dim, top_k));
-    DL_TRY(check_ws(ws, ws_bytes, dl_indexer_topk_workspace(pages)));
+    DL_TRY(check_ws(ws, ws_bytes, dl_indexer_topk_rows_workspace(pages, R)));
     (void)hipGetLastError();
     Ws w(ws);
     TopkWs t;
-    topk_ws_layout(w, *pages, t);
-    return launch_indexer_topk(*pages, q_idx, k_pool, n_heads, dim, top_k, sel, sel_score, t, (hipStream_t)stream);
+    topk_ws_layout(w, *pages, t, R);
+    return launch_indexer_topk(*pages, q_idx, k_pool, n_heads, dim, top_k, sel, sel_score, t, (hipStream_t)stream, R);
+}
+
+int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_pool, int32_t n_heads, int32_t dim,
+                    int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws, size_t ws_bytes, void *stream)
+{
+    return dl_indexer_topk_rows(pages, 1, q_idx, k_pool, n_heads, dim, top_k, sel, sel_score, ws, ws_bytes, stream);
 }
 
 size_t dl_sparse_attn_workspace(int32_t batch, int32_t n_heads, int32_t d_v, int32_t top_k, const dl_mat *w_uv,
@@ -669,60 +683,70 @@ int dl_moe_ffn(const float *h, int32_t B, int32_t D, int32_t inter, const int32_
                    out, out_dt, f, (hipStream_t)stream);
 }
 
-static int check_layer(const dl_layer_desc *d, const dl_pages *pg)
+static int check_layer(const dl_layer_desc *d, const dl_pages *pg, int R = 1)
 {
     if (!d) return fail(DL_ERR_NULL, "desc NULL");
     DL_TRY(check_pages(pg));
+    if ((long)pg->batch * R > 4096) return fail(DL_ERR_SHAPE, "rows %ld (<= 4096)", (long)pg->batch * R);
     DL_TRY(check_indexer(d->idx_heads, d->idx_dim, d->top_k));
-    DL_TRY(check_attn_shapes(pg->batch, d->n_heads, d->d_c, d->d_v, d->top_k, d->q_dt, d->kv_dt, nullptr, false));
+    DL_TRY(check_attn_shapes(pg->batch * R, d->n_heads, d->d_c, d->d_v, d->top_k, d->q_dt, d->kv_dt, nullptr, false));
     int D = 0;
     DL_TRY(check_proj(d->n_heads, d->d_v, d->w_uv.w ? &d->w_uv : nullptr, &d->w_o, &D));
     if (D != d->D) return fail(DL_ERR_SHAPE, "w_o rows %d != D %d", D, d->D);
     if (!d->w_r) return fail(DL_ERR_NULL, "w_r");
-    DL_TRY(check_ffn_shapes(pg->batch, d->D, d->inter, d->expert_top_k, d->n_routed, d->n_shared, &d->w_gate,
+    DL_TRY(check_ffn_shapes(pg->batch * R, d->D, d->inter, d->expert_top_k, d->n_routed, d->n_shared, &d->w_gate,
                             &d->w_up, &d->w_down));
     if (d->out_dt != DL_F32 && d->out_dt != DL_BF16) return fail(DL_ERR_DTYPE, "out dtype %d", d->out_dt);
     if (d->D % 4 || d->D > 16384) return fail(DL_ERR_UNSUPPORTED, "hidden size %d (multiple of 4, <= 16384)", d->D);
     return DL_OK;
 }
 
-size_t dl_layer_workspace(const dl_layer_desc *desc, const dl_pages *pages)
+size_t dl_layer_workspace_rows(const dl_layer_desc *desc, const dl_pages *pages, int32_t rows_per_seq)
 {
-    if (!desc || !pages) return 0;
+    if (!desc || !pages || rows_per_seq < 1 || rows_per_seq > DL_MAX_ROWS_PER_SEQ) return 0;
     Ws w(nullptr);
     LayerWs L;
-    layer_ws_layout(w, desc, pages, nullptr, L);
+    layer_ws_layout(w, desc, pages, nullptr, L, rows_per_seq);
     return w.used();
 }
 
-int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_t ws_bytes, void *stream)
+size_t dl_layer_workspace(const dl_layer_desc *desc, const dl_pages *pages)
+{
+    return dl_layer_workspace_rows(desc, pages, 1);
+}
+
+int dl_layer_step_rows(const dl_layer_desc *d, const dl_layer_io *io, int32_t rows_per_seq, void *ws, size_t ws_bytes,
+                       void *stream)
 {
     g_err[0] = 0;
     if (!io) return fail(DL_ERR_NULL, "io NULL");
-    DL_TRY(check_layer(d, &io->pages));
+    const int R = rows_per_seq;
+    if (R < 1 || R > DL_MAX_ROWS_PER_SEQ) return fail(DL_ERR_UNSUPPORTED, "rows per sequence %d (1..%d)", R, DL_MAX_ROWS_PER_SEQ);
+    DL_TRY(check_layer(d, &io->pages, R));
     if (d->kv_dt == DL_FP8_E4M3 && !io->kv_scale) return fail(DL_ERR_NULL, "FP8 KV needs kv_scale");
     if (d->kv_dt == DL_F32 && io->kv_scale) return fail(DL_ERR_DTYPE, "fp32 KV takes no kv_scale");
     if (!io->x || !io->q || !io->q_idx || !io->kv_pool || !io->k_pool || !io->y) return fail(DL_ERR_NULL, "io tensor NULL");
-    DL_TRY(check_ws(ws, ws_bytes, dl_layer_workspace(d, &io->pages)));
+    DL_TRY(check_ws(ws, ws_bytes, dl_layer_workspace_rows(d, &io->pages, R)));
     (void)hipGetLastError();
     hipStream_t s = (hipStream_t)stream;
     const dl_pages &pg = io->pages;
-    const int B = pg.batch;
+    const int B = pg.batch * R;  // rows: every row is a token of the step from here on
     Ws w(ws);
     LayerWs L;
-    layer_ws_layout(w, d, &pg, io, L);
+    layer_ws_layout(w, d, &pg, io, L, R);
     Marks mk;
     DL_TRY(marks_begin(mk, s));
     const dl_mat *wuv = d->w_uv.w ? &d->w_uv : nullptr;
     const bool f8_ffn = d->w_gate.dtype == DL_FP8_E4M3;
     const bool fuse_route = route_plan_ok(d->n_routed, d->expert_top_k, B);
     mk.at(0);
-    DL_TRY(launch_indexer_topk(pg, io->q_idx, io->k_pool, d->idx_heads, d->idx_dim, d->top_k, L.sel, nullptr, L.topk, s));
+    DL_TRY(launch_indexer_topk(pg, io->q_idx, io->k_pool, d->idx_heads, d->idx_dim, d->top_k, L.sel, nullptr, L.topk, s,
+                               R));
     mk.at(1);
     bool h_split = false;
     DL_TRY(run_attn_proj(pg, io->q, d->q_dt, io->kv_pool, io->kv_scale, d->kv_dt, d->n_heads, d->d_c, d->d_v,
                          d->sm_scale, L.sel, d->top_k, wuv, &d->w_o, io->x, d->q_dt, L.o, L.h, L.attn,
-                         f8_ffn ? L.ffn.hq : nullptr, L.ffn.hqs, &h_split, s, mk));
+                         f8_ffn ? L.ffn.hq : nullptr, L.ffn.hqs, &h_split, s, mk, R));
     mk.at(3);
     if (fuse_route) {
         DL_TRY(launch_route_partial(L.h, B, d->D, d->w_r, d->n_routed, L.rpart, s));
@@ -735,6 +759,11 @@ int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_
     mk.at(4);
     return run_ffn(L.h, B, d->D, d->inter, L.experts, L.gates, d->expert_top_k, &d->w_gate, &d->w_up, &d->w_down,
                    d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s, mk, io->y32, fuse_route, h_split);
+}
+
+int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_t ws_bytes, void *stream)
+{
+    return dl_layer_step_rows(d, io, 1, ws, ws_bytes, stream);
 }
 
 int dl_probe_read(const void *buf, size_t bytes, size_t *bytes_read, void *stream)

@@ -47,12 +47,15 @@ struct TopkWs {
     SelState *state;   // [4, B]
     int *cnt;          // [B, nchunk, 2]
 };
-void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t);
+void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R = 1);
 int launch_probe_read(const void *buf, size_t bytes, size_t *bytes_read, hipStream_t s);
 int launch_kv_append(const dl_pages &pg, const void *latent, int lat_dt, int Dc, const void *key, int key_dt, int DI,
                      float key_scale, uint8_t *kv, float *kv_scale, int8_t *kp, hipStream_t s);
+// R query rows per sequence (multi-row decode): q_idx [B*R, HI, DI], sel [B*R, top_k]; row i is the token at
+// position seq_lens[i / R] - R + i % R and sees the positions up to its own.
+static constexpr int DL_MAX_ROWS_PER_SEQ = 4;
 int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k_pool, int HI, int DI, int top_k,
-                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s);
+                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s, int R = 1);
 
 // ------------------------------------------------------------- GEMV engine
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
@@ -120,7 +123,7 @@ int attention_splits(int top_k, int B, int H);
 // With the matrix-core path and o == nullptr only the split partials are written (the caller merges).
 int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
                      int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, float *opart,
-                     float *ml, hipStream_t s);
+                     float *ml, hipStream_t s, int R = 1);
 bool attention_merge_uv_ok(int Dv, int hd);
 // Merge of the split partials + W_UV (fp32, exact decode) + 4-part FP8 split of u for W_O.
 int launch_attn_merge_uv(int B, int H, int Dv, int top_k, const float *opart, const float *ml, float *o,

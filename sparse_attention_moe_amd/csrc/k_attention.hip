@@ -41,7 +41,7 @@ __device__ __forceinline__ float lat(const void *kv, const float *ks, int fp8, l
 
 __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q, int q_dt, const void *__restrict__ kv,
                                               const float *__restrict__ ks, int fp8, const int32_t *__restrict__ pt,
-                                              int max_pages, int ps_shift, const int32_t *__restrict__ sel, int top_k,
+                                              int max_pages, int R, int ps_shift, const int32_t *__restrict__ sel, int top_k,
                                               int H, int Dc, int Dv, float sm_scale, float *__restrict__ o)
 {
     __shared__ float s_q[ATT_HG][ATT_MAX_DC];
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q, int q_
     }
     for (int j = tid; j < top_k; j += 256) {
         const int p = sel[(long)b * top_k + j];
-        s_row[j] = p < 0 ? -1 : ((long)pt[(long)b * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
+        s_row[j] = p < 0 ? -1 : ((long)pt[(long)(b / R) * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
     }
     __syncthreads();
     // logits
@@ -269,7 +269,7 @@ __device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32
 template <int KQ, int NVB, bool MULTI>  // MULTI: more than one chunk of 64 positions per split
 __global__ __launch_bounds__(256, 1) void k_attn_mla(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                      const float *__restrict__ ks, const int32_t *__restrict__ pt,
-                                                     int max_pages, int ps_shift, const int32_t *__restrict__ sel,
+                                                     int max_pages, int R, int ps_shift, const int32_t *__restrict__ sel,
                                                      int top_k, int H, int pps, float sm_scale,
                                                      float *__restrict__ opart, float *__restrict__ ml)
 {
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mla(const uint16_t *__restrict_
     for (int i = tid; i < pps; i += 256) {
         const int j = jbase + i;
         const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
-        s_row[i] = p < 0 ? -1 : ((long)pt[(long)b * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
+        s_row[i] = p < 0 ? -1 : ((long)pt[(long)(b / R) * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
     }
     const int nch = MULTI ? max(0, min(pps, top_k - jbase) + AM_NJ - 1) / AM_NJ : (jbase < top_k ? 1 : 0);
     // scores in log2 units: p = 2^(S - m) with S = sm_scale * log2(e) * q.c, so the exponentials are exp2
@@ -678,38 +678,39 @@ int attention_splits(int top_k, int B, int H)
 
 int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv, const float *kv_scale, int kv_dt,
                      int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k, float *o, float *opart,
-                     float *ml, hipStream_t s)
+                     float *ml, hipStream_t s, int R)
 {
+    const int rows = pg.batch * R;  // row i reads the cache of sequence i / R
     if (attention_mfma_ok(H, Dc, Dv, q_dt, kv_dt) && opart && ml) {
         if (top_k > AM_MAXPPS * AM_MAXSPLIT) return fail(DL_ERR_UNSUPPORTED, "attention top_k %d", top_k);
         const int ps_shift = __builtin_ctz((unsigned)pg.page_size);
-        const int pps = attention_pps(top_k, pg.batch, H);
+        const int pps = attention_pps(top_k, rows, H);
         const int nsplit = (top_k + pps - 1) / pps;
-        dim3 g(nsplit, (H + 63) / 64, pg.batch);
+        dim3 g(nsplit, (H + 63) / 64, rows);
 #define DL_AM(KQ_, NVB_)                                                                                            \
     if (Dc == KQ_ * 32 && Dv == NVB_ * 128) {                                                                       \
         if (pps > AM_NJ)                                                                                            \
             hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_, true>), g, dim3(256), 0, s, (const uint16_t *)q,              \
-                               (const uint8_t *)kv, kv_scale, pg.page_table, pg.max_pages_per_seq, ps_shift, sel,    \
+                               (const uint8_t *)kv, kv_scale, pg.page_table, pg.max_pages_per_seq, R, ps_shift, sel,    \
                                top_k, H, pps, sm_scale, opart, ml);                                                 \
         else                                                                                                        \
             hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_, false>), g, dim3(256), 0, s, (const uint16_t *)q,             \
-                               (const uint8_t *)kv, kv_scale, pg.page_table, pg.max_pages_per_seq, ps_shift, sel,    \
+                               (const uint8_t *)kv, kv_scale, pg.page_table, pg.max_pages_per_seq, R, ps_shift, sel,    \
                                top_k, H, pps, sm_scale, opart, ml);                                                 \
     }
         DL_AM(18, 4) DL_AM(18, 2) DL_AM(18, 1) DL_AM(16, 4) DL_AM(16, 2) DL_AM(16, 1) DL_AM(8, 2) DL_AM(8, 1)
         DL_AM(4, 1)
 #undef DL_AM
-        if (o) hipLaunchKernelGGL(k_attn_merge, dim3(pg.batch * H), dim3(256), 0, s, opart, ml, nsplit, H, Dv, o);
+        if (o) hipLaunchKernelGGL(k_attn_merge, dim3(rows * H), dim3(256), 0, s, opart, ml, nsplit, H, Dv, o);
         return hip_check("attention_mfma");
     }
     if (top_k > ATT_MAX_K || Dc > ATT_MAX_DC) return fail(DL_ERR_UNSUPPORTED, "attention top_k %d / d_c %d", top_k, Dc);
     if (Dv % 4 || (256 % (Dv / 4))) return fail(DL_ERR_UNSUPPORTED, "attention d_v %d (power of two 4..1024)", Dv);
     if (Dc % 4) return fail(DL_ERR_UNSUPPORTED, "attention d_c %d", Dc);
     const int ps_shift = __builtin_ctz((unsigned)pg.page_size);
-    dim3 g((H + ATT_HG - 1) / ATT_HG, pg.batch);
+    dim3 g((H + ATT_HG - 1) / ATT_HG, rows);
     hipLaunchKernelGGL(k_attn, g, dim3(256), 0, s, q, q_dt, kv, kv_scale, kv_dt == DL_FP8_E4M3 ? 1 : 0, pg.page_table,
-                       pg.max_pages_per_seq, ps_shift, sel, top_k, H, Dc, Dv, sm_scale, o);
+                       pg.max_pages_per_seq, R, ps_shift, sel, top_k, H, Dc, Dv, sm_scale, o);
     return hip_check("attention");
 }
 

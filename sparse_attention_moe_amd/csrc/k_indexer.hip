@@ -31,6 +31,15 @@ static constexpr int NB2 = 4096;
 static constexpr int SCORE_POS_PER_BLOCK = 1024;  // 4 waves x 4 steps x 64 positions
 static constexpr int SEL_CHUNK = 4096;            // 256 threads x 16 positions
 
+// Rows and sequences: with R query rows per sequence (multi-row decode), row i belongs to sequence i / R and
+// is the token at position seq_lens[i / R] - R + i % R, so it sees the positions before and including its own
+// (causal among the R rows).  R = 1 is ordinary decode.
+__device__ __forceinline__ int row_len(const int32_t *seq_lens, int row, int R)
+{
+    const int L = seq_lens[row / R] - (R - 1 - row % R);
+    return L > 0 ? L : 0;
+}
+
 __device__ __forceinline__ int bin1_of(int s)
 {
     if (s < 256) return s;
@@ -139,13 +148,14 @@ __device__ SelState advance(const SelState prev, const unsigned *gh, int top_k, 
 }
 
 // Per-row initial selection state; clears the histograms of all passes.
-__global__ void k_sel_init(const int32_t *seq_lens, int B, int top_k, unsigned *hist1, unsigned *hist2, SelState *st)
+__global__ void k_sel_init(const int32_t *seq_lens, int R, int B, int top_k, unsigned *hist1, unsigned *hist2,
+                           SelState *st)
 {
     const int b = blockIdx.x;
     for (int i = threadIdx.x; i < NB1; i += blockDim.x) hist1[(long)b * NB1 + i] = 0;
     for (int i = threadIdx.x; i < 2 * NB2; i += blockDim.x) hist2[(long)b * 2 * NB2 + i] = 0;
     if (threadIdx.x == 0) {
-        int L = seq_lens[b];
+        int L = row_len(seq_lens, b, R);
         SelState s;
         s.n_sel = min(L, top_k);
         if (L <= top_k) {  // keep everything: every score (>= 0) is above T = -1
@@ -158,33 +168,38 @@ __global__ void k_sel_init(const int32_t *seq_lens, int B, int top_k, unsigned *
     }
 }
 
-// Scores of 1,024 positions per workgroup.  NHG groups of 16 indexer heads, KCH chunks of 64 key bytes.
-template <int NHG, int KCH>
+// Scores of 1,024 positions of one sequence per workgroup.  NHG groups of 16 indexer heads, KCH chunks of 64 key
+// bytes, RW query rows per sequence: every key is loaded once and scored against all RW rows (RW x NHG matrix
+// instructions per 16 positions and 64 key bytes), each row keeping the positions it sees.
+template <int NHG, int KCH, int RW>
 __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ q_idx, const int8_t *__restrict__ k_pool,
                                                      const int32_t *__restrict__ page_table,
                                                      const int32_t *__restrict__ seq_lens, int max_pages, int ps_shift,
                                                      int HI, int DI, int32_t *__restrict__ scores, long Lmax,
                                                      unsigned *__restrict__ hist1)
 {
-    __shared__ unsigned s_hist[NB1];
-    const int b = blockIdx.y;
-    const int L = seq_lens[b];
+    __shared__ unsigned s_hist[RW][NB1];
+    const int sq = blockIdx.y;
+    const int L = seq_lens[sq];  // positions of the sequence; row r sees the first L - (RW - 1 - r)
     const long blk0 = (long)blockIdx.x * SCORE_POS_PER_BLOCK;
     if (blk0 >= L) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
-    for (int i = tid; i < NB1; i += 256) s_hist[i] = 0;
+    for (int i = tid; i < RW * NB1; i += 256) (&s_hist[0][0])[i] = 0;
 
     // A operand: q rows (indexer heads) for this lane: head hg*16+ln, bytes kc*64 + lg*16 .. +16
-    v4i A[NHG][KCH];
+    v4i A[RW][NHG][KCH];
 #pragma unroll
-    for (int hg = 0; hg < NHG; hg++)
+    for (int r = 0; r < RW; r++)
 #pragma unroll
-        for (int kc = 0; kc < KCH; kc++) {
-            int h = hg * 16 + ln, d = kc * 64 + lg * 16;
-            A[hg][kc] = (h < HI && d < DI) ? ldg16(q_idx + ((long)b * HI + h) * DI + d) : v4i{0, 0, 0, 0};
-        }
-    const int32_t *pt = page_table + (long)b * max_pages;
+        for (int hg = 0; hg < NHG; hg++)
+#pragma unroll
+            for (int kc = 0; kc < KCH; kc++) {
+                int h = hg * 16 + ln, d = kc * 64 + lg * 16;
+                A[r][hg][kc] = (h < HI && d < DI) ? ldg16(q_idx + (((long)sq * RW + r) * HI + h) * DI + d)
+                                                  : v4i{0, 0, 0, 0};
+            }
+    const int32_t *pt = page_table + (long)sq * max_pages;
     const int ps_mask = (1 << ps_shift) - 1;
     // cache rows of every position this lane loads (step st, group sg: position g0(st) + sg*16 + ln), all
     // page-table reads in flight at once
@@ -217,35 +232,46 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
     for (int st = 0; st < 4; st++) {
         const long g0 = blk0 + (long)(st * 4 + wave) * 64;  // this wave's 64 positions
         v4i (&Bk)[4][KCH] = (st & 1) ? K1 : K0;
-        int mine = 0;
+        int mine[RW];
+#pragma unroll
+        for (int r = 0; r < RW; r++) mine[r] = 0;
 #pragma unroll
         for (int sg = 0; sg < 4; sg++) {
-            int part = 0;
 #pragma unroll
-            for (int hg = 0; hg < NHG; hg++) {
-                v4i acc = {0, 0, 0, 0};
+            for (int r = 0; r < RW; r++) {
+                int part = 0;
 #pragma unroll
-                for (int kc = 0; kc < KCH; kc++)
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[hg][kc], Bk[sg][kc], acc, 0, 0, 0);
-                // lane holds heads hg*16 + 4*lg + i of position sg*16 + ln
-                part += max(acc[0], 0) + max(acc[1], 0) + max(acc[2], 0) + max(acc[3], 0);
+                for (int hg = 0; hg < NHG; hg++) {
+                    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+                    for (int kc = 0; kc < KCH; kc++)
+                        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[r][hg][kc], Bk[sg][kc], acc, 0, 0, 0);
+                    // lane holds heads hg*16 + 4*lg + i of position sg*16 + ln
+                    part += max(acc[0], 0) + max(acc[1], 0) + max(acc[2], 0) + max(acc[3], 0);
+                }
+                part += __shfl_xor(part, 16, 64);
+                part += __shfl_xor(part, 32, 64);
+                if (lg == sg) mine[r] = part;
             }
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            if (lg == sg) mine = part;
         }
         if (st + 2 < 4) load_keys(st + 2, Bk);  // this buffer is free again
         const long pos = g0 + lane;
-        if (pos < L) {
-            scores[(long)b * Lmax + pos] = mine;
-            atomicAdd(&s_hist[bin1_of(mine)], 1u);
+#pragma unroll
+        for (int r = 0; r < RW; r++) {
+            if (pos < L - (RW - 1 - r)) {
+                scores[((long)sq * RW + r) * Lmax + pos] = mine[r];
+                atomicAdd(&s_hist[r][bin1_of(mine[r])], 1u);
+            }
         }
     }
     __syncthreads();
-    unsigned *gh = hist1 + (long)b * NB1;
-    for (int i = tid; i < NB1; i += 256) {
-        const unsigned v = s_hist[i];
-        if (v) atomicAdd(gh + i, v);
+#pragma unroll
+    for (int r = 0; r < RW; r++) {
+        unsigned *gh = hist1 + ((long)sq * RW + r) * NB1;
+        for (int i = tid; i < NB1; i += 256) {
+            const unsigned v = s_hist[r][i];
+            if (v) atomicAdd(gh + i, v);
+        }
     }
 }
 
@@ -268,14 +294,14 @@ __device__ __forceinline__ void load16(const int32_t *sc, long p0, int L, int v[
 // inside the new [lo, hi] with 4,096 bins into histogram PASS + 1.
 template <int PASS>
 __global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ scores, long Lmax,
-                                                    const int32_t *__restrict__ seq_lens, int top_k,
+                                                    const int32_t *__restrict__ seq_lens, int R, int top_k,
                                                     const unsigned *__restrict__ hist_in, unsigned *__restrict__ hist_out,
                                                     SelState *__restrict__ st, int B)
 {
     __shared__ unsigned s_hist[NB2 > NB1 ? NB2 : NB1];
     __shared__ int s_tmp[260];
     const int b = blockIdx.y;
-    const int L = seq_lens[b];
+    const int L = row_len(seq_lens, b, R);
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
     if (c0 >= L && blockIdx.x != 0) return;
     const int tid = threadIdx.x;
@@ -308,7 +334,7 @@ __global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ 
 
 // Per chunk: how many scores are > T and == T.
 __global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ scores, long Lmax,
-                                                   const int32_t *__restrict__ seq_lens, int top_k,
+                                                   const int32_t *__restrict__ seq_lens, int R, int top_k,
                                                    const unsigned *__restrict__ hist3, SelState *__restrict__ st, int B,
                                                    int nchunk, int *__restrict__ cnt)
 {
@@ -316,7 +342,7 @@ __global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ s
     __shared__ int s_tmp[260];
     __shared__ int s_red[2][4];
     const int b = blockIdx.y;
-    const int L = seq_lens[b];
+    const int L = row_len(seq_lens, b, R);
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
     if (c0 >= L && blockIdx.x != 0) return;
     const int tid = threadIdx.x;
@@ -345,14 +371,14 @@ __global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ s
 
 // Ordered compaction of the kept positions of one chunk.
 __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ scores, long Lmax,
-                                                   const int32_t *__restrict__ seq_lens, const SelState *__restrict__ st,
+                                                   const int32_t *__restrict__ seq_lens, int R, const SelState *__restrict__ st,
                                                    int nchunk, const int *__restrict__ cnt, int top_k,
                                                    int32_t *__restrict__ sel, int32_t *__restrict__ sel_score)
 {
     __shared__ int s_w[2][4];
     __shared__ int s_base[2];
     const int b = blockIdx.y;
-    const int L = seq_lens[b];
+    const int L = row_len(seq_lens, b, R);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const SelState s = st[3L * gridDim.y + b];
     int32_t *so = sel + (long)b * top_k;
@@ -421,9 +447,9 @@ __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ s
 // ------------------------------------------------------------------ host side
 static int max_len(const dl_pages &pg) { return pg.max_pages_per_seq * pg.page_size; }
 
-void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t)
+void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R)
 {
-    const long B = pg.batch, Lmax = max_len(pg);
+    const long B = (long)pg.batch * R, Lmax = max_len(pg);  // one selection per row
     const long nchunk = (Lmax + SEL_CHUNK - 1) / SEL_CHUNK;
     t.scores = w.take<int32_t>(B * Lmax);
     t.hist1 = w.take<unsigned>(B * NB1);
@@ -434,24 +460,29 @@ void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t)
 
 template <int NHG, int KCH>
 static void launch_score(dim3 g, hipStream_t s, const int8_t *q, const int8_t *kp, const dl_pages &pg, int ps_shift,
-                         int HI, int DI, const TopkWs &t, long Lmax)
+                         int HI, int DI, const TopkWs &t, long Lmax, int R)
 {
-    hipLaunchKernelGGL((k_index_score<NHG, KCH>), g, dim3(256), 0, s, q, kp, pg.page_table, pg.seq_lens,
-                       pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax, t.hist1);
+#define DL_SCORE_R(R_)                                                                                              \
+    if (R == R_)                                                                                                    \
+        hipLaunchKernelGGL((k_index_score<NHG, KCH, R_>), g, dim3(256), 0, s, q, kp, pg.page_table, pg.seq_lens,   \
+                           pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax, t.hist1);
+    DL_SCORE_R(1) DL_SCORE_R(2) DL_SCORE_R(3) DL_SCORE_R(4)
+#undef DL_SCORE_R
 }
 
 int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k_pool, int HI, int DI, int top_k,
-                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s)
+                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s, int R)
 {
-    const int B = pg.batch;
+    if (R < 1 || R > DL_MAX_ROWS_PER_SEQ) return fail(DL_ERR_UNSUPPORTED, "rows per sequence %d (1..%d)", R, DL_MAX_ROWS_PER_SEQ);
+    const int B = pg.batch * R;  // rows
     const long Lmax = max_len(pg);
     const int ps_shift = __builtin_ctz((unsigned)pg.page_size);
     const int nchunk = (int)((Lmax + SEL_CHUNK - 1) / SEL_CHUNK);
-    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, pg.seq_lens, B, top_k, t.hist1, t.hist2, t.state);
-    dim3 gs((unsigned)((Lmax + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK), B);
+    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, pg.seq_lens, R, B, top_k, t.hist1, t.hist2, t.state);
+    dim3 gs((unsigned)((Lmax + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK), pg.batch);
     const int nhg = (HI + 15) / 16, kch = (DI + 63) / 64;
 #define DL_SCORE_CASE(H_, K_) \
-    if (nhg == H_ && kch == K_) launch_score<H_, K_>(gs, s, q_idx, k_pool, pg, ps_shift, HI, DI, t, Lmax); else
+    if (nhg == H_ && kch == K_) launch_score<H_, K_>(gs, s, q_idx, k_pool, pg, ps_shift, HI, DI, t, Lmax, R); else
     DL_SCORE_CASE(1, 1) DL_SCORE_CASE(1, 2) DL_SCORE_CASE(1, 3) DL_SCORE_CASE(1, 4)
     DL_SCORE_CASE(2, 1) DL_SCORE_CASE(2, 2) DL_SCORE_CASE(2, 3) DL_SCORE_CASE(2, 4)
     DL_SCORE_CASE(3, 1) DL_SCORE_CASE(3, 2) DL_SCORE_CASE(3, 3) DL_SCORE_CASE(3, 4)
@@ -462,14 +493,14 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     // 31-bit scores: pass 1 leaves a range of at most 2^23 values; each refinement takes 12 bits, so the
     // state after histogram 3 is always final.
     unsigned *h2 = t.hist2, *h3 = t.hist2 + (long)B * NB2;
-    hipLaunchKernelGGL((k_sel_refine<1>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, top_k, t.hist1, h2,
+    hipLaunchKernelGGL((k_sel_refine<1>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, top_k, t.hist1, h2,
                        t.state, B);
-    hipLaunchKernelGGL((k_sel_refine<2>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, top_k, h2, h3, t.state,
-                       B);
-    hipLaunchKernelGGL(k_sel_count, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, top_k, h3, t.state, B, nchunk,
-                       t.cnt);
-    hipLaunchKernelGGL(k_sel_write, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, t.state, nchunk, t.cnt, top_k,
-                       sel, sel_score);
+    hipLaunchKernelGGL((k_sel_refine<2>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, top_k, h2, h3,
+                       t.state, B);
+    hipLaunchKernelGGL(k_sel_count, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, top_k, h3, t.state, B,
+                       nchunk, t.cnt);
+    hipLaunchKernelGGL(k_sel_write, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, t.state, nchunk, t.cnt,
+                       top_k, sel, sel_score);
     return hip_check("indexer_topk");
 }
 

@@ -59,6 +59,7 @@ class LayerSpec:
     key_values: str = "uniform"  # indexer q/k: "uniform" in [-127,127] or "ternary" {-1,0,1}
     dup_router_rows: bool = False  # make expert 1 a copy of expert 0 (exact router ties)
     sm_scale: Optional[float] = None     # None -> 1/sqrt(Dc)
+    R: int = 1                  # query rows per sequence (multi-row decode); per-row tensors have B * R rows
 
     @property
     def wo_in(self) -> int:
@@ -145,9 +146,9 @@ def make_layer(spec: LayerSpec, seed: int = 0, device="cpu", instance: int = 0,
 
     Returned keys (dtype, shape):
       seq_lens int32 [B]; page_table int32 [B, max_pages]; n_pages
-      x   act [B, D]            (bf16, or fp32 when not spec.fp8)
-      q   act [B, H, Dc]
-      q_idx int8 [B, HI, DI];  k_pool int8 [P, page, DI]
+      x   act [B*R, D]          (bf16, or fp32 when not spec.fp8; R = spec.R query rows per sequence)
+      q   act [B*R, H, Dc]
+      q_idx int8 [B*R, HI, DI];  k_pool int8 [P, page, DI]
       kv  uint8/fp32 [P, page, Dc];  kv_scale fp32 [P, page, ceil(Dc/128)] (fp8 only)
       w_uv (fp8 only) uint8 [H, head_dim, Dv] + w_uv_scale [H, head_dim/128, Dv/128]
       w_o  [D, wo_in] (+ w_o_scale);  w_r fp32 [E, D];  r_bias fp32 [E]
@@ -175,9 +176,10 @@ def make_layer(spec: LayerSpec, seed: int = 0, device="cpu", instance: int = 0,
     out["n_pages"] = torch.tensor(n_pages)
     act_dt = torch.bfloat16 if spec.fp8 else torch.float32
 
-    out["x"] = _randn((B, spec.D), dev, seed, instance, "x").to(act_dt)
-    out["q"] = _randn((B, spec.H, spec.Dc), dev, seed, instance, "q").to(act_dt)
-    out["q_idx"] = _int8_uniform((B, spec.HI, spec.DI), dev, seed, instance, "q_idx", spec.key_values)
+    rows = B * spec.R
+    out["x"] = _randn((rows, spec.D), dev, seed, instance, "x").to(act_dt)
+    out["q"] = _randn((rows, spec.H, spec.Dc), dev, seed, instance, "q").to(act_dt)
+    out["q_idx"] = _int8_uniform((rows, spec.HI, spec.DI), dev, seed, instance, "q_idx", spec.key_values)
     out["k_pool"] = _int8_uniform((n_pages, ps, spec.DI), dev, seed, instance, "k_pool", spec.key_values)
     lat = _randn((n_pages, ps, spec.Dc), dev, seed, instance, "kv")
     if spec.fp8:

@@ -287,3 +287,39 @@ def test_kv_append_bit_exact(bf16):
     assert bad.size == 0, f"{len(bad)} latent bytes differ, first {bad[:3].tolist()}: {got_kv[tuple(bad[0])]} vs {kv[tuple(bad[0])]}"
     assert np.array_equal(got_s.view(np.uint32), kvs.view(np.uint32))
     assert np.array_equal(got_k, kp)
+
+
+# ------------------------------------------------------------- multi-row decode (R query rows per sequence)
+@pytest.mark.parametrize("R", [2, 3, 4])
+def test_indexer_rows_bit_exact(R):
+    # ragged: a long sequence spanning many score blocks, one shorter than R (its first rows see nothing), a
+    # padding sequence, one with an exact multiple of the page size
+    spec = synth.spec_replace(synth.small_fp8_spec(name=f"rows{R}", seq_lens=(5000, 2, 0, 1024, 777), topk=512), R=R)
+    t = _layer(spec, seed=20 + R, weights=False)
+    rows = spec.B * R
+    sel = torch.empty(rows, spec.topk, dtype=torch.int32, device=DEV)
+    ss = torch.empty_like(sel)
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+    say(f"[gpu] indexer_topk rows R={R} B={spec.B} lens={spec.seq_lens}")
+    dl.indexer_topk(pg, t["q_idx"], t["k_pool"], spec.topk, sel, ss, rows_per_seq=R)
+    torch.cuda.synchronize()
+    sel, ss = host(sel), host(ss)
+    orc = oracle.LayerOracle(spec, t)
+    for i in range(rows):
+        r = orc.row(i, stages=("sel",))
+        assert np.array_equal(sel[i], r["sel"]), f"row {i}: first diff at {np.nonzero(sel[i] != r['sel'])[0][:5]}"
+        n = int((r["sel"] >= 0).sum())
+        assert np.array_equal(ss[i][:n], r["scores"][r["sel"][:n]])
+        assert np.all(ss[i][n:] == 0)
+
+
+@pytest.mark.parametrize("R", [2, 3])
+def test_layer_step_rows(R):
+    spec = synth.spec_replace(synth.small_fp8_spec(name=f"step-rows{R}", seq_lens=(3000, 2, 700), B=3), R=R)
+    t = _layer(spec, seed=30 + R)
+    step = dl.LayerStep(spec, t, debug=True)
+    say(f"[gpu] layer_step rows R={R} lens={spec.seq_lens}")
+    y = step()
+    torch.cuda.synchronize()
+    w = check_rows(spec, t, step.dbg, y, list(range(spec.B * R)))
+    say(f"rows R={R}: {w}")

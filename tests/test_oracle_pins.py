@@ -423,3 +423,40 @@ def test_kv_append_row(Dc, bf16):
     # exact halves with a unit scale: ties to even
     _, _, kt = oracle.kv_append_row(np.zeros(64, np.float32), np.array([0.5, 1.5, 2.5, -0.5, -2.5, 126.5], np.float32), 1.0)
     assert list(kt) == [0, 2, 2, 0, -2, 126]
+
+
+# ------------------------------------------------------------- multi-row decode (R query rows per sequence)
+def test_multirow_last_row_is_single_row_decode_and_rows_are_causal():
+    # R = 3 rows per sequence: the last row of a sequence sees every cached position, so it is exactly the
+    # single-row decode of its inputs; row r sees L - (R - 1 - r) positions, so its scores are the prefix of the
+    # scores its query gets over the whole sequence, and its selection never reaches beyond its own position.
+    R = 3
+    spec = synth.spec_replace(synth.config(1), R=R, seq_lens=(700,), topk=256)
+    t = synth.make_layer(spec, seed=9)
+    multi = oracle.LayerOracle(spec, t)
+    single_spec = synth.spec_replace(spec, R=1)
+    for r in range(R):
+        one = {k: v for k, v in t.items()}
+        for name in ("x", "q", "q_idx"):
+            one[name] = t[name][r:r + 1]
+        full = oracle.LayerOracle(single_spec, one).row(0, stages=("sel",))
+        got = multi.row(r, stages=("sel",) if r < R - 1 else ("sel", "o", "h", "route", "y"))
+        vis = 700 - (R - 1 - r)
+        assert len(got["scores"]) == vis
+        assert np.array_equal(got["scores"], full["scores"][:vis])
+        kept = got["sel"][got["sel"] >= 0]
+        assert kept.size == min(spec.topk, vis) and kept.max() < vis
+        if r == R - 1:
+            ref = oracle.LayerOracle(single_spec, one).row(0)
+            assert np.array_equal(got["sel"], ref["sel"])
+            assert np.array_equal(got["y"], ref["y"])
+
+
+def test_multirow_short_sequence_rows_are_padding():
+    # a sequence holding fewer positions than rows: its first rows see nothing (all -1), the rest see 1, 2, ...
+    spec = synth.spec_replace(synth.config(1), R=4, seq_lens=(2,), topk=8)
+    t = synth.make_layer(spec, seed=2)
+    orc = oracle.LayerOracle(spec, t)
+    vis = [len(orc.row(r, stages=("sel",))["scores"]) for r in range(4)]
+    assert vis == [0, 0, 1, 2]
+    assert np.all(orc.row(1, stages=("sel",))["sel"] == -1)
