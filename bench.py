@@ -36,7 +36,8 @@ def algorithmic_bytes(spec, lens, n_touched: int) -> dict:
     """Bytes the method must read per step (weights and caches once; activations are negligible)."""
     keys = sum(int(l) for l in lens) * spec.DI
     nb = (spec.Dc + 127) // 128
-    kv = sum(min(int(l), spec.topk) for l in lens) * (spec.Dc + 4 * nb)
+    R = getattr(spec, "R", 1)  # query rows per sequence: each row keeps its own positions (up to its own)
+    kv = sum(min(max(0, int(l) - (R - 1 - r)), spec.topk) for l in lens for r in range(R)) * (spec.Dc + 4 * nb)
     hd = spec.head_dim or spec.Dv
     wuv = spec.H * hd * spec.Dv + spec.H * (hd // 128) * (spec.Dv // 128) * 4 if spec.head_dim else 0
     wo = spec.D * spec.wo_in + (spec.D // 128) * (spec.wo_in // 128) * 4
@@ -126,9 +127,9 @@ def cpu_baseline(spec, t, rows):
     for b in rows:
         orc.row(b)
     dt = time.perf_counter() - t0
-    per_step = dt / len(rows) * spec.B
+    per_step = dt / len(rows) * spec.B * getattr(spec, "R", 1)
     return {"value": 1.0 / per_step, "unit": "layer-steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} of {spec.B} rows of one {spec.name} step (indexer over the full context, "
+            "sample": f"{len(rows)} of {spec.B * getattr(spec, 'R', 1)} rows of one {spec.name} step (indexer over the full context, "
                       f"attention, projections, router, FFN), {dt:.1f} s, scaled to a whole step"}
 
 
@@ -143,6 +144,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1)
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe")
+    ap.add_argument("--rows-per-seq", type=int, default=1,
+                    help="query rows per sequence (multi-row decode, e.g. MTP verification); 1 = ordinary decode")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device (counter calibration)")
     args = ap.parse_args()
@@ -150,6 +153,8 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     spec = synth.config(args.config)
+    if args.rows_per_seq != 1:
+        spec = synth.spec_replace(spec, R=args.rows_per_seq, name=f"{spec.name}-rows{args.rows_per_seq}")
     dev = "cuda"
     insts, steps_obj = [], []
     t0 = time.perf_counter()
@@ -221,8 +226,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "batch": spec.B, "context": int(max(spec.seq_lens)), "hidden": spec.D,
                    "heads": spec.H, "latent": spec.Dc, "top_k": spec.topk, "experts": f"{spec.E}+{spec.n_shared}",
-                   "expert_top_k": spec.ke, "inter": spec.I, "instances_rotated": n},
-        "tokens_per_s_per_layer": round(steps_per_s * spec.B, 1),
+                   "expert_top_k": spec.ke, "inter": spec.I, "rows_per_seq": spec.R, "instances_rotated": n},
+        "tokens_per_s_per_layer": round(steps_per_s * spec.B * spec.R, 1),
         "step_hbm": {"algorithmic_bytes": int(avg_bytes["total"]), "achieved_gbs": round(step_gbs, 1),
                      "peak_gbs": HBM_PEAK_GBS, "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                      "touched_experts": round(avg_touch, 2)},
