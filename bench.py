@@ -133,6 +133,85 @@ def cpu_baseline(spec, t, rows):
                       f"attention, projections, router, FFN), {dt:.1f} s, scaled to a whole step"}
 
 
+def share_tp8(args, spec, n: int = 8):
+    """One GPU's share of an n-GPU layer step (design: DP attention, tensor-parallel experts): the indexer and
+    attention (+ W_UV, W_O, residual) for its B/n sequences, the router for all B tokens (each GPU routes every
+    token after the all-gather of h), and the FFN for all B tokens on intermediate rows [0, I/n) of every expert.
+    The all-gather of h and the reduce-scatter of y need a second GPU and are not run."""
+    dev = "cuda"
+    Bl = spec.B // n
+    insts = []
+    t0 = time.perf_counter()
+    for i in range(args.instances):
+        t = synth.make_layer(spec, seed=args.seed, device=dev, instance=i)
+        w = synth.tp_slice(t, spec, 0, n)
+        for k in ("w_gate", "w_up", "w_down"):
+            t[k] = None
+        m = {k: dl.pack_weights(w[k], w[k + "_scale"]) for k in ("w_gate", "w_up", "w_down")}
+        mats = {k: dl.mat(m[k], w[k + "_scale"], dl.DL_LAYOUT_TILES) for k in m}
+        keep = (m, w)
+        pg = dl.pages(t["seq_lens"][:Bl].contiguous(), t["page_table"][:Bl].contiguous(), spec.page_size)
+        sel = torch.empty(Bl, spec.topk, dtype=torch.int32, device=dev)
+        hl = torch.empty(Bl, spec.D, dtype=torch.float32, device=dev)
+        h = (t["x"].float() + 0.1 * torch.randn(spec.B, spec.D, device=dev)).contiguous()  # all-gathered h
+        ex = torch.empty(spec.B, spec.ke, dtype=torch.int32, device=dev)
+        g = torch.empty(spec.B, spec.ke, dtype=torch.float32, device=dev)
+        y = torch.empty(spec.B, spec.D, dtype=torch.float32, device=dev)
+        wuv = dl.mat(dl.pack_weights(t["w_uv"], t["w_uv_scale"]), t["w_uv_scale"], dl.DL_LAYOUT_TILES)
+        wo = dl.mat(dl.pack_weights(t["w_o"], t["w_o_scale"]), t["w_o_scale"], dl.DL_LAYOUT_TILES)
+        insts.append(dict(t=t, mats=mats, keep=keep, pg=pg, sel=sel, hl=hl, h=h, ex=ex, g=g, y=y, wuv=wuv, wo=wo,
+                          q_idx=t["q_idx"][:Bl].contiguous(), q=t["q"][:Bl].contiguous(), x=t["x"][:Bl].contiguous()))
+    torch.cuda.synchronize()
+    print(f"[bench] generated {args.instances} x {spec.name} shares in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    ws = {}
+
+    def step(it):
+        t = it["t"]
+        dl.indexer_topk(it["pg"], it["q_idx"], t["k_pool"], spec.topk, it["sel"], ws=ws.get("i"))
+        dl.sparse_attn_decode(it["pg"], it["q"], t["kv"], t["kv_scale"], spec.H, spec.Dc, spec.Dv, spec.scale,
+                              it["sel"], spec.topk, it["hl"], w_uv=it["wuv"], w_o=it["wo"], residual=it["x"],
+                              ws=ws.get("a"))
+        dl.moe_route(it["h"], t["w_r"], t["r_bias"], spec.ke, it["ex"], it["g"], ws=ws.get("r"))
+        mt = it["mats"]
+        dl.moe_ffn(it["h"], it["ex"], it["g"], mt["w_gate"], mt["w_up"], mt["w_down"], spec.E, spec.n_shared,
+                   it["y"], residual=it["h"], ws=ws.get("f"))
+
+    L = dl.load()
+    it0 = insts[0]
+    ws["i"] = dl.workspace(L.dl_indexer_topk_workspace(dl.C.byref(it0["pg"])), dev)
+    ws["a"] = dl.workspace(L.dl_sparse_attn_workspace(Bl, spec.H, spec.Dv, spec.topk, dl.C.byref(it0["wuv"]),
+                                                      dl.C.byref(it0["wo"])), dev)
+    ws["r"] = dl.workspace(L.dl_moe_route_workspace(spec.B, spec.D, spec.E), dev)
+    ws["f"] = dl.workspace(L.dl_moe_ffn_workspace(spec.B, spec.D, spec.I // n, spec.ke, spec.E, spec.n_shared), dev)
+    for i in range(args.warmup):
+        step(insts[i % len(insts)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(insts[i % len(insts)])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    touched_n = sum(touched(spec, it["ex"].cpu().numpy()) for it in insts) / len(insts)
+    share = synth.spec_replace(spec, B=Bl, seq_lens=spec.seq_lens[:Bl])
+    b = algorithmic_bytes(share, share.seq_lens, 0)
+    gu = touched_n * EXPERT_BYTES_GATE_UP(spec) / n
+    dn = touched_n * EXPERT_BYTES_DOWN(spec) / n
+    total = b["total"] + gu + dn
+    rec = {"metric": "one GPU's share of an 8-GPU decode layer step (exchanges not run), layer-steps/s",
+           "value": round(1000.0 / ms, 2), "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8-weights/int8-indexer/fp32-accum", "data": "synthetic",
+           "config": {"workload": f"{spec.name}-tp{n}-share", "sequences": Bl, "tokens_routed": spec.B,
+                      "inter_slice": spec.I // n, "context": int(max(spec.seq_lens))},
+           "share_hbm": {"algorithmic_bytes": int(total), "achieved_gbs": round(total / (ms * 1e-3) / 1e9, 1),
+                         "frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "touched_experts": round(touched_n, 2)}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +223,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1)
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe")
+    ap.add_argument("--share", choices=["tp8"], default=None,
+                    help="time one GPU's share of an 8-GPU layer instead (DP attention on one sequence, router for "
+                         "every token, tensor-parallel expert slice of inter/8 rows); the exchanges are not run")
     ap.add_argument("--rows-per-seq", type=int, default=1,
                     help="query rows per sequence (multi-row decode, e.g. MTP verification); 1 = ordinary decode")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -153,6 +235,8 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     spec = synth.config(args.config)
+    if args.share:
+        return share_tp8(args, spec)
     if args.rows_per_seq != 1:
         spec = synth.spec_replace(spec, R=args.rows_per_seq, name=f"{spec.name}-rows{args.rows_per_seq}")
     dev = "cuda"

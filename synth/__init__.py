@@ -307,3 +307,23 @@ def make_append(seed: int = 0, B: int = 9, Dc: int = 576, DI: int = 128, page_si
         "kv_scale": torch.rand((n_pages, page_size, nb), generator=gp).to(device),
         "k_pool": torch.randint(-128, 128, (n_pages, page_size, DI), generator=gp, dtype=torch.int8).to(device),
     }
+
+
+def tp_slice(t: Dict[str, torch.Tensor], spec: LayerSpec, s: int, n: int) -> Dict[str, torch.Tensor]:
+    """Expert weights of tensor-parallel slice s of n: intermediate rows [s I/n, (s+1) I/n) of every expert's gate
+    and up matrices and the same columns of its down matrix, with their block scales (I/n must be a multiple of
+    128 so that slices hold whole scale blocks).  Pure slicing: no arithmetic.  The slices' FFN contributions add
+    up to the whole FFN because SwiGLU acts on each intermediate row separately."""
+    I = spec.I
+    assert I % n == 0 and (I // n) % 128 == 0, "slices of whole 128-row scale blocks"
+    r0, r1 = s * I // n, (s + 1) * I // n
+    b0, b1 = r0 // 128, r1 // 128
+    out = {
+        "w_gate": t["w_gate"][:, r0:r1].contiguous(), "w_up": t["w_up"][:, r0:r1].contiguous(),
+        "w_down": t["w_down"][:, :, r0:r1].contiguous(),
+    }
+    if spec.fp8:
+        out["w_gate_scale"] = t["w_gate_scale"][:, b0:b1].contiguous()
+        out["w_up_scale"] = t["w_up_scale"][:, b0:b1].contiguous()
+        out["w_down_scale"] = t["w_down_scale"][:, :, b0:b1].contiguous()
+    return out

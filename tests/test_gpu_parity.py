@@ -323,3 +323,34 @@ def test_layer_step_rows(R):
     torch.cuda.synchronize()
     w = check_rows(spec, t, step.dbg, y, list(range(spec.B * R)))
     say(f"rows R={R}: {w}")
+
+
+# ------------------------------------------------------------- one GPU's tensor-parallel share of the FFN
+@pytest.mark.parametrize("n", [2, 4])
+def test_ffn_tensor_parallel_slices_sum_to_whole(n):
+    # Each of n GPUs would hold I/n intermediate rows of every expert; here the n shares run one after the other
+    # on one GPU.  Their outputs (the residual added by share 0 only) must add up to the oracle's whole FFN.
+    spec = synth.small_fp8_spec(name=f"tp{n}", B=4, seq_lens=(900, 600, 300, 1), I=512)
+    t = _layer(spec, seed=40 + n)
+    B = spec.B
+    h = (torch.randn(B, spec.D, generator=torch.Generator().manual_seed(7)) * 0.5).to(DEV)
+    ex = torch.empty(B, spec.ke, dtype=torch.int32, device=DEV)
+    g = torch.empty(B, spec.ke, dtype=torch.float32, device=DEV)
+    dl.moe_route(h, t["w_r"], t["r_bias"], spec.ke, ex, g)
+    total = torch.zeros(B, spec.D, dtype=torch.float32, device=DEV)
+    for s_ in range(n):
+        w = synth.tp_slice(t, spec, s_, n)
+        part = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
+        say(f"[gpu] moe_ffn tensor-parallel share {s_}/{n} inter={spec.I // n}")
+        dl.moe_ffn(h, ex, g, dl.mat(w["w_gate"], w["w_gate_scale"]), dl.mat(w["w_up"], w["w_up_scale"]),
+                   dl.mat(w["w_down"], w["w_down_scale"]), spec.E, spec.n_shared, part,
+                   residual=h if s_ == 0 else None)
+        total += part
+    torch.cuda.synchronize()
+    orc = oracle.LayerOracle(spec, t)
+    hh = host(h).astype(np.float64)
+    exh, gh = host(ex), host(g)
+    got = host(total).astype(np.float64)
+    for b in range(B):
+        y64 = oracle.ffn(hh[b], exh[b], gh[b].astype(np.float64), orc.expert, spec.E, spec.n_shared)
+        assert_close(f"tp{n} row {b} y-h", got[b] - hh[b], y64 - hh[b])

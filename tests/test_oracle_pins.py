@@ -460,3 +460,21 @@ def test_multirow_short_sequence_rows_are_padding():
     vis = [len(orc.row(r, stages=("sel",))["scores"]) for r in range(4)]
     assert vis == [0, 0, 1, 2]
     assert np.all(orc.row(1, stages=("sel",))["sel"] == -1)
+
+
+def test_ffn_tensor_parallel_slices_add_up():
+    # splitting every expert's intermediate rows (gate/up rows, down columns) into slices splits the FFN output
+    # into a sum: SwiGLU acts on each intermediate row on its own, so sum_s f_s(h) = f(h)
+    spec = synth.config(1)
+    t = synth.make_layer(spec, seed=3)
+    orc = oracle.LayerOracle(spec, t)
+    r = orc.row(0)
+    h, ex, g = r["h"], r["experts"], r["gates"]
+    n = 2
+    total = np.zeros_like(h)
+    for s_ in range(n):
+        sub = dict(t)
+        sub.update(synth.tp_slice(t, spec, s_, n))
+        so = oracle.LayerOracle(synth.spec_replace(spec, I=spec.I // n), sub)
+        total += oracle.ffn(h, ex, g, so.expert, spec.E, spec.n_shared) - h
+    np.testing.assert_allclose(total + h, r["y64"], rtol=0, atol=1e-12 * max(1.0, float(np.abs(r["y64"]).max())))
