@@ -428,16 +428,22 @@ __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ s
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         int sv = v[i];
+        // slots outside [0, top_k) are dropped: only an inconsistent state (never produced from consistent
+        // counts) can ask for them, and they would lie outside the row
         if (sv > T) {
             int slot = g + min(e, need);
-            so[slot] = (int32_t)(p0 + i);
-            if (ss) ss[slot] = sv;
+            if (slot >= 0 && slot < top_k) {
+                so[slot] = (int32_t)(p0 + i);
+                if (ss) ss[slot] = sv;
+            }
             g++;
         } else if (sv == T) {
             if (e < need) {
                 int slot = g + e;
-                so[slot] = (int32_t)(p0 + i);
-                if (ss) ss[slot] = sv;
+                if (slot >= 0 && slot < top_k) {
+                    so[slot] = (int32_t)(p0 + i);
+                    if (ss) ss[slot] = sv;
+                }
             }
             e++;
         }
