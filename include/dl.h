@@ -151,6 +151,25 @@ int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_
                     int32_t dim, int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* Pool-granular selection (Kiln, "What moved the number ...": a separate pool-key cache scored by its own
+ * kernel; "The decode kernels, and why they are opt-in": decode attention gathers the 512 selected pools).
+ * The pages do not say how a pool's key is formed, so the pool-key cache is an input: one int8 key per pool
+ * of `pool` consecutive positions (pool p = positions [p pool, (p + 1) pool)), paged like the position keys
+ * with page_size / pool pools per page: pool_keys int8 [n_pages, page_size / pool, dim], pool p of row b at
+ * page page_table[b, p / (page_size / pool)], entry p % (page_size / pool).  Every pool holding a cached
+ * position (ceil(seq_lens[b] / pool) of them) is scored exactly as in dl_indexer_topk; the kept pools are
+ * the first min(top_pools, pool count) under (score descending, pool ascending), in ascending order, and
+ * each is written as its `pool` positions:
+ *   sel        int32 [B, top_pools * pool]  out: positions ascending; positions >= seq_lens[b] and unused
+ *              slots are -1 (all -1 entries come after the valid ones)
+ *   pool_score int32 [B, top_pools]         out, nullable: scores of the kept pools, then 0
+ * pool = 1 is dl_indexer_topk on pool_keys.  Limits: pool a power of two <= page_size; top_pools * pool
+ * <= 65536; otherwise as dl_indexer_topk.  Workspace: dl_indexer_topk_pooled_workspace(pages, pool). */
+size_t dl_indexer_topk_pooled_workspace(const dl_pages *pages, int32_t pool);
+int dl_indexer_topk_pooled(const dl_pages *pages, int32_t pool, const int8_t *q_idx, const int8_t *pool_keys,
+                           int32_t n_heads, int32_t dim, int32_t top_pools, int32_t *sel, int32_t *pool_score,
+                           void *ws, size_t ws_bytes, void *stream);
+
 /* Multi-row decode (multi-token-prediction verification: TileRT, "Running the Generation Example with
  * Multi-Token Prediction (MTP)", depth 1 or 3; Kiln, "What did we measure that did not pay?": MTP
  * drafts verified in one step).  Each sequence b carries R = rows_per_seq query rows, the last R tokens

@@ -156,6 +156,27 @@ def topk(scores: np.ndarray, k: int) -> np.ndarray:
     return sel
 
 
+def pooled_topk(q_idx: np.ndarray, pool_keys: np.ndarray, page_table_row: np.ndarray, L: int, pool: int,
+                top_pools: int):
+    """Pool-granular selection (Kiln: a separate pool-key cache, "What moved the number ..."; decode gathers
+    the selected pools, "The decode kernels, and why they are opt-in").  Reading: pool p covers positions
+    [p pool, (p + 1) pool); its key is entry p of the pool-key cache (pool_keys [pages, page / pool, DI], paged
+    like the position keys); the ceil(L / pool) pools are scored like positions and the top pools kept under the
+    same order; each kept pool, in ascending order, contributes its positions below L.  Returns (sel positions
+    [top_pools * pool] with -1 padding, pool scores [ceil(L / pool)], kept pools [top_pools])."""
+    Lp = (L + pool - 1) // pool
+    scores = indexer_scores(q_idx, pool_keys, page_table_row, Lp)
+    pools = topk(scores, top_pools)
+    sel = np.full(top_pools * pool, -1, dtype=np.int32)
+    for k, pl in enumerate(pools):
+        if pl < 0:
+            break
+        for j in range(pool):
+            p = int(pl) * pool + j
+            sel[k * pool + j] = p if p < L else -1
+    return sel, scores, pools
+
+
 def attention(q_b: np.ndarray, kv: np.ndarray, kv_scale: Optional[np.ndarray], page_table_row: np.ndarray,
               sel: np.ndarray, sm_scale: float, Dv: int, want_p: bool = False):
     """q_b [H, Dc] (fp32 or bf16 bits); kv [P, page, Dc] uint8 codes or fp32; -> o fp64 [H, Dv]."""

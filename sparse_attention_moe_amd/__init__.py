@@ -21,7 +21,8 @@ STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE",
           -5: "DL_ERR_WORKSPACE", -6: "DL_ERR_HIP"}
 
 EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append", "dl_indexer_topk_workspace", "dl_indexer_topk",
-           "dl_indexer_topk_rows_workspace", "dl_indexer_topk_rows", "dl_layer_workspace_rows", "dl_layer_step_rows",
+           "dl_indexer_topk_rows_workspace", "dl_indexer_topk_rows", "dl_indexer_topk_pooled_workspace",
+           "dl_indexer_topk_pooled", "dl_layer_workspace_rows", "dl_layer_step_rows",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
            "dl_profile_read", "dl_probe_read"]
@@ -81,6 +82,9 @@ def load(require_gpu: bool = True):
         L.dl_pack_weights.argtypes = [C.POINTER(Mat), P, P]
         L.dl_last_error.restype = C.c_char_p
         L.dl_kv_append.argtypes = [C.POINTER(Pages), P, i32, i32, P, i32, i32, C.c_float, P, P, P, P]
+        L.dl_indexer_topk_pooled_workspace.restype = sz
+        L.dl_indexer_topk_pooled_workspace.argtypes = [C.POINTER(Pages), i32]
+        L.dl_indexer_topk_pooled.argtypes = [C.POINTER(Pages), i32, P, P, i32, i32, i32, P, P, P, sz, P]
         L.dl_indexer_topk_rows_workspace.restype = sz
         L.dl_indexer_topk_rows_workspace.argtypes = [C.POINTER(Pages), i32]
         L.dl_indexer_topk_rows.argtypes = [C.POINTER(Pages), i32, P, P, i32, i32, i32, P, P, P, sz, P]
@@ -182,6 +186,17 @@ def indexer_topk(pg: Pages, q_idx, k_pool, top_k: int, sel, sel_score=None, ws=N
     _check(L.dl_indexer_topk_rows(C.byref(pg), rows_per_seq, _ptr(q_idx), _ptr(k_pool), q_idx.shape[1],
                                   q_idx.shape[2], top_k, _ptr(sel), _ptr(sel_score), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+    return sel
+
+
+def indexer_topk_pooled(pg: Pages, pool: int, q_idx, pool_keys, top_pools: int, sel, pool_score=None, ws=None,
+                        stream=None):
+    """Pool-granular selection: sel [B, top_pools * pool] positions of the kept pools (see dl.h)."""
+    L = load()
+    if ws is None:
+        ws = workspace(L.dl_indexer_topk_pooled_workspace(C.byref(pg), pool), q_idx.device)
+    _check(L.dl_indexer_topk_pooled(C.byref(pg), pool, _ptr(q_idx), _ptr(pool_keys), q_idx.shape[1], q_idx.shape[2],
+                                    top_pools, _ptr(sel), _ptr(pool_score), _ptr(ws), ws.numel(), _stream(stream)))
     return sel
 
 

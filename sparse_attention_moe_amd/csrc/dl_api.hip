@@ -554,6 +554,35 @@ size_t dl_indexer_topk_rows_workspace(const dl_pages *pages, int32_t rows_per_se
 
 size_t dl_indexer_topk_workspace(const dl_pages *pages) { return dl_indexer_topk_rows_workspace(pages, 1); }
 
+size_t dl_indexer_topk_pooled_workspace(const dl_pages *pages, int32_t pool)
+{
+    if (!pages || pool < 1 || pool > pages->page_size || (pool & (pool - 1))) return 0;
+    Ws w(nullptr);
+    TopkWs t;
+    topk_ws_layout(w, *pages, t, 1, pool);
+    return w.used();
+}
+
+int dl_indexer_topk_pooled(const dl_pages *pages, int32_t pool, const int8_t *q_idx, const int8_t *pool_keys,
+                           int32_t n_heads, int32_t dim, int32_t top_pools, int32_t *sel, int32_t *pool_score,
+                           void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    DL_TRY(check_pages(pages));
+    if (pool < 1 || pool > pages->page_size || (pool & (pool - 1)))
+        return fail(DL_ERR_UNSUPPORTED, "pool %d (power of two, <= page size %d)", pool, pages->page_size);
+    if (!q_idx || !pool_keys || !sel) return fail(DL_ERR_NULL, "q_idx/pool_keys/sel NULL");
+    DL_TRY(check_indexer(n_heads, dim, top_pools));
+    if ((long)top_pools * pool > 65536) return fail(DL_ERR_SHAPE, "top_pools * pool %ld (<= 65536)", (long)top_pools * pool);
+    DL_TRY(check_ws(ws, ws_bytes, dl_indexer_topk_pooled_workspace(pages, pool)));
+    (void)hipGetLastError();
+    Ws w(ws);
+    TopkWs t;
+    topk_ws_layout(w, *pages, t, 1, pool);
+    return launch_indexer_topk(*pages, q_idx, pool_keys, n_heads, dim, top_pools, sel, pool_score, t,
+                               (hipStream_t)stream, 1, pool);
+}
+
 int dl_kv_append(const dl_pages *pages, const void *latent, int32_t lat_dt, int32_t d_c, const void *key,
                  int32_t key_dt, int32_t idx_dim, float key_scale, uint8_t *kv_pool, float *kv_scale, int8_t *k_pool,
                  void *stream)

@@ -47,7 +47,7 @@ struct TopkWs {
     SelState *state;   // [4, B]
     int *cnt;          // [B, nchunk, 2]
 };
-void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R = 1);
+void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R = 1, int pool = 1);
 int launch_probe_read(const void *buf, size_t bytes, size_t *bytes_read, hipStream_t s);
 int launch_kv_append(const dl_pages &pg, const void *latent, int lat_dt, int Dc, const void *key, int key_dt, int DI,
                      float key_scale, uint8_t *kv, float *kv_scale, int8_t *kp, hipStream_t s);
@@ -55,7 +55,7 @@ int launch_kv_append(const dl_pages &pg, const void *latent, int lat_dt, int Dc,
 // position seq_lens[i / R] - R + i % R and sees the positions up to its own.
 static constexpr int DL_MAX_ROWS_PER_SEQ = 4;
 int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k_pool, int HI, int DI, int top_k,
-                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s, int R = 1);
+                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s, int R = 1, int pool = 1);
 
 // ------------------------------------------------------------- GEMV engine
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };

@@ -34,10 +34,13 @@ static constexpr int SEL_CHUNK = 4096;            // 256 threads x 16 positions
 // Rows and sequences: with R query rows per sequence (multi-row decode), row i belongs to sequence i / R and
 // is the token at position seq_lens[i / R] - R + i % R, so it sees the positions before and including its own
 // (causal among the R rows).  R = 1 is ordinary decode.
-__device__ __forceinline__ int row_len(const int32_t *seq_lens, int row, int R)
+// With pool > 1 (pool-granular selection) the scored and selected items are pools of `pool` consecutive
+// positions, keyed by a separate pool-key cache; a row's length is then counted in pools (the last may be
+// partial).
+__device__ __forceinline__ int row_len(const int32_t *seq_lens, int row, int R, int pool = 1)
 {
     const int L = seq_lens[row / R] - (R - 1 - row % R);
-    return L > 0 ? L : 0;
+    return L > 0 ? (L + pool - 1) / pool : 0;
 }
 
 __device__ __forceinline__ int bin1_of(int s)
@@ -148,14 +151,14 @@ __device__ SelState advance(const SelState prev, const unsigned *gh, int top_k, 
 }
 
 // Per-row initial selection state; clears the histograms of all passes.
-__global__ void k_sel_init(const int32_t *seq_lens, int R, int B, int top_k, unsigned *hist1, unsigned *hist2,
-                           SelState *st)
+__global__ void k_sel_init(const int32_t *seq_lens, int R, int pool, int B, int top_k, unsigned *hist1,
+                           unsigned *hist2, SelState *st)
 {
     const int b = blockIdx.x;
     for (int i = threadIdx.x; i < NB1; i += blockDim.x) hist1[(long)b * NB1 + i] = 0;
     for (int i = threadIdx.x; i < 2 * NB2; i += blockDim.x) hist2[(long)b * 2 * NB2 + i] = 0;
     if (threadIdx.x == 0) {
-        int L = row_len(seq_lens, b, R);
+        int L = row_len(seq_lens, b, R, pool);
         SelState s;
         s.n_sel = min(L, top_k);
         if (L <= top_k) {  // keep everything: every score (>= 0) is above T = -1
@@ -174,13 +177,15 @@ __global__ void k_sel_init(const int32_t *seq_lens, int R, int B, int top_k, uns
 template <int NHG, int KCH, int RW>
 __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ q_idx, const int8_t *__restrict__ k_pool,
                                                      const int32_t *__restrict__ page_table,
-                                                     const int32_t *__restrict__ seq_lens, int max_pages, int ps_shift,
-                                                     int HI, int DI, int32_t *__restrict__ scores, long Lmax,
-                                                     unsigned *__restrict__ hist1)
+                                                     const int32_t *__restrict__ seq_lens, int pool, int max_pages,
+                                                     int ps_shift, int HI, int DI, int32_t *__restrict__ scores,
+                                                     long Lmax, unsigned *__restrict__ hist1)
 {
     __shared__ unsigned s_hist[RW][NB1];
     const int sq = blockIdx.y;
-    const int L = seq_lens[sq];  // positions of the sequence; row r sees the first L - (RW - 1 - r)
+    // items (positions, or pools of `pool` positions) of the sequence; row r sees the items of its first
+    // seq_lens - (RW - 1 - r) positions
+    const int L = row_len(seq_lens, sq * RW + RW - 1, RW, pool);
     const long blk0 = (long)blockIdx.x * SCORE_POS_PER_BLOCK;
     if (blk0 >= L) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
         const long pos = g0 + lane;
 #pragma unroll
         for (int r = 0; r < RW; r++) {
-            if (pos < L - (RW - 1 - r)) {
+            if (pos < row_len(seq_lens, sq * RW + r, RW, pool)) {
                 scores[((long)sq * RW + r) * Lmax + pos] = mine[r];
                 atomicAdd(&s_hist[r][bin1_of(mine[r])], 1u);
             }
@@ -294,14 +299,14 @@ __device__ __forceinline__ void load16(const int32_t *sc, long p0, int L, int v[
 // inside the new [lo, hi] with 4,096 bins into histogram PASS + 1.
 template <int PASS>
 __global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ scores, long Lmax,
-                                                    const int32_t *__restrict__ seq_lens, int R, int top_k,
+                                                    const int32_t *__restrict__ seq_lens, int R, int pool, int top_k,
                                                     const unsigned *__restrict__ hist_in, unsigned *__restrict__ hist_out,
                                                     SelState *__restrict__ st, int B)
 {
     __shared__ unsigned s_hist[NB2 > NB1 ? NB2 : NB1];
     __shared__ int s_tmp[260];
     const int b = blockIdx.y;
-    const int L = row_len(seq_lens, b, R);
+    const int L = row_len(seq_lens, b, R, pool);
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
     if (c0 >= L && blockIdx.x != 0) return;
     const int tid = threadIdx.x;
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ 
 
 // Per chunk: how many scores are > T and == T.
 __global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ scores, long Lmax,
-                                                   const int32_t *__restrict__ seq_lens, int R, int top_k,
+                                                   const int32_t *__restrict__ seq_lens, int R, int pool, int top_k,
                                                    const unsigned *__restrict__ hist3, SelState *__restrict__ st, int B,
                                                    int nchunk, int *__restrict__ cnt)
 {
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ s
     __shared__ int s_tmp[260];
     __shared__ int s_red[2][4];
     const int b = blockIdx.y;
-    const int L = row_len(seq_lens, b, R);
+    const int L = row_len(seq_lens, b, R, pool);
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
     if (c0 >= L && blockIdx.x != 0) return;
     const int tid = threadIdx.x;
@@ -371,23 +376,37 @@ __global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ s
 
 // Ordered compaction of the kept positions of one chunk.
 __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ scores, long Lmax,
-                                                   const int32_t *__restrict__ seq_lens, int R, const SelState *__restrict__ st,
+                                                   const int32_t *__restrict__ seq_lens, int R, int pool, const SelState *__restrict__ st,
                                                    int nchunk, const int *__restrict__ cnt, int top_k,
                                                    int32_t *__restrict__ sel, int32_t *__restrict__ sel_score)
 {
     __shared__ int s_w[2][4];
     __shared__ int s_base[2];
     const int b = blockIdx.y;
-    const int L = row_len(seq_lens, b, R);
+    const int L = row_len(seq_lens, b, R, pool);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const SelState s = st[3L * gridDim.y + b];
-    int32_t *so = sel + (long)b * top_k;
+    // pool > 1: slot k holds positions [k pool, (k + 1) pool) of the output row (the kept pool's positions,
+    // those at or past the row's last position written as -1); sel_score holds one score per slot
+    int32_t *so = sel + (long)b * top_k * pool;
     int32_t *ss = sel_score ? sel_score + (long)b * top_k : nullptr;
-    if (blockIdx.x == 0)  // padding of the unused slots
-        for (int i = s.n_sel + tid; i < top_k; i += 256) {
-            so[i] = -1;
-            if (ss) ss[i] = 0;
+    const int plen = pool > 1 ? row_len(seq_lens, b, R) : 0;  // positions the row sees
+    if (blockIdx.x == 0) {  // padding of the unused slots
+        for (int i = s.n_sel * pool + tid; i < top_k * pool; i += 256) so[i] = -1;
+        if (ss)
+            for (int i = s.n_sel + tid; i < top_k; i += 256) ss[i] = 0;
+    }
+    auto put = [&](int slot, int item, int score) {
+        if (pool == 1) {
+            so[slot] = item;
+        } else {
+            for (int j = 0; j < pool; j++) {
+                const int p = item * pool + j;
+                so[slot * pool + j] = p < plen ? p : -1;
+            }
         }
+        if (ss) ss[slot] = score;
+    };
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
     if (c0 >= L) return;
     const int T = s.lo, need = s.need;
@@ -432,18 +451,12 @@ __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ s
         // counts) can ask for them, and they would lie outside the row
         if (sv > T) {
             int slot = g + min(e, need);
-            if (slot >= 0 && slot < top_k) {
-                so[slot] = (int32_t)(p0 + i);
-                if (ss) ss[slot] = sv;
-            }
+            if (slot >= 0 && slot < top_k) put(slot, (int)(p0 + i), sv);
             g++;
         } else if (sv == T) {
             if (e < need) {
                 int slot = g + e;
-                if (slot >= 0 && slot < top_k) {
-                    so[slot] = (int32_t)(p0 + i);
-                    if (ss) ss[slot] = sv;
-                }
+                if (slot >= 0 && slot < top_k) put(slot, (int)(p0 + i), sv);
             }
             e++;
         }
@@ -453,9 +466,9 @@ __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ s
 // ------------------------------------------------------------------ host side
 static int max_len(const dl_pages &pg) { return pg.max_pages_per_seq * pg.page_size; }
 
-void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R)
+void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R, int pool)
 {
-    const long B = (long)pg.batch * R, Lmax = max_len(pg);  // one selection per row
+    const long B = (long)pg.batch * R, Lmax = max_len(pg) / pool;  // one selection per row, over items
     const long nchunk = (Lmax + SEL_CHUNK - 1) / SEL_CHUNK;
     t.scores = w.take<int32_t>(B * Lmax);
     t.hist1 = w.take<unsigned>(B * NB1);
@@ -466,29 +479,32 @@ void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R)
 
 template <int NHG, int KCH>
 static void launch_score(dim3 g, hipStream_t s, const int8_t *q, const int8_t *kp, const dl_pages &pg, int ps_shift,
-                         int HI, int DI, const TopkWs &t, long Lmax, int R)
+                         int HI, int DI, const TopkWs &t, long Lmax, int R, int pool)
 {
 #define DL_SCORE_R(R_)                                                                                              \
     if (R == R_)                                                                                                    \
         hipLaunchKernelGGL((k_index_score<NHG, KCH, R_>), g, dim3(256), 0, s, q, kp, pg.page_table, pg.seq_lens,   \
-                           pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax, t.hist1);
+                           pool, pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax, t.hist1);
     DL_SCORE_R(1) DL_SCORE_R(2) DL_SCORE_R(3) DL_SCORE_R(4)
 #undef DL_SCORE_R
 }
 
 int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k_pool, int HI, int DI, int top_k,
-                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s, int R)
+                        int32_t *sel, int32_t *sel_score, const TopkWs &t, hipStream_t s, int R, int pool)
 {
     if (R < 1 || R > DL_MAX_ROWS_PER_SEQ) return fail(DL_ERR_UNSUPPORTED, "rows per sequence %d (1..%d)", R, DL_MAX_ROWS_PER_SEQ);
+    if (pool < 1 || pool > pg.page_size || (pool & (pool - 1))) return fail(DL_ERR_UNSUPPORTED, "pool %d", pool);
     const int B = pg.batch * R;  // rows
-    const long Lmax = max_len(pg);
-    const int ps_shift = __builtin_ctz((unsigned)pg.page_size);
+    const long Lmax = max_len(pg) / pool;  // items per row
+    // the key cache holds page_size / pool items per page
+    const int ps_shift = __builtin_ctz((unsigned)(pg.page_size / pool));
     const int nchunk = (int)((Lmax + SEL_CHUNK - 1) / SEL_CHUNK);
-    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, pg.seq_lens, R, B, top_k, t.hist1, t.hist2, t.state);
+    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, pg.seq_lens, R, pool, B, top_k, t.hist1, t.hist2,
+                       t.state);
     dim3 gs((unsigned)((Lmax + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK), pg.batch);
     const int nhg = (HI + 15) / 16, kch = (DI + 63) / 64;
 #define DL_SCORE_CASE(H_, K_) \
-    if (nhg == H_ && kch == K_) launch_score<H_, K_>(gs, s, q_idx, k_pool, pg, ps_shift, HI, DI, t, Lmax, R); else
+    if (nhg == H_ && kch == K_) launch_score<H_, K_>(gs, s, q_idx, k_pool, pg, ps_shift, HI, DI, t, Lmax, R, pool); else
     DL_SCORE_CASE(1, 1) DL_SCORE_CASE(1, 2) DL_SCORE_CASE(1, 3) DL_SCORE_CASE(1, 4)
     DL_SCORE_CASE(2, 1) DL_SCORE_CASE(2, 2) DL_SCORE_CASE(2, 3) DL_SCORE_CASE(2, 4)
     DL_SCORE_CASE(3, 1) DL_SCORE_CASE(3, 2) DL_SCORE_CASE(3, 3) DL_SCORE_CASE(3, 4)
@@ -499,14 +515,14 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     // 31-bit scores: pass 1 leaves a range of at most 2^23 values; each refinement takes 12 bits, so the
     // state after histogram 3 is always final.
     unsigned *h2 = t.hist2, *h3 = t.hist2 + (long)B * NB2;
-    hipLaunchKernelGGL((k_sel_refine<1>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, top_k, t.hist1, h2,
+    hipLaunchKernelGGL((k_sel_refine<1>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k, t.hist1,
+                       h2, t.state, B);
+    hipLaunchKernelGGL((k_sel_refine<2>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k, h2, h3,
                        t.state, B);
-    hipLaunchKernelGGL((k_sel_refine<2>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, top_k, h2, h3,
-                       t.state, B);
-    hipLaunchKernelGGL(k_sel_count, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, top_k, h3, t.state, B,
+    hipLaunchKernelGGL(k_sel_count, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k, h3, t.state, B,
                        nchunk, t.cnt);
-    hipLaunchKernelGGL(k_sel_write, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, t.state, nchunk, t.cnt,
-                       top_k, sel, sel_score);
+    hipLaunchKernelGGL(k_sel_write, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, t.state, nchunk,
+                       t.cnt, top_k, sel, sel_score);
     return hip_check("indexer_topk");
 }
 

@@ -60,6 +60,7 @@ class LayerSpec:
     dup_router_rows: bool = False  # make expert 1 a copy of expert 0 (exact router ties)
     sm_scale: Optional[float] = None     # None -> 1/sqrt(Dc)
     R: int = 1                  # query rows per sequence (multi-row decode); per-row tensors have B * R rows
+    pool: int = 1               # >1: also a pool-key cache, one indexer key per pool of `pool` positions
 
     @property
     def wo_in(self) -> int:
@@ -181,6 +182,9 @@ def make_layer(spec: LayerSpec, seed: int = 0, device="cpu", instance: int = 0,
     out["q"] = _randn((rows, spec.H, spec.Dc), dev, seed, instance, "q").to(act_dt)
     out["q_idx"] = _int8_uniform((rows, spec.HI, spec.DI), dev, seed, instance, "q_idx", spec.key_values)
     out["k_pool"] = _int8_uniform((n_pages, ps, spec.DI), dev, seed, instance, "k_pool", spec.key_values)
+    if spec.pool > 1:
+        out["pool_keys"] = _int8_uniform((n_pages, ps // spec.pool, spec.DI), dev, seed, instance, "pool_keys",
+                                         spec.key_values)
     lat = _randn((n_pages, ps, spec.Dc), dev, seed, instance, "kv")
     if spec.fp8:
         codes, sc = quant_fp8_blocks(lat.reshape(n_pages * ps, 1, spec.Dc), 1, 128)

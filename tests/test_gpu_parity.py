@@ -354,3 +354,26 @@ def test_ffn_tensor_parallel_slices_sum_to_whole(n):
     for b in range(B):
         y64 = oracle.ffn(hh[b], exh[b], gh[b].astype(np.float64), orc.expert, spec.E, spec.n_shared)
         assert_close(f"tp{n} row {b} y-h", got[b] - hh[b], y64 - hh[b])
+
+
+# ------------------------------------------------------------- pool-granular selection
+@pytest.mark.parametrize("pool", [2, 4, 16])
+def test_indexer_pooled_bit_exact(pool):
+    top_pools = 512 // pool
+    spec = synth.spec_replace(synth.small_fp8_spec(name=f"pool{pool}", seq_lens=(9001, 3, 0, 4096, 777), topk=512),
+                              pool=pool)
+    t = _layer(spec, seed=50 + pool, weights=False)
+    B = spec.B
+    sel = torch.empty(B, top_pools * pool, dtype=torch.int32, device=DEV)
+    ps = torch.empty(B, top_pools, dtype=torch.int32, device=DEV)
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+    say(f"[gpu] indexer_topk_pooled pool={pool} top_pools={top_pools} lens={spec.seq_lens}")
+    dl.indexer_topk_pooled(pg, pool, t["q_idx"], t["pool_keys"], top_pools, sel, ps)
+    torch.cuda.synchronize()
+    sel, ps = host(sel), host(ps)
+    qh, pth, pkh = host(t["q_idx"]), host(t["page_table"]), host(t["pool_keys"])
+    for b in range(B):
+        want, sc, pools = oracle.pooled_topk(qh[b], pkh, pth[b], spec.seq_lens[b], pool, top_pools)
+        assert np.array_equal(sel[b], want), f"row {b}: first diff at {np.nonzero(sel[b] != want)[0][:5]}"
+        n = int((pools >= 0).sum())
+        assert np.array_equal(ps[b][:n], sc[pools[:n]]) and np.all(ps[b][n:] == 0)

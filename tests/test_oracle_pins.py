@@ -478,3 +478,25 @@ def test_ffn_tensor_parallel_slices_add_up():
         so = oracle.LayerOracle(synth.spec_replace(spec, I=spec.I // n), sub)
         total += oracle.ffn(h, ex, g, so.expert, spec.E, spec.n_shared) - h
     np.testing.assert_allclose(total + h, r["y64"], rtol=0, atol=1e-12 * max(1.0, float(np.abs(r["y64"]).max())))
+
+
+# ------------------------------------------------------------- pool-granular selection
+def test_pooled_selection_pool1_is_per_position_and_expansion():
+    spec = synth.spec_replace(synth.config(1), pool=4, seq_lens=(1001,), topk=64)
+    t = synth.make_layer(spec, seed=11)
+    q, pt = synth.to_numpy(t["q_idx"])[0], synth.to_numpy(t["page_table"])[0]
+    kp = synth.to_numpy(t["k_pool"])
+    # pool = 1 over the position keys is exactly the per-position selection
+    sel1, _, _ = oracle.pooled_topk(q, kp, pt, 1001, 1, 64)
+    assert np.array_equal(sel1, oracle.topk(oracle.indexer_scores(q, kp, pt, 1001), 64))
+    # pool = 4: 251 pools (the last holds one position); the kept pools are the top ones by (score, pool) found by
+    # plain sorting, expanded to their positions below L, ascending, -1 after
+    pk = synth.to_numpy(t["pool_keys"])
+    sel, sc, pools = oracle.pooled_topk(q, pk, pt, 1001, 4, 40)
+    assert sc.size == 251
+    want = sorted(sorted(range(251), key=lambda p: (-int(sc[p]), p))[:40])
+    assert list(pools) == want
+    valid = sel[sel >= 0]
+    assert np.all(np.diff(valid) > 0) and np.all(sel[valid.size:] == -1) and valid.max() < 1001
+    assert set(valid // 4) == set(want)
+    assert valid.size == 40 * 4 - (3 if 250 in want else 0)
