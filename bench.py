@@ -34,7 +34,8 @@ EXPERT_BYTES_DOWN = lambda s: s.D * s.I + (s.D // 128) * (s.I // 128) * 4
 
 def algorithmic_bytes(spec, lens, n_touched: int) -> dict:
     """Bytes the method must read per step (weights and caches once; activations are negligible)."""
-    keys = sum(int(l) for l in lens) * spec.DI
+    pool = getattr(spec, "pool", 1)  # > 1: one indexer key per pool of `pool` positions
+    keys = sum((int(l) + pool - 1) // pool for l in lens) * spec.DI
     nb = (spec.Dc + 127) // 128
     R = getattr(spec, "R", 1)  # query rows per sequence: each row keeps its own positions (up to its own)
     kv = sum(min(max(0, int(l) - (R - 1 - r)), spec.topk) for l in lens for r in range(R)) * (spec.Dc + 4 * nb)
@@ -122,7 +123,7 @@ def cpu_baseline(spec, t, rows):
     cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
     orc = oracle.LayerOracle(spec, t)
     for b in rows:  # host copies of the caches and the touched experts are made before timing
-        _ = orc.a("k_pool"), orc.a("kv"), orc.a("kv_scale")
+        _ = orc.a("k_pool" if getattr(spec, "pool", 1) == 1 else "pool_keys"), orc.a("kv"), orc.a("kv_scale")
     t0 = time.perf_counter()
     for b in rows:
         orc.row(b)
@@ -228,6 +229,9 @@ def main():
                          "every token, tensor-parallel expert slice of inter/8 rows); the exchanges are not run")
     ap.add_argument("--rows-per-seq", type=int, default=1,
                     help="query rows per sequence (multi-row decode, e.g. MTP verification); 1 = ordinary decode")
+    ap.add_argument("--pool", type=int, default=1,
+                    help="pool-granular selection: score one key per pool of this many positions and keep top_k/pool "
+                         "pools; 1 = per-position selection")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device (counter calibration)")
     args = ap.parse_args()
@@ -239,6 +243,8 @@ def main():
         return share_tp8(args, spec)
     if args.rows_per_seq != 1:
         spec = synth.spec_replace(spec, R=args.rows_per_seq, name=f"{spec.name}-rows{args.rows_per_seq}")
+    if args.pool != 1:
+        spec = synth.spec_replace(spec, pool=args.pool, name=f"{spec.name}-pool{args.pool}")
     dev = "cuda"
     insts, steps_obj = [], []
     t0 = time.perf_counter()
@@ -310,7 +316,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "batch": spec.B, "context": int(max(spec.seq_lens)), "hidden": spec.D,
                    "heads": spec.H, "latent": spec.Dc, "top_k": spec.topk, "experts": f"{spec.E}+{spec.n_shared}",
-                   "expert_top_k": spec.ke, "inter": spec.I, "rows_per_seq": spec.R, "instances_rotated": n},
+                   "expert_top_k": spec.ke, "inter": spec.I, "rows_per_seq": spec.R, "pool": spec.pool,
+                   "instances_rotated": n},
         "tokens_per_s_per_layer": round(steps_per_s * spec.B * spec.R, 1),
         "step_hbm": {"algorithmic_bytes": int(avg_bytes["total"]), "achieved_gbs": round(step_gbs, 1),
                      "peak_gbs": HBM_PEAK_GBS, "frac": round(step_gbs / HBM_PEAK_GBS, 4),

@@ -296,6 +296,14 @@ int dl_layer_step(const dl_layer_desc *desc, const dl_layer_io *io, void *ws, si
 size_t dl_layer_workspace_rows(const dl_layer_desc *desc, const dl_pages *pages, int32_t rows_per_seq);
 int dl_layer_step_rows(const dl_layer_desc *desc, const dl_layer_io *io, int32_t rows_per_seq, void *ws,
                        size_t ws_bytes, void *stream);
+/* The step with pool-granular selection (as dl_indexer_topk_pooled): io->k_pool is the pool-key cache
+ * [n_pages, page_size / pool, idx_dim]; desc->top_k counts positions and must be a multiple of pool; the
+ * top_k / pool best pools are kept and expanded to their positions, which attention then reads.  pool = 1
+ * is dl_layer_step.  Limits: pool a power of two <= page_size; as dl_layer_step otherwise (one row per
+ * sequence).  Workspace: dl_layer_workspace_pooled(desc, pages, pool); 0 for an unsupported pool. */
+size_t dl_layer_workspace_pooled(const dl_layer_desc *desc, const dl_pages *pages, int32_t pool);
+int dl_layer_step_pooled(const dl_layer_desc *desc, const dl_layer_io *io, int32_t pool, void *ws, size_t ws_bytes,
+                         void *stream);
 
 /* ---------------------------------------------------------------- measurement
  * When enabled, every dl_layer_step records a HIP event on its stream at each phase boundary:

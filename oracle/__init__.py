@@ -336,9 +336,13 @@ class LayerOracle:
         L = max(0, int(self.a("seq_lens")[seq]) - (R - 1 - rr))
         pt = self.a("page_table")[seq]
         r: Dict[str, np.ndarray] = {}
-        scores = indexer_scores(self.a("q_idx")[b], self.a("k_pool"), pt, L)
-        r["scores"] = scores
-        r["sel"] = topk(scores, sp.topk)
+        pool = getattr(sp, "pool", 1)
+        if pool > 1:  # pool-granular selection: top_k positions are top_k / pool whole pools
+            r["sel"], r["scores"], r["pools"] = pooled_topk(self.a("q_idx")[b], self.a("pool_keys"), pt, L, pool,
+                                                            sp.topk // pool)
+        else:
+            r["scores"] = indexer_scores(self.a("q_idx")[b], self.a("k_pool"), pt, L)
+            r["sel"] = topk(r["scores"], sp.topk)
         if "o" not in stages:
             return r
         r["o"] = attention(self.a("q")[b], self.a("kv"), self.a("kv_scale"), pt, r["sel"], sp.scale, sp.Dv)

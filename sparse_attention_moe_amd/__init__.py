@@ -23,6 +23,7 @@ STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE",
 EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append", "dl_indexer_topk_workspace", "dl_indexer_topk",
            "dl_indexer_topk_rows_workspace", "dl_indexer_topk_rows", "dl_indexer_topk_pooled_workspace",
            "dl_indexer_topk_pooled", "dl_layer_workspace_rows", "dl_layer_step_rows",
+           "dl_layer_workspace_pooled", "dl_layer_step_pooled",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
            "dl_profile_read", "dl_probe_read"]
@@ -91,6 +92,9 @@ def load(require_gpu: bool = True):
         L.dl_layer_workspace_rows.restype = sz
         L.dl_layer_workspace_rows.argtypes = [C.POINTER(LayerDesc), C.POINTER(Pages), i32]
         L.dl_layer_step_rows.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), i32, P, sz, P]
+        L.dl_layer_workspace_pooled.restype = sz
+        L.dl_layer_workspace_pooled.argtypes = [C.POINTER(LayerDesc), C.POINTER(Pages), i32]
+        L.dl_layer_step_pooled.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), i32, P, sz, P]
         L.dl_indexer_topk_workspace.restype = sz
         L.dl_indexer_topk_workspace.argtypes = [C.POINTER(Pages)]
         L.dl_indexer_topk.argtypes = [C.POINTER(Pages), P, P, i32, i32, i32, P, P, P, sz, P]
@@ -275,6 +279,9 @@ class LayerStep:
         self.spec, self.t = spec, t
         dev = t["x"].device
         self.R = getattr(spec, "R", 1)
+        self.pool = getattr(spec, "pool", 1)  # > 1: pool-granular selection over t["pool_keys"]
+        if self.R > 1 and self.pool > 1:
+            raise ValueError("multi-row decode with pool-granular selection has no entry point")
         B = spec.B * self.R  # rows
         self.keep = []
         self.pg = pages(t["seq_lens"], t["page_table"], spec.page_size)
@@ -309,6 +316,8 @@ class LayerStep:
         io.pages = self.pg
         io.x, io.q, io.q_idx = _ptr(t["x"]), _ptr(t["q"]), _ptr(t["q_idx"])
         io.kv_pool, io.kv_scale, io.k_pool = _ptr(t["kv"]), _ptr(t.get("kv_scale")), _ptr(t["k_pool"])
+        if self.pool > 1:
+            io.k_pool = _ptr(t["pool_keys"])
         io.y = _ptr(self.y)
         self.dbg = {}
         if debug:
@@ -321,13 +330,23 @@ class LayerStep:
             for k, v in self.dbg.items():
                 setattr(io, k, _ptr(v))
         self.io = io
-        self.ws = workspace(L.dl_layer_workspace_rows(C.byref(d), C.byref(self.pg), self.R), dev)
+        if self.pool > 1:
+            n = L.dl_layer_workspace_pooled(C.byref(d), C.byref(self.pg), self.pool)
+        else:
+            n = L.dl_layer_workspace_rows(C.byref(d), C.byref(self.pg), self.R)
+        if n == 0:
+            raise ValueError(f"layer workspace: unsupported shape (R={self.R}, pool={self.pool})")
+        self.ws = workspace(n, dev)
 
     def mat(self, name: str) -> Mat:
         w, sc, lay = self.w[name]
         return mat(w, sc, lay)
 
     def __call__(self, stream=None):
-        _check(load().dl_layer_step_rows(C.byref(self.desc), C.byref(self.io), self.R, _ptr(self.ws), self.ws.numel(),
-                                         _stream(stream)))
+        if self.pool > 1:
+            _check(load().dl_layer_step_pooled(C.byref(self.desc), C.byref(self.io), self.pool, _ptr(self.ws),
+                                               self.ws.numel(), _stream(stream)))
+        else:
+            _check(load().dl_layer_step_rows(C.byref(self.desc), C.byref(self.io), self.R, _ptr(self.ws),
+                                             self.ws.numel(), _stream(stream)))
         return self.y

@@ -437,10 +437,10 @@ struct LayerWs {
 };
 
 static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, const dl_layer_io *io, LayerWs &L,
-                            int R = 1)
+                            int R = 1, int pool = 1)
 {
     const int B = pg->batch * R;  // rows
-    topk_ws_layout(w, *pg, L.topk, R);
+    topk_ws_layout(w, *pg, L.topk, R, pool);
     L.sel = (io && io->sel) ? io->sel : w.take<int32_t>((long)B * d->top_k);
     L.o = (io && io->o) ? io->o : w.take<float>((long)B * d->n_heads * d->d_v);
     attn_ws_layout(w, B, d->n_heads, d->d_v, d->top_k, d->w_uv.w ? &d->w_uv : nullptr, nullptr, L.attn);
@@ -730,47 +730,65 @@ static int check_layer(const dl_layer_desc *d, const dl_pages *pg, int R = 1)
     return DL_OK;
 }
 
-size_t dl_layer_workspace_rows(const dl_layer_desc *desc, const dl_pages *pages, int32_t rows_per_seq)
+static bool pool_ok(const dl_pages *pg, int pool)
 {
-    if (!desc || !pages || rows_per_seq < 1 || rows_per_seq > DL_MAX_ROWS_PER_SEQ) return 0;
+    return pool >= 1 && pool <= pg->page_size && !(pool & (pool - 1));
+}
+
+// Workspace of the step with R rows per sequence and selection by pools of `pool` positions.
+static size_t layer_workspace(const dl_layer_desc *desc, const dl_pages *pages, int R, int pool)
+{
+    if (!desc || !pages || R < 1 || R > DL_MAX_ROWS_PER_SEQ || !pool_ok(pages, pool)) return 0;
     Ws w(nullptr);
     LayerWs L;
-    layer_ws_layout(w, desc, pages, nullptr, L, rows_per_seq);
+    layer_ws_layout(w, desc, pages, nullptr, L, R, pool);
     return w.used();
+}
+
+size_t dl_layer_workspace_rows(const dl_layer_desc *desc, const dl_pages *pages, int32_t rows_per_seq)
+{
+    return layer_workspace(desc, pages, rows_per_seq, 1);
 }
 
 size_t dl_layer_workspace(const dl_layer_desc *desc, const dl_pages *pages)
 {
-    return dl_layer_workspace_rows(desc, pages, 1);
+    return layer_workspace(desc, pages, 1, 1);
 }
 
-int dl_layer_step_rows(const dl_layer_desc *d, const dl_layer_io *io, int32_t rows_per_seq, void *ws, size_t ws_bytes,
-                       void *stream)
+size_t dl_layer_workspace_pooled(const dl_layer_desc *desc, const dl_pages *pages, int32_t pool)
+{
+    return layer_workspace(desc, pages, 1, pool);
+}
+
+static int layer_step(const dl_layer_desc *d, const dl_layer_io *io, int R, int pool, void *ws, size_t ws_bytes,
+                      void *stream)
 {
     g_err[0] = 0;
     if (!io) return fail(DL_ERR_NULL, "io NULL");
-    const int R = rows_per_seq;
     if (R < 1 || R > DL_MAX_ROWS_PER_SEQ) return fail(DL_ERR_UNSUPPORTED, "rows per sequence %d (1..%d)", R, DL_MAX_ROWS_PER_SEQ);
     DL_TRY(check_layer(d, &io->pages, R));
+    if (!pool_ok(&io->pages, pool))
+        return fail(DL_ERR_UNSUPPORTED, "pool %d (power of two, <= page size %d)", pool, io->pages.page_size);
+    if (d->top_k % pool) return fail(DL_ERR_SHAPE, "top_k %d is not a multiple of pool %d", d->top_k, pool);
     if (d->kv_dt == DL_FP8_E4M3 && !io->kv_scale) return fail(DL_ERR_NULL, "FP8 KV needs kv_scale");
     if (d->kv_dt == DL_F32 && io->kv_scale) return fail(DL_ERR_DTYPE, "fp32 KV takes no kv_scale");
     if (!io->x || !io->q || !io->q_idx || !io->kv_pool || !io->k_pool || !io->y) return fail(DL_ERR_NULL, "io tensor NULL");
-    DL_TRY(check_ws(ws, ws_bytes, dl_layer_workspace_rows(d, &io->pages, R)));
+    DL_TRY(check_ws(ws, ws_bytes, layer_workspace(d, &io->pages, R, pool)));
     (void)hipGetLastError();
     hipStream_t s = (hipStream_t)stream;
     const dl_pages &pg = io->pages;
     const int B = pg.batch * R;  // rows: every row is a token of the step from here on
     Ws w(ws);
     LayerWs L;
-    layer_ws_layout(w, d, &pg, io, L, R);
+    layer_ws_layout(w, d, &pg, io, L, R, pool);
     Marks mk;
     DL_TRY(marks_begin(mk, s));
     const dl_mat *wuv = d->w_uv.w ? &d->w_uv : nullptr;
     const bool f8_ffn = d->w_gate.dtype == DL_FP8_E4M3;
     const bool fuse_route = route_plan_ok(d->n_routed, d->expert_top_k, B);
     mk.at(0);
-    DL_TRY(launch_indexer_topk(pg, io->q_idx, io->k_pool, d->idx_heads, d->idx_dim, d->top_k, L.sel, nullptr, L.topk, s,
-                               R));
+    DL_TRY(launch_indexer_topk(pg, io->q_idx, io->k_pool, d->idx_heads, d->idx_dim, d->top_k / pool, L.sel, nullptr,
+                               L.topk, s, R, pool));
     mk.at(1);
     bool h_split = false;
     DL_TRY(run_attn_proj(pg, io->q, d->q_dt, io->kv_pool, io->kv_scale, d->kv_dt, d->n_heads, d->d_c, d->d_v,
@@ -790,9 +808,21 @@ int dl_layer_step_rows(const dl_layer_desc *d, const dl_layer_io *io, int32_t ro
                    d->n_routed, d->n_shared, L.h, DL_F32, io->y, d->out_dt, L.ffn, s, mk, io->y32, fuse_route, h_split);
 }
 
+int dl_layer_step_rows(const dl_layer_desc *d, const dl_layer_io *io, int32_t rows_per_seq, void *ws, size_t ws_bytes,
+                       void *stream)
+{
+    return layer_step(d, io, rows_per_seq, 1, ws, ws_bytes, stream);
+}
+
+int dl_layer_step_pooled(const dl_layer_desc *d, const dl_layer_io *io, int32_t pool, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    return layer_step(d, io, 1, pool, ws, ws_bytes, stream);
+}
+
 int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_t ws_bytes, void *stream)
 {
-    return dl_layer_step_rows(d, io, 1, ws, ws_bytes, stream);
+    return layer_step(d, io, 1, 1, ws, ws_bytes, stream);
 }
 
 int dl_probe_read(const void *buf, size_t bytes, size_t *bytes_read, void *stream)

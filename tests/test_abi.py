@@ -122,3 +122,17 @@ def test_kv_append_rejects_bad_arguments(lib):
     for ks in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.dl_kv_append(C.byref(P), 1, F32, 576, 1, F32, 128, ks, 1, 1, 1, None) == -2, ks
     assert b"key_scale" in lib.dl_last_error()
+
+
+def test_pooled_selection_rejects_bad_pools(lib):
+    P = dl.Pages(2, 64, 4, 0x1000, 0x2000)
+    ws = C.c_void_p(0x10000)
+    for pool in (0, 3, 128):  # not a power of two, or wider than a page
+        assert lib.dl_indexer_topk_pooled_workspace(C.byref(P), pool) == 0
+        assert lib.dl_indexer_topk_pooled(C.byref(P), pool, 1, 1, 16, 128, 512, 1, None, ws, 1 << 30, None) == -4
+        assert b"pool" in lib.dl_last_error()
+        assert lib.dl_layer_workspace_pooled(C.byref(dl.LayerDesc()), C.byref(P), pool) == 0
+    assert lib.dl_indexer_topk_pooled_workspace(C.byref(P), 4) > 0
+    # top_pools * pool beyond the selection limit
+    assert lib.dl_indexer_topk_pooled(C.byref(P), 64, 1, 1, 16, 128, 2048, 1, None, ws, 1 << 30, None) == -2
+    assert lib.dl_layer_step_pooled(C.byref(dl.LayerDesc()), None, 4, ws, 1 << 30, None) == -1

@@ -377,3 +377,17 @@ def test_indexer_pooled_bit_exact(pool):
         assert np.array_equal(sel[b], want), f"row {b}: first diff at {np.nonzero(sel[b] != want)[0][:5]}"
         n = int((pools >= 0).sum())
         assert np.array_equal(ps[b][:n], sc[pools[:n]]) and np.all(ps[b][n:] == 0)
+
+
+@pytest.mark.parametrize("pool", [4, 16])
+def test_layer_step_pooled(pool):
+    # The whole step with pool-granular selection: positions come from whole pools, the rest as in dl_layer_step.
+    spec = synth.spec_replace(synth.small_fp8_spec(name=f"step-pool{pool}", seq_lens=(3001, 5, 0, 700), B=4),
+                              pool=pool)
+    t = _layer(spec, seed=60 + pool)
+    step = dl.LayerStep(spec, t, debug=True)
+    say(f"[gpu] layer_step pooled pool={pool} lens={spec.seq_lens}")
+    y = step()
+    torch.cuda.synchronize()
+    w = check_rows(spec, t, step.dbg, y, list(range(spec.B)))
+    say(f"pooled pool={pool}: {w}")
