@@ -113,25 +113,107 @@ def read_ceiling(reps: int, mib: int = 1536) -> dict:
     return out
 
 
+def null_phases(reps: int, kernels: int = 16, blocks: int = 256) -> dict:
+    """Fixed cost of the step's dependent launches: `kernels` back-to-back launches of an empty kernel
+    (dl_probe_null; the step launches 16 kernels), one workgroup per compute unit."""
+    dl.probe_null(kernels, blocks)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dl.probe_null(kernels, blocks)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    return {"kernels": kernels, "workgroups": blocks, "us_per_chain": round(us, 2),
+            "us_per_kernel": round(us / kernels, 3)}
+
+
+class Unfused:
+    """The step as its four separate entry points (dl_indexer_topk, dl_sparse_attn_decode with W_UV, W_O and the
+    residual, dl_moe_route, dl_moe_ffn) on the same tiled weights and preallocated workspaces."""
+
+    def __init__(self, spec, t, step):
+        dev = t["x"].device
+        B = spec.B
+        self.spec, self.t = spec, t
+        self.pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+        self.sel = torch.empty(B, spec.topk, dtype=torch.int32, device=dev)
+        self.h = torch.empty(B, spec.D, dtype=torch.float32, device=dev)
+        self.ex = torch.empty(B, spec.ke, dtype=torch.int32, device=dev)
+        self.g = torch.empty(B, spec.ke, dtype=torch.float32, device=dev)
+        self.y = torch.empty_like(step.y)
+        self.m = {k: step.mat(k) for k in ("w_uv", "w_o", "w_gate", "w_up", "w_down")}
+        self.keep = step  # the tiled weights live in the step object
+        import ctypes as C
+        L = dl.load()
+        self.ws_i = dl.workspace(L.dl_indexer_topk_workspace(C.byref(self.pg)), dev)
+        self.ws_a = dl.workspace(L.dl_sparse_attn_workspace(B, spec.H, spec.Dv, spec.topk, C.byref(self.m["w_uv"]),
+                                                            C.byref(self.m["w_o"])), dev)
+        self.ws_r = dl.workspace(L.dl_moe_route_workspace(B, spec.D, spec.E), dev)
+        self.ws_f = dl.workspace(L.dl_moe_ffn_workspace(B, spec.D, spec.I, spec.ke, spec.E, spec.n_shared), dev)
+
+    def __call__(self):
+        sp, t = self.spec, self.t
+        dl.indexer_topk(self.pg, t["q_idx"], t["k_pool"], sp.topk, self.sel, ws=self.ws_i)
+        dl.sparse_attn_decode(self.pg, t["q"], t["kv"], t.get("kv_scale"), sp.H, sp.Dc, sp.Dv, sp.scale, self.sel,
+                              sp.topk, self.h, w_uv=self.m["w_uv"], w_o=self.m["w_o"], residual=t["x"], ws=self.ws_a)
+        dl.moe_route(self.h, t["w_r"], t["r_bias"], sp.ke, self.ex, self.g, ws=self.ws_r)
+        dl.moe_ffn(self.h, self.ex, self.g, self.m["w_gate"], self.m["w_up"], self.m["w_down"], sp.E, sp.n_shared,
+                   self.y, residual=self.h, ws=self.ws_f)
+        return self.y
+
+
+def timed(fn_list, steps: int) -> float:
+    """Mean milliseconds per call over `steps` calls (rotating over fn_list), two events around them all."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        fn_list[i % len(fn_list)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def per_step_ms(fn_list, steps: int) -> list:
+    """Milliseconds of each of `steps` calls, one event between consecutive calls."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn_list[i % len(fn_list)]()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
 def touched(spec, experts: np.ndarray) -> int:
     return len(set(int(e) for e in experts.ravel())) + spec.n_shared
 
 
-def cpu_baseline(spec, t, rows):
-    """The oracle, as it stands, on a bounded sample: `rows` rows of one step (each row is independent)."""
+def cpu_baseline(spec, t, seconds: float):
+    """The oracle, as it stands, on a bounded sample of one step: its rows (each row of a step is independent),
+    cycled until about `seconds` of CPU work, then scaled to a whole step.  A first, untimed pass over the rows
+    makes the host copies of the caches and of the experts the rows touch."""
     import oracle
     cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
     orc = oracle.LayerOracle(spec, t)
-    for b in rows:  # host copies of the caches and the touched experts are made before timing
-        _ = orc.a("k_pool" if getattr(spec, "pool", 1) == 1 else "pool_keys"), orc.a("kv"), orc.a("kv_scale")
-    t0 = time.perf_counter()
-    for b in rows:
+    rows = spec.B * getattr(spec, "R", 1)
+    for b in range(rows):
         orc.row(b)
-    dt = time.perf_counter() - t0
-    per_step = dt / len(rows) * spec.B * getattr(spec, "R", 1)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.row(n % rows)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds or n >= 64 * rows:
+            break
+    per_step = dt / n * rows
     return {"value": 1.0 / per_step, "unit": "layer-steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} of {spec.B * getattr(spec, 'R', 1)} rows of one {spec.name} step (indexer over the full context, "
-                      f"attention, projections, router, FFN), {dt:.1f} s, scaled to a whole step"}
+            "sample": f"{n} row evaluations cycling over the {rows} rows of one {spec.name} step (indexer over the "
+                      f"full context, attention, projections, router, FFN), {dt:.1f} s, scaled to a whole step"}
 
 
 def share_tp8(args, spec, n: int = 8):
@@ -222,7 +304,7 @@ def main():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time of the oracle baseline sample")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--share", choices=["tp8"], default=None,
                     help="time one GPU's share of an 8-GPU layer instead (DP attention on one sequence, router for "
@@ -277,6 +359,17 @@ def main():
     ph, nst = dl.profile_read()
     dl.profile_enable(False)
     ph = {k: v / nst for k, v in ph.items()}
+    # timed region 3: one event between consecutive steps, for the spread of single steps
+    each = per_step_ms(steps_obj, args.steps)
+    # timed region 4: the same steps as four separate entry points
+    unfused_ms = None
+    if spec.R == 1 and spec.pool == 1:  # the separate entry points are the ordinary decode path
+        unf = [Unfused(spec, t, so) for t, so in zip(insts, steps_obj)]
+        for u in unf:
+            u()
+        unfused_ms = round(timed(unf, args.steps), 4)
+        del unf
+    nulls = null_phases(args.steps)
     # the current-token append (the step before S1; not part of the timed step): its own launches, bf16 inputs
     app_rec = None
     if spec.Dc >= 256:
@@ -319,6 +412,8 @@ def main():
                    "expert_top_k": spec.ke, "inter": spec.I, "rows_per_seq": spec.R, "pool": spec.pool,
                    "instances_rotated": n},
         "tokens_per_s_per_layer": round(steps_per_s * spec.B * spec.R, 1),
+        "ms_per_step_median": round(float(np.median(each)), 4), "ms_per_step_min": round(float(np.min(each)), 4),
+        "unfused_ms_per_step": unfused_ms, "null_phases": nulls,
         "step_hbm": {"algorithmic_bytes": int(avg_bytes["total"]), "achieved_gbs": round(step_gbs, 1),
                      "peak_gbs": HBM_PEAK_GBS, "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                      "touched_experts": round(avg_touch, 2)},
@@ -334,7 +429,7 @@ def main():
     if not args.no_read_ceiling:
         rec["read_ceiling"] = read_ceiling(args.steps)
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(spec, insts[0], list(range(args.cpu_rows)))
+        rec["cpu_baseline"] = cpu_baseline(spec, insts[0], args.cpu_seconds)
     print(json.dumps(rec), flush=True)
     if args.copy_mib:
         copy_calibration(args.copy_mib)

@@ -324,6 +324,13 @@ int dl_profile_read(double *ms_sum, int64_t *steps);
  * HBM read rate reachable for the buffer's contents.  DL_ERR_SHAPE if bytes is below one round. */
 int dl_probe_read(const void *buf, size_t bytes, size_t *bytes_read, void *stream);
 
+/* Measurement aid, not part of the step (Kiln's "null" kernel, which does no work and so exposes fixed costs:
+ * "What moved the number from 19.4 to 122.9 tokens a second?"): enqueue n_kernels launches, one after
+ * another on `stream`, of a kernel with `blocks` workgroups of 256 threads that do nothing.  Timing them
+ * with events gives the fixed cost of a dependent launch, the floor under every phase of the step.
+ * Limits 1 <= n_kernels <= 1024, 1 <= blocks <= 65536 (else DL_ERR_SHAPE). */
+int dl_probe_null(int32_t n_kernels, int32_t blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

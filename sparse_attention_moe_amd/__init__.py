@@ -26,7 +26,7 @@ EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append",
            "dl_layer_workspace_pooled", "dl_layer_step_pooled",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
-           "dl_profile_read", "dl_probe_read"]
+           "dl_profile_read", "dl_probe_read", "dl_probe_null"]
 N_PHASES = 9
 PHASES = ["indexer_topk", "attention", "projection", "router", "plan_split_h", "expert_gate_up", "split_z",
           "expert_down", "combine"]
@@ -115,6 +115,7 @@ def load(require_gpu: bool = True):
         L.dl_profile_enable.argtypes = [C.c_int]
         L.dl_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
         L.dl_probe_read.argtypes = [P, sz, C.POINTER(sz), P]
+        L.dl_probe_null.argtypes = [i32, i32, P]
         if L.dl_abi_version() != ABI_VERSION:
             raise ImportError(f"libdl ABI {L.dl_abi_version()} != {ABI_VERSION}")
         _lib = L
@@ -251,6 +252,11 @@ def probe_read(buf: torch.Tensor, stream=None) -> int:
     n = C.c_size_t(0)
     _check(L.dl_probe_read(_ptr(buf), buf.numel() * buf.element_size(), C.byref(n), _stream(stream)))
     return n.value
+
+
+def probe_null(n_kernels: int, blocks: int, stream=None):
+    """Enqueue n_kernels dependent launches of an empty kernel of `blocks` workgroups (measurement aid)."""
+    _check(load().dl_probe_null(n_kernels, blocks, _stream(stream)))
 
 
 def profile_enable(on: bool):

@@ -833,6 +833,15 @@ int dl_probe_read(const void *buf, size_t bytes, size_t *bytes_read, void *strea
     return launch_probe_read(buf, bytes, bytes_read, (hipStream_t)stream);
 }
 
+int dl_probe_null(int32_t n_kernels, int32_t blocks, void *stream)
+{
+    g_err[0] = 0;
+    if (n_kernels < 1 || n_kernels > 1024 || blocks < 1 || blocks > 65536)
+        return fail(DL_ERR_SHAPE, "probe_null: %d kernels of %d workgroups (1..1024, 1..65536)", n_kernels, blocks);
+    (void)hipGetLastError();
+    return launch_probe_null(n_kernels, blocks, (hipStream_t)stream);
+}
+
 int dl_profile_enable(int on)
 {
     g_err[0] = 0;

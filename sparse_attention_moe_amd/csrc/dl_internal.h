@@ -49,6 +49,7 @@ struct TopkWs {
 };
 void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R = 1, int pool = 1);
 int launch_probe_read(const void *buf, size_t bytes, size_t *bytes_read, hipStream_t s);
+int launch_probe_null(int n_kernels, int blocks, hipStream_t s);
 int launch_kv_append(const dl_pages &pg, const void *latent, int lat_dt, int Dc, const void *key, int key_dt, int DI,
                      float key_scale, uint8_t *kv, float *kv_scale, int8_t *kp, hipStream_t s);
 // R query rows per sequence (multi-row decode): q_idx [B*R, HI, DI], sel [B*R, top_k]; row i is the token at

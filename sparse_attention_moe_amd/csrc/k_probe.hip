@@ -1,7 +1,9 @@
-// Measurement aid, not part of the decode step: a plain streaming read of a device buffer, to measure the
-// HBM read rate the weight streams can reach for a given content (the rate depends on the bytes read).
-// Every wave reads its own contiguous range with 16-byte non-temporal loads, 16 in flight per lane, the way
-// the expert GEMV streams weights.
+// Measurement aids, not part of the decode step.
+// - A plain streaming read of a device buffer, to measure the HBM read rate the weight streams can reach for a
+//   given content (the rate depends on the bytes read).  Every wave reads its own contiguous range with 16-byte
+//   non-temporal loads, 16 in flight per lane, the way the expert GEMV streams weights.
+// - A chain of kernels that do no work (Kiln's "null" kernel, used there to expose fixed costs, "What moved the
+//   number from 19.4 to 122.9 tokens a second?"): the time of one dependent launch with nothing in it.
 #include "dl_common.h"
 #include "dl_internal.h"
 
@@ -39,6 +41,14 @@ int launch_probe_read(const void *buf, size_t bytes, size_t *bytes_read, hipStre
     hipLaunchKernelGGL(k_probe_read, dim3((unsigned)blocks), dim3(256), 0, s, (const v4i *)buf, per_wave);
     if (bytes_read) *bytes_read = (size_t)(per_wave * waves * 16);
     return hip_check("probe_read");
+}
+
+__global__ __launch_bounds__(256) void k_probe_null() {}
+
+int launch_probe_null(int n_kernels, int blocks, hipStream_t s)
+{
+    for (int i = 0; i < n_kernels; i++) hipLaunchKernelGGL(k_probe_null, dim3(blocks), dim3(256), 0, s);
+    return hip_check("probe_null");
 }
 
 }  // namespace dl

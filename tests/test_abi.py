@@ -136,3 +136,10 @@ def test_pooled_selection_rejects_bad_pools(lib):
     # top_pools * pool beyond the selection limit
     assert lib.dl_indexer_topk_pooled(C.byref(P), 64, 1, 1, 16, 128, 2048, 1, None, ws, 1 << 30, None) == -2
     assert lib.dl_layer_step_pooled(C.byref(dl.LayerDesc()), None, 4, ws, 1 << 30, None) == -1
+
+
+def test_probe_null_rejects_bad_counts(lib):
+    assert lib.dl_probe_null(0, 1, None) == -2
+    assert lib.dl_probe_null(1025, 1, None) == -2
+    assert lib.dl_probe_null(4, 0, None) == -2
+    assert lib.dl_probe_null(4, 65537, None) == -2
