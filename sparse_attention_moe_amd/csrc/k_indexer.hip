@@ -396,9 +396,17 @@ __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ s
         if (ss)
             for (int i = s.n_sel + tid; i < top_k; i += 256) ss[i] = 0;
     }
+    // pools of 4 or more positions go out as 16-byte stores when the output is 16-byte aligned
+    const bool vec = pool >= 4 && ((uintptr_t)sel & 15) == 0;
     auto put = [&](int slot, int item, int score) {
         if (pool == 1) {
             so[slot] = item;
+        } else if (vec) {
+            for (int j = 0; j < pool; j += 4) {
+                const int p = item * pool + j;
+                *(v4i *)(so + slot * pool + j) =
+                    v4i{p < plen ? p : -1, p + 1 < plen ? p + 1 : -1, p + 2 < plen ? p + 2 : -1, p + 3 < plen ? p + 3 : -1};
+            }
         } else {
             for (int j = 0; j < pool; j++) {
                 const int p = item * pool + j;

@@ -357,17 +357,19 @@ def test_ffn_tensor_parallel_slices_sum_to_whole(n):
 
 
 # ------------------------------------------------------------- pool-granular selection
-@pytest.mark.parametrize("pool", [2, 4, 16])
-def test_indexer_pooled_bit_exact(pool):
+@pytest.mark.parametrize("pool,offset", [(2, 0), (4, 0), (16, 0), (4, 1)])
+def test_indexer_pooled_bit_exact(pool, offset):
+    # offset 1: the output starts 4 bytes past a 16-byte boundary, which takes the one-position-at-a-time stores
     top_pools = 512 // pool
     spec = synth.spec_replace(synth.small_fp8_spec(name=f"pool{pool}", seq_lens=(9001, 3, 0, 4096, 777), topk=512),
                               pool=pool)
     t = _layer(spec, seed=50 + pool, weights=False)
     B = spec.B
-    sel = torch.empty(B, top_pools * pool, dtype=torch.int32, device=DEV)
+    buf = torch.empty(B * top_pools * pool + offset, dtype=torch.int32, device=DEV)
+    sel = buf[offset:].view(B, top_pools * pool)
     ps = torch.empty(B, top_pools, dtype=torch.int32, device=DEV)
     pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
-    say(f"[gpu] indexer_topk_pooled pool={pool} top_pools={top_pools} lens={spec.seq_lens}")
+    say(f"[gpu] indexer_topk_pooled pool={pool} top_pools={top_pools} offset={offset} lens={spec.seq_lens}")
     dl.indexer_topk_pooled(pg, pool, t["q_idx"], t["pool_keys"], top_pools, sel, ps)
     torch.cuda.synchronize()
     sel, ps = host(sel), host(ps)
