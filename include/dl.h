@@ -232,7 +232,9 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
  *   f_e(h) = W_down[e] (silu(W_gate[e] h) * (W_up[e] h)),  silu(g) = g / (1 + e^-g)
  *   out[b] = residual[b] + sum_{j<top_k} gates[b,j] f_{experts[b,j]}(h[b]) + sum_s f_{n_routed+s}(h[b])
  * summed in that order (residual NULL: 0).
- *   h fp32 [B, D]; experts int32 [B, top_k] (each < n_routed); gates fp32 [B, top_k];
+ *   h fp32 [B, D]; experts int32 [B, top_k] (each < n_routed, larger ids are clamped to n_routed - 1;
+ *   a negative id marks a slot whose expert is not applied here, e.g. one another GPU holds in an
+ *   expert-parallel layout: the slot adds nothing, as if its gate were 0); gates fp32 [B, top_k];
  *   w_gate, w_up: count = n_routed + n_shared, rows = inter, cols = D;
  *   w_down: count = n_routed + n_shared, rows = D, cols = inter;
  *   residual fp32 [B, D] nullable; out [B, D] in out_dt (DL_F32 or DL_BF16, rounded once, RNE).
@@ -245,6 +247,19 @@ int dl_moe_ffn(const float *h, int32_t B, int32_t D, int32_t inter, const int32_
                int32_t top_k, const dl_mat *w_gate, const dl_mat *w_up, const dl_mat *w_down, int32_t n_routed,
                int32_t n_shared, const float *residual, void *out, int32_t out_dt, void *ws, size_t ws_bytes,
                void *stream);
+
+/* One GPU's expert-parallel share of the expert FFN (the layout Kiln weighs against tensor-parallel experts in
+ * "Expert parallelism without an all-to-all"): the weight stacks hold the routed experts
+ * [expert_lo, expert_lo + n_local) followed by n_shared shared experts (count = n_local + n_shared).  experts
+ * holds the router's global ids; a pick inside the range is applied with its local index, any other pick is
+ * skipped (another GPU applies it), so summing the shares of all GPUs, with the shared experts and the residual
+ * counted on one of them, gives dl_moe_ffn of the whole layer.  Otherwise as dl_moe_ffn, except that top_k may
+ * exceed n_local.  expert_lo >= 0 (else DL_ERR_SHAPE).  Workspace: dl_moe_ffn_workspace(B, D, inter, top_k,
+ * n_local, n_shared). */
+int dl_moe_ffn_ep(const float *h, int32_t B, int32_t D, int32_t inter, const int32_t *experts, const float *gates,
+                  int32_t top_k, int32_t expert_lo, const dl_mat *w_gate, const dl_mat *w_up, const dl_mat *w_down,
+                  int32_t n_local, int32_t n_shared, const float *residual, void *out, int32_t out_dt, void *ws,
+                  size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------- the whole step
  * dl_layer_step == dl_indexer_topk -> dl_sparse_attn_decode(w_uv, w_o, residual = x) -> dl_moe_route

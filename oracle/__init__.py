@@ -245,8 +245,12 @@ def router(h: np.ndarray, w_r: np.ndarray, bias: Optional[np.ndarray], ke: int):
 def ffn(h: np.ndarray, experts: Sequence[int], gates: Sequence[float], expert_weights, n_routed: int,
         n_shared: int) -> np.ndarray:
     """Dense per-token expert loop.  expert_weights(e) -> (wg, sg, wu, su, wd, sd) numpy for expert e
-    (scales None for fp32).  Returns y fp64 [D] (unrounded)."""
-    ids = [int(e) for e in experts] + [n_routed + s for s in range(n_shared)]
+    (scales None for fp32).  Returns y fp64 [D] (unrounded): h + sum over slots of gate * expert output + the
+    shared experts.  A negative expert id marks a slot computed elsewhere (an expert held by another GPU in an
+    expert-parallel layout): it adds nothing."""
+    ids = [int(e) for e in experts if int(e) >= 0] + [n_routed + s for s in range(n_shared)]
+    if not ids:
+        return _c(h, np.float64).copy()
     uniq = sorted(set(ids))
     loc = {e: i for i, e in enumerate(uniq)}
     parts = [expert_weights(e) for e in uniq]
@@ -259,7 +263,7 @@ def ffn(h: np.ndarray, experts: Sequence[int], gates: Sequence[float], expert_we
     mg, mu, md = _mat(wg, sg, keep), _mat(wu, su, keep), _mat(wd, sd, keep)
     # local numbering: routed ids map into the compact stack; the shared experts are the last entries
     ke = len(experts)
-    lex = np.array([loc[int(e)] for e in experts], dtype=np.int32)
+    lex = np.array([loc[int(e)] if int(e) >= 0 else -1 for e in experts], dtype=np.int32)
     # place shared experts at local index n_routed_local + s by building an order where they come last
     n_loc_routed = len(uniq) - n_shared
     assert all(loc[n_routed + s] == n_loc_routed + s for s in range(n_shared))

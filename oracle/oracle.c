@@ -433,6 +433,8 @@ int o_ffn(const double *h, const int32_t *experts, const double *gates, int32_t 
     for (long d = 0; d < D; d++)
         y[d] = h[d];
     for (int j = 0; j < ke + n_shared; j++) {
+        if (j < ke && experts[j] < 0)
+            continue; /* a pair computed elsewhere (an expert held by another GPU) */
         long e = j < ke ? experts[j] : (long)n_routed + (j - ke);
         double g = j < ke ? gates[j] : 1.0;
         if (expert_apply(wg, wu, wd, e, h, D, I, f)) {

@@ -25,7 +25,7 @@ EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append",
            "dl_indexer_topk_pooled", "dl_layer_workspace_rows", "dl_layer_step_rows",
            "dl_layer_workspace_pooled", "dl_layer_step_pooled",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
-           "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
+           "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_moe_ffn_ep", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
            "dl_profile_read", "dl_probe_read", "dl_probe_null"]
 N_PHASES = 9
 PHASES = ["indexer_topk", "attention", "projection", "router", "plan_split_h", "expert_gate_up", "split_z",
@@ -109,6 +109,8 @@ def load(require_gpu: bool = True):
         L.dl_moe_ffn_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
         L.dl_moe_ffn.argtypes = [P, i32, i32, i32, P, P, i32, C.POINTER(Mat), C.POINTER(Mat), C.POINTER(Mat), i32,
                                  i32, P, P, i32, P, sz, P]
+        L.dl_moe_ffn_ep.argtypes = [P, i32, i32, i32, P, P, i32, i32, C.POINTER(Mat), C.POINTER(Mat), C.POINTER(Mat),
+                                    i32, i32, P, P, i32, P, sz, P]
         L.dl_layer_workspace.restype = sz
         L.dl_layer_workspace.argtypes = [C.POINTER(LayerDesc), C.POINTER(Pages)]
         L.dl_layer_step.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), P, sz, P]
@@ -243,6 +245,21 @@ def moe_ffn(h, experts, gates, w_gate: Mat, w_up: Mat, w_down: Mat, n_routed, n_
     _check(L.dl_moe_ffn(_ptr(h), B, D, inter, _ptr(experts), _ptr(gates), ke, C.byref(w_gate), C.byref(w_up),
                         C.byref(w_down), n_routed, n_shared, _ptr(residual), _ptr(out), _dt(out), _ptr(ws), ws.numel(),
                         _stream(stream)))
+    return out
+
+
+def moe_ffn_ep(h, experts, gates, expert_lo: int, w_gate: Mat, w_up: Mat, w_down: Mat, n_local, n_shared, out,
+               residual=None, ws=None, stream=None):
+    """dl_moe_ffn_ep: the FFN share of the experts [expert_lo, expert_lo + n_local) (+ n_shared shared experts)."""
+    L = load()
+    B, D = h.shape
+    ke = experts.shape[1]
+    inter = w_gate.rows
+    if ws is None:
+        ws = workspace(L.dl_moe_ffn_workspace(B, D, inter, ke, n_local, n_shared), h.device)
+    _check(L.dl_moe_ffn_ep(_ptr(h), B, D, inter, _ptr(experts), _ptr(gates), ke, expert_lo, C.byref(w_gate),
+                           C.byref(w_up), C.byref(w_down), n_local, n_shared, _ptr(residual), _ptr(out), _dt(out),
+                           _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

@@ -359,12 +359,12 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
 static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, const float *gates, int ke,
                    const dl_mat *wg, const dl_mat *wu, const dl_mat *wd, int E, int S, const void *resid,
                    int resid_dt, void *out, int out_dt, const FfnWs &f, hipStream_t s, const Marks &mk = Marks(),
-                   float *out32 = nullptr, bool plan_ready = false, bool h_split_ready = false)
+                   float *out32 = nullptr, bool plan_ready = false, bool h_split_ready = false, int expert_lo = -1)
 {
     const bool f8 = wg->dtype == DL_FP8_E4M3;
     const int NE = E + S;
     const long P = (long)B * (ke + S);
-    if (!plan_ready) DL_TRY(launch_plan(experts, B, ke, E, S, f.plan, s));
+    if (!plan_ready) DL_TRY(launch_plan(experts, B, ke, E, S, f.plan, s, expert_lo));
     // gate/up + SwiGLU -> Z
     GemvArgs g = mat_args(wg);
     g.w2 = (const uint8_t *)(f8 ? wu->w : nullptr);
@@ -467,13 +467,15 @@ static void layer_ws_layout(Ws &w, const dl_layer_desc *d, const dl_pages *pg, c
                   L.ffn);
 }
 
+// local: the stack holds one GPU's share of the routed experts, so a token may pick more experts than it holds
 static int check_ffn_shapes(int B, int D, int I, int ke, int E, int S, const dl_mat *wg, const dl_mat *wu,
-                            const dl_mat *wd)
+                            const dl_mat *wd, bool local = false)
 {
     if (B < 1 || D < 1 || I < 1) return fail(DL_ERR_SHAPE, "ffn B=%d D=%d I=%d", B, D, I);
     if (D % 4) return fail(DL_ERR_UNSUPPORTED, "ffn hidden size %d (multiple of 4)", D);
     if (D > 65536 || I > 16384) return fail(DL_ERR_UNSUPPORTED, "ffn D=%d (<= 65536) I=%d (<= 16384)", D, I);
-    if (ke < 1 || ke > 32 || ke > E) return fail(DL_ERR_SHAPE, "expert top_k %d of %d", ke, E);
+    if (E < 1) return fail(DL_ERR_SHAPE, "routed experts %d", E);
+    if (ke < 1 || ke > 32 || (!local && ke > E)) return fail(DL_ERR_SHAPE, "expert top_k %d of %d", ke, E);
     if (ke + S > 40) return fail(DL_ERR_UNSUPPORTED, "top_k + shared experts %d (<= 40)", ke + S);
     if (S < 0 || E > 1024 || E + S > 4096) return fail(DL_ERR_SHAPE, "experts %d + %d", E, S);
     if ((long)B * (ke + S) > 16384) return fail(DL_ERR_SHAPE, "B*(top_k+shared) > 16384");
@@ -710,6 +712,25 @@ int dl_moe_ffn(const float *h, int32_t B, int32_t D, int32_t inter, const int32_
     ffn_ws_layout(w, B, D, inter, top_k, n_routed, n_shared, w_gate->dtype == DL_FP8_E4M3, f);
     return run_ffn(h, B, D, inter, experts, gates, top_k, w_gate, w_up, w_down, n_routed, n_shared, residual, DL_F32,
                    out, out_dt, f, (hipStream_t)stream);
+}
+
+int dl_moe_ffn_ep(const float *h, int32_t B, int32_t D, int32_t inter, const int32_t *experts, const float *gates,
+                  int32_t top_k, int32_t expert_lo, const dl_mat *w_gate, const dl_mat *w_up, const dl_mat *w_down,
+                  int32_t n_local, int32_t n_shared, const float *residual, void *out, int32_t out_dt, void *ws,
+                  size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (!h || !experts || !gates || !out) return fail(DL_ERR_NULL, "h/experts/gates/out NULL");
+    if (expert_lo < 0) return fail(DL_ERR_SHAPE, "expert_lo %d", expert_lo);
+    DL_TRY(check_ffn_shapes(B, D, inter, top_k, n_local, n_shared, w_gate, w_up, w_down, true));
+    if (out_dt != DL_F32 && out_dt != DL_BF16) return fail(DL_ERR_DTYPE, "out dtype %d", out_dt);
+    DL_TRY(check_ws(ws, ws_bytes, dl_moe_ffn_workspace(B, D, inter, top_k, n_local, n_shared)));
+    (void)hipGetLastError();
+    Ws w(ws);
+    FfnWs f;
+    ffn_ws_layout(w, B, D, inter, top_k, n_local, n_shared, w_gate->dtype == DL_FP8_E4M3, f);
+    return run_ffn(h, B, D, inter, experts, gates, top_k, w_gate, w_up, w_down, n_local, n_shared, residual, DL_F32,
+                   out, out_dt, f, (hipStream_t)stream, Marks(), nullptr, false, false, expert_lo);
 }
 
 static int check_layer(const dl_layer_desc *d, const dl_pages *pg, int R = 1)

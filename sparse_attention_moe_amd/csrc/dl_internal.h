@@ -150,7 +150,8 @@ int route_chunks(int D);  // hidden-size chunks of the router's partial dot prod
 // part [route_chunks(D), B, E] is scratch (fp64).
 int launch_route(const float *h, int B, int D, const float *w_r, const float *bias, int E, int ke, int32_t *experts,
                  float *gates, float *logits, double *part, hipStream_t s);
-int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s);
+// lo < 0: picks are stack indices (negative: computed elsewhere); lo >= 0: the stack holds experts [lo, lo + E)
+int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s, int lo = -1);
 // Router top-k (from launch_route_partial's chunk partials), with p != nullptr fused with the dispatch plan.
 bool route_plan_ok(int E, int ke, int B);
 int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s);

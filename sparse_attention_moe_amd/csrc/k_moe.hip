@@ -177,8 +177,10 @@ __device__ __forceinline__ int token_topk(const double *lrow, int E, int ke)
 // From the picks s_exp[b * ke + j] (in LDS) of a whole workgroup of 1024 threads: active experts in
 // ascending id (shared experts last), each expert's pairs in (token, slot) order, the pair index of every
 // (token, slot), and the prefix over active experts of their token groups of PLAN_TPG (grp_off, n_active + 1
-// entries) that the expert GEMV enumerates its work by.  `distinct`: no token picks an expert twice (router output), so an expert's pair
-// rank is the number of earlier tokens in its token mask (B <= 64); otherwise the earlier picks are counted.
+// entries) that the expert GEMV enumerates its work by.  `distinct`: no token picks an expert twice (router
+// output), so an expert's pair rank is the number of earlier tokens in its token mask (B <= 64); otherwise the
+// earlier picks are counted.  A negative pick is skipped: its pair index is -1 and the pairs computed here stay
+// contiguous (shared experts' pairs right after the routed ones).  s_cnt holds E + 1 entries.
 __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool distinct, int *s_cnt, int *s_off,
                            unsigned long long *s_mask, const MoePlan &p)
 {
@@ -191,6 +193,7 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
     __syncthreads();
     for (int i = tid; i < np; i += nT) {
         const int e = s_exp[i];
+        if (e < 0) continue;  // a pair computed elsewhere
         atomicAdd(&s_cnt[e], 1);
         if (use_mask) atomicOr(&s_mask[e], 1ull << (i / ke));
     }
@@ -215,6 +218,7 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
             if (lane >= o) { ia += ta; ip += tp; ig += tg; }
         }
         const int na_tot = __shfl(ia, 63, 64), ng_tot = __shfl(ig, 63, 64);
+        const int npr = __shfl(ip, 63, 64);  // routed pairs computed here (skipped ones excluded)
         int a = ia - na, q = ip - npl, gq = ig - ng;
         for (int i = 0; i < per; i++) {
             const int e = lane * per + i;
@@ -232,19 +236,25 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
         const int gs = (B + PLAN_TPG - 1) / PLAN_TPG;  // token groups of a shared expert
         for (int sx = lane; sx < S; sx += 64) {
             p.active[na_tot + sx] = E + sx;
-            p.tok_off[na_tot + sx] = np + sx * B;
+            p.tok_off[na_tot + sx] = npr + sx * B;
             p.tok_cnt[na_tot + sx] = B;
             p.grp_off[na_tot + sx] = ng_tot + sx * gs;
         }
         if (lane == 0) {
             p.grp_off[na_tot + S] = ng_tot + S * gs;
             *p.n_active = na_tot + S;
-            *p.n_pairs = np + S * B;
+            *p.n_pairs = npr + S * B;
+            s_cnt[E] = npr;  // for the shared pairs below (s_cnt holds E + 1 entries)
         }
     }
     __syncthreads();
+    const int npr = s_cnt[E];
     for (int i = tid; i < np; i += nT) {
         const int b = i / ke, j = i - b * ke, e = s_exp[i];
+        if (e < 0) {
+            p.pair_idx[(long)b * kk + j] = -1;
+            continue;
+        }
         int rank = 0;
         if (use_mask) rank = __popcll(s_mask[e] & ((1ull << b) - 1ull));
         else
@@ -255,21 +265,26 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
     }
     for (int i = tid; i < S * B; i += nT) {
         const int sx = i / B, b = i - sx * B;
-        const int q = np + sx * B + b;
+        const int q = npr + sx * B + b;
         p.pair_tok[q] = b;
         p.pair_idx[(long)b * kk + ke + sx] = q;
     }
 }
 
-// Dispatch plan of caller-given picks (experts [B, ke], each < E; ids out of range are clamped so that
-// no access leaves the arrays).
+// Dispatch plan of caller-given picks (experts [B, ke]).  A negative id marks a pair computed elsewhere (an
+// expert another GPU holds): it gets no row and adds nothing.  lo < 0: ids of E or more are clamped to E - 1 so
+// that no access leaves the arrays.  lo >= 0 (one GPU's expert-parallel share): the stack holds experts
+// [lo, lo + E); a pick in that range becomes its local index, any other pick is computed elsewhere.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ experts, int B, int ke, int E, int S,
-                                               MoePlan p)
+                                               int lo, MoePlan p)
 {
     __shared__ int s_exp[16384];
-    __shared__ int s_cnt[RP_MAXE], s_off[RP_MAXE];
+    __shared__ int s_cnt[RP_MAXE + 1], s_off[RP_MAXE];  // s_cnt[E]: routed pairs computed
     __shared__ unsigned long long s_mask[RP_MAXE];
-    for (int i = threadIdx.x; i < B * ke; i += blockDim.x) s_exp[i] = min(max(experts[i], 0), E - 1);
+    for (int i = threadIdx.x; i < B * ke; i += blockDim.x) {
+        const int e = experts[i];
+        s_exp[i] = lo < 0 ? (e < 0 ? -1 : min(e, E - 1)) : (e >= lo && e - lo < E ? e - lo : -1);
+    }
     __syncthreads();
     build_plan(s_exp, B, ke, E, S, false, s_cnt, s_off, s_mask, p);
 }
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
 {
     __shared__ double s_l[RP_LCAP];
     __shared__ int s_exp[16384];
-    __shared__ int s_cnt[RP_MAXE], s_off[RP_MAXE];
+    __shared__ int s_cnt[RP_MAXE + 1], s_off[RP_MAXE];  // s_cnt[E]: routed pairs computed
     __shared__ unsigned long long s_mask[RP_MAXE];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nT = 1024;
@@ -374,9 +389,9 @@ int launch_route(const float *h, int B, int D, const float *w_r, const float *bi
     return launch_route_plan(part, B, D, bias, E, ke, 0, experts, gates, logits, nullptr, s);
 }
 
-int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s)
+int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePlan &p, hipStream_t s, int lo)
 {
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, experts, B, ke, E, S, p);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, experts, B, ke, E, S, lo, p);
     return hip_check("plan");
 }
 
@@ -406,18 +421,21 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, in
     const float *gt = gates + (long)b * ke;
     for (int j0 = 0; j0 < kk; j0 += 8) {
         v4f f[8];
+        int q[8];
 #pragma unroll
-        for (int u = 0; u < 8; u++)
-            if (j0 + u < kk) f[u] = *(const v4f *)(F + (long)pi[j0 + u] * D + d);
+        for (int u = 0; u < 8; u++) {
+            q[u] = j0 + u < kk ? pi[j0 + u] : -1;  // -1: past the slots, or a pair computed elsewhere
+            if (q[u] >= 0) f[u] = *(const v4f *)(F + (long)q[u] * D + d);
+        }
         for (int k = 1; k < nslot; k++) {
 #pragma unroll
             for (int u = 0; u < 8; u++)
-                if (j0 + u < kk) f[u] += *(const v4f *)(F + k * fstride + (long)pi[j0 + u] * D + d);
+                if (q[u] >= 0) f[u] += *(const v4f *)(F + k * fstride + (long)q[u] * D + d);
         }
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             const int j = j0 + u;
-            if (j < kk) {
+            if (q[u] >= 0) {
                 if (j < ke) {
                     const float g = gt[j];
                     acc.x = fmaf(g, f[u].x, acc.x); acc.y = fmaf(g, f[u].y, acc.y);

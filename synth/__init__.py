@@ -313,6 +313,20 @@ def make_append(seed: int = 0, B: int = 9, Dc: int = 576, DI: int = 128, page_si
     }
 
 
+def ep_slice(t: Dict[str, torch.Tensor], spec: LayerSpec, g: int, n: int, shared: bool = True) -> Dict[str, torch.Tensor]:
+    """Expert weights held by GPU g of n in an expert-parallel layout: routed experts [g E/n, (g+1) E/n), then
+    (shared=True) the shared experts, with their block scales.  Pure copying: no arithmetic."""
+    E = spec.E
+    assert E % n == 0, "whole experts per GPU"
+    e0, e1 = g * E // n, (g + 1) * E // n
+    names = ["w_gate", "w_up", "w_down"] + (["w_gate_scale", "w_up_scale", "w_down_scale"] if spec.fp8 else [])
+    out = {}
+    for k in names:
+        parts = [t[k][e0:e1]] + ([t[k][E:E + spec.n_shared]] if shared and spec.n_shared else [])
+        out[k] = torch.cat(parts).contiguous()
+    return out
+
+
 def tp_slice(t: Dict[str, torch.Tensor], spec: LayerSpec, s: int, n: int) -> Dict[str, torch.Tensor]:
     """Expert weights of tensor-parallel slice s of n: intermediate rows [s I/n, (s+1) I/n) of every expert's gate
     and up matrices and the same columns of its down matrix, with their block scales (I/n must be a multiple of

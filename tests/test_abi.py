@@ -143,3 +143,18 @@ def test_probe_null_rejects_bad_counts(lib):
     assert lib.dl_probe_null(1025, 1, None) == -2
     assert lib.dl_probe_null(4, 0, None) == -2
     assert lib.dl_probe_null(4, 65537, None) == -2
+
+
+def test_ffn_ep_rejects_bad_arguments(lib):
+    wg = dl.Mat(1, 1, dl.DL_FP8_E4M3, 33, 2048, 6144)
+    wd = dl.Mat(1, 1, dl.DL_FP8_E4M3, 33, 6144, 2048)
+    ws = C.c_void_p(0x10000)
+    need = lib.dl_moe_ffn_workspace(8, 6144, 2048, 8, 32, 1)
+    # a negative first expert, no local routed expert, a stack that does not hold n_local + n_shared matrices
+    assert lib.dl_moe_ffn_ep(1, 8, 6144, 2048, 1, 1, 8, -1, C.byref(wg), C.byref(wg), C.byref(wd), 32, 1, None, 1,
+                             dl.DL_BF16, ws, need, None) == -2
+    assert lib.dl_moe_ffn_ep(1, 8, 6144, 2048, 1, 1, 8, 0, C.byref(wg), C.byref(wg), C.byref(wd), 0, 1, None, 1,
+                             dl.DL_BF16, ws, need, None) == -2
+    assert lib.dl_moe_ffn_ep(1, 8, 6144, 2048, 1, 1, 8, 32, C.byref(wg), C.byref(wg), C.byref(wd), 31, 1, None, 1,
+                             dl.DL_BF16, ws, need, None) == -2
+    assert b"w_gate" in lib.dl_last_error()

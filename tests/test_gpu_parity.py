@@ -393,3 +393,64 @@ def test_layer_step_pooled(pool):
     torch.cuda.synchronize()
     w = check_rows(spec, t, step.dbg, y, list(range(spec.B)))
     say(f"pooled pool={pool}: {w}")
+
+
+# ------------------------------------------------------------- one GPU's expert-parallel share of the FFN
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_ffn_expert_parallel_shares_sum_to_whole(n):
+    # GPU g of n holds routed experts [g E/n, (g+1) E/n); each share applies only its picks (with n = 8 a token picks
+    # more experts than a GPU holds).  The shares, run one after the other on one GPU, with the shared expert and
+    # the residual on share 0, must add up to the oracle's whole FFN.
+    spec = synth.small_fp8_spec(name=f"ep{n}", B=4, seq_lens=(900, 600, 300, 1), I=512)
+    t = _layer(spec, seed=70 + n)
+    B, per = spec.B, spec.E // n
+    h = (torch.randn(B, spec.D, generator=torch.Generator().manual_seed(9)) * 0.5).to(DEV)
+    ex = torch.empty(B, spec.ke, dtype=torch.int32, device=DEV)
+    g = torch.empty(B, spec.ke, dtype=torch.float32, device=DEV)
+    dl.moe_route(h, t["w_r"], t["r_bias"], spec.ke, ex, g)
+    total = torch.zeros(B, spec.D, dtype=torch.float32, device=DEV)
+    for s_ in range(n):
+        w = synth.ep_slice(t, spec, s_, n, shared=s_ == 0)
+        part = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
+        ns = spec.n_shared if s_ == 0 else 0
+        say(f"[gpu] moe_ffn_ep share {s_}/{n} experts [{s_ * per}, {(s_ + 1) * per}) shared={ns}")
+        dl.moe_ffn_ep(h, ex, g, s_ * per, dl.mat(w["w_gate"], w["w_gate_scale"]), dl.mat(w["w_up"], w["w_up_scale"]),
+                      dl.mat(w["w_down"], w["w_down_scale"]), per, ns, part, residual=h if s_ == 0 else None)
+        total += part
+    torch.cuda.synchronize()
+    orc = oracle.LayerOracle(spec, t)
+    hh = host(h).astype(np.float64)
+    exh, gh = host(ex), host(g)
+    got = host(total).astype(np.float64)
+    for b in range(B):
+        y64 = oracle.ffn(hh[b], exh[b], gh[b].astype(np.float64), orc.expert, spec.E, spec.n_shared)
+        assert_close(f"ep{n} row {b} y-h", got[b] - hh[b], y64 - hh[b])
+
+
+def test_ffn_skips_negative_expert_ids():
+    # dl_moe_ffn with some slots marked -1 (applied elsewhere) against the oracle, which skips them too; one token
+    # has every slot elsewhere, so its output is the residual plus the shared expert
+    spec = synth.small_fp8_spec(name="skip", B=4, seq_lens=(900, 600, 300, 1), I=512)
+    t = _layer(spec, seed=77)
+    B = spec.B
+    h = (torch.randn(B, spec.D, generator=torch.Generator().manual_seed(10)) * 0.5).to(DEV)
+    ex = torch.empty(B, spec.ke, dtype=torch.int32, device=DEV)
+    g = torch.empty(B, spec.ke, dtype=torch.float32, device=DEV)
+    dl.moe_route(h, t["w_r"], t["r_bias"], spec.ke, ex, g)
+    exs = ex.clone()
+    exs[0, 1] = -1
+    exs[1, 0] = -1
+    exs[1, 3] = -1
+    exs[2, :] = -1
+    y = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
+    say("[gpu] moe_ffn with skipped slots")
+    dl.moe_ffn(h, exs, g, dl.mat(t["w_gate"], t["w_gate_scale"]), dl.mat(t["w_up"], t["w_up_scale"]),
+               dl.mat(t["w_down"], t["w_down_scale"]), spec.E, spec.n_shared, y, residual=h)
+    torch.cuda.synchronize()
+    orc = oracle.LayerOracle(spec, t)
+    hh = host(h).astype(np.float64)
+    exh, gh = host(exs), host(g)
+    got = host(y).astype(np.float64)
+    for b in range(B):
+        y64 = oracle.ffn(hh[b], exh[b], gh[b].astype(np.float64), orc.expert, spec.E, spec.n_shared)
+        assert_close(f"skip row {b} y-h", got[b] - hh[b], y64 - hh[b])

@@ -500,3 +500,28 @@ def test_pooled_selection_pool1_is_per_position_and_expansion():
     assert np.all(np.diff(valid) > 0) and np.all(sel[valid.size:] == -1) and valid.max() < 1001
     assert set(valid // 4) == set(want)
     assert valid.size == 40 * 4 - (3 if 250 in want else 0)
+
+
+# ------------------------------------------------------------- one GPU's expert-parallel share of the FFN
+def test_ffn_expert_parallel_groups_add_up_and_skipped_slot_is_a_zero_gate():
+    # a negative expert id marks a slot whose expert another GPU holds: it must add exactly what a zero gate adds
+    # (nothing), and splitting the experts into groups (each group's FFN with the other groups' slots skipped, the
+    # shared expert and the residual counted once) must sum to the whole FFN
+    spec = synth.small_fp8_spec(name="ep-pin", seq_lens=(300,), E=16, ke=4, n_shared=1, I=256, D=512)
+    t = synth.make_layer(spec, seed=6)
+    orc = oracle.LayerOracle(spec, t)
+    r = orc.row(0)
+    h, ex, g = r["h"], np.asarray(r["experts"]), np.asarray(r["gates"], dtype=np.float64)
+    for j in range(spec.ke):
+        e2, g0 = ex.copy(), g.copy()
+        e2[j], g0[j] = -1, 0.0
+        assert np.array_equal(oracle.ffn(h, e2, g, orc.expert, spec.E, spec.n_shared),
+                              oracle.ffn(h, ex, g0, orc.expert, spec.E, spec.n_shared))
+    n, per = 4, spec.E // 4
+    total = np.zeros_like(r["y64"])
+    for grp in range(n):
+        mine = np.where((ex >= grp * per) & (ex < (grp + 1) * per), ex, -1)
+        total += oracle.ffn(h, mine, g, orc.expert, spec.E, spec.n_shared if grp == 0 else 0) - h
+    np.testing.assert_allclose(total + h, r["y64"], rtol=0, atol=1e-12 * max(1.0, float(np.abs(r["y64"]).max())))
+    # every slot elsewhere and no shared expert: the output is the residual, exactly
+    assert np.array_equal(oracle.ffn(h, np.full(spec.ke, -1), g, orc.expert, spec.E, 0), np.asarray(h, np.float64))
