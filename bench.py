@@ -216,18 +216,33 @@ def cpu_baseline(spec, t, seconds: float):
                       f"full context, attention, projections, router, FFN), {dt:.1f} s, scaled to a whole step"}
 
 
-def share_tp8(args, spec, n: int = 8):
-    """One GPU's share of an n-GPU layer step (design: DP attention, tensor-parallel experts): the indexer and
-    attention (+ W_UV, W_O, residual) for its B/n sequences, the router for all B tokens (each GPU routes every
-    token after the all-gather of h), and the FFN for all B tokens on intermediate rows [0, I/n) of every expert.
-    The all-gather of h and the reduce-scatter of y need a second GPU and are not run."""
+def share_step(args, spec, mode: str, n: int = 8):
+    """One GPU's share of an n-GPU layer step (DP attention): the indexer and attention (+ W_UV, W_O, residual) for
+    its B/n sequences, the router for all B tokens (each GPU routes every token after the all-gather of h), and
+    - mode "tp8": the FFN for all B tokens on intermediate rows [0, I/n) of every expert (tensor-parallel experts);
+    - mode "ep8": the FFN for the picks of the E/n routed experts the GPU holds, plus the shared expert
+      (expert-parallel).  The GPU taken is the one whose experts the instance's routing touches most: the layer
+      step waits for the slowest GPU.
+    The all-gather of h and the reduce-scatter (or all-to-all) of y need a second GPU and are not run."""
     dev = "cuda"
     Bl = spec.B // n
+    per = spec.E // n
     insts = []
     t0 = time.perf_counter()
     for i in range(args.instances):
         t = synth.make_layer(spec, seed=args.seed, device=dev, instance=i)
-        w = synth.tp_slice(t, spec, 0, n)
+        h = (t["x"].float() + 0.1 * torch.randn(spec.B, spec.D, device=dev)).contiguous()  # all-gathered h
+        ex = torch.empty(spec.B, spec.ke, dtype=torch.int32, device=dev)
+        g = torch.empty(spec.B, spec.ke, dtype=torch.float32, device=dev)
+        gpu, loads = 0, None
+        if mode == "ep8":
+            dl.moe_route(h, t["w_r"], t["r_bias"], spec.ke, ex, g)  # untimed: which GPU carries the most experts
+            picks = ex.cpu().numpy().ravel()
+            loads = [len(set(int(e) for e in picks if k * per <= e < (k + 1) * per)) for k in range(n)]
+            gpu = int(np.argmax(loads))
+            w = synth.ep_slice(t, spec, gpu, n)
+        else:
+            w = synth.tp_slice(t, spec, 0, n)
         for k in ("w_gate", "w_up", "w_down"):
             t[k] = None
         m = {k: dl.pack_weights(w[k], w[k + "_scale"]) for k in ("w_gate", "w_up", "w_down")}
@@ -236,13 +251,11 @@ def share_tp8(args, spec, n: int = 8):
         pg = dl.pages(t["seq_lens"][:Bl].contiguous(), t["page_table"][:Bl].contiguous(), spec.page_size)
         sel = torch.empty(Bl, spec.topk, dtype=torch.int32, device=dev)
         hl = torch.empty(Bl, spec.D, dtype=torch.float32, device=dev)
-        h = (t["x"].float() + 0.1 * torch.randn(spec.B, spec.D, device=dev)).contiguous()  # all-gathered h
-        ex = torch.empty(spec.B, spec.ke, dtype=torch.int32, device=dev)
-        g = torch.empty(spec.B, spec.ke, dtype=torch.float32, device=dev)
         y = torch.empty(spec.B, spec.D, dtype=torch.float32, device=dev)
         wuv = dl.mat(dl.pack_weights(t["w_uv"], t["w_uv_scale"]), t["w_uv_scale"], dl.DL_LAYOUT_TILES)
         wo = dl.mat(dl.pack_weights(t["w_o"], t["w_o_scale"]), t["w_o_scale"], dl.DL_LAYOUT_TILES)
         insts.append(dict(t=t, mats=mats, keep=keep, pg=pg, sel=sel, hl=hl, h=h, ex=ex, g=g, y=y, wuv=wuv, wo=wo,
+                          gpu=gpu, loads=loads,
                           q_idx=t["q_idx"][:Bl].contiguous(), q=t["q"][:Bl].contiguous(), x=t["x"][:Bl].contiguous()))
     torch.cuda.synchronize()
     print(f"[bench] generated {args.instances} x {spec.name} shares in {time.perf_counter() - t0:.1f} s",
@@ -257,8 +270,12 @@ def share_tp8(args, spec, n: int = 8):
                               ws=ws.get("a"))
         dl.moe_route(it["h"], t["w_r"], t["r_bias"], spec.ke, it["ex"], it["g"], ws=ws.get("r"))
         mt = it["mats"]
-        dl.moe_ffn(it["h"], it["ex"], it["g"], mt["w_gate"], mt["w_up"], mt["w_down"], spec.E, spec.n_shared,
-                   it["y"], residual=it["h"], ws=ws.get("f"))
+        if mode == "ep8":
+            dl.moe_ffn_ep(it["h"], it["ex"], it["g"], it["gpu"] * per, mt["w_gate"], mt["w_up"], mt["w_down"], per,
+                          spec.n_shared, it["y"], residual=it["h"], ws=ws.get("f"))
+        else:
+            dl.moe_ffn(it["h"], it["ex"], it["g"], mt["w_gate"], mt["w_up"], mt["w_down"], spec.E, spec.n_shared,
+                       it["y"], residual=it["h"], ws=ws.get("f"))
 
     L = dl.load()
     it0 = insts[0]
@@ -266,7 +283,11 @@ def share_tp8(args, spec, n: int = 8):
     ws["a"] = dl.workspace(L.dl_sparse_attn_workspace(Bl, spec.H, spec.Dv, spec.topk, dl.C.byref(it0["wuv"]),
                                                       dl.C.byref(it0["wo"])), dev)
     ws["r"] = dl.workspace(L.dl_moe_route_workspace(spec.B, spec.D, spec.E), dev)
-    ws["f"] = dl.workspace(L.dl_moe_ffn_workspace(spec.B, spec.D, spec.I // n, spec.ke, spec.E, spec.n_shared), dev)
+    if mode == "ep8":
+        ws["f"] = dl.workspace(L.dl_moe_ffn_workspace(spec.B, spec.D, spec.I, spec.ke, per, spec.n_shared), dev)
+    else:
+        ws["f"] = dl.workspace(L.dl_moe_ffn_workspace(spec.B, spec.D, spec.I // n, spec.ke, spec.E, spec.n_shared),
+                               dev)
     for i in range(args.warmup):
         step(insts[i % len(insts)])
     torch.cuda.synchronize()
@@ -277,21 +298,31 @@ def share_tp8(args, spec, n: int = 8):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    touched_n = sum(touched(spec, it["ex"].cpu().numpy()) for it in insts) / len(insts)
     share = synth.spec_replace(spec, B=Bl, seq_lens=spec.seq_lens[:Bl])
     b = algorithmic_bytes(share, share.seq_lens, 0)
-    gu = touched_n * EXPERT_BYTES_GATE_UP(spec) / n
-    dn = touched_n * EXPERT_BYTES_DOWN(spec) / n
+    if mode == "ep8":  # the GPU's touched routed experts + the shared expert, whole
+        touched_n = sum(max(it["loads"]) + spec.n_shared for it in insts) / len(insts)
+        gu = touched_n * EXPERT_BYTES_GATE_UP(spec)
+        dn = touched_n * EXPERT_BYTES_DOWN(spec)
+    else:  # 1/n of every touched expert
+        touched_n = sum(touched(spec, it["ex"].cpu().numpy()) for it in insts) / len(insts)
+        gu = touched_n * EXPERT_BYTES_GATE_UP(spec) / n
+        dn = touched_n * EXPERT_BYTES_DOWN(spec) / n
     total = b["total"] + gu + dn
     rec = {"metric": "one GPU's share of an 8-GPU decode layer step (exchanges not run), layer-steps/s",
            "value": round(1000.0 / ms, 2), "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp8-weights/int8-indexer/fp32-accum", "data": "synthetic",
-           "config": {"workload": f"{spec.name}-tp{n}-share", "sequences": Bl, "tokens_routed": spec.B,
-                      "inter_slice": spec.I // n, "context": int(max(spec.seq_lens))},
+           "config": {"workload": f"{spec.name}-{mode[:2]}{n}-share", "sequences": Bl, "tokens_routed": spec.B,
+                      "context": int(max(spec.seq_lens))},
            "share_hbm": {"algorithmic_bytes": int(total), "achieved_gbs": round(total / (ms * 1e-3) / 1e9, 1),
                          "frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "touched_experts": round(touched_n, 2)}}
+    if mode == "ep8":
+        rec["config"]["experts_per_gpu"] = per
+        rec["expert_loads"] = [it["loads"] for it in insts]  # distinct routed experts each GPU would apply
+    else:
+        rec["config"]["inter_slice"] = spec.I // n
     print(json.dumps(rec), flush=True)
 
 
@@ -306,9 +337,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU time of the oracle baseline sample")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe")
-    ap.add_argument("--share", choices=["tp8"], default=None,
+    ap.add_argument("--share", choices=["tp8", "ep8"], default=None,
                     help="time one GPU's share of an 8-GPU layer instead (DP attention on one sequence, router for "
-                         "every token, tensor-parallel expert slice of inter/8 rows); the exchanges are not run")
+                         "every token, and the FFN as a tensor-parallel slice of inter/8 rows of every expert (tp8) "
+                         "or as the E/8 experts the GPU holds (ep8)); the exchanges are not run")
     ap.add_argument("--rows-per-seq", type=int, default=1,
                     help="query rows per sequence (multi-row decode, e.g. MTP verification); 1 = ordinary decode")
     ap.add_argument("--pool", type=int, default=1,
@@ -322,7 +354,7 @@ def main():
         sys.exit(2)
     spec = synth.config(args.config)
     if args.share:
-        return share_tp8(args, spec)
+        return share_step(args, spec, args.share)
     if args.rows_per_seq != 1:
         spec = synth.spec_replace(spec, R=args.rows_per_seq, name=f"{spec.name}-rows{args.rows_per_seq}")
     if args.pool != 1:
