@@ -31,21 +31,16 @@ struct Ws {
 };
 
 // ------------------------------------------------------------- indexer + top-k
-struct SelState {      // per row and pass, in the workspace
-    int lo, hi;        // the threshold score T lies in [lo, hi]
-    int above;         // number of scores > hi
-    int done;          // 1: T == lo == hi is final
-    int need;          // how many scores == T are kept (lowest positions first)
-    int n_sel;         // min(top_k, L)
-    int pad0, pad1;
+struct Thr {           // the selection threshold of a row: items scoring above hi are kept,
+    int lo, hi, need;  // need of the items inside [lo, hi]
 };
-
 struct TopkWs {
-    int32_t *scores;   // [B, Lmax]
-    unsigned *hist1;   // [B, NB1]
-    unsigned *hist2;   // [2, B, NB2]
-    SelState *state;   // [4, B]
-    int *cnt;          // [B, nchunk, 2]
+    int32_t *scores;   // [B, Lmax] scores of the row's items
+    unsigned *hist1;   // [B, NB1] log-linear histogram of the scores
+    unsigned *bits;    // [B, nchunk * 128] kept items, one bit each (whole 4,096-item chunks)
+    int2 *cand;        // [B, nchunk * 4,096] (item, score) inside the threshold bin, per chunk
+    int32_t *ccnt;     // [B, nchunk] how many per chunk
+    Thr *thr;          // [B]
 };
 void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R = 1, int pool = 1);
 int launch_probe_read(const void *buf, size_t bytes, size_t *bytes_read, hipStream_t s);

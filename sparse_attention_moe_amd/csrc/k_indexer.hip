@@ -8,26 +8,24 @@
 // the 64-token, 128-byte layout) per step.
 //
 // Selection (trnrt summary, "The interesting bit": the top 2,048 positions are kept; ties go to
-// the lower position).  Radix select on the exact integer scores:
-//   pass 1 (fused into scoring): a log-linear histogram (exact below 256, then 128 bins per
-//            binade) locates the bin holding the k-th largest score;
-//   refine:  4,096-bin histograms of the scores inside [lo, hi] narrow the range until lo == hi;
-//   count:   per 4,096-position chunk, how many scores are > T and == T;
-//   write:   an ordered compaction: a position is kept if its score is > T, or == T and fewer than
-//            `need` equal scores precede it; its output slot is the number of kept positions
-//            before it, so the list comes out in ascending position order.
-// Each histogram is turned into the next range at the start of the following kernel, by every one of
-// its workgroups (the same deterministic pick, from 16 KB that the kernel boundary made visible);
-// workgroup 0 records the result for later kernels.  No workgroup waits on, or fences for, another:
-// on this part an in-kernel device-scope fence writes back the whole L2 of the XCD, which costs far
-// more than recomputing a 4,096-bin pick.
+// the lower position), exact on the integer scores:
+//   histogram (fused into scoring): a log-linear histogram (exact below 256, then 128 bins per
+//            binade) locates the bin [lo, hi] holding the k-th largest score and the count above it;
+//   mark:    one pass over the scores: positions scoring above hi are set in a per-row bitmap (each
+//            word written whole by the workgroup owning its positions), positions inside [lo, hi]
+//            go with their scores to the workgroup's own region of the candidate list, with a count;
+//   final:   one workgroup per row keeps the `need` best candidates by a radix select on a unique key
+//            (score above, complemented position below, so ties go to the lower position), sets their
+//            bits, then compacts the bitmap in position order, so the list comes out ascending.
+// Every mark workgroup picks the bin from the histogram (the same deterministic pick, made visible by
+// the kernel boundary); workgroup 0 records it for the final kernel.  No workgroup waits on, or fences
+// for, another: on this part an in-kernel device-wide barrier costs far more than a kernel boundary.
 #include "dl_common.h"
 #include "dl_internal.h"
 
 namespace dl {
 
 static constexpr int NB1 = 256 + 23 * 128;  // log-linear bins covering 0 .. 2^31-1
-static constexpr int NB2 = 4096;
 static constexpr int SCORE_POS_PER_BLOCK = 1024;  // 4 waves x 4 steps x 64 positions
 static constexpr int SEL_CHUNK = 4096;            // 256 threads x 16 positions
 
@@ -125,50 +123,28 @@ __device__ void block_pick(const unsigned *gh, unsigned *sh, int k, int *s_tmp, 
     __syncthreads();
 }
 
-// The selection state after one more histogram: pass 1 uses the log-linear bins, later passes 4,096
-// equal bins spanning the current [lo, hi].  A finished state passes through unchanged.
-template <bool FIRST>
-__device__ SelState advance(const SelState prev, const unsigned *gh, int top_k, unsigned *sh, int *s_tmp)
+// Where the selection threshold lies, from the row's log-linear histogram: items scoring above hi are kept,
+// `need` of the items inside [lo, hi] are kept.  A row of at most top_k items keeps everything (hi = -1: every
+// score is >= 0).  Called by all 256 threads of a workgroup.
+__device__ Thr threshold(const unsigned *gh, int L, int top_k, unsigned *sh, int *s_tmp)
 {
-    if (prev.done) return prev;
-    SelState s = prev;
-    int bin, above;
-    if (FIRST) {
-        block_pick<NB1>(gh, sh, top_k, s_tmp, bin, above);
-        int lo, hi;
-        bin1_range(bin, lo, hi);
-        s.lo = lo; s.hi = hi; s.above = above;
-    } else {
-        const unsigned lo = (unsigned)prev.lo, hi = (unsigned)prev.hi;
-        const int shift = max(0, (32 - __clz(hi - lo)) - 12);
-        block_pick<NB2>(gh, sh, top_k - prev.above, s_tmp, bin, above);
-        const unsigned nlo = lo + ((unsigned)bin << shift);
-        const unsigned nhi = min(hi, nlo + ((1u << shift) - 1u));
-        s.lo = (int)nlo; s.hi = (int)nhi; s.above = prev.above + above;
+    Thr t;
+    if (L <= top_k) {
+        t.lo = 0x7FFFFFFF; t.hi = -1; t.need = 0;
+        return t;
     }
-    if (s.lo == s.hi) { s.done = 1; s.need = top_k - s.above; }
-    return s;
+    int bin, above;
+    block_pick<NB1>(gh, sh, top_k, s_tmp, bin, above);
+    bin1_range(bin, t.lo, t.hi);
+    t.need = top_k - above;
+    return t;
 }
 
-// Per-row initial selection state; clears the histograms of all passes.
-__global__ void k_sel_init(const int32_t *seq_lens, int R, int pool, int B, int top_k, unsigned *hist1,
-                           unsigned *hist2, SelState *st)
+// Clears the row's histogram.
+__global__ void k_sel_init(unsigned *hist1)
 {
     const int b = blockIdx.x;
     for (int i = threadIdx.x; i < NB1; i += blockDim.x) hist1[(long)b * NB1 + i] = 0;
-    for (int i = threadIdx.x; i < 2 * NB2; i += blockDim.x) hist2[(long)b * 2 * NB2 + i] = 0;
-    if (threadIdx.x == 0) {
-        int L = row_len(seq_lens, b, R, pool);
-        SelState s;
-        s.n_sel = min(L, top_k);
-        if (L <= top_k) {  // keep everything: every score (>= 0) is above T = -1
-            s.lo = s.hi = -1; s.above = L; s.done = 1; s.need = 0;
-        } else {
-            s.lo = 0; s.hi = 0x7FFFFFFF; s.above = 0; s.done = 0; s.need = 0;
-        }
-        s.pad0 = s.pad1 = 0;
-        st[b] = s;  // state 0 of row b
-    }
 }
 
 // Scores of 1,024 positions of one sequence per workgroup.  NHG groups of 16 indexer heads, KCH chunks of 64 key
@@ -295,110 +271,94 @@ __device__ __forceinline__ void load16(const int32_t *sc, long p0, int L, int v[
     }
 }
 
-// One refinement pass (PASS = 1, 2): advance the state with histogram PASS, then histogram the scores
-// inside the new [lo, hi] with 4,096 bins into histogram PASS + 1.
-template <int PASS>
-__global__ __launch_bounds__(256) void k_sel_refine(const int32_t *__restrict__ scores, long Lmax,
-                                                    const int32_t *__restrict__ seq_lens, int R, int pool, int top_k,
-                                                    const unsigned *__restrict__ hist_in, unsigned *__restrict__ hist_out,
-                                                    SelState *__restrict__ st, int B)
+// Mark: per 4,096-item chunk of a row longer than top_k, the bitmap words of its items (bit set: score above
+// the threshold bin), and its items inside the bin, with their scores, in the chunk's own region of the
+// candidate list ([row][chunk * 4,096 + i]) with their count; workgroup 0 records the bin.
+__global__ __launch_bounds__(256) void k_sel_mark(const int32_t *__restrict__ scores, long Lmax,
+                                                  const int32_t *__restrict__ seq_lens, int R, int pool, int top_k,
+                                                  const unsigned *__restrict__ hist1, unsigned *__restrict__ bits,
+                                                  long Lw, int2 *__restrict__ cand, int32_t *__restrict__ ccnt,
+                                                  int nchunk, Thr *__restrict__ thr)
 {
-    __shared__ unsigned s_hist[NB2 > NB1 ? NB2 : NB1];
+    __shared__ unsigned s_hist[NB1];
     __shared__ int s_tmp[260];
+    __shared__ int s_w[4];
     const int b = blockIdx.y;
     const int L = row_len(seq_lens, b, R, pool);
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
-    if (c0 >= L && blockIdx.x != 0) return;
-    const int tid = threadIdx.x;
-    const SelState prev = st[(long)(PASS - 1) * B + b];
-    const SelState cur = PASS == 1 ? advance<true>(prev, hist_in + (long)b * NB1, top_k, s_hist, s_tmp)
-                                   : advance<false>(prev, hist_in + (long)b * NB2, top_k, s_hist, s_tmp);
-    if (blockIdx.x == 0 && tid == 0) st[(long)PASS * B + b] = cur;
-    if (c0 >= L || cur.done) return;
-    const unsigned lo = (unsigned)cur.lo, hi = (unsigned)cur.hi;
-    const int shift = max(0, (32 - __clz(hi - lo)) - 12);
-    __syncthreads();
-    for (int i = tid; i < NB2; i += 256) s_hist[i] = 0;
-    __syncthreads();
-    // the thread's 16 consecutive scores, all loads in flight at once (positions past L read INT32_MIN,
-    // which is outside every range)
+    if (L <= top_k || c0 >= L) return;  // short rows keep everything without a bitmap
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the thread's 16 consecutive scores, loaded while the bin is picked (items past L read INT32_MIN:
+    // neither above hi nor inside the bin)
     int v[16];
     load16(scores + (long)b * Lmax, c0 + (long)tid * 16, L, v);
+    const Thr t = threshold(hist1 + (long)b * NB1, L, top_k, s_hist, s_tmp);
+    if (blockIdx.x == 0 && tid == 0) thr[b] = t;
+    unsigned m = 0;
+    int nc = 0;
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        const unsigned x = (unsigned)v[i];
-        if (v[i] >= 0 && x >= lo && x <= hi) atomicAdd(&s_hist[(x - lo) >> shift], 1u);
+        if (v[i] > t.hi) m |= 1u << i;
+        else if (v[i] >= t.lo) nc++;
     }
+    // two threads fill one 32-bit word: the even one the low half
+    const unsigned mo = (unsigned)__shfl_xor((int)m, 1, 64);
+    if ((tid & 1) == 0) bits[(long)b * Lw + (c0 >> 5) + (tid >> 1)] = m | (mo << 16);
+    // candidates: exclusive scan over the workgroup into the chunk's region
+    const int inc = wave_incl_scan(nc);
+    if (lane == 63) s_w[wave] = inc;
     __syncthreads();
-    unsigned *gh = hist_out + (long)b * NB2;
-    for (int i = tid; i < NB2; i += 256) {
-        const unsigned v = s_hist[i];
-        if (v) atomicAdd(gh + i, v);
-    }
+    int before = 0;
+    for (int w = 0; w < wave; w++) before += s_w[w];
+    if (tid == 0) ccnt[(long)b * nchunk + blockIdx.x] = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    int o = before + inc - nc;
+    int2 *cr = cand + (long)b * nchunk * SEL_CHUNK + c0;
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        if (v[i] <= t.hi && v[i] >= t.lo) cr[o++] = int2{(int)(c0 + (long)tid * 16 + i), v[i]};
 }
 
-// Per chunk: how many scores are > T and == T.
-__global__ __launch_bounds__(256) void k_sel_count(const int32_t *__restrict__ scores, long Lmax,
+static constexpr int FCAP = 8192;   // candidates whose keys the final kernel holds in LDS; more are re-read
+static constexpr int FCH = 2048;    // chunks per row the final kernel handles (rows of up to 8M items)
+static constexpr int FBW = 4096;    // bitmap words per compaction round (16 per thread)
+static constexpr int FOUT = 4096;   // kept items staged in LDS per round before their coalesced stores
+
+// Final: one workgroup per row.  Rows of at most top_k items keep items 0 .. L-1.  Longer rows keep the
+// marked items and the `need` best candidates: radix select, most significant 8-bit digit first, of the
+// need-th largest key ((score - lo) << PB | (2^PB - 1 - item)); keys are unique, so exactly `need` keys match
+// the final prefix or exceed it.  The bitmap, with their bits added, is compacted in item order; its first
+// round of words is loaded before the select, so that latency overlaps it.
+// pool > 1: slot k holds items' positions [k pool, (k + 1) pool), those at or past the row's length as -1.
+__global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ scores, long Lmax,
                                                    const int32_t *__restrict__ seq_lens, int R, int pool, int top_k,
-                                                   const unsigned *__restrict__ hist3, SelState *__restrict__ st, int B,
-                                                   int nchunk, int *__restrict__ cnt)
-{
-    __shared__ unsigned s_hist[NB2];
-    __shared__ int s_tmp[260];
-    __shared__ int s_red[2][4];
-    const int b = blockIdx.y;
-    const int L = row_len(seq_lens, b, R, pool);
-    const long c0 = (long)blockIdx.x * SEL_CHUNK;
-    if (c0 >= L && blockIdx.x != 0) return;
-    const int tid = threadIdx.x;
-    const SelState cur = advance<false>(st[2L * B + b], hist3 + (long)b * NB2, top_k, s_hist, s_tmp);
-    if (blockIdx.x == 0 && tid == 0) st[3L * B + b] = cur;
-    if (c0 >= L) return;
-    const int T = cur.lo;
-    int v[16];
-    load16(scores + (long)b * Lmax, c0 + (long)tid * 16, L, v);
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        gt += v[i] > T;
-        eq += v[i] == T;
-    }
-    gt = wave_sum_i(gt);
-    eq = wave_sum_i(eq);
-    if ((tid & 63) == 0) { s_red[0][tid >> 6] = gt; s_red[1][tid >> 6] = eq; }
-    __syncthreads();
-    if (tid == 0) {
-        long o = ((long)b * nchunk + blockIdx.x) * 2;
-        cnt[o] = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
-        cnt[o + 1] = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-    }
-}
-
-// Ordered compaction of the kept positions of one chunk.
-__global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ scores, long Lmax,
-                                                   const int32_t *__restrict__ seq_lens, int R, int pool, const SelState *__restrict__ st,
-                                                   int nchunk, const int *__restrict__ cnt, int top_k,
+                                                   const unsigned *__restrict__ bits, long Lw,
+                                                   const int2 *__restrict__ cand, const int32_t *__restrict__ ccnt,
+                                                   int nchunk, const Thr *__restrict__ thr, int PB,
                                                    int32_t *__restrict__ sel, int32_t *__restrict__ sel_score)
 {
-    __shared__ int s_w[2][4];
-    __shared__ int s_base[2];
-    const int b = blockIdx.y;
+    typedef unsigned long long u64;
+    __shared__ unsigned s_hist[256];
+    __shared__ int s_off[FCH + 1];
+    __shared__ u64 s_key[FCAP];
+    __shared__ unsigned s_bm[FBW];  // bits of the kept candidates in the current round of bitmap words
+    __shared__ int s_out[FOUT];     // the round's kept items, in order
+    __shared__ int s_w[4];
+    __shared__ int s_pick[3];
+    const int b = blockIdx.x;
     const int L = row_len(seq_lens, b, R, pool);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const SelState s = st[3L * gridDim.y + b];
-    // pool > 1: slot k holds positions [k pool, (k + 1) pool) of the output row (the kept pool's positions,
-    // those at or past the row's last position written as -1); sel_score holds one score per slot
+    const int32_t *sr = scores + (long)b * Lmax;
     int32_t *so = sel + (long)b * top_k * pool;
     int32_t *ss = sel_score ? sel_score + (long)b * top_k : nullptr;
     const int plen = pool > 1 ? row_len(seq_lens, b, R) : 0;  // positions the row sees
-    if (blockIdx.x == 0) {  // padding of the unused slots
-        for (int i = s.n_sel * pool + tid; i < top_k * pool; i += 256) so[i] = -1;
-        if (ss)
-            for (int i = s.n_sel + tid; i < top_k; i += 256) ss[i] = 0;
-    }
+    const int n_sel = min(L, top_k);
+    for (int i = n_sel * pool + tid; i < top_k * pool; i += 256) so[i] = -1;  // padding of the unused slots
+    if (ss)
+        for (int i = n_sel + tid; i < top_k; i += 256) ss[i] = 0;
     // pools of 4 or more positions go out as 16-byte stores when the output is 16-byte aligned
     const bool vec = pool >= 4 && ((uintptr_t)sel & 15) == 0;
-    auto put = [&](int slot, int item, int score) {
+    auto put = [&](int slot, int item) {
+        if (slot < 0 || slot >= top_k) return;  // only an inconsistent list could ask; it would leave the row
         if (pool == 1) {
             so[slot] = item;
         } else if (vec) {
@@ -413,61 +373,163 @@ __global__ __launch_bounds__(256) void k_sel_write(const int32_t *__restrict__ s
                 so[slot * pool + j] = p < plen ? p : -1;
             }
         }
-        if (ss) ss[slot] = score;
+        if (ss) ss[slot] = sr[item];
     };
-    const long c0 = (long)blockIdx.x * SEL_CHUNK;
-    if (c0 >= L) return;
-    const int T = s.lo, need = s.need;
-    // counts of all earlier chunks of this row
-    int pg = 0, pe = 0;
-    for (int c = tid; c < (int)blockIdx.x; c += 256) {
-        pg += cnt[((long)b * nchunk + c) * 2];
-        pe += cnt[((long)b * nchunk + c) * 2 + 1];
+    if (L <= top_k) {
+        for (int i = tid; i < L; i += 256) put(i, i);
+        return;
     }
-    pg = wave_sum_i(pg);
-    pe = wave_sum_i(pe);
-    if (lane == 0) { s_w[0][wave] = pg; s_w[1][wave] = pe; }
-    __syncthreads();
-    if (tid == 0) {
-        s_base[0] = s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
-        s_base[1] = s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
-    }
-    __syncthreads();
-    const int base_g = s_base[0], base_e = s_base[1];
-    const long p0 = c0 + (long)tid * 16;
-    int v[16];
-    load16(scores + (long)b * Lmax, p0, L, v);
-    int gt = 0, eq = 0;
+    const unsigned *br = bits + (long)b * Lw;
+    const int2 *cr = cand + (long)b * nchunk * SEL_CHUNK;
+    const Thr t = thr[b];
+    const int nw = (L + 31) >> 5;
+    // words w0 + tid * 16 .. + 16 of a round (whole chunks are 128 words, so 4-word groups never pass the
+    // row's chunks; words past L hold no bits)
+    unsigned wv[16];
+    auto load_round = [&](int w0) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        gt += v[i] > T;
-        eq += v[i] == T;
-    }
-    // exclusive scan of (gt, eq) over the 256 threads
-    int ig = wave_incl_scan(gt), ie = wave_incl_scan(eq);
-    __syncthreads();
-    if (lane == 63) { s_w[0][wave] = ig; s_w[1][wave] = ie; }
-    __syncthreads();
-    int wg = 0, we = 0;
-    for (int w = 0; w < wave; w++) { wg += s_w[0][w]; we += s_w[1][w]; }
-    int g = base_g + wg + ig - gt;  // kept-above scores before my first position
-    int e = base_e + we + ie - eq;  // equal scores before my first position
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-        int sv = v[i];
-        // slots outside [0, top_k) are dropped: only an inconsistent state (never produced from consistent
-        // counts) can ask for them, and they would lie outside the row
-        if (sv > T) {
-            int slot = g + min(e, need);
-            if (slot >= 0 && slot < top_k) put(slot, (int)(p0 + i), sv);
-            g++;
-        } else if (sv == T) {
-            if (e < need) {
-                int slot = g + e;
-                if (slot >= 0 && slot < top_k) put(slot, (int)(p0 + i), sv);
-            }
-            e++;
+        for (int j = 0; j < 4; j++) {
+            const int wi = w0 + tid * 16 + j * 4;
+            const uint4 q = wi < nw ? *(const uint4 *)(br + wi) : uint4{0u, 0u, 0u, 0u};
+            wv[4 * j] = q.x; wv[4 * j + 1] = q.y; wv[4 * j + 2] = q.z; wv[4 * j + 3] = q.w;
         }
+    };
+    load_round(0);
+    // candidate counts of the row's chunks -> offsets of each chunk's run in the candidate order
+    const int nch = (L + SEL_CHUNK - 1) / SEL_CHUNK;
+    {
+        int carry = 0;
+        for (int c0 = 0; c0 < nch; c0 += 256) {
+            const int ch = c0 + tid;
+            const int n = ch < nch ? ccnt[(long)b * nchunk + ch] : 0;
+            const int inc = wave_incl_scan(n);
+            if (lane == 63) s_w[wave] = inc;
+            __syncthreads();
+            int before = 0;
+            for (int w = 0; w < wave; w++) before += s_w[w];
+            if (ch < nch) s_off[ch] = carry + before + inc - n;
+            carry += s_w[0] + s_w[1] + s_w[2] + s_w[3];
+            __syncthreads();
+        }
+        if (tid == 0) s_off[nch] = carry;
+        __syncthreads();
+    }
+    const int c = s_off[nch];  // the items inside the bin: >= need
+    const u64 pm = (1ull << PB) - 1ull;
+    // candidate i of the row: the last chunk whose offset is <= i, then its place in that chunk's run
+    auto entry = [&](int i) -> int2 {
+        int lo = 0, hi = nch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        return cr[(long)lo * SEL_CHUNK + (i - s_off[lo])];
+    };
+    auto key_of = [&](int2 e) -> u64 {
+        return ((u64)(unsigned)(e.y - t.lo) << PB) | (pm - (u64)(unsigned)e.x);
+    };
+    const bool in_lds = c <= FCAP;
+    if (in_lds)
+        for (int i = tid; i < c; i += 256) s_key[i] = key_of(entry(i));
+    __syncthreads();
+    u64 prefix = 0, pmask = 0;
+    if (t.need < c && in_lds && c <= 256) {
+        // few candidates: the kept ones are those with fewer than `need` larger keys; the need-th largest key
+        // becomes the threshold
+        const u64 mine = tid < c ? s_key[tid] : 0ull;
+        int rank = 0;
+        for (int j = 0; j < c; j++) rank += s_key[j] > mine;
+        if (tid < c && rank == t.need - 1) s_key[FCAP - 1] = mine;  // unique keys: exactly one thread
+        __syncthreads();
+        prefix = s_key[FCAP - 1];
+        pmask = ~0ull;
+        __syncthreads();
+    } else if (t.need < c) {
+        // the score offset is below 2^23 (the widest bin), so keys are below 2^(23 + PB)
+        int krem = t.need;
+        for (int shift = ((23 + PB - 1) / 8) * 8; shift >= 0; shift -= 8) {
+            s_hist[tid] = 0;
+            __syncthreads();
+            for (int i = tid; i < c; i += 256) {
+                const u64 k = in_lds ? s_key[i] : key_of(entry(i));
+                if ((k & pmask) == prefix) atomicAdd(&s_hist[(unsigned)(k >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            // digit d: keys with a larger digit number fewer than krem, with d or larger at least krem
+            const int d = 255 - tid;
+            const int seg = (int)s_hist[d];
+            int inc = wave_incl_scan(seg);
+            if (lane == 63) s_w[wave] = inc;
+            __syncthreads();
+            int before = 0;
+            for (int w = 0; w < wave; w++) before += s_w[w];
+            inc += before;
+            if (inc >= krem && inc - seg < krem) { s_pick[0] = d; s_pick[1] = inc - seg; s_pick[2] = seg; }
+            __syncthreads();
+            const int dd = s_pick[0], above = s_pick[1], cnt = s_pick[2];
+            __syncthreads();
+            prefix |= (u64)dd << shift;
+            pmask |= 255ull << shift;
+            krem -= above;
+            if (cnt == krem) break;  // every key with this prefix is kept
+        }
+    }
+    // ordered compaction, one round of FBW words at a time: the kept candidates' bits of the round are set in
+    // LDS and added to the marked words
+    int base = 0;
+    for (int w0 = 0; w0 < nw; w0 += FBW) {
+        if (w0 > 0) load_round(w0);
+        for (int i = tid; i < FBW; i += 256) s_bm[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < c; i += 256) {
+            const u64 k = in_lds ? s_key[i] : key_of(entry(i));
+            if ((k & pmask) >= prefix) {
+                const int item = (int)(pm - (k & pm));
+                const int wi = (item >> 5) - w0;
+                if (wi >= 0 && wi < FBW) atomicOr(&s_bm[wi], 1u << (item & 31));
+            }
+        }
+        __syncthreads();
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            wv[j] |= s_bm[tid * 16 + j];
+            cnt += __popc(wv[j]);
+        }
+        const int inc = wave_incl_scan(cnt);
+        if (lane == 63) s_w[wave] = inc;
+        __syncthreads();
+        int before = 0;
+        for (int w = 0; w < wave; w++) before += s_w[w];
+        const int tot = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+        int o = before + inc - cnt;  // within the round
+        if (tot <= FOUT) {
+            // the bits go to LDS in order, then every thread stores consecutive slots
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                unsigned x = wv[j];
+                while (x) {
+                    const int bit = __ffs((int)x) - 1;
+                    x &= x - 1u;
+                    s_out[o++] = (w0 + tid * 16 + j) * 32 + bit;
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < tot; i += 256) put(base + i, s_out[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                unsigned x = wv[j];
+                while (x) {
+                    const int bit = __ffs((int)x) - 1;
+                    x &= x - 1u;
+                    put(base + o++, (w0 + tid * 16 + j) * 32 + bit);
+                }
+            }
+        }
+        base += tot;
+        __syncthreads();
     }
 }
 
@@ -480,9 +542,10 @@ void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R, int pool)
     const long nchunk = (Lmax + SEL_CHUNK - 1) / SEL_CHUNK;
     t.scores = w.take<int32_t>(B * Lmax);
     t.hist1 = w.take<unsigned>(B * NB1);
-    t.hist2 = w.take<unsigned>(B * 2 * NB2);  // histograms of passes 2 and 3
-    t.state = w.take<SelState>(4 * B);        // state after 0 .. 3 histograms
-    t.cnt = w.take<int>(B * nchunk * 2);
+    t.bits = w.take<unsigned>(B * nchunk * (SEL_CHUNK / 32));
+    t.cand = w.take<int2>(B * nchunk * SEL_CHUNK);
+    t.ccnt = w.take<int32_t>(B * nchunk);
+    t.thr = w.take<Thr>(B);
 }
 
 template <int NHG, int KCH>
@@ -507,8 +570,10 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     // the key cache holds page_size / pool items per page
     const int ps_shift = __builtin_ctz((unsigned)(pg.page_size / pool));
     const int nchunk = (int)((Lmax + SEL_CHUNK - 1) / SEL_CHUNK);
-    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, pg.seq_lens, R, pool, B, top_k, t.hist1, t.hist2,
-                       t.state);
+    const long Lw = (long)nchunk * (SEL_CHUNK / 32);  // bitmap words per row
+    const int PB = Lmax > 1 ? 32 - __builtin_clz((unsigned)(Lmax - 1)) : 1;  // bits of an item index
+    if (nchunk > FCH) return fail(DL_ERR_UNSUPPORTED, "indexer: %ld items per row (<= %d)", Lmax, FCH * SEL_CHUNK);
+    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, t.hist1);
     dim3 gs((unsigned)((Lmax + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK), pg.batch);
     const int nhg = (HI + 15) / 16, kch = (DI + 63) / 64;
 #define DL_SCORE_CASE(H_, K_) \
@@ -519,18 +584,10 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     DL_SCORE_CASE(4, 1) DL_SCORE_CASE(4, 2) DL_SCORE_CASE(4, 3) DL_SCORE_CASE(4, 4)
     return fail(DL_ERR_UNSUPPORTED, "indexer shape heads=%d dim=%d", HI, DI);
 #undef DL_SCORE_CASE
-    dim3 gc(nchunk, B);
-    // 31-bit scores: pass 1 leaves a range of at most 2^23 values; each refinement takes 12 bits, so the
-    // state after histogram 3 is always final.
-    unsigned *h2 = t.hist2, *h3 = t.hist2 + (long)B * NB2;
-    hipLaunchKernelGGL((k_sel_refine<1>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k, t.hist1,
-                       h2, t.state, B);
-    hipLaunchKernelGGL((k_sel_refine<2>), gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k, h2, h3,
-                       t.state, B);
-    hipLaunchKernelGGL(k_sel_count, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k, h3, t.state, B,
-                       nchunk, t.cnt);
-    hipLaunchKernelGGL(k_sel_write, gc, dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, t.state, nchunk,
-                       t.cnt, top_k, sel, sel_score);
+    hipLaunchKernelGGL(k_sel_mark, dim3(nchunk, B), dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k,
+                       t.hist1, t.bits, Lw, t.cand, t.ccnt, nchunk, t.thr);
+    hipLaunchKernelGGL(k_sel_final, dim3(B), dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k, t.bits,
+                       Lw, t.cand, t.ccnt, nchunk, t.thr, PB, sel, sel_score);
     return hip_check("indexer_topk");
 }
 
