@@ -70,12 +70,46 @@ def test_indexer_topk_k_above_length_and_empty_rows():
 
 
 def test_indexer_topk_all_equal_scores():
-    spec = synth.small_fp8_spec(name="flat", seq_lens=(6000, 3000), B=2)
+    # every item is a candidate: 6,000 and 3,000 are selected among in LDS, 20,000 from the workspace
+    spec = synth.small_fp8_spec(name="flat", seq_lens=(6000, 3000, 20000), B=3)
     t = _layer(spec, seed=3, weights=False)
     t["q_idx"].zero_()  # every score is 0: the lowest positions win
     sel, _ = _topk(spec, t)
-    assert np.array_equal(sel[0], np.arange(spec.topk))
-    assert np.array_equal(sel[1], np.arange(spec.topk))
+    for b in range(spec.B):
+        assert np.array_equal(sel[b], np.arange(spec.topk))
+
+
+def _bin1(s: int) -> int:
+    # the scoring kernel's log-linear histogram bin: exact below 256, then 128 bins per binade
+    if s < 256:
+        return s
+    n = s.bit_length() - 1
+    return 256 + (n - 8) * 128 + ((s >> (n - 7)) & 127)
+
+
+def test_indexer_topk_many_candidates_in_the_threshold_bin():
+    # Scores packed densely around 14,000 (head 0 only: 127 k0 + k1 with k0 in [120, 127]), so the histogram bin
+    # holding the k-th score contains many items with distinct scores: the 50,000-item row selects among a few
+    # thousand of them in LDS, the 600,000-item row among more than 8,192, read back from the workspace.
+    spec = synth.small_fp8_spec(name="dense-bin", seq_lens=(50000, 600000), B=2, topk=512)
+    t = _layer(spec, seed=12, weights=False)
+    g = torch.Generator(device="cpu").manual_seed(12)
+    kp = torch.zeros_like(t["k_pool"], device="cpu")
+    kp[..., 0] = torch.randint(120, 128, kp.shape[:-1], generator=g, dtype=torch.int8)
+    kp[..., 1] = torch.randint(-128, 128, kp.shape[:-1], generator=g, dtype=torch.int8)
+    t["k_pool"] = kp.to(DEV)
+    q = torch.zeros_like(t["q_idx"], device="cpu")
+    q[:, 0, 0], q[:, 0, 1] = 127, 1
+    t["q_idx"] = q.to(DEV)
+    orc = oracle.LayerOracle(spec, t)
+    cands = []
+    for b in range(spec.B):
+        sc = orc.row(b, stages=("sel",))["scores"]
+        bins = np.array([_bin1(int(x)) for x in sc])
+        cands.append(int((bins == np.sort(bins)[::-1][spec.topk - 1]).sum()))
+    say(f"[cpu] candidates in the threshold bin: {cands}")
+    assert 256 < cands[0] <= 8192 < cands[1]
+    _check_topk(spec, t)
 
 
 LAYERS = {
