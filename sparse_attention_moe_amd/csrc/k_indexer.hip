@@ -26,8 +26,16 @@
 namespace dl {
 
 static constexpr int NB1 = 256 + 23 * 128;  // log-linear bins covering 0 .. 2^31-1
-static constexpr int SCORE_POS_PER_BLOCK = 1024;  // 4 waves x 4 steps x 64 positions
-static constexpr int SEL_CHUNK = 4096;            // 256 threads x 16 positions
+// Scoring workgroups of score_wpb() waves, 4 steps of 64 positions each.  Sixteen waves fill a compute unit with
+// one workgroup, so its barrier after the page lookups holds back every key load on the unit until all of the
+// unit's lookups are back: with four workgroups per unit, the lookups of the later ones queued behind the key
+// stream of the earlier ones (measured: back at 3 us for the first two, 17 us for the last).  Shapes whose
+// registers do not fit four waves per SIMD (128 each) keep workgroups of four waves.
+__host__ __device__ constexpr int score_wpb(int NHG, int KCH, int RW)
+{
+    return (KCH == 1 && NHG * RW <= 9) || (KCH == 2 && NHG * RW <= 2) ? 16 : 4;
+}
+static constexpr int SEL_CHUNK = 4096;  // select passes: 256 threads x 16 items
 
 // Rows and sequences: with R query rows per sequence (multi-row decode), row i belongs to sequence i / R and
 // is the token at position seq_lens[i / R] - R + i % R, so it sees the positions before and including its own
@@ -147,16 +155,18 @@ __global__ void k_sel_init(unsigned *hist1)
     for (int i = threadIdx.x; i < NB1; i += blockDim.x) hist1[(long)b * NB1 + i] = 0;
 }
 
-// Scores of 1,024 positions of one sequence per workgroup.  NHG groups of 16 indexer heads, KCH chunks of 64 key
-// bytes, RW query rows per sequence: every key is loaded once and scored against all RW rows (RW x NHG matrix
-// instructions per 16 positions and 64 key bytes), each row keeping the positions it sees.
+// Scores of score_wpb() x 256 positions of one sequence per workgroup.  NHG groups of 16 indexer heads, KCH
+// chunks of 64 key bytes, RW query rows per sequence: every key is loaded once and scored against all RW rows (RW x
+// NHG matrix instructions per 16 positions and 64 key bytes), each row keeping the positions it sees.
 template <int NHG, int KCH, int RW>
-__global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ q_idx, const int8_t *__restrict__ k_pool,
+__global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(const int8_t *__restrict__ q_idx, const int8_t *__restrict__ k_pool,
                                                      const int32_t *__restrict__ page_table,
                                                      const int32_t *__restrict__ seq_lens, int pool, int max_pages,
                                                      int ps_shift, int HI, int DI, int32_t *__restrict__ scores,
                                                      long Lmax, unsigned *__restrict__ hist1)
 {
+    constexpr int SCORE_WPB = score_wpb(NHG, KCH, RW);
+    constexpr int SCORE_POS_PER_BLOCK = SCORE_WPB * 4 * 64;
     __shared__ unsigned s_hist[RW][NB1];
     const int sq = blockIdx.y;
     // items (positions, or pools of `pool` positions) of the sequence; row r sees the items of its first
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
     if (blk0 >= L) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
-    for (int i = tid; i < RW * NB1; i += 256) (&s_hist[0][0])[i] = 0;
+    for (int i = tid; i < RW * NB1; i += SCORE_WPB * 64) (&s_hist[0][0])[i] = 0;
 
     // A operand: q rows (indexer heads) for this lane: head hg*16+ln, bytes kc*64 + lg*16 .. +16
     v4i A[RW][NHG][KCH];
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
     for (int st = 0; st < 4; st++)
 #pragma unroll
         for (int sg = 0; sg < 4; sg++) {
-            const long pos = blk0 + (long)(st * 4 + wave) * 64 + sg * 16 + ln;
+            const long pos = blk0 + (long)(st * SCORE_WPB + wave) * 64 + sg * 16 + ln;
             row[st][sg] = pos < L ? ((long)pt[pos >> ps_shift] << ps_shift) + (pos & ps_mask) : -1;
         }
     __syncthreads();
@@ -211,7 +221,7 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
     load_keys(1, K1);
 #pragma unroll
     for (int st = 0; st < 4; st++) {
-        const long g0 = blk0 + (long)(st * 4 + wave) * 64;  // this wave's 64 positions
+        const long g0 = blk0 + (long)(st * SCORE_WPB + wave) * 64;  // this wave's 64 positions
         v4i (&Bk)[4][KCH] = (st & 1) ? K1 : K0;
         int mine[RW];
 #pragma unroll
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(256) void k_index_score(const int8_t *__restrict__ 
 #pragma unroll
     for (int r = 0; r < RW; r++) {
         unsigned *gh = hist1 + ((long)sq * RW + r) * NB1;
-        for (int i = tid; i < NB1; i += 256) {
+        for (int i = tid; i < NB1; i += SCORE_WPB * 64) {
             const unsigned v = s_hist[r][i];
             if (v) atomicAdd(gh + i, v);
         }
@@ -549,13 +559,17 @@ void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R, int pool)
 }
 
 template <int NHG, int KCH>
-static void launch_score(dim3 g, hipStream_t s, const int8_t *q, const int8_t *kp, const dl_pages &pg, int ps_shift,
-                         int HI, int DI, const TopkWs &t, long Lmax, int R, int pool)
+static void launch_score(hipStream_t s, const int8_t *q, const int8_t *kp, const dl_pages &pg, int ps_shift, int HI,
+                         int DI, const TopkWs &t, long Lmax, int R, int pool)
 {
 #define DL_SCORE_R(R_)                                                                                              \
-    if (R == R_)                                                                                                    \
-        hipLaunchKernelGGL((k_index_score<NHG, KCH, R_>), g, dim3(256), 0, s, q, kp, pg.page_table, pg.seq_lens,   \
-                           pool, pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax, t.hist1);
+    if (R == R_) {                                                                                                  \
+        constexpr int W = score_wpb(NHG, KCH, R_), P = W * 4 * 64; /* waves, positions per workgroup */            \
+        const int nblk = (int)((Lmax + P - 1) / P);                                                                 \
+        hipLaunchKernelGGL((k_index_score<NHG, KCH, R_>), dim3(nblk, pg.batch), dim3(W * 64), 0, s, q, kp,           \
+                           pg.page_table, pg.seq_lens, pool, pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax,  \
+                           t.hist1);                                                                                \
+    }
     DL_SCORE_R(1) DL_SCORE_R(2) DL_SCORE_R(3) DL_SCORE_R(4)
 #undef DL_SCORE_R
 }
@@ -574,10 +588,9 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     const int PB = Lmax > 1 ? 32 - __builtin_clz((unsigned)(Lmax - 1)) : 1;  // bits of an item index
     if (nchunk > FCH) return fail(DL_ERR_UNSUPPORTED, "indexer: %ld items per row (<= %d)", Lmax, FCH * SEL_CHUNK);
     hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, t.hist1);
-    dim3 gs((unsigned)((Lmax + SCORE_POS_PER_BLOCK - 1) / SCORE_POS_PER_BLOCK), pg.batch);
     const int nhg = (HI + 15) / 16, kch = (DI + 63) / 64;
 #define DL_SCORE_CASE(H_, K_) \
-    if (nhg == H_ && kch == K_) launch_score<H_, K_>(gs, s, q_idx, k_pool, pg, ps_shift, HI, DI, t, Lmax, R, pool); else
+    if (nhg == H_ && kch == K_) launch_score<H_, K_>(s, q_idx, k_pool, pg, ps_shift, HI, DI, t, Lmax, R, pool); else
     DL_SCORE_CASE(1, 1) DL_SCORE_CASE(1, 2) DL_SCORE_CASE(1, 3) DL_SCORE_CASE(1, 4)
     DL_SCORE_CASE(2, 1) DL_SCORE_CASE(2, 2) DL_SCORE_CASE(2, 3) DL_SCORE_CASE(2, 4)
     DL_SCORE_CASE(3, 1) DL_SCORE_CASE(3, 2) DL_SCORE_CASE(3, 3) DL_SCORE_CASE(3, 4)
