@@ -319,15 +319,18 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     }
 }
 
-// One-shot projection GEMV (one FP8 matrix, either layout, tokens 0..ntok-1): a workgroup owns 128 rows
-// (8 tiles) and a group of 8 K-blocks, wave w the blocks 2w and 2w + 1 of it.  Every wave issues all of its
-// weight loads (32 KB) before any arithmetic, so the whole matrix is in flight at once instead of a few
-// blocks per wave, then adds its token groups' activations; the four waves' sums go through LDS and are added
-// in wave order into partial slot (K group) of [slot][token][row].
+// One-shot projection GEMV (one FP8 matrix, either layout, tokens 0..ntok-1): a workgroup owns PROJ_RT * 16
+// rows (PROJ_RT tiles) and a group of 8 K-blocks, wave w the blocks 2w and 2w + 1 of it.  Every wave issues all
+// of its weight loads (PROJ_RT * 4 KB) before any arithmetic, so the whole matrix is in flight at once instead of
+// a few blocks per wave, then adds its token groups' activations; the four waves' sums go through LDS and are
+// added in wave order into partial slot (K group) of [slot][token][row].  Four tiles per workgroup give W_O
+// (6,144 rows x 64 K-blocks) 768 workgroups, three per compute unit; eight gave 384, so half the units held two
+// and half one, and the kernel lasted as long as the units reading twice the bytes.
+static constexpr int PROJ_RT = 4;
 template <int NS, bool TL>
 __global__ __launch_bounds__(256) void k_proj_shot(GemvArgs a)
 {
-    constexpr int RT = 8, KB = 2;
+    constexpr int RT = PROJ_RT, KB = 2;
     __shared__ v4f s_acc[4][RT][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ln = lane & 15, lg = lane >> 4;
     const int rb = blockIdx.x, kq = blockIdx.y;
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(256) void k_proj_shot(GemvArgs a)
                          : ldw16x2(a.w + (long)((rb * RT + r) * 16 + ln) * a.cols + (kb0 + k) * 128 + lg * 16, 64);
     float ws[KB];
 #pragma unroll
-    for (int k = 0; k < KB; k++) ws[k] = a.wsc[(long)rb * a.nkb + kb0 + k];
+    for (int k = 0; k < KB; k++) ws[k] = a.wsc[(long)(rb * RT / 8) * a.nkb + kb0 + k];  // 128-row scale blocks
     constexpr int TPG = 16 / NS;  // tokens per group: the NS parts share the 16 columns
     for (int t0 = 0; t0 < a.ntok_host; t0 += TPG) {
         const int t = t0 + ln % TPG, sp = ln / TPG;
@@ -370,11 +373,11 @@ __global__ __launch_bounds__(256) void k_proj_shot(GemvArgs a)
 #pragma unroll
         for (int r = 0; r < RT; r++) s_acc[w][r][lane] = sum_parts<NS>(tot[r]);
         __syncthreads();
-        // wave w adds the four waves' sums of tiles 2w, 2w + 1
+        // wave w adds the four waves' sums of its RT / 4 tiles
         if (tv && sp == 0) {
 #pragma unroll
-            for (int q = 0; q < 2; q++) {
-                const int r = 2 * w + q;
+            for (int q = 0; q < RT / 4; q++) {
+                const int r = (RT / 4) * w + q;
                 const v4f v = ((s_acc[0][r][lane] + s_acc[1][r][lane]) + s_acc[2][r][lane]) + s_acc[3][r][lane];
                 *(v4f *)(a.part + (long)kq * a.n_out + (long)t * a.o_ts + (rb * RT + r) * 16 + 4 * lg) = v;
             }
@@ -595,8 +598,9 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
         // share of the items runs concurrently
         if (a.oneshot) {
             if (ns != 4 || !a.part) return fail(DL_ERR_UNSUPPORTED, "one-shot gemv parts=%d", ns);
-            if (a.tiled) hipLaunchKernelGGL((k_proj_shot<4, true>), dim3(a.rows / 128, a.nkb / 8), dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((k_proj_shot<4, false>), dim3(a.rows / 128, a.nkb / 8), dim3(256), 0, s, a);
+            const dim3 g(a.rows / (PROJ_RT * 16), a.nkb / 8);
+            if (a.tiled) hipLaunchKernelGGL((k_proj_shot<4, true>), g, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_proj_shot<4, false>), g, dim3(256), 0, s, a);
             if (!a.reduce_in_consumer) {
                 const dim3 gr((unsigned)((a.n_out + 255) / 256));
                 if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv_reduce<EPI_RESID>), gr, dim3(256), 0, s, a);
