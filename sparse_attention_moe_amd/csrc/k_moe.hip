@@ -289,15 +289,16 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ exper
     build_plan(s_exp, B, ke, E, S, false, s_cnt, s_off, s_mask, p);
 }
 
-// Router top-k fused with the dispatch plan, one workgroup of 1024 threads.  Tokens are taken in blocks
-// of RP_LCAP / E: the block's logits (chunk partials summed in chunk order, plus the bias) go to LDS,
-// then wave w picks the experts of tokens w, w + 16, ... and their gates (softmax over the picked
-// logits, summed in pick order).  With p.active != nullptr the plan follows (B * ke <= 16384).
+// Router top-k, fused with the dispatch plan when one workgroup of 1024 threads routes every token.  A workgroup
+// routes tokens [blockIdx.x * tpb, + tpb), in blocks of RP_LCAP / E: the block's logits (chunk partials summed in
+// chunk order, plus the bias) go to LDS, then wave w picks the experts of tokens w, w + 16, ... and their gates
+// (softmax over the picked logits, summed in pick order).  With p.active != nullptr (a single workgroup) the plan
+// follows (B * ke <= 16384).
 template <int NSLOT>  // experts per lane: E <= 64 * NSLOT
 __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ part, int nchunk, int B, int E, int ke,
                                                      int S, const float *__restrict__ bias,
                                                      int32_t *__restrict__ experts, float *__restrict__ gates,
-                                                     float *__restrict__ logits, MoePlan p)
+                                                     float *__restrict__ logits, MoePlan p, int tpb)
 {
     __shared__ double s_l[RP_LCAP];
     __shared__ int s_exp[16384];
@@ -307,8 +308,9 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
     const int nT = 1024;
     const bool plan = p.active != nullptr;
     const int tb = RP_LCAP / E;
-    for (int b0 = 0; b0 < B; b0 += tb) {
-        const int nb = min(tb, B - b0);
+    const int t0 = blockIdx.x * tpb, t1 = min(B, t0 + tpb);  // this workgroup's tokens
+    for (int b0 = t0; b0 < t1; b0 += tb) {
+        const int nb = min(tb, t1 - b0);
         // two logits per thread per pass, every chunk's partial of both in flight at once, summed in chunk order
         for (int i0 = tid; i0 < nb * E; i0 += 2 * nT) {
             double pc[2][ROUTE_MAXC];
@@ -372,12 +374,18 @@ int launch_route_plan(const double *part, int B, int D, const float *bias, int E
 {
     MoePlan none;
     memset(&none, 0, sizeof none);
-    const MoePlan &pp = p ? *p : none;
+    // up to 16 tokens one workgroup routes them all and builds the plan; more are routed 16 per workgroup (one
+    // token per wave), and the plan kernel follows: the single workgroup's token loop was the cost at batch 64
+    const bool one = B <= 16;
+    const MoePlan &pp = p && one ? *p : none;
+    const dim3 g(one ? 1 : (B + 15) / 16);
+    const int tpb = one ? B : 16;
 #define DL_RP(NS_)                                                                                                  \
-    hipLaunchKernelGGL((k_route_plan<NS_>), dim3(1), dim3(1024), 0, s, part, route_chunks(D), B, E, ke, S, bias,     \
-                       experts, gates, logits, pp)
+    hipLaunchKernelGGL((k_route_plan<NS_>), g, dim3(1024), 0, s, part, route_chunks(D), B, E, ke, S, bias, experts, \
+                       gates, logits, pp, tpb)
     if (E <= 256) DL_RP(4); else DL_RP(16);
 #undef DL_RP
+    if (p && !one) return launch_plan(experts, B, ke, E, S, *p, s);
     return hip_check("route_plan");
 }
 
