@@ -25,7 +25,8 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 // ROUTE_KW per wave; 16 tokens form the N side.  Every fp32 product is exact in fp64 and the sums are fp64.
 // Lane (r, g) = (lane % 16, lane / 16) holds expert r's and token r's features 16 j + 4 g .. + 4 of the wave's
 // range; instruction i of a group takes the i-th of those four, so A and B agree on the K index.  The four
-// waves' sums are added in order through LDS.
+// waves' sums are added in order through LDS.  The grid's third axis strides over the 16-token tiles, so a large
+// batch spreads over more workgroups instead of lengthening each one's serial loop.
 __global__ __launch_bounds__(256) void k_route_partial(const float *__restrict__ h, int B, int D,
                                                        const float *__restrict__ wr, int E, double *__restrict__ part)
 {
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void k_route_partial(const float *__restrict__
         const int k = kq + 16 * j;
         wv[j] = (e < E && k < D) ? *(const v4f *)(wr + (long)e * D + k) : v4f{0.f, 0.f, 0.f, 0.f};
     }
-    for (int t0 = 0; t0 < B; t0 += 16) {
+    for (int t0 = blockIdx.z * 16; t0 < B; t0 += gridDim.z * 16) {
         const int t = t0 + r;
         v4f hv[NJ];
 #pragma unroll
@@ -364,7 +365,7 @@ bool route_plan_ok(int E, int ke, int B) { return E <= RP_MAXE && ke <= 32 && (l
 
 int launch_route_partial(const float *h, int B, int D, const float *w_r, int E, double *part, hipStream_t s)
 {
-    dim3 g((E + 15) / 16, route_chunks(D));
+    dim3 g((E + 15) / 16, route_chunks(D), max(1, min((B + 15) / 16, 64)));
     hipLaunchKernelGGL(k_route_partial, g, dim3(256), 0, s, h, B, D, w_r, E, part);
     return hip_check("route_partial");
 }
