@@ -275,7 +275,8 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
 // Dispatch plan of caller-given picks (experts [B, ke]).  A negative id marks a pair computed elsewhere (an
 // expert another GPU holds): it gets no row and adds nothing.  lo < 0: ids of E or more are clamped to E - 1 so
 // that no access leaves the arrays.  lo >= 0 (one GPU's expert-parallel share): the stack holds experts
-// [lo, lo + E); a pick in that range becomes its local index, any other pick is computed elsewhere.
+// [lo, lo + E); a pick in that range becomes its local index, any other pick is computed elsewhere.  Picks with
+// no expert twice in a token (the router's) take the token-mask ranks; each pick looks back over its own token.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ experts, int B, int ke, int E, int S,
                                                int lo, MoePlan p)
 {
@@ -287,7 +288,14 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ exper
         s_exp[i] = lo < 0 ? (e < 0 ? -1 : min(e, E - 1)) : (e >= lo && e - lo < E ? e - lo : -1);
     }
     __syncthreads();
-    build_plan(s_exp, B, ke, E, S, false, s_cnt, s_off, s_mask, p);
+    int dup = 0;
+    for (int i = threadIdx.x; i < B * ke; i += blockDim.x) {
+        const int e = s_exp[i];
+        if (e >= 0)
+            for (int i2 = i - i % ke; i2 < i; i2++) dup |= s_exp[i2] == e;
+    }
+    const bool distinct = !__syncthreads_or(dup);
+    build_plan(s_exp, B, ke, E, S, distinct, s_cnt, s_off, s_mask, p);
 }
 
 // Router top-k, fused with the dispatch plan when one workgroup of 1024 threads routes every token.  A workgroup

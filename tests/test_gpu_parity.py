@@ -488,3 +488,32 @@ def test_ffn_skips_negative_expert_ids():
     for b in range(B):
         y64 = oracle.ffn(hh[b], exh[b], gh[b].astype(np.float64), orc.expert, spec.E, spec.n_shared)
         assert_close(f"skip row {b} y-h", got[b] - hh[b], y64 - hh[b])
+
+
+def test_ffn_repeated_expert_in_a_token():
+    # caller-given picks may name one expert in two slots of a token: each slot is its own pair (its own gate),
+    # ranked after the token's earlier picks; the oracle applies the expert once per slot as well
+    spec = synth.small_fp8_spec(name="rep", B=4, seq_lens=(900, 600, 300, 1), I=512)
+    t = _layer(spec, seed=78)
+    B = spec.B
+    h = (torch.randn(B, spec.D, generator=torch.Generator().manual_seed(12)) * 0.5).to(DEV)
+    ex = torch.empty(B, spec.ke, dtype=torch.int32, device=DEV)
+    g = torch.empty(B, spec.ke, dtype=torch.float32, device=DEV)
+    dl.moe_route(h, t["w_r"], t["r_bias"], spec.ke, ex, g)
+    exr = ex.clone()
+    exr[1, 2] = exr[1, 0]
+    exr[3, spec.ke - 1] = exr[3, 1]
+    exr[3, 0] = exr[3, 1]
+    y = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
+    say("[gpu] moe_ffn with a repeated expert")
+    dl.moe_ffn(h, exr, g, dl.mat(t["w_gate"], t["w_gate_scale"]), dl.mat(t["w_up"], t["w_up_scale"]),
+               dl.mat(t["w_down"], t["w_down_scale"]), spec.E, spec.n_shared, y, residual=h)
+    torch.cuda.synchronize()
+    orc = oracle.LayerOracle(spec, t)
+    hh = host(h).astype(np.float64)
+    exh, gh = host(exr), host(g)
+    assert len(set(exh[3].tolist())) == spec.ke - 2
+    got = host(y).astype(np.float64)
+    for b in range(B):
+        y64 = oracle.ffn(hh[b], exh[b], gh[b].astype(np.float64), orc.expert, spec.E, spec.n_shared)
+        assert_close(f"rep row {b} y-h", got[b] - hh[b], y64 - hh[b])
