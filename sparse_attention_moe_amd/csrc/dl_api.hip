@@ -318,6 +318,23 @@ static int run_attn_proj(const dl_pages &pg, const void *q, int q_dt, const void
 
 // ------------------------------------------------------------------ FFN
 static constexpr int GU_MAXK = 4;  // most K chunks of the FP8 gate/up pass (partial slots: twice that)
+// Work-queue pieces per unit of the FP8 expert GEMVs (partial slots): gate/up and down.
+static constexpr int GU_NPC = 2, DN_NPC = 1;
+static_assert(GU_NPC <= 2 * GU_MAXK, "gate/up pieces exceed the partial slots");
+
+// Queue mode for a plan-mode FP8 GEMV: npc pieces per unit (at most the bit length of nkb, so none is empty).
+static bool gemv_queue(GemvArgs &a, int *counter, int npc)
+{
+    int maxp = 0;
+    while ((a.nkb >> maxp) > 0) maxp++;
+    if (a.nkb > GEMV_MAXCHUNK || !a.grp_off) return false;
+    a.queue = counter;
+    a.npc = std::min(npc, maxp);
+    a.flat = 0;
+    a.ksplit = 1;
+    a.kchunk = a.nkb;
+    return true;
+}
 
 struct FfnWs {
     MoePlan plan;
@@ -325,7 +342,8 @@ struct FfnWs {
     float *gpart, *upart;      // [2 GU_MAXK, P, I] gate/up partial slots (FP8 path)
     float *Z;                  // [P, I]
     uint8_t *zq; float *zqs;   // 2 parts of Z
-    float *F;                  // [P, D] expert outputs
+    float *F;                  // [DN_NPC, P, D] expert outputs (partial slots in the FP8 path)
+    int *queue;                // [2 GEMV_QINTS] work-queue counters (gate/up, down)
 };
 
 static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool fp8, FfnWs &f)
@@ -340,6 +358,8 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
     f.plan.tok_cnt = w.take<int>(NE);
     f.plan.pair_tok = w.take<int>(P);
     f.plan.pair_idx = w.take<int>(P);
+    f.queue = w.take<int>(2 * GEMV_QINTS);
+    f.plan.queue = fp8 ? f.queue : nullptr;
     f.hq = nullptr; f.hqs = nullptr; f.zq = nullptr; f.zqs = nullptr;
     if (fp8) {
         f.hq = w.take<uint8_t>((long)FFN_PARTS * B * D);
@@ -353,7 +373,7 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
         f.zq = w.take<uint8_t>((long)FFN_PARTS * P * I);
         f.zqs = w.take<float>((long)FFN_PARTS * P * (I / 128));
     }
-    f.F = w.take<float>(P * D);
+    f.F = w.take<float>((fp8 ? DN_NPC : 1) * P * D);
 }
 
 static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, const float *gates, int ke,
@@ -386,7 +406,8 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
         if (!h_split_ready)
             DL_TRY(launch_quant(h, B, nullptr, D, f.hq, f.hqs, (long)B * D, (long)B * (D / 128), FFN_PARTS, s));
         g.aq = f.hq; g.asc = f.hqs; g.aq_part = (long)B * D; g.asc_part = (long)B * (D / 128);
-        gemv_flat(g, FFN_PARTS, EPI_SWIGLU, (long)na_est * (I / 32) * g.max_groups, GU_MAXK);
+        if (!gemv_queue(g, f.queue, GU_NPC))
+            gemv_flat(g, FFN_PARTS, EPI_SWIGLU, (long)na_est * (I / 32) * g.max_groups, GU_MAXK);
         g.part = f.gpart;
         g.part2 = f.upart;
         g.n_out = P * I;
@@ -413,13 +434,18 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
         DL_TRY(launch_swiglu_quant(f.gpart, f.upart, gemv_slots(g), P * I, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I,
                                    P * (I / 128), FFN_PARTS, s));
         d.aq = f.zq; d.asc = f.zqs; d.aq_part = P * I; d.asc_part = P * (I / 128);
+        if (gemv_queue(d, f.queue + GEMV_QINTS, DN_NPC)) {
+            d.part = f.F;
+            d.n_out = P * D;
+            d.reduce_in_consumer = true;
+        }
     } else {
         d.af = f.Z;
     }
     mk.at(7);
     DL_TRY(launch_gemv(d, FFN_PARTS, EPI_STORE, f8, s));
     mk.at(8);
-    DL_TRY(launch_combine(f.F, 1, P * D, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
+    DL_TRY(launch_combine(f.F, d.queue ? d.npc : 1, P * D, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
                           out32, s));
     mk.at(9);
     return DL_OK;

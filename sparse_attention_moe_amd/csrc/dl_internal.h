@@ -88,13 +88,17 @@ struct GemvArgs {
     int oneshot;       // one-shot projection kernel: partial slot per group of 8 K-blocks
     float *part, *part2;
     long n_out;        // elements of the output array (partial buffer stride)
+    int *queue;        // work queue mode (plan mode only): piece counter, zero on entry; npc pieces per unit
+    int npc;
     bool reduce_in_consumer;  // the next kernel sums the partials itself (no reduction launch)
 };
 // Partial slots the GEMV writes: 2 per K chunk in flat mode, else 1 per chunk (0 without a split).
-__host__ __device__ inline int gemv_slots(const GemvArgs &a) { return a.flat ? 2 * a.ksplit : a.ksplit; }
+__host__ __device__ inline int gemv_slots(const GemvArgs &a) { return a.queue ? a.npc : a.flat ? 2 * a.ksplit : a.ksplit; }
 static constexpr int MAX_KSPLIT = 16;
 static constexpr int GEMV_MAXCHUNK = 128;  // most 128-wide K-blocks in one chunk of the FP8 GEMV
 static constexpr int GEMV_MAXMAT = 4096;  // active matrices of one FP8 GEMV (plan mode)
+// Work-queue counters of one FP8 GEMV: GEMV_QPOOLS pools, one counter every GEMV_QSTRIDE ints (256 B apart).
+static constexpr int GEMV_QPOOLS = 8, GEMV_QSTRIDE = 64, GEMV_QINTS = GEMV_QPOOLS * GEMV_QSTRIDE;
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
 // Flat mode for an FP8 GEMV of about `units_est` units: the K split (<= max_ksplit chunks) with chunks no
 // longer than a wave's share of steps.
@@ -140,6 +144,7 @@ struct MoePlan {
     int *tok_cnt;    // [NE]
     int *pair_tok;   // [B*(ke+S)]
     int *pair_idx;   // [B, ke+S]
+    int *queue;      // [2 GEMV_QINTS] work-queue counters of the expert GEMVs, cleared with the plan (nullptr: none)
 };
 int route_chunks(int D);  // hidden-size chunks of the router's partial dot products
 // part [route_chunks(D), B, E] is scratch (fp64).

@@ -45,6 +45,20 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // split between two neighbouring waves: the first writes partial slot 2 kc, the second 2 kc + 1, and a chunk
 // done by one wave zero-fills 2 kc + 1.  Either way consecutive segments of a wave mostly share the matrix
 // and token group (no new metadata) and the load pipeline runs on across segment boundaries.
+//
+// With a work queue the waves take pieces instead of fixed shares.  Every unit's K range is cut at the same
+// npc - 1 points (halving: the first piece is half the range, the next a quarter, ..., the last two equal), and
+// piece j of every unit writes partial slot j, so the sums do not depend on which wave ran a piece.  Pieces are
+// numbered piece-major (all units' first pieces, then all units' second ones, ...), so the long pieces go first
+// and the short ones last.  The pieces are dealt into GEMV_QPOOLS pools (piece i to pool i % GEMV_QPOOLS, so each
+// pool keeps the long-first order and the pools advance through the weights side by side); workgroup b draws
+// from pool b % GEMV_QPOOLS, which with the round-robin
+// dispatch over the eight XCDs is its XCD's own.  Each wave's first piece of its pool is fixed by its index, each
+// further one comes from the pool's device counter, drawn right after the current piece's first loads so that
+// the atomic's round trip stays off the wait for any load issued before it.  A counter serves one atomic at a
+// time: a single one for the whole device made the waves queue for their tickets (and a wave's loads complete
+// in order behind its atomic).  Balance is within each pool: moving drained pools' waves on to the others
+// evened the XCDs out but piled them onto the remaining counters, and both passes got slower.
 template <bool SW, int RT>
 struct Stage {
     v8i A[RT], A2[RT];
@@ -216,7 +230,28 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     const int *goff = a.grp_off ? s_goff : nullptr;
     const long S = units * a.nkb;  // steps of all units
     long s0, s1;
-    if (a.flat) {
+    // queue: pieces, pool, tickets handed out by index, the pool's counter, the next ticket (lane 0), this slot
+    int qtot = 0, npool = 1, pool = 0, qbase = 0, qtk = 0, qslot = 0;
+    int *qc = nullptr;
+    auto qindex = [&](int t) { return (long)t * npool + pool; };  // ticket t of the wave's pool -> piece
+    // piece t -> steps [s0, s1) of unit t % units, K-blocks [nkb - nkb >> j, nkb - nkb >> (j + 1)) with j = t / units
+    auto qpiece = [&](int t, long &ps, long &pe, int &slot) {
+        const int j = (int)(t / units);
+        const long u0 = (t - (long)j * units) * a.nkb;
+        ps = u0 + a.nkb - (a.nkb >> j);
+        pe = u0 + (j + 1 >= a.npc ? a.nkb : a.nkb - (a.nkb >> (j + 1)));
+        slot = j;
+    };
+    if (a.queue) {
+        qtot = (int)(units * a.npc);
+        npool = min((int)gridDim.x, GEMV_QPOOLS);
+        pool = blockIdx.x % npool;
+        qc = a.queue + pool * GEMV_QSTRIDE;
+        qbase = 4 * (((int)gridDim.x - pool + npool - 1) / npool);
+        const int t0 = (blockIdx.x / npool) * 4 + (threadIdx.x >> 6);
+        if (qindex(t0) >= qtot) return;
+        qpiece((int)qindex(t0), s0, s1, qslot);
+    } else if (a.flat) {
         // at least kchunk steps per wave, so a chunk is split at most once
         long W = nwaves;
         if (S / a.kchunk < W) W = S / a.kchunk > 0 ? S / a.kchunk : 1;
@@ -238,10 +273,26 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
         const long ce = unit * a.nkb + min(a.nkb, (kb / a.kchunk + 1) * a.kchunk);
         return ce < s1 ? ce : s1;
     };
-    const bool parts = a.flat || a.ksplit > 1;
+    // the segment after the one ending at e: the rest of the wave's share, or the next piece from the queue
+    auto next_seg = [&](long e_cur, long &ns, long &ne, int &nslot) -> bool {
+        if (a.queue) {
+            const long t = qindex(__builtin_amdgcn_readlane(qtk, 0));
+            if (t >= qtot) return false;
+            qpiece((int)t, ns, ne, nslot);
+            return true;
+        }
+        if (e_cur >= s1) return false;
+        ns = e_cur;
+        ne = seg_end(e_cur);
+        return true;
+    };
+    const bool parts = a.flat || a.ksplit > 1 || a.queue;
     Ctx<RT> c, n;
-    long e = seg_end(s0), e2 = e;
+    long e = a.queue ? s1 : seg_end(s0), ns = 0, ne = 0;
+    int slot = qslot, nslot = 0;
+    bool more = false;
     make_ctx<NS, RT, SW, TL>(a, s0, e, groups, tiles, n_act, goff, nullptr, c);
+    if (!a.queue) slot = a.flat ? 2 * c.kc + c.piece : c.kc;
     v4f tot[RT], tot2[RT];
 #pragma unroll
     for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -249,17 +300,24 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     int kb = c.kb0;  // K-block of step s, in segment c
     long s = s0;
     load_stage<SW, RT, TL>(X, c, a.cols, kb);
+    if (a.queue && lane == 0) qtk = qbase + atomicAdd(qc, 1);
     // Step s: first the loads of step s + 1 into the other stage (from the next segment's context when s + 1
     // starts one; the last step re-reads its own tile, so every step issues the same loads), then the
     // arithmetic of step s, which waits only for the older stage.  The stages alternate by unrolling two
     // steps, never by copying registers that loads are still filling.
     auto step = [&](Stage<SW, RT> &P, Stage<SW, RT> &Q) __attribute__((always_inline)) -> bool {
-        if (s + 1 == e && e < s1) {
-            e2 = seg_end(e);
-            make_ctx<NS, RT, SW, TL>(a, e, e2, groups, tiles, n_act, goff, &c, n);
-            load_stage<SW, RT, TL>(Q, n, a.cols, n.kb0);
+        if (s + 1 == e) {
+            more = next_seg(e, ns, ne, nslot);
+            if (more) {
+                make_ctx<NS, RT, SW, TL>(a, ns, ne, groups, tiles, n_act, goff, &c, n);
+                if (!a.queue) nslot = a.flat ? 2 * n.kc + n.piece : n.kc;
+                load_stage<SW, RT, TL>(Q, n, a.cols, n.kb0);
+                if (a.queue && lane == 0) qtk = qbase + atomicAdd(qc, 1);
+            } else {
+                load_stage<SW, RT, TL>(Q, c, a.cols, kb);
+            }
         } else {
-            load_stage<SW, RT, TL>(Q, c, a.cols, s + 1 < s1 ? kb + 1 : kb);
+            load_stage<SW, RT, TL>(Q, c, a.cols, kb + 1);
         }
         const int kr = kb - c.kb0;
         const float tmask = c.tv ? 1.f : 0.f;
@@ -280,7 +338,6 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
             }
             if (c.tv && ln < TPG) {
                 const long ooff = a.tok_cnt ? (long)(c.off + c.tt) * a.o_ts : (long)c.tt * a.o_ts + (long)c.m * a.o_ms;
-                const long slot = a.flat ? 2 * c.kc + c.piece : c.kc;
 #pragma unroll
                 for (int r = 0; r < RT; r++) {
                     const int rr = c.r0 + r * 16 + 4 * lg;
@@ -305,15 +362,17 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
             }
 #pragma unroll
             for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
-            if (e < s1) {
-                c = n;
-                e = e2;
-            }
+            if (!more) return false;
+            c = n;
+            s = ns;
+            e = ne;
+            slot = nslot;
             kb = c.kb0;
-        } else {
-            kb++;
+            return true;
         }
-        return ++s < s1;
+        kb++;
+        ++s;
+        return true;
     };
     while (step(X, Y) && step(Y, X)) {
     }
@@ -610,14 +669,16 @@ int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s)
         }
         const void *k = gemv_kernel(ns, epi, a.tiled != 0);
         if (!k) return fail(DL_ERR_UNSUPPORTED, "gemv parts=%d", ns);
-        if ((a.flat || a.ksplit > 1) && !a.part) return fail(DL_ERR_UNSUPPORTED, "gemv split without partials");
+        if ((a.flat || a.ksplit > 1 || a.queue) && !a.part) return fail(DL_ERR_UNSUPPORTED, "gemv split without partials");
+        if (a.queue && (!a.grp_off || a.npc < 1 || (a.nkb >> (a.npc - 1)) < 1))
+            return fail(DL_ERR_UNSUPPORTED, "gemv queue of %d pieces over %d K-blocks", a.npc, a.nkb);
         if (a.kchunk > GEMV_MAXCHUNK)
             return fail(DL_ERR_UNSUPPORTED, "gemv K chunk of %d blocks (<= %d)", a.kchunk, GEMV_MAXCHUNK);
         GemvArgs arg = a;
         void *args[] = {(void *)&arg};
         if (hipLaunchKernel(k, dim3(resident_blocks(k, 256)), dim3(256), args, 0, s) != hipSuccess)
             return hip_check("gemv_fp8");
-        if ((a.ksplit > 1 || a.flat) && !a.reduce_in_consumer) {
+        if ((a.ksplit > 1 || a.flat || a.queue) && !a.reduce_in_consumer) {
             const dim3 gr((unsigned)((a.n_out + 255) / 256));
             if (epi == EPI_STORE) hipLaunchKernelGGL((k_gemv_reduce<EPI_STORE>), gr, dim3(256), 0, s, a);
             else if (epi == EPI_RESID) hipLaunchKernelGGL((k_gemv_reduce<EPI_RESID>), gr, dim3(256), 0, s, a);

@@ -199,6 +199,7 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
         if (use_mask) atomicOr(&s_mask[e], 1ull << (i / ke));
     }
     __syncthreads();
+    if (p.queue && tid < 2 * GEMV_QPOOLS) p.queue[tid * GEMV_QSTRIDE] = 0;  // the expert GEMVs' work-queue counters
     if (tid < 64) {
         // lane owns experts [lane * per, (lane + 1) * per)
         const int per = (E + 63) / 64;
