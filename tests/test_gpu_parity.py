@@ -517,3 +517,33 @@ def test_ffn_repeated_expert_in_a_token():
     for b in range(B):
         y64 = oracle.ffn(hh[b], exh[b], gh[b].astype(np.float64), orc.expert, spec.E, spec.n_shared)
         assert_close(f"rep row {b} y-h", got[b] - hh[b], y64 - hh[b])
+
+
+@pytest.mark.parametrize("D,I,E,ke,B", [(128, 128, 8, 2, 3), (384, 384, 16, 4, 5), (2048, 256, 64, 6, 40)])
+def test_ffn_work_queue_shapes(D, I, E, ke, B):
+    # the expert GEMVs' work queues over K ranges of one 128-block (a single piece per unit), of three blocks
+    # (pieces of two and one), and a batch above 16 tokens with 40 x 6 picks over 64 experts (several token
+    # groups per expert); two calls in a row give bit-identical outputs whichever waves took which pieces
+    spec = synth.small_fp8_spec(name=f"q{D}", B=B, seq_lens=tuple(500 + 37 * i for i in range(B)), D=D, I=I, E=E,
+                                ke=ke, topk=256)
+    t = _layer(spec, seed=90 + D)
+    h = (torch.randn(B, D, generator=torch.Generator().manual_seed(D)) * 0.5).to(DEV)
+    ex = torch.empty(B, ke, dtype=torch.int32, device=DEV)
+    g = torch.empty(B, ke, dtype=torch.float32, device=DEV)
+    dl.moe_route(h, t["w_r"], t["r_bias"], ke, ex, g)
+    ys = []
+    say(f"[gpu] moe_ffn queue shapes D={D} I={I} E={E} ke={ke} B={B}")
+    for _ in range(2):
+        y = torch.empty(B, D, dtype=torch.float32, device=DEV)
+        dl.moe_ffn(h, ex, g, dl.mat(t["w_gate"], t["w_gate_scale"]), dl.mat(t["w_up"], t["w_up_scale"]),
+                   dl.mat(t["w_down"], t["w_down_scale"]), E, spec.n_shared, y, residual=h)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    orc = oracle.LayerOracle(spec, t)
+    hh = host(h).astype(np.float64)
+    exh, gh = host(ex), host(g)
+    got = host(ys[0]).astype(np.float64)
+    for b in range(B):
+        y64 = oracle.ffn(hh[b], exh[b], gh[b].astype(np.float64), orc.expert, E, spec.n_shared)
+        assert_close(f"q{D} row {b} y-h", got[b] - hh[b], y64 - hh[b])
