@@ -322,12 +322,16 @@ static constexpr int GU_MAXK = 4;  // most K chunks of the FP8 gate/up pass (par
 static constexpr int GU_NPC = 2, DN_NPC = 1;
 static_assert(GU_NPC <= 2 * GU_MAXK, "gate/up pieces exceed the partial slots");
 
-// Queue mode for a plan-mode FP8 GEMV: npc pieces per unit (at most the bit length of nkb, so none is empty).
-static bool gemv_queue(GemvArgs &a, int *counter, int npc)
+// Queue mode for a plan-mode FP8 GEMV of `pairs` (token, expert) pairs: npc pieces per unit (at most the bit
+// length of nkb, so none is empty).  False (the caller keeps a static split) when the pieces could not be
+// numbered in 31 bits or a piece would exceed the scale registers' 128 K-blocks.
+static bool gemv_queue(GemvArgs &a, int *counter, int npc, long pairs)
 {
     int maxp = 0;
     while ((a.nkb >> maxp) > 0) maxp++;
     if (a.nkb > GEMV_MAXCHUNK || !a.grp_off) return false;
+    // units <= row tiles x token groups, and the groups of all slots are at most the pairs plus one per slot
+    if ((long)(a.rows / 32) * (a.n_active_host + pairs) * std::min(npc, maxp) >= (1L << 31)) return false;
     a.queue = counter;
     a.npc = std::min(npc, maxp);
     a.flat = 0;
@@ -406,7 +410,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
         if (!h_split_ready)
             DL_TRY(launch_quant(h, B, nullptr, D, f.hq, f.hqs, (long)B * D, (long)B * (D / 128), FFN_PARTS, s));
         g.aq = f.hq; g.asc = f.hqs; g.aq_part = (long)B * D; g.asc_part = (long)B * (D / 128);
-        if (!gemv_queue(g, f.queue, GU_NPC))
+        if (!gemv_queue(g, f.queue, GU_NPC, P))
             gemv_flat(g, FFN_PARTS, EPI_SWIGLU, (long)na_est * (I / 32) * g.max_groups, GU_MAXK);
         g.part = f.gpart;
         g.part2 = f.upart;
@@ -434,7 +438,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
         DL_TRY(launch_swiglu_quant(f.gpart, f.upart, gemv_slots(g), P * I, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I,
                                    P * (I / 128), FFN_PARTS, s));
         d.aq = f.zq; d.asc = f.zqs; d.aq_part = P * I; d.asc_part = P * (I / 128);
-        if (gemv_queue(d, f.queue + GEMV_QINTS, DN_NPC)) {
+        if (gemv_queue(d, f.queue + GEMV_QINTS, DN_NPC, P)) {
             d.part = f.F;
             d.n_out = P * D;
             d.reduce_in_consumer = true;

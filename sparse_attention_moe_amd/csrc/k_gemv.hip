@@ -47,15 +47,15 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // and token group (no new metadata) and the load pipeline runs on across segment boundaries.
 //
 // With a work queue the waves take pieces instead of fixed shares.  Every unit's K range is cut at the same
-// npc - 1 points (halving: the first piece is half the range, the next a quarter, ..., the last two equal), and
-// piece j of every unit writes partial slot j, so the sums do not depend on which wave ran a piece.  Pieces are
-// numbered piece-major (all units' first pieces, then all units' second ones, ...), so the long pieces go first
-// and the short ones last.  The pieces are dealt into GEMV_QPOOLS pools (piece i to pool i % GEMV_QPOOLS, so each
-// pool keeps the long-first order and the pools advance through the weights side by side); workgroup b draws
-// from pool b % GEMV_QPOOLS, which with the round-robin
-// dispatch over the eight XCDs is its XCD's own.  Each wave's first piece of its pool is fixed by its index, each
-// further one comes from the pool's device counter, drawn right after the current piece's first loads so that
-// the atomic's round trip stays off the wait for any load issued before it.  A counter serves one atomic at a
+// npc - 1 points (halving: the first piece is half the range, the next a quarter, ..., the last two equal; one
+// piece is the whole range), and piece j of every unit writes partial slot j, so the sums do not depend on which
+// wave ran a piece.  Pieces are numbered piece-major (all units' first pieces, then all units' second ones, ...),
+// so the long pieces go first and the short ones last.  The pieces are dealt into GEMV_QPOOLS pools (piece i to
+// pool i % GEMV_QPOOLS, so each pool keeps the long-first order and the pools advance through the weights side by
+// side); workgroup b draws from pool b % GEMV_QPOOLS, which with the round-robin dispatch over the eight XCDs is
+// its XCD's own.  Each wave's first piece of its pool is fixed by its index, each further one comes from the
+// pool's device counter, drawn right after the current piece's first loads so that the atomic's round trip stays
+// off the wait for any load issued before it.  A counter serves one atomic at a
 // time: a single one for the whole device made the waves queue for their tickets (and a wave's loads complete
 // in order behind its atomic).  Balance is within each pool: moving drained pools' waves on to the others
 // evened the XCDs out but piled them onto the remaining counters, and both passes got slower.
