@@ -137,7 +137,7 @@ class Unfused:
         dev = t["x"].device
         B = spec.B
         self.spec, self.t = spec, t
-        self.pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+        self.pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size, step.key_layout)
         self.sel = torch.empty(B, spec.topk, dtype=torch.int32, device=dev)
         self.h = torch.empty(B, spec.D, dtype=torch.float32, device=dev)
         self.ex = torch.empty(B, spec.ke, dtype=torch.int32, device=dev)
@@ -155,7 +155,7 @@ class Unfused:
 
     def __call__(self):
         sp, t = self.spec, self.t
-        dl.indexer_topk(self.pg, t["q_idx"], t["k_pool"], sp.topk, self.sel, ws=self.ws_i)
+        dl.indexer_topk(self.pg, t["q_idx"], self.keep.keys, sp.topk, self.sel, ws=self.ws_i)
         dl.sparse_attn_decode(self.pg, t["q"], t["kv"], t.get("kv_scale"), sp.H, sp.Dc, sp.Dv, sp.scale, self.sel,
                               sp.topk, self.h, w_uv=self.m["w_uv"], w_o=self.m["w_o"], residual=t["x"], ws=self.ws_a)
         dl.moe_route(self.h, t["w_r"], t["r_bias"], sp.ke, self.ex, self.g, ws=self.ws_r)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DL_ABI_VERSION 1
+#define DL_ABI_VERSION 2
 
 typedef enum {
     DL_OK = 0,
@@ -67,13 +67,23 @@ typedef enum { DL_F32 = 0, DL_BF16 = 1, DL_FP8_E4M3 = 2, DL_I8 = 3, DL_I32 = 4 }
 
 /* Paged cache geometry of a batch.  Position p of row b lives in page
  * page_table[b * max_pages_per_seq + p / page_size], slot p % page_size.
- * page_size is a power of two; entries past ceil(seq_lens[b] / page_size) are never read. */
+ * page_size is a power of two; entries past ceil(seq_lens[b] / page_size) are never read.
+ * key_layout is the layout of the int8 index-key cache (k_pool, or the pool-key cache) that the calls taking
+ * these pages read or write; every other cache is row-major:
+ *   DL_LAYOUT_ROWS  (0): [n_pages, items per page, dim], item-major.
+ *   DL_LAYOUT_TILES (1): the same bytes regrouped per 16 consecutive items of a page (item index i of the
+ *     whole array, group i / 16): inside a group's 16 * dim bytes, byte kc*1024 + g*256 + (i % 16)*16 + j holds
+ *     key byte kc*64 + g*16 + j of item i (kc < dim / 64, g < 4, j < 16).  These are the operand bytes of the
+ *     scoring kernel's int8 matrix instructions, so each of its loads reads 1 KB contiguous instead of sixteen
+ *     64-byte pieces of different lines.  Needs dim % 64 == 0 and items per page a multiple of 16;
+ *     dl_tile_index_keys converts a row-major cache. */
 typedef struct {
     int32_t batch;             /* B >= 1 */
     int32_t page_size;         /* tokens per page, power of two, 1..1024 */
     int32_t max_pages_per_seq; /* columns of page_table; max seq_len <= this * page_size */
     const int32_t *seq_lens;   /* device int32 [B], 0 <= seq_lens[b] <= max_pages_per_seq * page_size */
     const int32_t *page_table; /* device int32 [B, max_pages_per_seq], page ids of the pools */
+    int32_t key_layout;        /* DL_LAYOUT_ROWS or DL_LAYOUT_TILES (index-key cache only) */
 } dl_pages;
 
 /* A stack of weight matrices [count][rows = out][cols = in].
@@ -103,6 +113,10 @@ int dl_abi_version(void);
  * Scales are unchanged.  Done once when weights are loaded, the way Kiln's loader fits each
  * 128 x 128 block to a kernel tile ("Expert parallelism without an all-to-all"). */
 int dl_pack_weights(const dl_mat *src, void *dst, void *stream);
+/* Regroup a row-major int8 index-key cache (n_items = n_pages * items per page rows of dim bytes) into
+ * DL_LAYOUT_TILES at dst (device, n_items * dim bytes, not overlapping src).  n_items % 16 == 0,
+ * dim % 64 == 0, 64 <= dim <= 256.  Done once when a cache is loaded; dl_kv_append keeps it tiled. */
+int dl_tile_index_keys(const int8_t *src, int8_t *dst, int64_t n_items, int32_t dim, void *stream);
 /* Message of the last failed call on this host thread (library-owned, valid until the next call). */
 const char *dl_last_error(void);
 
@@ -124,7 +138,7 @@ const char *dl_last_error(void);
  *   latent   [B, d_c] in lat_dt (DL_F32 or DL_BF16)
  *   key      [B, idx_dim] in key_dt (DL_F32 or DL_BF16); unused (may be NULL) when idx_dim == 0
  *   kv_pool  FP8 codes [n_pages, page_size, d_c], kv_scale fp32 [n_pages, page_size, ceil(d_c/128)],
- *   k_pool   int8 [n_pages, page_size, idx_dim]: in/out — only the addressed slots are written, every
+ *   k_pool   int8 [n_pages, page_size, idx_dim] in pages->key_layout: in/out — only the addressed slots are written, every
  *            other byte of the pools is left unchanged (the exception to "outputs are overwritten").
  * page_table entries of the written pages must be valid page ids of the pools (not checked).
  * Limits: 1 <= d_c <= 1024; 0 <= idx_dim <= 1024; key_scale finite and > 0 when idx_dim > 0.
@@ -141,7 +155,7 @@ int dl_kv_append(const dl_pages *pages, const void *latent, int32_t lat_dt, int3
  * accumulated exactly in int32.  The kept set is the first min(top_k, seq_lens[b]) positions under
  * the order (score descending, position ascending) — ties go to the lower position.
  *   q_idx   int8 [B, n_heads, dim]
- *   k_pool  int8 [n_pages, page_size, dim]
+ *   k_pool  int8 [n_pages, page_size, dim] in pages->key_layout
  *   sel     int32 [B, top_k]  out: kept positions in ascending order, then -1
  *   sel_score int32 [B, top_k] out, nullable: score of each kept position (0 for padding)
  * Limits: 1 <= n_heads <= 64, dim % 16 == 0, dim <= 256, n_heads * dim <= 131071 (int32 bound),

@@ -14,7 +14,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdl.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 DL_F32, DL_BF16, DL_FP8_E4M3, DL_I8, DL_I32 = 0, 1, 2, 3, 4
 STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE", -4: "DL_ERR_UNSUPPORTED",
@@ -26,7 +26,7 @@ EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append",
            "dl_layer_workspace_pooled", "dl_layer_step_pooled",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_moe_ffn_ep", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
-           "dl_profile_read", "dl_probe_read", "dl_probe_null"]
+           "dl_profile_read", "dl_probe_read", "dl_probe_null", "dl_tile_index_keys"]
 N_PHASES = 9
 PHASES = ["indexer_topk", "attention", "projection", "router", "plan_split_h", "expert_gate_up", "split_z",
           "expert_down", "combine"]
@@ -40,7 +40,7 @@ class DLError(RuntimeError):
 
 class Pages(C.Structure):
     _fields_ = [("batch", C.c_int32), ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32),
-                ("seq_lens", C.c_void_p), ("page_table", C.c_void_p)]
+                ("seq_lens", C.c_void_p), ("page_table", C.c_void_p), ("key_layout", C.c_int32)]
 
 
 DL_LAYOUT_ROWS, DL_LAYOUT_TILES = 0, 1
@@ -118,6 +118,7 @@ def load(require_gpu: bool = True):
         L.dl_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
         L.dl_probe_read.argtypes = [P, sz, C.POINTER(sz), P]
         L.dl_probe_null.argtypes = [i32, i32, P]
+        L.dl_tile_index_keys.argtypes = [P, P, C.c_int64, i32, P]
         if L.dl_abi_version() != ABI_VERSION:
             raise ImportError(f"libdl ABI {L.dl_abi_version()} != {ABI_VERSION}")
         _lib = L
@@ -153,8 +154,23 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return t
 
 
-def pages(seq_lens: torch.Tensor, page_table: torch.Tensor, page_size: int) -> Pages:
-    return Pages(seq_lens.numel(), page_size, page_table.shape[1], _ptr(seq_lens), _ptr(page_table))
+def pages(seq_lens: torch.Tensor, page_table: torch.Tensor, page_size: int, key_layout: int = DL_LAYOUT_ROWS) -> Pages:
+    """dl_pages of a batch; key_layout is the layout of the index-key cache read or written with these pages."""
+    return Pages(seq_lens.numel(), page_size, page_table.shape[1], _ptr(seq_lens), _ptr(page_table), key_layout)
+
+
+def key_tiles_ok(dim: int, items_per_page: int) -> bool:
+    """Whether an index-key cache of this shape can be held in DL_LAYOUT_TILES."""
+    return dim % 64 == 0 and 64 <= dim <= 256 and items_per_page % 16 == 0
+
+
+def tile_index_keys(keys: torch.Tensor, stream=None) -> torch.Tensor:
+    """DL_LAYOUT_TILES copy of a row-major int8 index-key cache [..., dim]; same shape and bytes."""
+    L = load()
+    dst = torch.empty_like(keys)
+    _check(L.dl_tile_index_keys(_ptr(keys), _ptr(dst), keys.numel() // keys.shape[-1], keys.shape[-1],
+                                _stream(stream)))
+    return dst
 
 
 def mat(w: Optional[torch.Tensor], scale: Optional[torch.Tensor] = None, layout: int = DL_LAYOUT_ROWS) -> Mat:
@@ -307,7 +323,16 @@ class LayerStep:
             raise ValueError("multi-row decode with pool-granular selection has no entry point")
         B = spec.B * self.R  # rows
         self.keep = []
-        self.pg = pages(t["seq_lens"], t["page_table"], spec.page_size)
+        # the index keys in DL_LAYOUT_TILES where their shape allows (the scoring kernel's loads are then 1 KB
+        # contiguous); the step reads them through the pages' key_layout
+        key_name = "pool_keys" if self.pool > 1 else "k_pool"
+        keys = t[key_name]
+        self.key_layout = DL_LAYOUT_ROWS
+        if tiles and keys is not None and keys.dtype == torch.int8 and key_tiles_ok(spec.DI, spec.page_size // self.pool):
+            keys = tile_index_keys(keys)
+            self.key_layout = DL_LAYOUT_TILES
+        self.keys = keys
+        self.pg = pages(t["seq_lens"], t["page_table"], spec.page_size, self.key_layout)
         d = LayerDesc()
         d.D, d.n_heads, d.d_c, d.d_v = spec.D, spec.H, spec.Dc, spec.Dv
         d.idx_heads, d.idx_dim, d.top_k = spec.HI, spec.DI, spec.topk
@@ -338,9 +363,7 @@ class LayerStep:
         io = LayerIO()
         io.pages = self.pg
         io.x, io.q, io.q_idx = _ptr(t["x"]), _ptr(t["q"]), _ptr(t["q_idx"])
-        io.kv_pool, io.kv_scale, io.k_pool = _ptr(t["kv"]), _ptr(t.get("kv_scale")), _ptr(t["k_pool"])
-        if self.pool > 1:
-            io.k_pool = _ptr(t["pool_keys"])
+        io.kv_pool, io.kv_scale, io.k_pool = _ptr(t["kv"]), _ptr(t.get("kv_scale")), _ptr(self.keys)
         io.y = _ptr(self.y)
         self.dbg = {}
         if debug:

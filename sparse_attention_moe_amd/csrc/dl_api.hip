@@ -105,6 +105,17 @@ static int check_pages(const dl_pages *pg)
     if (!pow2(pg->page_size) || pg->page_size > 1024) return fail(DL_ERR_SHAPE, "page_size %d", pg->page_size);
     if (pg->max_pages_per_seq < 1) return fail(DL_ERR_SHAPE, "max_pages_per_seq %d", pg->max_pages_per_seq);
     if ((long)pg->max_pages_per_seq * pg->page_size > (1L << 30)) return fail(DL_ERR_SHAPE, "context too long");
+    if (pg->key_layout != DL_LAYOUT_ROWS && pg->key_layout != DL_LAYOUT_TILES)
+        return fail(DL_ERR_SHAPE, "key_layout %d", pg->key_layout);
+    return DL_OK;
+}
+
+// Tiled index keys need whole 64-byte chunks and whole 16-item groups in every page.
+static int check_key_tiles(const dl_pages *pg, int dim, int pool)
+{
+    if (pg->key_layout == DL_LAYOUT_TILES && (dim % 64 || (pg->page_size / pool) % 16))
+        return fail(DL_ERR_UNSUPPORTED, "tiled index keys need dim %% 64 == 0 (%d) and 16 | items per page (%d)", dim,
+                    pg->page_size / pool);
     return DL_OK;
 }
 
@@ -573,6 +584,19 @@ int dl_pack_weights(const dl_mat *src, void *dst, void *stream)
     (void)hipGetLastError();
     return launch_pack((const uint8_t *)src->w, (uint8_t *)dst, src->count, src->rows, src->cols, (hipStream_t)stream);
 }
+int dl_tile_index_keys(const int8_t *src, int8_t *dst, int64_t n_items, int32_t dim, void *stream)
+{
+    g_err[0] = 0;
+    if (!src || !dst) return fail(DL_ERR_NULL, "src/dst NULL");
+    if (n_items < 16 || n_items % 16 || dim < 64 || dim > 256 || dim % 64)
+        return fail(DL_ERR_SHAPE, "tile keys: n_items %lld (multiple of 16), dim %d (64, 128, 192 or 256)",
+                    (long long)n_items, dim);
+    const long bytes = (long)n_items * dim;
+    const char *a = (const char *)src, *b = (const char *)dst;
+    if (a < b + bytes && b < a + bytes) return fail(DL_ERR_SHAPE, "src and dst overlap");
+    (void)hipGetLastError();
+    return launch_tile_keys(src, dst, n_items, dim, (hipStream_t)stream);
+}
 const char *dl_last_error(void) { return g_err; }
 
 size_t dl_indexer_topk_rows_workspace(const dl_pages *pages, int32_t rows_per_seq)
@@ -605,6 +629,7 @@ int dl_indexer_topk_pooled(const dl_pages *pages, int32_t pool, const int8_t *q_
         return fail(DL_ERR_UNSUPPORTED, "pool %d (power of two, <= page size %d)", pool, pages->page_size);
     if (!q_idx || !pool_keys || !sel) return fail(DL_ERR_NULL, "q_idx/pool_keys/sel NULL");
     DL_TRY(check_indexer(n_heads, dim, top_pools));
+    DL_TRY(check_key_tiles(pages, dim, pool));
     if ((long)top_pools * pool > 65536) return fail(DL_ERR_SHAPE, "top_pools * pool %ld (<= 65536)", (long)top_pools * pool);
     DL_TRY(check_ws(ws, ws_bytes, dl_indexer_topk_pooled_workspace(pages, pool)));
     (void)hipGetLastError();
@@ -629,6 +654,7 @@ int dl_kv_append(const dl_pages *pages, const void *latent, int32_t lat_dt, int3
     if (idx_dim > 0 && key_dt != DL_F32 && key_dt != DL_BF16) return fail(DL_ERR_DTYPE, "key dtype %d", key_dt);
     if (idx_dim > 0 && !(key_scale > 0.f && key_scale <= 3.4028235e38f))
         return fail(DL_ERR_SHAPE, "key_scale %g (finite, > 0)", (double)key_scale);
+    if (idx_dim > 0) DL_TRY(check_key_tiles(pages, idx_dim, 1));
     (void)hipGetLastError();
     return launch_kv_append(*pages, latent, lat_dt, d_c, key, key_dt, idx_dim, key_scale, kv_pool, kv_scale, k_pool,
                             (hipStream_t)stream);
@@ -645,6 +671,7 @@ int dl_indexer_topk_rows(const dl_pages *pages, int32_t rows_per_seq, const int8
     if ((long)pages->batch * R > 4096) return fail(DL_ERR_SHAPE, "rows %ld (<= 4096)", (long)pages->batch * R);
     if (!q_idx || !k_pool || !sel) return fail(DL_ERR_NULL, "q_idx/k_pool/sel NULL");
     DL_TRY(check_indexer(n_heads, dim, top_k));
+    DL_TRY(check_key_tiles(pages, dim, 1));
     DL_TRY(check_ws(ws, ws_bytes, dl_indexer_topk_rows_workspace(pages, R)));
     (void)hipGetLastError();
     Ws w(ws);
@@ -821,6 +848,7 @@ static int layer_step(const dl_layer_desc *d, const dl_layer_io *io, int R, int 
     if (!pool_ok(&io->pages, pool))
         return fail(DL_ERR_UNSUPPORTED, "pool %d (power of two, <= page size %d)", pool, io->pages.page_size);
     if (d->top_k % pool) return fail(DL_ERR_SHAPE, "top_k %d is not a multiple of pool %d", d->top_k, pool);
+    DL_TRY(check_key_tiles(&io->pages, d->idx_dim, pool));
     if (d->kv_dt == DL_FP8_E4M3 && !io->kv_scale) return fail(DL_ERR_NULL, "FP8 KV needs kv_scale");
     if (d->kv_dt == DL_F32 && io->kv_scale) return fail(DL_ERR_DTYPE, "fp32 KV takes no kv_scale");
     if (!io->x || !io->q || !io->q_idx || !io->kv_pool || !io->k_pool || !io->y) return fail(DL_ERR_NULL, "io tensor NULL");

@@ -33,6 +33,14 @@ __device__ __forceinline__ uint32_t f32x2_to_fp8(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// Byte offset of key byte i of item `row` in an index-key cache of DI bytes per item: row-major, or the tiled
+// layout (per 16 consecutive items: [DI / 64 chunks][4 groups of 16 bytes][16 items][16 bytes]).
+__host__ __device__ __forceinline__ long key_offset(long row, int i, int DI, bool tiles)
+{
+    return tiles ? (row & ~15L) * DI + (i >> 6) * 1024 + ((i >> 4) & 3) * 256 + (row & 15) * 16 + (i & 15)
+                 : row * DI + i;
+}
+
 __device__ __forceinline__ float act_load(const void *p, int dt, long i)
 {
     return dt == DL_BF16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];

@@ -107,6 +107,8 @@ void gemv_flat(GemvArgs &a, int ns, int epi, long units_est, int max_ksplit);
 // the shape does not fit (then nothing is changed).
 bool gemv_oneshot(GemvArgs &a, bool fp8);
 int launch_pack(const uint8_t *src, uint8_t *dst, long count, int rows, int cols, hipStream_t s);
+// Row-major int8 index keys [n_items][DI] -> the tiled key layout (n_items % 16 == 0, DI % 64 == 0).
+int launch_tile_keys(const int8_t *src, int8_t *dst, long n_items, int DI, hipStream_t s);
 
 // SwiGLU of summed gate/up partial slots, split into NS FP8 parts (rows may come from the device).
 int launch_swiglu_quant(const float *pg, const float *pu, int nslot, long stride, long rows_host,

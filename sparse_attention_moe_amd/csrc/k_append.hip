@@ -25,7 +25,7 @@ __device__ __forceinline__ float wave_max_f(float v)
 __global__ __launch_bounds__(256) void k_kv_append(const int *__restrict__ seq_lens, const int *__restrict__ pt,
                                                     int max_pages, int ps_shift, const void *latent, int lat_dt, int Dc,
                                                     const void *key, int key_dt, int DI, float key_scale,
-                                                    uint8_t *kv, float *kv_scale, int8_t *kp)
+                                                    uint8_t *kv, float *kv_scale, int8_t *kp, int key_tiles)
 {
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ps_mask = (1 << ps_shift) - 1;
@@ -66,8 +66,28 @@ __global__ __launch_bounds__(256) void k_kv_append(const int *__restrict__ seq_l
     }
     for (int i = tid; i < DI; i += 256) {
         const float t = __builtin_rintf(__fdiv_rn(act_load(key, key_dt, (long)b * DI + i), key_scale));
-        kp[slot * DI + i] = (int8_t)fminf(fmaxf(t, -127.f), 127.f);
+        kp[key_offset(slot, i, DI, key_tiles)] = (int8_t)fminf(fmaxf(t, -127.f), 127.f);
     }
+}
+
+// Row-major key cache -> tiles: thread o writes the 16 bytes at tiled offset 16 o, read from their item's row.
+__global__ __launch_bounds__(256) void k_tile_keys(const int8_t *__restrict__ src, int8_t *__restrict__ dst, long n16,
+                                                   int DI)
+{
+    for (long o = (long)blockIdx.x * 256 + threadIdx.x; o < n16; o += (long)gridDim.x * 256) {
+        const long byte = o * 16, gsz = 16L * DI, grp = byte / gsz;
+        const int in = (int)(byte - grp * gsz);  // kc * 1024 + g * 256 + p * 16
+        const int kc = in >> 10, g = (in >> 8) & 3, p = (in >> 4) & 15;
+        *(v4i *)(dst + byte) = *(const v4i *)(src + (grp * 16 + p) * DI + kc * 64 + g * 16);
+    }
+}
+
+int launch_tile_keys(const int8_t *src, int8_t *dst, long n_items, int DI, hipStream_t s)
+{
+    const long n16 = n_items * DI / 16;
+    const long blocks = std::min<long>((n16 + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_tile_keys, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n16, DI);
+    return hip_check("tile_keys");
 }
 
 int launch_kv_append(const dl_pages &pg, const void *latent, int lat_dt, int Dc, const void *key, int key_dt, int DI,
@@ -76,7 +96,8 @@ int launch_kv_append(const dl_pages &pg, const void *latent, int lat_dt, int Dc,
     int shift = 0;
     while ((1 << shift) < pg.page_size) shift++;
     hipLaunchKernelGGL(k_kv_append, dim3(pg.batch), dim3(256), 0, s, pg.seq_lens, pg.page_table, pg.max_pages_per_seq,
-                       shift, latent, lat_dt, Dc, key, key_dt, DI, key_scale, kv, kv_scale, kp);
+                       shift, latent, lat_dt, Dc, key, key_dt, DI, key_scale, kv, kv_scale, kp,
+                       pg.key_layout == DL_LAYOUT_TILES);
     return hip_check("kv_append");
 }
 

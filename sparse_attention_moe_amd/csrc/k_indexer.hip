@@ -163,7 +163,7 @@ __global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(co
                                                      const int32_t *__restrict__ page_table,
                                                      const int32_t *__restrict__ seq_lens, int pool, int max_pages,
                                                      int ps_shift, int HI, int DI, int32_t *__restrict__ scores,
-                                                     long Lmax, unsigned *__restrict__ hist1)
+                                                     long Lmax, unsigned *__restrict__ hist1, int tiles)
 {
     constexpr int SCORE_WPB = score_wpb(NHG, KCH, RW);
     constexpr int SCORE_POS_PER_BLOCK = SCORE_WPB * 4 * 64;
@@ -210,9 +210,11 @@ __global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(co
 #pragma unroll
             for (int kc = 0; kc < KCH; kc++) {
                 const int d = kc * 64 + lg * 16;
-                // streaming loads: every key byte is read once per step
+                // streaming loads: every key byte is read once per step.  Tiled keys: the 64 lanes read the
+                // item group's 1 KB chunk kc contiguously (lane = lg * 16 + ln, item ln of the group)
+                const long off = tiles ? (row[st][sg] & ~15L) * DI + kc * 1024 + lane * 16 : row[st][sg] * DI + d;
                 Bk[sg][kc] = (row[st][sg] >= 0 && d < DI)
-                                 ? __builtin_nontemporal_load((const v4i *)(k_pool + row[st][sg] * DI + d))
+                                 ? __builtin_nontemporal_load((const v4i *)(k_pool + off))
                                  : v4i{0, 0, 0, 0};
             }
     };
@@ -568,7 +570,7 @@ static void launch_score(hipStream_t s, const int8_t *q, const int8_t *kp, const
         const int nblk = (int)((Lmax + P - 1) / P);                                                                 \
         hipLaunchKernelGGL((k_index_score<NHG, KCH, R_>), dim3(nblk, pg.batch), dim3(W * 64), 0, s, q, kp,           \
                            pg.page_table, pg.seq_lens, pool, pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax,  \
-                           t.hist1);                                                                                \
+                           t.hist1, pg.key_layout == DL_LAYOUT_TILES);                                              \
     }
     DL_SCORE_R(1) DL_SCORE_R(2) DL_SCORE_R(3) DL_SCORE_R(4)
 #undef DL_SCORE_R

@@ -158,3 +158,25 @@ def test_ffn_ep_rejects_bad_arguments(lib):
     assert lib.dl_moe_ffn_ep(1, 8, 6144, 2048, 1, 1, 8, 32, C.byref(wg), C.byref(wg), C.byref(wd), 31, 1, None, 1,
                              dl.DL_BF16, ws, need, None) == -2
     assert b"w_gate" in lib.dl_last_error()
+
+
+def test_index_key_tiles_reject_bad_shapes(lib):
+    ws = C.c_void_p(0x10000)
+    # the tiling entry point: NULL, items not a multiple of 16, dim not a multiple of 64 (or out of range), overlap
+    assert lib.dl_tile_index_keys(None, 0x2000, 64, 128, None) == -1
+    assert lib.dl_tile_index_keys(0x1000, 0x100000, 40, 128, None) == -2
+    assert lib.dl_tile_index_keys(0x1000, 0x100000, 64, 48, None) == -2
+    assert lib.dl_tile_index_keys(0x1000, 0x100000, 64, 320, None) == -2
+    assert lib.dl_tile_index_keys(0x1000, 0x1800, 64, 128, None) == -2
+    assert b"overlap" in lib.dl_last_error()
+    # an unknown layout, tiles with a key width that is not whole 64-byte chunks, pages of fewer than 16 items
+    bad = dl.Pages(2, 64, 4, 0x1000, 0x2000, 7)
+    assert lib.dl_indexer_topk(C.byref(bad), 1, 1, 16, 128, 2048, 1, None, ws, 1 << 30, None) == -2
+    T = dl.Pages(2, 64, 4, 0x1000, 0x2000, dl.DL_LAYOUT_TILES)
+    assert lib.dl_indexer_topk(C.byref(T), 1, 1, 16, 48, 2048, 1, None, ws, 1 << 30, None) == -4
+    assert b"tiled" in lib.dl_last_error()
+    T8 = dl.Pages(2, 8, 64, 0x1000, 0x2000, dl.DL_LAYOUT_TILES)
+    assert lib.dl_indexer_topk(C.byref(T8), 1, 1, 16, 128, 256, 1, None, ws, 1 << 30, None) == -4
+    # pools of 8 positions leave 8 pool keys per 64-position page
+    assert lib.dl_indexer_topk_pooled(C.byref(T), 8, 1, 1, 16, 128, 64, 1, None, ws, 1 << 30, None) == -4
+    assert lib.dl_kv_append(C.byref(T), 1, dl.DL_F32, 576, 1, dl.DL_F32, 48, 1.0, 1, 1, 1, None) == -4

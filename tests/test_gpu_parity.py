@@ -23,18 +23,29 @@ def _layer(spec, seed=0, weights=True):
     return synth.make_layer(spec, seed=seed, device=DEV, weights=weights)
 
 
-def _topk(spec, t):
+def untile_keys(a: np.ndarray) -> np.ndarray:
+    """Row-major view of an index-key cache [..., items, dim] held in DL_LAYOUT_TILES: per 16 consecutive items,
+    byte kc*1024 + g*256 + p*16 + j is key byte kc*64 + g*16 + j of item p (the layout dl.h documents)."""
+    dim = a.shape[-1]
+    g = a.reshape(-1, dim // 64, 4, 16, 16)          # [group, kc, g, item, j]
+    return g.transpose(0, 3, 1, 2, 4).reshape(a.shape)
+
+
+def _topk(spec, t, tiled=False):
     sel = torch.empty(spec.B, spec.topk, dtype=torch.int32, device=DEV)
     ss = torch.empty_like(sel)
-    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
-    say(f"[gpu] indexer_topk {spec.name} HI={spec.HI} DI={spec.DI} k={spec.topk}")
-    dl.indexer_topk(pg, t["q_idx"], t["k_pool"], spec.topk, sel, ss)
+    keys = dl.tile_index_keys(t["k_pool"]) if tiled else t["k_pool"]
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size, dl.DL_LAYOUT_TILES if tiled else dl.DL_LAYOUT_ROWS)
+    say(f"[gpu] indexer_topk {spec.name} HI={spec.HI} DI={spec.DI} k={spec.topk} tiled={tiled}")
+    dl.indexer_topk(pg, t["q_idx"], keys, spec.topk, sel, ss)
     torch.cuda.synchronize()
+    if tiled:
+        assert np.array_equal(untile_keys(host(keys)), host(t["k_pool"]))
     return host(sel), host(ss)
 
 
-def _check_topk(spec, t, rows=None):
-    sel, ss = _topk(spec, t)
+def _check_topk(spec, t, rows=None, tiled=False):
+    sel, ss = _topk(spec, t, tiled)
     orc = oracle.LayerOracle(spec, t)
     for b in (rows if rows is not None else range(spec.B)):
         r = orc.row(b, stages=("sel",))
@@ -61,6 +72,15 @@ def test_indexer_topk_small(name):
     spec = SMALL[name]
     t = _layer(spec, seed=1, weights=False)
     _check_topk(spec, t)
+
+
+@pytest.mark.parametrize("name", [n for n, sp in SMALL.items() if sp.fp8 and sp.DI % 64 == 0 and sp.page_size % 16 == 0])
+def test_indexer_topk_tiled_keys(name):
+    # the same selections from the key cache in DL_LAYOUT_TILES (and the tiling itself against the documented
+    # byte order)
+    spec = SMALL[name]
+    t = _layer(spec, seed=1, weights=False)
+    _check_topk(spec, t, tiled=True)
 
 
 def test_indexer_topk_k_above_length_and_empty_rows():
@@ -293,10 +313,12 @@ def test_rows_and_tiles_layouts_agree():
 
 
 # ------------------------------------------------------------- current-token append
-@pytest.mark.parametrize("bf16", [False, True])
-def test_kv_append_bit_exact(bf16):
+@pytest.mark.parametrize("bf16,tiled", [(False, False), (True, False), (True, True)])
+def test_kv_append_bit_exact(bf16, tiled):
     t = synth.make_append(seed=3, bf16=bf16, device=DEV)
-    h = {k: synth.to_numpy(v) for k, v in t.items()}
+    h = {k: synth.to_numpy(v) for k, v in t.items()}  # the caches as generated, row-major
+    if tiled:
+        t["k_pool"] = dl.tile_index_keys(t["k_pool"])
     lens, pt, ps = h["seq_lens"], h["page_table"], 64
     kv, kvs, kp = h["kv_pool"].copy(), h["kv_scale"].copy(), h["k_pool"].copy()
     Dc, DI = kv.shape[2], kp.shape[2]
@@ -312,11 +334,13 @@ def test_kv_append_bit_exact(bf16):
         codes, scales, k8 = oracle.kv_append_row(h["latent"][b], h["key"][b], float(h["key_scale"]))
         kv[page, slot], kvs[page, slot], kp[page, slot] = codes, scales, k8
     assert len(written) == lens.shape[0] - 2          # one padding row, one row sharing a slot
-    say(f"[gpu] kv_append bf16={bf16} B={lens.shape[0]} Dc={Dc} DI={DI}")
-    pg = dl.pages(t["seq_lens"], t["page_table"], ps)
+    say(f"[gpu] kv_append bf16={bf16} tiled={tiled} B={lens.shape[0]} Dc={Dc} DI={DI}")
+    pg = dl.pages(t["seq_lens"], t["page_table"], ps, dl.DL_LAYOUT_TILES if tiled else dl.DL_LAYOUT_ROWS)
     dl.kv_append(pg, t["latent"], t["key"], float(h["key_scale"]), t["kv_pool"], t["kv_scale"], t["k_pool"])
     torch.cuda.synchronize()
     got_kv, got_s, got_k = host(t["kv_pool"]), host(t["kv_scale"]), host(t["k_pool"])
+    if tiled:
+        got_k = untile_keys(got_k)
     bad = np.argwhere(got_kv != kv)
     assert bad.size == 0, f"{len(bad)} latent bytes differ, first {bad[:3].tolist()}: {got_kv[tuple(bad[0])]} vs {kv[tuple(bad[0])]}"
     assert np.array_equal(got_s.view(np.uint32), kvs.view(np.uint32))
@@ -391,8 +415,9 @@ def test_ffn_tensor_parallel_slices_sum_to_whole(n):
 
 
 # ------------------------------------------------------------- pool-granular selection
-@pytest.mark.parametrize("pool,offset", [(2, 0), (4, 0), (16, 0), (4, 1)])
-def test_indexer_pooled_bit_exact(pool, offset):
+@pytest.mark.parametrize("pool,offset,tiled", [(2, 0, False), (4, 0, False), (16, 0, False), (4, 1, False),
+                                               (2, 0, True), (4, 0, True)])
+def test_indexer_pooled_bit_exact(pool, offset, tiled):
     # offset 1: the output starts 4 bytes past a 16-byte boundary, which takes the one-position-at-a-time stores
     top_pools = 512 // pool
     spec = synth.spec_replace(synth.small_fp8_spec(name=f"pool{pool}", seq_lens=(9001, 3, 0, 4096, 777), topk=512),
@@ -402,9 +427,10 @@ def test_indexer_pooled_bit_exact(pool, offset):
     buf = torch.empty(B * top_pools * pool + offset, dtype=torch.int32, device=DEV)
     sel = buf[offset:].view(B, top_pools * pool)
     ps = torch.empty(B, top_pools, dtype=torch.int32, device=DEV)
-    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
-    say(f"[gpu] indexer_topk_pooled pool={pool} top_pools={top_pools} offset={offset} lens={spec.seq_lens}")
-    dl.indexer_topk_pooled(pg, pool, t["q_idx"], t["pool_keys"], top_pools, sel, ps)
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size, dl.DL_LAYOUT_TILES if tiled else dl.DL_LAYOUT_ROWS)
+    keys = dl.tile_index_keys(t["pool_keys"]) if tiled else t["pool_keys"]
+    say(f"[gpu] indexer_topk_pooled pool={pool} top_pools={top_pools} offset={offset} tiled={tiled} lens={spec.seq_lens}")
+    dl.indexer_topk_pooled(pg, pool, t["q_idx"], keys, top_pools, sel, ps)
     torch.cuda.synchronize()
     sel, ps = host(sel), host(ps)
     qh, pth, pkh = host(t["q_idx"]), host(t["page_table"]), host(t["pool_keys"])
