@@ -169,7 +169,8 @@ int dl_indexer_topk(const dl_pages *pages, const int8_t *q_idx, const int8_t *k_
  * kernel; "The decode kernels, and why they are opt-in": decode attention gathers the 512 selected pools).
  * The pages do not say how a pool's key is formed, so the pool-key cache is an input: one int8 key per pool
  * of `pool` consecutive positions (pool p = positions [p pool, (p + 1) pool)), paged like the position keys
- * with page_size / pool pools per page: pool_keys int8 [n_pages, page_size / pool, dim], pool p of row b at
+ * with page_size / pool pools per page: pool_keys int8 [n_pages, page_size / pool, dim] in pages->key_layout
+ * (tiles need 16 | page_size / pool), pool p of row b at
  * page page_table[b, p / (page_size / pool)], entry p % (page_size / pool).  Every pool holding a cached
  * position (ceil(seq_lens[b] / pool) of them) is scored exactly as in dl_indexer_topk; the kept pools are
  * the first min(top_pools, pool count) under (score descending, pool ascending), in ascending order, and
@@ -304,7 +305,7 @@ typedef struct dl_layer_io {
     const int8_t *q_idx;  /* [B, idx_heads, idx_dim] */
     const void *kv_pool;  /* [n_pages, page_size, d_c] kv_dt */
     const float *kv_scale;/* [n_pages, page_size, ceil(d_c/128)] or NULL */
-    const int8_t *k_pool; /* [n_pages, page_size, idx_dim] */
+    const int8_t *k_pool; /* [n_pages, page_size, idx_dim] in pages.key_layout */
     void *y;              /* out [B, D] out_dt */
     /* optional debug outputs (nullable), for stage-wise checks of the fused step */
     int32_t *sel;         /* [B, top_k] */
