@@ -536,11 +536,13 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__
     const int nkb = Dv / 128, nrb = (hd + 127) / 128;
     const int per_row = 256 / hd;  // 2 (hd = 128) or 1 (hd = 256)
     const int r = tid / per_row, part = tid % per_row;
-    const int c_lo = part * (Dv / per_row), ncol = Dv / per_row;  // ncol <= 512
+    // ncol <= 256 for every shape attention_merge_uv_ok admits (Dv <= 512 with two threads a row, Dv <= 256 with
+    // one), so 16 code vectors a thread: 64 registers fewer than room for 512 columns, three workgroups a unit
+    const int c_lo = part * (Dv / per_row), ncol = Dv / per_row;
     const uint8_t *wm = wuv + (long)h * hd * Dv;
-    v4i wcode[32];
+    v4i wcode[16];
 #pragma unroll
-    for (int q = 0; q < 32; q++) {
+    for (int q = 0; q < 16; q++) {
         wcode[q] = v4i{0, 0, 0, 0};
         const int c = c_lo + q * 16;
         if (q * 16 < ncol) {
@@ -595,7 +597,7 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__
     // 2. u = W_UV[h] o: thread -> (row r, its columns)
     float acc = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
+    for (int kb = 0; kb < 2; kb++) {
         if (kb * 128 >= ncol) break;
         float blk = 0.f;
 #pragma unroll
