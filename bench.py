@@ -27,7 +27,19 @@ import sparse_attention_moe_amd as dl  # noqa: E402
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-METRIC = "decode layer-steps/s + achieved HBM GB/s (% of peak), batch 8 @ 128K ctx"
+METRIC_BASE = "decode layer-steps/s + achieved HBM GB/s (% of peak)"
+
+
+def metric_label(spec) -> str:
+    """The metric named for the workload actually run (the headline one is batch 8 @ 128K ctx)."""
+    lens = [int(l) for l in spec.seq_lens]
+
+    def ctx(n):
+        return f"{n >> 20}M" if n % (1 << 20) == 0 else f"{n >> 10}K" if n % 1024 == 0 else str(n)
+    c = f"{ctx(lens[0])} ctx" if len(set(lens)) == 1 else f"ragged {ctx(min(lens))}-{ctx(max(lens))} ctx"
+    extra = (f", {spec.R} rows/seq" if getattr(spec, "R", 1) > 1 else "") + \
+            (f", pools of {spec.pool}" if getattr(spec, "pool", 1) > 1 else "")
+    return f"{METRIC_BASE}, batch {spec.B} @ {c}{extra}"
 EXPERT_BYTES_GATE_UP = lambda s: 2 * s.I * s.D + 2 * (s.I // 128) * (s.D // 128) * 4  # per touched expert
 EXPERT_BYTES_DOWN = lambda s: s.D * s.I + (s.D // 128) * (s.I // 128) * 4
 
@@ -197,7 +209,7 @@ def cpu_baseline(spec, t, seconds: float):
     cycled until about `seconds` of CPU work, then scaled to a whole step.  A first, untimed pass over the rows
     makes the host copies of the caches and of the experts the rows touch."""
     import oracle
-    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    cores = oracle.threads()
     orc = oracle.LayerOracle(spec, t)
     rows = spec.B * getattr(spec, "R", 1)
     for b in range(rows):
@@ -211,7 +223,8 @@ def cpu_baseline(spec, t, seconds: float):
         if dt >= seconds or n >= 64 * rows:
             break
     per_step = dt / n * rows
-    return {"value": 1.0 / per_step, "unit": "layer-steps/s", "cores": cores, "kind": "oracle",
+    return {"value": 1.0 / per_step, "unit": "layer-steps/s", "cores": cores, "host_cpus": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "kind": "oracle",
             "sample": f"{n} row evaluations cycling over the {rows} rows of one {spec.name} step (indexer over the "
                       f"full context, attention, projections, router, FFN), {dt:.1f} s, scaled to a whole step"}
 
@@ -309,7 +322,8 @@ def share_step(args, spec, mode: str, n: int = 8):
         gu = touched_n * EXPERT_BYTES_GATE_UP(spec) / n
         dn = touched_n * EXPERT_BYTES_DOWN(spec) / n
     total = b["total"] + gu + dn
-    rec = {"metric": "one GPU's share of an 8-GPU decode layer step (exchanges not run), layer-steps/s",
+    rec = {"metric": f"one GPU's share of an 8-GPU decode layer step (exchanges not run), layer-steps/s, "
+                     f"{metric_label(spec).split(', ', 2)[-1]}",
            "value": round(1000.0 / ms, 2), "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp8-weights/int8-indexer/fp32-accum", "data": "synthetic",
@@ -365,7 +379,9 @@ def main():
     for i in range(args.instances):
         t = synth.make_layer(spec, seed=args.seed, device=dev, instance=i)
         insts.append(t)
+        # debug outputs allocated but switched off: the timed steps write only y, as in production
         steps_obj.append(dl.LayerStep(spec, t, debug=True))
+        steps_obj[-1].debug_outputs(False)
     torch.cuda.synchronize()
     print(f"[bench] generated {args.instances} x {spec.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
           flush=True)
@@ -424,7 +440,12 @@ def main():
         app_bytes = B_app * (2 * spec.Dc + 2 * spec.DI + spec.Dc + 4 * nb + spec.DI)
         app_rec = {"us_per_call": round(app_us, 2), "rows": B_app, "bytes_per_call": app_bytes,
                    "bound": "latency", "achieved_gbs": round(app_bytes / (app_us * 1e-6) / 1e9, 2)}
-    # algorithmic bytes of the steps actually run (touched experts per instance)
+    # algorithmic bytes of the steps actually run (touched experts per instance, from one untimed step each with
+    # the debug outputs on)
+    for so in steps_obj:
+        so.debug_outputs(True)
+        so()
+    torch.cuda.synchronize()
     per_inst = []
     for s in steps_obj:
         ex = s.dbg["experts"].cpu().numpy()
@@ -435,7 +456,7 @@ def main():
     step_gbs = avg_bytes["total"] / (ms * 1e-3) / 1e9
     gu_gbs = avg_bytes["expert_gate_up"] / (ph["expert_gate_up"] * 1e-3) / 1e9
     rec = {
-        "metric": METRIC, "value": round(steps_per_s, 2), "unit": "layer-steps/s", "n_gpus": 1,
+        "metric": metric_label(spec), "value": round(steps_per_s, 2), "unit": "layer-steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8-weights/int8-indexer/fp32-accum",
         "data": "synthetic",

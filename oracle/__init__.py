@@ -69,6 +69,7 @@ def lib():
         L.o_fp8_round.restype = C.c_uint8
         L.o_fp8_round.argtypes = [C.c_double]
         L.o_kv_append_row.argtypes = [P, i32, i32, P, i32, i32, C.c_float, P, P, P]
+        L.o_threads.restype = C.c_int
         L.o_init()
         _lib = L
     return _lib
@@ -90,6 +91,11 @@ def _act(a: np.ndarray):
 
 
 # ------------------------------------------------------------------ decoding
+def threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(lib().o_threads())
+
+
 def fp8_decode(codes) -> np.ndarray:
     L = lib()
     c = np.asarray(codes, dtype=np.uint8).ravel()

@@ -540,3 +540,7 @@ int o_kv_append_row(const void *latent, int32_t lat_dt, int32_t Dc, const void *
 }
 
 void o_init(void) { fp8_table_init(); }
+
+/* Threads the OpenMP loops above run on (for reporting the oracle's timing). */
+#include <omp.h>
+int o_threads(void) { return omp_get_max_threads(); }

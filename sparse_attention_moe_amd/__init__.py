@@ -373,9 +373,8 @@ class LayerStep:
                             gates=torch.empty(B, spec.ke, dtype=torch.float32, device=dev),
                             o=torch.empty(B, spec.H, spec.Dv, dtype=torch.float32, device=dev),
                             y32=torch.empty(B, spec.D, dtype=torch.float32, device=dev))
-            for k, v in self.dbg.items():
-                setattr(io, k, _ptr(v))
         self.io = io
+        self.debug_outputs(debug)
         if self.pool > 1:
             n = L.dl_layer_workspace_pooled(C.byref(d), C.byref(self.pg), self.pool)
         else:
@@ -387,6 +386,12 @@ class LayerStep:
     def mat(self, name: str) -> Mat:
         w, sc, lay = self.w[name]
         return mat(w, sc, lay)
+
+    def debug_outputs(self, on: bool):
+        """Point the step's optional debug outputs at self.dbg (on) or pass NULL for them (off: the production
+        step, which writes only y)."""
+        for k, v in self.dbg.items():
+            setattr(self.io, k, _ptr(v) if on else None)
 
     def __call__(self, stream=None):
         if self.pool > 1:

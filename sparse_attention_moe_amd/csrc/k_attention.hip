@@ -603,6 +603,7 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__
 #pragma unroll
         for (int qq = 0; qq < 8; qq++) {
             const int q = kb * 8 + qq, c = c_lo + q * 16;
+            if (q * 16 >= ncol) break;  // Dv = 128 with two threads a row: 64 columns, s_o holds only Dv values
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const v2f lo = fp8x2_lo((uint32_t)wcode[q][i]), hi = fp8x2_hi((uint32_t)wcode[q][i]);
@@ -640,9 +641,11 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__
     }
 }
 
+// A thread's columns stay inside one 128-column scale block or cover whole blocks: Dv 128, 256 or 512 with
+// hd = 128 (two threads a row), Dv 128 or 256 with hd = 256 (one thread a row).
 bool attention_merge_uv_ok(int Dv, int hd)
 {
-    return Dv % 128 == 0 && Dv <= 512 && (hd == 128 || (hd == 256 && Dv <= 256));
+    return (Dv == 128 || Dv == 256 || Dv == 512) && (hd == 128 || (hd == 256 && Dv <= 256));
 }
 
 int launch_attn_merge_uv(int B, int H, int Dv, int top_k, const float *opart, const float *ml, float *o,
