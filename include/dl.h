@@ -30,9 +30,11 @@
  *               modified; outputs are overwritten completely (including -1 padding).  Descriptor structs (dl_pages,
  *               dl_mat, dl_layer_desc, dl_layer_io) live in HOST memory and are read during the
  *               call only.
- *   Streams     Work is only enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
- *               stream).  Nothing synchronises; the caller orders its own writes of the inputs on
- *               that stream.  Concurrent calls need distinct workspaces.
+ *   Streams     Work is only enqueued on `stream` (a hipStream_t passed as void*).  NULL is HIP's null
+ *               stream, which is torch's default stream: work goes there only when the caller passes
+ *               it, exactly as on any other stream.  The library never synchronises a stream or the
+ *               device; the caller orders its own writes of the inputs on that stream.  Concurrent
+ *               calls need distinct workspaces.
  *   Errors      Arguments are checked on the host before anything is enqueued.  On error the call
  *               returns a negative dl_status, enqueues nothing and sets dl_last_error().  A request
  *               the kernels do not support is rejected (DL_ERR_UNSUPPORTED), never degraded.  A
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define DL_ABI_VERSION 2
+#define DL_ABI_VERSION 3
 
 typedef enum {
     DL_OK = 0,
@@ -107,6 +109,10 @@ typedef struct {
 } dl_mat;
 
 int dl_abi_version(void);
+/* HIP_VERSION the library was compiled against (major * 10^7 + minor * 10^5 + patch).  A loader refuses a
+ * library whose HIP major version differs from the runtime it will share the process with (the library runs on
+ * whatever libamdhip64 the process loaded first, e.g. the one bundled with torch). */
+int dl_hip_version(void);
 
 /* Re-tile a row-major FP8 weight stack (src->layout == DL_LAYOUT_ROWS, rows % 16 == 0,
  * cols % 128 == 0) into DL_LAYOUT_TILES at dst (device, count*rows*cols bytes, not overlapping src).
@@ -314,6 +320,7 @@ typedef struct dl_layer_io {
     float *gates;         /* [B, expert_top_k] */
     float *o;             /* [B, n_heads, d_v] attention output before projection */
     float *y32;           /* [B, D] the output in fp32 before its one rounding */
+    float *logits;        /* [B, n_routed] router logits W_r h + bias (fp64 sums rounded to fp32) */
 } dl_layer_io;
 
 size_t dl_layer_workspace(const dl_layer_desc *desc, const dl_pages *pages);
@@ -334,32 +341,6 @@ int dl_layer_step_rows(const dl_layer_desc *desc, const dl_layer_io *io, int32_t
 size_t dl_layer_workspace_pooled(const dl_layer_desc *desc, const dl_pages *pages, int32_t pool);
 int dl_layer_step_pooled(const dl_layer_desc *desc, const dl_layer_io *io, int32_t pool, void *ws, size_t ws_bytes,
                          void *stream);
-
-/* ---------------------------------------------------------------- measurement
- * When enabled, every dl_layer_step records a HIP event on its stream at each phase boundary:
- *   0 indexer + top-k   1 attention   2 W_UV + W_O (+ activation split)   3 router
- *   4 dispatch plan + split of h   5 expert gate/up (one kernel)   6 split of Z
- *   7 expert down (one kernel)   8 combine
- * dl_profile_read waits for the recorded steps, adds each phase's elapsed milliseconds into
- * ms_sum[DL_N_PHASES], stores the number of steps in *steps and forgets them.  Measurement only:
- * single host thread, events are created on first use and kept until dl_profile_enable(0). */
-#define DL_N_PHASES 9
-int dl_profile_enable(int on);
-int dl_profile_read(double *ms_sum, int64_t *steps);
-
-/* Measurement aid, not part of the step: enqueue one streaming read of the first *bytes_read bytes of
- * the device buffer buf (16-byte non-temporal loads, each wave of a full-device grid reading its own
- * contiguous range, as the expert GEMV streams its weights); *bytes_read (host) receives the count,
- * which rounds `bytes` down to whole rounds of the grid.  Timing it with events on `stream` gives the
- * HBM read rate reachable for the buffer's contents.  DL_ERR_SHAPE if bytes is below one round. */
-int dl_probe_read(const void *buf, size_t bytes, size_t *bytes_read, void *stream);
-
-/* Measurement aid, not part of the step (Kiln's "null" kernel, which does no work and so exposes fixed costs:
- * "What moved the number from 19.4 to 122.9 tokens a second?"): enqueue n_kernels launches, one after
- * another on `stream`, of a kernel with `blocks` workgroups of 256 threads that do nothing.  Timing them
- * with events gives the fixed cost of a dependent launch, the floor under every phase of the step.
- * Limits 1 <= n_kernels <= 1024, 1 <= blocks <= 65536 (else DL_ERR_SHAPE). */
-int dl_probe_null(int32_t n_kernels, int32_t blocks, void *stream);
 
 #ifdef __cplusplus
 }

@@ -14,13 +14,13 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdl.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 DL_F32, DL_BF16, DL_FP8_E4M3, DL_I8, DL_I32 = 0, 1, 2, 3, 4
 STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE", -4: "DL_ERR_UNSUPPORTED",
           -5: "DL_ERR_WORKSPACE", -6: "DL_ERR_HIP"}
 
-EXPORTS = ["dl_abi_version", "dl_last_error", "dl_pack_weights", "dl_kv_append", "dl_indexer_topk_workspace", "dl_indexer_topk",
+EXPORTS = ["dl_abi_version", "dl_hip_version", "dl_last_error", "dl_pack_weights", "dl_kv_append", "dl_indexer_topk_workspace", "dl_indexer_topk",
            "dl_indexer_topk_rows_workspace", "dl_indexer_topk_rows", "dl_indexer_topk_pooled_workspace",
            "dl_indexer_topk_pooled", "dl_layer_workspace_rows", "dl_layer_step_rows",
            "dl_layer_workspace_pooled", "dl_layer_step_pooled",
@@ -63,7 +63,7 @@ class LayerIO(C.Structure):
     _fields_ = [("pages", Pages), ("x", C.c_void_p), ("q", C.c_void_p), ("q_idx", C.c_void_p),
                 ("kv_pool", C.c_void_p), ("kv_scale", C.c_void_p), ("k_pool", C.c_void_p), ("y", C.c_void_p),
                 ("sel", C.c_void_p), ("h", C.c_void_p), ("experts", C.c_void_p), ("gates", C.c_void_p),
-                ("o", C.c_void_p), ("y32", C.c_void_p)]
+                ("o", C.c_void_p), ("y32", C.c_void_p), ("logits", C.c_void_p)]
 
 
 _lib = None
@@ -80,6 +80,7 @@ def load(require_gpu: bool = True):
         L = C.CDLL(LIB_PATH)
         P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
         L.dl_abi_version.restype = C.c_int
+        L.dl_hip_version.restype = C.c_int
         L.dl_pack_weights.argtypes = [C.POINTER(Mat), P, P]
         L.dl_last_error.restype = C.c_char_p
         L.dl_kv_append.argtypes = [C.POINTER(Pages), P, i32, i32, P, i32, i32, C.c_float, P, P, P, P]
@@ -121,8 +122,22 @@ def load(require_gpu: bool = True):
         L.dl_tile_index_keys.argtypes = [P, P, C.c_int64, i32, P]
         if L.dl_abi_version() != ABI_VERSION:
             raise ImportError(f"libdl ABI {L.dl_abi_version()} != {ABI_VERSION}")
+        check_hip_version(L.dl_hip_version(), torch.version.hip)
         _lib = L
     return _lib
+
+
+def check_hip_version(lib_hip: int, torch_hip: Optional[str]):
+    """Refuse a library built against another HIP major version than the runtime torch brings into the process
+    (the library then runs on that runtime: the one loaded first wins).  lib_hip is HIP_VERSION as the library
+    reports it (major * 10^7 + minor * 10^5 + patch); torch_hip is torch.version.hip ("7.0.51831")."""
+    if not torch_hip:
+        raise ImportError("torch is not a ROCm build (torch.version.hip is empty): libdl needs HIP")
+    lib_major = lib_hip // 10_000_000
+    torch_major = int(str(torch_hip).split(".")[0])
+    if lib_major != torch_major:
+        raise ImportError(f"libdl was built against HIP {lib_major}.{lib_hip // 100_000 % 100}, torch runs HIP "
+                          f"{torch_hip}: major versions differ")
 
 
 def _check(rc: int):
@@ -372,7 +387,8 @@ class LayerStep:
                             experts=torch.empty(B, spec.ke, dtype=torch.int32, device=dev),
                             gates=torch.empty(B, spec.ke, dtype=torch.float32, device=dev),
                             o=torch.empty(B, spec.H, spec.Dv, dtype=torch.float32, device=dev),
-                            y32=torch.empty(B, spec.D, dtype=torch.float32, device=dev))
+                            y32=torch.empty(B, spec.D, dtype=torch.float32, device=dev),
+                            logits=torch.empty(B, spec.E, dtype=torch.float32, device=dev))
         self.io = io
         self.debug_outputs(debug)
         if self.pool > 1:

@@ -7,6 +7,9 @@
 
 #include "dl_common.h"
 #include "dl_internal.h"
+#include "../../include/dl_measure.h"
+
+#include <hip/hip_version.h>
 
 #include <algorithm>
 
@@ -569,6 +572,7 @@ using namespace dl;
 extern "C" {
 
 int dl_abi_version(void) { return DL_ABI_VERSION; }
+int dl_hip_version(void) { return HIP_VERSION; }
 
 int dl_pack_weights(const dl_mat *src, void *dst, void *stream)
 {
@@ -745,6 +749,7 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
     return launch_route(h, B, D, w_r, bias, n_experts, top_k, experts, gates, logits, part, (hipStream_t)stream);
 }
 
+
 size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared)
 {
     Ws w(nullptr);
@@ -877,10 +882,10 @@ static int layer_step(const dl_layer_desc *d, const dl_layer_io *io, int R, int 
     if (fuse_route) {
         DL_TRY(launch_route_partial(L.h, B, d->D, d->w_r, d->n_routed, L.rpart, s));
         DL_TRY(launch_route_plan(L.rpart, B, d->D, d->r_bias, d->n_routed, d->expert_top_k, d->n_shared, L.experts,
-                                 L.gates, nullptr, &L.ffn.plan, s));
+                                 L.gates, io->logits, &L.ffn.plan, s));
     } else {
-        DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates, nullptr,
-                            L.rpart, s));
+        DL_TRY(launch_route(L.h, B, d->D, d->w_r, d->r_bias, d->n_routed, d->expert_top_k, L.experts, L.gates,
+                            io->logits, L.rpart, s));
     }
     mk.at(4);
     return run_ffn(L.h, B, d->D, d->inter, L.experts, L.gates, d->expert_top_k, &d->w_gate, &d->w_up, &d->w_down,

@@ -72,7 +72,8 @@ def check_rows(spec, t: Dict[str, torch.Tensor], dbg: Dict[str, torch.Tensor], y
     Every stage in `stages` is compared for every row (a near-tie expert swap skips only that row's FFN)."""
     orc = oracle.LayerOracle(spec, t)
     x = host(t["x"]).astype(np.float64)
-    worst = {"o": 0.0, "h-x": 0.0, "y-h": 0.0, "y": 0.0, "gates": 0.0, "near_ties": 0}
+    worst = {"o": 0.0, "h-x": 0.0, "y-h": 0.0, "y": 0.0, "gates": 0.0, "near_ties": 0, "logit_abs": 0.0,
+             "gap_min": float("inf"), "gaps_below_1e-5": 0}
     n_cmp = {"sel": 0, "o": 0, "h": 0, "route": 0, "y": 0}
     sel_g = host(dbg["sel"]) if "sel" in dbg else None
     for b in rows:
@@ -93,6 +94,15 @@ def check_rows(spec, t: Dict[str, torch.Tensor], dbg: Dict[str, torch.Tensor], y
         n_cmp["h"] += 1
         if "experts" not in r:
             continue
+        if "logits" in dbg:
+            # how far the GPU's router logits sit from the oracle's fp64 ones, against the margin that decides
+            # the expert choice: the gap between the k_e-th and the next oracle logit of the token
+            worst["logit_abs"] = max(worst["logit_abs"], float(np.max(np.abs(host(dbg["logits"])[b] - r["logits"]))))
+            srt = np.sort(r["logits"])[::-1]
+            if len(srt) > spec.ke:
+                gap = float(srt[spec.ke - 1] - srt[spec.ke])
+                worst["gap_min"] = min(worst["gap_min"], gap)
+                worst["gaps_below_1e-5"] += gap < 1e-5
         mm = expert_mismatch(host(dbg["experts"])[b], r["experts"], r["logits"])
         if mm is not None and mm != "near-tie":
             raise AssertionError(f"row {b}: {mm}")

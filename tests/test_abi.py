@@ -11,10 +11,14 @@ import sparse_attention_moe_amd as dl
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "dl.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dl_[a-z_0-9]+)\s*\(", src)))
+def _declared(headers=None):
+    inc = os.path.join(ROOT, "include")
+    names = set()
+    for h in headers or sorted(f for f in os.listdir(inc) if f.endswith(".h")):
+        src = open(os.path.join(inc, h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(dl_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,6 +34,29 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert lib.dl_abi_version() == dl.ABI_VERSION
+
+
+def test_method_header_declares_no_measurement_aid():
+    # dl.h holds the decode step and its workspace queries; probes and phase events live in dl_measure.h
+    step = _declared(["dl.h"])
+    assert not [n for n in step if n.startswith(("dl_probe", "dl_profile"))]
+    assert set(_declared(["dl_measure.h"])) == {"dl_probe_read", "dl_probe_null", "dl_profile_enable",
+                                                 "dl_profile_read"}
+
+
+def test_version_guards(lib):
+    # the ABI version is checked at load; the HIP major version the library was built against must match the
+    # runtime torch brings (the library runs on it)
+    import torch
+    hv = lib.dl_hip_version()
+    assert hv // 10_000_000 >= 6
+    dl.check_hip_version(hv, f"{hv // 10_000_000}.0.51831")  # same major, other minor: accepted
+    with pytest.raises(ImportError, match="major"):
+        dl.check_hip_version(hv, f"{hv // 10_000_000 - 1}.4.0")
+    with pytest.raises(ImportError, match="ROCm"):
+        dl.check_hip_version(hv, None)
+    if torch.version.hip:
+        dl.check_hip_version(hv, torch.version.hip)  # this process's torch
 
 
 def test_indexer_rejects_bad_arguments(lib):
