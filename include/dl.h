@@ -247,6 +247,18 @@ size_t dl_moe_route_workspace(int32_t B, int32_t D, int32_t n_experts);
 int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const float *bias, int32_t n_experts,
                  int32_t top_k, int32_t *experts, float *gates, float *logits, void *ws, size_t ws_bytes, void *stream);
 
+/* dl_moe_route for callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same computation and results as dl_moe_route, with no workspace
+ * argument.  Its scratch (the router's fp64 chunk partials) is a file-scope device array of
+ * DL_MOE_ROUTE_NOALLOC_MAX_SCRATCH bytes inside the library, one per GPU the library runs on, held until the
+ * process ends; the call allocates nothing.  Calls that overlap on one GPU share that array and race: order them
+ * (one stream, or events).  Nothing in the array needs clearing: every call writes what it reads.
+ * Limits: as dl_moe_route, and ceil(D / 1024) * B * n_experts * 8 <= DL_MOE_ROUTE_NOALLOC_MAX_SCRATCH
+ * (DL_ERR_SHAPE otherwise; e.g. B <= 128 at D = 6144 with 256 experts). */
+#define DL_MOE_ROUTE_NOALLOC_MAX_SCRATCH (2u << 20)
+int dl_moe_route_noalloc(const float *h, int32_t B, int32_t D, const float *w_r, const float *bias, int32_t n_experts,
+                         int32_t top_k, int32_t *experts, float *gates, float *logits, void *stream);
+
 /* ---------------------------------------------------------------- S7 - S9
  * Expert FFN (Kiln, "A collective costs per graph ...": each expert applied once to all of its
  * tokens; "What moved the number ...": experts with no token are skipped):

@@ -24,7 +24,7 @@ EXPORTS = ["dl_abi_version", "dl_hip_version", "dl_last_error", "dl_pack_weights
            "dl_indexer_topk_rows_workspace", "dl_indexer_topk_rows", "dl_indexer_topk_pooled_workspace",
            "dl_indexer_topk_pooled", "dl_layer_workspace_rows", "dl_layer_step_rows",
            "dl_layer_workspace_pooled", "dl_layer_step_pooled",
-           "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route",
+           "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route", "dl_moe_route_noalloc",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_moe_ffn_ep", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
            "dl_profile_read", "dl_probe_read", "dl_probe_null", "dl_tile_index_keys"]
 N_PHASES = 9
@@ -106,6 +106,7 @@ def load(require_gpu: bool = True):
         L.dl_moe_route_workspace.restype = sz
         L.dl_moe_route_workspace.argtypes = [i32, i32, i32]
         L.dl_moe_route.argtypes = [P, i32, i32, P, P, i32, i32, P, P, P, P, sz, P]
+        L.dl_moe_route_noalloc.argtypes = [P, i32, i32, P, P, i32, i32, P, P, P, P]
         L.dl_moe_ffn_workspace.restype = sz
         L.dl_moe_ffn_workspace.argtypes = [i32, i32, i32, i32, i32, i32]
         L.dl_moe_ffn.argtypes = [P, i32, i32, i32, P, P, i32, C.POINTER(Mat), C.POINTER(Mat), C.POINTER(Mat), i32,
@@ -262,6 +263,17 @@ def moe_route(h, w_r, bias, top_k, experts, gates, logits=None, ws=None, stream=
         ws = workspace(L.dl_moe_route_workspace(B, D, E), h.device)
     _check(L.dl_moe_route(_ptr(h), B, D, _ptr(w_r), _ptr(bias), E, top_k, _ptr(experts), _ptr(gates), _ptr(logits),
                           _ptr(ws), ws.numel(), _stream(stream)))
+    return experts, gates
+
+
+def moe_route_noalloc(h, w_r, bias, top_k, experts, gates, logits=None, stream=None):
+    """dl_moe_route_noalloc: the router with the library's own static device scratch (no workspace, no
+    allocation); calls that overlap on one GPU race."""
+    L = load()
+    B, D = h.shape
+    E = w_r.shape[0]
+    _check(L.dl_moe_route_noalloc(_ptr(h), B, D, _ptr(w_r), _ptr(bias), E, top_k, _ptr(experts), _ptr(gates),
+                                  _ptr(logits), _stream(stream)))
     return experts, gates
 
 

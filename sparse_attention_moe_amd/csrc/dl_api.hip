@@ -12,6 +12,7 @@
 #include <hip/hip_version.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace dl {
 
@@ -565,6 +566,38 @@ static int check_proj(int H, int Dv, const dl_mat *w_uv, const dl_mat *w_o, int 
     return DL_OK;
 }
 
+// ------------------------------------------------------------------ the router without a workspace
+// Scratch of dl_moe_route_noalloc: the router's fp64 chunk partials live in this file-scope device array (each
+// device that runs the library holds its own copy until the process ends).  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in); it takes the device address from hipGetSymbolAddress,
+// once per device, and passes that.
+static constexpr size_t DL_ROUTE_SCRATCH_BYTES = (size_t)DL_MOE_ROUTE_NOALLOC_MAX_SCRATCH;
+static __device__ __align__(256) double scratch[DL_ROUTE_SCRATCH_BYTES / sizeof(double)];
+
+static constexpr int DL_MAX_DEVICES = 64;
+static double *g_scratch_ptr[DL_MAX_DEVICES];
+static bool g_scratch_init[DL_MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+// The scratch array's device address on the current device (looked up once per device).
+static int route_scratch(double **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(DL_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= DL_MAX_DEVICES) return fail(DL_ERR_UNSUPPORTED, "device %d (< %d)", dev, DL_MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_init[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(DL_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = (double *)ptr;
+        g_scratch_init[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    return DL_OK;
+}
+
 }  // namespace dl
 
 using namespace dl;
@@ -749,6 +782,25 @@ int dl_moe_route(const float *h, int32_t B, int32_t D, const float *w_r, const f
     return launch_route(h, B, D, w_r, bias, n_experts, top_k, experts, gates, logits, part, (hipStream_t)stream);
 }
 
+
+int dl_moe_route_noalloc(const float *h, int32_t B, int32_t D, const float *w_r, const float *bias, int32_t n_experts,
+                         int32_t top_k, int32_t *experts, float *gates, float *logits, void *stream)
+{
+    g_err[0] = 0;
+    if (!h || !w_r || !experts || !gates) return fail(DL_ERR_NULL, "h/w_r/experts/gates NULL");
+    if (B < 1 || B > 65536 || D < 1) return fail(DL_ERR_SHAPE, "B=%d D=%d", B, D);
+    if (top_k < 1 || top_k > 32 || n_experts < top_k || n_experts > 1024)
+        return fail(DL_ERR_SHAPE, "top_k %d of %d experts", top_k, n_experts);
+    if (D % 4 || D > 16384) return fail(DL_ERR_UNSUPPORTED, "router hidden size %d (multiple of 4, <= 16384)", D);
+    const size_t need = (size_t)route_chunks(D) * B * n_experts * sizeof(double);
+    if (need > DL_ROUTE_SCRATCH_BYTES)
+        return fail(DL_ERR_SHAPE, "router scratch %zu bytes > %zu (chunks of 1,024 features x B x experts x 8 B)",
+                    need, DL_ROUTE_SCRATCH_BYTES);
+    double *part = nullptr;
+    DL_TRY(route_scratch(&part));
+    (void)hipGetLastError();
+    return launch_route(h, B, D, w_r, bias, n_experts, top_k, experts, gates, logits, part, (hipStream_t)stream);
+}
 
 size_t dl_moe_ffn_workspace(int32_t B, int32_t D, int32_t inter, int32_t top_k, int32_t n_routed, int32_t n_shared)
 {
