@@ -290,7 +290,7 @@ static int run_attn_proj(const dl_pages &pg, const void *q, int q_dt, const void
                          int kv_dt, int H, int Dc, int Dv, float sm_scale, const int32_t *sel, int top_k,
                          const dl_mat *w_uv, const dl_mat *w_o, const void *resid, int resid_dt, float *o,
                          float *out, const AttnWs &a, uint8_t *hq, float *hqs, bool *h_split, hipStream_t s,
-                         const Marks &mk, int R = 1)
+                         const Marks &mk, int R = 1, bool o_wanted = true)
 {
     const int B = pg.batch * R;  // rows
     if (h_split) *h_split = false;
@@ -308,7 +308,9 @@ static int run_attn_proj(const dl_pages &pg, const void *q, int q_dt, const void
                             s, R));
     mk.at(2);
     const long K = (long)H * hd;
-    DL_TRY(launch_attn_merge_uv(B, H, Dv, top_k, a.opart, a.ml, o, (const uint8_t *)w_uv->w, w_uv->scale, hd,
+    // with W_UV fused into the merge, o is only an output when the caller asks for it
+    DL_TRY(launch_attn_merge_uv(B, H, Dv, top_k, a.opart, a.ml, o_wanted ? o : nullptr, (const uint8_t *)w_uv->w,
+                                w_uv->scale, hd,
                                 w_uv->layout == DL_LAYOUT_TILES, a.uq, a.uqs, (long)B * K, (long)B * (K / 128), s));
     GemvArgs g = mat_args(w_o);
     g.n_active_host = 1;
@@ -756,7 +758,7 @@ int dl_sparse_attn_decode(const dl_pages *pages, const void *q, int32_t q_dt, co
     attn_ws_layout(w, pages->batch, n_heads, d_v, top_k, w_uv, w_o, a);
     float *o = w_o ? a.o : out;
     return run_attn_proj(*pages, q, q_dt, kv_pool, kv_scale, kv_dt, n_heads, d_c, d_v, sm_scale, sel, top_k, w_uv, w_o,
-                         residual, res_dt, o, out, a, nullptr, nullptr, nullptr, s, Marks());
+                         residual, res_dt, o, out, a, nullptr, nullptr, nullptr, s, Marks(), 1, !w_o);
 }
 
 size_t dl_moe_route_workspace(int32_t B, int32_t D, int32_t n_experts)
@@ -929,7 +931,7 @@ static int layer_step(const dl_layer_desc *d, const dl_layer_io *io, int R, int 
     bool h_split = false;
     DL_TRY(run_attn_proj(pg, io->q, d->q_dt, io->kv_pool, io->kv_scale, d->kv_dt, d->n_heads, d->d_c, d->d_v,
                          d->sm_scale, L.sel, d->top_k, wuv, &d->w_o, io->x, d->q_dt, L.o, L.h, L.attn,
-                         f8_ffn ? L.ffn.hq : nullptr, L.ffn.hqs, &h_split, s, mk, R));
+                         f8_ffn ? L.ffn.hq : nullptr, L.ffn.hqs, &h_split, s, mk, R, io->o != nullptr));
     mk.at(3);
     if (fuse_route) {
         DL_TRY(launch_route_partial(L.h, B, d->D, d->w_r, d->n_routed, L.rpart, s));

@@ -186,6 +186,9 @@ __global__ __launch_bounds__(256) void k_attn(const void *__restrict__ q, int q_
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
+#ifndef DL_ATT_NT_STORE
+#define DL_ATT_NT_STORE 1
+#endif
 static constexpr int AM_NJ = 64;        // kept positions per chunk
 static constexpr int AM_MAXSPLIT = 32;  // splits of the kept positions
 static constexpr int AM_MAXPPS = 512;   // kept positions per split (8 chunks)
@@ -313,35 +316,52 @@ __global__ __launch_bounds__(256, 1) void k_attn_mla(const uint16_t *__restrict_
     for (int vb = 0; vb < NVB; vb++)
 #pragma unroll
         for (int t = 0; t < 8; t++) acc[vb][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // gather of chunk c into registers: 16 codes per load, and the chunk's block scales (a position past the
+    // kept ones reads code 0 and scale 0)
+    constexpr int NSC = (AM_NJ * NB + 255) / 256;  // scales per thread
+    v4i GR[NLD];
+    float GS[NSC];
+    auto gather = [&](int c) __attribute__((always_inline)) {
+        const int cbase = c * AM_NJ;
+#pragma unroll
+        for (int k = 0; k < NLD; k++) {
+            const int id = k * 256 + tid;
+            GR[k] = v4i{0, 0, 0, 0};
+            if (id < AM_NJ * (Dc / 16)) {
+                const long row = s_row[cbase + id / (Dc / 16)];
+                if (row >= 0) GR[k] = *(const v4i *)(kv + row * Dc + (id % (Dc / 16)) * 16);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NSC; k++) {
+            const int i = k * 256 + tid;
+            GS[k] = 0.f;
+            if (i < AM_NJ * NB) {
+                const long row = s_row[cbase + i / NB];
+                if (row >= 0) GS[k] = ks[row * NB + i % NB];
+            }
+        }
+    };
+    // (Issuing the next chunk's gather before computing the current one measured slower: its registers, live
+    // across the chunk's arithmetic, spill, and each spill reload waits behind the loads in flight.)
     for (int ch = 0; ch < nch; ch++) {
         const int cb = ch * AM_NJ;  // chunk base within the split
         __syncthreads();            // s_row is complete; the previous chunk's LDS reads are done
-        // gather: 16 codes per load, converted to bf16 in registers, two 16-byte LDS writes
-        {
-            v4i R[NLD];
+        gather(ch);
+        // chunk ch's codes converted to bf16 (two 16-byte LDS writes per load) and its scales into LDS
 #pragma unroll
-            for (int k = 0; k < NLD; k++) {
-                const int id = k * 256 + tid;
-                R[k] = v4i{0, 0, 0, 0};
-                if (id < AM_NJ * (Dc / 16)) {
-                    const long row = s_row[cb + id / (Dc / 16)];
-                    if (row >= 0) R[k] = *(const v4i *)(kv + row * Dc + (id % (Dc / 16)) * 16);
-                }
+        for (int k = 0; k < NLD; k++) {
+            const int id = k * 256 + tid;
+            if (id < AM_NJ * (Dc / 16)) {
+                __bf16 *dst = s_cb + (id / (Dc / 16)) * CBP + (id % (Dc / 16)) * 16;
+                *(v8bf *)dst = fp8x8_to_bf16((uint32_t)GR[k][0], (uint32_t)GR[k][1]);
+                *(v8bf *)(dst + 8) = fp8x8_to_bf16((uint32_t)GR[k][2], (uint32_t)GR[k][3]);
             }
-            for (int i = tid; i < AM_NJ * NB; i += 256) {
-                const int pos = i / NB, blk = i % NB;
-                const long row = s_row[cb + pos];
-                s_sc[blk][pos] = row < 0 ? 0.f : ks[row * NB + blk];
-            }
+        }
 #pragma unroll
-            for (int k = 0; k < NLD; k++) {
-                const int id = k * 256 + tid;
-                if (id < AM_NJ * (Dc / 16)) {
-                    __bf16 *dst = s_cb + (id / (Dc / 16)) * CBP + (id % (Dc / 16)) * 16;
-                    *(v8bf *)dst = fp8x8_to_bf16((uint32_t)R[k][0], (uint32_t)R[k][1]);
-                    *(v8bf *)(dst + 8) = fp8x8_to_bf16((uint32_t)R[k][2], (uint32_t)R[k][3]);
-                }
-            }
+        for (int k = 0; k < NSC; k++) {
+            const int i = k * 256 + tid;
+            if (i < AM_NJ * NB) s_sc[i % NB][i / NB] = GS[k];
         }
         __syncthreads();
         // values: thread -> 8 features x 8 positions, transposed to [feature][position]
@@ -364,21 +384,40 @@ __global__ __launch_bounds__(256, 1) void k_attn_mla(const uint16_t *__restrict_
         // scores: S[j] = 16 heads x positions j*16 .. +16; lane holds heads 4 lg + i of position cb + j*16 + ln
         v4f S[4];
         if (active) {
+            // the four position tiles are four independent accumulator chains, interleaved so that consecutive
+            // instructions do not wait on each other; each 128-feature block's operands are read before its
+            // instructions (one wave per SIMD: nothing else would hide the LDS latency)
+            v4f sacc[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) sacc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int blk = 0; blk < NB; blk++) {
+                v4f a[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) a[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q2 = 0; q2 < 4; q2 += 2) {
+                    v8bf Bt[2][4];
+#pragma unroll
+                    for (int q = 0; q < 2; q++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            if (blk * 4 + q2 + q < KQ)
+                                Bt[q][j] = *(const v8bf *)(s_cb + (j * 16 + ln) * CBP + lg * 8 + (blk * 4 + q2 + q) * 32);
+#pragma unroll
+                    for (int q = 0; q < 2; q++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            if (blk * 4 + q2 + q < KQ) a[j] = mfma_bf16(Aq[blk * 4 + q2 + q], Bt[q][j], a[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) sacc[j] += a[j] * s_sc[blk][j * 16 + ln];
+            }
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const __bf16 *cr = s_cb + (j * 16 + ln) * CBP + lg * 8;
-                v4f sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int blk = 0; blk < NB; blk++) {
-                    v4f a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = blk * 4; kk < (blk * 4 + 4 < KQ ? blk * 4 + 4 : KQ); kk++)
-                        a = mfma_bf16(Aq[kk], *(const v8bf *)(cr + kk * 32), a);
-                    sacc += a * s_sc[blk][j * 16 + ln];
-                }
                 const bool valid = s_row[cb + j * 16 + ln] >= 0;
 #pragma unroll
-                for (int i = 0; i < 4; i++) S[j][i] = valid ? sacc[i] * sl2 : -INFINITY;
+                for (int i = 0; i < 4; i++) S[j][i] = valid ? sacc[j][i] * sl2 : -INFINITY;
             }
         }
         __syncthreads();  // every wave's scores are done: the latent rows become P; the values are complete
@@ -427,12 +466,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_mla(const uint16_t *__restrict_
                     Ah[e] = hb;
                     Al[e] = (__bf16)(x - (float)hb);
                 }
+                v8bf Bv[8];
 #pragma unroll
                 for (int t = 0; t < 8; t++) {
                     const int f = vb * 128 + t * 16 + ln;
-                    const v8bf Bv = *(const v8bf *)(s_v + f * PP + (((kstep * 4 + lg) ^ ((vb * 8 + t) & 7)) << 3));
-                    acc[vb][t] = mfma_bf16(Ah, Bv, acc[vb][t]);
-                    acc[vb][t] = mfma_bf16(Al, Bv, acc[vb][t]);
+                    Bv[t] = *(const v8bf *)(s_v + f * PP + (((kstep * 4 + lg) ^ ((vb * 8 + t) & 7)) << 3));
+                }
+#pragma unroll
+                for (int t = 0; t < 8; t++) {
+                    acc[vb][t] = mfma_bf16(Ah, Bv[t], acc[vb][t]);
+                    acc[vb][t] = mfma_bf16(Al, Bv[t], acc[vb][t]);
                 }
             }
         }
@@ -457,8 +500,12 @@ __global__ __launch_bounds__(256, 1) void k_attn_mla(const uint16_t *__restrict_
                 // streaming store: read once by the merge, so it should not sit dirty in the last-level
                 // cache until the expert weight stream evicts it (its write-back would then compete with
                 // that stream for HBM)
+#if DL_ATT_NT_STORE
                 __builtin_nontemporal_store(*(const v4f *)&st[head][col],
                                             (v4f *)(op + (long)head * Dv + vb * 128 + half * 64 + col));
+#else
+                *(v4f *)(op + (long)head * Dv + vb * 128 + half * 64 + col) = *(const v4f *)&st[head][col];
+#endif
             }
         }
     }
@@ -509,7 +556,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ op
     }
 }
 
-// Split merge fused with the per-head value up-projection and its FP8 split: one workgroup per (row, head).
+// Split merge fused with the per-head value up-projection and its FP8 split, one workgroup per (row, head): the
+// form for a few rows with many splits each (at batch 8, 32 splits a row it is ~3 µs faster than the per-head
+// form below, which wins once several rows share a head's W_UV).
 //   o      = merged attention output (also stored: [B, H, Dv])
 //   u[r]   = sum_v W_UV[h][r][v] o[v]   on the vector units in fp32 (each code decoded exactly, one scale
 //            per 128-column block), hd = 128 or 256 rows
@@ -518,7 +567,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ op
 // Every global load (split maxima and sums, the partial sums, the W_UV codes) is issued up front.  Threads
 // take 4 features of one half of the splits; the halves meet in LDS.
 template <int NSU>
-__global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__ opart, const float *__restrict__ ml,
+__global__ __launch_bounds__(256) void k_attn_merge_uv_row(const float *__restrict__ opart, const float *__restrict__ ml,
                                                        int nsplit, int H, int Dv, float *__restrict__ o,
                                                        const uint8_t *__restrict__ wuv, const float *__restrict__ wsc,
                                                        int hd, int tiled, uint8_t *__restrict__ uq,
@@ -591,7 +640,7 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__
     for (int v = tid; v < Dv; v += 256) {
         const float ov = s_half[0][v] + s_half[1][v];
         s_o[v] = ov;
-        o[(long)bh * Dv + v] = ov;
+        if (o) o[(long)bh * Dv + v] = ov;
     }
     __syncthreads();
     // 2. u = W_UV[h] o: thread -> (row r, its columns)
@@ -641,20 +690,235 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv(const float *__restrict__
     }
 }
 
-// A thread's columns stay inside one 128-column scale block or cover whole blocks: Dv 128, 256 or 512 with
-// hd = 128 (two threads a row), Dv 128 or 256 with hd = 256 (one thread a row).
+// Split merge fused with the per-head value up-projection and its FP8 split: one workgroup per (head h, block of at
+// most MW_RB rows), so W_UV[h] is read once per block of rows instead of once per row, and applied on the matrix
+// cores.  Blocks of one head are MW_HEADS workgroups apart in the grid, so they share an XCD and its L2.
+//   o      = merged attention output, o[b] = sum_s w_s O_s[b] with w_s = e^(m_s - M) / sum_s e^(m_s - M) l_s
+//            summed in split order (also stored when o != nullptr: [rows, H, Dv]);
+//   u[b]   = W_UV[h] o[b]: the FP8 codes of W_UV are exact bf16 values, and o enters as bf16 high and low halves
+//            (o * block scale, about 16 significant bits), so v_mfma_f32_16x16x32_bf16 forms every product
+//            exactly and sums in fp32: [16 W_UV rows] x [32 features] x [16 rows of the block] per instruction;
+//   uq, uqs: u split into NSU FP8 parts with one scale per (part, row b, 128-block) — the activation layout the
+//            W_O pass reads ([part][rows][H*hd] and [part][rows][H*hd/128]).
+// Every partial of the block (at most 128 KB: rb * nsplit * Dv <= 32,768 floats) is loaded up front, 32 16-byte
+// loads a thread, together with this wave's W_UV codes.
+static constexpr int MW_RB = 16;      // rows per workgroup at most (the N side of one instruction)
+static constexpr int MW_ROW_FORM_MAX_ROWS = 8;  // up to this many rows, one workgroup per (row, head)
+static constexpr int MW_LOADS = 32;   // 16-byte partial loads per thread
+
+// Row tiles of W_UV[h] per wave (hd / 64) and K-blocks (Dv / 128).
+template <int TPW, int NKB, int NSU, bool TL>
+__global__ __launch_bounds__(256, 2) void k_merge_wuv(const float *__restrict__ opart, const float *__restrict__ ml,
+                                                      int nsplit, int rows, int H, int rb, float *__restrict__ o,
+                                                      const uint8_t *__restrict__ wuv, const float *__restrict__ wsc,
+                                                      uint8_t *__restrict__ uq, float *__restrict__ uqs, long uq_part,
+                                                      long uqs_part)
+{
+    constexpr int Dv = NKB * 128, hd = TPW * 64, NRB = hd / 128;
+    constexpr int FQ = Dv / 4;  // feature quads of a row
+    __shared__ float s_wt[MW_RB][AM_MAXSPLIT];
+    __shared__ __attribute__((aligned(16))) float s_o[MW_RB][Dv + 4];  // padded: the operand reads take 16 rows
+    __shared__ float s_u[MW_RB][hd + 1];
+    const int h = blockIdx.x, b0 = blockIdx.y * rb;
+    const int nb = min(rb, rows - b0);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    // 1. the split maxima and sums of this wave's rows (w, w + 4, ...), first, so that the weights below wait
+    //    only for them
+    float mv[MW_RB / 4], lv[MW_RB / 4];
+#pragma unroll
+    for (int q = 0; q < MW_RB / 4; q++) {
+        const int b = min(w + 4 * q, nb - 1);
+        const int sp = min(lane, nsplit - 1);
+        const long mi = (((long)(b0 + b) * nsplit + sp) * H + h) * 2;
+        mv[q] = ml[mi];
+        lv[q] = ml[mi + 1];
+    }
+    // 2. this wave's W_UV[h] operands: row tiles w * TPW .. + TPW (16 rows each), every 128-column block; lane
+    //    (ln, lg) holds row ln's columns lg*16 .. +16 and 64 + lg*16 .. +16 of the block (32 codes)
+    v4i A[TPW][NKB][2];
+#pragma unroll
+    for (int t = 0; t < TPW; t++)
+#pragma unroll
+        for (int kb = 0; kb < NKB; kb++) {
+            const int tile = w * TPW + t;
+            const uint8_t *p = TL ? wuv + (((long)h * (hd / 16) + tile) * NKB + kb) * 2048 + lane * 16
+                                  : wuv + ((long)h * hd + tile * 16 + ln) * Dv + kb * 128 + lg * 16;
+            A[t][kb][0] = __builtin_nontemporal_load((const v4i *)p);
+            A[t][kb][1] = __builtin_nontemporal_load((const v4i *)(p + (TL ? 1024 : 64)));
+        }
+    // 3. every partial of the block: load k of a thread is split k % nsplit of its pair k / nsplit, where pair j of
+    //    thread tid is (row, feature quad) number tid + 256 j; so a pair's splits are summed in one thread, in order.
+    //    Every load is issued (loads past the thread's pairs re-read a valid one and are not used).
+    const int npair = MW_LOADS / nsplit;
+    const long sstride = (long)H * Dv;
+    auto pair_ptr = [&](int j) {
+        const int pi = tid + 256 * min(j, npair - 1);
+        const int b = min(pi / FQ, nb - 1), fq = pi % FQ;
+        return opart + ((long)(b0 + b) * nsplit * H + h) * Dv + fq * 4;
+    };
+    v4f pv[MW_LOADS];
+    {
+        const float *ptr = pair_ptr(0);
+        int sp = 0, j = 0;
+#pragma unroll
+        for (int k = 0; k < MW_LOADS; k++) {
+            pv[k] = *(const v4f *)ptr;
+            ptr += sstride;
+            if (++sp == nsplit) {
+                sp = 0;
+                ptr = pair_ptr(++j);
+            }
+        }
+    }
+    // split weights w_s = e^(m_s - M) / sum_s e^(m_s - M) l_s (0 for an empty split)
+#pragma unroll
+    for (int q = 0; q < MW_RB / 4; q++) {
+        const int b = w + 4 * q;
+        if (b < nb) {
+            const bool ok = lane < nsplit;
+            const float m = ok ? mv[q] : -INFINITY;
+            const float l = ok ? lv[q] : 0.f;
+            const float M = wave_max(m);
+            const float e = m == -INFINITY ? 0.f : expf(m - M);
+            const float den = wave_sum(e * l);
+            if (lane < AM_MAXSPLIT) s_wt[b][lane] = den > 0.f ? e / den : 0.f;
+        }
+    }
+    __syncthreads();
+    // 3. merge: o[b] = sum over the splits in order of w_s O_s[b]
+    {
+        int sp = 0, j = 0;
+        v4f cur = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < MW_LOADS; k++) {
+            const int pi = tid + 256 * j, b = pi / FQ, fq = pi % FQ;
+            if (j < npair && b < nb) {
+                const float wt = s_wt[b][sp];
+                if (wt != 0.f) cur += pv[k] * wt;
+                if (sp == nsplit - 1) {
+                    *(v4f *)&s_o[b][fq * 4] = cur;
+                    cur = v4f{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            if (++sp == nsplit) { sp = 0; j++; }
+        }
+    }
+    __syncthreads();
+    if (o)
+        for (int i = tid; i < nb * FQ; i += 256) {
+            const int b = i / FQ, fq = i % FQ;
+            *(v4f *)(o + ((long)(b0 + b) * H + h) * Dv + fq * 4) = *(const v4f *)&s_o[b][fq * 4];
+        }
+    // 4. u = W_UV[h] o on the matrix cores.  K order inside a 128-column block: step ks takes lane byte range
+    //    [8 ks, 8 ks + 8) of its 32 codes, i.e. columns (ks < 2 ? 0 : 64) + lg*16 + (ks & 1) * 8 .. + 8; the o side
+    //    reads the same columns.
+    {
+        v4f acc[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; t++) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+        const int rblk = (w * TPW * 16) / 128;  // this wave's tiles lie in one 128-row scale block
+        const bool bv = ln < nb;
+#pragma unroll
+        for (int kb = 0; kb < NKB; kb++) {
+            const float sc = wsc[((long)h * NRB + rblk) * NKB + kb];
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {
+                const int c = kb * 128 + (ks < 2 ? 0 : 64) + lg * 16 + (ks & 1) * 8;
+                v4f x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+                if (bv) {
+                    x0 = *(const v4f *)&s_o[ln][c] * sc;
+                    x1 = *(const v4f *)&s_o[ln][c + 4] * sc;
+                }
+                const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                v8bf Bh, Bl;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const __bf16 hb = (__bf16)xs[e];
+                    Bh[e] = hb;
+                    Bl[e] = (__bf16)(xs[e] - (float)hb);
+                }
+#pragma unroll
+                for (int t = 0; t < TPW; t++) {
+                    const uint32_t w0 = (uint32_t)A[t][kb][ks >> 1][(ks & 1) * 2];
+                    const uint32_t w1 = (uint32_t)A[t][kb][ks >> 1][(ks & 1) * 2 + 1];
+                    const v8bf Aw = fp8x8_to_bf16(w0, w1);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aw, Bh, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aw, Bl, acc[t], 0, 0, 0);
+                }
+            }
+        }
+        // lane (ln, lg) holds u[row ln][W_UV rows tile*16 + 4 lg .. + 4]
+        if (bv) {
+#pragma unroll
+            for (int t = 0; t < TPW; t++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) s_u[ln][(w * TPW + t) * 16 + 4 * lg + i] = acc[t][i];
+        }
+    }
+    __syncthreads();
+    // 5. split u into NSU parts, one wave per (row, 128-row block of u)
+    const long K = (long)H * hd;
+    for (int it = w; it < nb * NRB; it += 4) {
+        const int b = it / NRB, j = it % NRB;
+        const int r0 = j * 128 + lane * 2;
+        float x0 = s_u[b][r0], x1 = s_u[b][r0 + 1];
+        const long e = (long)(b0 + b) * K + (long)h * hd + r0;
+        const long sc_i = (long)(b0 + b) * (K / 128) + (long)h * NRB + j;
+#pragma unroll
+        for (int sp = 0; sp < NSU; sp++) {
+            const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+            const float scale = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+            const float iv = 1.0f / scale;
+            const uint32_t code = f32x2_to_fp8(fminf(fmaxf(x0 * iv, -448.f), 448.f), fminf(fmaxf(x1 * iv, -448.f), 448.f));
+            *(uint16_t *)(uq + sp * uq_part + e) = (uint16_t)code;
+            if (lane == 0) uqs[sp * uqs_part + sc_i] = scale;
+            const v2f d = fp8x2_lo(code);
+            x0 -= d.x * scale;
+            x1 -= d.y * scale;
+        }
+    }
+}
+
+// Value widths 128, 256 or 512 with hd = 128, and 128 or 256 with hd = 256 (the kernel's register budget).
 bool attention_merge_uv_ok(int Dv, int hd)
 {
     return (Dv == 128 || Dv == 256 || Dv == 512) && (hd == 128 || (hd == 256 && Dv <= 256));
+}
+
+// Rows per merge workgroup: every partial of the block fits the threads' loads, and about 256 workgroups.
+static int merge_rows(int rows, int H, int nsplit, int Dv)
+{
+    // pairs (row, feature quad) per thread: MW_LOADS / nsplit, so rb * Dv / 4 <= 256 * (MW_LOADS / nsplit)
+    int rb = std::max(1, std::min(MW_RB, (256 * (MW_LOADS / nsplit)) / (Dv / 4)));
+    const int want = std::max(1, (rows * H + 255) / 256);
+    return std::min(rb, std::max(1, std::min(want, rows)));
 }
 
 int launch_attn_merge_uv(int B, int H, int Dv, int top_k, const float *opart, const float *ml, float *o,
                          const uint8_t *wuv, const float *wsc, int hd, int tiled, uint8_t *uq, float *uqs,
                          long uq_part, long uqs_part, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_attn_merge_uv<4>), dim3(B * H), dim3(256), 0, s, opart, ml, attention_splits(top_k, B, H), H, Dv,
-                       o, wuv, wsc, hd, tiled, uq, uqs, uq_part, uqs_part);
-    return hip_check("attn_merge_uv");
+    const int nsplit = attention_splits(top_k, B, H);
+    if (B <= MW_ROW_FORM_MAX_ROWS) {
+        hipLaunchKernelGGL((k_attn_merge_uv_row<4>), dim3(B * H), dim3(256), 0, s, opart, ml, nsplit, H, Dv, o, wuv, wsc, hd,
+                           tiled, uq, uqs, uq_part, uqs_part);
+        return hip_check("attn_merge_uv_row");
+    }
+    const int rb = merge_rows(B, H, nsplit, Dv);
+    const dim3 g(H, (B + rb - 1) / rb);
+#define DL_MW(TPW_, NKB_)                                                                                           \
+    if (hd == TPW_ * 64 && Dv == NKB_ * 128) {                                                                     \
+        if (tiled)                                                                                                 \
+            hipLaunchKernelGGL((k_merge_wuv<TPW_, NKB_, 4, true>), g, dim3(256), 0, s, opart, ml, nsplit, B, H, rb, o, \
+                               wuv, wsc, uq, uqs, uq_part, uqs_part);                                               \
+        else                                                                                                       \
+            hipLaunchKernelGGL((k_merge_wuv<TPW_, NKB_, 4, false>), g, dim3(256), 0, s, opart, ml, nsplit, B, H, rb,  \
+                               o, wuv, wsc, uq, uqs, uq_part, uqs_part);                                            \
+        return hip_check("attn_merge_uv");                                                                          \
+    }
+    DL_MW(2, 1) DL_MW(2, 2) DL_MW(2, 4) DL_MW(4, 1) DL_MW(4, 2)
+#undef DL_MW
+    return fail(DL_ERR_UNSUPPORTED, "attention merge: d_v %d with head_dim %d", Dv, hd);
 }
 
 bool attention_mfma_ok(int H, int Dc, int Dv, int q_dt, int kv_dt)
@@ -665,10 +929,13 @@ bool attention_mfma_ok(int H, int Dc, int Dv, int q_dt, int kv_dt)
 
 // Kept positions per split: about 256 workgroups over the batch, whole chunks of 64, at most 512; the number
 // of splits follows (at most 32).
+#ifndef DL_ATT_WGS
+#define DL_ATT_WGS 256
+#endif
 static int attention_pps(int top_k, int B, int H)
 {
     const int hs = (H + 63) / 64;
-    const long want = std::max(1L, 256L / ((long)B * hs));
+    const long want = std::max(1L, (long)DL_ATT_WGS / ((long)B * hs));
     int ch = (int)((top_k + AM_NJ * want - 1) / (AM_NJ * want));
     ch = std::max(ch, (top_k + AM_NJ * AM_MAXSPLIT - 1) / (AM_NJ * AM_MAXSPLIT));
     ch = std::min(std::max(ch, 1), AM_MAXPPS / AM_NJ);

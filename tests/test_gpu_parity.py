@@ -133,15 +133,13 @@ def test_indexer_topk_many_candidates_in_the_threshold_bin():
 
 
 LAYERS = {
-    # value and head widths of the attention merge + W_UV kernel other than the named workloads' 512 / 128
-    "fp8-dv128-hd128": synth.small_fp8_spec(name="dv128hd128", Dc=256, Dv=128, head_dim=128, seq_lens=(1900, 300),
-                                            B=2),
-    "fp8-dv256-hd128": synth.small_fp8_spec(name="dv256hd128", Dc=256, Dv=256, head_dim=128, seq_lens=(1200, 2100),
-                                            B=2),
-    "fp8-dv128-hd256": synth.small_fp8_spec(name="dv128hd256", Dc=128, Dv=128, head_dim=256, seq_lens=(2500, 64),
-                                            B=2),
-    "fp8-dv256-hd256": synth.small_fp8_spec(name="dv256hd256", Dc=512, Dv=256, head_dim=256, seq_lens=(700, 3000),
-                                            B=2),
+    # value and head widths of the attention merge + W_UV kernels other than the named workloads' 512 / 128, at two
+    # rows (one workgroup per row and head) and at ten (one per head and block of rows, on the matrix cores)
+    **{f"fp8-dv{dv}-hd{hd}-b{b}": synth.small_fp8_spec(name=f"dv{dv}hd{hd}b{b}", Dc=dc, Dv=dv, head_dim=hd,
+                                                        seq_lens=tuple(lens[i % 2] + 37 * i for i in range(b)), B=b)
+       for dc, dv, hd, lens in ((256, 128, 128, (1900, 300)), (256, 256, 128, (1200, 2100)),
+                                (128, 128, 256, (2500, 64)), (512, 256, 256, (700, 3000)))
+       for b in (2, 10)},
     "tiny-fp32": synth.config(1),
     "fp8-ragged-pad": synth.small_fp8_spec(),
     "fp8-zipf-perm": synth.small_fp8_spec(name="zipf", zipf_s=1.1, permute_pages=True, B=4,
@@ -164,8 +162,11 @@ def test_layer_step_small(name):
     say(f"{name}: {w}")
 
 
-def test_fused_equals_unfused_and_replays():
-    spec = synth.small_fp8_spec(name="fused", B=3, seq_lens=(3000, 700, 0))
+@pytest.mark.parametrize("lens", [(3000, 700, 0), tuple(300 + 211 * i for i in range(10))])
+def test_fused_equals_unfused_and_replays(lens):
+    # the fused step reads tiled weights, the separate calls row-major ones; 3 and 10 rows take the two forms of
+    # the attention merge + W_UV kernel
+    spec = synth.small_fp8_spec(name="fused", B=len(lens), seq_lens=lens)
     t = _layer(spec, seed=5)
     step = dl.LayerStep(spec, t, debug=True)
     say("[gpu] fused step + 4 separate calls")
