@@ -40,6 +40,7 @@ struct TopkWs {
     unsigned *bits;    // [B, nchunk * 128] kept items, one bit each (whole 4,096-item chunks)
     int2 *cand;        // [B, nchunk * 4,096] (item, score) inside the threshold bin, per chunk
     int32_t *ccnt;     // [B, nchunk] how many per chunk
+    int32_t *acnt;     // [B, nchunk] items marked (above the bin) per chunk
     Thr *thr;          // [B]
 };
 void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R = 1, int pool = 1);

@@ -23,6 +23,8 @@
 #include "dl_common.h"
 #include "dl_internal.h"
 
+#include <algorithm>
+
 namespace dl {
 
 static constexpr int NB1 = 256 + 23 * 128;  // log-linear bins covering 0 .. 2^31-1
@@ -290,11 +292,12 @@ __global__ __launch_bounds__(256) void k_sel_mark(const int32_t *__restrict__ sc
                                                   const int32_t *__restrict__ seq_lens, int R, int pool, int top_k,
                                                   const unsigned *__restrict__ hist1, unsigned *__restrict__ bits,
                                                   long Lw, int2 *__restrict__ cand, int32_t *__restrict__ ccnt,
-                                                  int nchunk, Thr *__restrict__ thr)
+                                                  int32_t *__restrict__ acnt, int nchunk, Thr *__restrict__ thr)
 {
     __shared__ unsigned s_hist[NB1];
     __shared__ int s_tmp[260];
     __shared__ int s_w[4];
+    __shared__ int s_a[4];
     const int b = blockIdx.y;
     const int L = row_len(seq_lens, b, R, pool);
     const long c0 = (long)blockIdx.x * SEL_CHUNK;
@@ -316,13 +319,18 @@ __global__ __launch_bounds__(256) void k_sel_mark(const int32_t *__restrict__ sc
     // two threads fill one 32-bit word: the even one the low half
     const unsigned mo = (unsigned)__shfl_xor((int)m, 1, 64);
     if ((tid & 1) == 0) bits[(long)b * Lw + (c0 >> 5) + (tid >> 1)] = m | (mo << 16);
-    // candidates: exclusive scan over the workgroup into the chunk's region
+    // candidates: exclusive scan over the workgroup into the chunk's region; and the chunk's marked items
     const int inc = wave_incl_scan(nc);
+    const int na = wave_sum_i(__popc(m));
     if (lane == 63) s_w[wave] = inc;
+    if (lane == 0) s_a[wave] = na;
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wave; w++) before += s_w[w];
-    if (tid == 0) ccnt[(long)b * nchunk + blockIdx.x] = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    if (tid == 0) {
+        ccnt[(long)b * nchunk + blockIdx.x] = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+        acnt[(long)b * nchunk + blockIdx.x] = s_a[0] + s_a[1] + s_a[2] + s_a[3];
+    }
     int o = before + inc - nc;
     int2 *cr = cand + (long)b * nchunk * SEL_CHUNK + c0;
 #pragma unroll
@@ -330,33 +338,44 @@ __global__ __launch_bounds__(256) void k_sel_mark(const int32_t *__restrict__ sc
         if (v[i] <= t.hi && v[i] >= t.lo) cr[o++] = int2{(int)(c0 + (long)tid * 16 + i), v[i]};
 }
 
-static constexpr int FCAP = 8192;   // candidates whose keys the final kernel holds in LDS; more are re-read
+static constexpr int FCAP = 4096;   // candidates whose keys the final kernel holds in LDS; more are re-read
 static constexpr int FCH = 2048;    // chunks per row the final kernel handles (rows of up to 8M items)
-static constexpr int FBW = 4096;    // bitmap words per compaction round (16 per thread)
-static constexpr int FOUT = 4096;   // kept items staged in LDS per round before their coalesced stores
+static constexpr int FCPW = 2;      // chunks a final workgroup compacts (256 bitmap words: one per thread)
+static constexpr int FBW = FCPW * (SEL_CHUNK / 32);
 
-// Final: one workgroup per row.  Rows of at most top_k items keep items 0 .. L-1.  Longer rows keep the
-// marked items and the `need` best candidates: radix select, most significant 8-bit digit first, of the
-// need-th largest key ((score - lo) << PB | (2^PB - 1 - item)); keys are unique, so exactly `need` keys match
-// the final prefix or exceed it.  The bitmap, with their bits added, is compacted in item order; its first
-// round of words is loaded before the select, so that latency overlaps it.
+// Final: gridDim.x workgroups per row, workgroup g owning chunks [FCPW g, FCPW (g + 1)).  Rows of at most top_k
+// items keep items 0 .. L-1.  In longer rows every workgroup finds the same `need` best candidates (the row has
+// few: the items of one histogram bin): with at most 256 in LDS, each candidate's rank among them; otherwise a
+// radix select, most significant 8-bit digit first, of the need-th largest key ((score - lo) << PB |
+// (2^PB - 1 - item)); keys are unique, so exactly `need` keys match the final prefix or exceed it.  The kept
+// items before its chunks (the marked counts of the earlier chunks and their kept candidates) give the
+// workgroup's first output slot; it then adds its kept candidates' bits to its bitmap words and compacts them
+// in item order, so the list comes out ascending and every slot is written by exactly one workgroup.
 // pool > 1: slot k holds items' positions [k pool, (k + 1) pool), those at or past the row's length as -1.
 __global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ scores, long Lmax,
                                                    const int32_t *__restrict__ seq_lens, int R, int pool, int top_k,
                                                    const unsigned *__restrict__ bits, long Lw,
                                                    const int2 *__restrict__ cand, const int32_t *__restrict__ ccnt,
-                                                   int nchunk, const Thr *__restrict__ thr, int PB,
-                                                   int32_t *__restrict__ sel, int32_t *__restrict__ sel_score)
+                                                   const int32_t *__restrict__ acnt, int nchunk,
+                                                   const Thr *__restrict__ thr, int PB, int32_t *__restrict__ sel,
+                                                   int32_t *__restrict__ sel_score)
 {
     typedef unsigned long long u64;
     __shared__ unsigned s_hist[256];
     __shared__ int s_off[FCH + 1];
-    __shared__ u64 s_key[FCAP];
-    __shared__ unsigned s_bm[FBW];  // bits of the kept candidates in the current round of bitmap words
-    __shared__ int s_out[FOUT];     // the round's kept items, in order
+    __shared__ int s_kc[FCH];       // kept candidates per chunk (chunks before and in this workgroup's range)
+    // the candidates' keys, then (once the kept ones are known) this workgroup's kept items in order
+    __shared__ union {
+        u64 key[FCAP];
+        int out[FBW * 32];
+    } s_ko;
+    static_assert(FBW * 32 * sizeof(int) <= FCAP * sizeof(u64), "kept items fit the keys' LDS");
+    u64 *s_key = s_ko.key;
+    int *s_out = s_ko.out;
+    __shared__ unsigned s_bm[FBW];  // bits of the kept candidates in this workgroup's words
     __shared__ int s_w[4];
     __shared__ int s_pick[3];
-    const int b = blockIdx.x;
+    const int b = blockIdx.y, g = blockIdx.x;
     const int L = row_len(seq_lens, b, R, pool);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t *sr = scores + (long)b * Lmax;
@@ -364,9 +383,11 @@ __global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ s
     int32_t *ss = sel_score ? sel_score + (long)b * top_k : nullptr;
     const int plen = pool > 1 ? row_len(seq_lens, b, R) : 0;  // positions the row sees
     const int n_sel = min(L, top_k);
-    for (int i = n_sel * pool + tid; i < top_k * pool; i += 256) so[i] = -1;  // padding of the unused slots
-    if (ss)
-        for (int i = n_sel + tid; i < top_k; i += 256) ss[i] = 0;
+    if (g == 0) {  // padding of the unused slots
+        for (int i = n_sel * pool + tid; i < top_k * pool; i += 256) so[i] = -1;
+        if (ss)
+            for (int i = n_sel + tid; i < top_k; i += 256) ss[i] = 0;
+    }
     // pools of 4 or more positions go out as 16-byte stores when the output is 16-byte aligned
     const bool vec = pool >= 4 && ((uintptr_t)sel & 15) == 0;
     auto put = [&](int slot, int item) {
@@ -387,28 +408,32 @@ __global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ s
         }
         if (ss) ss[slot] = sr[item];
     };
+    const int i0 = g * FCPW * SEL_CHUNK;  // this workgroup's first item
     if (L <= top_k) {
-        for (int i = tid; i < L; i += 256) put(i, i);
+        for (int i = i0 + tid; i < min(L, i0 + FCPW * SEL_CHUNK); i += 256) put(i, i);
         return;
     }
+    const int nch = (L + SEL_CHUNK - 1) / SEL_CHUNK;
+    const int ca = g * FCPW, cb = min(nch, ca + FCPW);  // this workgroup's chunks
+    if (ca >= nch) return;
     const unsigned *br = bits + (long)b * Lw;
     const int2 *cr = cand + (long)b * nchunk * SEL_CHUNK;
     const Thr t = thr[b];
+    // this thread's bitmap word (loaded first, so that its latency overlaps the select)
     const int nw = (L + 31) >> 5;
-    // words w0 + tid * 16 .. + 16 of a round (whole chunks are 128 words, so 4-word groups never pass the
-    // row's chunks; words past L hold no bits)
-    unsigned wv[16];
-    auto load_round = [&](int w0) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int wi = w0 + tid * 16 + j * 4;
-            const uint4 q = wi < nw ? *(const uint4 *)(br + wi) : uint4{0u, 0u, 0u, 0u};
-            wv[4 * j] = q.x; wv[4 * j + 1] = q.y; wv[4 * j + 2] = q.z; wv[4 * j + 3] = q.w;
-        }
-    };
-    load_round(0);
+    const int wi = ca * (SEL_CHUNK / 32) + tid;
+    unsigned word = wi < nw && tid < (cb - ca) * (SEL_CHUNK / 32) ? br[wi] : 0u;
+    // marked items of the chunks before this workgroup's
+    int abefore = 0;
+    for (int c0 = 0; c0 < ca; c0 += 256) {
+        const int ch = c0 + tid;
+        abefore += wave_sum_i(ch < ca ? acnt[(long)b * nchunk + ch] : 0);
+    }
+    if (lane == 0) s_w[wave] = abefore;
+    __syncthreads();
+    abefore = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    __syncthreads();
     // candidate counts of the row's chunks -> offsets of each chunk's run in the candidate order
-    const int nch = (L + SEL_CHUNK - 1) / SEL_CHUNK;
     {
         int carry = 0;
         for (int c0 = 0; c0 < nch; c0 += 256) {
@@ -419,7 +444,10 @@ __global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ s
             __syncthreads();
             int before = 0;
             for (int w = 0; w < wave; w++) before += s_w[w];
-            if (ch < nch) s_off[ch] = carry + before + inc - n;
+            if (ch < nch) {
+                s_off[ch] = carry + before + inc - n;
+                s_kc[ch] = 0;
+            }
             carry += s_w[0] + s_w[1] + s_w[2] + s_w[3];
             __syncthreads();
         }
@@ -429,13 +457,17 @@ __global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ s
     const int c = s_off[nch];  // the items inside the bin: >= need
     const u64 pm = (1ull << PB) - 1ull;
     // candidate i of the row: the last chunk whose offset is <= i, then its place in that chunk's run
-    auto entry = [&](int i) -> int2 {
+    auto chunk_of = [&](int i) -> int {
         int lo = 0, hi = nch - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_off[mid] <= i) lo = mid;
             else hi = mid - 1;
         }
+        return lo;
+    };
+    auto entry = [&](int i) -> int2 {
+        const int lo = chunk_of(i);
         return cr[(long)lo * SEL_CHUNK + (i - s_off[lo])];
     };
     auto key_of = [&](int2 e) -> u64 {
@@ -487,62 +519,48 @@ __global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ s
             if (cnt == krem) break;  // every key with this prefix is kept
         }
     }
-    // ordered compaction, one round of FBW words at a time: the kept candidates' bits of the round are set in
-    // LDS and added to the marked words
-    int base = 0;
-    for (int w0 = 0; w0 < nw; w0 += FBW) {
-        if (w0 > 0) load_round(w0);
-        for (int i = tid; i < FBW; i += 256) s_bm[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < c; i += 256) {
-            const u64 k = in_lds ? s_key[i] : key_of(entry(i));
-            if ((k & pmask) >= prefix) {
+    // kept candidates of the chunks before and in this workgroup's range: counts per chunk, and the bits of those
+    // in its range
+    for (int i = tid; i < FBW; i += 256) s_bm[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < s_off[cb]; i += 256) {
+        const u64 k = in_lds ? s_key[i] : key_of(entry(i));
+        if ((k & pmask) >= prefix) {
+            const int ch = chunk_of(i);
+            if (ch < ca) {
+                atomicAdd(&s_kc[ch], 1);
+            } else {
                 const int item = (int)(pm - (k & pm));
-                const int wi = (item >> 5) - w0;
-                if (wi >= 0 && wi < FBW) atomicOr(&s_bm[wi], 1u << (item & 31));
+                atomicOr(&s_bm[(item >> 5) - ca * (SEL_CHUNK / 32)], 1u << (item & 31));
             }
         }
-        __syncthreads();
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            wv[j] |= s_bm[tid * 16 + j];
-            cnt += __popc(wv[j]);
-        }
-        const int inc = wave_incl_scan(cnt);
-        if (lane == 63) s_w[wave] = inc;
-        __syncthreads();
-        int before = 0;
-        for (int w = 0; w < wave; w++) before += s_w[w];
-        const int tot = s_w[0] + s_w[1] + s_w[2] + s_w[3];
-        int o = before + inc - cnt;  // within the round
-        if (tot <= FOUT) {
-            // the bits go to LDS in order, then every thread stores consecutive slots
-#pragma unroll
-            for (int j = 0; j < 16; j++) {
-                unsigned x = wv[j];
-                while (x) {
-                    const int bit = __ffs((int)x) - 1;
-                    x &= x - 1u;
-                    s_out[o++] = (w0 + tid * 16 + j) * 32 + bit;
-                }
-            }
-            __syncthreads();
-            for (int i = tid; i < tot; i += 256) put(base + i, s_out[i]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; j++) {
-                unsigned x = wv[j];
-                while (x) {
-                    const int bit = __ffs((int)x) - 1;
-                    x &= x - 1u;
-                    put(base + o++, (w0 + tid * 16 + j) * 32 + bit);
-                }
-            }
-        }
-        base += tot;
-        __syncthreads();
     }
+    __syncthreads();
+    int kbefore = 0;
+    for (int c0 = 0; c0 < ca; c0 += 256) kbefore += wave_sum_i(c0 + tid < ca ? s_kc[c0 + tid] : 0);
+    if (lane == 0) s_w[wave] = kbefore;
+    __syncthreads();
+    const int base = abefore + s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    __syncthreads();
+    // ordered compaction of this workgroup's words: thread tid owns word ca * 128 + tid
+    if (tid < FBW) word |= s_bm[tid];
+    const int cnt = __popc(word);
+    const int inc = wave_incl_scan(cnt);
+    if (lane == 63) s_w[wave] = inc;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; w++) before += s_w[w];
+    const int tot = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    int o = before + inc - cnt;
+    // the items go to LDS in order, then every thread stores consecutive slots
+    unsigned x = word;
+    while (x) {
+        const int bit = __ffs((int)x) - 1;
+        x &= x - 1u;
+        s_out[o++] = wi * 32 + bit;
+    }
+    __syncthreads();
+    for (int i = tid; i < tot; i += 256) put(base + i, s_out[i]);
 }
 
 // ------------------------------------------------------------------ host side
@@ -557,6 +575,7 @@ void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R, int pool)
     t.bits = w.take<unsigned>(B * nchunk * (SEL_CHUNK / 32));
     t.cand = w.take<int2>(B * nchunk * SEL_CHUNK);
     t.ccnt = w.take<int32_t>(B * nchunk);
+    t.acnt = w.take<int32_t>(B * nchunk);
     t.thr = w.take<Thr>(B);
 }
 
@@ -600,9 +619,13 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     return fail(DL_ERR_UNSUPPORTED, "indexer shape heads=%d dim=%d", HI, DI);
 #undef DL_SCORE_CASE
     hipLaunchKernelGGL(k_sel_mark, dim3(nchunk, B), dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k,
-                       t.hist1, t.bits, Lw, t.cand, t.ccnt, nchunk, t.thr);
-    hipLaunchKernelGGL(k_sel_final, dim3(B), dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k, t.bits,
-                       Lw, t.cand, t.ccnt, nchunk, t.thr, PB, sel, sel_score);
+                       t.hist1, t.bits, Lw, t.cand, t.ccnt, t.acnt, nchunk, t.thr);
+    // rows of at most top_k items are written in FCPW-chunk pieces too; with top_k above the longest row that is
+    // up to top_k items
+    const long span = std::max(Lmax, (long)top_k);
+    const int gfin = (int)((span + FCPW * SEL_CHUNK - 1) / (FCPW * SEL_CHUNK));
+    hipLaunchKernelGGL(k_sel_final, dim3(gfin, B), dim3(256), 0, s, t.scores, Lmax, pg.seq_lens, R, pool, top_k,
+                       t.bits, Lw, t.cand, t.ccnt, t.acnt, nchunk, t.thr, PB, sel, sel_score);
     return hip_check("indexer_topk");
 }
 

@@ -110,7 +110,7 @@ def _bin1(s: int) -> int:
 def test_indexer_topk_many_candidates_in_the_threshold_bin():
     # Scores packed densely around 14,000 (head 0 only: 127 k0 + k1 with k0 in [120, 127]), so the histogram bin
     # holding the k-th score contains many items with distinct scores: the 50,000-item row selects among a few
-    # thousand of them in LDS, the 600,000-item row among more than 8,192, read back from the workspace.
+    # thousand of them in LDS, the 600,000-item row among more than 4,096, read back from the workspace.
     spec = synth.small_fp8_spec(name="dense-bin", seq_lens=(50000, 600000), B=2, topk=512)
     t = _layer(spec, seed=12, weights=False)
     g = torch.Generator(device="cpu").manual_seed(12)
@@ -128,7 +128,7 @@ def test_indexer_topk_many_candidates_in_the_threshold_bin():
         bins = np.array([_bin1(int(x)) for x in sc])
         cands.append(int((bins == np.sort(bins)[::-1][spec.topk - 1]).sum()))
     say(f"[cpu] candidates in the threshold bin: {cands}")
-    assert 256 < cands[0] <= 8192 < cands[1]
+    assert 256 < cands[0] <= 4096 < cands[1]
     _check_topk(spec, t)
 
 
