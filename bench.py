@@ -64,7 +64,7 @@ def algorithmic_bytes(spec, lens, n_touched: int) -> dict:
 # HBM traffic of the gate/up kernel as read by rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE per dispatch,
 # scaled by what the same counters read for a plain copy of known size).  Reported only while the kernel's
 # source is the one the counters were taken on.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_b8-128k.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_b8-128k.md")
 KERNEL_SOURCES = ("sparse_attention_moe_amd/csrc/k_gemv.hip", "sparse_attention_moe_amd/csrc/dl_common.h")
 
 
