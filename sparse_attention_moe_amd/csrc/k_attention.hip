@@ -7,15 +7,16 @@
 //
 // Two kernels:
 //  * k_attn_mla (FP8 latents, bf16 queries, 16 | heads): split over the kept positions like flash
-//    decoding.  A workgroup owns one row, a run of kept positions and up to 64 heads (16 per wave), so
-//    every kept latent is gathered once for all heads; positions are staged 64 at a time into LDS through
-//    the page table.  Scores are [16 heads x 64] x [64 x d_c] products on the matrix cores
-//    (v_mfma_f32_16x16x32_bf16): the queries are bf16 already and every e4m3 code is exactly a bf16, so the
-//    products are exact and each 128-feature block's sum takes its scale once.  The softmax runs online in
-//    fp32 inside each wave.  The values are transposed once per chunk into bf16 [feature][position] rows in
-//    LDS, and O += P' C with P' = p * (block scale) split into bf16 high and low halves (about 16
-//    significant bits), so the output keeps fp32-level accuracy.  The splits are merged afterwards
-//    (max-rescaled sums).
+//    decoding.  A workgroup owns one row, a run of kept positions and up to 64 heads (two waves per 16
+//    heads), so every kept latent is gathered once for all heads.  Positions are staged 64 at a time as raw
+//    e4m3 bytes in LDS by the direct global-to-LDS loads, the next chunk landing while the current one is
+//    computed.  Scores are [16 heads x 128] x [128 x 16 positions] products on the FP8 matrix cores
+//    (v_mfma_f32_16x16x128_f8f6f4): each query, scaled by a power of two, is split into two e4m3 parts
+//    whose sum is the bf16 query exactly, so the products are exact and each 128-feature block's sum takes
+//    its scale once.  The softmax runs online in fp32.  The values are transposed once per chunk into
+//    [feature][position] byte rows, and O += P' C with P' = p * (block scale) split into bf16 high and low
+//    halves (about 16 significant bits) on v_mfma_f32_16x16x32_bf16, so the output keeps fp32-level
+//    accuracy.  The splits are merged afterwards (max-rescaled sums), with W_UV applied in the merge.
 //  * k_attn (any shape, fp32 or FP8 latents): a workgroup owns 4 heads of one row and scores every
 //    kept position on the vector units in fp32.
 #include "dl_common.h"
@@ -245,6 +246,23 @@ __device__ __forceinline__ float row_sum16(float v)
     return v;
 }
 
+// A workgroup barrier over LDS alone: this wave's LDS writes complete, then every wave meets.  Unlike
+// __syncthreads it leaves the wave's global loads in flight (the direct-to-LDS ones included).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// O += A B on v_mfma_f32_16x16x128_f8f6f4, both operands e4m3 without block scales.  Lane (l % 16, l / 16)
+// holds 32 K bytes of row l % 16 of A and of column l % 16 of B; any K order works if A and B share it.
+__device__ __forceinline__ v4f mfma_fp8_acc(v8i a, v8i b, v4f c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // Byte transpose of four dwords: out[k] = (a.k, b.k, c.k, d.k).
 __device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t out[4])
 {
@@ -256,265 +274,392 @@ __device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32
     out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
-// grid (nsplit, ceil(H/64), B), 256 threads.  A workgroup owns one row, one run of kept positions (the split)
-// and up to 64 heads: wave w takes heads 16 (4 blockIdx.y + w) .. +16, so each kept latent is gathered once
-// for all heads.  Per chunk of 64 positions:
-//   gather   the latent codes (through the page table), converted exactly to bf16 once, as [position][feature]
-//            rows in LDS;
-//   values   the first Dv features transposed once into [feature][position] rows (position groups XOR-swizzled
-//            by the feature's 16-group);
-//   scores   S = Q C^T on v_mfma_f32_16x16x32_bf16 (queries in registers), each 128-feature block's sum taking
-//            its scale once;
-//   softmax  online per head in fp32, entirely inside the wave (DPP row reductions);
-//   output   O += P' C with P' = p * (block scale) in bf16 high and low halves (about 16 significant bits).
-// P of each wave reuses the LDS of the bf16 latents once every wave's scores are done.
-// opart [B, nsplit, H, Dv] holds the unnormalised sums, ml [B, nsplit, H, 2] the running (max, sum).
-template <int KQ, int NVB, bool MULTI>  // MULTI: more than one chunk of 64 positions per split
-__global__ __launch_bounds__(256, 1) void k_attn_mla(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
+// Sixteen zero bytes: the source of every direct-to-LDS load that has nothing to load.
+static __device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};  // never written
+// Running maxima move only when a chunk's maximum exceeds them by more than this (log2 units), so p <= 2^8 and the
+// sums are rescaled rarely.
+static constexpr float AM_TAU = 8.f;
+
+// grid (nsplit, ceil(H/64), B), 512 threads.  A workgroup owns one row, one run of kept positions (the split)
+// and up to 64 heads, so each kept latent is gathered once for all of them.  Waves w and w + 4 share the 16
+// heads 16 (4 blockIdx.y + w % 4) .. +16, so two waves share each SIMD and hide each other's latencies: wave w
+// holds the query's first NBA = (NB + 1) / 2 128-feature blocks, owns positions 0..31 of every chunk of 64 and
+// accumulates value features 0..d_v/2; wave w + 4 the other blocks, positions 32..63 and features d_v/2..d_v.
+// Per chunk:
+//   gather   the latent codes and block scales of the chunk's positions (through the page table) straight into
+//            LDS as raw e4m3 bytes with the direct global-to-LDS loads, one chunk ahead: chunk c + 1 lands in
+//            the other of two buffers while chunk c is computed, and no register holds it meanwhile;
+//   values   the first Dv features transposed once into [feature][position] byte rows;
+//   scores   S = Q C^T on v_mfma_f32_16x16x128_f8f6f4 straight from the e4m3 codes: each wave's part of a
+//            head's query is scaled by a power of two and split into two e4m3 parts whose sum is the scaled
+//            bf16 query exactly (bar elements 2^9 below that part's largest), so the products and sums are those
+//            of the bf16 query; each 128-feature block's sum takes its scale once.  Each wave scores all 64
+//            positions over its blocks and hands its partner the partial sums of the partner's positions;
+//   softmax  online per head in fp32, each wave over its own positions with its own running reference (raised
+//            only when a chunk exceeds it by more than AM_TAU, so the rescaling of the sums is rare); both waves'
+//            p and references go to LDS, and p is rescaled to the larger of the two as it is read;
+//   output   O += P' C with P' = p * (block scale) in bf16 high and low halves (about 16 significant bits) on
+//            v_mfma_f32_16x16x32_bf16, the e4m3 values converted to bf16 (exactly) as they are read.
+// opart [B, nsplit, H, Dv] holds the unnormalised sums, ml [B, nsplit, H, 2] the (max, sum) they refer to.
+template <int KQ, int NVB, bool MULTI>  // MULTI: more than one chunk of 64 positions per split (unused)
+__global__ __launch_bounds__(512, 1) void k_attn_mla(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                      const float *__restrict__ ks, const int32_t *__restrict__ pt,
                                                      int max_pages, int R, int ps_shift, const int32_t *__restrict__ sel,
                                                      int top_k, int H, int pps, float sm_scale,
                                                      float *__restrict__ opart, float *__restrict__ ml)
 {
     constexpr int Dc = KQ * 32, NB = (Dc + 127) / 128, Dv = NVB * 128;
-    constexpr int CBP = Dc + 8;                         // bf16 latent row pitch
-    constexpr int PP = AM_NJ + 8;                       // value row pitch (bf16)
-    constexpr int NLD = (AM_NJ * (Dc / 16) + 255) / 256;  // 16-byte code loads per thread per chunk
-    constexpr int CB_BYTES = AM_NJ * CBP * 2;
-    constexpr int P_BYTES = 4 * 16 * (AM_NJ + 4) * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t s_cbuf[CB_BYTES > P_BYTES ? CB_BYTES : P_BYTES];
-    __shared__ __attribute__((aligned(16))) __bf16 s_v[Dv * PP];
-    __shared__ __attribute__((aligned(16))) float s_sc[NB][AM_NJ];
+    constexpr int NBA = (NB + 1) / 2;        // query blocks of the first wave of a pair (the second: NB - NBA)
+    constexpr int NG = Dc / 16 + 1;          // 16-byte granules per position row in LDS (one unused, so that
+    constexpr int RP = NG * 16;              // consecutive rows start in different banks); row pitch
+    constexpr int NIW = (NG + 7) / 8;        // 64-lane code loads per wave and chunk (NG in all)
+    constexpr int NSW = (NB + 7) / 8;        // 64-lane scale loads per wave and chunk (NB in all)
+    constexpr int VP = AM_NJ + 8;            // value row pitch (bytes)
+    constexpr int FV = Dv / 2;               // value features per wave
+    constexpr int NT = FV / 16;              // 16-feature tiles per wave
+    constexpr int NVW = (FV + 127) / 128;    // 128-feature scale blocks per wave
+    constexpr int TPB = NT / NVW;            // tiles per scale block
+    constexpr int SPP = 76;                  // s_p row pitch (floats)
+    static_assert(AM_NJ == 64 && Dv <= 512 && Dv <= Dc, "one position per lane in a scale load; a value per thread");
+    // [position][RP] codes and [block][position] scales, each followed by the padding the last loads fill
+    __shared__ __attribute__((aligned(16))) uint8_t s_c0[NIW * 8 * 1024], s_c1[NIW * 8 * 1024];
+    __shared__ __attribute__((aligned(16))) float s_s0[NSW * 8 * 64], s_s1[NSW * 8 * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t s_vt[Dv * VP];     // [feature][position] values
+    // (flat arrays indexed by one integer: the compiler can then tell every access apart from the direct loads'
+    // targets; through a deep chain of address steps it cannot, and waits for those loads first)
+    __shared__ __attribute__((aligned(16))) float s_p[4 * 16 * SPP];  // [head group][head][position]
+    __shared__ float s_mx[2 * 64];                                      // running maxima [half][group, head]
+    __shared__ float s_l[64];
     __shared__ long s_row[AM_MAXPPS];
-    __bf16 *s_cb = (__bf16 *)s_cbuf;                       // [position][CBP] bf16 latents
-    float(*s_p)[16][AM_NJ + 4] = (float(*)[16][AM_NJ + 4])s_cbuf;  // [wave][head][position] after the scores
     const int split = blockIdx.x, b = blockIdx.z;
     const int nsplit = gridDim.x;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
-    const int h0 = (blockIdx.y * 4 + w) * 16;
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
+    const int hg = w & 3, half = w >> 2;
+    const int h0 = (blockIdx.y * 4 + hg) * 16;
     const bool active = h0 < H;
+    const int kb0 = half ? NBA : 0, nkb = half ? NB - NBA : NBA;
     const int ps_mask = (1 << ps_shift) - 1;
     const int jbase = split * pps;
-    // queries of this wave's 16 heads, as the A operand of every K step: head ln, features 32 kk + 8 lg .. + 8
-    v8bf Aq[KQ];
+    // this wave's query blocks as FP8 A operands: head ln, features 128 kb + 32 lg .. + 32 (zero past d_c),
+    // times 2^e with e chosen per head so that the largest |q| of these blocks lies in [128, 256), as e4m3 high
+    // and low parts; qi[i] = 2^-e of head 4 lg + i
+    v8i Qh[NBA], Ql[NBA];
+    float qi[4];
+    {
+        uint4 qv[NBA][4];
+        float mx = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KQ; kk++)
-        Aq[kk] = active ? *(const v8bf *)(q + ((long)b * H + h0 + ln) * Dc + kk * 32 + lg * 8) : v8bf{};
-    for (int i = tid; i < pps; i += 256) {
+        for (int kk = 0; kk < NBA; kk++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int f = (kb0 + kk) * 128 + lg * 32 + e * 8;
+                qv[kk][e] = active && kk < nkb && f < Dc ? *(const uint4 *)(q + ((long)b * H + h0 + ln) * Dc + f)
+                                                         : uint4{0, 0, 0, 0};
+                const uint32_t x[4] = {qv[kk][e].x, qv[kk][e].y, qv[kk][e].z, qv[kk][e].w};
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(x[k] << 16)), fabsf(__uint_as_float(x[k] & 0xFFFF0000u))));
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // mx in [2^ex, 2^(ex+1)); scale 2^se, se = 7 - ex (kept where both 2^se and 2^-se are normal floats)
+        const int ex = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 255u) - 127 : 7;
+        const int se = min(max(7 - ex, -126), 126);
+        const float sc = __uint_as_float((uint32_t)(se + 127) << 23);
+        const float inv = __uint_as_float((uint32_t)(127 - se) << 23);
+#pragma unroll
+        for (int kk = 0; kk < NBA; kk++) {
+            uint32_t hw[8], lw[8];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t x[4] = {qv[kk][e].x, qv[kk][e].y, qv[kk][e].z, qv[kk][e].w};
+#pragma unroll
+                for (int k = 0; k < 4; k += 2) {
+                    // 4 consecutive elements (two dwords of bf16 pairs) -> one dword of codes per part
+                    const float v0 = __uint_as_float(x[k] << 16) * sc, v1 = __uint_as_float(x[k] & 0xFFFF0000u) * sc;
+                    const float v2 = __uint_as_float(x[k + 1] << 16) * sc;
+                    const float v3 = __uint_as_float(x[k + 1] & 0xFFFF0000u) * sc;
+                    const uint32_t h01 = f32x2_to_fp8(v0, v1), h23 = f32x2_to_fp8(v2, v3);
+                    const v2f b01 = fp8x2_lo(h01), b23 = fp8x2_lo(h23);
+                    const uint32_t l01 = f32x2_to_fp8(v0 - b01.x, v1 - b01.y), l23 = f32x2_to_fp8(v2 - b23.x, v3 - b23.y);
+                    hw[e * 2 + k / 2] = h01 | h23 << 16;
+                    lw[e * 2 + k / 2] = l01 | l23 << 16;
+                }
+            }
+            Qh[kk] = v8i{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+            Ql[kk] = v8i{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) qi[i] = __shfl(inv, 4 * lg + i, 64);
+    }
+    // scores in log2 units: p = 2^(S - m) with S = sm_scale * log2(e) * q.c, so the exponentials are exp2
+    const float sl2 = sm_scale * 1.4426950408889634f;
+    for (int i = tid; i < pps; i += 512) {
         const int j = jbase + i;
         const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
         s_row[i] = p < 0 ? -1 : ((long)pt[(long)(b / R) * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
     }
-    const int nch = MULTI ? max(0, min(pps, top_k - jbase) + AM_NJ - 1) / AM_NJ : (jbase < top_k ? 1 : 0);
-    // scores in log2 units: p = 2^(S - m) with S = sm_scale * log2(e) * q.c, so the exponentials are exp2
-    const float sl2 = sm_scale * 1.4426950408889634f;
-    float m[4], l[4];
-    v4f acc[NVB][8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) { m[i] = -INFINITY; l[i] = 0.f; }
-#pragma unroll
-    for (int vb = 0; vb < NVB; vb++)
-#pragma unroll
-        for (int t = 0; t < 8; t++) acc[vb][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    // gather of chunk c into registers: 16 codes per load, and the chunk's block scales (a position past the
-    // kept ones reads code 0 and scale 0)
-    constexpr int NSC = (AM_NJ * NB + 255) / 256;  // scales per thread
-    v4i GR[NLD];
-    float GS[NSC];
-    auto gather = [&](int c) __attribute__((always_inline)) {
+    const int nch = max(0, min(pps, top_k - jbase) + AM_NJ - 1) / AM_NJ;
+    // chunk c's codes and scales into LDS.  Code load i (of a wave: i = w, w + 8, ...) fills 64 consecutive 16-byte
+    // slots; slot s is granule s % NG of position s / NG (granule NG - 1 is padding).  Scale load i fills 64 floats:
+    // block i of the chunk's positions.  Every wave issues the same number of loads, all of them unconditionally:
+    // a slot with nothing to load (padding, a position past the kept ones, no next chunk) reads zeros, so such a
+    // position has value 0 and scale 0.  (A direct-to-LDS load on a conditional path makes the compiler wait for
+    // it before later LDS accesses, which would undo the overlap.)
+    const uint8_t *const dummy = (const uint8_t *)g_zero16;
+    auto gather = [&](int c, bool more, uint8_t *dc, float *dsc) __attribute__((always_inline)) {
         const int cbase = c * AM_NJ;
+        // the lane's slot arithmetic is redone per chunk: hoisted out of the chunk loop its results would stay
+        // live across the chunk's arithmetic and spill
+        int ln64 = lane;
+        asm volatile("" : "+v"(ln64));
+        long rows[NIW], srows[NSW];
 #pragma unroll
-        for (int k = 0; k < NLD; k++) {
-            const int id = k * 256 + tid;
-            GR[k] = v4i{0, 0, 0, 0};
-            if (id < AM_NJ * (Dc / 16)) {
-                const long row = s_row[cbase + id / (Dc / 16)];
-                if (row >= 0) GR[k] = *(const v4i *)(kv + row * Dc + (id % (Dc / 16)) * 16);
-            }
+        for (int k = 0; k < NIW; k++) rows[k] = s_row[min(cbase + ((k * 8 + w) * 64 + ln64) / NG, AM_MAXPPS - 1)];
+#pragma unroll
+        for (int k = 0; k < NSW; k++) srows[k] = s_row[min(cbase + ln64, AM_MAXPPS - 1)];
+#pragma unroll
+        for (int k = 0; k < NIW; k++) {
+            const int i = k * 8 + w, sl = i * 64 + ln64, p = sl / NG, g = sl - p * NG;
+            const bool ok = more && p < AM_NJ && g < Dc / 16 && rows[k] >= 0;
+            const uint8_t *src = ok ? kv + rows[k] * Dc + g * 16 : dummy;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(dc + i * 1024), 16, 0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < NSC; k++) {
-            const int i = k * 256 + tid;
-            GS[k] = 0.f;
-            if (i < AM_NJ * NB) {
-                const long row = s_row[cbase + i / NB];
-                if (row >= 0) GS[k] = ks[row * NB + i % NB];
-            }
+        for (int k = 0; k < NSW; k++) {
+            const int blk = k * 8 + w;
+            const bool ok = more && blk < NB && srows[k] >= 0;
+            const void *src = ok ? (const void *)(ks + srows[k] * NB + blk) : (const void *)dummy;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(dsc + blk * 64), 4, 0, 0);
         }
     };
-    // (Issuing the next chunk's gather before computing the current one measured slower: its registers, live
-    // across the chunk's arithmetic, spill, and each spill reload waits behind the loads in flight.)
-    for (int ch = 0; ch < nch; ch++) {
-        const int cb = ch * AM_NJ;  // chunk base within the split
-        __syncthreads();            // s_row is complete; the previous chunk's LDS reads are done
-        gather(ch);
-        // chunk ch's codes converted to bf16 (two 16-byte LDS writes per load) and its scales into LDS
+    // mh, lh: this wave's running max and sum over its own positions, heads 4 lg + i; ma: the max acc refers to
+    float mh[4], lh[4], ma[4];
+    v4f acc[NT];
 #pragma unroll
-        for (int k = 0; k < NLD; k++) {
-            const int id = k * 256 + tid;
-            if (id < AM_NJ * (Dc / 16)) {
-                __bf16 *dst = s_cb + (id / (Dc / 16)) * CBP + (id % (Dc / 16)) * 16;
-                *(v8bf *)dst = fp8x8_to_bf16((uint32_t)GR[k][0], (uint32_t)GR[k][1]);
-                *(v8bf *)(dst + 8) = fp8x8_to_bf16((uint32_t)GR[k][2], (uint32_t)GR[k][3]);
+    for (int i = 0; i < 4; i++) { mh[i] = -INFINITY; lh[i] = 0.f; ma[i] = -INFINITY; }
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // chunk c from buffers (cc, cs), prefetching chunk c + 1 into (nc, ns)
+    auto chunk = [&](int c, const uint8_t *cc, const float *cs, uint8_t *nc, float *ns) __attribute__((always_inline)) {
+        const int cb = c * AM_NJ;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c have landed
+        __syncthreads();                // everyone's have; every wave is done with chunk c - 1
+        gather(c + 1, c + 1 < nch, nc, ns);
+        // per-lane offsets are recomputed per chunk (a few VALU operations) rather than held in registers
+        // across it: the lane id passes through an opaque copy
+        int lnc = lane;
+        asm volatile("" : "+v"(lnc));
+        const int ln = lnc & 15, lg = lnc >> 4, tid = w * 64 + lnc;
+        // values: thread u -> 8 features x 8 positions, a byte transpose to [feature][position].  Lane l of a wave
+        // takes position group l % 8 and feature group l / 8; it reads its 8 rows starting at row (l % 8) of
+        // the group, so the 64 lanes' reads and writes each spread over all banks, and rotates each feature's
+        // 8 bytes back into position order.  (Positions past the kept ones were loaded as zeros.)
+        if (tid < Dv) {
+            const int pg = tid & 7, fq = tid >> 3;
+            uint32_t r0[8], r1[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const uint2 v = *(const uint2 *)(cc + (pg * 8 + ((e + pg) & 7)) * RP + fq * 8);
+                r0[e] = v.x;
+                r1[e] = v.y;
             }
-        }
-#pragma unroll
-        for (int k = 0; k < NSC; k++) {
-            const int i = k * 256 + tid;
-            if (i < AM_NJ * NB) s_sc[i % NB][i / NB] = GS[k];
-        }
-        __syncthreads();
-        // values: thread -> 8 features x 8 positions, transposed to [feature][position]
-        for (int u = tid; u < (Dv / 8) * (AM_NJ / 8); u += 256) {
-            const int fq = u % (Dv / 8), pg = u / (Dv / 8);
-            v4i r[8];
-#pragma unroll
-            for (int e = 0; e < 8; e++) r[e] = *(const v4i *)(s_cb + (pg * 8 + e) * CBP + fq * 8);
+            uint32_t lo0[4], lo1[4], hi0[4], hi1[4];
+            tr4x4(r0[0], r0[1], r0[2], r0[3], lo0);
+            tr4x4(r0[4], r0[5], r0[6], r0[7], lo1);
+            tr4x4(r1[0], r1[1], r1[2], r1[3], hi0);
+            tr4x4(r1[4], r1[5], r1[6], r1[7], hi1);
+            const int sh = pg * 8;
 #pragma unroll
             for (int k = 0; k < 8; k++) {
-                const uint32_t sl = (k & 1) ? 0x07060302u : 0x05040100u;
-                v4i o;
-#pragma unroll
-                for (int mm = 0; mm < 4; mm++)
-                    o[mm] = (int)__builtin_amdgcn_perm((uint32_t)r[2 * mm + 1][k >> 1], (uint32_t)r[2 * mm][k >> 1], sl);
-                const int f = fq * 8 + k;
-                *(v4i *)(s_v + f * PP + ((pg ^ ((f >> 4) & 7)) << 3)) = o;
+                const uint64_t x = k < 4 ? ((uint64_t)lo1[k] << 32 | lo0[k]) : ((uint64_t)hi1[k - 4] << 32 | hi0[k - 4]);
+                *(uint64_t *)(s_vt + (fq * 8 + k) * VP + pg * 8) = x << sh | x >> ((64 - sh) & 63);
             }
         }
-        // scores: S[j] = 16 heads x positions j*16 .. +16; lane holds heads 4 lg + i of position cb + j*16 + ln
-        v4f S[4];
+        // partial scores over this wave's blocks, all four position tiles: tile j covers positions
+        // 16 ((j + 2 half) % 4) + ln, so tiles 0, 1 are this wave's own positions and 2, 3 its partner's; lane
+        // holds heads 4 lg + i, in true units (times 2^-e)
+        v4f sp[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) sp[j] = v4f{0.f, 0.f, 0.f, 0.f};
         if (active) {
-            // the four position tiles are four independent accumulator chains, interleaved so that consecutive
-            // instructions do not wait on each other; each 128-feature block's operands are read before its
-            // instructions (one wave per SIMD: nothing else would hide the LDS latency)
-            v4f sacc[4];
 #pragma unroll
-            for (int j = 0; j < 4; j++) sacc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < NBA; kk++) {
+                if (kk >= nkb) break;
+                const int kb = kb0 + kk;
+                // B: 32 code bytes of the position, the lane's K range of block kb (re-read within d_c where the
+                // block is half past it: the query's part there is zero)
+                const int f = kb * 128 + lg * 32 < Dc ? kb * 128 + lg * 32 : kb * 128 + (lg & 1) * 32;
 #pragma unroll
-            for (int blk = 0; blk < NB; blk++) {
-                v4f a[4];
+                for (int jp = 0; jp < 4; jp += 2) {
+                    v8i Bc[2];
 #pragma unroll
-                for (int j = 0; j < 4; j++) a[j] = v4f{0.f, 0.f, 0.f, 0.f};
+                    for (int jj = 0; jj < 2; jj++) {
+                        const uint8_t *src = cc + (((jp + jj + 2 * half) & 3) * 16 + ln) * RP + f;
+                        const v4i x0 = *(const v4i *)src, x1 = *(const v4i *)(src + 16);
+                        Bc[jj] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                    }
 #pragma unroll
-                for (int q2 = 0; q2 < 4; q2 += 2) {
-                    v8bf Bt[2][4];
-#pragma unroll
-                    for (int q = 0; q < 2; q++)
-#pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            if (blk * 4 + q2 + q < KQ)
-                                Bt[q][j] = *(const v8bf *)(s_cb + (j * 16 + ln) * CBP + lg * 8 + (blk * 4 + q2 + q) * 32);
-#pragma unroll
-                    for (int q = 0; q < 2; q++)
-#pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            if (blk * 4 + q2 + q < KQ) a[j] = mfma_bf16(Aq[blk * 4 + q2 + q], Bt[q][j], a[j]);
+                    for (int jj = 0; jj < 2; jj++) {
+                        v4f a = mfma_fp8_acc(Qh[kk], Bc[jj], v4f{0.f, 0.f, 0.f, 0.f});
+                        a = mfma_fp8_acc(Ql[kk], Bc[jj], a);
+                        sp[jp + jj] += a * cs[kb * AM_NJ + ((jp + jj + 2 * half) & 3) * 16 + ln];
+                    }
                 }
-#pragma unroll
-                for (int j = 0; j < 4; j++) sacc[j] += a[j] * s_sc[blk][j * 16 + ln];
             }
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) sp[j][i] *= qi[i];
+            // the partner's positions (tiles 2, 3) into its P rows
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    s_p[(hg * 16 + 4 * lg + i) * SPP + (2 * (1 - half) + jj) * 16 + ln] = sp[2 + jj][i];
+        }
+        lds_barrier();  // the values and the partial scores are complete (the next chunk's loads stay in flight)
+        if (active) {
+            // own positions (tiles 0, 1: positions 32 half + 16 jj + ln); whole scores, then the online softmax
+            v4f S[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++) {
+                const int j = half * 2 + jj;
                 const bool valid = s_row[cb + j * 16 + ln] >= 0;
 #pragma unroll
-                for (int i = 0; i < 4; i++) S[j][i] = valid ? sacc[j][i] * sl2 : -INFINITY;
+                for (int i = 0; i < 4; i++)
+                    S[jj][i] = valid ? (sp[jj][i] + s_p[(hg * 16 + 4 * lg + i) * SPP + j * 16 + ln]) * sl2 : -INFINITY;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float mc = row_max16(fmaxf(S[0][i], S[1][i]));
+                const float mn = mc > mh[i] + AM_TAU || mh[i] == -INFINITY ? mc : mh[i];
+                const float al = mn == mh[i] ? 1.f : __builtin_amdgcn_exp2f(mh[i] - mn);
+                mh[i] = mn;
+                float ps = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < 2; jj++) {
+                    const float pv = S[jj][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S[jj][i] - mn);
+                    s_p[(hg * 16 + 4 * lg + i) * SPP + (half * 2 + jj) * 16 + ln] = pv;
+                    ps += pv;
+                }
+                lh[i] = lh[i] * al + row_sum16(ps);
+                if (ln == 0) s_mx[half * 64 + hg * 16 + 4 * lg + i] = mn;
             }
         }
-        __syncthreads();  // every wave's scores are done: the latent rows become P; the values are complete
-        if (!active) continue;
-        // online softmax per head (row 4 lg + i), within the wave
-        float alpha[4];
+        lds_barrier();  // p of all 64 positions and both halves' maxima are in LDS
+        if (!active) return;
+        // acc refers to the larger of the two references from now on (a rare change: AM_TAU)
+        {
+            float al[4];
+            bool moved = false;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float mc = row_max16(fmaxf(fmaxf(S[0][i], S[1][i]), fmaxf(S[2][i], S[3][i])));
-            const float mn = fmaxf(m[i], mc);
-            alpha[i] = mn == -INFINITY ? 1.f : exp2f(m[i] - mn);
-            m[i] = mn;
-            float ps = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float pv = S[j][i] == -INFINITY ? 0.f : exp2f(S[j][i] - mn);
-                s_p[w][4 * lg + i][j * 16 + ln] = pv;
-                ps += pv;
+            for (int i = 0; i < 4; i++) {
+                const float mn = fmaxf(s_mx[hg * 16 + 4 * lg + i], s_mx[64 + hg * 16 + 4 * lg + i]);
+                al[i] = mn == ma[i] ? 1.f : __builtin_amdgcn_exp2f(ma[i] - mn);
+                moved |= mn != ma[i];
+                ma[i] = mn;
             }
-            l[i] = l[i] * alpha[i] + row_sum16(ps);
+            if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+                for (int t = 0; t < NT; t++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) acc[t][i] *= al[i];
+            }
         }
-        if (MULTI && ch > 0) {  // rescale the running sums (still zero in the first chunk)
-#pragma unroll
-            for (int vb = 0; vb < NVB; vb++)
-#pragma unroll
-                for (int t = 0; t < 8; t++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++) acc[vb][t][i] *= alpha[i];
+        // p of half h (positions 32 h ..) is relative to that half's max: factor 2^(m_h - max) for head ln
+        float corr[2];
+        {
+            const float m0 = s_mx[hg * 16 + ln], m1 = s_mx[64 + hg * 16 + ln], mn = fmaxf(m0, m1);
+            corr[0] = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mn);
+            corr[1] = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
         }
-        // O += P' C over two K steps of 32 positions: A = P' (head ln, positions 8 lg .. + 8), B = values
-        // (feature 16 t + ln of block vb, the same positions)
+        // O += P' C over two K steps of 32 positions (the two halves): A = P' (head ln, positions 8 lg .. + 8),
+        // B = values (feature half FV + 16 t + ln, the same positions)
 #pragma unroll
         for (int kstep = 0; kstep < 2; kstep++) {
             const int pl = kstep * 32 + lg * 8;  // first position of this lane's K group (within the chunk)
-            const v4f p0 = *(const v4f *)&s_p[w][ln][pl], p1 = *(const v4f *)&s_p[w][ln][pl + 4];
+            const v4f p0 = *(const v4f *)&s_p[(hg * 16 + ln) * SPP + pl], p1 = *(const v4f *)&s_p[(hg * 16 + ln) * SPP + pl + 4];
             const float pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
-            for (int vb = 0; vb < NVB; vb++) {
-                const v4f c0 = *(const v4f *)&s_sc[vb][pl], c1 = *(const v4f *)&s_sc[vb][pl + 4];
+            for (int vw = 0; vw < NVW; vw++) {
+                const int vb = half * FV / 128 + vw;  // scale block of these features
+                const v4f c0 = *(const v4f *)&cs[vb * AM_NJ + pl], c1 = *(const v4f *)&cs[vb * AM_NJ + pl + 4];
                 const float sc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
                 v8bf Ah, Al;
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    const float x = pr[e] * sc[e];
+                    // (a position past the kept ones has p = 0 and scale 0)
+                    const float x = pr[e] * corr[kstep] * sc[e];
                     const __bf16 hb = (__bf16)x;
                     Ah[e] = hb;
                     Al[e] = (__bf16)(x - (float)hb);
                 }
-                v8bf Bv[8];
 #pragma unroll
-                for (int t = 0; t < 8; t++) {
-                    const int f = vb * 128 + t * 16 + ln;
-                    Bv[t] = *(const v8bf *)(s_v + f * PP + (((kstep * 4 + lg) ^ ((vb * 8 + t) & 7)) << 3));
-                }
+                for (int t0 = 0; t0 < TPB; t0 += 4) {
+                    uint2 Bv[4];
 #pragma unroll
-                for (int t = 0; t < 8; t++) {
-                    acc[vb][t] = mfma_bf16(Ah, Bv[t], acc[vb][t]);
-                    acc[vb][t] = mfma_bf16(Al, Bv[t], acc[vb][t]);
+                    for (int t = 0; t < 4; t++)
+                        if (t0 + t < TPB) Bv[t] = *(const uint2 *)(s_vt + (half * FV + vw * 128 + (t0 + t) * 16 + ln) * VP + pl);
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        if (t0 + t >= TPB) break;
+                        const v8bf Bb = fp8x8_to_bf16(Bv[t].x, Bv[t].y);
+                        acc[vw * TPB + t0 + t] = mfma_bf16(Ah, Bb, acc[vw * TPB + t0 + t]);
+                        acc[vw * TPB + t0 + t] = mfma_bf16(Al, Bb, acc[vw * TPB + t0 + t]);
+                    }
                 }
             }
         }
+    };
+    __syncthreads();  // s_row is complete
+    if (nch > 0) gather(0, true, s_c0, s_s0);
+    for (int ch = 0; ch < nch; ch += 2) {
+        chunk(ch, s_c0, s_s0, s_c1, s_s1);
+        if (ch + 1 >= nch) break;
+        chunk(ch + 1, s_c1, s_s1, s_c0, s_s0);
     }
-    if (!active) return;
-    // lane holds O[head h0 + 4 lg + i][feature vb*128 + 16 t + ln]; each 128-feature block goes through this
-    // wave's P rows in LDS (free now) and out as 16-byte stores
-    float *op = opart + (((long)b * nsplit + split) * H + h0) * Dv;
-    float(*st)[AM_NJ + 4] = s_p[w];
+    __syncthreads();  // every wave is done with s_p
+    // lane holds O[head h0 + 4 lg + i][feature half FV + 16 t + ln]; 32 features at a time go through this
+    // wave's half of its group's P rows in LDS ([16][36] floats) and out as 16-byte stores
+    if (active) {
+        float *op = opart + (((long)b * nsplit + split) * H + h0) * Dv + half * FV;
+        float *st = s_p + hg * 16 * SPP + half * 16 * 36;
 #pragma unroll
-    for (int vb = 0; vb < NVB; vb++) {
-        // two halves of 64 features per pass (the rows hold 64 + 4 floats)
+        for (int pass = 0; pass < NT / 2; pass++) {
 #pragma unroll
-        for (int half = 0; half < 2; half++) {
+            for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-            for (int t = 0; t < 4; t++)
+                for (int i = 0; i < 4; i++) st[(4 * lg + i) * 36 + tt * 16 + ln] = acc[pass * 2 + tt][i];
 #pragma unroll
-                for (int i = 0; i < 4; i++) st[4 * lg + i][t * 16 + ln] = acc[vb][half * 4 + t][i];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int head = r * 4 + lg, col = ln * 4;
+            for (int r = 0; r < 2; r++) {
+                const int head = r * 8 + (lane >> 3), col = (lane & 7) * 4;
                 // streaming store: read once by the merge, so it should not sit dirty in the last-level
                 // cache until the expert weight stream evicts it (its write-back would then compete with
                 // that stream for HBM)
 #if DL_ATT_NT_STORE
-                __builtin_nontemporal_store(*(const v4f *)&st[head][col],
-                                            (v4f *)(op + (long)head * Dv + vb * 128 + half * 64 + col));
+                __builtin_nontemporal_store(*(const v4f *)&st[head * 36 + col],
+                                            (v4f *)(op + (long)head * Dv + pass * 32 + col));
 #else
-                *(v4f *)(op + (long)head * Dv + vb * 128 + half * 64 + col) = *(const v4f *)&st[head][col];
+                *(v4f *)(op + (long)head * Dv + pass * 32 + col) = *(const v4f *)&st[head * 36 + col];
 #endif
             }
         }
+        // the sum over all 64 positions of every chunk, relative to ma: each half's sum rescaled from its max
+        if (half == 1 && ln == 0)
+#pragma unroll
+            for (int i = 0; i < 4; i++) s_l[hg * 16 + 4 * lg + i] = mh[i] == -INFINITY ? 0.f : lh[i] * __builtin_amdgcn_exp2f(mh[i] - ma[i]);
     }
-    if (ln == 0) {
+    __syncthreads();  // the second halves' sums are in LDS
+    if (active && half == 0 && ln == 0) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             float *m2 = ml + (((long)b * nsplit + split) * H + h0 + 4 * lg + i) * 2;
-            m2[0] = m[i] * 0.6931471805599453f;  // natural-log units for the merge
-            m2[1] = l[i];
+            m2[0] = ma[i] * 0.6931471805599453f;  // natural-log units for the merge
+            m2[1] = (mh[i] == -INFINITY ? 0.f : lh[i] * __builtin_amdgcn_exp2f(mh[i] - ma[i])) + s_l[hg * 16 + 4 * lg + i];
         }
     }
 }
@@ -962,11 +1107,11 @@ int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv
 #define DL_AM(KQ_, NVB_)                                                                                            \
     if (Dc == KQ_ * 32 && Dv == NVB_ * 128) {                                                                       \
         if (pps > AM_NJ)                                                                                            \
-            hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_, true>), g, dim3(256), 0, s, (const uint16_t *)q,              \
+            hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_, true>), g, dim3(512), 0, s, (const uint16_t *)q,              \
                                (const uint8_t *)kv, kv_scale, pg.page_table, pg.max_pages_per_seq, R, ps_shift, sel,    \
                                top_k, H, pps, sm_scale, opart, ml);                                                 \
         else                                                                                                        \
-            hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_, false>), g, dim3(256), 0, s, (const uint16_t *)q,             \
+            hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_, false>), g, dim3(512), 0, s, (const uint16_t *)q,             \
                                (const uint8_t *)kv, kv_scale, pg.page_table, pg.max_pages_per_seq, R, ps_shift, sel,    \
                                top_k, H, pps, sm_scale, opart, ml);                                                 \
     }
