@@ -26,7 +26,10 @@
  *   Memory      Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte aligned,
  *               row-major and densely packed in the stated shape.  The library never allocates,
  *               frees or keeps device memory; scratch comes from the caller's workspace `ws` of
- *               `ws_bytes` bytes (query the size first; 256-byte alignment).  Inputs are never
+ *               `ws_bytes` bytes (query the size first; 256-byte alignment).  A workspace also carries
+ *               a scheduling hint from one call to the next (the expert kernels' per-XCD shares of
+ *               their work, from the rates measured in the last call); it never changes a result, so
+ *               any workspace of the right size works, and reusing one per stream is fastest.  Inputs are never
  *               modified; outputs are overwritten completely (including -1 padding).  Descriptor structs (dl_pages,
  *               dl_mat, dl_layer_desc, dl_layer_io) live in HOST memory and are read during the
  *               call only.

@@ -98,8 +98,45 @@ __host__ __device__ inline int gemv_slots(const GemvArgs &a) { return a.queue ? 
 static constexpr int MAX_KSPLIT = 16;
 static constexpr int GEMV_MAXCHUNK = 128;  // most 128-wide K-blocks in one chunk of the FP8 GEMV
 static constexpr int GEMV_MAXMAT = 4096;  // active matrices of one FP8 GEMV (plan mode)
-// Work-queue counters of one FP8 GEMV: GEMV_QPOOLS pools, one counter every GEMV_QSTRIDE ints (256 B apart).
+// Work-queue state of one FP8 GEMV: GEMV_QPOOLS pools, one line of GEMV_QSTRIDE ints (256 B) each: [0] the
+// pool's piece counter, [1] its finished waves, [2..3] and [4..5] the start and end time of its last launch
+// (s_memrealtime ticks).  Ints [GEMV_QTAB, GEMV_QTAB + GEMV_QPOOLS) of pool 0's line hold the pools' shares of a
+// round of GEMV_QROUND pieces (written by the plan from the pools' measured rates).
 static constexpr int GEMV_QPOOLS = 8, GEMV_QSTRIDE = 64, GEMV_QINTS = GEMV_QPOOLS * GEMV_QSTRIDE;
+static constexpr int GEMV_QROUND = 512, GEMV_QTAB = 16;
+
+// The pools' shares m[0..7] of a round: at least 1 each and GEMV_QROUND in all, else (never written) equal ones.
+__device__ inline void gemv_shares_read(const int *q, int m[GEMV_QPOOLS])
+{
+    int tot = 0;
+    bool ok = true;
+#pragma unroll
+    for (int p = 0; p < GEMV_QPOOLS; p++) {
+        m[p] = q[GEMV_QTAB + p];
+        ok = ok && m[p] >= 1 && m[p] <= GEMV_QROUND;
+        tot += ok ? m[p] : 0;
+    }
+    if (!ok || tot != GEMV_QROUND)
+#pragma unroll
+        for (int p = 0; p < GEMV_QPOOLS; p++) m[p] = GEMV_QROUND / GEMV_QPOOLS;
+}
+
+// Position in its round of pool p's k-th slot (k < m[p]).  The slots of all pools are ordered by (k + 1/2) / m_p,
+// ties to the lower pool, so each pool's slots are spread evenly over the round and the pools advance through the
+// pieces side by side; equal shares give the plain interleave p, p + 8, ....  The positions of all (p, k) are a
+// permutation of the round: the position is the number of slots ordered before (p, k).
+__device__ inline int gemv_slot_pos(const int m[GEMV_QPOOLS], int p, int k)
+{
+    const int B = m[p], B2 = 2 * m[p];
+    int pos = k;
+#pragma unroll
+    for (int q = 0; q < GEMV_QPOOLS; q++) {
+        if (q == p) continue;
+        const int A = (2 * k + 1) * m[q];  // slot k' of pool q comes first iff (2k' + 1) m_p < A (<= A for q < p)
+        pos += min(m[q], (A + B - (q < p ? 0 : 1)) / B2);
+    }
+    return pos;
+}
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
 // Flat mode for an FP8 GEMV of about `units_est` units: the K split (<= max_ksplit chunks) with chunks no
 // longer than a wave's share of steps.

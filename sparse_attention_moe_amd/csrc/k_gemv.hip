@@ -50,15 +50,16 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // npc - 1 points (halving: the first piece is half the range, the next a quarter, ..., the last two equal; one
 // piece is the whole range), and piece j of every unit writes partial slot j, so the sums do not depend on which
 // wave ran a piece.  Pieces are numbered piece-major (all units' first pieces, then all units' second ones, ...),
-// so the long pieces go first and the short ones last.  The pieces are dealt into GEMV_QPOOLS pools (piece i to
-// pool i % GEMV_QPOOLS, so each pool keeps the long-first order and the pools advance through the weights side by
-// side); workgroup b draws from pool b % GEMV_QPOOLS, which with the round-robin dispatch over the eight XCDs is
-// its XCD's own.  Each wave's first piece of its pool is fixed by its index, each further one comes from the
+// so the long pieces go first and the short ones last.  The pieces are dealt into GEMV_QPOOLS pools in rounds of
+// GEMV_QROUND: pool p takes m_p slots of every round, spread evenly over it (equal shares give piece i to pool
+// i % GEMV_QPOOLS), so each pool keeps the long-first order and the pools advance through the weights side by
+// side; the shares come from the pools' measured rates in the previous launch (set by the plan).  Workgroup b
+// draws from pool b % GEMV_QPOOLS, which with the round-robin dispatch over the eight XCDs is its XCD's own.  Each wave's first piece of its pool is fixed by its index, each further one comes from the
 // pool's device counter, drawn right after the current piece's first loads so that the atomic's round trip stays
 // off the wait for any load issued before it.  A counter serves one atomic at a
 // time: a single one for the whole device made the waves queue for their tickets (and a wave's loads complete
-// in order behind its atomic).  Balance is within each pool: moving drained pools' waves on to the others
-// evened the XCDs out but piled them onto the remaining counters, and both passes got slower.
+// in order behind its atomic).  Balance between the pools comes from their shares: moving drained pools' waves
+// on to the others evened the XCDs out but piled them onto the remaining counters, and both passes got slower.
 template <bool SW, int RT>
 struct Stage {
     v8i A[RT], A2[RT];
@@ -219,6 +220,25 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     const int n_act = a.n_active_dev ? *a.n_active_dev : a.n_active_host;
     const int groups = (a.ntok_host + TPG - 1) / TPG;  // uniform mode
     const int tiles = a.rows / (16 * RT);
+    // queue: pieces, pool, tickets handed out by index, the pool's counter, the next ticket (lane 0), this slot,
+    // the pools' shares of a round
+    int qtot = 0, npool = 1, pool = 0, qbase = 0, qtk = 0, qslot = 0;
+    int qm[GEMV_QPOOLS];
+    int *qc = nullptr;
+    if (a.queue) {
+        npool = min((int)gridDim.x, GEMV_QPOOLS);
+        pool = blockIdx.x % npool;
+        qc = a.queue + pool * GEMV_QSTRIDE;
+        qbase = 4 * (((int)gridDim.x - pool + npool - 1) / npool);  // the pool's waves
+        gemv_shares_read(a.queue, qm);
+        if (blockIdx.x < npool && threadIdx.x == 0)
+            *(unsigned long long *)(qc + 2) = __builtin_amdgcn_s_memrealtime();
+    }
+    // a wave of the pool is done: the last one records the time
+    auto q_done = [&]() {
+        if (a.queue && lane == 0 && atomicAdd(qc + 1, 1) == qbase - 1)
+            *(unsigned long long *)(qc + 4) = __builtin_amdgcn_s_memrealtime();
+    };
     long units;
     if (a.grp_off) {
         for (int i = threadIdx.x; i <= n_act; i += 256) s_goff[i] = a.grp_off[i];
@@ -230,10 +250,12 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     const int *goff = a.grp_off ? s_goff : nullptr;
     const long S = units * a.nkb;  // steps of all units
     long s0, s1;
-    // queue: pieces, pool, tickets handed out by index, the pool's counter, the next ticket (lane 0), this slot
-    int qtot = 0, npool = 1, pool = 0, qbase = 0, qtk = 0, qslot = 0;
-    int *qc = nullptr;
-    auto qindex = [&](int t) { return (long)t * npool + pool; };  // ticket t of the wave's pool -> piece
+    // ticket t of the wave's pool -> piece: its (t mod m_pool)-th slot of round t / m_pool
+    auto qindex = [&](int t) {
+        if (npool < GEMV_QPOOLS) return (long)t * npool + pool;
+        const int n = qm[pool];
+        return (long)(t / n) * GEMV_QROUND + gemv_slot_pos(qm, pool, t % n);
+    };
     // piece t -> steps [s0, s1) of unit t % units, K-blocks [nkb - nkb >> j, nkb - nkb >> (j + 1)) with j = t / units
     auto qpiece = [&](int t, long &ps, long &pe, int &slot) {
         const int j = (int)(t / units);
@@ -244,12 +266,11 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     };
     if (a.queue) {
         qtot = (int)(units * a.npc);
-        npool = min((int)gridDim.x, GEMV_QPOOLS);
-        pool = blockIdx.x % npool;
-        qc = a.queue + pool * GEMV_QSTRIDE;
-        qbase = 4 * (((int)gridDim.x - pool + npool - 1) / npool);
         const int t0 = (blockIdx.x / npool) * 4 + (threadIdx.x >> 6);
-        if (qindex(t0) >= qtot) return;
+        if (qindex(t0) >= qtot) {
+            q_done();
+            return;
+        }
         qpiece((int)qindex(t0), s0, s1, qslot);
     } else if (a.flat) {
         // at least kchunk steps per wave, so a chunk is split at most once
@@ -265,7 +286,10 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
         s0 = (i0 / a.ksplit) * a.nkb + min((long)a.nkb, (i0 % a.ksplit) * a.kchunk);
         s1 = (i1 / a.ksplit) * a.nkb + min((long)a.nkb, (i1 % a.ksplit) * a.kchunk);
     }
-    if (s0 >= s1) return;
+    if (s0 >= s1) {
+        q_done();
+        return;
+    }
     // end of the segment starting at step x: the end of its chunk, or s1
     auto seg_end = [&](long x) {
         const long unit = x / a.nkb;
@@ -376,6 +400,7 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     };
     while (step(X, Y) && step(Y, X)) {
     }
+    q_done();
 }
 
 // One-shot projection GEMV (one FP8 matrix, either layout, tokens 0..ntok-1): a workgroup owns PROJ_RT * 16

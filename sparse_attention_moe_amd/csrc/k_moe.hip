@@ -182,6 +182,68 @@ __device__ __forceinline__ int token_topk(const double *lrow, int E, int ke)
 // output), so an expert's pair rank is the number of earlier tokens in its token mask (B <= 64); otherwise the
 // earlier picks are counted.  A negative pick is skipped: its pair index is -1 and the pairs computed here stay
 // contiguous (shared experts' pairs right after the routed ones).  s_cnt holds E + 1 entries.
+// The pools' shares of the next launch of one expert GEMV (q: its GEMV_QINTS block), from the last launch's
+// measured times: pool p ran m_p of every GEMV_QROUND pieces and took T_p, so its rate is m_p / T_p; the new
+// shares move three quarters of the way to the rates' proportions, within half and one and a half times an equal
+// share.  (The pools are the XCDs: the dispatch deals workgroups round-robin over them, and their read rates
+// differ by up to about 15% on one device, the slow ones the same from launch to launch.)  Which
+// pool runs a piece never changes a result (piece j of a unit always writes partial slot j).  Shares or times
+// that were never written give equal shares.  Lanes 0..7 of one wave.
+__device__ void gemv_pool_shares(int *q, int lane)
+{
+    int m[GEMV_QPOOLS];
+    gemv_shares_read(q, m);
+    float rl = 0.f;
+    bool okl = true;
+    if (lane < GEMV_QPOOLS) {
+        const unsigned long long t0 = *(const unsigned long long *)(q + lane * GEMV_QSTRIDE + 2);
+        const unsigned long long t1 = *(const unsigned long long *)(q + lane * GEMV_QSTRIDE + 4);
+        int ml = 0;
+#pragma unroll
+        for (int p = 0; p < GEMV_QPOOLS; p++) ml = lane == p ? m[p] : ml;
+        okl = t1 > t0 && t1 - t0 < 100000000ull;  // under a second of 100 MHz ticks
+        rl = okl ? ml / (float)(t1 - t0) : 0.f;
+    }
+    const bool ok = __builtin_amdgcn_ballot_w64(!okl) == 0;
+    float r[GEMV_QPOOLS], rs = 0.f;
+#pragma unroll
+    for (int p = 0; p < GEMV_QPOOLS; p++) {
+        r[p] = __shfl(rl, p, 64);
+        rs += r[p];
+    }
+    constexpr int EQ = GEMV_QROUND / GEMV_QPOOLS, LO = EQ / 2, HI = EQ + EQ / 2;
+    int n[GEMV_QPOOLS];
+    if (!ok || !(rs > 0.f)) {
+#pragma unroll
+        for (int p = 0; p < GEMV_QPOOLS; p++) n[p] = EQ;
+    } else {
+        float x[GEMV_QPOOLS];
+        int tot = 0;
+#pragma unroll
+        for (int p = 0; p < GEMV_QPOOLS; p++) {
+            x[p] = fminf(fmaxf(0.25f * m[p] + 0.75f * GEMV_QROUND * r[p] / rs, (float)LO), (float)HI);
+            n[p] = (int)x[p];
+            tot += n[p];
+        }
+        // the remaining slots to the largest remainders (at most HI each)
+        for (; tot < GEMV_QROUND; tot++) {
+            int b = 0;
+            float bf = -1.f;
+#pragma unroll
+            for (int p = 0; p < GEMV_QPOOLS; p++)
+                if (n[p] < HI && x[p] - n[p] > bf) { b = p; bf = x[p] - n[p]; }
+#pragma unroll
+            for (int p = 0; p < GEMV_QPOOLS; p++) n[p] += p == b;
+        }
+    }
+    if (lane < GEMV_QPOOLS) {
+        int nl = 0;
+#pragma unroll
+        for (int p = 0; p < GEMV_QPOOLS; p++) nl = lane == p ? n[p] : nl;
+        q[GEMV_QTAB + lane] = nl;
+    }
+}
+
 __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool distinct, int *s_cnt, int *s_off,
                            unsigned long long *s_mask, const MoePlan &p)
 {
@@ -199,7 +261,13 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
         if (use_mask) atomicOr(&s_mask[e], 1ull << (i / ke));
     }
     __syncthreads();
-    if (p.queue && tid < 2 * GEMV_QPOOLS) p.queue[tid * GEMV_QSTRIDE] = 0;  // the expert GEMVs' work-queue counters
+    // the expert GEMVs' work queues: the pools' shares from their last launch, cleared counters
+    if (p.queue && nT >= 256 && (tid >> 6) >= 2 && (tid >> 6) < 4)
+        gemv_pool_shares(p.queue + ((tid >> 6) - 2) * GEMV_QINTS, lane);
+    if (p.queue && tid < 2 * GEMV_QPOOLS) {
+        p.queue[tid * GEMV_QSTRIDE] = 0;
+        p.queue[tid * GEMV_QSTRIDE + 1] = 0;
+    }
     if (tid < 64) {
         // lane owns experts [lane * per, (lane + 1) * per)
         const int per = (E + 63) / 64;
