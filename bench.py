@@ -155,13 +155,15 @@ class Unfused:
         self.ex = torch.empty(B, spec.ke, dtype=torch.int32, device=dev)
         self.g = torch.empty(B, spec.ke, dtype=torch.float32, device=dev)
         self.y = torch.empty_like(step.y)
-        self.m = {k: step.mat(k) for k in ("w_uv", "w_o", "w_gate", "w_up", "w_down")}
+        # a matrix the workload does not have (the tiny workload's W_UV) is passed as NULL
+        self.m = {k: (step.mat(k) if step.mat(k).w else None) for k in ("w_uv", "w_o", "w_gate", "w_up", "w_down")}
         self.keep = step  # the tiled weights live in the step object
         import ctypes as C
         L = dl.load()
         self.ws_i = dl.workspace(L.dl_indexer_topk_workspace(C.byref(self.pg)), dev)
-        self.ws_a = dl.workspace(L.dl_sparse_attn_workspace(B, spec.H, spec.Dv, spec.topk, C.byref(self.m["w_uv"]),
-                                                            C.byref(self.m["w_o"])), dev)
+        ref = lambda m: C.byref(m) if m is not None else None
+        self.ws_a = dl.workspace(L.dl_sparse_attn_workspace(B, spec.H, spec.Dv, spec.topk, ref(self.m["w_uv"]),
+                                                            ref(self.m["w_o"])), dev)
         self.ws_r = dl.workspace(L.dl_moe_route_workspace(B, spec.D, spec.E), dev)
         self.ws_f = dl.workspace(L.dl_moe_ffn_workspace(B, spec.D, spec.I, spec.ke, spec.E, spec.n_shared), dev)
 

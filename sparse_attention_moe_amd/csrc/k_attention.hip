@@ -301,7 +301,7 @@ static constexpr float AM_TAU = 8.f;
 //   output   O += P' C with P' = p * (block scale) in bf16 high and low halves (about 16 significant bits) on
 //            v_mfma_f32_16x16x32_bf16, the e4m3 values converted to bf16 (exactly) as they are read.
 // opart [B, nsplit, H, Dv] holds the unnormalised sums, ml [B, nsplit, H, 2] the (max, sum) they refer to.
-template <int KQ, int NVB, bool MULTI>  // MULTI: more than one chunk of 64 positions per split (unused)
+template <int KQ, int NVB, bool MULTI>  // MULTI: more than one chunk of 64 positions per split
 __global__ __launch_bounds__(512, 1) void k_attn_mla(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                      const float *__restrict__ ks, const int32_t *__restrict__ pt,
                                                      int max_pages, int R, int ps_shift, const int32_t *__restrict__ sel,
@@ -341,6 +341,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_mla(const uint16_t *__restrict_
     const int kb0 = half ? NBA : 0, nkb = half ? NB - NBA : NBA;
     const int ps_mask = (1 << ps_shift) - 1;
     const int jbase = split * pps;
+    // the split's kept positions -> cache rows (first: their two dependent loads overlap the query's)
+    for (int i = tid; i < pps; i += 512) {
+        const int j = jbase + i;
+        const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
+        s_row[i] = p < 0 ? -1 : ((long)pt[(long)(b / R) * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
+    }
     // this wave's query blocks as FP8 A operands: head ln, features 128 kb + 32 lg .. + 32 (zero past d_c),
     // times 2^e with e chosen per head so that the largest |q| of these blocks lies in [128, 256), as e4m3 high
     // and low parts; qi[i] = 2^-e of head 4 lg + i
@@ -395,11 +401,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_mla(const uint16_t *__restrict_
     }
     // scores in log2 units: p = 2^(S - m) with S = sm_scale * log2(e) * q.c, so the exponentials are exp2
     const float sl2 = sm_scale * 1.4426950408889634f;
-    for (int i = tid; i < pps; i += 512) {
-        const int j = jbase + i;
-        const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
-        s_row[i] = p < 0 ? -1 : ((long)pt[(long)(b / R) * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
-    }
     const int nch = max(0, min(pps, top_k - jbase) + AM_NJ - 1) / AM_NJ;
     // chunk c's codes and scales into LDS.  Code load i (of a wave: i = w, w + 8, ...) fills 64 consecutive 16-byte
     // slots; slot s is granule s % NG of position s / NG (granule NG - 1 is padding).  Scale load i fills 64 floats:
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_mla(const uint16_t *__restrict_
         const int cb = c * AM_NJ;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c have landed
         __syncthreads();                // everyone's have; every wave is done with chunk c - 1
-        gather(c + 1, c + 1 < nch, nc, ns);
+        if (MULTI) gather(c + 1, c + 1 < nch, nc, ns);  // (one chunk per split: nothing to prefetch)
         // per-lane offsets are recomputed per chunk (a few VALU operations) rather than held in registers
         // across it: the lane id passes through an opaque copy
         int lnc = lane;
