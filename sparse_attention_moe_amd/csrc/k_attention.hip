@@ -6,17 +6,19 @@
 // whole latent (d_c features), the value its first d_v features.
 //
 // Two kernels:
-//  * k_attn_mla (FP8 latents, bf16 queries, 16 | heads): split over the kept positions like flash
-//    decoding.  A workgroup owns one row, a run of kept positions and up to 64 heads (two waves per 16
-//    heads), so every kept latent is gathered once for all heads.  Positions are staged 64 at a time as raw
-//    e4m3 bytes in LDS by the direct global-to-LDS loads, the next chunk landing while the current one is
-//    computed.  Scores are [16 heads x 128] x [128 x 16 positions] products on the FP8 matrix cores
-//    (v_mfma_f32_16x16x128_f8f6f4): each query, scaled by a power of two, is split into two e4m3 parts
-//    whose sum is the bf16 query exactly, so the products are exact and each 128-feature block's sum takes
-//    its scale once.  The softmax runs online in fp32.  The values are transposed once per chunk into
-//    [feature][position] byte rows, and O += P' C with P' = p * (block scale) split into bf16 high and low
-//    halves (about 16 significant bits) on v_mfma_f32_16x16x32_bf16, so the output keeps fp32-level
-//    accuracy.  The splits are merged afterwards (max-rescaled sums), with W_UV applied in the merge.
+//  * k_attn_mla, k_attn_mla1 (FP8 latents, bf16 queries, 16 | heads): split over the kept positions like
+//    flash decoding.  A workgroup owns one row, a run of kept positions (the split) and up to 64 heads, so
+//    every kept latent is gathered once for all heads; positions are staged 64 at a time (a chunk) in LDS.
+//    k_attn_mla (splits of several chunks, 512 threads, two waves per 16 heads): the chunk's raw e4m3 bytes
+//    arrive by the direct global-to-LDS loads, the next chunk landing while the current one is computed;
+//    scores on the FP8 matrix cores (v_mfma_f32_16x16x128_f8f6f4) with each query, scaled by a power of two,
+//    split into two e4m3 parts whose sum is the bf16 query exactly.  k_attn_mla1 (one chunk, 256 threads):
+//    the codes are converted once to bf16 in LDS and scored on v_mfma_f32_16x16x32_bf16 (every e4m3 code is
+//    exactly a bf16).  Either way the products are exact and each 128-feature block's sum takes its scale
+//    once; the softmax runs online in fp32; the values are transposed once per chunk into [feature][position]
+//    rows, and O += P' C with P' = p * (block scale) split into bf16 high and low halves (about 16
+//    significant bits), so the output keeps fp32-level accuracy.  The splits are merged afterwards
+//    (max-rescaled sums), with W_UV applied in the merge.
 //  * k_attn (any shape, fp32 or FP8 latents): a workgroup owns 4 heads of one row and scores every
 //    kept position on the vector units in fp32.
 #include "dl_common.h"
@@ -274,13 +276,268 @@ __device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32
     out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
+// Splits of one chunk (64 kept positions): grid (nsplit, ceil(H/64), B), 256 threads.  A workgroup owns one row,
+// its split and up to 64 heads: wave w takes heads 16 (4 blockIdx.y + w) .. +16, so each kept latent is gathered
+// once for all heads.  With nothing to prefetch, the fewer fixed steps of this form beat the chunked kernel below
+// (batch 8 / 128K: 18.6 against 21.9 us; batch 1 / 1M: 13.6 against 16.3 us).  For its chunk:
+//   gather   the latent codes (through the page table), converted exactly to bf16 once, as [position][feature]
+//            rows in LDS;
+//   values   the first Dv features transposed once into [feature][position] rows (position groups XOR-swizzled
+//            by the feature's 16-group);
+//   scores   S = Q C^T on v_mfma_f32_16x16x32_bf16 (queries in registers), each 128-feature block's sum taking
+//            its scale once;
+//   softmax  online per head in fp32, entirely inside the wave (DPP row reductions);
+//   output   O += P' C with P' = p * (block scale) in bf16 high and low halves (about 16 significant bits).
+// P of each wave reuses the LDS of the bf16 latents once every wave's scores are done.
+// opart [B, nsplit, H, Dv] holds the unnormalised sums, ml [B, nsplit, H, 2] the running (max, sum).
+template <int KQ, int NVB>
+__global__ __launch_bounds__(256, 1) void k_attn_mla1(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
+                                                     const float *__restrict__ ks, const int32_t *__restrict__ pt,
+                                                     int max_pages, int R, int ps_shift, const int32_t *__restrict__ sel,
+                                                     int top_k, int H, int pps, float sm_scale,
+                                                     float *__restrict__ opart, float *__restrict__ ml)
+{
+    constexpr int Dc = KQ * 32, NB = (Dc + 127) / 128, Dv = NVB * 128;
+    constexpr int CBP = Dc + 8;                         // bf16 latent row pitch
+    constexpr int PP = AM_NJ + 8;                       // value row pitch (bf16)
+    constexpr int NLD = (AM_NJ * (Dc / 16) + 255) / 256;  // 16-byte code loads per thread per chunk
+    constexpr int CB_BYTES = AM_NJ * CBP * 2;
+    constexpr int P_BYTES = 4 * 16 * (AM_NJ + 4) * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t s_cbuf[CB_BYTES > P_BYTES ? CB_BYTES : P_BYTES];
+    __shared__ __attribute__((aligned(16))) __bf16 s_v[Dv * PP];
+    __shared__ __attribute__((aligned(16))) float s_sc[NB][AM_NJ];
+    __shared__ long s_row[AM_MAXPPS];
+    __bf16 *s_cb = (__bf16 *)s_cbuf;                       // [position][CBP] bf16 latents
+    float(*s_p)[16][AM_NJ + 4] = (float(*)[16][AM_NJ + 4])s_cbuf;  // [wave][head][position] after the scores
+    const int split = blockIdx.x, b = blockIdx.z;
+    const int nsplit = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    const int h0 = (blockIdx.y * 4 + w) * 16;
+    const bool active = h0 < H;
+    const int ps_mask = (1 << ps_shift) - 1;
+    const int jbase = split * pps;
+    // queries of this wave's 16 heads, as the A operand of every K step: head ln, features 32 kk + 8 lg .. + 8
+    v8bf Aq[KQ];
+#pragma unroll
+    for (int kk = 0; kk < KQ; kk++)
+        Aq[kk] = active ? *(const v8bf *)(q + ((long)b * H + h0 + ln) * Dc + kk * 32 + lg * 8) : v8bf{};
+    for (int i = tid; i < pps; i += 256) {
+        const int j = jbase + i;
+        const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
+        s_row[i] = p < 0 ? -1 : ((long)pt[(long)(b / R) * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
+    }
+    const int nch = jbase < top_k ? 1 : 0;
+    // scores in log2 units: p = 2^(S - m) with S = sm_scale * log2(e) * q.c, so the exponentials are exp2
+    const float sl2 = sm_scale * 1.4426950408889634f;
+    float m[4], l[4];
+    v4f acc[NVB][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) { m[i] = -INFINITY; l[i] = 0.f; }
+#pragma unroll
+    for (int vb = 0; vb < NVB; vb++)
+#pragma unroll
+        for (int t = 0; t < 8; t++) acc[vb][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    // gather of chunk c into registers: 16 codes per load, and the chunk's block scales (a position past the
+    // kept ones reads code 0 and scale 0)
+    constexpr int NSC = (AM_NJ * NB + 255) / 256;  // scales per thread
+    v4i GR[NLD];
+    float GS[NSC];
+    auto gather = [&](int c) __attribute__((always_inline)) {
+        const int cbase = c * AM_NJ;
+#pragma unroll
+        for (int k = 0; k < NLD; k++) {
+            const int id = k * 256 + tid;
+            GR[k] = v4i{0, 0, 0, 0};
+            if (id < AM_NJ * (Dc / 16)) {
+                const long row = s_row[cbase + id / (Dc / 16)];
+                if (row >= 0) GR[k] = *(const v4i *)(kv + row * Dc + (id % (Dc / 16)) * 16);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NSC; k++) {
+            const int i = k * 256 + tid;
+            GS[k] = 0.f;
+            if (i < AM_NJ * NB) {
+                const long row = s_row[cbase + i / NB];
+                if (row >= 0) GS[k] = ks[row * NB + i % NB];
+            }
+        }
+    };
+    for (int ch = 0; ch < nch; ch++) {
+        const int cb = ch * AM_NJ;  // chunk base within the split
+        __syncthreads();            // s_row is complete; the previous chunk's LDS reads are done
+        gather(ch);
+        // chunk ch's codes converted to bf16 (two 16-byte LDS writes per load) and its scales into LDS
+#pragma unroll
+        for (int k = 0; k < NLD; k++) {
+            const int id = k * 256 + tid;
+            if (id < AM_NJ * (Dc / 16)) {
+                __bf16 *dst = s_cb + (id / (Dc / 16)) * CBP + (id % (Dc / 16)) * 16;
+                *(v8bf *)dst = fp8x8_to_bf16((uint32_t)GR[k][0], (uint32_t)GR[k][1]);
+                *(v8bf *)(dst + 8) = fp8x8_to_bf16((uint32_t)GR[k][2], (uint32_t)GR[k][3]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NSC; k++) {
+            const int i = k * 256 + tid;
+            if (i < AM_NJ * NB) s_sc[i % NB][i / NB] = GS[k];
+        }
+        __syncthreads();
+        // values: thread -> 8 features x 8 positions, transposed to [feature][position]
+        for (int u = tid; u < (Dv / 8) * (AM_NJ / 8); u += 256) {
+            const int fq = u % (Dv / 8), pg = u / (Dv / 8);
+            v4i r[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) r[e] = *(const v4i *)(s_cb + (pg * 8 + e) * CBP + fq * 8);
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                const uint32_t sl = (k & 1) ? 0x07060302u : 0x05040100u;
+                v4i o;
+#pragma unroll
+                for (int mm = 0; mm < 4; mm++)
+                    o[mm] = (int)__builtin_amdgcn_perm((uint32_t)r[2 * mm + 1][k >> 1], (uint32_t)r[2 * mm][k >> 1], sl);
+                const int f = fq * 8 + k;
+                *(v4i *)(s_v + f * PP + ((pg ^ ((f >> 4) & 7)) << 3)) = o;
+            }
+        }
+        // scores: S[j] = 16 heads x positions j*16 .. +16; lane holds heads 4 lg + i of position cb + j*16 + ln
+        v4f S[4];
+        if (active) {
+            // the four position tiles are four independent accumulator chains, interleaved so that consecutive
+            // instructions do not wait on each other; each 128-feature block's operands are read before its
+            // instructions (one wave per SIMD: nothing else would hide the LDS latency)
+            v4f sacc[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) sacc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int blk = 0; blk < NB; blk++) {
+                v4f a[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) a[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q2 = 0; q2 < 4; q2 += 2) {
+                    v8bf Bt[2][4];
+#pragma unroll
+                    for (int q = 0; q < 2; q++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            if (blk * 4 + q2 + q < KQ)
+                                Bt[q][j] = *(const v8bf *)(s_cb + (j * 16 + ln) * CBP + lg * 8 + (blk * 4 + q2 + q) * 32);
+#pragma unroll
+                    for (int q = 0; q < 2; q++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            if (blk * 4 + q2 + q < KQ) a[j] = mfma_bf16(Aq[blk * 4 + q2 + q], Bt[q][j], a[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) sacc[j] += a[j] * s_sc[blk][j * 16 + ln];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const bool valid = s_row[cb + j * 16 + ln] >= 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) S[j][i] = valid ? sacc[j][i] * sl2 : -INFINITY;
+            }
+        }
+        __syncthreads();  // every wave's scores are done: the latent rows become P; the values are complete
+        if (!active) continue;
+        // online softmax per head (row 4 lg + i), within the wave
+        float alpha[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float mc = row_max16(fmaxf(fmaxf(S[0][i], S[1][i]), fmaxf(S[2][i], S[3][i])));
+            const float mn = fmaxf(m[i], mc);
+            alpha[i] = mn == -INFINITY ? 1.f : exp2f(m[i] - mn);
+            m[i] = mn;
+            float ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float pv = S[j][i] == -INFINITY ? 0.f : exp2f(S[j][i] - mn);
+                s_p[w][4 * lg + i][j * 16 + ln] = pv;
+                ps += pv;
+            }
+            l[i] = l[i] * alpha[i] + row_sum16(ps);
+        }
+        // O += P' C over two K steps of 32 positions: A = P' (head ln, positions 8 lg .. + 8), B = values
+        // (feature 16 t + ln of block vb, the same positions)
+#pragma unroll
+        for (int kstep = 0; kstep < 2; kstep++) {
+            const int pl = kstep * 32 + lg * 8;  // first position of this lane's K group (within the chunk)
+            const v4f p0 = *(const v4f *)&s_p[w][ln][pl], p1 = *(const v4f *)&s_p[w][ln][pl + 4];
+            const float pr[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+            for (int vb = 0; vb < NVB; vb++) {
+                const v4f c0 = *(const v4f *)&s_sc[vb][pl], c1 = *(const v4f *)&s_sc[vb][pl + 4];
+                const float sc[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                v8bf Ah, Al;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const float x = pr[e] * sc[e];
+                    const __bf16 hb = (__bf16)x;
+                    Ah[e] = hb;
+                    Al[e] = (__bf16)(x - (float)hb);
+                }
+                v8bf Bv[8];
+#pragma unroll
+                for (int t = 0; t < 8; t++) {
+                    const int f = vb * 128 + t * 16 + ln;
+                    Bv[t] = *(const v8bf *)(s_v + f * PP + (((kstep * 4 + lg) ^ ((vb * 8 + t) & 7)) << 3));
+                }
+#pragma unroll
+                for (int t = 0; t < 8; t++) {
+                    acc[vb][t] = mfma_bf16(Ah, Bv[t], acc[vb][t]);
+                    acc[vb][t] = mfma_bf16(Al, Bv[t], acc[vb][t]);
+                }
+            }
+        }
+    }
+    if (!active) return;
+    // lane holds O[head h0 + 4 lg + i][feature vb*128 + 16 t + ln]; each 128-feature block goes through this
+    // wave's P rows in LDS (free now) and out as 16-byte stores
+    float *op = opart + (((long)b * nsplit + split) * H + h0) * Dv;
+    float(*st)[AM_NJ + 4] = s_p[w];
+#pragma unroll
+    for (int vb = 0; vb < NVB; vb++) {
+        // two halves of 64 features per pass (the rows hold 64 + 4 floats)
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) st[4 * lg + i][t * 16 + ln] = acc[vb][half * 4 + t][i];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int head = r * 4 + lg, col = ln * 4;
+                // streaming store: read once by the merge, so it should not sit dirty in the last-level
+                // cache until the expert weight stream evicts it (its write-back would then compete with
+                // that stream for HBM)
+#if DL_ATT_NT_STORE
+                __builtin_nontemporal_store(*(const v4f *)&st[head][col],
+                                            (v4f *)(op + (long)head * Dv + vb * 128 + half * 64 + col));
+#else
+                *(v4f *)(op + (long)head * Dv + vb * 128 + half * 64 + col) = *(const v4f *)&st[head][col];
+#endif
+            }
+        }
+    }
+    if (ln == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float *m2 = ml + (((long)b * nsplit + split) * H + h0 + 4 * lg + i) * 2;
+            m2[0] = m[i] * 0.6931471805599453f;  // natural-log units for the merge
+            m2[1] = l[i];
+        }
+    }
+}
+
 // Sixteen zero bytes: the source of every direct-to-LDS load that has nothing to load.
 static __device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};  // never written
 // Running maxima move only when a chunk's maximum exceeds them by more than this (log2 units), so p <= 2^8 and the
 // sums are rescaled rarely.
 static constexpr float AM_TAU = 8.f;
 
-// grid (nsplit, ceil(H/64), B), 512 threads.  A workgroup owns one row, one run of kept positions (the split)
+// Splits of several chunks: grid (nsplit, ceil(H/64), B), 512 threads.  A workgroup owns one row, one run of kept
+// positions (the split)
 // and up to 64 heads, so each kept latent is gathered once for all of them.  Waves w and w + 4 share the 16
 // heads 16 (4 blockIdx.y + w % 4) .. +16, so two waves share each SIMD and hide each other's latencies: wave w
 // holds the query's first NBA = (NB + 1) / 2 128-feature blocks, owns positions 0..31 of every chunk of 64 and
@@ -301,7 +558,7 @@ static constexpr float AM_TAU = 8.f;
 //   output   O += P' C with P' = p * (block scale) in bf16 high and low halves (about 16 significant bits) on
 //            v_mfma_f32_16x16x32_bf16, the e4m3 values converted to bf16 (exactly) as they are read.
 // opart [B, nsplit, H, Dv] holds the unnormalised sums, ml [B, nsplit, H, 2] the (max, sum) they refer to.
-template <int KQ, int NVB, bool MULTI>  // MULTI: more than one chunk of 64 positions per split
+template <int KQ, int NVB>
 __global__ __launch_bounds__(512, 1) void k_attn_mla(const uint16_t *__restrict__ q, const uint8_t *__restrict__ kv,
                                                      const float *__restrict__ ks, const int32_t *__restrict__ pt,
                                                      int max_pages, int R, int ps_shift, const int32_t *__restrict__ sel,
@@ -449,7 +706,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_mla(const uint16_t *__restrict_
         const int cb = c * AM_NJ;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c have landed
         __syncthreads();                // everyone's have; every wave is done with chunk c - 1
-        if (MULTI) gather(c + 1, c + 1 < nch, nc, ns);  // (one chunk per split: nothing to prefetch)
+        gather(c + 1, c + 1 < nch, nc, ns);
         // per-lane offsets are recomputed per chunk (a few VALU operations) rather than held in registers
         // across it: the lane id passes through an opaque copy
         int lnc = lane;
@@ -1108,11 +1365,11 @@ int launch_attention(const dl_pages &pg, const void *q, int q_dt, const void *kv
 #define DL_AM(KQ_, NVB_)                                                                                            \
     if (Dc == KQ_ * 32 && Dv == NVB_ * 128) {                                                                       \
         if (pps > AM_NJ)                                                                                            \
-            hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_, true>), g, dim3(512), 0, s, (const uint16_t *)q,              \
+            hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_>), g, dim3(512), 0, s, (const uint16_t *)q,                    \
                                (const uint8_t *)kv, kv_scale, pg.page_table, pg.max_pages_per_seq, R, ps_shift, sel,    \
                                top_k, H, pps, sm_scale, opart, ml);                                                 \
         else                                                                                                        \
-            hipLaunchKernelGGL((k_attn_mla<KQ_, NVB_, false>), g, dim3(512), 0, s, (const uint16_t *)q,             \
+            hipLaunchKernelGGL((k_attn_mla1<KQ_, NVB_>), g, dim3(256), 0, s, (const uint16_t *)q,                   \
                                (const uint8_t *)kv, kv_scale, pg.page_table, pg.max_pages_per_seq, R, ps_shift, sel,    \
                                top_k, H, pps, sm_scale, opart, ml);                                                 \
     }
