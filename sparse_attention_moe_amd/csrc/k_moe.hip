@@ -245,7 +245,7 @@ __device__ void gemv_pool_shares(int *q, int lane)
 }
 
 __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool distinct, int *s_cnt, int *s_off,
-                           unsigned long long *s_mask, const MoePlan &p)
+                           unsigned long long *s_mask, const MoePlan &p, bool shares)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const int nT = blockDim.x;
@@ -262,7 +262,7 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
     }
     __syncthreads();
     // the expert GEMVs' work queues: the pools' shares from their last launch, cleared counters
-    if (p.queue && nT >= 256 && (tid >> 6) >= 2 && (tid >> 6) < 4)
+    if (shares && p.queue && nT >= 256 && (tid >> 6) >= 2 && (tid >> 6) < 4)
         gemv_pool_shares(p.queue + ((tid >> 6) - 2) * GEMV_QINTS, lane);
     if (p.queue && tid < 2 * GEMV_QPOOLS) {
         p.queue[tid * GEMV_QSTRIDE] = 0;
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ exper
             for (int i2 = i - i % ke; i2 < i; i2++) dup |= s_exp[i2] == e;
     }
     const bool distinct = !__syncthreads_or(dup);
-    build_plan(s_exp, B, ke, E, S, distinct, s_cnt, s_off, s_mask, p);
+    build_plan(s_exp, B, ke, E, S, distinct, s_cnt, s_off, s_mask, p, true);
 }
 
 // Router top-k, fused with the dispatch plan when one workgroup of 1024 threads routes every token.  A workgroup
@@ -385,32 +385,45 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nT = 1024;
     const bool plan = p.active != nullptr;
+    // the expert GEMVs' pool shares for this step, by the last two waves (idle while the tokens are routed)
+    if (plan && p.queue && wv >= 14) gemv_pool_shares(p.queue + (wv - 14) * GEMV_QINTS, lane);
     const int tb = RP_LCAP / E;
     const int t0 = blockIdx.x * tpb, t1 = min(B, t0 + tpb);  // this workgroup's tokens
     for (int b0 = t0; b0 < t1; b0 += tb) {
         const int nb = min(tb, t1 - b0);
-        // two logits per thread per pass, every chunk's partial of both in flight at once, summed in chunk order
+        // two logits per thread per pass, summed in chunk order; eight chunks' partials of both are loaded at
+        // once, unconditionally (indices clamped into the arrays), so that the loads are in flight together: a
+        // load under a condition is waited for on its own
         for (int i0 = tid; i0 < nb * E; i0 += 2 * nT) {
-            double pc[2][ROUTE_MAXC];
+            double v2[2] = {0.0, 0.0};
+            float bv[2];  // the biases, loaded with the partials (without a bias: any readable word, unused)
 #pragma unroll
             for (int k = 0; k < 2; k++) {
-                const int i = i0 + k * nT;
-                const int b = b0 + i / E, e = i % E;
-                const bool ok = i < nb * E;
+                const int i = min(i0 + k * nT, nb * E - 1);
+                bv[k] = *(bias ? bias + i % E : (const float *)part);
+            }
+            for (int c0 = 0; c0 < nchunk; c0 += 8) {
+                double pc[2][8];
 #pragma unroll
-                for (int c = 0; c < ROUTE_MAXC; c++)
-                    pc[k][c] = (ok && c < nchunk) ? part[((long)c * B + b) * E + e] : 0.0;
+                for (int k = 0; k < 2; k++) {
+                    const int i = min(i0 + k * nT, nb * E - 1);
+                    const int b = b0 + i / E, e = i % E;
+#pragma unroll
+                    for (int c = 0; c < 8; c++) pc[k][c] = part[((long)min(c0 + c, nchunk - 1) * B + b) * E + e];
+                }
+#pragma unroll
+                for (int k = 0; k < 2; k++)
+#pragma unroll
+                    for (int c = 0; c < 8; c++)
+                        if (c0 + c < nchunk) v2[k] += pc[k][c];
             }
 #pragma unroll
             for (int k = 0; k < 2; k++) {
                 const int i = i0 + k * nT;
                 if (i >= nb * E) break;
                 const int b = b0 + i / E, e = i % E;
-                double v = 0.0;
-#pragma unroll
-                for (int c = 0; c < ROUTE_MAXC; c++)
-                    if (c < nchunk) v += pc[k][c];
-                if (bias) v += (double)bias[e];
+                double v = v2[k];
+                if (bias) v += (double)bv[k];
                 s_l[i] = v;
                 if (logits) logits[(long)b * E + e] = (float)v;
             }
@@ -433,7 +446,7 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
         }
         __syncthreads();
     }
-    if (plan) build_plan(s_exp, B, ke, E, S, true, s_cnt, s_off, s_mask, p);
+    if (plan) build_plan(s_exp, B, ke, E, S, true, s_cnt, s_off, s_mask, p, false);
 }
 
 int route_chunks(int D) { return (D + ROUTE_KC - 1) / ROUTE_KC; }
