@@ -209,6 +209,19 @@ int dl_indexer_topk_rows(const dl_pages *pages, int32_t rows_per_seq, const int8
                          int32_t n_heads, int32_t dim, int32_t top_k, int32_t *sel, int32_t *sel_score, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* Multi-row decode with pool-granular selection: R = rows_per_seq rows per sequence as in
+ * dl_indexer_topk_rows, each selecting whole pools as in dl_indexer_topk_pooled over its own visible
+ * length (row r of sequence b sees the ceil((seq_lens[b] - (R - 1 - r)) / pool) pools holding its visible
+ * positions, and writes the positions of its kept pools below that length, -1 after):
+ *   q_idx int8 [B * R, n_heads, dim]; sel int32 [B * R, top_pools * pool]; pool_score int32 [B * R,
+ *   top_pools] (nullable).
+ * R = 1 is dl_indexer_topk_pooled; pool = 1 is dl_indexer_topk_rows.  Limits as those two.
+ * Workspace: dl_indexer_topk_rows_pooled_workspace(pages, rows_per_seq, pool); 0 for unsupported values. */
+size_t dl_indexer_topk_rows_pooled_workspace(const dl_pages *pages, int32_t rows_per_seq, int32_t pool);
+int dl_indexer_topk_rows_pooled(const dl_pages *pages, int32_t rows_per_seq, int32_t pool, const int8_t *q_idx,
+                                const int8_t *pool_keys, int32_t n_heads, int32_t dim, int32_t top_pools,
+                                int32_t *sel, int32_t *pool_score, void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- S3 - S5
  * Sparse MLA decode attention over the kept positions only (Kiln, "The decode kernels ...":
  * gather the selected entries instead of masking all keys), every head reading the same latent
@@ -356,6 +369,16 @@ int dl_layer_step_rows(const dl_layer_desc *desc, const dl_layer_io *io, int32_t
 size_t dl_layer_workspace_pooled(const dl_layer_desc *desc, const dl_pages *pages, int32_t pool);
 int dl_layer_step_pooled(const dl_layer_desc *desc, const dl_layer_io *io, int32_t pool, void *ws, size_t ws_bytes,
                          void *stream);
+
+/* The step over R = rows_per_seq rows per sequence with pool-granular selection: the multi-token-prediction
+ * verification step of dl_layer_step_rows reading the pool-key cache like dl_layer_step_pooled (each row
+ * selects top_k / pool pools over its own visible length, dl_indexer_topk_rows_pooled).  R = 1 is
+ * dl_layer_step_pooled, pool = 1 is dl_layer_step_rows; limits as those two.
+ * Workspace: dl_layer_workspace_rows_pooled(desc, pages, rows_per_seq, pool); 0 for unsupported values. */
+size_t dl_layer_workspace_rows_pooled(const dl_layer_desc *desc, const dl_pages *pages, int32_t rows_per_seq,
+                                      int32_t pool);
+int dl_layer_step_rows_pooled(const dl_layer_desc *desc, const dl_layer_io *io, int32_t rows_per_seq, int32_t pool,
+                              void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

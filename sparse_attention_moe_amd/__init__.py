@@ -23,7 +23,8 @@ STATUS = {0: "DL_OK", -1: "DL_ERR_NULL", -2: "DL_ERR_SHAPE", -3: "DL_ERR_DTYPE",
 EXPORTS = ["dl_abi_version", "dl_hip_version", "dl_last_error", "dl_pack_weights", "dl_kv_append", "dl_indexer_topk_workspace", "dl_indexer_topk",
            "dl_indexer_topk_rows_workspace", "dl_indexer_topk_rows", "dl_indexer_topk_pooled_workspace",
            "dl_indexer_topk_pooled", "dl_layer_workspace_rows", "dl_layer_step_rows",
-           "dl_layer_workspace_pooled", "dl_layer_step_pooled",
+           "dl_layer_workspace_pooled", "dl_layer_step_pooled", "dl_indexer_topk_rows_pooled_workspace",
+           "dl_indexer_topk_rows_pooled", "dl_layer_workspace_rows_pooled", "dl_layer_step_rows_pooled",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route", "dl_moe_route_noalloc",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_moe_ffn_ep", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
            "dl_profile_read", "dl_probe_read", "dl_probe_null", "dl_tile_index_keys"]
@@ -96,6 +97,12 @@ def load(require_gpu: bool = True):
         L.dl_layer_workspace_pooled.restype = sz
         L.dl_layer_workspace_pooled.argtypes = [C.POINTER(LayerDesc), C.POINTER(Pages), i32]
         L.dl_layer_step_pooled.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), i32, P, sz, P]
+        L.dl_indexer_topk_rows_pooled_workspace.restype = sz
+        L.dl_indexer_topk_rows_pooled_workspace.argtypes = [C.POINTER(Pages), i32, i32]
+        L.dl_indexer_topk_rows_pooled.argtypes = [C.POINTER(Pages), i32, i32, P, P, i32, i32, i32, P, P, P, sz, P]
+        L.dl_layer_workspace_rows_pooled.restype = sz
+        L.dl_layer_workspace_rows_pooled.argtypes = [C.POINTER(LayerDesc), C.POINTER(Pages), i32, i32]
+        L.dl_layer_step_rows_pooled.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), i32, i32, P, sz, P]
         L.dl_indexer_topk_workspace.restype = sz
         L.dl_indexer_topk_workspace.argtypes = [C.POINTER(Pages)]
         L.dl_indexer_topk.argtypes = [C.POINTER(Pages), P, P, i32, i32, i32, P, P, P, sz, P]
@@ -229,13 +236,21 @@ def indexer_topk(pg: Pages, q_idx, k_pool, top_k: int, sel, sel_score=None, ws=N
 
 
 def indexer_topk_pooled(pg: Pages, pool: int, q_idx, pool_keys, top_pools: int, sel, pool_score=None, ws=None,
-                        stream=None):
-    """Pool-granular selection: sel [B, top_pools * pool] positions of the kept pools (see dl.h)."""
+                        stream=None, rows_per_seq: int = 1):
+    """Pool-granular selection: sel [B * rows_per_seq, top_pools * pool] positions of the kept pools (see dl.h)."""
     L = load()
+    if rows_per_seq == 1:
+        if ws is None:
+            ws = workspace(L.dl_indexer_topk_pooled_workspace(C.byref(pg), pool), q_idx.device)
+        _check(L.dl_indexer_topk_pooled(C.byref(pg), pool, _ptr(q_idx), _ptr(pool_keys), q_idx.shape[1],
+                                        q_idx.shape[2], top_pools, _ptr(sel), _ptr(pool_score), _ptr(ws), ws.numel(),
+                                        _stream(stream)))
+        return sel
     if ws is None:
-        ws = workspace(L.dl_indexer_topk_pooled_workspace(C.byref(pg), pool), q_idx.device)
-    _check(L.dl_indexer_topk_pooled(C.byref(pg), pool, _ptr(q_idx), _ptr(pool_keys), q_idx.shape[1], q_idx.shape[2],
-                                    top_pools, _ptr(sel), _ptr(pool_score), _ptr(ws), ws.numel(), _stream(stream)))
+        ws = workspace(L.dl_indexer_topk_rows_pooled_workspace(C.byref(pg), rows_per_seq, pool), q_idx.device)
+    _check(L.dl_indexer_topk_rows_pooled(C.byref(pg), rows_per_seq, pool, _ptr(q_idx), _ptr(pool_keys),
+                                         q_idx.shape[1], q_idx.shape[2], top_pools, _ptr(sel), _ptr(pool_score),
+                                         _ptr(ws), ws.numel(), _stream(stream)))
     return sel
 
 
@@ -346,8 +361,6 @@ class LayerStep:
         dev = t["x"].device
         self.R = getattr(spec, "R", 1)
         self.pool = getattr(spec, "pool", 1)  # > 1: pool-granular selection over t["pool_keys"]
-        if self.R > 1 and self.pool > 1:
-            raise ValueError("multi-row decode with pool-granular selection has no entry point")
         B = spec.B * self.R  # rows
         self.keep = []
         # the index keys in DL_LAYOUT_TILES where their shape allows (the scoring kernel's loads are then 1 KB
@@ -403,7 +416,9 @@ class LayerStep:
                             logits=torch.empty(B, spec.E, dtype=torch.float32, device=dev))
         self.io = io
         self.debug_outputs(debug)
-        if self.pool > 1:
+        if self.R > 1 and self.pool > 1:
+            n = L.dl_layer_workspace_rows_pooled(C.byref(d), C.byref(self.pg), self.R, self.pool)
+        elif self.pool > 1:
             n = L.dl_layer_workspace_pooled(C.byref(d), C.byref(self.pg), self.pool)
         else:
             n = L.dl_layer_workspace_rows(C.byref(d), C.byref(self.pg), self.R)
@@ -422,7 +437,10 @@ class LayerStep:
             setattr(self.io, k, _ptr(v) if on else None)
 
     def __call__(self, stream=None):
-        if self.pool > 1:
+        if self.R > 1 and self.pool > 1:
+            _check(load().dl_layer_step_rows_pooled(C.byref(self.desc), C.byref(self.io), self.R, self.pool,
+                                                    _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        elif self.pool > 1:
             _check(load().dl_layer_step_pooled(C.byref(self.desc), C.byref(self.io), self.pool, _ptr(self.ws),
                                                self.ws.numel(), _stream(stream)))
         else:

@@ -679,6 +679,40 @@ int dl_indexer_topk_pooled(const dl_pages *pages, int32_t pool, const int8_t *q_
                                (hipStream_t)stream, 1, pool);
 }
 
+size_t dl_indexer_topk_rows_pooled_workspace(const dl_pages *pages, int32_t rows_per_seq, int32_t pool)
+{
+    if (!pages || rows_per_seq < 1 || rows_per_seq > DL_MAX_ROWS_PER_SEQ) return 0;
+    if (pool < 1 || pool > pages->page_size || (pool & (pool - 1))) return 0;
+    Ws w(nullptr);
+    TopkWs t;
+    topk_ws_layout(w, *pages, t, rows_per_seq, pool);
+    return w.used();
+}
+
+int dl_indexer_topk_rows_pooled(const dl_pages *pages, int32_t rows_per_seq, int32_t pool, const int8_t *q_idx,
+                                const int8_t *pool_keys, int32_t n_heads, int32_t dim, int32_t top_pools,
+                                int32_t *sel, int32_t *pool_score, void *ws, size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    DL_TRY(check_pages(pages));
+    const int R = rows_per_seq;
+    if (R < 1 || R > DL_MAX_ROWS_PER_SEQ) return fail(DL_ERR_UNSUPPORTED, "rows per sequence %d (1..%d)", R, DL_MAX_ROWS_PER_SEQ);
+    if ((long)pages->batch * R > 4096) return fail(DL_ERR_SHAPE, "rows %ld (<= 4096)", (long)pages->batch * R);
+    if (pool < 1 || pool > pages->page_size || (pool & (pool - 1)))
+        return fail(DL_ERR_UNSUPPORTED, "pool %d (power of two, <= page size %d)", pool, pages->page_size);
+    if (!q_idx || !pool_keys || !sel) return fail(DL_ERR_NULL, "q_idx/pool_keys/sel NULL");
+    DL_TRY(check_indexer(n_heads, dim, top_pools));
+    DL_TRY(check_key_tiles(pages, dim, pool));
+    if ((long)top_pools * pool > 65536) return fail(DL_ERR_SHAPE, "top_pools * pool %ld (<= 65536)", (long)top_pools * pool);
+    DL_TRY(check_ws(ws, ws_bytes, dl_indexer_topk_rows_pooled_workspace(pages, R, pool)));
+    (void)hipGetLastError();
+    Ws w(ws);
+    TopkWs t;
+    topk_ws_layout(w, *pages, t, R, pool);
+    return launch_indexer_topk(*pages, q_idx, pool_keys, n_heads, dim, top_pools, sel, pool_score, t,
+                               (hipStream_t)stream, R, pool);
+}
+
 int dl_kv_append(const dl_pages *pages, const void *latent, int32_t lat_dt, int32_t d_c, const void *key,
                  int32_t key_dt, int32_t idx_dim, float key_scale, uint8_t *kv_pool, float *kv_scale, int8_t *k_pool,
                  void *stream)
@@ -956,6 +990,18 @@ int dl_layer_step_pooled(const dl_layer_desc *d, const dl_layer_io *io, int32_t 
                          void *stream)
 {
     return layer_step(d, io, 1, pool, ws, ws_bytes, stream);
+}
+
+size_t dl_layer_workspace_rows_pooled(const dl_layer_desc *desc, const dl_pages *pages, int32_t rows_per_seq,
+                                      int32_t pool)
+{
+    return layer_workspace(desc, pages, rows_per_seq, pool);
+}
+
+int dl_layer_step_rows_pooled(const dl_layer_desc *d, const dl_layer_io *io, int32_t rows_per_seq, int32_t pool,
+                              void *ws, size_t ws_bytes, void *stream)
+{
+    return layer_step(d, io, rows_per_seq, pool, ws, ws_bytes, stream);
 }
 
 int dl_layer_step(const dl_layer_desc *d, const dl_layer_io *io, void *ws, size_t ws_bytes, void *stream)

@@ -473,6 +473,44 @@ def test_layer_step_pooled(pool):
     say(f"pooled pool={pool}: {w}")
 
 
+@pytest.mark.parametrize("R,pool", [(2, 4), (4, 2), (3, 16)])
+def test_indexer_rows_pooled_bit_exact(R, pool):
+    # several rows per sequence, each selecting whole pools over its own visible length: a long sequence, one
+    # shorter than R (its first rows see nothing), a padding sequence, lengths that are not multiples of the pool
+    top_pools = 512 // pool
+    spec = synth.spec_replace(synth.small_fp8_spec(name=f"rows{R}-pool{pool}", seq_lens=(9001, 2, 0, 4096, 777),
+                                                   topk=512), R=R, pool=pool)
+    t = _layer(spec, seed=80 + R * pool, weights=False)
+    rows = spec.B * R
+    sel = torch.empty(rows, top_pools * pool, dtype=torch.int32, device=DEV)
+    ps = torch.empty(rows, top_pools, dtype=torch.int32, device=DEV)
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+    say(f"[gpu] indexer_topk rows+pools R={R} pool={pool} lens={spec.seq_lens}")
+    dl.indexer_topk_pooled(pg, pool, t["q_idx"], t["pool_keys"], top_pools, sel, ps, rows_per_seq=R)
+    torch.cuda.synchronize()
+    sel, ps = host(sel), host(ps)
+    orc = oracle.LayerOracle(spec, t)
+    for i in range(rows):
+        r = orc.row(i, stages=("sel",))
+        assert np.array_equal(sel[i], r["sel"]), f"row {i}: first diff at {np.nonzero(sel[i] != r['sel'])[0][:5]}"
+        n = int((r["pools"] >= 0).sum())
+        assert np.array_equal(ps[i][:n], r["scores"][r["pools"][:n]]) and np.all(ps[i][n:] == 0)
+
+
+@pytest.mark.parametrize("R,pool", [(2, 4), (4, 2)])
+def test_layer_step_rows_pooled(R, pool):
+    # the multi-token-prediction verification step reading the pool-key cache: every row against the oracle
+    spec = synth.spec_replace(synth.small_fp8_spec(name=f"step-rows{R}-pool{pool}", seq_lens=(3001, 2, 700), B=3),
+                              R=R, pool=pool)
+    t = _layer(spec, seed=90 + R * pool)
+    step = dl.LayerStep(spec, t, debug=True)
+    say(f"[gpu] layer_step rows+pools R={R} pool={pool} lens={spec.seq_lens}")
+    y = step()
+    torch.cuda.synchronize()
+    w = check_rows(spec, t, step.dbg, y, list(range(spec.B * R)))
+    say(f"rows+pools R={R} pool={pool}: {w}")
+
+
 # ------------------------------------------------------------- one GPU's expert-parallel share of the FFN
 @pytest.mark.parametrize("n", [2, 4, 8])
 def test_ffn_expert_parallel_shares_sum_to_whole(n):
