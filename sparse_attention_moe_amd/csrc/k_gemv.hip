@@ -761,15 +761,24 @@ __global__ __launch_bounds__(256) void k_resid_reduce_split(GemvArgs a, float *_
     const int kb = (int)(wave % nkb);
     const long e = row * D + kb * 128 + lane * 2;
     const int nslot = gemv_slots(a);
-    v2f pc[2 * MAX_KSPLIT];
-#pragma unroll
-    for (int c = 0; c < 2 * MAX_KSPLIT; c++)
-        pc[c] = c < nslot ? *(const v2f *)(a.part + (long)c * a.n_out + e) : v2f{0.f, 0.f};
+    // eight slots' loads at a time, unconditional (the slot index clamped; unused values dropped), issued before
+    // the residual's (whose type decides its load), so that they are in flight together: a load under a
+    // condition is waited for on its own
     v2f v = {0.f, 0.f};
+    float x0 = 0.f, x1 = 0.f;
+    for (int c0 = 0; c0 < nslot; c0 += 8) {
+        v2f pc[8];
 #pragma unroll
-    for (int c = 0; c < 2 * MAX_KSPLIT; c++)
-        if (c < nslot) v += pc[c];
-    float r0 = v.x + act_load(a.resid, a.resid_dt, e), r1 = v.y + act_load(a.resid, a.resid_dt, e + 1);
+        for (int c = 0; c < 8; c++) pc[c] = *(const v2f *)(a.part + (long)min(c0 + c, nslot - 1) * a.n_out + e);
+        if (c0 == 0) {
+            x0 = act_load(a.resid, a.resid_dt, e);
+            x1 = act_load(a.resid, a.resid_dt, e + 1);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+            if (c0 + c < nslot) v += pc[c];
+    }
+    float r0 = v.x + x0, r1 = v.y + x1;
     *(v2f *)(h + e) = v2f{r0, r1};
     if (!hq) return;
 #pragma unroll
