@@ -337,6 +337,7 @@ static int run_attn_proj(const dl_pages &pg, const void *q, int q_dt, const void
 static constexpr int GU_MAXK = 4;  // most K chunks of the FP8 gate/up pass (partial slots: twice that)
 // Work-queue pieces per unit of the FP8 expert GEMVs (partial slots): gate/up and down.
 static constexpr int GU_NPC = 2, DN_NPC = 1;
+static constexpr int FUSED_DN_NPC = 2;  // K pieces (output slots) of the down pieces in the fused FFN
 static_assert(GU_NPC <= 2 * GU_MAXK, "gate/up pieces exceed the partial slots");
 
 // Queue mode for a plan-mode FP8 GEMV of `pairs` (token, expert) pairs: npc pieces per unit (at most the bit
@@ -363,9 +364,15 @@ struct FfnWs {
     float *gpart, *upart;      // [2 GU_MAXK, P, I] gate/up partial slots (FP8 path)
     float *Z;                  // [P, I]
     uint8_t *zq; float *zqs;   // 2 parts of Z
-    float *F;                  // [DN_NPC, P, D] expert outputs (partial slots in the FP8 path)
+    float *F;                  // [max(DN_NPC, FUSED_DN_NPC), P, D] expert outputs (partial slots in the FP8 path)
     int *queue;                // [2 GEMV_QINTS] work-queue counters (gate/up, down)
+    int *sync;                 // hand-off counters of the fused FFN (FfnFused::sync; FP8 path)
 };
+
+// Gate/up, SwiGLU and down as one launch where the weights allow it (k_ffn_fp8); 0 keeps three launches.
+#ifndef DL_FFN_FUSE
+#define DL_FFN_FUSE 1
+#endif
 
 static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool fp8, FfnWs &f)
 {
@@ -394,7 +401,12 @@ static void ffn_ws_layout(Ws &w, int B, int D, int I, int ke, int E, int S, bool
         f.zq = w.take<uint8_t>((long)FFN_PARTS * P * I);
         f.zqs = w.take<float>((long)FFN_PARTS * P * (I / 128));
     }
-    f.F = w.take<float>((fp8 ? DN_NPC : 1) * P * D);
+    f.F = w.take<float>((fp8 ? std::max(DN_NPC, FUSED_DN_NPC) : 1) * P * D);
+    // token groups: at most one per active slot plus one per pair
+    f.plan.ffn_gmax = (int)(NE + P);
+    f.plan.ffn_nrb = I / 128;
+    f.sync = fp8 ? w.take<int>((long)f.plan.ffn_gmax * (I / 128 + 1)) : nullptr;
+    f.plan.ffn_sync = f.sync;
 }
 
 static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, const float *gates, int ke,
@@ -436,10 +448,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     } else {
         g.af = h;
     }
-    mk.at(5);
-    DL_TRY(launch_gemv(g, FFN_PARTS, EPI_SWIGLU, f8, s));
-    mk.at(6);
-    // down -> F
+    // down -> F (set up before the gate/up launch: the fused form takes both)
     GemvArgs d = mat_args(wd);
     d.active = f.plan.active;
     d.n_active_dev = f.plan.n_active;
@@ -451,22 +460,41 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     d.pair_act = nullptr;  // Z rows are per pair
     d.o_ts = D;
     d.out = f.F;
+    bool fused = false;
     if (f8) {
-        DL_TRY(launch_swiglu_quant(f.gpart, f.upart, gemv_slots(g), P * I, P, f.plan.n_pairs, I, f.zq, f.zqs, P * I,
-                                   P * (I / 128), FFN_PARTS, s));
         d.aq = f.zq; d.asc = f.zqs; d.aq_part = P * I; d.asc_part = P * (I / 128);
         if (gemv_queue(d, f.queue + GEMV_QINTS, DN_NPC, P)) {
             d.part = f.F;
             d.n_out = P * D;
             d.reduce_in_consumer = true;
         }
+        fused = DL_FFN_FUSE && f.sync && g.queue && d.queue && g.tiled && d.tiled && g.npc <= 2 && d.npc == 1 &&
+                I % 128 == 0 && D % 64 == 0;
     } else {
         d.af = f.Z;
     }
-    mk.at(7);
-    DL_TRY(launch_gemv(d, FFN_PARTS, EPI_STORE, f8, s));
+    mk.at(5);
+    if (fused) {
+        FfnFused ff;
+        ff.g = g;
+        ff.d = d;
+        ff.sync = f.sync;
+        ff.gmax = f.plan.ffn_gmax;
+        ff.d.npc = d.nkb >= 2 ? FUSED_DN_NPC : 1;
+        DL_TRY(launch_ffn_fused(ff, s));
+        mk.at(6);
+        mk.at(7);
+    } else {
+        DL_TRY(launch_gemv(g, FFN_PARTS, EPI_SWIGLU, f8, s));
+        mk.at(6);
+        if (f8)
+            DL_TRY(launch_swiglu_quant(f.gpart, f.upart, gemv_slots(g), P * I, P, f.plan.n_pairs, I, f.zq, f.zqs,
+                                       P * I, P * (I / 128), FFN_PARTS, s));
+        mk.at(7);
+        DL_TRY(launch_gemv(d, FFN_PARTS, EPI_STORE, f8, s));
+    }
     mk.at(8);
-    DL_TRY(launch_combine(f.F, d.queue ? d.npc : 1, P * D, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
+    DL_TRY(launch_combine(f.F, fused ? (d.nkb >= 2 ? FUSED_DN_NPC : 1) : d.queue ? d.npc : 1, P * D, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
                           out32, s));
     mk.at(9);
     return DL_OK;

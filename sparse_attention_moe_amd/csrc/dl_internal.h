@@ -138,6 +138,16 @@ __device__ inline int gemv_slot_pos(const int m[GEMV_QPOOLS], int p, int k)
     return pos;
 }
 int launch_gemv(const GemvArgs &a, int ns, int epi, bool fp8, hipStream_t s);
+// Gate/up, SwiGLU + FP8 split and down of the expert FFN in one launch (k_ffn_fp8): g the gate/up GEMV (queue and
+// plan mode, tiled, partial slots in part / part2), d the down GEMV (plan mode, tiled, npc <= 2 K pieces into as
+// many slots of part, activations aq / asc = the FP8 parts of Z).  sync: [gmax][I / 128] finished gate/up pieces per (token group,
+// 128-row block of Z), then [gmax] finished blocks per token group; zero on entry (the plan clears them).
+struct FfnFused {
+    GemvArgs g, d;
+    int *sync;
+    int gmax;
+};
+int launch_ffn_fused(const FfnFused &f, hipStream_t s);
 // Flat mode for an FP8 GEMV of about `units_est` units: the K split (<= max_ksplit chunks) with chunks no
 // longer than a wave's share of steps.
 void gemv_flat(GemvArgs &a, int ns, int epi, long units_est, int max_ksplit);
@@ -185,6 +195,8 @@ struct MoePlan {
     int *pair_tok;   // [B*(ke+S)]
     int *pair_idx;   // [B, ke+S]
     int *queue;      // [2 GEMV_QINTS] work-queue counters of the expert GEMVs, cleared with the plan (nullptr: none)
+    int *ffn_sync;   // hand-off counters of the fused FFN (FfnFused::sync), cleared with the plan (nullptr: none)
+    int ffn_gmax, ffn_nrb;
 };
 int route_chunks(int D);  // hidden-size chunks of the router's partial dot products
 // part [route_chunks(D), B, E] is scratch (fp64).

@@ -38,6 +38,52 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// Device-scope accesses (coherent across the eight XCDs' L2 caches: stores write through, loads do not hit a
+// line another XCD may have changed) for data handed between workgroups inside one launch.
+__device__ __forceinline__ float ld_dev(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ int ld_dev(const int *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_dev(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_dev(uint16_t *p, uint16_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// A ticket from a queue counter into tk (lane 0; the other lanes keep theirs): the counter's old value, waited for
+// only where it is read.  The address passes through a register the compiler cannot see into: with a uniform address
+// it rewrites the atomic into a wave-wide form and waits for its result at once, and that wait (in issue order)
+// also drains the weight loads issued just before it.
+__device__ __forceinline__ void q_take(int *qc, int lane, int &tk)
+{
+    __attribute__((address_space(1))) int *p = (__attribute__((address_space(1))) int *)qc;
+    asm volatile("" : "+v"(p));
+    if (lane == 0) tk = __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The NS FP8 parts of a wave's 128 values (two per lane, at element e of the row): part 0 is the value rounded to
+// e4m3 with an amax / 448 scale over the 128, part s the remainder of parts < s with its own scale.  Codes go to
+// q + s * q_part + e, scales to sc + s * sc_part + si; DEV: device-scope stores.
+template <int NS, bool DEV>
+__device__ __forceinline__ void split_store(float r0, float r1, uint8_t *q, float *sc, long q_part, long sc_part, long e,
+                                            long si, int lane)
+{
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
+        const float scale = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+        const float inv = 1.0f / scale;
+        const float c0 = fminf(fmaxf(r0 * inv, -448.f), 448.f);
+        const float c1 = fminf(fmaxf(r1 * inv, -448.f), 448.f);
+        const uint32_t code = f32x2_to_fp8(c0, c1);
+        uint16_t *qp = (uint16_t *)(q + s * q_part + e);
+        if (DEV) st_dev(qp, (uint16_t)code);
+        else *qp = (uint16_t)code;
+        if (lane == 0) {
+            if (DEV) st_dev(sc + s * sc_part + si, scale);
+            else sc[s * sc_part + si] = scale;
+        }
+        const v2f d = fp8x2_lo(code);
+        r0 -= d.x * scale;
+        r1 -= d.y * scale;
+    }
+}
+
 // Work: units (active matrix u, RT*16-row tile, group of 16 tokens), numbered with the token group fastest,
 // then the tile, then u; a unit's K range is nkb steps of one 128-wide block, cut into chunks of kchunk
 // blocks.  The steps of all units form one sequence.  Without `flat` each wave owns a contiguous share of whole
@@ -69,7 +115,6 @@ struct Stage {
 
 // Weight scales of the segment's K range (at most 128 blocks): lane j holds the scale of K-block kb0 + j in wsv
 // and of kb0 + 64 + j in wsvB; the compute loop reads them with readlane, so no scale is loaded per K-block.
-template <int RT>
 struct Ctx {
     int u, m, cnt, off, t0, r0, kc, kb0, kb1, piece, whole;
     bool valid, tv;
@@ -96,8 +141,8 @@ __device__ __forceinline__ v8i ldw16x2(const uint8_t *p, int gap)
 // Operand bytes of lane l = (ln, lg): row ln of the tile, K bytes {lg*16 .. +16} and {64 + lg*16 .. +16}
 // of the 128-wide block.  Row-major weights: two loads 64 B apart in the row; tiled weights: 16 B at
 // l*16 and 1024 + l*16 of the tile's 2 KB.  The activations use the same K assignment.
-template <bool SW, int RT, bool TL>
-__device__ __forceinline__ void load_stage(Stage<SW, RT> &st, const Ctx<RT> &c, long cols, int kb)
+template <bool SW, int RT, bool TL, bool COH = false>
+__device__ __forceinline__ void load_stage(Stage<SW, RT> &st, const Ctx &c, long cols, int kb)
 {
 #pragma unroll
     for (int r = 0; r < RT; r++) {
@@ -114,7 +159,7 @@ __device__ __forceinline__ void load_stage(Stage<SW, RT> &st, const Ctx<RT> &c, 
     // lanes of empty token slots read a valid row of the group (their column is scaled by 0); every lane
     // loads, so each step issues the same loads
     st.Bv = ld16x2(c.ap + kb * 128, 64);
-    st.as = c.asp[kb];
+    st.as = COH ? ld_dev(c.asp + kb) : c.asp[kb];
 }
 
 // Segment (steps [s, e) of one unit's chunk) -> context.  Units are (u, tile, g) with g fastest; in plan mode
@@ -122,7 +167,7 @@ __device__ __forceinline__ void load_stage(Stage<SW, RT> &st, const Ctx<RT> &c, 
 // `prev` (same matrix and token group) when possible: then no memory is read.
 template <int NS, int RT, bool SW, bool TL>
 __device__ __forceinline__ void make_ctx(const GemvArgs &a, long s, long e, int groups, int tiles, int n_act,
-                                         const int *goff, const Ctx<RT> *prev, Ctx<RT> &c)
+                                         const int *goff, const Ctx *prev, Ctx &c)
 {
     constexpr int TPG = 16 / NS;
     const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
@@ -300,7 +345,7 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     // the segment after the one ending at e: the rest of the wave's share, or the next piece from the queue
     auto next_seg = [&](long e_cur, long &ns, long &ne, int &nslot) -> bool {
         if (a.queue) {
-            const long t = qindex(__builtin_amdgcn_readlane(qtk, 0));
+            const long t = qindex(qbase + __builtin_amdgcn_readlane(qtk, 0));
             if (t >= qtot) return false;
             qpiece((int)t, ns, ne, nslot);
             return true;
@@ -311,7 +356,7 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
         return true;
     };
     const bool parts = a.flat || a.ksplit > 1 || a.queue;
-    Ctx<RT> c, n;
+    Ctx c, n;
     long e = a.queue ? s1 : seg_end(s0), ns = 0, ne = 0;
     int slot = qslot, nslot = 0;
     bool more = false;
@@ -324,7 +369,7 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     int kb = c.kb0;  // K-block of step s, in segment c
     long s = s0;
     load_stage<SW, RT, TL>(X, c, a.cols, kb);
-    if (a.queue && lane == 0) qtk = qbase + atomicAdd(qc, 1);
+    if (a.queue) q_take(qc, lane, qtk);
     // Step s: first the loads of step s + 1 into the other stage (from the next segment's context when s + 1
     // starts one; the last step re-reads its own tile, so every step issues the same loads), then the
     // arithmetic of step s, which waits only for the older stage.  The stages alternate by unrolling two
@@ -336,7 +381,7 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
                 make_ctx<NS, RT, SW, TL>(a, ns, ne, groups, tiles, n_act, goff, &c, n);
                 if (!a.queue) nslot = a.flat ? 2 * n.kc + n.piece : n.kc;
                 load_stage<SW, RT, TL>(Q, n, a.cols, n.kb0);
-                if (a.queue && lane == 0) qtk = qbase + atomicAdd(qc, 1);
+                if (a.queue) q_take(qc, lane, qtk);
             } else {
                 load_stage<SW, RT, TL>(Q, c, a.cols, kb);
             }
@@ -401,6 +446,364 @@ __global__ __launch_bounds__(256, (EPI == EPI_SWIGLU || NS == 4) ? 2 : 3) void k
     while (step(X, Y) && step(Y, X)) {
     }
     q_done();
+}
+
+// ------------------------------------------------------------------ fused expert FFN
+// Gate/up, the SwiGLU with its FP8 split, and down in one launch over one work queue per XCD pool, so the waves that
+// run out of gate/up pieces go on to down pieces instead of idling until the slowest one ends.  Pieces are
+// numbered gate/up first (units (slot, 32-row tile, token group), npc K pieces each, unit-major), then down
+// (units (slot, 64-row tile, token group), d.npc K pieces each into as many output slots, unit-major: the shorter
+// pieces shorten the launch's tail, where the last waves finish their last pieces); each pool's
+// tickets follow that order, so a pool hands out down pieces only after all of its gate/up pieces.  The hand-offs
+// between phases go through device-scope stores and counters instead of a kernel boundary:
+// - a gate/up piece stores its partial sums device-scope and then counts itself in done[group][block] (group: token
+//   group of a slot, block: 128 rows of the intermediate).  The count is taken one step into the wave's next piece,
+//   right after that step's loads are issued: the wait for all but those loads, which the step's arithmetic needs
+//   anyway, has then covered the stores, so the weight stream does not drain for it;
+// - the piece that completes a block forms Z = silu(G) * U for the group's tokens over those 128 rows, split into
+//   FP8 parts as k_swiglu_quant does (same sums in slot order, same rounding), stores it device-scope and counts
+//   the block in ready[group];
+// - a down piece begins once ready[group] holds every block of its group.  Its count is read in the first step of
+//   the wave's previous piece, so only the hand-over from gate/up to down ever spins.
+// A wave waits only for pieces that running waves have taken: a taken gate/up piece runs to its end without
+// waiting, every gate/up ticket of a pool precedes its down tickets, and the grid is what the device holds at
+// once.  A wait that still passes its bound (about a third of a second) stops and fills the piece's outputs with
+// NaN, so the launch always ends and such a failure cannot go unnoticed.
+static constexpr int FFN_SPIN = 1 << 18;
+
+template <bool TL>
+__global__ __launch_bounds__(256, 2) void k_ffn_fp8(FfnFused f)
+{
+    constexpr int NS = 2, RT = 2, TPG = 16 / NS;
+    constexpr int NLD = 4 * RT + 2 + 1;  // vector memory instructions of one load_stage<true, RT>
+    __shared__ int s_goff[GEMV_MAXMAT + 1];
+    const GemvArgs &g = f.g, &d = f.d;
+    const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+    const int n_act = *g.n_active_dev;
+    for (int i = threadIdx.x; i <= n_act; i += 256) s_goff[i] = g.grp_off[i];
+    __syncthreads();
+    const int ngrp = s_goff[n_act];
+    const int tiles_g = g.rows / (16 * RT), tiles_d = d.rows / (32 * RT);
+    const long units_g = (long)tiles_g * ngrp, units_d = (long)tiles_d * ngrp;
+    const long qgu = units_g * g.npc, qtot = qgu + units_d * d.npc;
+    const int nrb = g.rows / 128, ppb = 128 / (16 * RT) * g.npc;  // blocks of Z per group; gate/up pieces per block
+    int *const done = f.sync, *const ready = f.sync + (long)f.gmax * nrb;
+    // the queue, as in k_gemv_fp8
+    const int npool = min((int)gridDim.x, GEMV_QPOOLS);
+    const int pool = blockIdx.x % npool;
+    int *qc = g.queue + pool * GEMV_QSTRIDE;
+    const int qbase = 4 * (((int)gridDim.x - pool + npool - 1) / npool);
+    int qm[GEMV_QPOOLS];
+    gemv_shares_read(g.queue, qm);
+    if (blockIdx.x < npool && threadIdx.x == 0)
+        *(unsigned long long *)(qc + 2) = __builtin_amdgcn_s_memrealtime();
+    // a wave leaves the gate/up phase: the pool's last one records the time (the pools' shares follow their
+    // gate/up rates; the down pieces fill in behind)
+    auto q_done = [&]() {
+        if (lane == 0 && atomicAdd(qc + 1, 1) == qbase - 1)
+            *(unsigned long long *)(qc + 4) = __builtin_amdgcn_s_memrealtime();
+    };
+    auto qindex = [&](int t) -> long {
+        if (npool < GEMV_QPOOLS) return (long)t * npool + pool;
+        const int n = qm[pool];
+        return (long)(t / n) * GEMV_QROUND + gemv_slot_pos(qm, pool, t % n);
+    };
+    // slot of token group G: the last slot u with goff[u] <= G
+    auto group_slot = [&](int G) {
+        int lo = 0, hi = n_act - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_goff[mid] <= G) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    };
+    // token group of down unit x (units numbered group fastest, then tile, then slot)
+    auto dn_group = [&](long x) {
+        int lo = 0, hi = n_act - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((long)tiles_d * s_goff[mid] <= x) lo = mid; else hi = mid - 1;
+        }
+        const int gc = s_goff[lo + 1] - s_goff[lo];
+        return s_goff[lo] + (int)((x - (long)tiles_d * s_goff[lo]) % gc);
+    };
+    // gate/up piece t -> steps [ps, pe) and partial slot: the K pieces of k_gemv_fp8, numbered unit-major here
+    // (a unit's pieces side by side), so the slots' blocks complete in slot order from early on and the down
+    // pieces, which follow the same slot order, find them ready
+    auto gu_piece = [&](long t, long &ps, long &pe, int &sl) {
+        const long unit = t / g.npc;
+        const int j = (int)(t - unit * g.npc);
+        const long u0 = unit * g.nkb;
+        ps = u0 + g.nkb - (g.nkb >> j);
+        pe = u0 + (j + 1 >= g.npc ? g.nkb : g.nkb - (g.nkb >> (j + 1)));
+        sl = j;
+    };
+    // down piece x (after the gate/up ones) -> steps [ps, pe) and output slot: K pieces as for gate/up, unit-major
+    auto dn_piece = [&](long x, long &ps, long &pe, int &sl) {
+        const long unit = x / d.npc;
+        const int j = (int)(x - unit * d.npc);
+        const long u0 = unit * d.nkb;
+        ps = u0 + d.nkb - (d.nkb >> j);
+        pe = u0 + (j + 1 >= d.npc ? d.nkb : d.nkb - (d.nkb >> (j + 1)));
+        sl = j;
+    };
+    // a down context covers 64 rows: tiles 0-1 in A, 2-3 in A2 (same 128-row scale block)
+    auto fix_dn = [&](Ctx &x) {
+        x.wp2 = x.wp + (TL ? 2L * d.nkb * 2048 : 32L * d.cols);
+        x.wsp2 = x.wsp;
+        x.wsv2 = x.wsv;
+        x.wsvB2 = x.wsvB;
+    };
+    // block idx = G * nrb + rb of Z: SwiGLU of the group's tokens over rows [128 rb, +128), split into FP8 parts
+    auto swiglu_block = [&](int idx) {
+        const int G = idx / nrb, rb = idx - G * nrb;
+        const int u = group_slot(G);
+        const int t0 = (G - s_goff[u]) * TPG, off = g.tok_off[u] + t0;
+        const int nt = min(TPG, g.tok_cnt[u] - t0), nsl = g.npc;
+        const long base = (long)rb * 128 + lane * 2;
+        // TB tokens at a time: all their loads in flight together, within the registers the piece loop leaves
+        constexpr int TB = 2;
+#pragma unroll 1
+        for (int t0b = 0; t0b < nt; t0b += TB) {
+            v2f gc[TB][2], uc[TB][2];
+#pragma unroll
+            for (int t = 0; t < TB; t++)
+#pragma unroll
+                for (int c = 0; c < 2; c++) {
+                    const long o = (long)min(c, nsl - 1) * g.n_out + (long)(off + min(t0b + t, nt - 1)) * g.o_ts + base;
+                    gc[t][c] = v2f{ld_dev(g.part + o), ld_dev(g.part + o + 1)};
+                    uc[t][c] = v2f{ld_dev(g.part2 + o), ld_dev(g.part2 + o + 1)};
+                }
+#pragma unroll
+            for (int t = 0; t < TB; t++) {
+                if (t0b + t >= nt) break;
+                v2f gs = {0.f, 0.f}, us = {0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 2; c++)
+                    if (c < nsl) { gs += gc[t][c]; us += uc[t][c]; }
+                const long row = off + t0b + t;
+                split_store<NS, true>(silu(gs.x) * us.x, silu(gs.y) * us.y, const_cast<uint8_t *>(d.aq),
+                                      const_cast<float *>(d.asc), d.aq_part, d.asc_part, row * g.rows + base,
+                                      row * nrb + rb, lane);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the parts are stored before the block is counted
+        if (lane == 0) atomicAdd(ready + G, 1);
+    };
+    bool poison = false;
+    // until ready[G] holds every block (v: its value as last read)
+    auto wait_ready = [&](int G, int v) {
+        for (int it = 0; v < nrb && it < FFN_SPIN; it++) {
+            __builtin_amdgcn_s_sleep(8);
+            v = __builtin_amdgcn_readfirstlane(ld_dev(ready + G));
+        }
+        if (v < nrb) poison = true;
+    };
+
+    long t = qindex((blockIdx.x / npool) * 4 + (threadIdx.x >> 6));  // the wave's first piece, fixed by its index
+    if (t >= qtot) {
+        q_done();
+        return;
+    }
+    Ctx c, n;
+    Stage<true, RT> X, Y;
+    v4f tot[RT], tot2[RT];
+#pragma unroll
+    for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
+    long s = 0, e = 0, ns = 0, ne = 0;
+    int kb = 0, slot = 0, nslot = 0, qtk = 0;
+    int gn = -1, rdy = 0;  // down: group of the wave's next piece and its ready count (read early; lane values)
+    bool more = false;
+
+    // ---- gate/up pieces
+    if (t < qgu) {
+        int pend = -1;              // block of the last piece, stored but not yet counted
+        int cnt_idx = -1, cnt_old = 0;  // block counted one piece ago, and the count it found (lane 0)
+        auto count_back = [&]() {  // the count taken one piece ago: did that piece complete its block?
+            if (cnt_idx >= 0 && __builtin_amdgcn_readlane(cnt_old, 0) == ppb - 1) swiglu_block(cnt_idx);
+            cnt_idx = -1;
+        };
+        gu_piece(t, s, e, slot);
+        make_ctx<NS, RT, true, TL>(g, s, e, 0, tiles_g, n_act, s_goff, nullptr, c);
+        kb = c.kb0;
+        load_stage<true, RT, TL>(X, c, g.cols, kb);
+        q_take(qc, lane, qtk);
+        auto step = [&](Stage<true, RT> &P, Stage<true, RT> &Q) __attribute__((always_inline)) -> bool {
+            if (s + 1 == e) {
+                // first (before the next piece's loads hold registers) a count not yet read (a short piece)
+                count_back();
+                t = qindex(qbase + __builtin_amdgcn_readlane(qtk, 0));
+                more = t < qgu;
+                if (more) {
+                    gu_piece(t, ns, ne, nslot);
+                    make_ctx<NS, RT, true, TL>(g, ns, ne, 0, tiles_g, n_act, s_goff, &c, n);
+                    load_stage<true, RT, TL>(Q, n, g.cols, n.kb0);
+                    q_take(qc, lane, qtk);
+                } else {
+                    load_stage<true, RT, TL>(Q, c, g.cols, kb);
+                }
+            } else {
+                load_stage<true, RT, TL>(Q, c, g.cols, kb + 1);
+            }
+            if (pend >= 0) {
+                // only this step's loads may still be outstanding: the previous piece's stores are complete
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
+                if (lane == 0) cnt_old = atomicAdd(done + pend, 1);
+                cnt_idx = pend;
+                pend = -1;
+            }
+            const int kr = kb - c.kb0;
+            const float tmask = c.tv ? 1.f : 0.f;
+            const float ws = lane_f(kr < 64 ? c.wsv : c.wsvB, kr & 63) * tmask;
+            const float ws2 = lane_f(kr < 64 ? c.wsv2 : c.wsvB2, kr & 63) * tmask;
+            const float f1 = ws * P.as, f2 = ws2 * P.as;
+#pragma unroll
+            for (int r = 0; r < RT; r++) {
+                tot[r] += mfma_fp8(P.A[r], P.Bv) * f1;
+                tot2[r] += mfma_fp8(P.A2[r], P.Bv) * f2;
+            }
+            if (s + 1 != e && kb == c.kb0 + 2) count_back();  // the count has returned by now
+            if (s + 1 == e) {
+#pragma unroll
+                for (int r = 0; r < RT; r++) {
+                    tot[r] = sum_parts<NS>(tot[r]);
+                    tot2[r] = sum_parts<NS>(tot2[r]);
+                }
+                if (c.tv && ln < TPG) {
+                    const long ooff = (long)(c.off + c.tt) * g.o_ts + (long)slot * g.n_out;
+#pragma unroll
+                    for (int r = 0; r < RT; r++) {
+                        const long o = ooff + c.r0 + r * 16 + 4 * lg;
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            st_dev(g.part + o + i, tot[r][i]);
+                            st_dev(g.part2 + o + i, tot2[r][i]);
+                        }
+                    }
+                }
+                pend = (s_goff[c.u] + c.t0 / TPG) * nrb + c.r0 / 128;
+#pragma unroll
+                for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
+                if (!more) return false;
+                c = n;
+                s = ns;
+                e = ne;
+                slot = nslot;
+                kb = c.kb0;
+                return true;
+            }
+            kb++;
+            ++s;
+            return true;
+        };
+        while (step(X, Y) && step(Y, X)) {
+        }
+        // the wave's last gate/up piece: counted once its stores are complete (after any count still unread)
+        count_back();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0) cnt_old = atomicAdd(done + pend, 1);
+        cnt_idx = pend;
+        count_back();
+    }
+    q_done();
+
+    // ---- down pieces
+    if (t >= qgu && t < qtot) {
+        {
+            const int G = dn_group((t - qgu) / d.npc);
+            wait_ready(G, __builtin_amdgcn_readfirstlane(ld_dev(ready + G)));
+        }
+        dn_piece(t - qgu, s, e, slot);
+        make_ctx<NS, 2 * RT, false, TL>(d, s, e, 0, tiles_d, n_act, s_goff, nullptr, c);
+        fix_dn(c);
+        kb = c.kb0;
+        load_stage<true, RT, TL, true>(X, c, d.cols, kb);
+        q_take(qc, lane, qtk);
+        auto step = [&](Stage<true, RT> &P, Stage<true, RT> &Q) __attribute__((always_inline)) -> bool {
+            if (s + 1 == e) {
+                const long tn = qindex(qbase + __builtin_amdgcn_readlane(qtk, 0));
+                more = tn < qtot;
+                if (more) {
+                    if (c.kb1 - c.kb0 < 2) {  // a one-step piece: no step read the count early
+                        gn = dn_group((tn - qgu) / d.npc);
+                        rdy = ld_dev(ready + gn);
+                    }
+                    wait_ready(gn, __builtin_amdgcn_readfirstlane(rdy));
+                    dn_piece(tn - qgu, ns, ne, nslot);
+                    make_ctx<NS, 2 * RT, false, TL>(d, ns, ne, 0, tiles_d, n_act, s_goff, &c, n);
+                    fix_dn(n);
+                    load_stage<true, RT, TL, true>(Q, n, d.cols, n.kb0);
+                    q_take(qc, lane, qtk);
+                } else {
+                    load_stage<true, RT, TL, true>(Q, c, d.cols, kb);
+                }
+            } else {
+                load_stage<true, RT, TL, true>(Q, c, d.cols, kb + 1);
+                if (kb == c.kb0) {
+                    // the next ticket has returned by now: read its group's count, used at the piece's end
+                    const long tn = qindex(qbase + __builtin_amdgcn_readlane(qtk, 0));
+                    gn = dn_group((min(tn, qtot - 1) - qgu) / d.npc);
+                    rdy = ld_dev(ready + gn);
+                }
+            }
+            const int kr = kb - c.kb0;
+            const float tmask = c.tv ? 1.f : 0.f;
+            const float ws = lane_f(kr < 64 ? c.wsv : c.wsvB, kr & 63) * tmask;
+            const float ws2 = lane_f(kr < 64 ? c.wsv2 : c.wsvB2, kr & 63) * tmask;
+            const float f1 = ws * P.as, f2 = ws2 * P.as;
+#pragma unroll
+            for (int r = 0; r < RT; r++) {
+                tot[r] += mfma_fp8(P.A[r], P.Bv) * f1;
+                tot2[r] += mfma_fp8(P.A2[r], P.Bv) * f2;
+            }
+            if (s + 1 == e) {
+#pragma unroll
+                for (int r = 0; r < RT; r++) {
+                    tot[r] = sum_parts<NS>(tot[r]);
+                    tot2[r] = sum_parts<NS>(tot2[r]);
+                }
+                if (c.tv && ln < TPG) {
+                    const float bad = poison ? __builtin_nanf("") : 0.f;
+                    const long ooff = (long)(c.off + c.tt) * d.o_ts + (long)slot * d.n_out;
+#pragma unroll
+                    for (int r = 0; r < RT; r++) {
+                        const long o = ooff + c.r0 + r * 16 + 4 * lg;
+                        *(v4f *)(d.part + o) = tot[r] + bad;
+                        *(v4f *)(d.part + o + 32) = tot2[r] + bad;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < RT; r++) tot[r] = tot2[r] = v4f{0.f, 0.f, 0.f, 0.f};
+                if (!more) return false;
+                c = n;
+                s = ns;
+                e = ne;
+                slot = nslot;
+                kb = c.kb0;
+                return true;
+            }
+            kb++;
+            ++s;
+            return true;
+        };
+        while (step(X, Y) && step(Y, X)) {
+        }
+    }
+}
+
+int launch_ffn_fused(const FfnFused &f, hipStream_t s)
+{
+    const GemvArgs &g = f.g, &d = f.d;
+    if (!g.queue || !g.grp_off || !g.n_active_dev || !d.grp_off || !g.tiled || !d.tiled || g.npc < 1 || g.npc > 2 ||
+        d.npc < 1 || d.npc > 2 || (d.nkb >> (d.npc - 1)) < 1 || g.rows % 128 || d.rows % 64 || g.cols != d.rows || d.cols != g.rows || !g.part || !g.part2 ||
+        !d.part || !f.sync || f.gmax < 1)
+        return fail(DL_ERR_UNSUPPORTED, "fused FFN: unsupported arguments");
+    const void *k = (const void *)k_ffn_fp8<true>;
+    FfnFused arg = f;
+    void *args[] = {(void *)&arg};
+    if (hipLaunchKernel(k, dim3(resident_blocks(k, 256)), dim3(256), args, 0, s) != hipSuccess)
+        return hip_check("ffn_fp8");
+    return hip_check("ffn_fp8");
 }
 
 // One-shot projection GEMV (one FP8 matrix, either layout, tokens 0..ntok-1): a workgroup owns PROJ_RT * 16
@@ -575,21 +978,7 @@ __global__ __launch_bounds__(256) void k_quant(const float *__restrict__ x, long
         const int kb = (int)(it % nkb);
         const long e = row * cols + kb * 128 + lane * 2;
         const v2f v = *(const v2f *)(x + e);
-        float r0 = v.x, r1 = v.y;
-#pragma unroll
-        for (int s = 0; s < NS; s++) {
-            const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
-            const float scale = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
-            const float inv = 1.0f / scale;
-            const float c0 = fminf(fmaxf(r0 * inv, -448.f), 448.f);
-            const float c1 = fminf(fmaxf(r1 * inv, -448.f), 448.f);
-            const uint32_t code = f32x2_to_fp8(c0, c1);
-            *(uint16_t *)(q + s * q_part + e) = (uint16_t)code;
-            if (lane == 0) sc[s * sc_part + row * nkb + kb] = scale;
-            const v2f d = fp8x2_lo(code);
-            r0 -= d.x * scale;
-            r1 -= d.y * scale;
-        }
+        split_store<NS, false>(v.x, v.y, q, sc, q_part, sc_part, e, row * nkb + kb, lane);
     }
 }
 
@@ -620,21 +1009,7 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const float *__restrict__ 
 #pragma unroll
         for (int c = 0; c < 8; c++)
             if (c < nslot) { g += gc[c]; u += uc[c]; }
-        float r0 = silu(g.x) * u.x, r1 = silu(g.y) * u.y;
-#pragma unroll
-        for (int s = 0; s < NS; s++) {
-            const float amax = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
-            const float scale = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
-            const float inv = 1.0f / scale;
-            const float c0 = fminf(fmaxf(r0 * inv, -448.f), 448.f);
-            const float c1 = fminf(fmaxf(r1 * inv, -448.f), 448.f);
-            const uint32_t code = f32x2_to_fp8(c0, c1);
-            *(uint16_t *)(q + s * q_part + e) = (uint16_t)code;
-            if (lane == 0) sc[s * sc_part + row * nkb + kb] = scale;
-            const v2f d = fp8x2_lo(code);
-            r0 -= d.x * scale;
-            r1 -= d.y * scale;
-        }
+        split_store<NS, false>(silu(g.x) * u.x, silu(g.y) * u.y, q, sc, q_part, sc_part, e, row * nkb + kb, lane);
     }
 }
 

@@ -252,6 +252,7 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
     const int kk = ke + S;
     const int np = B * ke;
     const bool use_mask = distinct && B <= 64;
+    __shared__ int s_ngrp;  // token groups of the plan
     for (int e = tid; e < E; e += nT) { s_cnt[e] = 0; s_mask[e] = 0ull; }
     __syncthreads();
     for (int i = tid; i < np; i += nT) {
@@ -315,10 +316,18 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
             *p.n_active = na_tot + S;
             *p.n_pairs = npr + S * B;
             s_cnt[E] = npr;  // for the shared pairs below (s_cnt holds E + 1 entries)
+            s_ngrp = ng_tot + S * gs;
         }
     }
     __syncthreads();
     const int npr = s_cnt[E];
+    if (p.ffn_sync) {
+        // the fused FFN's counters of the plan's token groups
+        const int ng = min(s_ngrp, p.ffn_gmax);
+        int *ready = p.ffn_sync + (long)p.ffn_gmax * p.ffn_nrb;
+        for (int i = tid; i < ng * p.ffn_nrb; i += nT) p.ffn_sync[i] = 0;
+        for (int i = tid; i < ng; i += nT) ready[i] = 0;
+    }
     for (int i = tid; i < np; i += nT) {
         const int b = i / ke, j = i - b * ke, e = s_exp[i];
         if (e < 0) {
