@@ -19,12 +19,17 @@ extern "C" {
  *   0 indexer + top-k   1 attention   2 W_UV + W_O (+ activation split)   3 router
  *   4 dispatch plan + split of h   5 expert gate/up (one kernel)   6 split of Z
  *   7 expert down (one kernel)   8 combine
+ * When the expert FFN runs as one kernel (dl_profile_ffn_fused), phase 5 holds all of it (gate/up, split
+ * of Z and down) and phases 6 and 7 hold no work.
  * dl_profile_read waits for the recorded steps, adds each phase's elapsed milliseconds into
  * ms_sum[DL_N_PHASES], stores the number of steps in *steps and forgets them.  Measurement only:
  * single host thread, events are created on first use and kept until dl_profile_enable(0). */
 #define DL_N_PHASES 9
 int dl_profile_enable(int on);
 int dl_profile_read(double *ms_sum, int64_t *steps);
+/* How the most recent expert FFN (of any entry point, in this process) ran: 1 as one kernel (gate/up, the split
+ * of Z and down in a single launch: FP8 weights in DL_LAYOUT_TILES), 0 as three kernels, -1 before the first. */
+int dl_profile_ffn_fused(void);
 
 /* Measurement aid, not part of the step: enqueue one streaming read of the first *bytes_read bytes of
  * the device buffer buf (16-byte non-temporal loads, each wave of a full-device grid reading its own

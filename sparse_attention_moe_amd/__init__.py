@@ -27,7 +27,7 @@ EXPORTS = ["dl_abi_version", "dl_hip_version", "dl_last_error", "dl_pack_weights
            "dl_indexer_topk_rows_pooled", "dl_layer_workspace_rows_pooled", "dl_layer_step_rows_pooled",
            "dl_sparse_attn_workspace", "dl_sparse_attn_decode", "dl_moe_route_workspace", "dl_moe_route", "dl_moe_route_noalloc",
            "dl_moe_ffn_workspace", "dl_moe_ffn", "dl_moe_ffn_ep", "dl_layer_workspace", "dl_layer_step", "dl_profile_enable",
-           "dl_profile_read", "dl_probe_read", "dl_probe_null", "dl_tile_index_keys"]
+           "dl_profile_read", "dl_profile_ffn_fused", "dl_probe_read", "dl_probe_null", "dl_tile_index_keys"]
 N_PHASES = 9
 PHASES = ["indexer_topk", "attention", "projection", "router", "plan_split_h", "expert_gate_up", "split_z",
           "expert_down", "combine"]
@@ -125,6 +125,8 @@ def load(require_gpu: bool = True):
         L.dl_layer_step.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerIO), P, sz, P]
         L.dl_profile_enable.argtypes = [C.c_int]
         L.dl_profile_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+        L.dl_profile_ffn_fused.argtypes = []
+        L.dl_profile_ffn_fused.restype = C.c_int
         L.dl_probe_read.argtypes = [P, sz, C.POINTER(sz), P]
         L.dl_probe_null.argtypes = [i32, i32, P]
         L.dl_tile_index_keys.argtypes = [P, P, C.c_int64, i32, P]
@@ -319,6 +321,11 @@ def moe_ffn_ep(h, experts, gates, expert_lo: int, w_gate: Mat, w_up: Mat, w_down
                            C.byref(w_up), C.byref(w_down), n_local, n_shared, _ptr(residual), _ptr(out), _dt(out),
                            _ptr(ws), ws.numel(), _stream(stream)))
     return out
+
+
+def profile_ffn_fused() -> int:
+    """1 if the most recent expert FFN ran as one kernel, 0 if as three, -1 before the first (measurement aid)."""
+    return int(load().dl_profile_ffn_fused())
 
 
 def probe_read(buf: torch.Tensor, stream=None) -> int:

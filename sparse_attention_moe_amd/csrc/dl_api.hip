@@ -65,6 +65,7 @@ struct StepMarks {
     hipEvent_t ev[DL_N_PHASES + 1];
 };
 static bool g_prof = false;
+static int g_ffn_fused = -1;  // the last expert FFN ran fused (1), as three kernels (0), none yet (-1)
 static StepMarks *g_pend = nullptr;  // recorded, not yet read
 static int g_npend = 0, g_cap = 0;
 static StepMarks *g_free = nullptr;
@@ -338,6 +339,13 @@ static constexpr int GU_MAXK = 4;  // most K chunks of the FP8 gate/up pass (par
 // Work-queue pieces per unit of the FP8 expert GEMVs (partial slots): gate/up and down.
 static constexpr int GU_NPC = 2, DN_NPC = 1;
 static constexpr int FUSED_DN_NPC = 2;  // K pieces (output slots) of the down pieces in the fused FFN
+// at most the bit length of nkb, so no piece is empty
+static int fused_dn_npc(int nkb)
+{
+    int maxp = 0;
+    while ((nkb >> maxp) > 0) maxp++;
+    return std::min(FUSED_DN_NPC, maxp);
+}
 static_assert(GU_NPC <= 2 * GU_MAXK, "gate/up pieces exceed the partial slots");
 
 // Queue mode for a plan-mode FP8 GEMV of `pairs` (token, expert) pairs: npc pieces per unit (at most the bit
@@ -473,6 +481,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
     } else {
         d.af = f.Z;
     }
+    g_ffn_fused = fused;
     mk.at(5);
     if (fused) {
         FfnFused ff;
@@ -480,7 +489,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
         ff.d = d;
         ff.sync = f.sync;
         ff.gmax = f.plan.ffn_gmax;
-        ff.d.npc = d.nkb >= 2 ? FUSED_DN_NPC : 1;
+        ff.d.npc = fused_dn_npc(d.nkb);
         DL_TRY(launch_ffn_fused(ff, s));
         mk.at(6);
         mk.at(7);
@@ -494,7 +503,7 @@ static int run_ffn(const float *h, int B, int D, int I, const int32_t *experts, 
         DL_TRY(launch_gemv(d, FFN_PARTS, EPI_STORE, f8, s));
     }
     mk.at(8);
-    DL_TRY(launch_combine(f.F, fused ? (d.nkb >= 2 ? FUSED_DN_NPC : 1) : d.queue ? d.npc : 1, P * D, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
+    DL_TRY(launch_combine(f.F, fused ? fused_dn_npc(d.nkb) : d.queue ? d.npc : 1, P * D, f.plan, gates, B, D, ke, S, resid, resid_dt, out, out_dt,
                           out32, s));
     mk.at(9);
     return DL_OK;
@@ -1067,6 +1076,8 @@ int dl_profile_enable(int on)
     }
     return DL_OK;
 }
+
+int dl_profile_ffn_fused(void) { return g_ffn_fused; }
 
 int dl_profile_read(double *ms_sum, int64_t *steps)
 {

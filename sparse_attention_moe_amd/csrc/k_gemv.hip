@@ -497,8 +497,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn_fp8(FfnFused f)
     gemv_shares_read(g.queue, qm);
     if (blockIdx.x < npool && threadIdx.x == 0)
         *(unsigned long long *)(qc + 2) = __builtin_amdgcn_s_memrealtime();
-    // a wave leaves the gate/up phase: the pool's last one records the time (the pools' shares follow their
-    // gate/up rates; the down pieces fill in behind)
+    // a wave is done: the pool's last one records the time (the pools' shares follow their rates over the launch)
     auto q_done = [&]() {
         if (lane == 0 && atomicAdd(qc + 1, 1) == qbase - 1)
             *(unsigned long long *)(qc + 4) = __builtin_amdgcn_s_memrealtime();
@@ -705,7 +704,6 @@ __global__ __launch_bounds__(256, 2) void k_ffn_fp8(FfnFused f)
         cnt_idx = pend;
         count_back();
     }
-    q_done();
 
     // ---- down pieces
     if (t >= qgu && t < qtot) {
@@ -789,6 +787,7 @@ __global__ __launch_bounds__(256, 2) void k_ffn_fp8(FfnFused f)
         while (step(X, Y) && step(Y, X)) {
         }
     }
+    q_done();
 }
 
 int launch_ffn_fused(const FfnFused &f, hipStream_t s)

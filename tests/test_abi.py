@@ -41,7 +41,7 @@ def test_method_header_declares_no_measurement_aid():
     step = _declared(["dl.h"])
     assert not [n for n in step if n.startswith(("dl_probe", "dl_profile"))]
     assert set(_declared(["dl_measure.h"])) == {"dl_probe_read", "dl_probe_null", "dl_profile_enable",
-                                                 "dl_profile_read"}
+                                                 "dl_profile_read", "dl_profile_ffn_fused"}
 
 
 def test_version_guards(lib):
