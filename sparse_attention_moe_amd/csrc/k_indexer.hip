@@ -195,29 +195,40 @@ __global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(co
     const int32_t *pt = page_table + (long)sq * max_pages;
     const int ps_mask = (1 << ps_shift) - 1;
     // cache rows of every position this lane loads (step st, group sg: position g0(st) + sg*16 + ln), all
-    // page-table reads in flight at once
+    // page-table reads in flight at once.  Every read, here and of the keys below, is unconditional (a read under
+    // a condition is waited for on its own): positions past the end take the last position's row, and their
+    // scores are never stored
     long row[4][4];
+    int pe[4][4];
 #pragma unroll
     for (int st = 0; st < 4; st++)
 #pragma unroll
         for (int sg = 0; sg < 4; sg++) {
             const long pos = blk0 + (long)(st * SCORE_WPB + wave) * 64 + sg * 16 + ln;
-            row[st][sg] = pos < L ? ((long)pt[pos >> ps_shift] << ps_shift) + (pos & ps_mask) : -1;
+            pe[st][sg] = pt[min(pos, (long)L - 1) >> ps_shift];
+        }
+#pragma unroll
+    for (int st = 0; st < 4; st++)
+#pragma unroll
+        for (int sg = 0; sg < 4; sg++) {
+            const long pos = min(blk0 + (long)(st * SCORE_WPB + wave) * 64 + sg * 16 + ln, (long)L - 1);
+            row[st][sg] = ((long)pe[st][sg] << ps_shift) + (pos & ps_mask);
         }
     __syncthreads();
-    // keys of step st: 4 groups of 16 positions x KCH chunks of 64 bytes; two steps in flight
+    // keys of step st: 4 groups of 16 positions x KCH chunks of 64 bytes; two steps in flight.  Key bytes past DI
+    // (a last chunk narrower than 64) are read from inside the item (row-major) or its group (tiled) instead and
+    // meet zero query columns, so they add nothing
     auto load_keys = [&](int st, v4i (&Bk)[4][KCH]) {
 #pragma unroll
         for (int sg = 0; sg < 4; sg++)
 #pragma unroll
             for (int kc = 0; kc < KCH; kc++) {
-                const int d = kc * 64 + lg * 16;
+                const int d = min(kc * 64 + lg * 16, DI - 16);
                 // streaming loads: every key byte is read once per step.  Tiled keys: the 64 lanes read the
                 // item group's 1 KB chunk kc contiguously (lane = lg * 16 + ln, item ln of the group)
-                const long off = tiles ? (row[st][sg] & ~15L) * DI + kc * 1024 + lane * 16 : row[st][sg] * DI + d;
-                Bk[sg][kc] = (row[st][sg] >= 0 && d < DI)
-                                 ? __builtin_nontemporal_load((const v4i *)(k_pool + off))
-                                 : v4i{0, 0, 0, 0};
+                const long off = tiles ? (row[st][sg] & ~15L) * DI + min(kc * 1024 + lane * 16, 16 * DI - 16)
+                                       : row[st][sg] * DI + d;
+                Bk[sg][kc] = __builtin_nontemporal_load((const v4i *)(k_pool + off));
             }
     };
     v4i K0[4][KCH], K1[4][KCH];
@@ -419,15 +430,20 @@ __global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ s
     const unsigned *br = bits + (long)b * Lw;
     const int2 *cr = cand + (long)b * nchunk * SEL_CHUNK;
     const Thr t = thr[b];
-    // this thread's bitmap word (loaded first, so that its latency overlaps the select)
+    // this thread's bitmap word and the first round of the two count loops below, loaded first and together
+    // (unconditional, with clamped indices: a load under a condition is waited for on its own)
     const int nw = (L + 31) >> 5;
     const int wi = ca * (SEL_CHUNK / 32) + tid;
-    unsigned word = wi < nw && tid < (cb - ca) * (SEL_CHUNK / 32) ? br[wi] : 0u;
+    const unsigned wv = br[min(wi, nw - 1)];
+    const int a0 = acnt[(long)b * nchunk + min(tid, max(ca - 1, 0))];
+    const int n0 = ccnt[(long)b * nchunk + min(tid, nch - 1)];
+    unsigned word = wi < nw && tid < (cb - ca) * (SEL_CHUNK / 32) ? wv : 0u;
     // marked items of the chunks before this workgroup's
     int abefore = 0;
     for (int c0 = 0; c0 < ca; c0 += 256) {
         const int ch = c0 + tid;
-        abefore += wave_sum_i(ch < ca ? acnt[(long)b * nchunk + ch] : 0);
+        const int v = c0 == 0 ? a0 : acnt[(long)b * nchunk + min(ch, ca - 1)];
+        abefore += wave_sum_i(ch < ca ? v : 0);
     }
     if (lane == 0) s_w[wave] = abefore;
     __syncthreads();
@@ -438,7 +454,8 @@ __global__ __launch_bounds__(256) void k_sel_final(const int32_t *__restrict__ s
         int carry = 0;
         for (int c0 = 0; c0 < nch; c0 += 256) {
             const int ch = c0 + tid;
-            const int n = ch < nch ? ccnt[(long)b * nchunk + ch] : 0;
+            const int v = c0 == 0 ? n0 : ccnt[(long)b * nchunk + min(ch, nch - 1)];
+            const int n = ch < nch ? v : 0;
             const int inc = wave_incl_scan(n);
             if (lane == 63) s_w[wave] = inc;
             __syncthreads();

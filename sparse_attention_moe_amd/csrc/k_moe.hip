@@ -528,14 +528,22 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, in
     const int *pi = pair_idx + (long)b * kk;
     const float *gt = gates + (long)b * ke;
     for (int j0 = 0; j0 < kk; j0 += 8) {
-        v4f f[8];
+        v4f f[8], f2[8];
         int q[8];
+        // every load unconditional (a missing pair reads pair 0's row and is dropped below), so the slots' loads
+        // are in flight together: a load under a condition is waited for on its own
+#pragma unroll
+        for (int u = 0; u < 8; u++) q[u] = pi[min(j0 + u, kk - 1)];
 #pragma unroll
         for (int u = 0; u < 8; u++) {
-            q[u] = j0 + u < kk ? pi[j0 + u] : -1;  // -1: past the slots, or a pair computed elsewhere
-            if (q[u] >= 0) f[u] = *(const v4f *)(F + (long)q[u] * D + d);
+            q[u] = j0 + u < kk ? q[u] : -1;  // -1: past the slots, or a pair computed elsewhere
+            f[u] = *(const v4f *)(F + (long)max(q[u], 0) * D + d);
+            if (nslot > 1) f2[u] = *(const v4f *)(F + fstride + (long)max(q[u], 0) * D + d);
         }
-        for (int k = 1; k < nslot; k++) {
+        if (nslot > 1)
+#pragma unroll
+            for (int u = 0; u < 8; u++) f[u] += f2[u];
+        for (int k = 2; k < nslot; k++) {
 #pragma unroll
             for (int u = 0; u < 8; u++)
                 if (q[u] >= 0) f[u] += *(const v4f *)(F + k * fstride + (long)q[u] * D + d);
