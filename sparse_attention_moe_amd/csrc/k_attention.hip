@@ -317,14 +317,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_mla1(const uint16_t *__restrict
     const int ps_mask = (1 << ps_shift) - 1;
     const int jbase = split * pps;
     // queries of this wave's 16 heads, as the A operand of every K step: head ln, features 32 kk + 8 lg .. + 8
+    // (loads unconditional, with clamped indices: a load under a condition is waited for on its own; a wave past
+    // the heads reads the last head's row and computes nothing with it)
     v8bf Aq[KQ];
+    const int hq = min(h0 + ln, H - 1);
 #pragma unroll
-    for (int kk = 0; kk < KQ; kk++)
-        Aq[kk] = active ? *(const v8bf *)(q + ((long)b * H + h0 + ln) * Dc + kk * 32 + lg * 8) : v8bf{};
+    for (int kk = 0; kk < KQ; kk++) Aq[kk] = *(const v8bf *)(q + ((long)b * H + hq) * Dc + kk * 32 + lg * 8);
     for (int i = tid; i < pps; i += 256) {
         const int j = jbase + i;
-        const int p = j < top_k ? sel[(long)b * top_k + j] : -1;
-        s_row[i] = p < 0 ? -1 : ((long)pt[(long)(b / R) * max_pages + (p >> ps_shift)] << ps_shift) + (p & ps_mask);
+        const int ps = sel[(long)b * top_k + min(j, top_k - 1)];
+        const int p = j < top_k ? ps : -1;
+        const int pg = pt[(long)(b / R) * max_pages + (max(p, 0) >> ps_shift)];
+        s_row[i] = p < 0 ? -1 : ((long)pg << ps_shift) + (p & ps_mask);
     }
     const int nch = jbase < top_k ? 1 : 0;
     // scores in log2 units: p = 2^(S - m) with S = sm_scale * log2(e) * q.c, so the exponentials are exp2
@@ -1011,18 +1015,29 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv_row(const float *__restri
     }
     // partial sums: thread -> features 4 fq .. + 4 of splits [HS sh, HS sh + HS)
     const int fq = tid & 127, sh = tid >> 7;
+    // this thread's two W_UV block scales, loaded now rather than where they are used
+    float wsv[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) wsv[kb] = wsc[((long)h * nrb + r / 128) * nkb + min(c_lo / 128 + kb, nkb - 1)];
+    // (every load unconditional, with clamped indices, and masked after: a load under a condition is waited for
+    // on its own)
     v4f pv[HS];
+    const int fqc = min(fq, Dv / 4 - 1);
 #pragma unroll
     for (int k = 0; k < HS; k++) {
-        const int s2 = sh * HS + k;
-        pv[k] = (s2 < nsplit && fq * 4 < Dv) ? *(const v4f *)(opart + (((long)b * nsplit + s2) * H + h) * Dv + fq * 4)
-                                            : v4f{0.f, 0.f, 0.f, 0.f};
+        const int s2 = min(sh * HS + k, nsplit - 1);
+        pv[k] = *(const v4f *)(opart + (((long)b * nsplit + s2) * H + h) * Dv + fqc * 4);
     }
+#pragma unroll
+    for (int k = 0; k < HS; k++)
+        if (!(sh * HS + k < nsplit && fq * 4 < Dv)) pv[k] = v4f{0.f, 0.f, 0.f, 0.f};
     // split weights w_s = e^(m_s - M) / sum_s e^(m_s - M) l_s (0 for an empty split), by wave 0
     if (wv == 0) {
         const bool ok = lane < nsplit;
-        const float m = ok ? ml[(((long)b * nsplit + lane) * H + h) * 2] : -INFINITY;
-        const float l = ok ? ml[(((long)b * nsplit + lane) * H + h) * 2 + 1] : 0.f;
+        const int lc = min(lane, nsplit - 1);
+        const float m0 = ml[(((long)b * nsplit + lc) * H + h) * 2], l0 = ml[(((long)b * nsplit + lc) * H + h) * 2 + 1];
+        const float m = ok ? m0 : -INFINITY;
+        const float l = ok ? l0 : 0.f;
         const float M = wave_max(m);
         const float e = m == -INFINITY ? 0.f : expf(m - M);
         const float den = wave_sum(e * l);
@@ -1065,7 +1080,7 @@ __global__ __launch_bounds__(256) void k_attn_merge_uv_row(const float *__restri
                 blk = fmaf(hi.y, s_o[c + 4 * i + 3], blk);
             }
         }
-        acc = fmaf(blk, wsc[((long)h * nrb + r / 128) * nkb + (c_lo / 128 + kb)], acc);
+        acc = fmaf(blk, wsv[kb], acc);
     }
     s_u[r][part] = acc;
     __syncthreads();
