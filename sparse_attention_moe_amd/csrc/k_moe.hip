@@ -175,8 +175,8 @@ __device__ __forceinline__ int token_topk(const double *lrow, int E, int ke)
 }
 
 // ------------------------------------------------------------------ dispatch plan
-// From the picks s_exp[b * ke + j] (in LDS) of a whole workgroup of 1024 threads: active experts in
-// ascending id (shared experts last), each expert's pairs in (token, slot) order, the pair index of every
+// From the picks s_exp[b * ke + j] (in LDS) of a whole workgroup of 1024 threads: active experts, the shared
+// ones first, then the routed ones in ascending id, each expert's pairs in (token, slot) order, the pair index of every
 // (token, slot), and the prefix over active experts of their token groups of PLAN_TPG (grp_off, n_active + 1
 // entries) that the expert GEMV enumerates its work by.  `distinct`: no token picks an expert twice (router
 // output), so an expert's pair rank is the number of earlier tokens in its token mask (B <= 64); otherwise the
@@ -290,7 +290,10 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
         }
         const int na_tot = __shfl(ia, 63, 64), ng_tot = __shfl(ig, 63, 64);
         const int npr = __shfl(ip, 63, 64);  // routed pairs computed here (skipped ones excluded)
-        int a = ia - na, q = ip - npl, gq = ig - ng;
+        // slots: the shared experts first (the most tokens: the fused FFN finishes their gate/up, and so can start
+        // their down pieces, earliest), then the routed ones in expert order; pairs: routed, then shared
+        const int gs = (B + PLAN_TPG - 1) / PLAN_TPG;  // token groups of a shared expert
+        int a = S + ia - na, q = ip - npl, gq = S * gs + ig - ng;
         for (int i = 0; i < per; i++) {
             const int e = lane * per + i;
             if (e < E && s_cnt[e] > 0) {
@@ -304,12 +307,11 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
                 gq += (s_cnt[e] + PLAN_TPG - 1) / PLAN_TPG;
             }
         }
-        const int gs = (B + PLAN_TPG - 1) / PLAN_TPG;  // token groups of a shared expert
         for (int sx = lane; sx < S; sx += 64) {
-            p.active[na_tot + sx] = E + sx;
-            p.tok_off[na_tot + sx] = npr + sx * B;
-            p.tok_cnt[na_tot + sx] = B;
-            p.grp_off[na_tot + sx] = ng_tot + sx * gs;
+            p.active[sx] = E + sx;
+            p.tok_off[sx] = npr + sx * B;
+            p.tok_cnt[sx] = B;
+            p.grp_off[sx] = sx * gs;
         }
         if (lane == 0) {
             p.grp_off[na_tot + S] = ng_tot + S * gs;
