@@ -125,9 +125,9 @@ def read_ceiling(reps: int, mib: int = 1536) -> dict:
     return out
 
 
-def null_phases(reps: int, kernels: int = 16, blocks: int = 256) -> dict:
+def null_phases(reps: int, kernels: int = 12, blocks: int = 256) -> dict:
     """Fixed cost of the step's dependent launches: `kernels` back-to-back launches of an empty kernel
-    (dl_probe_null; the step launches 16 kernels), one workgroup per compute unit."""
+    (dl_probe_null; the step launches 12 kernels up to 16 tokens), one workgroup per compute unit."""
     dl.probe_null(kernels, blocks)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -460,7 +460,8 @@ def main():
     # step ran it, else the gate/up GEMV
     fused = dl.profile_ffn_fused() == 1
     dom_bytes = avg_bytes["expert_gate_up"] + (avg_bytes["expert_down"] if fused else 0)
-    dom_name = "k_ffn_fp8 (expert FFN: gate/up, SwiGLU split, down)" if fused else "k_gemv_fp8<2,SWIGLU> (expert gate/up)"
+    dom_name = ("k_ffn_fp8 (expert FFN: gate/up, SwiGLU split, down)" if fused else
+                "k_gemv_fp8<2,SWIGLU> (expert gate/up)" if spec.fp8 else "k_gemv_f32<SWIGLU> (expert gate/up)")
     gu_gbs = dom_bytes / (ph["expert_gate_up"] * 1e-3) / 1e9
     rec = {
         "metric": metric_label(spec), "value": round(steps_per_s, 2), "unit": "layer-steps/s", "n_gpus": 1,
