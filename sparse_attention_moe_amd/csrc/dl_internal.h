@@ -105,20 +105,28 @@ static constexpr int GEMV_MAXMAT = 4096;  // active matrices of one FP8 GEMV (pl
 static constexpr int GEMV_QPOOLS = 8, GEMV_QSTRIDE = 64, GEMV_QINTS = GEMV_QPOOLS * GEMV_QSTRIDE;
 static constexpr int GEMV_QROUND = 512, GEMV_QTAB = 16;
 
-// The pools' shares m[0..7] of a round: at least 1 each and GEMV_QROUND in all, else (never written) equal ones.
-__device__ inline void gemv_shares_read(const int *q, int m[GEMV_QPOOLS])
+// The pools' shares m[0..7] of a round from the stored raw[0..7]: at least 1 each and GEMV_QROUND in all, else
+// (never written) equal ones.
+__device__ inline void gemv_shares_valid(const int raw[GEMV_QPOOLS], int m[GEMV_QPOOLS])
 {
     int tot = 0;
     bool ok = true;
 #pragma unroll
     for (int p = 0; p < GEMV_QPOOLS; p++) {
-        m[p] = q[GEMV_QTAB + p];
+        m[p] = raw[p];
         ok = ok && m[p] >= 1 && m[p] <= GEMV_QROUND;
         tot += ok ? m[p] : 0;
     }
     if (!ok || tot != GEMV_QROUND)
 #pragma unroll
         for (int p = 0; p < GEMV_QPOOLS; p++) m[p] = GEMV_QROUND / GEMV_QPOOLS;
+}
+__device__ inline void gemv_shares_read(const int *q, int m[GEMV_QPOOLS])
+{
+    int raw[GEMV_QPOOLS];
+#pragma unroll
+    for (int p = 0; p < GEMV_QPOOLS; p++) raw[p] = q[GEMV_QTAB + p];
+    gemv_shares_valid(raw, m);
 }
 
 // Position in its round of pool p's k-th slot (k < m[p]).  The slots of all pools are ordered by (k + 1/2) / m_p,

@@ -189,15 +189,28 @@ __device__ __forceinline__ int token_topk(const double *lrow, int E, int ke)
 // differ by up to about 15% on one device, the slow ones the same from launch to launch.)  Which
 // pool runs a piece never changes a result (piece j of a unit always writes partial slot j).  Shares or times
 // that were never written give equal shares.  Lanes 0..7 of one wave.
-__device__ void gemv_pool_shares(int *q, int lane)
+// The inputs of the shares, split from the arithmetic below so that a caller can issue these loads early and
+// use them later: the current shares and lane l's pool's start and end times (lanes 8..63 read pool 7's, unused).
+struct PoolIn {
+    int m[GEMV_QPOOLS];
+    unsigned long long t0, t1;
+};
+__device__ __forceinline__ void gemv_pool_load(const int *q, int lane, PoolIn &in)
+{
+#pragma unroll
+    for (int p = 0; p < GEMV_QPOOLS; p++) in.m[p] = q[GEMV_QTAB + p];
+    const int l = min(lane, GEMV_QPOOLS - 1);
+    in.t0 = *(const unsigned long long *)(q + l * GEMV_QSTRIDE + 2);
+    in.t1 = *(const unsigned long long *)(q + l * GEMV_QSTRIDE + 4);
+}
+__device__ void gemv_pool_shares(int *q, int lane, const PoolIn &in)
 {
     int m[GEMV_QPOOLS];
-    gemv_shares_read(q, m);
+    gemv_shares_valid(in.m, m);
     float rl = 0.f;
     bool okl = true;
     if (lane < GEMV_QPOOLS) {
-        const unsigned long long t0 = *(const unsigned long long *)(q + lane * GEMV_QSTRIDE + 2);
-        const unsigned long long t1 = *(const unsigned long long *)(q + lane * GEMV_QSTRIDE + 4);
+        const unsigned long long t0 = in.t0, t1 = in.t1;
         int ml = 0;
 #pragma unroll
         for (int p = 0; p < GEMV_QPOOLS; p++) ml = lane == p ? m[p] : ml;
@@ -263,8 +276,11 @@ __device__ void build_plan(const int *s_exp, int B, int ke, int E, int S, bool d
     }
     __syncthreads();
     // the expert GEMVs' work queues: the pools' shares from their last launch, cleared counters
-    if (shares && p.queue && nT >= 256 && (tid >> 6) >= 2 && (tid >> 6) < 4)
-        gemv_pool_shares(p.queue + ((tid >> 6) - 2) * GEMV_QINTS, lane);
+    if (shares && p.queue && nT >= 256 && (tid >> 6) >= 2 && (tid >> 6) < 4) {
+        PoolIn in;
+        gemv_pool_load(p.queue + ((tid >> 6) - 2) * GEMV_QINTS, lane, in);
+        gemv_pool_shares(p.queue + ((tid >> 6) - 2) * GEMV_QINTS, lane, in);
+    }
     if (p.queue && tid < 2 * GEMV_QPOOLS) {
         p.queue[tid * GEMV_QSTRIDE] = 0;
         p.queue[tid * GEMV_QSTRIDE + 1] = 0;
@@ -396,8 +412,11 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nT = 1024;
     const bool plan = p.active != nullptr;
-    // the expert GEMVs' pool shares for this step, by the last two waves (idle while the tokens are routed)
-    if (plan && p.queue && wv >= 14) gemv_pool_shares(p.queue + (wv - 14) * GEMV_QINTS, lane);
+    // the expert GEMVs' pool shares for this step, by the last two waves: their inputs loaded now, the arithmetic
+    // while waves 0..nb-1 pick the experts of the first block's tokens
+    const bool shares = plan && p.queue && wv >= 14;
+    PoolIn pin;
+    if (shares) gemv_pool_load(p.queue + (wv - 14) * GEMV_QINTS, lane, pin);
     const int tb = RP_LCAP / E;
     const int t0 = blockIdx.x * tpb, t1 = min(B, t0 + tpb);  // this workgroup's tokens
     for (int b0 = t0; b0 < t1; b0 += tb) {
@@ -455,6 +474,7 @@ __global__ __launch_bounds__(1024) void k_route_plan(const double *__restrict__ 
                 if (plan) s_exp[b * ke + lane] = me;
             }
         }
+        if (shares && b0 == t0) gemv_pool_shares(p.queue + (wv - 14) * GEMV_QINTS, lane, pin);
         __syncthreads();
     }
     if (plan) build_plan(s_exp, B, ke, E, S, true, s_cnt, s_off, s_mask, p, false);
