@@ -171,16 +171,28 @@ __global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(co
     constexpr int SCORE_POS_PER_BLOCK = SCORE_WPB * 4 * 64;
     __shared__ unsigned s_hist[RW][NB1];
     const int sq = blockIdx.y;
-    // items (positions, or pools of `pool` positions) of the sequence; row r sees the items of its first
-    // seq_lens - (RW - 1 - r) positions
-    const int L = row_len(seq_lens, sq * RW + RW - 1, RW, pool);
     const long blk0 = (long)blockIdx.x * SCORE_POS_PER_BLOCK;
-    if (blk0 >= L) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
-    for (int i = tid; i < RW * NB1; i += SCORE_WPB * 64) (&s_hist[0][0])[i] = 0;
-
-    // A operand: q rows (indexer heads) for this lane: head hg*16+ln, bytes kc*64 + lg*16 .. +16
+    // The sequence's length, the query rows and the page-table entries of every position this lane loads are
+    // read together, before the length is known (one round trip instead of two): the entries of positions
+    // clamped to the page table's reach, and every read unconditional (a read under a condition is waited for on
+    // its own), masked afterwards.  Positions past the end then take the workgroup's first position's row, and
+    // their scores are never stored.
+    const int32_t *pt = page_table + (long)sq * max_pages;
+    const int ps_mask = (1 << ps_shift) - 1;
+    const long pmax = ((long)max_pages << ps_shift) - 1;  // the last item the page table reaches
+    int pe[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; st++)
+#pragma unroll
+        for (int sg = 0; sg < 4; sg++) {
+            const long pos = blk0 + (long)(st * SCORE_WPB + wave) * 64 + sg * 16 + ln;
+            pe[st][sg] = pt[min(pos, pmax) >> ps_shift];
+        }
+    const int pe0 = pt[min(blk0, pmax) >> ps_shift];
+    // A operand: q rows (indexer heads) for this lane: head hg*16+ln, bytes kc*64 + lg*16 .. +16 (zero past the
+    // heads or the key dimension)
     v4i A[RW][NHG][KCH];
 #pragma unroll
     for (int r = 0; r < RW; r++)
@@ -188,31 +200,29 @@ __global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(co
         for (int hg = 0; hg < NHG; hg++)
 #pragma unroll
             for (int kc = 0; kc < KCH; kc++) {
-                int h = hg * 16 + ln, d = kc * 64 + lg * 16;
-                A[r][hg][kc] = (h < HI && d < DI) ? ldg16(q_idx + (((long)sq * RW + r) * HI + h) * DI + d)
-                                                  : v4i{0, 0, 0, 0};
+                const int h = min(hg * 16 + ln, HI - 1), d = min(kc * 64 + lg * 16, DI - 16);
+                A[r][hg][kc] = ldg16(q_idx + (((long)sq * RW + r) * HI + h) * DI + d);
             }
-    const int32_t *pt = page_table + (long)sq * max_pages;
-    const int ps_mask = (1 << ps_shift) - 1;
-    // cache rows of every position this lane loads (step st, group sg: position g0(st) + sg*16 + ln), all
-    // page-table reads in flight at once.  Every read, here and of the keys below, is unconditional (a read under
-    // a condition is waited for on its own): positions past the end take the last position's row, and their
-    // scores are never stored
+#pragma unroll
+    for (int hg = 0; hg < NHG; hg++)
+#pragma unroll
+        for (int kc = 0; kc < KCH; kc++)
+            if (!(hg * 16 + ln < HI && kc * 64 + lg * 16 < DI))
+#pragma unroll
+                for (int r = 0; r < RW; r++) A[r][hg][kc] = v4i{0, 0, 0, 0};
+    // items (positions, or pools of `pool` positions) of the sequence; row r sees the items of its first
+    // seq_lens - (RW - 1 - r) positions
+    const int L = row_len(seq_lens, sq * RW + RW - 1, RW, pool);
+    if (blk0 >= L) return;
+    for (int i = tid; i < RW * NB1; i += SCORE_WPB * 64) (&s_hist[0][0])[i] = 0;
     long row[4][4];
-    int pe[4][4];
 #pragma unroll
     for (int st = 0; st < 4; st++)
 #pragma unroll
         for (int sg = 0; sg < 4; sg++) {
             const long pos = blk0 + (long)(st * SCORE_WPB + wave) * 64 + sg * 16 + ln;
-            pe[st][sg] = pt[min(pos, (long)L - 1) >> ps_shift];
-        }
-#pragma unroll
-    for (int st = 0; st < 4; st++)
-#pragma unroll
-        for (int sg = 0; sg < 4; sg++) {
-            const long pos = min(blk0 + (long)(st * SCORE_WPB + wave) * 64 + sg * 16 + ln, (long)L - 1);
-            row[st][sg] = ((long)pe[st][sg] << ps_shift) + (pos & ps_mask);
+            row[st][sg] = pos < L ? ((long)pe[st][sg] << ps_shift) + (pos & ps_mask)
+                                  : ((long)pe0 << ps_shift) + (blk0 & ps_mask);
         }
     __syncthreads();
     // keys of step st: 4 groups of 16 positions x KCH chunks of 64 bytes; two steps in flight.  Key bytes past DI
