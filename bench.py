@@ -346,7 +346,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=12,
+                    help="untimed steps first (3 per rotated instance: the expert kernels' pool shares settle in 2-3 calls)")
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
