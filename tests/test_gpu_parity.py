@@ -401,9 +401,28 @@ def test_layer_step_rows(R):
     say(f"rows R={R}: {w}")
 
 
+def _ffn_mats(w, tiled):
+    """dl_mat views of an FFN's gate, up and down stacks: row-major (the three-launch path), or re-tiled
+    (DL_LAYOUT_TILES: the fused FFN kernel); returns the views and the tensors they point into."""
+    keep, mats = [], []
+    for k in ("w_gate", "w_up", "w_down"):
+        wk, sk = w[k], w[k + "_scale"]
+        if tiled:
+            wk = dl.pack_weights(wk, sk)
+        keep.append(wk)
+        mats.append(dl.mat(wk, sk, dl.DL_LAYOUT_TILES if tiled else dl.DL_LAYOUT_ROWS))
+    return mats, keep
+
+
+def _check_ffn_path(tiled):
+    # FP8 weights in tiles run the fused FFN kernel, row-major ones the three launches
+    assert dl.profile_ffn_fused() == (1 if tiled else 0)
+
+
 # ------------------------------------------------------------- one GPU's tensor-parallel share of the FFN
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("n", [2, 4])
-def test_ffn_tensor_parallel_slices_sum_to_whole(n):
+def test_ffn_tensor_parallel_slices_sum_to_whole(n, tiled):
     # Each of n GPUs would hold I/n intermediate rows of every expert; here the n shares run one after the other
     # on one GPU.  Their outputs (the residual added by share 0 only) must add up to the oracle's whole FFN.
     spec = synth.small_fp8_spec(name=f"tp{n}", B=4, seq_lens=(900, 600, 300, 1), I=512)
@@ -417,10 +436,10 @@ def test_ffn_tensor_parallel_slices_sum_to_whole(n):
     for s_ in range(n):
         w = synth.tp_slice(t, spec, s_, n)
         part = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
-        say(f"[gpu] moe_ffn tensor-parallel share {s_}/{n} inter={spec.I // n}")
-        dl.moe_ffn(h, ex, g, dl.mat(w["w_gate"], w["w_gate_scale"]), dl.mat(w["w_up"], w["w_up_scale"]),
-                   dl.mat(w["w_down"], w["w_down_scale"]), spec.E, spec.n_shared, part,
-                   residual=h if s_ == 0 else None)
+        say(f"[gpu] moe_ffn tensor-parallel share {s_}/{n} inter={spec.I // n} tiled={tiled}")
+        (wg, wu, wd), keep = _ffn_mats(w, tiled)
+        dl.moe_ffn(h, ex, g, wg, wu, wd, spec.E, spec.n_shared, part, residual=h if s_ == 0 else None)
+        _check_ffn_path(tiled)
         total += part
     torch.cuda.synchronize()
     orc = oracle.LayerOracle(spec, t)
@@ -513,7 +532,8 @@ def test_layer_step_rows_pooled(R, pool):
 
 # ------------------------------------------------------------- one GPU's expert-parallel share of the FFN
 @pytest.mark.parametrize("n", [2, 4, 8])
-def test_ffn_expert_parallel_shares_sum_to_whole(n):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_ffn_expert_parallel_shares_sum_to_whole(n, tiled):
     # GPU g of n holds routed experts [g E/n, (g+1) E/n); each share applies only its picks (with n = 8 a token picks
     # more experts than a GPU holds).  The shares, run one after the other on one GPU, with the shared expert and
     # the residual on share 0, must add up to the oracle's whole FFN.
@@ -529,9 +549,10 @@ def test_ffn_expert_parallel_shares_sum_to_whole(n):
         w = synth.ep_slice(t, spec, s_, n, shared=s_ == 0)
         part = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
         ns = spec.n_shared if s_ == 0 else 0
-        say(f"[gpu] moe_ffn_ep share {s_}/{n} experts [{s_ * per}, {(s_ + 1) * per}) shared={ns}")
-        dl.moe_ffn_ep(h, ex, g, s_ * per, dl.mat(w["w_gate"], w["w_gate_scale"]), dl.mat(w["w_up"], w["w_up_scale"]),
-                      dl.mat(w["w_down"], w["w_down_scale"]), per, ns, part, residual=h if s_ == 0 else None)
+        say(f"[gpu] moe_ffn_ep share {s_}/{n} experts [{s_ * per}, {(s_ + 1) * per}) shared={ns} tiled={tiled}")
+        (wg, wu, wd), keep = _ffn_mats(w, tiled)
+        dl.moe_ffn_ep(h, ex, g, s_ * per, wg, wu, wd, per, ns, part, residual=h if s_ == 0 else None)
+        _check_ffn_path(tiled)
         total += part
     torch.cuda.synchronize()
     orc = oracle.LayerOracle(spec, t)
@@ -543,7 +564,32 @@ def test_ffn_expert_parallel_shares_sum_to_whole(n):
         assert_close(f"ep{n} row {b} y-h", got[b] - hh[b], y64 - hh[b])
 
 
-def test_ffn_skips_negative_expert_ids():
+@pytest.mark.parametrize("tiled", [False, True])
+def test_ffn_expert_parallel_share_without_picks(tiled):
+    # a share holding none of the picked experts and no shared expert has no active slot at all: its output is
+    # exactly the residual it is given (zero without one), whatever the other shares compute
+    spec = synth.small_fp8_spec(name="ep-empty", B=4, seq_lens=(900, 600, 300, 1), I=512)
+    t = _layer(spec, seed=79)
+    B, n = spec.B, 2
+    per = spec.E // n
+    h = (torch.randn(B, spec.D, generator=torch.Generator().manual_seed(13)) * 0.5).to(DEV)
+    # every token picks among the first half of the experts
+    ex = torch.tensor([[(b * spec.ke + j) % per for j in range(spec.ke)] for b in range(B)], dtype=torch.int32,
+                      device=DEV)
+    g = torch.full((B, spec.ke), 1.0 / spec.ke, dtype=torch.float32, device=DEV)
+    w = synth.ep_slice(t, spec, 1, n, shared=False)
+    (wg, wu, wd), keep = _ffn_mats(w, tiled)
+    for resid in (None, h):
+        part = torch.full((B, spec.D), float("nan"), dtype=torch.float32, device=DEV)
+        say(f"[gpu] moe_ffn_ep share 1/{n} with no picks residual={resid is not None} tiled={tiled}")
+        dl.moe_ffn_ep(h, ex, g, per, wg, wu, wd, per, 0, part, residual=resid)
+        _check_ffn_path(tiled)
+        torch.cuda.synchronize()
+        assert torch.equal(part, h if resid is not None else torch.zeros_like(h))
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_ffn_skips_negative_expert_ids(tiled):
     # dl_moe_ffn with some slots marked -1 (applied elsewhere) against the oracle, which skips them too; one token
     # has every slot elsewhere, so its output is the residual plus the shared expert
     spec = synth.small_fp8_spec(name="skip", B=4, seq_lens=(900, 600, 300, 1), I=512)
@@ -559,9 +605,10 @@ def test_ffn_skips_negative_expert_ids():
     exs[1, 3] = -1
     exs[2, :] = -1
     y = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
-    say("[gpu] moe_ffn with skipped slots")
-    dl.moe_ffn(h, exs, g, dl.mat(t["w_gate"], t["w_gate_scale"]), dl.mat(t["w_up"], t["w_up_scale"]),
-               dl.mat(t["w_down"], t["w_down_scale"]), spec.E, spec.n_shared, y, residual=h)
+    say(f"[gpu] moe_ffn with skipped slots tiled={tiled}")
+    (wg, wu, wd), keep = _ffn_mats(t, tiled)
+    dl.moe_ffn(h, exs, g, wg, wu, wd, spec.E, spec.n_shared, y, residual=h)
+    _check_ffn_path(tiled)
     torch.cuda.synchronize()
     orc = oracle.LayerOracle(spec, t)
     hh = host(h).astype(np.float64)
@@ -572,7 +619,8 @@ def test_ffn_skips_negative_expert_ids():
         assert_close(f"skip row {b} y-h", got[b] - hh[b], y64 - hh[b])
 
 
-def test_ffn_repeated_expert_in_a_token():
+@pytest.mark.parametrize("tiled", [False, True])
+def test_ffn_repeated_expert_in_a_token(tiled):
     # caller-given picks may name one expert in two slots of a token: each slot is its own pair (its own gate),
     # ranked after the token's earlier picks; the oracle applies the expert once per slot as well
     spec = synth.small_fp8_spec(name="rep", B=4, seq_lens=(900, 600, 300, 1), I=512)
@@ -587,9 +635,10 @@ def test_ffn_repeated_expert_in_a_token():
     exr[3, spec.ke - 1] = exr[3, 1]
     exr[3, 0] = exr[3, 1]
     y = torch.empty(B, spec.D, dtype=torch.float32, device=DEV)
-    say("[gpu] moe_ffn with a repeated expert")
-    dl.moe_ffn(h, exr, g, dl.mat(t["w_gate"], t["w_gate_scale"]), dl.mat(t["w_up"], t["w_up_scale"]),
-               dl.mat(t["w_down"], t["w_down_scale"]), spec.E, spec.n_shared, y, residual=h)
+    say(f"[gpu] moe_ffn with a repeated expert tiled={tiled}")
+    (wg, wu, wd), keep = _ffn_mats(t, tiled)
+    dl.moe_ffn(h, exr, g, wg, wu, wd, spec.E, spec.n_shared, y, residual=h)
+    _check_ffn_path(tiled)
     torch.cuda.synchronize()
     orc = oracle.LayerOracle(spec, t)
     hh = host(h).astype(np.float64)
@@ -601,8 +650,9 @@ def test_ffn_repeated_expert_in_a_token():
         assert_close(f"rep row {b} y-h", got[b] - hh[b], y64 - hh[b])
 
 
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("D,I,E,ke,B", [(128, 128, 8, 2, 3), (384, 384, 16, 4, 5), (2048, 256, 64, 6, 40)])
-def test_ffn_work_queue_shapes(D, I, E, ke, B):
+def test_ffn_work_queue_shapes(D, I, E, ke, B, tiled):
     # the expert GEMVs' work queues over K ranges of one 128-block (a single piece per unit), of three blocks
     # (pieces of two and one), and a batch above 16 tokens with 40 x 6 picks over 64 experts (several token
     # groups per expert); two calls in a row give bit-identical outputs whichever waves took which pieces
@@ -614,11 +664,12 @@ def test_ffn_work_queue_shapes(D, I, E, ke, B):
     g = torch.empty(B, ke, dtype=torch.float32, device=DEV)
     dl.moe_route(h, t["w_r"], t["r_bias"], ke, ex, g)
     ys = []
-    say(f"[gpu] moe_ffn queue shapes D={D} I={I} E={E} ke={ke} B={B}")
+    say(f"[gpu] moe_ffn queue shapes D={D} I={I} E={E} ke={ke} B={B} tiled={tiled}")
+    (wg, wu, wd), keep = _ffn_mats(t, tiled)
     for _ in range(2):
         y = torch.empty(B, D, dtype=torch.float32, device=DEV)
-        dl.moe_ffn(h, ex, g, dl.mat(t["w_gate"], t["w_gate_scale"]), dl.mat(t["w_up"], t["w_up_scale"]),
-                   dl.mat(t["w_down"], t["w_down_scale"]), E, spec.n_shared, y, residual=h)
+        dl.moe_ffn(h, ex, g, wg, wu, wd, E, spec.n_shared, y, residual=h)
+        _check_ffn_path(tiled)
         ys.append(y)
     torch.cuda.synchronize()
     assert torch.equal(ys[0], ys[1])
