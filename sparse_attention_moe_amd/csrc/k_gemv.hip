@@ -811,16 +811,18 @@ int launch_ffn_fused(const FfnFused &f, hipStream_t s)
 // a few blocks per wave, then adds its token groups' activations; the four waves' sums go through LDS and are
 // added in wave order into partial slot (K group) of [slot][token][row].  Four tiles per workgroup give W_O
 // (6,144 rows x 64 K-blocks) 768 workgroups, three per compute unit; eight gave 384, so half the units held two
-// and half one, and the kernel lasted as long as the units reading twice the bytes.
+// and half one, and the kernel lasted as long as the units reading twice the bytes.  The token groups run one
+// after another (16 of them at 64 tokens), each loading the next group's activations before its own products.
 static constexpr int PROJ_RT = 4;
 template <int NS, bool TL>
 __global__ __launch_bounds__(256) void k_proj_shot(GemvArgs a)
 {
     constexpr int RT = PROJ_RT, KB = 2;
-    __shared__ v4f s_acc[4][RT][64];
+    __shared__ v4f s_acc[2][4][RT][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ln = lane & 15, lg = lane >> 4;
     const int rb = blockIdx.x, kq = blockIdx.y;
     const int kb0 = kq * 8 + w * KB;
+    if (a.ntok_host <= 0) return;
     v8i A[KB][RT];
 #pragma unroll
     for (int k = 0; k < KB; k++)
@@ -832,43 +834,55 @@ __global__ __launch_bounds__(256) void k_proj_shot(GemvArgs a)
 #pragma unroll
     for (int k = 0; k < KB; k++) ws[k] = a.wsc[(long)(rb * RT / 8) * a.nkb + kb0 + k];  // 128-row scale blocks
     constexpr int TPG = 16 / NS;  // tokens per group: the NS parts share the 16 columns
-    for (int t0 = 0; t0 < a.ntok_host; t0 += TPG) {
-        const int t = t0 + ln % TPG, sp = ln / TPG;
-        const bool tv = t < a.ntok_host;
-        v8i Bv[KB];
-        float as[KB];
+    const int ntok = a.ntok_host, tl = ln % TPG, sp = ln / TPG;
+    const int tlast = (ntok - 1) / TPG * TPG;  // the last group's first token
+    // a token group's activation codes and scales; the token clamped into range (every load unconditional, so
+    // they are in flight together; a lane past the last token repeats it and its scale is zeroed below)
+    auto load_b = [&](int t0, v8i (&Bv)[KB], float (&as)[KB]) {
+        const int t = min(t0 + tl, ntok - 1);
 #pragma unroll
         for (int k = 0; k < KB; k++) {
-            if (tv) {
-                Bv[k] = ld16x2(a.aq + sp * a.aq_part + (long)t * a.cols + (kb0 + k) * 128 + lg * 16, 64);
-                as[k] = a.asc[sp * a.asc_part + (long)t * a.nkb + kb0 + k];
-            } else {
-                Bv[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-                as[k] = 0.f;
-            }
+            Bv[k] = ld16x2(a.aq + sp * a.aq_part + (long)t * a.cols + (kb0 + k) * 128 + lg * 16, 64);
+            as[k] = a.asc[sp * a.asc_part + (long)t * a.nkb + kb0 + k];
         }
+    };
+    // one token group: the next group's operands are loaded before this one's products, so their latency
+    // overlaps the arithmetic and the sums; the four waves' sums go through LDS buffer buf (two buffers
+    // alternate, so one barrier per group suffices: a buffer is written again only after the barrier of the
+    // group in between, which every wave passes after reading it)
+    auto group = [&](int t0, int buf, v8i (&Bc)[KB], float (&sc)[KB], v8i (&Bn)[KB], float (&sn)[KB]) {
+        load_b(min(t0 + TPG, tlast), Bn, sn);
+        const int t = t0 + tl;
+        const bool tv = t < ntok;
         v4f tot[RT];
 #pragma unroll
         for (int r = 0; r < RT; r++) tot[r] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KB; k++) {
-            const float f = ws[k] * as[k];
+            const float f = tv ? ws[k] * sc[k] : 0.f;
 #pragma unroll
-            for (int r = 0; r < RT; r++) tot[r] += mfma_fp8(A[k][r], Bv[k]) * f;
+            for (int r = 0; r < RT; r++) tot[r] += mfma_fp8(A[k][r], Bc[k]) * f;
         }
 #pragma unroll
-        for (int r = 0; r < RT; r++) s_acc[w][r][lane] = sum_parts<NS>(tot[r]);
+        for (int r = 0; r < RT; r++) s_acc[buf][w][r][lane] = sum_parts<NS>(tot[r]);
         __syncthreads();
         // wave w adds the four waves' sums of its RT / 4 tiles
         if (tv && sp == 0) {
 #pragma unroll
             for (int q = 0; q < RT / 4; q++) {
                 const int r = (RT / 4) * w + q;
-                const v4f v = ((s_acc[0][r][lane] + s_acc[1][r][lane]) + s_acc[2][r][lane]) + s_acc[3][r][lane];
+                const v4f v = ((s_acc[buf][0][r][lane] + s_acc[buf][1][r][lane]) + s_acc[buf][2][r][lane]) +
+                              s_acc[buf][3][r][lane];
                 *(v4f *)(a.part + (long)kq * a.n_out + (long)t * a.o_ts + (rb * RT + r) * 16 + 4 * lg) = v;
             }
         }
-        __syncthreads();
+    };
+    v8i B0[KB], B1[KB];
+    float s0[KB], s1[KB];
+    load_b(0, B0, s0);
+    for (int t0 = 0; t0 < ntok; t0 += 2 * TPG) {
+        group(t0, 0, B0, s0, B1, s1);
+        if (t0 + TPG < ntok) group(t0 + TPG, 1, B1, s1, B0, s0);
     }
 }
 
