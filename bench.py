@@ -125,9 +125,9 @@ def read_ceiling(reps: int, mib: int = 1536) -> dict:
     return out
 
 
-def null_phases(reps: int, kernels: int = 12, blocks: int = 256) -> dict:
+def null_phases(reps: int, kernels: int = 11, blocks: int = 256) -> dict:
     """Fixed cost of the step's dependent launches: `kernels` back-to-back launches of an empty kernel
-    (dl_probe_null; the step launches 12 kernels up to 16 tokens), one workgroup per compute unit."""
+    (dl_probe_null; the step launches 11 kernels up to 16 tokens), one workgroup per compute unit."""
     dl.probe_null(kernels, blocks)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -37,6 +37,7 @@ struct Thr {           // the selection threshold of a row: items scoring above 
 struct TopkWs {
     int32_t *scores;   // [B, Lmax] scores of the row's items
     unsigned *hist1;   // [B, NB1] log-linear histogram of the scores
+    unsigned long long *hflag;  // [sequences] epoch of the launch that last cleared the sequence's histograms
     unsigned *bits;    // [B, nchunk * 128] kept items, one bit each (whole 4,096-item chunks)
     int2 *cand;        // [B, nchunk * 4,096] (item, score) inside the threshold bin, per chunk
     int32_t *ccnt;     // [B, nchunk] how many per chunk

@@ -38,13 +38,6 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// Device-scope accesses (coherent across the eight XCDs' L2 caches: stores write through, loads do not hit a
-// line another XCD may have changed) for data handed between workgroups inside one launch.
-__device__ __forceinline__ float ld_dev(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ int ld_dev(const int *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ void st_dev(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ void st_dev(uint16_t *p, uint16_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-
 // A ticket from a queue counter into tk (lane 0; the other lanes keep theirs): the counter's old value, waited for
 // only where it is read.  The address passes through a register the compiler cannot see into: with a uniform address
 // it rewrites the atomic into a wave-wide form and waits for its result at once, and that wait (in issue order)

@@ -24,6 +24,10 @@
 #include "dl_internal.h"
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <stdint.h>
+#include <unistd.h>
 
 namespace dl {
 
@@ -150,13 +154,6 @@ __device__ Thr threshold(const unsigned *gh, int L, int top_k, unsigned *sh, int
     return t;
 }
 
-// Clears the row's histogram.
-__global__ void k_sel_init(unsigned *hist1)
-{
-    const int b = blockIdx.x;
-    for (int i = threadIdx.x; i < NB1; i += blockDim.x) hist1[(long)b * NB1 + i] = 0;
-}
-
 // Scores of score_wpb() x 256 positions of one sequence per workgroup.  NHG groups of 16 indexer heads, KCH
 // chunks of 64 key bytes, RW query rows per sequence: every key is loaded once and scored against all RW rows (RW x
 // NHG matrix instructions per 16 positions and 64 key bytes), each row keeping the positions it sees.
@@ -165,7 +162,9 @@ __global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(co
                                                      const int32_t *__restrict__ page_table,
                                                      const int32_t *__restrict__ seq_lens, int pool, int max_pages,
                                                      int ps_shift, int HI, int DI, int32_t *__restrict__ scores,
-                                                     long Lmax, unsigned *__restrict__ hist1, int tiles)
+                                                     long Lmax, unsigned *__restrict__ hist1,
+                                                     unsigned long long *__restrict__ hflag, unsigned long long epoch,
+                                                     int tiles)
 {
     constexpr int SCORE_WPB = score_wpb(NHG, KCH, RW);
     constexpr int SCORE_POS_PER_BLOCK = SCORE_WPB * 4 * 64;
@@ -174,6 +173,18 @@ __global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(co
     const long blk0 = (long)blockIdx.x * SCORE_POS_PER_BLOCK;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
+    // The sequence's first workgroup clears its rows' histograms and then stamps the sequence's flag with this
+    // launch's epoch (a value no earlier launch used); every workgroup adds to the histograms only once it has
+    // read that stamp.  The clear's stores write through to memory and are complete before the stamp is
+    // written, and the histogram atomics are device-scope, so they land on the cleared words.  The first
+    // workgroup of a sequence precedes the others in dispatch order, so it is resident or done when they wait.
+    if (blockIdx.x == 0) {
+        unsigned *gh = hist1 + (long)sq * RW * NB1;
+        for (int i = tid; i < RW * NB1; i += SCORE_WPB * 64) st_dev(gh + i, 0u);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) st_dev(hflag + sq, epoch);
+    }
     // The sequence's length, the query rows and the page-table entries of every position this lane loads are
     // read together, before the length is known (one round trip instead of two): the entries of positions
     // clamped to the page table's reach, and every read unconditional (a read under a condition is waited for on
@@ -278,6 +289,15 @@ __global__ __launch_bounds__(score_wpb(NHG, KCH, RW) * 64) void k_index_score(co
                 scores[((long)sq * RW + r) * Lmax + pos] = mine[r];
                 atomicAdd(&s_hist[r][bin1_of(mine[r])], 1u);
             }
+        }
+    }
+    // the histograms are cleared once the sequence's flag holds this launch's epoch (read by one thread; the
+    // barrier passes it on).  A bounded wait: the first workgroup stamps the flag within a few microseconds
+    if (tid == 0) {
+        unsigned long long f = ld_dev(hflag + sq);
+        for (int it = 0; f != epoch && it < (1 << 22); it++) {
+            __builtin_amdgcn_s_sleep(4);
+            f = ld_dev(hflag + sq);
         }
     }
     __syncthreads();
@@ -599,6 +619,7 @@ void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R, int pool)
     const long nchunk = (Lmax + SEL_CHUNK - 1) / SEL_CHUNK;
     t.scores = w.take<int32_t>(B * Lmax);
     t.hist1 = w.take<unsigned>(B * NB1);
+    t.hflag = w.take<unsigned long long>(pg.batch);
     t.bits = w.take<unsigned>(B * nchunk * (SEL_CHUNK / 32));
     t.cand = w.take<int2>(B * nchunk * SEL_CHUNK);
     t.ccnt = w.take<int32_t>(B * nchunk);
@@ -606,17 +627,37 @@ void topk_ws_layout(Ws &w, const dl_pages &pg, TopkWs &t, int R, int pool)
     t.thr = w.take<Thr>(B);
 }
 
+// A number no earlier scoring launch of this process used: a counter from a start drawn once per process (mixed
+// from the clock, the process id and an address), so that a flag left in reused memory is unlikely to match.
+static unsigned long long next_epoch()
+{
+    static std::atomic<unsigned long long> n{0};
+    static const unsigned long long base = [] {
+        unsigned long long x = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+        x ^= (unsigned long long)getpid() << 32;
+        x ^= (unsigned long long)(uintptr_t)&n;
+        // splitmix64 finaliser
+        x += 0x9E3779B97F4A7C15ull;
+        x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+        x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+        return x ^ (x >> 31);
+    }();
+    const unsigned long long e = base + n.fetch_add(1);
+    return e ? e : 1;
+}
+
 template <int NHG, int KCH>
 static void launch_score(hipStream_t s, const int8_t *q, const int8_t *kp, const dl_pages &pg, int ps_shift, int HI,
                          int DI, const TopkWs &t, long Lmax, int R, int pool)
 {
+    const unsigned long long epoch = next_epoch();
 #define DL_SCORE_R(R_)                                                                                              \
     if (R == R_) {                                                                                                  \
         constexpr int W = score_wpb(NHG, KCH, R_), P = W * 4 * 64; /* waves, positions per workgroup */            \
         const int nblk = (int)((Lmax + P - 1) / P);                                                                 \
         hipLaunchKernelGGL((k_index_score<NHG, KCH, R_>), dim3(nblk, pg.batch), dim3(W * 64), 0, s, q, kp,           \
                            pg.page_table, pg.seq_lens, pool, pg.max_pages_per_seq, ps_shift, HI, DI, t.scores, Lmax,  \
-                           t.hist1, pg.key_layout == DL_LAYOUT_TILES);                                              \
+                           t.hist1, t.hflag, epoch, pg.key_layout == DL_LAYOUT_TILES);                              \
     }
     DL_SCORE_R(1) DL_SCORE_R(2) DL_SCORE_R(3) DL_SCORE_R(4)
 #undef DL_SCORE_R
@@ -635,7 +676,6 @@ int launch_indexer_topk(const dl_pages &pg, const int8_t *q_idx, const int8_t *k
     const long Lw = (long)nchunk * (SEL_CHUNK / 32);  // bitmap words per row
     const int PB = Lmax > 1 ? 32 - __builtin_clz((unsigned)(Lmax - 1)) : 1;  // bits of an item index
     if (nchunk > FCH) return fail(DL_ERR_UNSUPPORTED, "indexer: %ld items per row (<= %d)", Lmax, FCH * SEL_CHUNK);
-    hipLaunchKernelGGL(k_sel_init, dim3(B), dim3(256), 0, s, t.hist1);
     const int nhg = (HI + 15) / 16, kch = (DI + 63) / 64;
 #define DL_SCORE_CASE(H_, K_) \
     if (nhg == H_ && kch == K_) launch_score<H_, K_>(s, q_idx, k_pool, pg, ps_shift, HI, DI, t, Lmax, R, pool); else

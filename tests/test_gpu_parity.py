@@ -83,6 +83,29 @@ def test_indexer_topk_tiled_keys(name):
     _check_topk(spec, t, tiled=True)
 
 
+def test_indexer_topk_reused_workspace():
+    # the scoring kernel clears the histograms itself: a workspace of garbage bytes (every flag word all ones), the
+    # same workspace again after a selection over other queries (its flags then hold the earlier launch's stamp),
+    # and a third call, all give the oracle's selection bit for bit
+    spec = synth.small_fp8_spec(name="reuse", seq_lens=(5000, 2049, 17, 3000))
+    t = _layer(spec, seed=3, weights=False)
+    t2 = _layer(spec, seed=4, weights=False)
+    pg = dl.pages(t["seq_lens"], t["page_table"], spec.page_size)
+    ws = dl.workspace(dl.load().dl_indexer_topk_rows_workspace(dl.C.byref(pg), 1), DEV)
+    ws.fill_(0xFF)
+    orc = oracle.LayerOracle(spec, t)
+    want = [orc.row(b, stages=("sel",))["sel"] for b in range(spec.B)]
+    for call, q in enumerate((t["q_idx"], t2["q_idx"], t["q_idx"], t["q_idx"])):
+        sel = torch.empty(spec.B, spec.topk, dtype=torch.int32, device=DEV)
+        say(f"[gpu] indexer_topk on a reused workspace, call {call}")
+        dl.indexer_topk(pg, q, t["k_pool"], spec.topk, sel, ws=ws)
+        torch.cuda.synchronize()
+        if q is t["q_idx"]:
+            got = host(sel)
+            for b in range(spec.B):
+                assert np.array_equal(got[b], want[b]), f"call {call} row {b}"
+
+
 def test_indexer_topk_k_above_length_and_empty_rows():
     spec = synth.small_fp8_spec(name="short", seq_lens=(100, 0, 511, 512, 513), B=5, topk=512)
     t = _layer(spec, seed=2, weights=False)
