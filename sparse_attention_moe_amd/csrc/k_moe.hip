@@ -37,20 +37,29 @@ __global__ __launch_bounds__(256) void k_route_partial(const float *__restrict__
     const int e0 = blockIdx.x * 16, c = blockIdx.y;
     const int kq = c * ROUTE_KC + w * ROUTE_KW + 4 * g;
     const int e = e0 + r;
+    // every load unconditional (expert, token and feature clamped into range, the values masked to zero after),
+    // and the first token tile's activations issued with the weights, so both are in flight together (the grid
+    // covers up to 1,024 tokens with one tile per workgroup; beyond that a workgroup loads its later tiles in turn)
+    const bool ev = e < E;
     v4f wv[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
-        const int k = kq + 16 * j;
-        wv[j] = (e < E && k < D) ? *(const v4f *)(wr + (long)e * D + k) : v4f{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < NJ; j++) wv[j] = *(const v4f *)(wr + (long)min(e, E - 1) * D + min(kq + 16 * j, D - 4));
+    auto load_h = [&](int t0, v4f (&hv)[NJ]) {
+        const int t = min(t0 + r, B - 1);
+#pragma unroll
+        for (int j = 0; j < NJ; j++) hv[j] = *(const v4f *)(h + (long)t * D + min(kq + 16 * j, D - 4));
+    };
+    v4f hn[NJ];
+    load_h(blockIdx.z * 16, hn);
+#pragma unroll
+    for (int j = 0; j < NJ; j++)
+        if (!(ev && kq + 16 * j < D)) wv[j] = v4f{0.f, 0.f, 0.f, 0.f};
     for (int t0 = blockIdx.z * 16; t0 < B; t0 += gridDim.z * 16) {
         const int t = t0 + r;
+        if (t0 != (int)blockIdx.z * 16) load_h(t0, hn);
         v4f hv[NJ];
 #pragma unroll
-        for (int j = 0; j < NJ; j++) {
-            const int k = kq + 16 * j;
-            hv[j] = (t < B && k < D) ? *(const v4f *)(h + (long)t * D + k) : v4f{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int j = 0; j < NJ; j++) hv[j] = (t < B && kq + 16 * j < D) ? hn[j] : v4f{0.f, 0.f, 0.f, 0.f};
         v4d acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int j = 0; j < NJ; j++)
