@@ -535,62 +535,78 @@ int launch_plan(const int32_t *experts, int B, int ke, int E, int S, const MoePl
 }
 
 // out[b, d] = resid[b, d] + sum_j gate[b, j] f_j[d] + sum_s f_s[d], in that order, where f is the sum of the
-// expert output's nslot partial slots (in slot order).  A thread owns 4
-// consecutive features of one token; the token's pair indices and gates are wave-uniform (scalar loads), and
-// the expert outputs are fetched 8 slots at a time so their loads are in flight together.
+// expert output's nslot partial slots (in slot order).  A thread owns 4 consecutive features of one token (a
+// workgroup's threads all hold the same token).  Lane j of a wave loads the token's pair index j and gate j, and
+// the wave reads them back with readlane, so those loads are one round trip (scalar loads of the same words were
+// each waited for before the next); the residual is loaded in both layouts at once (the one not used reads another
+// array in bounds), and the expert outputs 16 pairs at a time, so all of a thread's loads are in flight together.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, int nslot, long fstride,
                                                  const int *__restrict__ pair_idx,
                                                  const float *__restrict__ gates, int B, int D, int ke, int S,
                                                  const void *__restrict__ resid, int resid_dt, void *__restrict__ out,
                                                  int out_dt, float *__restrict__ out32)
 {
-    const int b = blockIdx.y;
-    const int d = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (d >= D) return;
+    constexpr int PU = 16;  // pairs per round
+    const int b = blockIdx.y, lane = threadIdx.x & 63;
+    const int d0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const bool dv = d0 < D;
+    const int d = min(d0, D - 4);  // lanes past the row compute on its last features and store nothing
     const int kk = ke + S;
     const long row = (long)b * D + d;
-    v4f acc;
-    if (!resid) acc = v4f{0.f, 0.f, 0.f, 0.f};
-    else if (resid_dt == DL_BF16) {
-        const uint2 r = *(const uint2 *)((const uint16_t *)resid + row);
-        acc = v4f{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
-                  __uint_as_float(r.y & 0xFFFF0000u)};
-    } else acc = *(const v4f *)((const float *)resid + row);
     const int *pi = pair_idx + (long)b * kk;
     const float *gt = gates + (long)b * ke;
-    for (int j0 = 0; j0 < kk; j0 += 8) {
-        v4f f[8], f2[8];
-        int q[8];
-        // every load unconditional (a missing pair reads pair 0's row and is dropped below), so the slots' loads
-        // are in flight together: a load under a condition is waited for on its own
-#pragma unroll
-        for (int u = 0; u < 8; u++) q[u] = pi[min(j0 + u, kk - 1)];
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-            q[u] = j0 + u < kk ? q[u] : -1;  // -1: past the slots, or a pair computed elsewhere
-            f[u] = *(const v4f *)(F + (long)max(q[u], 0) * D + d);
-            if (nslot > 1) f2[u] = *(const v4f *)(F + fstride + (long)max(q[u], 0) * D + d);
+    const bool rbf = resid && resid_dt == DL_BF16, rf32 = resid && resid_dt != DL_BF16;
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    bool first = true;
+    for (int j0 = 0; j0 < max(kk, 1); j0 += 64) {
+        // pair indices and gates j0 .. j0 + 63, one per lane (with no pairs at all: any readable words, unused)
+        const int qv = kk > 0 ? pi[min(j0 + lane, kk - 1)] : 0;
+        const float gv = ke > 0 ? gt[min(j0 + lane, ke - 1)] : 0.f;
+        if (first) {
+            // the residual, loaded after the indices so that one wait covers both, and taken into the sum first
+            const uint2 r16 = *(const uint2 *)((rbf ? (const uint16_t *)resid : (const uint16_t *)F) + row);
+            const v4f r32 = *(const v4f *)((rf32 ? (const float *)resid : F) + row);
+            const v4f a16 = v4f{__uint_as_float(r16.x << 16), __uint_as_float(r16.x & 0xFFFF0000u),
+                                __uint_as_float(r16.y << 16), __uint_as_float(r16.y & 0xFFFF0000u)};
+            acc = rbf ? a16 : rf32 ? r32 : acc;
+            first = false;
         }
-        if (nslot > 1)
+        for (int j1 = j0; j1 < min(kk, j0 + 64); j1 += PU) {
+            v4f f[PU], f2[PU];
+            int q[PU];
+            // the indices read back from their lanes (all shuffles first, then one wait), then every load
+            // unconditional (a missing pair reads pair 0's row and is dropped below)
 #pragma unroll
-            for (int u = 0; u < 8; u++) f[u] += f2[u];
-        for (int k = 2; k < nslot; k++) {
+            for (int u = 0; u < PU; u++) q[u] = __shfl(qv, min(j1 + u - j0, 63), 64);
 #pragma unroll
-            for (int u = 0; u < 8; u++)
-                if (q[u] >= 0) f[u] += *(const v4f *)(F + k * fstride + (long)q[u] * D + d);
-        }
+            for (int u = 0; u < PU; u++) q[u] = j1 + u < kk ? q[u] : -1;  // -1: past the slots, or elsewhere
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int j = j0 + u;
-            if (q[u] >= 0) {
-                if (j < ke) {
-                    const float g = gt[j];
-                    acc.x = fmaf(g, f[u].x, acc.x); acc.y = fmaf(g, f[u].y, acc.y);
-                    acc.z = fmaf(g, f[u].z, acc.z); acc.w = fmaf(g, f[u].w, acc.w);
-                } else acc += f[u];
+            for (int u = 0; u < PU; u++) {
+                f[u] = *(const v4f *)(F + (long)max(q[u], 0) * D + d);
+                f2[u] = *(const v4f *)(F + (nslot > 1 ? fstride : 0) + (long)max(q[u], 0) * D + d);
+            }
+            if (nslot > 1)
+#pragma unroll
+                for (int u = 0; u < PU; u++) f[u] += f2[u];
+            for (int k = 2; k < nslot; k++) {
+#pragma unroll
+                for (int u = 0; u < PU; u++)
+                    if (q[u] >= 0) f[u] += *(const v4f *)(F + k * fstride + (long)q[u] * D + d);
+            }
+#pragma unroll
+            for (int u = 0; u < PU; u++) {
+                const int j = j1 + u;
+                const float g = __shfl(gv, min(j - j0, 63), 64);
+                if (q[u] >= 0) {
+                    if (j < ke) {
+                        acc.x = fmaf(g, f[u].x, acc.x); acc.y = fmaf(g, f[u].y, acc.y);
+                        acc.z = fmaf(g, f[u].z, acc.z); acc.w = fmaf(g, f[u].w, acc.w);
+                    } else acc += f[u];
+                }
             }
         }
     }
+    if (!dv) return;
     if (out32) *(v4f *)(out32 + row) = acc;
     if (out_dt == DL_BF16) {
         uint2 o;
