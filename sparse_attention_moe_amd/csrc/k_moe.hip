@@ -589,9 +589,11 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ F, in
 #pragma unroll
                 for (int u = 0; u < PU; u++) f[u] += f2[u];
             for (int k = 2; k < nslot; k++) {
+                v4f f3[PU];
 #pragma unroll
-                for (int u = 0; u < PU; u++)
-                    if (q[u] >= 0) f[u] += *(const v4f *)(F + k * fstride + (long)q[u] * D + d);
+                for (int u = 0; u < PU; u++) f3[u] = *(const v4f *)(F + k * fstride + (long)max(q[u], 0) * D + d);
+#pragma unroll
+                for (int u = 0; u < PU; u++) f[u] += f3[u];
             }
 #pragma unroll
             for (int u = 0; u < PU; u++) {
