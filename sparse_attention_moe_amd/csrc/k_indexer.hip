@@ -18,8 +18,9 @@
 //            (score above, complemented position below, so ties go to the lower position), sets their
 //            bits, then compacts the bitmap in position order, so the list comes out ascending.
 // Every mark workgroup picks the bin from the histogram (the same deterministic pick, made visible by
-// the kernel boundary); workgroup 0 records it for the final kernel.  No workgroup waits on, or fences
-// for, another: on this part an in-kernel device-wide barrier costs far more than a kernel boundary.
+// the kernel boundary); workgroup 0 records it for the final kernel.  No device-wide barrier: on this part one
+// costs far more than a kernel boundary.  The one wait inside a kernel is the scoring workgroups' wait for their
+// sequence's first workgroup to have cleared the histograms (a per-launch stamp, read once at their end).
 #include "dl_common.h"
 #include "dl_internal.h"
 
