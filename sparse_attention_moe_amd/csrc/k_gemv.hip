@@ -592,7 +592,11 @@ __global__ __launch_bounds__(256, 2) void k_ffn_fp8(FfnFused f)
         if (v < nrb) poison = true;
     };
 
-    long t = qindex((blockIdx.x / npool) * 4 + (threadIdx.x >> 6));  // the wave's first piece, fixed by its index
+    // the wave's first piece, fixed by its index: dealt wave-major over the pool's workgroups (wave 0 of every
+    // workgroup, then wave 1, ...), so that when the pieces are fewer than the waves the busy waves spread over
+    // the compute units instead of filling the first workgroups' units (a unit streams at a bounded rate, and a
+    // unit holding twice the busy waves finishes its pieces twice as late)
+    long t = qindex((threadIdx.x >> 6) * (qbase / 4) + (int)(blockIdx.x / npool));
     if (t >= qtot) {
         q_done();
         return;
