@@ -76,7 +76,8 @@ struct Marks {
     hipStream_t s = nullptr;
     void at(int i) const
     {
-        if (m) hipEventRecord(m->ev[i], s);
+        // a record that fails leaves its event unrecorded, which dl_profile_read reports (elapsed time fails)
+        if (m) (void)hipEventRecord(m->ev[i], s);
     }
 };
 
@@ -1069,9 +1070,9 @@ int dl_profile_enable(int on)
     g_prof = on != 0;
     if (!g_prof) {
         for (int i = 0; i < g_npend; i++)
-            for (int j = 0; j <= DL_N_PHASES; j++) hipEventDestroy(g_pend[i].ev[j]);
+            for (int j = 0; j <= DL_N_PHASES; j++) (void)hipEventDestroy(g_pend[i].ev[j]);
         for (int i = 0; i < g_nfree; i++)
-            for (int j = 0; j <= DL_N_PHASES; j++) hipEventDestroy(g_free[i].ev[j]);
+            for (int j = 0; j <= DL_N_PHASES; j++) (void)hipEventDestroy(g_free[i].ev[j]);
         g_npend = g_nfree = 0;
     }
     return DL_OK;

@@ -958,7 +958,7 @@ __global__ __launch_bounds__(256) void k_gemv_f32(GemvArgs a)
         }
 #pragma unroll
         for (int t = 0; t < 16; t++) {
-            if (t >= nt) break;
+            if (t >= nt) continue;  // (uniform over the wave)
             float v = wave_sum(acc[t]);
             const float v2 = SW ? wave_sum(acc2[t]) : 0.f;
             if (lane == 0) {
