@@ -277,14 +277,15 @@ def test_route_standalone(B, E, ke, D, dup):
 
 
 # ------------------------------------------------------------------ the five named workloads
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_config(cfg):
+def test_full_config(cfg, seed):
     """The fused step at full size, in the launch configuration the benchmark times (tiled weights and keys),
     against the oracle on every row: kept positions bit-exact (and, from the indexer entry point on the same
     keys, their scores), experts bit-exact up to oracle logits within 1e-6, o, h - x, y - h, y and the gates
     within the floating-point bar; router logits compared to the oracle's fp64 ones."""
     spec = synth.config(cfg)
-    t = _layer(spec, seed=0)
+    t = _layer(spec, seed=seed)
     step = dl.LayerStep(spec, t, debug=True)
     say(f"[gpu] layer_step {spec.name}")
     y = step()
@@ -305,7 +306,7 @@ def test_full_config(cfg):
         n = int((r["sel"] >= 0).sum())
         assert np.array_equal(ss[b][:n], r["scores"][r["sel"][:n]]), f"row {b}: kept scores differ"
         assert np.all(ss[b][n:] == 0)
-    say(f"cfg{cfg}: {w}")
+    say(f"cfg{cfg} seed {seed}: {w}")
     assert w["logit_abs"] < 1e-4
     del step, t
     torch.cuda.empty_cache()
