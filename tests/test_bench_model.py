@@ -43,3 +43,14 @@ def test_short_rows_pools_and_multi_row_counts():
     br = bench.algorithmic_bytes(r, r.seq_lens, 1)
     # row r of a sequence sees seq_len - (R - 1 - r) positions: 2047 + 2048, 0 + 1, then 2 x 2048 for the rest
     assert br["selected_kv"] == (2047 + 2048 + 0 + 1 + 6 * 2 * 2048) * 596
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The build measures one GPU: asked for more, bench.py exits with status 2 and says so, before touching a GPU."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
